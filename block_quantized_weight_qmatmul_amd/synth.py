@@ -1,0 +1,201 @@
+"""Seeded synthetic inputs for block-quantized mat-vec workloads.
+
+This module only *draws* inputs: raw block bytes, activations, router ids and
+per-expert scales. It contains none of the arithmetic of the dequantize-and-
+multiply itself (no decoding of codes, no dot products), so that the CPU
+oracle and the HIP path can both be fed from it without sharing any of the
+computation they are compared on.
+
+Block byte formats the generator writes (GGML-style, 32 weights per block):
+
+* Q4_0, 18 bytes: a little-endian IEEE binary16 scale ``d`` in bytes [0, 2),
+  then 16 bytes of packed 4-bit codes. Codes are drawn i.i.d. uniform over
+  0..15 for every one of the 32 elements. Because every nibble is an
+  independent uniform draw, this is the same as drawing each of the 16 code
+  bytes uniformly over 0..255, which is what the generator does: it never
+  needs to know which nibble holds which element.
+* Q8_0, 34 bytes: the same binary16 scale, then 32 two's-complement int8
+  codes drawn uniformly over -127..127 (the encoder on the hf2q model page,
+  ``load_from_gguf`` lm_head Q8_0 block, never emits -128).
+
+Scales are drawn as fp32 uniforms and rounded to binary16 with numpy's
+round-to-nearest-even cast.
+
+Seeds: ``numpy.random.default_rng([20261202, cfg, copy, tensor, part])``
+with tensor ids 0 = scales, 1 = codes, 2 = activations, 3 = router logits,
+4 = per-expert scale; ``part`` tells apart several matrices of one config.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, List, Sequence, Tuple
+
+import numpy as np
+
+ROOT_SEED = 20261202
+
+T_SCALE, T_CODES, T_X, T_LOGITS, T_ESCALE = 0, 1, 2, 3, 4
+
+QK = 32  # weights per block
+BLOCK_BYTES = {"q4_0": 18, "q8_0": 34}
+QTYPE_ID = {"q4_0": 2, "q8_0": 8}  # GGML type numbers for Q4_0 and Q8_0
+
+# Scale ranges and code ranges the workloads draw from.
+Q4_0_D_RANGE = (0.001, 0.02)
+Q8_0_D_RANGE = (0.0005, 0.01)
+
+
+def rng(cfg: int, copy: int, tensor: int, part: int = 0) -> np.random.Generator:
+    return np.random.default_rng([ROOT_SEED, cfg, copy, tensor, part])
+
+
+def row_bytes(qtype: str, K: int) -> int:
+    if K % QK:
+        raise ValueError(f"K={K} is not a multiple of {QK}")
+    return K // QK * BLOCK_BYTES[qtype]
+
+
+def _scales_f16_bytes(r: np.random.Generator, shape, lo: float, hi: float) -> np.ndarray:
+    d32 = r.uniform(lo, hi, size=shape).astype(np.float32)
+    d16 = d32.astype(np.float16)  # round-to-nearest-even
+    return d16.astype("<f2").view(np.uint8).reshape(*shape, 2)
+
+
+def make_weights(qtype: str, N: int, K: int, cfg: int, copy: int = 0, part: int = 0,
+                 d_range: Tuple[float, float] | None = None, ldw: int | None = None) -> np.ndarray:
+    """Return a uint8 array ``[N, ldw]`` of N rows, each K/32 blocks of ``qtype``.
+
+    Bytes past the dense row length (when ``ldw`` exceeds it) are filled with
+    0xA5 so that a reader that strays into the row padding gets garbage.
+    """
+    bb = BLOCK_BYTES[qtype]
+    nb = K // QK
+    dense = row_bytes(qtype, K)
+    ldw = dense if ldw is None else ldw
+    if ldw < dense:
+        raise ValueError("ldw smaller than a dense row")
+    if d_range is None:
+        d_range = Q4_0_D_RANGE if qtype == "q4_0" else Q8_0_D_RANGE
+    blocks = np.empty((N, nb, bb), dtype=np.uint8)
+    blocks[..., 0:2] = _scales_f16_bytes(rng(cfg, copy, T_SCALE, part), (N, nb), *d_range)
+    rc = rng(cfg, copy, T_CODES, part)
+    if qtype == "q4_0":
+        blocks[..., 2:] = rc.integers(0, 256, size=(N, nb, bb - 2), dtype=np.uint8)
+    else:
+        blocks[..., 2:] = rc.integers(-127, 128, size=(N, nb, bb - 2)).astype(np.int8).view(np.uint8)
+    if ldw == dense:
+        return blocks.reshape(N, dense)
+    out = np.full((N, ldw), 0xA5, dtype=np.uint8)
+    out[:, :dense] = blocks.reshape(N, dense)
+    return out
+
+
+def make_x(M: int, K: int, cfg: int, copy: int = 0, part: int = 0) -> np.ndarray:
+    """Activations ``[M, K]`` fp32 drawn from N(0, 1)."""
+    return rng(cfg, copy, T_X, part).standard_normal((M, K), dtype=np.float64).astype(np.float32)
+
+
+def router_topk(T: int, n_experts: int, top_k: int, cfg: int, copy: int = 0, part: int = 0) -> np.ndarray:
+    """Expert ids ``[T, top_k]`` uint32: the top_k largest of N(0,1) router logits.
+
+    Ids come in descending logit order; equal logits go to the lower index
+    (a stable argsort of the negated logits).
+    """
+    logits = rng(cfg, copy, T_LOGITS, part).standard_normal((T, n_experts)).astype(np.float32)
+    order = np.argsort(-logits, axis=1, kind="stable")
+    return order[:, :top_k].astype(np.uint32)
+
+
+def expert_scale(n_experts: int, cfg: int, copy: int = 0, part: int = 0) -> np.ndarray:
+    """Per-expert fp32 scale drawn from U[0.5, 1.5]."""
+    return rng(cfg, copy, T_ESCALE, part).uniform(0.5, 1.5, size=n_experts).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# The five workloads. Each is a list of problems; a dense problem is
+# (name, qtype, M, N, K) and the MoE workload lists its two id calls.
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class Dense:
+    name: str
+    qtype: str
+    M: int
+    N: int
+    K: int
+
+    @property
+    def weight_bytes(self) -> int:
+        return self.N * row_bytes(self.qtype, self.K)
+
+
+@dataclasses.dataclass(frozen=True)
+class MoeId:
+    name: str
+    qtype: str
+    n_experts: int
+    n_tokens: int   # rows of X handed to the call
+    top_k: int      # experts per X row
+    N: int
+    K: int
+
+
+CONFIGS: Dict[int, dict] = {
+    0: {"name": "q4_0_m1_2048x2048",
+        "problems": [Dense("proj", "q4_0", 1, 2048, 2048)]},
+    1: {"name": "q4_0_m1_decode_layer_h4096",
+        "problems": [Dense("q", "q4_0", 1, 4096, 4096), Dense("k", "q4_0", 1, 1024, 4096),
+                     Dense("v", "q4_0", 1, 1024, 4096), Dense("o", "q4_0", 1, 4096, 4096),
+                     Dense("gate", "q4_0", 1, 14336, 4096), Dense("up", "q4_0", 1, 14336, 4096),
+                     Dense("down", "q4_0", 1, 4096, 14336)]},
+    2: {"name": "q8_0_m1_4096x14336",
+        "problems": [Dense("up", "q8_0", 1, 14336, 4096), Dense("down", "q8_0", 1, 4096, 14336)]},
+    3: {"name": "q4_0_m16_k5120",
+        "problems": [Dense("n5120", "q4_0", 16, 5120, 5120), Dense("n1024", "q4_0", 16, 1024, 5120),
+                     Dense("n27648", "q4_0", 16, 27648, 5120)]},
+    4: {"name": "q4_0_moe_id_e128_top8_h2816_i704"},
+}
+
+MOE = dict(n_experts=128, top_k=8, hidden=2816, inter=704)
+
+
+def moe_calls(T: int) -> List[MoeId]:
+    """The two id calls of one MoE FFN for T tokens.
+
+    gate_up: X is [T, hidden], ids [T, top_k], output rows T*top_k of 2*inter.
+    down: the slots are flattened (n_tokens = T*top_k, top_k = 1); X is the
+    [T*top_k, inter] per-slot input and the output is [T*top_k, hidden].
+    """
+    E, k, h, i = MOE["n_experts"], MOE["top_k"], MOE["hidden"], MOE["inter"]
+    return [MoeId("gate_up", "q4_0", E, T, k, 2 * i, h),
+            MoeId("down", "q4_0", E, T * k, 1, h, i)]
+
+
+def distinct(ids: np.ndarray) -> int:
+    return int(np.unique(ids).size)
+
+
+def dense_inputs(cfg: int, p: Dense, part: int, copy: int = 0, ldw: int | None = None):
+    """(W bytes [N, ldw], X [M, K]) for one dense problem of a config."""
+    W = make_weights(p.qtype, p.N, p.K, cfg, copy, part, ldw=ldw)
+    X = make_x(p.M, p.K, cfg, copy, part)
+    return W, X
+
+
+def moe_inputs(T: int, copy: int = 0, cfg: int = 4):
+    """All inputs of the MoE workload for T tokens.
+
+    Returns a dict with the stacked gate_up and down weights (uint8
+    [E, N, row_bytes]), the gate_up input X [T, hidden], the down input
+    [T*top_k, inter], ids [T, top_k] and the per-expert scale [E].
+    """
+    gu, dn = moe_calls(T)
+    E = MOE["n_experts"]
+    return {
+        "W_gate_up": make_weights("q4_0", E * gu.N, gu.K, cfg, copy, part=0).reshape(E, gu.N, -1),
+        "W_down": make_weights("q4_0", E * dn.N, dn.K, cfg, copy, part=1).reshape(E, dn.N, -1),
+        "X_gate_up": make_x(T, gu.K, cfg, copy, part=0),
+        "X_down": make_x(T * MOE["top_k"], dn.K, cfg, copy, part=1),
+        "ids": router_topk(T, E, MOE["top_k"], cfg, copy),
+        "expert_scale": expert_scale(E, cfg, copy),
+    }

@@ -1,0 +1,219 @@
+/*
+ * CPU oracle for block-quantized weight mat-vec (test infrastructure only).
+ *
+ * This file is TEST INFRASTRUCTURE. Only the test suite, the package's smoke
+ * check and the benchmark's CPU-baseline leg may load or call it. The HIP
+ * library never links, includes or calls anything here, and nothing here
+ * includes anything of the HIP library.
+ *
+ * What it computes is the plain definition, in fp64, with no blocking,
+ * fusion or reordering:
+ *
+ *   1. decode every 32-element block of a weight row into fp64 values
+ *      (a binary16 scale times an integer code), giving the dense row w[0..K);
+ *   2. y[m][n] = sum_{k<K} w[n][k] * x[m][k], summed in index order in fp64;
+ *      a[m][n] = sum_{k<K} |w[n][k] * x[m][k]|, the magnitude the acceptance
+ *      tolerance is scaled by.
+ *
+ * Block formats (32 weights per block, rows of K/32 blocks, row stride ldw
+ * bytes):
+ *
+ *   Q8_0 (34 B): bytes 0,1 = scale bits, low byte first; bytes 2..33 = int8
+ *   codes, element j in byte 2+j; w = code * d. This is the inverse of the
+ *   lm_head Q8_0 encoder on the hf2q page `src/inference/models/gemma4/
+ *   model.rs` (`load_from_gguf`, the block that builds `lm_head_q8`: it
+ *   writes `d_bits & 0xFF`, then `d_bits >> 8`, then each code as a byte).
+ *   Any int8 decodes as-is, -128 included.
+ *
+ *   Q4_0 (18 B): the pages name the format (the `MlxMoeWeights` doc calls
+ *   the weights "GGML block format"; a `qwen3-vl-2b-q4_0.gguf` model is
+ *   named in `MlxMoeWeights::dense_placeholder`) but never lay it out. The
+ *   reading taken here is the GGML Q4_0 block: bytes 0,1 = binary16 scale
+ *   (low byte first); byte 2+j (j < 16) holds element j in its low nibble and
+ *   element j+16 in its high nibble; w = (code - 8) * d.
+ *
+ *   The scale is decoded exactly from its IEEE 754 binary16 bit pattern:
+ *   subnormals kept, signed zero kept, Inf/NaN propagate.
+ *
+ * Expert-indexed variant (the `quantized_matmul_id_ggml` calls in
+ * `MlxModelWeights::encode_one_layer` on the hf2q page
+ * `src/inference/models/gemma4/gpu_full_attn.rs`, MoE blocks B11 and B13,
+ * with the parameter block n_tokens, top_k, n, k, n_experts, expert_stride):
+ * for token t < n_tokens and slot s < top_k, e = ids[t*top_k + s]; expert
+ * e's weights start at byte e*expert_stride of the stacked buffer; the
+ * output row is t*top_k + s and the input row is t. An optional per-expert
+ * scale multiplies the row (the pages fold `per_expert_scale` into the
+ * routing weights of the weighted sum that follows; since that sum is linear,
+ * scaling the id output row is the same product).
+ *
+ * Every function returns 0 on success and a negative value on bad arguments.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_QK 32
+#define ORACLE_Q4_0 2
+#define ORACLE_Q8_0 8
+
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+double oracle_f16_to_f64(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1F;
+    int f = h & 0x3FF;
+    double v;
+    if (e == 0) {
+        v = ldexp((double)f, -24); /* subnormal or zero: f * 2^-14 * 2^-10 */
+    } else if (e == 31) {
+        v = f ? NAN : INFINITY;
+    } else {
+        v = ldexp((double)(1024 + f), e - 25); /* (1 + f/1024) * 2^(e-15) */
+    }
+    return sign ? -v : v;
+}
+
+static int block_bytes(int qtype) {
+    if (qtype == ORACLE_Q4_0) return 18;
+    if (qtype == ORACLE_Q8_0) return 34;
+    return -1;
+}
+
+/* Decode one 32-element block into out[0..32). */
+static void decode_block(int qtype, const uint8_t* b, double* out) {
+    uint16_t bits = (uint16_t)(b[0] | (b[1] << 8));
+    double d = oracle_f16_to_f64(bits);
+    if (qtype == ORACLE_Q4_0) {
+        for (int j = 0; j < 16; ++j) {
+            int lo = b[2 + j] & 0x0F;
+            int hi = b[2 + j] >> 4;
+            out[j] = (double)(lo - 8) * d;
+            out[j + 16] = (double)(hi - 8) * d;
+        }
+    } else {
+        for (int j = 0; j < 32; ++j) {
+            int8_t q = (int8_t)b[2 + j];
+            out[j] = (double)q * d;
+        }
+    }
+}
+
+/* Dequantize one row of K weights (K % 32 == 0) into w[0..K). */
+int oracle_dequant_row(int qtype, const uint8_t* row, int K, double* w) {
+    int bb = block_bytes(qtype);
+    if (bb < 0 || K <= 0 || K % ORACLE_QK) return -1;
+    for (int b = 0; b < K / ORACLE_QK; ++b) decode_block(qtype, row + (size_t)b * bb, w + (size_t)b * ORACLE_QK);
+    return 0;
+}
+
+static void dot_row(const double* w, const float* x, int K, double* y, double* a) {
+    double s = 0.0, m = 0.0;
+    for (int k = 0; k < K; ++k) {
+        double p = w[k] * (double)x[k];
+        s += p;
+        m += fabs(p);
+    }
+    *y = s;
+    if (a) *a = m;
+}
+
+static void set_threads(int nthreads) {
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+}
+
+/*
+ * Dense product: Y[m*ldy + n] = sum_k w[n][k] * X[m*ldx + k] for m < M, n < N.
+ * W: N rows of K/32 blocks, row n at W + n*ldw. A (nullable) receives the
+ * absolute-product sums in the same layout as Y. nthreads <= 0 keeps the
+ * OpenMP default.
+ */
+int oracle_qmv(int qtype, const uint8_t* W, size_t ldw, const float* X, size_t ldx,
+               int M, int N, int K, double* Y, double* A, size_t ldy, int nthreads) {
+    int bb = block_bytes(qtype);
+    if (bb < 0 || M < 0 || N < 0 || K <= 0 || K % ORACLE_QK) return -1;
+    if (ldw < (size_t)(K / ORACLE_QK) * bb || ldx < (size_t)K || ldy < (size_t)N) return -1;
+    set_threads(nthreads);
+    int err = 0;
+#pragma omp parallel
+    {
+        double* w = (double*)malloc(sizeof(double) * (size_t)K);
+        if (!w) {
+#pragma omp atomic write
+            err = -2;
+        } else {
+#pragma omp for schedule(static)
+            for (int n = 0; n < N; ++n) {
+                oracle_dequant_row(qtype, W + (size_t)n * ldw, K, w);
+                for (int m = 0; m < M; ++m)
+                    dot_row(w, X + (size_t)m * ldx, K, &Y[(size_t)m * ldy + n],
+                            A ? &A[(size_t)m * ldy + n] : NULL);
+            }
+            free(w);
+        }
+    }
+    return err;
+}
+
+/*
+ * Expert-indexed product. For t < n_tokens, s < top_k:
+ *   e = ids[t*top_k + s]  (must be < n_experts, else the call fails with -3)
+ *   Y[(t*top_k + s)*ldy + n] = sc * sum_k w_e[n][k] * X[t*ldx + k]
+ * with w_e the N x K matrix at W + e*expert_stride (row stride ldw) and
+ * sc = expert_scale[e] when expert_scale is given, else 1.
+ * A receives |sc| * sum_k |w_e[n][k] * X[t*ldx + k]|.
+ */
+int oracle_qmv_id(int qtype, const uint8_t* W, size_t expert_stride, size_t ldw, int n_experts,
+                  const float* X, size_t ldx, const uint32_t* ids, int n_tokens, int top_k,
+                  const float* expert_scale, int N, int K, double* Y, double* A, size_t ldy,
+                  int nthreads) {
+    int bb = block_bytes(qtype);
+    if (bb < 0 || n_experts <= 0 || n_tokens < 0 || top_k <= 0 || N < 0 || K <= 0 || K % ORACLE_QK) return -1;
+    if (ldw < (size_t)(K / ORACLE_QK) * bb || ldx < (size_t)K || ldy < (size_t)N) return -1;
+    if (expert_stride < (size_t)N * ldw) return -1;
+    int P = n_tokens * top_k;
+    for (int p = 0; p < P; ++p)
+        if (ids[p] >= (uint32_t)n_experts) return -3;
+    set_threads(nthreads);
+    int err = 0;
+#pragma omp parallel
+    {
+        double* w = (double*)malloc(sizeof(double) * (size_t)K);
+        if (!w) {
+#pragma omp atomic write
+            err = -2;
+        } else {
+#pragma omp for schedule(static) collapse(2)
+            for (int p = 0; p < P; ++p) {
+                for (int n = 0; n < N; ++n) {
+                    uint32_t e = ids[p];
+                    int t = p / top_k;
+                    double sc = expert_scale ? (double)expert_scale[e] : 1.0;
+                    const uint8_t* row = W + (size_t)e * expert_stride + (size_t)n * ldw;
+                    double y, a;
+                    oracle_dequant_row(qtype, row, K, w);
+                    dot_row(w, X + (size_t)t * ldx, K, &y, &a);
+                    Y[(size_t)p * ldy + n] = sc * y;
+                    if (A) A[(size_t)p * ldy + n] = fabs(sc) * a;
+                }
+            }
+            free(w);
+        }
+    }
+    return err;
+}
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,317 @@
+"""Pins of the CPU oracle to facts other than itself (CPU only).
+
+Each test ties one part of the oracle to something that does not come from the
+oracle: hand-built blocks with hand-derived values (tests/golden/), the Q8_0
+encoder printed on the hf2q model page, IEEE binary16 as numpy implements it,
+closed forms, exact rational arithmetic on tiny inputs, and the expert-routing
+signature. A plausible mistake in the oracle (swapped nibbles, a dropped -8,
+a wrong byte order for the scale, a transposed operand, a wrong x or y row in
+the expert-indexed call) fails at least one of them.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from golden_io import read_blocks
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+# --------------------------------------------------------------------------
+# binary16 scale decode: every bit pattern against numpy's IEEE binary16.
+# --------------------------------------------------------------------------
+def test_f16_decode_matches_ieee_binary16_for_all_patterns():
+    bits = np.arange(1 << 16, dtype=np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.f16_to_f64(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # signed zero is kept
+    assert math.copysign(1.0, oracle.f16_to_f64(0x8000)) == -1.0
+
+
+# --------------------------------------------------------------------------
+# Hand-built blocks (tests/golden/).
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("fixture,qtype", [("q4_0_blocks.txt", "q4_0"), ("q8_0_blocks.txt", "q8_0")])
+def test_golden_blocks_dequantize_to_hand_derived_values(fixture, qtype):
+    blocks = read_blocks(fixture)
+    assert len(blocks) >= 4
+    for label, raw, want in blocks:
+        got = oracle.dequant_row(qtype, raw, 32)
+        assert np.array_equal(got, want), (label, got, want)
+
+
+@pytest.mark.parametrize("fixture,qtype", [("q4_0_blocks.txt", "q4_0"), ("q8_0_blocks.txt", "q8_0")])
+def test_one_hot_x_picks_one_weight_exactly(fixture, qtype):
+    """x = e_k gives y[n] = w[n, k]: one exact product, every other term is 0."""
+    blocks = read_blocks(fixture)
+    W = np.stack([raw for _, raw, _ in blocks])
+    want = np.stack([v for _, _, v in blocks])
+    for k in range(32):
+        x = np.zeros((1, 32), dtype=np.float32)
+        x[0, k] = 1.0
+        y, a = oracle.qmv(qtype, W, x)
+        assert np.array_equal(y[0], want[:, k])
+        assert np.array_equal(a[0], np.abs(want[:, k]))
+
+
+def test_rows_of_x_map_to_rows_of_y():
+    """X[m, k0 + m] = 1 for m < M gives Y[m, n] = w[n, k0 + m]."""
+    blocks = read_blocks("q4_0_blocks.txt")
+    W = np.stack([raw for _, raw, _ in blocks])
+    want = np.stack([v for _, _, v in blocks])
+    M, k0 = 16, 9
+    X = np.zeros((M, 32), dtype=np.float32)
+    for m in range(M):
+        X[m, k0 + m] = 1.0
+    Y, _ = oracle.qmv("q4_0", W, X)
+    for m in range(M):
+        assert np.array_equal(Y[m], want[:, k0 + m])
+
+
+# --------------------------------------------------------------------------
+# Q8_0: the encoder printed on the hf2q model page (`load_from_gguf`, the
+# lm_head Q8_0 block), restated here, then decoded by the oracle.
+# --------------------------------------------------------------------------
+def page_q8_0_encode(block):
+    """amax over the block; d = amax/127 (fp32); inv_d = 1/d; scale stored as
+    binary16 bits low byte first; each code = round-half-away(v * inv_d)
+    clamped to [-127, 127] and stored as an int8 byte."""
+    v = np.asarray(block, dtype=np.float32)
+    amax = np.float32(np.max(np.abs(v))) if v.size else np.float32(0)
+    d = np.float32(amax / np.float32(127.0)) if amax > 0 else np.float32(0.0)
+    inv_d = np.float32(np.float32(1.0) / d) if d != 0 else np.float32(0.0)
+    bits = int(np.array(d, dtype=np.float32).astype(np.float16).view(np.uint16))
+    out = [bits & 0xFF, bits >> 8]
+    for vi in v:
+        t = float(np.float32(vi * inv_d))
+        q = math.copysign(math.floor(abs(t) + 0.5), t)
+        q = int(max(-127.0, min(127.0, q)))
+        out.append(q & 0xFF)
+    return np.array(out, dtype=np.uint8), d
+
+
+def test_q8_0_page_encoder_bytes_for_a_worked_block():
+    # v_j = j - 16: amax = 16, d = 16/127 -> binary16 0x3008 (= 0.1259765625),
+    # inv_d = 127/16 = 7.9375; code of -16 is -127, of 15 is round(119.0625) = 119.
+    raw, d = page_q8_0_encode(np.arange(32, dtype=np.float32) - 16)
+    assert raw[0] == 0x08 and raw[1] == 0x30
+    assert raw[2] == 0x81  # -127
+    assert raw[2 + 31] == 119
+    assert raw[2 + 17] == 8 and raw[2 + 15] == 0xF8  # v = 1 -> 8, v = -1 -> -8
+    got = oracle.dequant_row("q8_0", raw, 32)
+    assert got[0] == -127 * 0.1259765625 and got[31] == 119 * 0.1259765625
+
+
+def test_q8_0_page_encoder_round_trip_bound():
+    r = np.random.default_rng(7)
+    cases = [r.standard_normal(32) * s for s in (1e-3, 1.0, 50.0)]
+    cases += [np.zeros(32), np.r_[np.zeros(31), 3.0], r.uniform(-1, 1, 32) * 1e-6]
+    for v in cases:
+        v = v.astype(np.float32)
+        raw, d = page_q8_0_encode(v)
+        d16 = float(np.float32(d).astype(np.float16))
+        got = oracle.dequant_row("q8_0", raw, 32)
+        bound = 127 * abs(d16 - float(d)) + float(d) * (0.5 + 1e-4)
+        assert np.all(np.abs(got - v.astype(np.float64)) <= bound + 1e-300)
+
+
+def test_q8_0_lm_head_size_closed_form():
+    # The page sizes a Q8_0 lm_head of vocab 262144 x hidden 2816 at "784 MB"
+    # (vs 1.47 GB in F16): 34 bytes per 32 weights.
+    vocab, hidden = 262144, 2816
+    q8 = vocab * hidden // 32 * oracle.BLOCK_BYTES[oracle.Q8_0]
+    assert round(q8 / 1e6) == 784
+    assert math.floor(vocab * hidden * 2 / 1e7) / 100 == 1.47  # the F16 size the page quotes
+    assert oracle.BLOCK_BYTES[oracle.Q4_0] == 2 + 32 // 2
+
+
+# --------------------------------------------------------------------------
+# Closed forms and invariants of the dense product.
+# --------------------------------------------------------------------------
+def _const_blocks(qtype, N, K, code_byte, d_bits):
+    bb = oracle.BLOCK_BYTES[oracle.QTYPES[qtype]]
+    blk = np.full(bb, code_byte, dtype=np.uint8)
+    blk[0], blk[1] = d_bits & 0xFF, d_bits >> 8
+    return np.tile(blk, (N, K // 32))
+
+
+@pytest.mark.parametrize("code", range(16))
+def test_q4_0_constant_code_ones_closed_form(code):
+    K, N = 4096, 3
+    W = _const_blocks("q4_0", N, K, code | (code << 4), 0x3800)  # d = 0.5
+    y, a = oracle.qmv("q4_0", W, np.ones((1, K), dtype=np.float32))
+    assert np.all(y == K * (code - 8) * 0.5)
+    assert np.all(a == K * abs(code - 8) * 0.5)
+
+
+def test_q8_0_constant_code_ones_closed_form():
+    K, N = 14336, 2
+    for q in (-128, -127, -1, 0, 1, 127):
+        W = _const_blocks("q8_0", N, K, q & 0xFF, 0x3400)  # d = 0.25
+        y, a = oracle.qmv("q8_0", W, np.ones((1, K), dtype=np.float32))
+        assert np.all(y == K * q * 0.25) and np.all(a == K * abs(q) * 0.25)
+
+
+def test_q4_0_all_codes_eight_give_exact_zero():
+    from block_quantized_weight_qmatmul_amd import synth
+    W = synth.make_weights("q4_0", 5, 2048, cfg=99)
+    W.reshape(5, -1, 18)[:, :, 2:] = 0x88
+    y, a = oracle.qmv("q4_0", W, synth.make_x(2, 2048, cfg=99))
+    assert np.all(y == 0) and np.all(a == 0)
+
+
+def test_power_of_two_scaling_is_exact():
+    from block_quantized_weight_qmatmul_amd import synth
+    W = synth.make_weights("q4_0", 16, 1024, cfg=98)
+    X = synth.make_x(3, 1024, cfg=98)
+    y, _ = oracle.qmv("q4_0", W, X)
+    y8, _ = oracle.qmv("q4_0", W, X * np.float32(8.0))
+    assert np.array_equal(y8, 8.0 * y)
+
+
+# --------------------------------------------------------------------------
+# Brute force on tiny inputs in exact rational arithmetic.
+# --------------------------------------------------------------------------
+def _enc_q4_0(codes, d_bits):
+    """Lay 32 codes out as the Q4_0 reading says: byte 2+j = code[j] | code[j+16] << 4."""
+    return bytes([d_bits & 0xFF, d_bits >> 8] + [codes[j] | (codes[j + 16] << 4) for j in range(16)])
+
+
+def _enc_q8_0(codes, d_bits):
+    return bytes([d_bits & 0xFF, d_bits >> 8] + [c & 0xFF for c in codes])
+
+
+def _f16_fraction(bits):
+    return Fraction(float(np.array(bits, dtype=np.uint16).view(np.float16)))
+
+
+@pytest.mark.parametrize("qtype", ["q4_0", "q8_0"])
+def test_brute_force_tiny_shapes_against_exact_rationals(qtype):
+    r = np.random.default_rng(11)
+    d_pool = [0x3C00, 0x3800, 0xC000, 0x0001, 0x03FF, 0x1234, 0x5A5A, 0xB555, 0x7BFF]
+    for K in (32, 64):
+        N, M = 16, 3
+        nb = K // 32
+        rows, dense = [], []
+        for n in range(N):
+            raw, vals = b"", []
+            for b in range(nb):
+                if qtype == "q4_0":
+                    codes = [(n + 3 * b + j) % 16 for j in range(32)]  # every code at every position
+                    ints = [c - 8 for c in codes]
+                    enc = _enc_q4_0
+                else:
+                    codes = [int(c) for c in r.integers(-128, 128, 32)]
+                    ints = codes
+                    enc = _enc_q8_0
+                d_bits = d_pool[(n + b) % len(d_pool)]
+                raw += enc(codes, d_bits)
+                d = _f16_fraction(d_bits)
+                vals += [Fraction(i) * d for i in ints]
+            rows.append(np.frombuffer(raw, dtype=np.uint8))
+            dense.append(vals)
+        W = np.stack(rows)
+        X = r.standard_normal((M, K)).astype(np.float32)
+        Y, A = oracle.qmv(qtype, W, X)
+        for m in range(M):
+            for n in range(N):
+                prods = [dense[n][k] * Fraction(float(X[m, k])) for k in range(K)]
+                exact = sum(prods)
+                mag = sum(abs(p) for p in prods)
+                bound = K * 2.0 ** -53 * float(mag)
+                assert abs(Fraction(Y[m, n]) - exact) <= Fraction(bound), (K, m, n)
+                assert abs(Fraction(A[m, n]) - mag) <= Fraction(bound)
+
+
+def test_long_row_sum_within_fp64_bound_of_exactly_rounded_sum():
+    """K = 14336: the oracle's fp64 sum is within K * 2^-53 * a of math.fsum of
+    the exact products (each product of a binary16-scaled small integer and an
+    fp32 value is exact in fp64)."""
+    from block_quantized_weight_qmatmul_amd import synth
+    K = 14336
+    W = synth.make_weights("q4_0", 4, K, cfg=97)
+    X = synth.make_x(1, K, cfg=97)
+    Y, A = oracle.qmv("q4_0", W, X)
+    for n in range(4):
+        blk = W[n].reshape(-1, 18)
+        d = blk[:, 0:2].copy().view("<f2").astype(np.float64).ravel()
+        lo = (blk[:, 2:] & 0x0F).astype(np.int64) - 8
+        hi = (blk[:, 2:] >> 4).astype(np.int64) - 8
+        w = (np.concatenate([lo, hi], axis=1) * d[:, None]).ravel()
+        prods = w * X[0].astype(np.float64)
+        exact = math.fsum(prods)
+        assert abs(Y[0, n] - exact) <= K * 2.0 ** -53 * A[0, n]
+
+
+# --------------------------------------------------------------------------
+# Expert-indexed call.
+# --------------------------------------------------------------------------
+def _signature_stack(qtype, E, N, K):
+    """Expert e: every scale is binary16(e + 1), every weight value is 1 * d."""
+    bb = oracle.BLOCK_BYTES[oracle.QTYPES[qtype]]
+    W = np.empty((E, N, K // 32, bb), dtype=np.uint8)
+    for e in range(E):
+        bits = int(np.array(e + 1, dtype=np.float16).view(np.uint16))
+        W[e, :, :, 0], W[e, :, :, 1] = bits & 0xFF, bits >> 8
+        W[e, :, :, 2:] = 0x99 if qtype == "q4_0" else 0x01
+    return W.reshape(E, N, -1)
+
+
+@pytest.mark.parametrize("qtype", ["q4_0", "q8_0"])
+def test_id_routing_signature_closed_form(qtype):
+    E, N, K = 128, 8, 2816
+    W = _signature_stack(qtype, E, N, K)
+    ids = np.array([[127, 0, 5, 5], [64, 3, 127, 1], [0, 0, 0, 0]], dtype=np.uint32)  # repeats, duplicates
+    X = np.ones((3, K), dtype=np.float32)
+    Y, A = oracle.qmv_id(qtype, W, X, ids, N, K)
+    for p, e in enumerate(ids.ravel()):
+        assert np.all(Y[p] == (int(e) + 1) * K) and np.all(A[p] == (int(e) + 1) * K)
+    sc = np.linspace(0.5, 1.5, E).astype(np.float32)
+    Ys, _ = oracle.qmv_id(qtype, W, X, ids, N, K, expert_scale=sc)
+    for p, e in enumerate(ids.ravel()):
+        assert np.all(Ys[p] == float(sc[e]) * (int(e) + 1) * K)
+
+
+def test_id_input_row_is_token_and_output_row_is_token_times_topk_plus_slot():
+    E, N, K = 6, 4, 64
+    W = _signature_stack("q4_0", E, N, K)
+    ids = np.array([[1, 4], [2, 2], [5, 0]], dtype=np.uint32)
+    X = np.stack([np.full(K, t + 1, dtype=np.float32) for t in range(3)])
+    Y, _ = oracle.qmv_id("q4_0", W, X, ids, N, K)
+    for t in range(3):
+        for s in range(2):
+            assert np.all(Y[t * 2 + s] == (t + 1) * (int(ids[t, s]) + 1) * K)
+
+
+def test_id_flattened_down_call_matches_per_slot_dense_calls():
+    """The down-projection form (n_tokens = T*top_k, top_k = 1) on expert e's
+    slice equals a dense call on that slice (the dense call is pinned above)."""
+    from block_quantized_weight_qmatmul_amd import synth
+    E, N, K, P = 5, 24, 704, 7
+    W = synth.make_weights("q4_0", E * N, K, cfg=96).reshape(E, N, -1)
+    X = synth.make_x(P, K, cfg=96)
+    ids = np.array([4, 0, 2, 2, 1, 4, 3], dtype=np.uint32)
+    Y, _ = oracle.qmv_id("q4_0", W, X, ids[:, None], N, K)
+    for p in range(P):
+        yd, _ = oracle.qmv("q4_0", W[ids[p]], X[p:p + 1])
+        assert np.array_equal(Y[p], yd[0])
+
+
+def test_id_rejects_out_of_range_expert():
+    W = _signature_stack("q4_0", 4, 2, 32)
+    with pytest.raises(ValueError):
+        oracle.qmv_id("q4_0", W, np.ones((1, 32), np.float32), np.array([[4]], np.uint32), 2, 32)
+
+
+def test_dense_rejects_bad_shapes():
+    W = np.zeros((2, 18), dtype=np.uint8)
+    with pytest.raises(ValueError):
+        oracle.qmv("q4_0", W, np.ones((1, 33), np.float32), K=33)
+    with pytest.raises(ValueError):
+        oracle.qmv("q4_0", W, np.ones((1, 64), np.float32))  # row shorter than K/32 blocks
