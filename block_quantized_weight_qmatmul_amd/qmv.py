@@ -1,0 +1,137 @@
+"""Python binding of the qmv C ABI (include/qmv.h): argument marshalling only.
+
+Every computation runs in the HIP kernels of ``libqmv.so``; this module only
+turns torch tensors (device memory, streams) into the pointers and sizes the
+C functions take, and turns a negative status into an exception. There is no
+fallback: if the library is missing, importing the functions raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libqmv.so")
+
+QMV_OK, QMV_EINVAL, QMV_EALIGN, QMV_EUNSUPPORTED, QMV_EHIP = 0, -1, -2, -3, -4
+QMV_Q4_0, QMV_Q8_0 = 2, 8
+QMV_MAX_M = 16
+BLOCK_BYTES = {QMV_Q4_0: 18, QMV_Q8_0: 34}
+QTYPES = {"q4_0": QMV_Q4_0, "q8_0": QMV_Q8_0}
+
+_lib = None
+
+
+class QmvError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"qmv status {status}: {message}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqmv.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "or python -m block_quantized_weight_qmatmul_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        P, S, I = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+        for name in ("qmv_q4_0", "qmv_q8_0"):
+            f = getattr(L, name)
+            f.restype = I
+            f.argtypes = [P, S, P, S, P, S, I, I, I, P]
+        L.qmv_id.restype = I
+        L.qmv_id.argtypes = [I, P, S, S, I, P, S, P, I, I, P, S, I, I, P, P, P]
+        L.qmv_last_error.restype = ctypes.c_char_p
+        L.qmv_last_error.argtypes = []
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().qmv_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != QMV_OK:
+        raise QmvError(status, last_error())
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream)
+    return int(getattr(stream, "cuda_stream", stream))
+
+
+# ---------------------------------------------------------------------------
+# Raw calls: pointers and sizes as integers, status returned (for tests of the
+# argument checks and for callers that manage their own memory).
+# ---------------------------------------------------------------------------
+def raw_qmv(qtype: int, W: int, ldw: int, X: int, ldx: int, Y: int, ldy: int, M: int, N: int, K: int,
+            stream: int = 0) -> int:
+    f = lib().qmv_q4_0 if qtype == QMV_Q4_0 else lib().qmv_q8_0
+    return f(W, ldw, X, ldx, Y, ldy, M, N, K, stream)
+
+
+def raw_qmv_id(qtype, W, expert_stride, ldw, n_experts, X, ldx, ids, n_tokens, top_k, Y, ldy, N, K,
+               expert_scale=0, err_flag=0, stream=0) -> int:
+    return lib().qmv_id(qtype, W, expert_stride, ldw, n_experts, X, ldx, ids, n_tokens, top_k, Y, ldy, N, K,
+                        expert_scale, err_flag, stream)
+
+
+# ---------------------------------------------------------------------------
+# Tensor calls.
+# ---------------------------------------------------------------------------
+def _dense(qtype: int, W, X, Y, K: Optional[int], stream) -> None:
+    """W: uint8 [N, ldw] (row stride W.stride(0) bytes); X: fp32 [M, K] or [K];
+    Y: fp32 [M, N] or [N]."""
+    if W.dim() != 2 or W.stride(1) != 1:
+        raise ValueError("W must be a 2-D uint8 tensor with contiguous rows")
+    N = W.shape[0]
+    x2 = X if X.dim() == 2 else X.view(1, -1)
+    y2 = Y if Y.dim() == 2 else Y.view(1, -1)
+    M = x2.shape[0]
+    if K is None:
+        K = x2.shape[1]
+    if x2.stride(1) != 1 or y2.stride(1) != 1 or y2.shape[0] != M or y2.shape[1] != N:
+        raise ValueError("X [M, K] and Y [M, N] need unit inner stride and matching M, N")
+    st = raw_qmv(qtype, _ptr(W), W.stride(0), _ptr(x2), x2.stride(0), _ptr(y2), y2.stride(0), M, N, K,
+                 _stream(stream))
+    _check(st)
+
+
+def qmv_q4_0(W, X, Y, K: Optional[int] = None, stream=None) -> None:
+    """Y = deq(W) @ X per row, Q4_0 weights (see include/qmv.h)."""
+    _dense(QMV_Q4_0, W, X, Y, K, stream)
+
+
+def qmv_q8_0(W, X, Y, K: Optional[int] = None, stream=None) -> None:
+    """Y = deq(W) @ X per row, Q8_0 weights (see include/qmv.h)."""
+    _dense(QMV_Q8_0, W, X, Y, K, stream)
+
+
+def qmv_id(qtype, W, X, ids, Y, N: int, K: int, expert_scale=None, err_flag=None, stream=None) -> None:
+    """Expert-indexed product (see include/qmv.h).
+
+    W: uint8 [E, N, ldw] stacked experts (expert stride W.stride(0) bytes,
+    row stride W.stride(1)); X: fp32 [n_tokens, K]; ids: uint32 or int32
+    [n_tokens, top_k]; Y: fp32 [n_tokens * top_k, N].
+    """
+    q = QTYPES[qtype] if isinstance(qtype, str) else int(qtype)
+    if W.dim() != 3 or W.stride(2) != 1:
+        raise ValueError("W must be a 3-D uint8 tensor [E, N, ldw] with contiguous rows")
+    ids2 = ids if ids.dim() == 2 else ids.view(-1, 1)
+    n_tokens, top_k = ids2.shape
+    if not ids2.is_contiguous():
+        raise ValueError("ids must be contiguous")
+    st = raw_qmv_id(q, _ptr(W), W.stride(0), W.stride(1), W.shape[0], _ptr(X), X.stride(0), _ptr(ids2),
+                    n_tokens, top_k, _ptr(Y), Y.stride(0), N, K, _ptr(expert_scale), _ptr(err_flag),
+                    _stream(stream))
+    _check(st)

@@ -1,0 +1,141 @@
+/*
+ * qmv.h — block-quantized weight mat-vec on AMD Instinct MI355X (gfx950).
+ *
+ * y = W x for weights stored as GGML-style 32-element blocks (Q4_0, Q8_0)
+ * against fp32 activations, for 1 to 16 activation rows, plus the
+ * expert-indexed variant over a stack of per-expert weight matrices.
+ *
+ * Source of the operations: the hf2q 0.1.1 pages.
+ *  - Dense call: `dispatch_qmatmul(session, registry, device, x, &MlxQWeight,
+ *    y, m, hint)` as used for the Q/K/V, O, FFN gate/up/down and router
+ *    projections in `MlxModelWeights::encode_one_layer`
+ *    (src/inference/models/gemma4/gpu_full_attn.rs). The weight handle
+ *    `MlxQWeight { buffer, info: QuantWeightInfo { ggml_dtype, rows, cols } }`
+ *    (src/inference/models/gemma4/model.rs, `lm_head_q8` block in
+ *    `load_from_gguf`) holds `rows` = output features N and `cols` = K,
+ *    in a byte buffer of shape [rows, blocks_per_row * block_bytes].
+ *  - Expert-indexed call: `quantized_matmul_id_ggml(...)` with parameter
+ *    block `GgmlQuantizedMatmulIdParams { n_tokens, top_k, n, k, n_experts,
+ *    expert_stride, ggml_type }` (gpu_full_attn.rs, MoE blocks B11 gate_up and
+ *    B13 down); stacked weights `[n_experts, N, packed_K]` with a byte stride
+ *    per expert (model.rs, `MlxMoeWeights`).
+ *
+ * Block formats (32 weights per block):
+ *   Q4_0, 18 bytes: binary16 scale d (little-endian), then 16 bytes where
+ *         byte j holds element j in its low nibble and element j+16 in its
+ *         high nibble; w = (code - 8) * d. (The pages only name the format;
+ *         this is the GGML Q4_0 layout.)
+ *   Q8_0, 34 bytes: binary16 scale d, then 32 int8 codes; w = code * d
+ *         (the inverse of the lm_head Q8_0 encoder in `load_from_gguf`).
+ *
+ * Conventions for every entry point:
+ *  - All array arguments are DEVICE pointers, owned by the caller. The
+ *    library never allocates, frees or synchronizes; each call only enqueues
+ *    kernels on `stream` (a hipStream_t; NULL = the null stream) and returns.
+ *  - Arguments are validated on the host before any HIP call. A rejected call
+ *    launches nothing, returns a negative status and sets a thread-local
+ *    message readable with qmv_last_error().
+ *  - Y is overwritten (not accumulated into) and must not overlap W, X, the
+ *    ids or the scales.
+ *  - Results: each output element is an fp32 sum whose error against the
+ *    exact value is far below 1e-4 * sum_k |w_k x_k| + 1e-6. Runs on the same
+ *    inputs and the same device give bitwise-identical outputs (no atomics).
+ *  - Calls are reentrant; concurrent calls on different streams are safe as
+ *    long as their outputs do not overlap.
+ */
+#ifndef QMV_H
+#define QMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define QMV_OK 0
+#define QMV_EINVAL (-1)       /* bad shape, stride, pointer or overlap */
+#define QMV_EALIGN (-2)       /* misaligned pointer or stride */
+#define QMV_EUNSUPPORTED (-3) /* unsupported qtype, or M outside 0..16 */
+#define QMV_EHIP (-4)         /* the HIP runtime reported a launch error */
+
+/* Weight types (GGML type numbers). */
+#define QMV_Q4_0 2
+#define QMV_Q8_0 8
+
+#define QMV_MAX_M 16
+
+/*
+ * qmv_q4_0 — Y[m, n] = sum_{k<K} w[n, k] * X[m, k], for m < M, n < N, with
+ * w the Q4_0-decoded weights.
+ *
+ *  W          device, N rows of K/32 Q4_0 blocks; row n starts at byte
+ *             n * ldw_bytes. Must be 2-byte aligned.
+ *  ldw_bytes  row stride in bytes, >= K/32 * 18, even.
+ *  X          device fp32, M rows of K values; row m starts at X + m*ldx.
+ *             4-byte aligned.
+ *  ldx        row stride of X in elements, >= K (ignored when M <= 1).
+ *  Y          device fp32, M rows of N values; row m at Y + m*ldy.
+ *  ldy        row stride of Y in elements, >= N (ignored when M <= 1).
+ *  M          number of activation rows, 0..16 (0: nothing to do).
+ *  N          output features, >= 0 (0: nothing to do).
+ *  K          input features, >= 0 and a multiple of 32 (0: Y is zeroed).
+ *  stream     hipStream_t to enqueue on.
+ * Returns QMV_OK or a negative status (see above).
+ */
+int qmv_q4_0(const void* W, size_t ldw_bytes, const float* X, size_t ldx, float* Y, size_t ldy,
+             int M, int N, int K, void* stream);
+
+/*
+ * qmv_q8_0 — as qmv_q4_0 with Q8_0 blocks (34 bytes): ldw_bytes >= K/32*34.
+ */
+int qmv_q8_0(const void* W, size_t ldw_bytes, const float* X, size_t ldx, float* Y, size_t ldy,
+             int M, int N, int K, void* stream);
+
+/*
+ * qmv_id — expert-indexed product over a stack of weight matrices.
+ *
+ * For t < n_tokens and s < top_k, with p = t*top_k + s and e = ids[p]:
+ *   Y[p, n] = sc_e * sum_{k<K} w_e[n, k] * X[t, k],   n < N,
+ * where w_e is the N x K matrix of type `qtype` starting at byte
+ * e * expert_stride_bytes of W (rows ldw_bytes apart), and sc_e =
+ * expert_scale[e] when expert_scale is non-NULL, else 1.
+ *
+ * The gate_up form of the pages is (n_tokens = T, top_k = k) with one X row
+ * per token; the down form flattens the slots: (n_tokens = T*k, top_k = 1)
+ * with one X row per slot.
+ *
+ *  qtype                QMV_Q4_0 or QMV_Q8_0.
+ *  W                    device, stacked weights, 2-byte aligned.
+ *  expert_stride_bytes  >= N * ldw_bytes, even.
+ *  ldw_bytes            row stride within an expert, >= K/32 * block bytes, even.
+ *  n_experts            > 0.
+ *  X, ldx               device fp32 [n_tokens, K] with row stride ldx >= K.
+ *  ids                  device uint32 [n_tokens * top_k].
+ *  n_tokens             >= 0 (0: nothing to do).
+ *  top_k                > 0.
+ *  Y, ldy               device fp32 [n_tokens * top_k, N], row stride ldy >= N.
+ *  N, K                 as for qmv_q4_0.
+ *  expert_scale         device fp32 [n_experts] or NULL.
+ *  err_flag             device int or NULL. An id >= n_experts is invalid
+ *                       input: its output row is filled with NaN and, when
+ *                       err_flag is given, 1 is stored to *err_flag (the
+ *                       library never clears it; the caller zeroes it).
+ * Each selected expert's weights are read from memory once per call, however
+ * many (token, slot) pairs select it.
+ * Returns QMV_OK or a negative status.
+ */
+int qmv_id(int qtype, const void* W, size_t expert_stride_bytes, size_t ldw_bytes, int n_experts,
+           const float* X, size_t ldx, const uint32_t* ids, int n_tokens, int top_k,
+           float* Y, size_t ldy, int N, int K, const float* expert_scale, int* err_flag,
+           void* stream);
+
+/* Message for the last non-zero status returned on the calling thread. */
+const char* qmv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMV_H */

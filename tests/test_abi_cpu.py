@@ -1,0 +1,107 @@
+"""The C-ABI library loads, exports what include/qmv.h declares, and rejects
+bad arguments on the host before any HIP call (runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_quantized_weight_qmatmul_amd import qmv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built():
+    if not os.path.exists(qmv.LIB_PATH):
+        from block_quantized_weight_qmatmul_amd import build
+        build.build()
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "qmv.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(qmv_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert {"qmv_q4_0", "qmv_q8_0", "qmv_id", "qmv_last_error"} <= set(names)
+    L = ctypes.CDLL(qmv.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+# Fake, never dereferenced device addresses: every case below is rejected on
+# the host before anything touches them.
+W, X, Y = 0x10000000, 0x20000000, 0x30000000
+Q4, Q8 = qmv.QMV_Q4_0, qmv.QMV_Q8_0
+
+
+@pytest.mark.parametrize("args,status,msg", [
+    ((Q4, W, 18 * 4, X, 128, Y, 16, 17, 16, 128), qmv.QMV_EUNSUPPORTED, "M=17"),
+    ((Q4, W, 18 * 4, X, 128, Y, 16, -1, 16, 128), qmv.QMV_EUNSUPPORTED, "M=-1"),
+    ((Q4, W, 18 * 4, X, 128, Y, 16, 1, -2, 128), qmv.QMV_EINVAL, "N=-2"),
+    ((Q4, W, 18 * 4, X, 128, Y, 16, 1, 16, 100), qmv.QMV_EINVAL, "K=100"),
+    ((Q4, 0, 18 * 4, X, 128, Y, 16, 1, 16, 128), qmv.QMV_EINVAL, "W is NULL"),
+    ((Q4, W, 18 * 4, 0, 128, Y, 16, 1, 16, 128), qmv.QMV_EINVAL, "X is NULL"),
+    ((Q4, W, 18 * 4, X, 128, 0, 16, 1, 16, 128), qmv.QMV_EINVAL, "Y is NULL"),
+    ((Q4, W, 18 * 4 - 2, X, 128, Y, 16, 1, 16, 128), qmv.QMV_EINVAL, "ldw_bytes"),
+    ((Q8, W, 18 * 4, X, 128, Y, 16, 1, 16, 128), qmv.QMV_EINVAL, "ldw_bytes"),
+    ((Q4, W, 18 * 4 + 1, X, 128, Y, 16, 1, 16, 128), qmv.QMV_EALIGN, "2-byte"),
+    ((Q4, W + 1, 18 * 4, X, 128, Y, 16, 1, 16, 128), qmv.QMV_EALIGN, "2-byte"),
+    ((Q4, W, 18 * 4, X + 2, 128, Y, 16, 1, 16, 128), qmv.QMV_EALIGN, "4-byte"),
+    ((Q4, W, 18 * 4, X, 127, Y, 16, 2, 16, 128), qmv.QMV_EINVAL, "ldx"),
+    ((Q4, W, 18 * 4, X, 128, Y, 15, 2, 16, 128), qmv.QMV_EINVAL, "ldy"),
+    ((Q4, W, 18 * 4, X, 128, W + 8, 16, 1, 16, 128), qmv.QMV_EINVAL, "overlaps"),
+    ((Q4, W, 18 * 4, X, 128, X + 64, 16, 1, 16, 128), qmv.QMV_EINVAL, "overlaps"),
+])
+def test_dense_argument_checks(args, status, msg):
+    q, *rest = args
+    assert qmv.raw_qmv(q, *rest) == status
+    assert msg in qmv.last_error()
+
+
+def test_empty_calls_are_no_ops_without_touching_memory():
+    # M = 0 or N = 0: nothing to do, pointers may be NULL, no HIP call made.
+    assert qmv.raw_qmv(Q4, 0, 0, 0, 0, 0, 0, 0, 16, 128) == qmv.QMV_OK
+    assert qmv.raw_qmv(Q8, 0, 0, 0, 0, 0, 0, 1, 0, 128) == qmv.QMV_OK
+    assert qmv.raw_qmv_id(Q4, 0, 0, 0, 4, 0, 0, 0, 0, 2, 0, 0, 16, 32) == qmv.QMV_OK
+
+
+def _id(**kw):
+    a = dict(qtype=Q4, W=W, es=18 * 16, ldw=18, E=4, X=X, ldx=32, ids=0x40000000, nt=1, k=2, Y=Y, ldy=16,
+             N=16, K=32, sc=0, err=0)
+    a.update(kw)
+    return qmv.raw_qmv_id(a["qtype"], a["W"], a["es"], a["ldw"], a["E"], a["X"], a["ldx"], a["ids"], a["nt"],
+                          a["k"], a["Y"], a["ldy"], a["N"], a["K"], a["sc"], a["err"])
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(qtype=3), qmv.QMV_EUNSUPPORTED, "qtype"),
+    (dict(E=0), qmv.QMV_EINVAL, "n_experts"),
+    (dict(k=0), qmv.QMV_EINVAL, "top_k"),
+    (dict(k=4096), qmv.QMV_EUNSUPPORTED, "top_k"),
+    (dict(nt=-1), qmv.QMV_EINVAL, "n_tokens"),
+    (dict(K=48), qmv.QMV_EINVAL, "K=48"),
+    (dict(ldw=16), qmv.QMV_EINVAL, "ldw_bytes"),
+    (dict(es=18 * 15), qmv.QMV_EINVAL, "expert_stride"),
+    (dict(ldx=31), qmv.QMV_EINVAL, "ldx"),
+    (dict(ldy=15), qmv.QMV_EINVAL, "ldy"),
+    (dict(ids=0), qmv.QMV_EINVAL, "NULL"),
+    (dict(es=18 * 16 + 1), qmv.QMV_EALIGN, "2-byte"),
+    (dict(ids=0x40000002), qmv.QMV_EALIGN, "4-byte"),
+    (dict(err=0x50000001), qmv.QMV_EALIGN, "4-byte"),
+    (dict(Y=W + 18 * 20), qmv.QMV_EINVAL, "overlaps"),
+    (dict(Y=0x40000000 - 4), qmv.QMV_EINVAL, "overlaps"),
+])
+def test_id_argument_checks(kw, status, msg):
+    assert _id(**kw) == status
+    assert msg in qmv.last_error()
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(qmv, "_lib", None)
+    monkeypatch.setattr(qmv, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        qmv.lib()

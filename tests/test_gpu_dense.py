@@ -1,0 +1,191 @@
+"""GPU parity of qmv_q4_0 / qmv_q8_0 against the CPU oracle (needs an MI355X).
+
+Every comparison is element by element at |gpu - oracle| <= 1e-4 * a + 1e-6
+(a = sum_k |w_k x_k| from the oracle), or bit-exact where the exact result is
+representable (one-hot and identity activations, all-zero weights).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from block_quantized_weight_qmatmul_amd import qmv, synth
+from golden_io import read_blocks
+from helpers import assert_within_tol
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+FN = {"q4_0": qmv.qmv_q4_0, "q8_0": qmv.qmv_q8_0}
+
+
+def run(qtype, W, X, K=None, ldy=None, y_fill=np.nan):
+    """Run the GPU kernel on host arrays W [N, ldw] uint8 and X [M, K] fp32."""
+    Wd = torch.from_numpy(np.ascontiguousarray(W)).to(DEV)
+    Xd = torch.from_numpy(np.ascontiguousarray(X)).to(DEV)
+    M, N = X.shape[0], W.shape[0]
+    Yfull = torch.full((M, ldy or N), y_fill, dtype=torch.float32, device=DEV)
+    Y = Yfull[:, :N]
+    FN[qtype](Wd, Xd, Y, K=K)
+    torch.cuda.synchronize()
+    return Yfull.cpu().numpy()[:, :N], Yfull.cpu().numpy()
+
+
+def check(qtype, W, X, what, rows=None):
+    y, _ = run(qtype, W, X)
+    if rows is None:
+        yo, a = oracle.qmv(qtype, W, X)
+        return assert_within_tol(y, yo, a, what)
+    yo, a = oracle.qmv(qtype, W[rows], X)
+    return assert_within_tol(y[:, rows], yo, a, what)
+
+
+# --------------------------------------------------------------------------
+# The workloads at full size.
+# --------------------------------------------------------------------------
+def _sample_rows(N, n, seed):
+    r = np.random.default_rng(seed)
+    return np.unique(np.r_[0, N - 1, r.integers(0, N, n)])
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2])
+def test_m1_workloads_full_size(cfg):
+    for part, p in enumerate(synth.CONFIGS[cfg]["problems"]):
+        W, X = synth.dense_inputs(cfg, p, part)
+        print(f"cfg{cfg} {p.name} {p.qtype} M={p.M} N={p.N} K={p.K}", flush=True)
+        r = check(p.qtype, W, X, f"cfg{cfg}/{p.name}")
+        print(f"  max ratio {r:.3g}")
+
+
+def test_m16_workload_sampled_rows():
+    cfg = 3
+    for part, p in enumerate(synth.CONFIGS[cfg]["problems"]):
+        W, X = synth.dense_inputs(cfg, p, part)
+        print(f"cfg3 {p.name} M={p.M} N={p.N} K={p.K}", flush=True)
+        r = check(p.qtype, W, X, f"cfg3/{p.name}", rows=_sample_rows(p.N, 1500, part))
+        print(f"  max ratio {r:.3g}")
+
+
+# --------------------------------------------------------------------------
+# Exact cases.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("fixture,qtype", [("q4_0_blocks.txt", "q4_0"), ("q8_0_blocks.txt", "q8_0")])
+@pytest.mark.parametrize("nblk", [1, 2, 64])
+def test_one_hot_is_bit_exact(fixture, qtype, nblk):
+    """Rows of hand-built blocks; x = e_k picks w[n, k] exactly (K = 32*nblk,
+    so both the generic (K=32) and the fast (K % 64 == 0) kernels are hit)."""
+    blocks = read_blocks(fixture)
+    rows = [np.concatenate([raw] * nblk) for _, raw, _ in blocks]
+    want = np.stack([np.tile(v, nblk) for _, _, v in blocks])
+    W = np.stack(rows)
+    K = 32 * nblk
+    for k in sorted({0, 1, 15, 16, 17, 31, K - 1, K // 2 + 3}):
+        X = np.zeros((1, K), dtype=np.float32)
+        X[0, k] = 1.0
+        y, _ = run(qtype, W, X)
+        assert np.array_equal(y[0], want[:, k].astype(np.float32)), (k, y[0], want[:, k])
+
+
+@pytest.mark.parametrize("qtype", ["q4_0", "q8_0"])
+def test_identity_rows_m16_bit_exact(qtype):
+    N, K = 40, 256
+    W = synth.make_weights(qtype, N, K, cfg=90)
+    M, k0 = 16, 37
+    X = np.zeros((M, K), dtype=np.float32)
+    for m in range(M):
+        X[m, k0 + m] = 1.0
+    y, _ = run(qtype, W, X)
+    deq = np.stack([oracle.dequant_row(qtype, W[n], K) for n in range(N)])
+    for m in range(M):
+        assert np.array_equal(y[m], deq[:, k0 + m].astype(np.float32))
+
+
+@pytest.mark.parametrize("K", [2048, 4096, 96])
+def test_all_codes_eight_give_exact_zero(K):
+    W = synth.make_weights("q4_0", 300, K, cfg=91)
+    W.reshape(300, -1, 18)[:, :, 2:] = 0x88
+    X = synth.make_x(1, K, cfg=91) * np.float32(1e4)
+    y, _ = run("q4_0", W, X)
+    assert np.all(y == 0)
+
+
+@pytest.mark.parametrize("qtype", ["q4_0", "q8_0"])
+def test_deterministic_bitwise(qtype):
+    W, X = synth.dense_inputs(1, synth.Dense("gate", qtype, 1, 14336, 4096), part=4)
+    y1, _ = run(qtype, W, X)
+    y2, _ = run(qtype, W, X)
+    assert np.array_equal(y1, y2)
+
+
+# --------------------------------------------------------------------------
+# Ragged, strided, misaligned and boundary shapes (fast and generic kernels).
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("qtype", ["q4_0", "q8_0"])
+@pytest.mark.parametrize("N,K", [(1, 64), (3, 32), (17, 96), (1000, 2080), (4097, 128), (257, 704),
+                                 (63, 2816), (129, 15360), (65, 16384), (5, 30720)])
+def test_ragged_shapes(qtype, N, K):
+    W = synth.make_weights(qtype, N, K, cfg=92, part=N)
+    X = synth.make_x(1, K, cfg=92, part=K)
+    check(qtype, W, X, f"{qtype} N={N} K={K}")
+
+
+@pytest.mark.parametrize("qtype", ["q4_0", "q8_0"])
+@pytest.mark.parametrize("pad", [2, 4, 64])
+def test_padded_row_stride(qtype, pad):
+    N, K = 515, 1024
+    ldw = synth.row_bytes(qtype, K) + pad
+    W = synth.make_weights(qtype, N, K, cfg=93, ldw=ldw)
+    X = synth.make_x(1, K, cfg=93)
+    check(qtype, W, X, f"{qtype} pad={pad}")
+
+
+@pytest.mark.parametrize("qtype", ["q4_0", "q8_0"])
+def test_weights_at_2_byte_offset(qtype):
+    N, K = 300, 512
+    W = synth.make_weights(qtype, N, K, cfg=94)
+    X = synth.make_x(1, K, cfg=94)
+    buf = torch.zeros(W.size + 64, dtype=torch.uint8, device=DEV)
+    Wd = buf[2:2 + W.size].view(N, -1)
+    Wd.copy_(torch.from_numpy(W))
+    Y = torch.empty((1, N), dtype=torch.float32, device=DEV)
+    FN[qtype](Wd, torch.from_numpy(X).to(DEV), Y)
+    torch.cuda.synchronize()
+    yo, a = oracle.qmv(qtype, W, X)
+    assert_within_tol(Y.cpu().numpy(), yo, a, "offset 2")
+
+
+@pytest.mark.parametrize("qtype", ["q4_0", "q8_0"])
+@pytest.mark.parametrize("M", [2, 3, 7, 16])
+def test_multi_row_x_with_strides(qtype, M):
+    N, K = 777, 1536
+    W = synth.make_weights(qtype, N, K, cfg=95, part=M)
+    Xfull = synth.make_x(M, K + 40, cfg=95, part=M)
+    Xd = torch.from_numpy(Xfull).to(DEV)[:, 8:8 + K]
+    Yfull = torch.full((M, N + 9), np.nan, dtype=torch.float32, device=DEV)
+    FN[qtype](torch.from_numpy(W).to(DEV), Xd, Yfull[:, :N])
+    torch.cuda.synchronize()
+    y = Yfull.cpu().numpy()
+    yo, a = oracle.qmv(qtype, W, np.ascontiguousarray(Xfull[:, 8:8 + K]))
+    assert_within_tol(y[:, :N], yo, a, f"M={M}")
+    assert np.all(np.isnan(y[:, N:]))  # the row padding of Y is left alone
+
+
+def test_k_zero_writes_zeros_and_empty_calls_do_nothing():
+    Y = torch.full((3, 10), 7.0, dtype=torch.float32, device=DEV)
+    W = torch.zeros((10, 2), dtype=torch.uint8, device=DEV)
+    X = torch.zeros((3, 4), dtype=torch.float32, device=DEV)
+    qmv.qmv_q4_0(W, X, Y, K=0)
+    torch.cuda.synchronize()
+    assert torch.all(Y == 0)
+    Y.fill_(7.0)
+    qmv.qmv_q8_0(W[:0], X, Y[:, :0], K=0)  # N = 0
+    torch.cuda.synchronize()
+    assert torch.all(Y == 7.0)
+
+
+def test_large_dynamic_range_activations():
+    N, K = 512, 4096
+    W = synth.make_weights("q4_0", N, K, cfg=89)
+    r = np.random.default_rng(89)
+    X = (synth.make_x(1, K, cfg=89) * np.exp(r.uniform(-40, 40, K))).astype(np.float32)
+    check("q4_0", W, X, "dynamic range")
