@@ -1,0 +1,356 @@
+#!/usr/bin/env python3
+"""Benchmark: Q4_0 block-quantized mat-vec throughput on MI355X.
+
+Workload (one "step"): the dense decode-layer projection set at M = 1 in
+Q4_0 with hidden size 4096 -- Q 4096->4096, K 4096->1024, V 4096->1024,
+O 4096->4096, FFN gate and up 4096->14336, down 14336->4096 -- on seeded
+synthetic weights (scales ~U[0.001, 0.02] as binary16, codes ~U{0..15}) and
+N(0, 1) activations. A step runs the projections as a decode layer can: Q, K
+and V together (one input), then O, then gate and up together (one input),
+then down: four batched launches (qmv_batch).
+
+The weights of R distinct copies of the layer set are resident in HBM
+(10 copies = 1.23 GB, several times the 256 MB Infinity Cache) and steps
+rotate through them, so every step streams its weights from HBM.
+
+Output: one JSON line with the effective weight bandwidth (algorithmic
+weight bytes / wall time per step), the roofline of the qmv kernel (bytes of
+its launches / their summed duration, from HIP events around each launch)
+and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+METRIC = "effective weight GB/s and % of HBM peak, Q4_0 qmatmul at M=1 and M=16"
+KERNEL_SRC = os.path.join(ROOT, "block_quantized_weight_qmatmul_amd", "csrc", "qmv.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qmv_decode_layer_h4096.json")
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def build_layer_sets(R, dev):
+    """R copies of the layer set on the device: list of dicts name -> (W, x, y)."""
+    import torch
+
+    from block_quantized_weight_qmatmul_amd import synth
+    probs = synth.CONFIGS[1]["problems"]
+    sets = []
+    for r in range(R):
+        xin = {  # one input per dependency group
+            "qkv": synth.make_x(1, 4096, cfg=1, copy=r, part=0),
+            "o": synth.make_x(1, 4096, cfg=1, copy=r, part=3),
+            "ffn": synth.make_x(1, 4096, cfg=1, copy=r, part=4),
+            "down": synth.make_x(1, 14336, cfg=1, copy=r, part=6),
+        }
+        xdev = {k: torch.from_numpy(v[0]).to(dev) for k, v in xin.items()}
+        group = {"q": "qkv", "k": "qkv", "v": "qkv", "o": "o", "gate": "ffn", "up": "ffn", "down": "down"}
+        s = {}
+        for part, p in enumerate(probs):
+            W = torch.from_numpy(synth.make_weights("q4_0", p.N, p.K, cfg=1, copy=r, part=part)).to(dev)
+            s[p.name] = (W, xdev[group[p.name]], torch.empty(p.N, dtype=torch.float32, device=dev))
+        sets.append(s)
+    return sets
+
+
+GROUPS = [("q", "k", "v"), ("o",), ("gate", "up"), ("down",)]
+
+
+def step_bytes():
+    from block_quantized_weight_qmatmul_amd import synth
+    return sum(p.weight_bytes for p in synth.CONFIGS[1]["problems"])
+
+
+def time_steps(fn, sets, steps, warmup):
+    """Wall time of `steps` steps (each fn(set)) after `warmup` untimed ones."""
+    import torch
+    R = len(sets)
+    for i in range(warmup):
+        fn(sets[i % R])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        fn(sets[i % R])
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1e3
+
+
+def launch_durations(sets, steps):
+    """Per-launch durations (s) of the grouped launches, from HIP events on
+    the launch stream around each launch, over `steps` steps."""
+    import torch
+
+    from block_quantized_weight_qmatmul_amd import qmv
+    R = len(sets)
+    evs = []
+    for i in range(steps):
+        s = sets[i % R]
+        for g in GROUPS:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            qmv.qmv_batch("q4_0", [s[n] for n in g])
+            b.record()
+            evs.append((g, a, b))
+    torch.cuda.synchronize()
+    return [(g, a.elapsed_time(b) / 1e3) for g, a, b in evs]
+
+
+def m16_throughput(dev, reps=20):
+    """Config 3 (Q4_0, M = 16, K = 5120, N in {5120, 1024, 27648}): GB/s over
+    rotated copies."""
+    import torch
+
+    from block_quantized_weight_qmatmul_amd import qmv, synth
+    probs = synth.CONFIGS[3]["problems"]
+    R = 4
+    data = []
+    for r in range(R):
+        for part, p in enumerate(probs):
+            W = torch.from_numpy(synth.make_weights("q4_0", p.N, p.K, cfg=3, copy=r, part=part)).to(dev)
+            X = torch.from_numpy(synth.make_x(p.M, p.K, cfg=3, copy=r, part=part)).to(dev)
+            data.append((W, X, torch.empty((p.M, p.N), device=dev)))
+    nbytes = sum(p.weight_bytes for p in probs)
+
+    def step(r):
+        for W, X, Y in data[r * len(probs):(r + 1) * len(probs)]:
+            qmv.qmv_q4_0(W, X, Y)
+    for r in range(R):
+        step(r)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        step(i % R)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3 / reps
+    return {"workload": "q4_0_m16_k5120_n5120_1024_27648", "weight_bytes": nbytes, "us_per_set": round(t * 1e6, 2),
+            "GBps": round(nbytes / t / 1e9, 1), "pct_hbm_peak": round(100 * nbytes / t / 1e9 / HBM_PEAK_GBS, 2)}
+
+
+def cpu_baseline(target_s: float):
+    """The CPU oracle (fp64, OpenMP over rows) timed on a bounded sample of
+    the layer set: the first rows of every projection, sized to take about
+    target_s seconds. Returns (GB/s of weight bytes, threads, description)."""
+    import numpy as np
+
+    import oracle
+    from block_quantized_weight_qmatmul_amd import synth
+    probs = synth.CONFIGS[1]["problems"]
+    full = {}
+    for part, p in enumerate(probs):
+        rows = max(16, p.N // 16)
+        W = synth.make_weights("q4_0", rows, p.K, cfg=1, part=part)
+        X = synth.make_x(1, p.K, cfg=1, part=part)
+        full[p.name] = (W, X)
+
+    def run(frac):
+        nbytes, t0 = 0, time.perf_counter()
+        for p in probs:
+            W, X = full[p.name]
+            rows = max(1, int(W.shape[0] * frac))
+            oracle.qmv("q4_0", W[:rows], X)
+            nbytes += rows * W.shape[1]
+        return nbytes, time.perf_counter() - t0
+    nb, t = run(1 / 16)  # calibration
+    frac = min(1.0, (1 / 16) * target_s / max(t, 1e-3))
+    nb, t = run(frac)
+    rows_frac = frac / 16
+    desc = (f"first {rows_frac * 100:.2f}% of the rows of each of the 7 projections of the layer set "
+            f"({nb / 1e6:.1f} MB of Q4_0 weights), one pass")
+    return nb / t / 1e9, oracle.max_threads(), desc
+
+
+def read_traffic(launch_bytes):
+    """HBM traffic of the qmv kernel from committed rocprofv3 --pmc summaries,
+    when they were taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def summarize(stats_dir, fetch_dir, write_dir, cmd_note):
+    """Turn rocprofv3 CSV output (kernel stats, FETCH_SIZE pass, WRITE_SIZE
+    pass of `bench.py --probe-copy-mb`) into the committed summary under
+    profiles/: the qmv kernel's average duration and its HBM traffic per
+    launch, scaled by what the counters read for a plain copy of known size."""
+    import csv
+    import glob
+    import statistics
+
+    def rows(d, pattern):
+        fs = glob.glob(os.path.join(d, "**", pattern), recursive=True)
+        return [r for f in fs for r in csv.DictReader(open(f))]
+
+    out = []
+    stats = rows(stats_dir, "*kernel_stats.csv")
+    for r in stats:
+        if "k_m1b" in r["Name"] or "copy" in r["Name"].lower() or "k_generic" in r["Name"]:
+            out.append(f"{r['Name'][:90]:90s} calls={r['Calls']:>6s} avg_ns={float(r['AverageNs']):10.1f} "
+                       f"min_ns={float(r['MinNs']):10.1f} max_ns={float(r['MaxNs']):10.1f}")
+
+    def counter(d, name):
+        per = {"qmv": [], "copy": []}
+        for r in rows(d, "*counter_collection.csv"):
+            if r["Counter_Name"] != name:
+                continue
+            k = r["Kernel_Name"]
+            if "k_m1b" in k:
+                per["qmv"].append(float(r["Counter_Value"]))
+            elif "MulFunctor" in k or "copyBuffer" in k:
+                per["copy"].append(float(r["Counter_Value"]))
+        # the calibration copies are the 5 largest of those dispatches
+        per["copy"] = sorted(per["copy"])[-5:]
+        return per
+    fetch, write = counter(fetch_dir, "FETCH_SIZE"), counter(write_dir, "WRITE_SIZE")
+    copy_bytes = 256 * 2**20
+    res = {"kernel_source_sha256_16": kernel_hash()}
+    if fetch["qmv"] and fetch["copy"] and write["qmv"] and write["copy"]:
+        f_scale = copy_bytes / (1024 * statistics.median(fetch["copy"]))
+        w_scale = copy_bytes / (1024 * statistics.median(write["copy"]))
+        rd = statistics.mean(fetch["qmv"]) * 1024 * f_scale
+        wr = statistics.mean(write["qmv"]) * 1024 * w_scale
+        res.update({"bytes_per_launch": round(rd + wr), "read_bytes_per_launch": round(rd),
+                    "write_bytes_per_launch": round(wr), "fetch_scale": round(f_scale, 4),
+                    "write_scale": round(w_scale, 4), "algorithmic_bytes_per_launch": round(step_bytes() / len(GROUPS)),
+                    "qmv_dispatches": len(fetch["qmv"])})
+        out.append(f"FETCH_SIZE: qmv mean {statistics.mean(fetch['qmv']):.1f} KiB/dispatch over "
+                   f"{len(fetch['qmv'])} dispatches; 256 MiB copy median {statistics.median(fetch['copy']):.1f} KiB "
+                   f"-> scale {f_scale:.4f}")
+        out.append(f"WRITE_SIZE: qmv mean {statistics.mean(write['qmv']):.1f} KiB/dispatch; copy median "
+                   f"{statistics.median(write['copy']):.1f} KiB -> scale {w_scale:.4f}")
+        out.append(f"traffic per launch: read {rd:.0f} B + write {wr:.0f} B = {rd + wr:.0f} B vs algorithmic "
+                   f"{step_bytes() / len(GROUPS):.0f} B (weights only)")
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(res, f, indent=1)
+    text = "\n".join([f"# qmv decode-layer set (Q4_0, M=1, hidden 4096), kernel source {kernel_hash()}",
+                      f"# command: {cmd_note}", *out]) + "\n"
+    with open(os.path.join(ROOT, "profiles", "k_m1b_decode_layer_h4096.txt"), "w") as f:
+        f.write(text)
+    print(text)
+
+
+def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize":
+        summarize(sys.argv[2], sys.argv[3], sys.argv[4], " ".join(sys.argv[5:]))
+        return
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=10, help="rotated copies of the layer set")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample size (0 = skip)")
+    ap.add_argument("--no-extra", action="store_true", help="skip the M=16 and launch-grouping extras")
+    ap.add_argument("--probe-copy-mb", type=int, default=0,
+                    help="after the steps, copy a buffer of this many MiB 5 times (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); the multi-GPU "
+              "sharding of the path is described, not implemented.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from block_quantized_weight_qmatmul_amd import qmv
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    qmv.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    sets = build_layer_sets(args.copies, dev)
+    nbytes = step_bytes()
+
+    def grouped(s):
+        for g in GROUPS:
+            qmv.qmv_batch("q4_0", [s[n] for n in g])
+
+    t = time_steps(grouped, sets, args.steps, args.warmup)
+    ms_per_step = t / args.steps * 1e3
+    value = nbytes * args.steps / t / 1e9
+
+    durs = launch_durations(sets, max(20, min(args.steps, 200)))
+    kern_bytes = {("q", "k", "v"): 9437184 + 2 * 2359296, ("o",): 9437184, ("gate", "up"): 2 * 33030144,
+                  ("down",): 33030144}
+    tot_b = sum(kern_bytes[g] for g, _ in durs)
+    tot_t = sum(d for _, d in durs)
+    achieved = tot_b / tot_t / 1e9
+    per_launch = tot_b / len(durs)
+    traffic = read_traffic(per_launch)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "k_m1b (qmv_batch, M=1)", "launches_per_step": len(GROUPS),
+                "avg_launch_us": round(tot_t / len(durs) * 1e6, 3),
+                "algorithmic_bytes_per_launch": round(per_launch)}
+
+    if args.probe_copy_mb:
+        src = torch.empty(args.probe_copy_mb * 2**20 // 4, dtype=torch.float32, device=dev).uniform_()
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.mul(src, 1.0, out=dst)  # a plain streaming copy: reads and writes probe_copy_mb MiB
+        torch.cuda.synchronize()
+        del src, dst
+
+    extra = {}
+    if not args.no_extra:
+        t1 = time_steps(lambda s: qmv.qmv_batch("q4_0", [s[n] for n in ("q", "k", "v", "o", "gate", "up", "down")]),
+                        sets, args.steps, args.warmup)
+        t7 = time_steps(lambda s: [qmv.qmv_q4_0(s[n][0], s[n][1], s[n][2]) for n in
+                                   ("q", "k", "v", "o", "gate", "up", "down")], sets, args.steps, args.warmup)
+        extra["layer_set_one_launch_GBps"] = round(nbytes * args.steps / t1 / 1e9, 1)
+        extra["layer_set_seven_launches_GBps"] = round(nbytes * args.steps / t7 / 1e9, 1)
+        extra["m16"] = m16_throughput(dev)
+    del sets
+    torch.cuda.empty_cache()
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        gbs, cores, desc = cpu_baseline(args.cpu_seconds)
+        cpu = {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle", "sample": desc}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "q4_0_m1_decode_layer_h4096", "M": 1, "hidden": 4096,
+                   "projections": "q,k,v 4096->4096,1024,1024; o 4096->4096; gate,up 4096->14336; down 14336->4096",
+                   "launches_per_step": "4 (qkv | o | gate+up | down)", "weight_bytes_per_step": nbytes,
+                   "rotated_copies": args.copies, "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

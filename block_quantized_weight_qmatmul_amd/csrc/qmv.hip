@@ -189,14 +189,18 @@ __device__ __forceinline__ void load_pair(const uint8_t* p, uint32_t* r) {
     const u32x4* v = reinterpret_cast<const u32x4*>(p);
 #pragma unroll
     for (int i = 0; i < DW / 4; ++i) {
+#ifdef QMV_LOAD_NT
         u32x4 t = __builtin_nontemporal_load(v + i);
+#else
+        u32x4 t = v[i];
+#endif
         r[4 * i + 0] = t.x;
         r[4 * i + 1] = t.y;
         r[4 * i + 2] = t.z;
         r[4 * i + 3] = t.w;
     }
     if constexpr (DW % 4) {
-        r[DW - 1] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p) + (DW - 1));
+        r[DW - 1] = reinterpret_cast<const uint32_t*>(p)[DW - 1];
     }
 }
 
@@ -210,62 +214,558 @@ __device__ __forceinline__ void stage_x(float* xs, const float* __restrict__ x, 
     for (int k = threadIdx.x; k < K; k += blockDim.x) xs[(k >> 6) * XS_PAIR + (k & 63)] = x[k];
 }
 
+// v + (v of another lane chosen by a DPP control); lanes outside row_mask
+// add 0.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_add(float v) {
+    const int t = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, true);
+    return v + __builtin_bit_cast(float, t);
+}
+
+// Sum of v over aligned groups of LPR lanes, with DPP lane moves only (no
+// LDS traffic). The full sum is valid in the last lane of each group
+// (lane % LPR == LPR - 1); other lanes hold partial sums.
 template <int LPR>
 __device__ __forceinline__ float lane_group_sum(float v) {
-#pragma unroll
-    for (int off = LPR / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, LPR);
+    if constexpr (LPR >= 2) v = dpp_add<0xB1>(v);   // quad_perm [1,0,3,2]
+    if constexpr (LPR >= 4) v = dpp_add<0x4E>(v);   // quad_perm [2,3,0,1]
+    if constexpr (LPR >= 8) v = dpp_add<0x141>(v);  // row_half_mirror
+    if constexpr (LPR >= 16) v = dpp_add<0x140>(v); // row_mirror
+    if constexpr (LPR >= 32) v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    if constexpr (LPR >= 64) v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
     return v;
 }
 
-// Rows [row0, row0 + RPT) of one M = 1 product, for a lane at position j of
-// its LPR-lane group. Weights at W (row stride ldw), activations in xs (LDS).
-// Returns the lane's partial sums; the caller reduces over the lane group.
-template <int QT, int LPR, int RPT>
-__device__ __forceinline__ void m1_rows(const uint8_t* __restrict__ W, size_t ldw, const float* xs, int P,
-                                        long row0, int N, int j, float* tot) {
+// Streams the rows of one M = 1 product through a workgroup: tiles of
+// ROWS = (64/LPR) * RPT * WAVES consecutive rows, tiles first_tile,
+// first_tile + tile_stride, ... Within a tile, lane j of a row's LPR-lane
+// group takes pairs j, j + LPR, ... of that row; each step is one pair of
+// RPT rows, and the loads of the next step are issued before the current one
+// is decoded (one step of register prefetch). The activation row x is staged
+// into LDS after the first loads are in flight. Each row's sum is reduced over
+// its lane group and written to y[row] * out_scale.
+template <int QT, int LPR, int RPT, int WAVES>
+__device__ __forceinline__ void m1_stream(const uint8_t* __restrict__ W, size_t ldw, const float* __restrict__ x,
+                                          float* __restrict__ y, int N, int K, long first_tile, long tile_stride,
+                                          float out_scale, float* xs) {
     using T = PairTraits<QT>;
-    constexpr int PB = T::DW * 4;
-    const uint8_t* wp[RPT];
+    constexpr int DW = T::DW, PB = DW * 4;
+    constexpr int GROUPS = 64 / LPR;
+    constexpr int ROWS = GROUPS * RPT * WAVES;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane / LPR, j = lane % LPR;
+    const int P = K >> 6;
+    const int IPT = (P + LPR - 1) / LPR;  // steps per tile
+    const long ntiles = ((long)N + ROWS - 1) / ROWS;
+    const long lrow = (long)(wave * GROUPS + g) * RPT;  // this lane's first row within a tile
+
+    long tile = first_tile;
+    if (tile >= ntiles) return;  // uniform over the workgroup
+    int it = 0;
+    uint32_t nxt[RPT][DW];
+    auto issue = [&](long tl, int i) {
+        const long row0 = tl * ROWS + lrow;
+        int p = j + i * LPR;
+        p = p < P ? p : P - 1;
 #pragma unroll
-    for (int r = 0; r < RPT; ++r) {
-        long rr = row0 + r < N ? row0 + r : N - 1;
-        wp[r] = W + rr * ldw;
-        tot[r] = 0.f;
-    }
-    for (int p = j; p < P; p += LPR) {
-        uint32_t buf[RPT][T::DW];
+        for (int r = 0; r < RPT; ++r) {
+            const long rr = row0 + r < N ? row0 + r : N - 1;
+            load_pair<DW>(W + rr * ldw + (size_t)p * PB, nxt[r]);
+        }
+    };
+    issue(tile, 0);
+    stage_x(xs, x, K);
+    __syncthreads();
+    float tot[RPT];
 #pragma unroll
-        for (int r = 0; r < RPT; ++r) load_pair<T::DW>(wp[r] + (size_t)p * PB, buf[r]);
-        const float4* xv = reinterpret_cast<const float4*>(xs + p * XS_PAIR);
+    for (int r = 0; r < RPT; ++r) tot[r] = 0.f;
+    while (true) {
+        uint32_t cur[RPT][DW];
 #pragma unroll
-        for (int r = 0; r < RPT; ++r) tot[r] += T::dot(buf[r], xv);
+        for (int r = 0; r < RPT; ++r)
+#pragma unroll
+            for (int d = 0; d < DW; ++d) cur[r][d] = nxt[r][d];
+        const int p = j + it * LPR;
+        int it2 = it + 1;
+        long tile2 = tile;
+        if (it2 == IPT) {
+            it2 = 0;
+            tile2 += tile_stride;
+        }
+        const bool more = tile2 < ntiles;
+        if (more) issue(tile2, it2);
+        if (p < P) {
+            const float4* xv = reinterpret_cast<const float4*>(xs + p * XS_PAIR);
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) tot[r] += T::dot(cur[r], xv);
+        }
+        if (it == IPT - 1) {
+            const long row0 = tile * ROWS + lrow;
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) {
+                const float sum = lane_group_sum<LPR>(tot[r]);
+                if (j == LPR - 1 && row0 + r < N) y[row0 + r] = sum * out_scale;
+                tot[r] = 0.f;
+            }
+        }
+        if (!more) break;
+        tile = tile2;
+        it = it2;
     }
 }
 
 // ---------------------------------------------------------------------------
 // M = 1 dense kernel (fast path). Requires K % 64 == 0, W and ldw 4-aligned.
+// Persistent: the grid is sized to the chip and workgroups loop over tiles.
 // ---------------------------------------------------------------------------
 template <int QT, int LPR, int RPT, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void k_m1(const uint8_t* __restrict__ W, size_t ldw,
                                                    const float* __restrict__ x, float* __restrict__ y, int N, int K) {
     extern __shared__ __align__(16) float xs[];
-    stage_x(xs, x, K);
-    __syncthreads();
-    constexpr int GROUPS = 64 / LPR;
-    constexpr int ROWS_PER_WG = GROUPS * RPT * WAVES;
+    m1_stream<QT, LPR, RPT, WAVES>(W, ldw, x, y, N, K, blockIdx.x, gridDim.x, PairTraits<QT>::OUT_SCALE, xs);
+}
+
+// ---------------------------------------------------------------------------
+// Batched M = 1 kernel: several independent products y_p = W_p x_p in one
+// launch (one problem is the plain call). Each problem gets a share of the
+// workgroups in proportion to its weight bytes; within a problem, every wave
+// gets an equal contiguous range of row groups (a row group = 64/LPR rows,
+// LPR lanes per row), so all waves finish together. A lane walks the pairs
+// j, j + LPR, ... of its row; the loads of the next two steps are in flight
+// while a step is decoded. The workgroup stages its problem's x into LDS
+// after issuing its first loads.
+// ---------------------------------------------------------------------------
+constexpr int MAXB = 16;  // problems per batched launch
+
+struct M1Prob {
+    const uint8_t* W;
+    const float* x;
+    float* y;
+    size_t ldw;
+    int N, K, lpr, wg0, nwg;
+};
+struct M1Batch {
+    M1Prob p[MAXB];
+    int n;
+};
+
+template <int LPR>
+__device__ __forceinline__ float group_sum_rt(float v) { return lane_group_sum<LPR>(v); }
+
+__device__ __forceinline__ float group_sum_dyn(float v, int lpr) {
+    switch (lpr) {
+        case 64: return lane_group_sum<64>(v);
+        case 32: return lane_group_sum<32>(v);
+        case 16: return lane_group_sum<16>(v);
+        case 8: return lane_group_sum<8>(v);
+        default: return lane_group_sum<4>(v);
+    }
+}
+
+template <int QT, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void k_m1b(const M1Batch B) {
+    using T = PairTraits<QT>;
+    constexpr int DW = T::DW, PB = DW * 4;
+    extern __shared__ __align__(16) float xs[];
+    int pi = 0;
+    while (pi + 1 < B.n && (int)blockIdx.x >= B.p[pi + 1].wg0) ++pi;
+    const uint8_t* __restrict__ W = B.p[pi].W;
+    const float* __restrict__ x = B.p[pi].x;
+    float* __restrict__ y = B.p[pi].y;
+    const size_t ldw = B.p[pi].ldw;
+    const int N = B.p[pi].N, K = B.p[pi].K, LPR = B.p[pi].lpr;
+    const int lw = blockIdx.x - B.p[pi].wg0;
+    const long T_waves = (long)B.p[pi].nwg * WAVES;
+
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int GROUPS = 64 / LPR;
     const int g = lane / LPR, j = lane % LPR;
     const int P = K >> 6;
-    for (long tile = blockIdx.x; tile * ROWS_PER_WG < N; tile += gridDim.x) {
-        const long row0 = tile * ROWS_PER_WG + (long)(wave * GROUPS + g) * RPT;
-        float tot[RPT];
-        m1_rows<QT, LPR, RPT>(W, ldw, xs, P, row0, N, j, tot);
-#pragma unroll
-        for (int r = 0; r < RPT; ++r) {
-            float s = lane_group_sum<LPR>(tot[r]);
-            if (j == 0 && row0 + r < N) y[row0 + r] = s * PairTraits<QT>::OUT_SCALE;
+    const int IPT = (P + LPR - 1) / LPR;
+    const long RG = ((long)N + GROUPS - 1) / GROUPS;
+    const long gw = (long)lw * WAVES + wave;
+    const long rg0 = RG * gw / T_waves, rg1 = RG * (gw + 1) / T_waves;
+    const long nitems = (rg1 - rg0) * IPT;
+
+    long irg = rg0;
+    int iit = 0;
+    long issued = 0;
+    auto issue = [&](uint32_t (&b)[DW]) {
+        if (issued < nitems) {
+            long row = irg * GROUPS + g;
+            row = row < N ? row : N - 1;
+            int p = j + iit * LPR;
+            p = p < P ? p : P - 1;
+            load_pair<DW>(W + row * ldw + (size_t)p * PB, b);
+        }
+        ++issued;
+        if (++iit == IPT) {
+            iit = 0;
+            ++irg;
+        }
+    };
+    uint32_t b0[DW], b1[DW];
+    issue(b0);
+    issue(b1);
+    stage_x(xs, x, K);
+    __syncthreads();
+
+    long prg = rg0;
+    int pit = 0;
+    float tot = 0.f;
+    auto process = [&](const uint32_t (&r)[DW]) {
+        const int p = j + pit * LPR;
+        if (p < P) tot += T::dot(r, reinterpret_cast<const float4*>(xs + p * XS_PAIR));
+        if (++pit == IPT) {
+            const float sum = group_sum_dyn(tot, LPR);
+            const long row = prg * GROUPS + g;
+            if (j == LPR - 1 && row < N) y[row] = sum * T::OUT_SCALE;
+            tot = 0.f;
+            pit = 0;
+            ++prg;
+        }
+    };
+    for (long it = 0; it < nitems; it += 2) {
+        process(b0);
+        issue(b0);
+        if (it + 1 < nitems) {
+            process(b1);
+            issue(b1);
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// M = 1 x-stationary kernel.
+//
+// Every lane owns one pair of blocks (64 activations) of K for the whole
+// kernel and keeps those activations in registers; weight rows stream past.
+// A row's P = K/64 pairs are split into S segments of `seg` pairs; a wave
+// covers one segment of 64/LPR rows (LPR lanes per row, lane j of a row
+// group holding pair s*seg + j), RPT rows per lane per step. The S waves of
+// a segment group hold the same rows; their partial sums meet in LDS. The
+// workgroup has S * WR waves (WR row-waves per segment). Loads run two steps
+// ahead of the arithmetic.
+// ---------------------------------------------------------------------------
+struct XsPlan {
+    int S, seg, WR;
+};
+
+template <int QT, int LPR, int RPT>
+__global__ __launch_bounds__(512) void k_m1x(const uint8_t* __restrict__ W, size_t ldw, const float* __restrict__ x,
+                                              float* __restrict__ y, int N, int K, XsPlan plan, float out_scale) {
+    using T = PairTraits<QT>;
+    constexpr int DW = T::DW, PB = DW * 4;
+    constexpr int GROUPS = 64 / LPR;
+    __shared__ float red[2][8][GROUPS * RPT];  // [step parity][wave][row slot]
+    const int S = plan.S, seg = plan.seg, WR = plan.WR;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int s = wave % S, rw = wave / S;
+    const int g = lane / LPR, j = lane % LPR;
+    const int P = K >> 6;
+    const int pidx = s * seg + j;
+    const bool active = j < seg && pidx < P;
+    const int pc = active ? pidx : 0;
+    const int ROWS_STEP = WR * GROUPS * RPT;
+    const long nsteps = ((long)N + ROWS_STEP - 1) / ROWS_STEP;
+    const long lrow = (long)(rw * GROUPS + g) * RPT;
+
+    // This lane's 64 activations, kept in registers.
+    float4 xr[16];
+    {
+        const float4* xp = reinterpret_cast<const float4*>(x + (size_t)pc * 64);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xr[i] = active ? xp[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    auto issue = [&](long step, uint32_t (&b)[RPT][DW]) {
+        const long row0 = step * ROWS_STEP + lrow;
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            long rr = row0 + r;
+            rr = rr < N ? rr : N - 1;
+            load_pair<DW>(W + rr * ldw + (size_t)pc * PB, b[r]);
+        }
+    };
+    auto finish = [&](long step, const uint32_t (&b)[RPT][DW], int parity) {
+        float v[RPT];
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) v[r] = active ? T::dot(b[r], xr) : 0.f;
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) v[r] = lane_group_sum<LPR>(v[r]);
+        const long row0 = step * ROWS_STEP + lrow;
+        if (S == 1) {
+            if (j == LPR - 1) {
+#pragma unroll
+                for (int r = 0; r < RPT; ++r)
+                    if (row0 + r < N) y[row0 + r] = v[r] * out_scale;
+            }
+            return;
+        }
+        if (j == LPR - 1) {
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) red[parity][wave][g * RPT + r] = v[r];
+        }
+        __syncthreads();
+        if (s == 0 && j == LPR - 1) {
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) {
+                float acc = v[r];
+                for (int q = 1; q < S; ++q) acc += red[parity][wave + q][g * RPT + r];
+                if (row0 + r < N) y[row0 + r] = acc * out_scale;
+            }
+        }
+    };
+
+    long step = blockIdx.x;
+    if (step >= nsteps) return;  // uniform over the workgroup
+    const long stride = gridDim.x;
+    uint32_t ba[RPT][DW], bb[RPT][DW];
+    issue(step, ba);
+    if (step + stride < nsteps) issue(step + stride, bb);
+    int parity = 0;
+    while (true) {
+        finish(step, ba, parity);
+        parity ^= 1;
+        if (step + 2 * stride < nsteps) issue(step + 2 * stride, ba);
+        step += stride;
+        if (step >= nsteps) break;
+        finish(step, bb, parity);
+        parity ^= 1;
+        if (step + 2 * stride < nsteps) issue(step + 2 * stride, bb);
+        step += stride;
+        if (step >= nsteps) break;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// M = 1 Q4_0 kernel on the matrix cores (v_mfma_f32_16x16x32_f16).
+//
+// A wave owns a tile of 16 weight rows (MFMA columns j = lane % 16) and a
+// segment of each row's block pairs. Lane group G = lane / 16 streams pair
+// q = p0 + 4t + G of row j at step t (36 bytes, two blocks), so the four lane
+// groups each feed their own block into one of the four 8-wide k slices of
+// every MFMA: slice G of MFMA u carries qs dword u of the lane's block, i.e.
+// 8 codes, as exact fp16 values (code - 8). The A operand is block diagonal:
+// row 4G + 0 holds the hi fp16 part and row 4G + 1 the lo fp16 part of the
+// matching activations in slice G, every other entry is zero. After the four
+// MFMAs of a block, lane (G, j) holds that block's sums for row j in D rows
+// 4G (hi) and 4G + 1 (lo), so the fp16 block scale is applied in fp32 right
+// there: acc += d * (D[4G] + D[4G+1]).
+//
+// The activations are split once per workgroup (x * 2^s = hi + lo with hi,
+// lo fp16 and 2^s bringing max |x| into [2^14, 2^15)) and stored in LDS in
+// the order the A operands read them: per block 128 bytes = 4 dwords u x
+// {hi, lo} x 8 halves. Products of fp16 values are exact in fp32 and hi + lo
+// carries 22 bits of each activation, so the result is fp32-accurate.
+// ---------------------------------------------------------------------------
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// 8 codes of one qs dword -> fp16 (code - 8), in the element order
+// [4u+0, 4u+2, 4u+1, 4u+3, 20+4u-4.., ...] = lo nibbles of bytes 0,2,1,3 then
+// hi nibbles of bytes 0,2,1,3 (u = the dword's index within the block).
+__device__ __forceinline__ half8_t q4_codes_f16(uint32_t q) {
+    const uint32_t M = 0x000F000Fu, MAGIC = 0x64006400u;  // fp16 1024 + nibble
+    const half2_t bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    const half2_t v0 = __builtin_bit_cast(half2_t, (q & M) | MAGIC) + bias;
+    const half2_t v1 = __builtin_bit_cast(half2_t, ((q >> 8) & M) | MAGIC) + bias;
+    const half2_t v2 = __builtin_bit_cast(half2_t, ((q >> 4) & M) | MAGIC) + bias;
+    const half2_t v3 = __builtin_bit_cast(half2_t, ((q >> 12) & M) | MAGIC) + bias;
+    half8_t r;
+    r[0] = v0[0]; r[1] = v0[1]; r[2] = v1[0]; r[3] = v1[1];
+    r[4] = v2[0]; r[5] = v2[1]; r[6] = v3[0]; r[7] = v3[1];
+    return r;
+}
+
+// Byte offset within a block's 128-byte LDS record of activation e (0..31),
+// piece p (0 = hi, 1 = lo); matches q4_codes_f16's element order.
+__device__ __forceinline__ int xh_offset(int e, int p) {
+    const int hi = e >> 4, kk = e & 15, u = kk >> 2, r = kk & 3;
+    const int pos = hi * 4 + ((r & 1) << 1 | (r >> 1));  // 0,2,1,3 -> 0,1,2,3 order
+    return u * 32 + p * 16 + pos * 2;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+// Split x (K floats) into scaled fp16 hi/lo pairs in the MFMA A-operand
+// order. Returns the power-of-two exponent s (x was multiplied by 2^s).
+// Called by all threads of the workgroup; ends with a barrier.
+__device__ int stage_x_f16(uint8_t* xh, const float* __restrict__ x, int K, float* red) {
+    float m = 0.f;
+    for (int k = threadIdx.x; k < K; k += blockDim.x) m = fmaxf(m, fabsf(x[k]));
+    m = wave_max(m);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    m = red[0];
+    for (int w = 1; w < nw; ++w) m = fmaxf(m, red[w]);
+    int s = 0;
+    if (m > 0.f && m <= 3.4e38f) {
+        int e;
+        frexpf(m, &e);  // m in [2^(e-1), 2^e)
+        s = 15 - e;
+        s = s > 126 ? 126 : (s < -126 ? -126 : s);
+    }
+    for (int k = threadIdx.x; k < K; k += blockDim.x) {
+        const float v = ldexpf(x[k], s);
+        const _Float16 h = (_Float16)v;
+        const _Float16 l = (_Float16)(v - (float)h);
+        uint8_t* rec = xh + (size_t)(k >> 5) * 128;
+        *reinterpret_cast<_Float16*>(rec + xh_offset(k & 31, 0)) = h;
+        *reinterpret_cast<_Float16*>(rec + xh_offset(k & 31, 1)) = l;
+    }
+    __syncthreads();
+    return s;
+}
+
+// Plan: tiles of 16 rows; each row's P pairs in S segments of `seg` pairs;
+// a workgroup has S * WR waves and works on WR tiles at a time.
+struct MhPlan {
+    int S, seg, WR;
+};
+
+__global__ __launch_bounds__(1024) void k_m1h(const uint8_t* __restrict__ W, size_t ldw, const float* __restrict__ x,
+                                              float* __restrict__ y, int N, int K, MhPlan plan, float out_scale) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    __shared__ float red[2][16][16];  // [tile parity][wave][row]
+    const int S = plan.S, seg = plan.seg, WR = plan.WR;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int sgi = wave % S, rw = wave / S;
+    const int G = lane >> 4, j = lane & 15;
+    const int P = K >> 6;
+    const int p0 = sgi * seg;
+    const int p1 = p0 + seg < P ? p0 + seg : P;
+    const int nsteps = (seg + 3) >> 2;  // the same for every wave of the grid
+    const long ntiles = ((long)N + 15) / 16;
+    const long tstride = (long)gridDim.x * WR;
+    const long tile0 = (long)blockIdx.x * WR + rw;
+    // Every wave walks the same number of (tile, step) items so that the
+    // workgroup's barriers line up; items past the last tile are masked.
+    const long rounds = (ntiles + tstride - 1) / tstride;
+    const long nitems = rounds * nsteps;
+    // A-operand lanes: row i = lane % 16 with i / 4 == G and i % 4 < 2.
+    const bool a_lane = (j >> 2) == G && (j & 3) < 2;
+    const int a_piece = j & 1;
+
+    // Issue cursor (tile, step) runs two items ahead of the compute cursor.
+    long itile = tile0;
+    int istep = 0;
+    long issued = 0;
+    auto issue = [&](uint32_t (&b)[9]) {
+        if (issued < nitems) {
+            long row = itile * 16 + j;
+            row = row < N ? row : N - 1;
+            int q = p0 + 4 * istep + G;
+            q = q < p1 ? q : p1 - 1;
+            q = q > 0 ? q : 0;
+            load_pair<9>(W + row * ldw + (size_t)q * 36, b);
+        }
+        ++issued;
+        if (++istep == nsteps) {
+            istep = 0;
+            itile += tstride;
+        }
+    };
+
+    uint32_t b0[9], b1[9];
+    issue(b0);
+    issue(b1);
+    const int sx = stage_x_f16(smem, x, K, &red[0][0][0]);
+    const float yscale = ldexpf(out_scale, -sx);
+
+    half8_t a[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) a[u] = (half8_t){0, 0, 0, 0, 0, 0, 0, 0};
+    float acc = 0.f;
+    int parity = 0;
+    long ptile = tile0;
+    int pstep = 0;
+
+    auto process = [&](const uint32_t (&r)[9]) {
+        const bool tile_ok = ptile < ntiles;
+        const int q = p0 + 4 * pstep + G;
+        const bool valid = tile_ok && q < p1;
+#pragma unroll
+        for (int R = 0; R < 2; ++R) {
+            const int bk = 2 * q + R;
+            if (a_lane) {
+                const uint8_t* rec = smem + (size_t)(valid ? bk : 0) * 128 + a_piece * 16;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const half8_t v = *reinterpret_cast<const half8_t*>(rec + u * 32);
+                    a[u] = valid ? v : (half8_t){0, 0, 0, 0, 0, 0, 0, 0};
+                }
+            }
+            uint32_t qd[4];
+            float d;
+            if (R == 0) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) qd[u] = __builtin_amdgcn_alignbyte(r[u + 1], r[u], 2);
+                d = half_lo(r[0]);
+            } else {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) qd[u] = r[5 + u];
+                d = half_hi(r[4]);
+            }
+            f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[u], q4_codes_f16(qd[u]), c, 0, 0, 0);
+            if (valid) acc = fmaf(d, c[0] + c[1], acc);
+        }
+        if (pstep == nsteps - 1) {
+            // Sum the four lane groups (block slices) of each row.
+            float v = acc + __shfl_xor(acc, 16, 64);
+            v += __shfl_xor(v, 32, 64);
+            acc = 0.f;
+            const long row = ptile * 16 + j;
+            if (S == 1) {
+                if (tile_ok && G == 0 && row < N) y[row] = v * yscale;
+            } else {
+                if (G == 0) red[parity][wave][j] = v;
+                __syncthreads();
+                if (tile_ok && sgi == 0 && G == 0 && row < N) {
+                    float tot = v;
+                    for (int q2 = 1; q2 < S; ++q2) tot += red[parity][wave + q2][j];
+                    y[row] = tot * yscale;
+                }
+                parity ^= 1;
+            }
+            pstep = 0;
+            ptile += tstride;
+        } else {
+            ++pstep;
+        }
+    };
+
+    for (long it = 0; it < nitems; it += 2) {
+        process(b0);
+        issue(b0);
+        if (it + 1 < nitems) {
+            process(b1);
+            issue(b1);
+        }
+    }
+}
+
+MhPlan make_mh_plan(int N, int K, int ncu, int target_waves_per_cu) {
+    const int P = K / 64;
+    const long ntiles = ((long)N + 15) / 16;
+    // Segments: enough (tile, segment) waves to fill the chip, each at least
+    // 4 pairs per lane group step and at most 16 segments.
+    long want = (long)ncu * target_waves_per_cu;
+    int S = 1;
+    while (S < 16 && ntiles * S < want && (P + 2 * S - 1) / (2 * S) >= 4) S *= 2;
+    MhPlan pl;
+    pl.S = S;
+    pl.seg = (P + S - 1) / S;
+    pl.WR = S >= 8 ? 1 : 8 / S;
+    return pl;
 }
 
 // ---------------------------------------------------------------------------
@@ -408,25 +908,16 @@ __global__ __launch_bounds__(WAVES * 64) void k_id(const uint8_t* __restrict__ W
     __syncthreads();
     const int count = s_count;
     const uint8_t* We = W + (size_t)e * estride;
-    const int lane = tid & 63, wave = tid >> 6;
 
     if (count == 1 && fast) {
         const int t = p / top_k;
-        stage_x(xs, X + (size_t)t * ldx, K);
-        __syncthreads();
-        const int g = lane / LPR, j = lane % LPR;
-        const long row0 = tile_row0 + (long)(wave * GROUPS + g) * RPT;
-        float tot[RPT];
-        m1_rows<QT, LPR, RPT>(We, ldw, xs, K >> 6, row0, N, j, tot);
         const float sc = (escale ? escale[e] : 1.f) * PairTraits<QT>::OUT_SCALE;
-#pragma unroll
-        for (int r = 0; r < RPT; ++r) {
-            float s = lane_group_sum<LPR>(tot[r]);
-            if (j == 0 && row0 + r < N) Y[(size_t)p * ldy + row0 + r] = s * sc;
-        }
+        m1_stream<QT, LPR, RPT, WAVES>(We, ldw, X + (size_t)t * ldx, Y + (size_t)p * ldy, N, K, blockIdx.x,
+                                       gridDim.x, sc, xs);
         return;
     }
     // General case: one wave per row, up to 16 pairs per pass.
+    const int lane = tid & 63, wave = tid >> 6;
     const float sc = escale ? escale[e] : 1.f;
     const int served = count < ID_MAX_LIST ? count : ID_MAX_LIST;
     for (int c0 = 0; c0 < served; c0 += 16) {
@@ -456,19 +947,28 @@ __global__ __launch_bounds__(WAVES * 64) void k_id(const uint8_t* __restrict__ W
 constexpr int KMAX_FAST = 15360;     // x staged in <= 64 KiB of LDS
 constexpr int KMAX_FAST_ID = 14336;  // same, next to the id kernel's pair list
 
-struct M1Shape {
-    int lpr, rpt;
-};
+constexpr size_t LDS_PER_CU = 160 * 1024;  // gfx950
+
+// Compute units of the current device (cached per device id).
+int num_cus() {
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < 64 && cache[dev] > 0) return cache[dev];
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    if (dev < 64) cache[dev] = n;
+    return n;
+}
 
 // Lanes per row: the largest power of two (<= 64) whose lane utilisation
 // P / (LPR * ceil(P / LPR)) is within 5% of the best one, so long rows keep
 // a full wave on one row and short rows still use every lane.
 int pick_lpr(int P) {
-    double best = 0;
-    int cands[] = {64, 32, 16, 8, 4};
-    double eff[5];
+    const int cands[] = {64, 32, 16, 8, 4};
+    double eff[5], best = 0;
     for (int i = 0; i < 5; ++i) {
-        int l = cands[i];
+        const int l = cands[i];
         eff[i] = (double)P / ((double)l * ((P + l - 1) / l));
         if (eff[i] > best) best = eff[i];
     }
@@ -477,33 +977,145 @@ int pick_lpr(int P) {
     return 4;
 }
 
-M1Shape pick_m1(int N, int K) {
-    M1Shape s;
-    s.lpr = pick_lpr(K / 64);
-    s.rpt = (N >= 4096) ? 2 : 1;
-    return s;
+struct M1Cfg {
+    int lpr, rpt, waves, wgs_per_cu;
+};
+
+M1Cfg pick_m1(int N, int K) {
+    M1Cfg c;
+    c.lpr = pick_lpr(K / 64);
+    c.rpt = 1;
+    c.waves = 8;
+    c.wgs_per_cu = 4;
+    (void)N;
+    return c;
 }
 
-template <int QT, int LPR, int RPT>
-int launch_m1_t(const uint8_t* W, size_t ldw, const float* X, float* Y, int N, int K, hipStream_t st) {
-    constexpr int WAVES = 4;
-    constexpr int ROWS_PER_WG = (64 / LPR) * RPT * WAVES;
-    const long tiles = ((long)N + ROWS_PER_WG - 1) / ROWS_PER_WG;
-    const int grid = (int)(tiles < 65535 ? tiles : 65535);
-    hipLaunchKernelGGL((k_m1<QT, LPR, RPT, WAVES>), dim3(grid), dim3(WAVES * 64), xs_bytes(K), st, W, ldw, X, Y,
-                       N, K);
+template <int QT, int LPR, int RPT, int WAVES>
+int launch_m1_t(const uint8_t* W, size_t ldw, const float* X, float* Y, int N, int K, int wgs_per_cu,
+                hipStream_t st) {
+    constexpr int ROWS = (64 / LPR) * RPT * WAVES;
+    const long tiles = ((long)N + ROWS - 1) / ROWS;
+    const size_t lds = xs_bytes(K);
+    long per_cu = (long)(LDS_PER_CU / (lds ? lds : 1));
+    per_cu = per_cu < 1 ? 1 : (per_cu < wgs_per_cu ? per_cu : wgs_per_cu);
+    long grid = (long)num_cus() * per_cu;
+    grid = grid < tiles ? grid : tiles;
+    hipLaunchKernelGGL((k_m1<QT, LPR, RPT, WAVES>), dim3((unsigned)grid), dim3(WAVES * 64), lds, st, W, ldw, X, Y, N,
+                       K);
     return check_launch("qmv m1 kernel");
 }
 
 template <int QT>
 int launch_m1(const uint8_t* W, size_t ldw, const float* X, float* Y, int N, int K, hipStream_t st) {
-    M1Shape s = pick_m1(N, K);
-#define QMV_M1_CASE(L, R) \
-    if (s.lpr == L && s.rpt == R) return launch_m1_t<QT, L, R>(W, ldw, X, Y, N, K, st);
-    QMV_M1_CASE(64, 1) QMV_M1_CASE(64, 2) QMV_M1_CASE(32, 1) QMV_M1_CASE(32, 2) QMV_M1_CASE(16, 1)
-    QMV_M1_CASE(16, 2) QMV_M1_CASE(8, 1) QMV_M1_CASE(8, 2) QMV_M1_CASE(4, 1) QMV_M1_CASE(4, 2)
+    const M1Cfg c = pick_m1(N, K);
+#define QMV_M1_CASE(L, R, WV) \
+    if (c.lpr == L && c.rpt == R && c.waves == WV) return launch_m1_t<QT, L, R, WV>(W, ldw, X, Y, N, K, c.wgs_per_cu, st);
+    QMV_M1_CASE(64, 1, 8) QMV_M1_CASE(32, 1, 8) QMV_M1_CASE(16, 1, 8) QMV_M1_CASE(8, 1, 8) QMV_M1_CASE(4, 1, 8)
 #undef QMV_M1_CASE
-    return fail(QMV_EINVAL, "internal: no m1 kernel for lpr=%d rpt=%d", s.lpr, s.rpt);
+    return fail(QMV_EINVAL, "internal: no m1 kernel for lpr=%d rpt=%d waves=%d", c.lpr, c.rpt, c.waves);
+}
+
+// Plan for the x-stationary kernel: lanes per row and K segments.
+struct M1xCfg {
+    int lpr, rpt, wr, wgs_per_cu;
+};
+
+XsPlan make_plan(int P, int lpr, int wr) {
+    XsPlan pl;
+    pl.S = (P + lpr - 1) / lpr;
+    pl.seg = (P + pl.S - 1) / pl.S;
+    pl.WR = wr;
+    while (pl.S * pl.WR > 8 && pl.WR > 1) --pl.WR;
+    return pl;
+}
+
+template <int QT, int LPR, int RPT>
+int launch_m1x_t(const uint8_t* W, size_t ldw, const float* X, float* Y, int N, int K, int wr, int wgs_per_cu,
+                 float out_scale, hipStream_t st) {
+    const XsPlan pl = make_plan(K / 64, LPR, wr);
+    if (pl.S > 8) return fail(QMV_EINVAL, "internal: K=%d too long for the x-stationary kernel", K);
+    const int rows_step = pl.WR * (64 / LPR) * RPT;
+    const long nsteps = ((long)N + rows_step - 1) / rows_step;
+    long grid = (long)num_cus() * wgs_per_cu;
+    grid = grid < nsteps ? grid : nsteps;
+    hipLaunchKernelGGL((k_m1x<QT, LPR, RPT>), dim3((unsigned)grid), dim3(64 * pl.S * pl.WR), 0, st, W, ldw, X, Y, N,
+                       K, pl, out_scale);
+    return check_launch("qmv m1x kernel");
+}
+
+int launch_m1h(const uint8_t* W, size_t ldw, const float* X, float* Y, int N, int K, int target_wpc, int wgs_per_cu,
+               int force_S, hipStream_t st) {
+    const int ncu = num_cus();
+    MhPlan pl = make_mh_plan(N, K, ncu, target_wpc);
+    if (force_S > 0) {
+        pl.S = force_S;
+        pl.seg = (K / 64 + force_S - 1) / force_S;
+        pl.WR = force_S >= 8 ? 1 : 8 / force_S;
+    }
+    const long ntiles = ((long)N + 15) / 16;
+    long grid = (long)ncu * wgs_per_cu;
+    const long need = (ntiles + pl.WR - 1) / pl.WR;
+    grid = grid < need ? grid : need;
+    const size_t lds = (size_t)(K / 32) * 128;
+    hipLaunchKernelGGL(k_m1h, dim3((unsigned)grid), dim3(64 * pl.S * pl.WR), lds, st, W, ldw, X, Y, N, K, pl, 1.0f);
+    return check_launch("qmv m1h kernel");
+}
+
+// Lanes per row for the batched kernel: favour more rows in flight (more
+// waves) over lane utilisation, since these products are latency-bound: the
+// largest power of two not above 4/3 of the pairs per row.
+int m1b_lpr(int P) {
+    int l = 64;
+    while (l > 4 && 3 * l > 4 * P) l >>= 1;
+    return l;
+}
+
+// Problems a batched M = 1 launch can take (checked by the caller).
+bool m1b_eligible(const uint8_t* W, size_t ldw, const float* x, int K) {
+    return K > 0 && K % 64 == 0 && K <= KMAX_FAST && ((uintptr_t)W & 3) == 0 && (ldw & 3) == 0 &&
+           ((uintptr_t)x & 3) == 0;
+}
+
+// Launch the batched M = 1 kernel over n problems (n <= MAXB), all eligible.
+// wgs_per_cu and waves are tuning knobs (0 = default).
+template <int QT>
+int launch_m1b(const M1Prob* probs, int n, int wgs_per_cu, int waves, hipStream_t st) {
+    if (waves == 0) waves = 8;
+    M1Batch B;
+    B.n = 0;
+    size_t lds = 0;
+    double total = 0;
+    const int bb = block_bytes(QT);
+    for (int i = 0; i < n; ++i) total += (double)probs[i].N * (probs[i].K / QK) * bb;
+    for (int i = 0; i < n; ++i) lds = xs_bytes(probs[i].K) > lds ? xs_bytes(probs[i].K) : lds;
+    if (wgs_per_cu == 0) {
+        wgs_per_cu = (int)(LDS_PER_CU / (lds ? lds : 1));
+        const int cap = waves == 16 ? 2 : 3;
+        wgs_per_cu = wgs_per_cu < 1 ? 1 : (wgs_per_cu > cap ? cap : wgs_per_cu);
+    }
+    const long budget = (long)num_cus() * wgs_per_cu;
+    int wg = 0;
+    for (int i = 0; i < n; ++i) {
+        M1Prob q = probs[i];
+        q.lpr = m1b_lpr(q.K / 64);
+        const long groups = ((long)q.N + 64 / q.lpr - 1) / (64 / q.lpr);
+        const double bytes = (double)q.N * (q.K / QK) * bb;
+        long nwg = (long)(budget * bytes / total + 0.5);
+        const long useful = (groups + waves - 1) / waves;  // at least one row group per wave
+        nwg = nwg < 1 ? 1 : (nwg > useful ? useful : nwg);
+        q.wg0 = wg;
+        q.nwg = (int)nwg;
+        wg += q.nwg;
+        B.p[B.n++] = q;
+    }
+    if (waves == 16)
+        hipLaunchKernelGGL((k_m1b<QT, 16>), dim3(wg), dim3(1024), lds, st, B);
+    else if (waves == 4)
+        hipLaunchKernelGGL((k_m1b<QT, 4>), dim3(wg), dim3(256), lds, st, B);
+    else
+        hipLaunchKernelGGL((k_m1b<QT, 8>), dim3(wg), dim3(512), lds, st, B);
+    return check_launch("qmv batched m1 kernel");
 }
 
 template <int QT>
@@ -662,23 +1274,112 @@ int qmv_id(int qtype, const void* Wv, size_t expert_stride_bytes, size_t ldw_byt
     return QMV_OK;
 }
 
+int qmv_batch(int qtype, const qmv_problem* problems, int n_problems, void* stream) {
+    if (qtype != QMV_Q4_0 && qtype != QMV_Q8_0) return fail(QMV_EUNSUPPORTED, "qmv_batch: qtype %d not supported", qtype);
+    if (n_problems < 0 || n_problems > QMV_MAX_BATCH)
+        return fail(QMV_EINVAL, "qmv_batch: n_problems=%d outside 0..%d", n_problems, QMV_MAX_BATCH);
+    if (n_problems == 0) return QMV_OK;
+    if (!problems) return fail(QMV_EINVAL, "qmv_batch: problems is NULL");
+    const int bb = block_bytes(qtype);
+    size_t wb[QMV_MAX_BATCH], xb[QMV_MAX_BATCH], yb[QMV_MAX_BATCH];
+    for (int i = 0; i < n_problems; ++i) {
+        const qmv_problem& p = problems[i];
+        if (p.N < 0) return fail(QMV_EINVAL, "qmv_batch: problem %d: N=%d < 0", i, p.N);
+        if (p.K < 0 || p.K % QK) return fail(QMV_EINVAL, "qmv_batch: problem %d: K=%d is not a non-negative multiple of 32", i, p.K);
+        const size_t row = (size_t)(p.K / QK) * bb;
+        if (p.N > 0 && !p.y) return fail(QMV_EINVAL, "qmv_batch: problem %d: y is NULL", i);
+        if (p.N > 0 && p.K > 0 && (!p.W || !p.x)) return fail(QMV_EINVAL, "qmv_batch: problem %d: W or x is NULL", i);
+        if (p.ldw_bytes < row) return fail(QMV_EINVAL, "qmv_batch: problem %d: ldw_bytes=%zu < K/32*%d=%zu", i, p.ldw_bytes, bb, row);
+        if (((uintptr_t)p.W & 1) || (p.ldw_bytes & 1)) return fail(QMV_EALIGN, "qmv_batch: problem %d: W and ldw_bytes must be 2-byte aligned", i);
+        if (((uintptr_t)p.x & 3) || ((uintptr_t)p.y & 3)) return fail(QMV_EALIGN, "qmv_batch: problem %d: x and y must be 4-byte aligned", i);
+        if (p.N > 0 && (size_t)p.N > (SIZE_MAX - row) / (p.ldw_bytes ? p.ldw_bytes : 1)) return fail(QMV_EINVAL, "qmv_batch: problem %d: N*ldw overflows", i);
+        wb[i] = (p.N > 0 && p.K > 0) ? (size_t)(p.N - 1) * p.ldw_bytes + row : 0;
+        xb[i] = (p.N > 0) ? (size_t)p.K * 4 : 0;
+        yb[i] = (size_t)p.N * 4;
+    }
+    for (int i = 0; i < n_problems; ++i)
+        for (int k = 0; k < n_problems; ++k) {
+            if (overlaps(problems[i].y, yb[i], problems[k].W, wb[k]) || overlaps(problems[i].y, yb[i], problems[k].x, xb[k]) ||
+                (k != i && overlaps(problems[i].y, yb[i], problems[k].y, yb[k])))
+                return fail(QMV_EINVAL, "qmv_batch: output of problem %d overlaps an input or another output (problem %d)", i, k);
+        }
+    hipStream_t st = (hipStream_t)stream;
+    M1Prob fast[QMV_MAX_BATCH];
+    int nf = 0;
+    for (int i = 0; i < n_problems; ++i) {
+        const qmv_problem& p = problems[i];
+        if (p.N == 0) continue;
+        const uint8_t* W = (const uint8_t*)p.W;
+        if (m1b_eligible(W, p.ldw_bytes, p.x, p.K)) {
+            M1Prob& q = fast[nf++];
+            q.W = W;
+            q.x = p.x;
+            q.y = p.y;
+            q.ldw = p.ldw_bytes;
+            q.N = p.N;
+            q.K = p.K;
+        } else {
+            const int rc = qtype == QMV_Q4_0 ? launch_generic<QMV_Q4_0>(W, p.ldw_bytes, p.x, p.K, p.y, p.N, 1, p.N, p.K, st)
+                                             : launch_generic<QMV_Q8_0>(W, p.ldw_bytes, p.x, p.K, p.y, p.N, 1, p.N, p.K, st);
+            if (rc) return rc;
+        }
+    }
+    if (nf == 0) return QMV_OK;
+    return qtype == QMV_Q4_0 ? launch_m1b<QMV_Q4_0>(fast, nf, 0, 0, st) : launch_m1b<QMV_Q8_0>(fast, nf, 0, 0, st);
+}
+
 const char* qmv_last_error(void) { return g_err; }
 
 #ifdef QMV_PROBE
-// Tuning entry, built only into a separate probe library: run the M = 1
-// kernel with an explicit lanes-per-row / rows-per-lane choice.
-int qmv_probe_m1(int qtype, int lpr, int rpt, const void* W, size_t ldw, const float* X, float* Y, int N, int K,
-                 void* stream) {
+// Tuning entries, built only into a separate probe library.
+int qmv_probe_m1(int qtype, int lpr, int rpt, int waves, int wgs_per_cu, const void* W, size_t ldw, const float* X,
+                 float* Y, int N, int K, void* stream) {
     hipStream_t st = (hipStream_t)stream;
     const uint8_t* w = (const uint8_t*)W;
+#define QMV_P(QT, L, R, WV)                            \
+    if (qtype == QT && lpr == L && rpt == R && waves == WV) \
+        return launch_m1_t<QT, L, R, WV>(w, ldw, X, Y, N, K, wgs_per_cu, st);
+#define QMV_PW(QT, WV) QMV_P(QT, 64, 1, WV) QMV_P(QT, 64, 2, WV) QMV_P(QT, 32, 1, WV) QMV_P(QT, 32, 2, WV) \
+    QMV_P(QT, 16, 1, WV) QMV_P(QT, 16, 2, WV)
+    QMV_PW(QMV_Q4_0, 4) QMV_PW(QMV_Q4_0, 8) QMV_PW(QMV_Q4_0, 16)
+    QMV_PW(QMV_Q8_0, 4) QMV_PW(QMV_Q8_0, 8) QMV_PW(QMV_Q8_0, 16)
+#undef QMV_PW
+#undef QMV_P
+    return fail(QMV_EINVAL, "probe: no variant");
+}
+
+int qmv_probe_m1x(int qtype, int lpr, int rpt, int wr, int wgs_per_cu, const void* W, size_t ldw, const float* X,
+                  float* Y, int N, int K, void* stream) {
+    hipStream_t st = (hipStream_t)stream;
+    const uint8_t* w = (const uint8_t*)W;
+    const float sc = qtype == QMV_Q4_0 ? 16.f : 1.f;
 #define QMV_P(QT, L, R) \
-    if (qtype == QT && lpr == L && rpt == R) return launch_m1_t<QT, L, R>(w, ldw, X, Y, N, K, st);
-#define QMV_PQ(QT) QMV_P(QT, 64, 1) QMV_P(QT, 64, 2) QMV_P(QT, 64, 4) QMV_P(QT, 32, 1) QMV_P(QT, 32, 2) \
-    QMV_P(QT, 32, 4) QMV_P(QT, 16, 1) QMV_P(QT, 16, 2) QMV_P(QT, 16, 4) QMV_P(QT, 8, 1) QMV_P(QT, 8, 2) QMV_P(QT, 4, 1)
+    if (qtype == QT && lpr == L && rpt == R) return launch_m1x_t<QT, L, R>(w, ldw, X, Y, N, K, wr, wgs_per_cu, sc, st);
+#define QMV_PQ(QT) QMV_P(QT, 64, 1) QMV_P(QT, 64, 2) QMV_P(QT, 32, 1) QMV_P(QT, 32, 2) QMV_P(QT, 16, 1) QMV_P(QT, 16, 2)
     QMV_PQ(QMV_Q4_0) QMV_PQ(QMV_Q8_0)
 #undef QMV_PQ
 #undef QMV_P
     return fail(QMV_EINVAL, "probe: no variant");
+}
+
+int qmv_probe_m1h(int target_wpc, int wgs_per_cu, int force_S, const void* W, size_t ldw, const float* X, float* Y,
+                  int N, int K, void* stream) {
+    return launch_m1h((const uint8_t*)W, ldw, X, Y, N, K, target_wpc, wgs_per_cu, force_S, (hipStream_t)stream);
+}
+
+int qmv_probe_m1b(int qtype, int waves, int wgs_per_cu, int n, const void* const* W, const size_t* ldw,
+                  const float* const* X, float* const* Y, const int* N, const int* K, void* stream) {
+    M1Prob pr[MAXB];
+    for (int i = 0; i < n && i < MAXB; ++i) {
+        pr[i].W = (const uint8_t*)W[i];
+        pr[i].x = X[i];
+        pr[i].y = Y[i];
+        pr[i].ldw = ldw[i];
+        pr[i].N = N[i];
+        pr[i].K = K[i];
+    }
+    return qtype == QMV_Q4_0 ? launch_m1b<QMV_Q4_0>(pr, n, wgs_per_cu, waves, (hipStream_t)stream)
+                             : launch_m1b<QMV_Q8_0>(pr, n, wgs_per_cu, waves, (hipStream_t)stream);
 }
 #endif
 

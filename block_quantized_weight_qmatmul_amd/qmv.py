@@ -20,7 +20,15 @@ QMV_MAX_M = 16
 BLOCK_BYTES = {QMV_Q4_0: 18, QMV_Q8_0: 34}
 QTYPES = {"q4_0": QMV_Q4_0, "q8_0": QMV_Q8_0}
 
+QMV_MAX_BATCH = 16
+
 _lib = None
+
+
+class Problem(ctypes.Structure):
+    """C layout of qmv_problem (include/qmv.h)."""
+    _fields_ = [("W", ctypes.c_void_p), ("ldw_bytes", ctypes.c_size_t), ("x", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("N", ctypes.c_int), ("K", ctypes.c_int)]
 
 
 class QmvError(RuntimeError):
@@ -44,6 +52,8 @@ def lib() -> ctypes.CDLL:
             f.argtypes = [P, S, P, S, P, S, I, I, I, P]
         L.qmv_id.restype = I
         L.qmv_id.argtypes = [I, P, S, S, I, P, S, P, I, I, P, S, I, I, P, P, P]
+        L.qmv_batch.restype = I
+        L.qmv_batch.argtypes = [I, ctypes.POINTER(Problem), I, P]
         L.qmv_last_error.restype = ctypes.c_char_p
         L.qmv_last_error.argtypes = []
         _lib = L
@@ -84,6 +94,12 @@ def raw_qmv_id(qtype, W, expert_stride, ldw, n_experts, X, ldx, ids, n_tokens, t
                expert_scale=0, err_flag=0, stream=0) -> int:
     return lib().qmv_id(qtype, W, expert_stride, ldw, n_experts, X, ldx, ids, n_tokens, top_k, Y, ldy, N, K,
                         expert_scale, err_flag, stream)
+
+
+def raw_qmv_batch(qtype: int, problems, stream: int = 0) -> int:
+    """problems: sequence of (W, ldw_bytes, x, y, N, K) integer tuples."""
+    arr = (Problem * max(1, len(problems)))(*[Problem(*p) for p in problems])
+    return lib().qmv_batch(qtype, arr, len(problems), stream)
 
 
 # ---------------------------------------------------------------------------
@@ -135,3 +151,18 @@ def qmv_id(qtype, W, X, ids, Y, N: int, K: int, expert_scale=None, err_flag=None
                     n_tokens, top_k, _ptr(Y), Y.stride(0), N, K, _ptr(expert_scale), _ptr(err_flag),
                     _stream(stream))
     _check(st)
+
+
+def qmv_batch(qtype, problems, stream=None) -> None:
+    """Several independent M = 1 products in one launch (see include/qmv.h).
+
+    problems: sequence of (W, x, y) tensors with W uint8 [N, ldw] (row stride
+    W.stride(0) bytes), x fp32 [K] and y fp32 [N].
+    """
+    q = QTYPES[qtype] if isinstance(qtype, str) else int(qtype)
+    raw = []
+    for W, x, y in problems:
+        if W.dim() != 2 or W.stride(1) != 1 or x.dim() != 1 or y.dim() != 1:
+            raise ValueError("each problem needs W [N, ldw] with contiguous rows, x [K] and y [N]")
+        raw.append((_ptr(W), W.stride(0), _ptr(x), _ptr(y), W.shape[0], x.shape[0]))
+    _check(raw_qmv_batch(q, raw, _stream(stream)))

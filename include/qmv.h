@@ -131,6 +131,37 @@ int qmv_id(int qtype, const void* W, size_t expert_stride_bytes, size_t ldw_byte
            float* Y, size_t ldy, int N, int K, const float* expert_scale, int* err_flag,
            void* stream);
 
+/*
+ * qmv_batch — several independent M = 1 products in one launch:
+ *   problems[i].y = deq(problems[i].W) x problems[i].x,  i < n_problems.
+ *
+ * This is the grouped launch of projections that run together: the pages
+ * encode Q, K and V (which share one input) as one concurrent group, and
+ * the FFN gate, up and router as another (`encode_one_layer`, the barrier
+ * groups before the first and the ninth block of dispatches). Problems may
+ * share x; their outputs must not overlap each other or any W or x.
+ *
+ *  qtype        QMV_Q4_0 or QMV_Q8_0 (all problems of a batch have one type).
+ *  problems     HOST array of n_problems descriptors, read during the call.
+ *  n_problems   0..QMV_MAX_BATCH (0: nothing to do).
+ * Each descriptor follows qmv_q4_0's rules for M = 1 (W 2-byte aligned,
+ * ldw_bytes even and >= K/32 * block bytes, x and y 4-byte aligned, K a
+ * non-negative multiple of 32). Every problem is validated before anything
+ * is launched; one bad descriptor rejects the whole call.
+ */
+#define QMV_MAX_BATCH 16
+
+typedef struct {
+    const void* W;    /* device: N rows of K/32 blocks */
+    size_t ldw_bytes; /* row stride in bytes */
+    const float* x;   /* device: K activations */
+    float* y;         /* device: N outputs (overwritten) */
+    int N;            /* output features, >= 0 */
+    int K;            /* input features, multiple of 32, >= 0 */
+} qmv_problem;
+
+int qmv_batch(int qtype, const qmv_problem* problems, int n_problems, void* stream);
+
 /* Message for the last non-zero status returned on the calling thread. */
 const char* qmv_last_error(void);
 

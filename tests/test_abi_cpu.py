@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert {"qmv_q4_0", "qmv_q8_0", "qmv_id", "qmv_last_error"} <= set(names)
+    assert {"qmv_q4_0", "qmv_q8_0", "qmv_id", "qmv_batch", "qmv_last_error"} <= set(names)
     L = ctypes.CDLL(qmv.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -105,3 +105,31 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(qmv, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         qmv.lib()
+
+
+def _bp(**kw):
+    d = dict(W=W, ldw=18 * 4, x=X, y=Y, N=16, K=128)
+    d.update(kw)
+    return (d["W"], d["ldw"], d["x"], d["y"], d["N"], d["K"])
+
+
+@pytest.mark.parametrize("probs,status,msg", [
+    ([_bp(K=100)], qmv.QMV_EINVAL, "K=100"),
+    ([_bp(N=-1)], qmv.QMV_EINVAL, "N=-1"),
+    ([_bp(), _bp(ldw=18 * 3, y=Y + 4096)], qmv.QMV_EINVAL, "problem 1: ldw_bytes"),
+    ([_bp(W=W + 1)], qmv.QMV_EALIGN, "2-byte"),
+    ([_bp(y=Y + 2)], qmv.QMV_EALIGN, "4-byte"),
+    ([_bp(x=0)], qmv.QMV_EINVAL, "NULL"),
+    ([_bp(), _bp(y=Y + 32)], qmv.QMV_EINVAL, "overlaps"),          # two outputs overlap
+    ([_bp(), _bp(W=Y - 8, y=Y + 4096)], qmv.QMV_EINVAL, "overlaps"),  # output 0 overlaps W of problem 1
+    ([_bp()] * 17, qmv.QMV_EINVAL, "n_problems"),
+])
+def test_batch_argument_checks(probs, status, msg):
+    assert qmv.raw_qmv_batch(Q4, probs) == status
+    assert msg in qmv.last_error()
+
+
+def test_batch_bad_qtype_and_empty():
+    assert qmv.raw_qmv_batch(5, [_bp()]) == qmv.QMV_EUNSUPPORTED
+    assert qmv.raw_qmv_batch(Q4, []) == qmv.QMV_OK
+    assert qmv.raw_qmv_batch(Q8, [_bp(N=0, W=0, x=0, ldw=34 * 4)]) == qmv.QMV_OK  # N = 0: nothing to launch

@@ -189,3 +189,55 @@ def test_large_dynamic_range_activations():
     r = np.random.default_rng(89)
     X = (synth.make_x(1, K, cfg=89) * np.exp(r.uniform(-40, 40, K))).astype(np.float32)
     check("q4_0", W, X, "dynamic range")
+
+
+# --------------------------------------------------------------------------
+# Batched launch (qmv_batch).
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("qtype", ["q4_0", "q8_0"])
+def test_batch_decode_layer_set_against_oracle(qtype):
+    """The decode-layer projection set as one batch; Q, K and V share x."""
+    probs = synth.CONFIGS[1]["problems"]
+    host, dev = [], []
+    xq = synth.make_x(1, 4096, cfg=1, part=0)
+    for part, p in enumerate(probs):
+        W = synth.make_weights(qtype, p.N, p.K, cfg=1, part=part)
+        X = xq if p.name in ("q", "k", "v") else synth.make_x(1, p.K, cfg=1, part=part)
+        host.append((W, X))
+    xs_dev = {}
+    for W, X in host:
+        key = id(X)
+        if key not in xs_dev:
+            xs_dev[key] = torch.from_numpy(X[0]).to(DEV)
+        dev.append((torch.from_numpy(W).to(DEV), xs_dev[key], torch.full((W.shape[0],), np.nan, device=DEV)))
+    qmv.qmv_batch(qtype, dev)
+    torch.cuda.synchronize()
+    for (W, X), (_, _, y), p in zip(host, dev, probs):
+        yo, a = oracle.qmv(qtype, W, X)
+        assert_within_tol(y.cpu().numpy()[None, :], yo, a, f"batch {p.name}")
+
+
+def test_batch_mixed_fast_and_fallback_problems():
+    """Problems the fast kernel takes and ones it does not (odd blocks per
+    row, 2-byte row stride, K = 0) in one call."""
+    specs = [(300, 4096, None), (7, 96, None), (129, 1024, synth.row_bytes("q4_0", 1024) + 2), (64, 2816, None),
+             (5, 0, 18)]
+    host, dev = [], []
+    for i, (N, K, ldw) in enumerate(specs):
+        if K:
+            W = synth.make_weights("q4_0", N, K, cfg=79, part=i, ldw=ldw)
+            X = synth.make_x(1, K, cfg=79, part=i)
+        else:
+            W = np.zeros((N, ldw), np.uint8)
+            X = np.zeros((1, 4), np.float32)
+        host.append((W, X, K))
+        dev.append((torch.from_numpy(W).to(DEV), torch.from_numpy(X[0]).to(DEV)[:K] if K else torch.from_numpy(X[0]).to(DEV)[:0],
+                    torch.full((N,), np.nan, device=DEV)))
+    qmv.qmv_batch("q4_0", dev)
+    torch.cuda.synchronize()
+    for (W, X, K), (_, _, y) in zip(host, dev):
+        if K == 0:
+            assert torch.all(y == 0)
+            continue
+        yo, a = oracle.qmv("q4_0", W, X)
+        assert_within_tol(y.cpu().numpy()[None, :], yo, a, f"mixed K={K}")
