@@ -769,6 +769,539 @@ MhPlan make_mh_plan(int N, int K, int ncu, int target_waves_per_cu) {
 }
 
 // ---------------------------------------------------------------------------
+// M = 2..16 kernel on the matrix cores (v_mfma_f32_16x16x32_f16).
+//
+// One MFMA multiplies 16 activation rows (A, padded with zero rows) by one
+// block of 16 weight rows (B): lane (G, j) of B supplies qs dword G of the
+// block of weight row j as 8 exact fp16 codes (code - 8). Every lane streams
+// whole 36-byte block pairs (pair 4t + G of its row at step t), so after the
+// loads each of the four lane groups holds different blocks; two 4 x 4
+// transposes across the four 16-lane rows (v_permlane16_swap, then
+// v_permlane32_swap) hand lane group G dword G of all eight blocks of the
+// step, and the same transposes gather the eight block scales. Each block
+// takes two MFMAs (x split into fp16 hi + lo), and the fp16 block scale is
+// applied in fp32 to the 16 x 16 partial: acc += d[row, block] * D.
+//
+// Activations are staged per chunk of 512 columns into LDS (double
+// buffered), already split into hi/lo and ordered as the A operands read
+// them; each activation row of a chunk is scaled by a power of two that puts
+// its largest magnitude in [2^14, 2^15) (fp16 range), undone when the chunk's
+// partial sums are added to the accumulator.
+// ---------------------------------------------------------------------------
+constexpr int MM_KC = 512;                        // activation columns per staged chunk
+constexpr int MM_CHUNK_BYTES = (MM_KC / 32) * 2 * 1024;  // blocks x {hi, lo} x 16 rows x 4 slices x 16 B
+
+// 4 x 4 transpose across the four 16-lane rows: on entry lane row R holds
+// v[c] = element (R, c); on exit it holds v[c] = element (c, R).
+__device__ __forceinline__ void xpose4(uint32_t* v) {
+    auto a = __builtin_amdgcn_permlane16_swap(v[0], v[1], false, false);
+    auto b = __builtin_amdgcn_permlane16_swap(v[2], v[3], false, false);
+    auto c = __builtin_amdgcn_permlane32_swap(a[0], b[0], false, false);
+    auto d = __builtin_amdgcn_permlane32_swap(a[1], b[1], false, false);
+    v[0] = c[0];
+    v[2] = c[1];
+    v[1] = d[0];
+    v[3] = d[1];
+}
+
+// Position (in halves) of block element e within its 8-half A/B slice.
+__device__ __forceinline__ int slice_pos(int e) {
+    const int r = e & 3;
+    return ((e >> 4) << 2) + ((r & 1) << 1 | (r >> 1));
+}
+
+template <int WAVES, int TW>
+__global__ __launch_bounds__(WAVES * 64) void k_mm(const uint8_t* __restrict__ W, size_t ldw,
+                                                   const float* __restrict__ X, size_t ldx, float* __restrict__ Y,
+                                                   size_t ldy, int M, int N, int K) {
+    extern __shared__ __align__(16) uint8_t smem[];   // 2 activation chunks
+    __shared__ float s_scale[2][16];                 // per chunk buffer: 2^-s for each activation row
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int G = lane >> 4, j = lane & 15;
+    const int P = K >> 6;
+    const int nchunks = (K + MM_KC - 1) / MM_KC;
+    const long row_base = ((long)blockIdx.x * WAVES + wave) * 16 * TW;
+
+    // ---- activation staging: thread t covers 16 columns of one row ----
+    auto stage = [&](int c, int buf) {
+        uint8_t* dst = smem + buf * MM_CHUNK_BYTES;
+        const int t = threadIdx.x;
+        for (int base = 0; base < 16 * 32; base += WAVES * 64) {
+            const int u = base + t;             // 0..511: row m = u / 32, columns (u % 32) * 16 ..
+            const int m = u >> 5, c0 = (u & 31) * 16;
+            float v[16];
+            float mx = 0.f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int k = c * MM_KC + c0 + e;
+                v[e] = (m < M && k < K) ? X[(size_t)m * ldx + k] : 0.f;
+                mx = fmaxf(mx, fabsf(v[e]));
+            }
+            // max over the 32 threads of this row (a half wave)
+#pragma unroll
+            for (int off = 16; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 32));
+            int sh = 0;
+            if (mx > 0.f && mx <= 3.4e38f) {
+                int ex;
+                frexpf(mx, &ex);
+                sh = 15 - ex;
+                sh = sh > 126 ? 126 : (sh < -126 ? -126 : sh);
+            }
+            if ((u & 31) == 0) s_scale[buf][m] = ldexpf(1.f, -sh);
+            const int blk = c0 >> 5, e0 = c0 & 31;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float xv = ldexpf(v[e], sh);
+                const _Float16 h = (_Float16)xv;
+                const _Float16 l = (_Float16)(xv - (float)h);
+                const int el = e0 + e, g = (el & 15) >> 2;
+                uint8_t* rec = dst + (size_t)blk * 2048 + m * 64 + g * 16 + slice_pos(el) * 2;
+                *reinterpret_cast<_Float16*>(rec) = h;
+                *reinterpret_cast<_Float16*>(rec + 1024) = l;
+            }
+        }
+    };
+
+    // ---- weight loads: one pair per lane per tile per step ----
+    const int steps_per_chunk = MM_KC / 256;
+    const int nsteps = nchunks * steps_per_chunk;
+    auto issue = [&](int step, uint32_t (&b)[TW][9]) {
+#pragma unroll
+        for (int tw = 0; tw < TW; ++tw) {
+            long row = row_base + tw * 16 + j;
+            row = row < N ? row : N - 1;
+            int q = step * 4 + G;
+            q = q < P ? q : P - 1;
+            load_pair<9>(W + row * ldw + (size_t)q * 36, b[tw]);
+        }
+    };
+
+    uint32_t b0[TW][9], b1[TW][9];
+    issue(0, b0);
+    if (nsteps > 1) issue(1, b1);
+    stage(0, 0);
+    __syncthreads();
+
+    f32x4_t acc[TW], cacc[TW];
+#pragma unroll
+    for (int tw = 0; tw < TW; ++tw) {
+        acc[tw] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        cacc[tw] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    }
+
+    auto compute = [&](int step, uint32_t (&r)[TW][9]) {
+        const int c = step / steps_per_chunk, buf = c & 1;
+        const uint8_t* xa = smem + buf * MM_CHUNK_BYTES + (step % steps_per_chunk) * 8 * 2048 + j * 64 + G * 16;
+        const int q = step * 4 + G;
+        const bool valid = q < P;
+#pragma unroll
+        for (int tw = 0; tw < TW; ++tw) {
+            // qs dwords of this lane's two blocks, then hand out slices
+            uint32_t v0[4], v1[4], dd[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                v0[u] = __builtin_amdgcn_alignbyte(r[tw][u + 1], r[tw][u], 2);
+                v1[u] = r[tw][5 + u];
+            }
+            // both block scales (fp16) packed in one dword; zero for pairs past K
+            const uint32_t dpk = valid ? ((r[tw][0] & 0xFFFFu) | (r[tw][4] & 0xFFFF0000u)) : 0u;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) dd[u] = dpk;
+            xpose4(v0);
+            xpose4(v1);
+            xpose4(dd);  // dd[s] = scales of lane group s's pair
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) {
+#pragma unroll
+                for (int R = 0; R < 2; ++R) {
+                    const int blk = 2 * s2 + R;  // block index within the step
+                    const half8_t ah = *reinterpret_cast<const half8_t*>(xa + blk * 2048);
+                    const half8_t al = *reinterpret_cast<const half8_t*>(xa + blk * 2048 + 1024);
+                    const half8_t bq = q4_codes_f16(R ? v1[s2] : v0[s2]);
+                    f32x4_t cc = {0.f, 0.f, 0.f, 0.f};
+                    cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bq, cc, 0, 0, 0);
+                    cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bq, cc, 0, 0, 0);
+                    const float d = R ? half_hi(dd[s2]) : half_lo(dd[s2]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) cacc[tw][i] = fmaf(d, cc[i], cacc[tw][i]);
+                }
+            }
+        }
+        if ((step + 1) % steps_per_chunk == 0 || step + 1 == nsteps) {
+            // fold this chunk's partial sums with the chunk's activation scales
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float sc = s_scale[buf][4 * G + i];
+#pragma unroll
+                for (int tw = 0; tw < TW; ++tw) {
+                    acc[tw][i] = fmaf(sc, cacc[tw][i], acc[tw][i]);
+                    cacc[tw][i] = 0.f;
+                }
+            }
+        }
+    };
+
+    for (int step = 0; step < nsteps; step += 2) {
+        // stage the next chunk while this one is consumed
+        const int c = step / steps_per_chunk;
+        if (step % steps_per_chunk == 0 && c + 1 < nchunks) stage(c + 1, (c + 1) & 1);
+        compute(step, b0);
+        if (step + 2 < nsteps) issue(step + 2, b0);
+        if (step + 1 < nsteps) {
+            compute(step + 1, b1);
+            if (step + 3 < nsteps) issue(step + 3, b1);
+        }
+        if ((step + 2) % steps_per_chunk == 0) __syncthreads();  // chunk c consumed, c + 1 staged
+    }
+    // lane (G, j) holds rows 4G..4G+3 of activation rows, weight row j of each tile
+#pragma unroll
+    for (int tw = 0; tw < TW; ++tw) {
+        const long row = row_base + tw * 16 + j;
+        if (row < N) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = 4 * G + i;
+                if (m < M) Y[(size_t)m * ldy + row] = acc[tw][i];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// M = 2..16, second form: the activations are converted once per call by a
+// small pre-pass into a stream-ordered scratch buffer, already in A-operand
+// order, and every wave loads its A operands straight from there (L2
+// resident, 1 KB contiguous per block and piece), so the main kernel has no
+// LDS staging and no barriers in its K loop.
+//
+// Pre-pass (one workgroup per activation row m < 16): s_m = the power of two
+// that puts max_k |x[m, k]| in [2^14, 2^15) (fp16 range; rows past M are
+// zero), then x * 2^s_m = hi + lo with hi, lo fp16. Scratch layout per block
+// b: piece p (hi, lo) x row m x slice G x 8 halves = 2 KB, then 16 floats
+// with 2^-s_m.
+//
+// Main kernel: a workgroup has S * WR waves; wave (s, rw) owns TW tiles of
+// 16 weight rows and the s-th of S segments of each row's block pairs; the S
+// partial sums meet in LDS once at the end.
+// ---------------------------------------------------------------------------
+// One workgroup per activation row m < 16 (1024 threads, up to XP_PER
+// elements per thread held in registers, so x is read once).
+constexpr int XP_THREADS = 1024, XP_PER = 16;
+constexpr int XP_KMAX = XP_THREADS * XP_PER;
+
+__global__ __launch_bounds__(XP_THREADS) void k_xprep(const float* __restrict__ X, size_t ldx, int M, int K,
+                                                      uint8_t* __restrict__ xa, int* __restrict__ zero_me,
+                                                      int n_zero) {
+    __shared__ float red[XP_THREADS / 64];
+    const int m = blockIdx.x;  // 0..15
+    for (int i = threadIdx.x; i < n_zero && m == 0; i += XP_THREADS) zero_me[i] = 0;
+    float v[XP_PER];
+    float mx = 0.f;
+#pragma unroll
+    for (int e = 0; e < XP_PER; ++e) {
+        const int k = threadIdx.x + e * XP_THREADS;
+        v[e] = (m < M && k < K) ? X[(size_t)m * ldx + k] : 0.f;
+        mx = fmaxf(mx, fabsf(v[e]));
+    }
+    mx = wave_max(mx);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    mx = red[0];
+#pragma unroll
+    for (int w = 1; w < XP_THREADS / 64; ++w) mx = fmaxf(mx, red[w]);
+    int sh = 0;
+    if (mx > 0.f && mx <= 3.4e38f) {
+        int ex;
+        frexpf(mx, &ex);
+        sh = 15 - ex;
+        sh = sh > 126 ? 126 : (sh < -126 ? -126 : sh);
+    }
+    const size_t nb = (size_t)K / 32;
+    if (threadIdx.x == 0) reinterpret_cast<float*>(xa + nb * 2048)[m] = ldexpf(1.f, -sh);
+#pragma unroll
+    for (int e = 0; e < XP_PER; ++e) {
+        const int k = threadIdx.x + e * XP_THREADS;
+        if (k < K) {
+            const float t = ldexpf(v[e], sh);
+            const _Float16 h = (_Float16)t;
+            const _Float16 l = (_Float16)(t - (float)h);
+            const int el = k & 31, g = (el & 15) >> 2;
+            uint8_t* rec = xa + (size_t)(k >> 5) * 2048 + m * 64 + g * 16 + slice_pos(el) * 2;
+            *reinterpret_cast<_Float16*>(rec) = h;
+            *reinterpret_cast<_Float16*>(rec + 1024) = l;
+        }
+    }
+}
+
+struct MmPlan {
+    int S, seg, WR;
+};
+
+template <int TW>
+__global__ __launch_bounds__(512) void k_mm2(const uint8_t* __restrict__ W, size_t ldw, const uint8_t* __restrict__ xa,
+                                             float* __restrict__ Y, size_t ldy, int M, int N, int K, MmPlan plan) {
+    __shared__ f32x4_t red[8][TW][64];
+    const int S = plan.S, seg = plan.seg;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int sgi = wave % S, rw = wave / S;
+    const int G = lane >> 4, j = lane & 15;
+    const int P = K >> 6;
+    const int p0 = sgi * seg;
+    const int p1 = p0 + seg < P ? p0 + seg : P;
+    const int nsteps = (seg + 3) >> 2;
+    const long row_base = ((long)blockIdx.x * plan.WR + rw) * 16 * TW;
+
+    auto issue = [&](int t, uint32_t (&b)[TW][9]) {
+#pragma unroll
+        for (int tw = 0; tw < TW; ++tw) {
+            long row = row_base + tw * 16 + j;
+            row = row < N ? row : N - 1;
+            int q = p0 + 4 * t + G;
+            q = q < p1 ? q : p1 - 1;
+            q = q > 0 ? q : 0;
+            load_pair<9>(W + row * ldw + (size_t)q * 36, b[tw]);
+        }
+    };
+    f32x4_t acc[TW];
+#pragma unroll
+    for (int tw = 0; tw < TW; ++tw) acc[tw] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    const uint8_t* xl = xa + j * 64 + G * 16;  // this lane's A slice within a block record
+
+    auto compute = [&](int t, uint32_t (&r)[TW][9]) {
+        const int qbase = p0 + 4 * t;  // pair of lane group 0
+        uint32_t v0[TW][4], v1[TW][4], dd[TW][4];
+#pragma unroll
+        for (int tw = 0; tw < TW; ++tw) {
+            const bool valid = qbase + G < p1;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                v0[tw][u] = __builtin_amdgcn_alignbyte(r[tw][u + 1], r[tw][u], 2);
+                v1[tw][u] = r[tw][5 + u];
+            }
+            const uint32_t dpk = valid ? ((r[tw][0] & 0xFFFFu) | (r[tw][4] & 0xFFFF0000u)) : 0u;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) dd[tw][u] = dpk;
+            xpose4(v0[tw]);
+            xpose4(v1[tw]);
+            xpose4(dd[tw]);
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+#pragma unroll
+            for (int R = 0; R < 2; ++R) {
+                int blk = 2 * (qbase + s2) + R;  // global block index
+                blk = blk < 2 * P ? blk : 2 * P - 1;
+                const uint8_t* rec = xl + (size_t)blk * 2048;
+                const half8_t ah = *reinterpret_cast<const half8_t*>(rec);
+                const half8_t al = *reinterpret_cast<const half8_t*>(rec + 1024);
+#pragma unroll
+                for (int tw = 0; tw < TW; ++tw) {
+                    const half8_t bq = q4_codes_f16(R ? v1[tw][s2] : v0[tw][s2]);
+                    f32x4_t cc = {0.f, 0.f, 0.f, 0.f};
+                    cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bq, cc, 0, 0, 0);
+                    cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bq, cc, 0, 0, 0);
+                    const float d = R ? half_hi(dd[tw][s2]) : half_lo(dd[tw][s2]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[tw][i] = fmaf(d, cc[i], acc[tw][i]);
+                }
+            }
+        }
+    };
+
+    uint32_t b0[TW][9], b1[TW][9];
+    if (nsteps > 0) issue(0, b0);
+    if (nsteps > 1) issue(1, b1);
+    for (int t = 0; t < nsteps; t += 2) {
+        compute(t, b0);
+        if (t + 2 < nsteps) issue(t + 2, b0);
+        if (t + 1 < nsteps) {
+            compute(t + 1, b1);
+            if (t + 3 < nsteps) issue(t + 3, b1);
+        }
+    }
+    const float* rscale = reinterpret_cast<const float*>(xa + (size_t)(K / 32) * 2048);
+    if (S > 1) {
+#pragma unroll
+        for (int tw = 0; tw < TW; ++tw) red[wave][tw][lane] = acc[tw];
+        __syncthreads();
+        if (sgi != 0) return;
+        for (int q2 = 1; q2 < S; ++q2)
+#pragma unroll
+            for (int tw = 0; tw < TW; ++tw) acc[tw] += red[wave + q2][tw][lane];
+    }
+#pragma unroll
+    for (int tw = 0; tw < TW; ++tw) {
+        const long row = row_base + tw * 16 + j;
+        if (row < N) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = 4 * G + i;
+                if (m < M) Y[(size_t)m * ldy + row] = acc[tw][i] * rscale[m];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// M = 2..16, third form: the eight waves of a workgroup work on eight
+// different 16-row tiles (TW tiles each) over the same K range, so they share
+// the A operands, which are copied chunk by chunk (512 columns = 32 KB) from
+// the converted activations into double-buffered LDS: the next chunk is
+// loaded into registers while the current one is consumed and written to the
+// other buffer before the one barrier per chunk. K is split over
+// grid.y workgroups when there are too few tiles to fill the chip; their
+// partial sums go to scratch and the last workgroup of a tile group (by an
+// atomic arrival count) adds them in segment order, so the result does not
+// depend on timing.
+// ---------------------------------------------------------------------------
+constexpr int MM3_WAVES = 8;
+
+template <int TW>
+__global__ __launch_bounds__(MM3_WAVES * 64) void k_mm3(const uint8_t* __restrict__ W, size_t ldw,
+                                                        const uint8_t* __restrict__ xa, float* __restrict__ Y,
+                                                        size_t ldy, int M, int N, int K, int chunks_per_seg,
+                                                        float* __restrict__ part, int* __restrict__ arrive) {
+    extern __shared__ __align__(16) uint8_t smem[];  // 2 x 32 KB A chunks
+    __shared__ int s_last;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
+    const int G = lane >> 4, j = lane & 15;
+    const int P = K >> 6;
+    const int nchunks = (K + MM_KC - 1) / MM_KC;
+    const int S = gridDim.y, sgi = blockIdx.y;
+    const int c0 = sgi * chunks_per_seg;
+    const int c1 = c0 + chunks_per_seg < nchunks ? c0 + chunks_per_seg : nchunks;
+    const long row_base = ((long)blockIdx.x * MM3_WAVES + wave) * 16 * TW;
+    const size_t xa_bytes = (size_t)(K / 32) * 2048;
+
+    // A chunk c: 16 blocks x 2 KB, contiguous in xa; 512 threads x 4 x 16 B.
+    typedef uint32_t u32x4a __attribute__((ext_vector_type(4)));
+    u32x4a stg[4];
+    auto fetch_a = [&](int c) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            size_t off = (size_t)c * MM_CHUNK_BYTES + (size_t)(i * MM3_WAVES * 64 + tid) * 16;
+            off = off < xa_bytes ? off : 0;  // the tail of the last chunk is never read
+            stg[i] = *reinterpret_cast<const u32x4a*>(xa + off);
+        }
+    };
+    auto put_a = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<u32x4a*>(smem + buf * MM_CHUNK_BYTES + (i * MM3_WAVES * 64 + tid) * 16) = stg[i];
+    };
+
+    auto issue = [&](int step, uint32_t (&b)[TW][9]) {
+#pragma unroll
+        for (int tw = 0; tw < TW; ++tw) {
+            long row = row_base + tw * 16 + j;
+            row = row < N ? row : N - 1;
+            int q = step * 4 + G;
+            q = q < P ? q : P - 1;
+            load_pair<9>(W + row * ldw + (size_t)q * 36, b[tw]);
+        }
+    };
+    f32x4_t acc[TW];
+#pragma unroll
+    for (int tw = 0; tw < TW; ++tw) acc[tw] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](int step, const uint8_t* xbuf, uint32_t (&r)[TW][9]) {
+        const int qbase = step * 4;
+        const bool valid = qbase + G < P;
+        uint32_t v0[TW][4], v1[TW][4], dd[TW][4];
+#pragma unroll
+        for (int tw = 0; tw < TW; ++tw) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                v0[tw][u] = __builtin_amdgcn_alignbyte(r[tw][u + 1], r[tw][u], 2);
+                v1[tw][u] = r[tw][5 + u];
+            }
+            const uint32_t dpk = valid ? ((r[tw][0] & 0xFFFFu) | (r[tw][4] & 0xFFFF0000u)) : 0u;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) dd[tw][u] = dpk;
+            xpose4(v0[tw]);
+            xpose4(v1[tw]);
+            xpose4(dd[tw]);
+        }
+        const uint8_t* xl = xbuf + (step & 1) * 8 * 2048 + j * 64 + G * 16;
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+#pragma unroll
+            for (int R = 0; R < 2; ++R) {
+                const uint8_t* rec = xl + (2 * s2 + R) * 2048;
+                const half8_t ah = *reinterpret_cast<const half8_t*>(rec);
+                const half8_t al = *reinterpret_cast<const half8_t*>(rec + 1024);
+#pragma unroll
+                for (int tw = 0; tw < TW; ++tw) {
+                    const half8_t bq = q4_codes_f16(R ? v1[tw][s2] : v0[tw][s2]);
+                    f32x4_t cc = {0.f, 0.f, 0.f, 0.f};
+                    cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bq, cc, 0, 0, 0);
+                    cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bq, cc, 0, 0, 0);
+                    const float d = R ? half_hi(dd[tw][s2]) : half_lo(dd[tw][s2]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[tw][i] = fmaf(d, cc[i], acc[tw][i]);
+                }
+            }
+        }
+    };
+
+    // Two steps (256 columns each) per chunk; W loads two steps ahead.
+    uint32_t b0[TW][9], b1[TW][9];
+    const int st0 = c0 * 2, st1 = c1 * 2;
+    if (st0 < st1) {
+        issue(st0, b0);
+        issue(st0 + 1, b1);
+        fetch_a(c0);
+        put_a(0);
+    }
+    __syncthreads();
+    for (int c = c0; c < c1; ++c) {
+        const int buf = (c - c0) & 1;
+        if (c + 1 < c1) fetch_a(c + 1);
+        const uint8_t* xbuf = smem + buf * MM_CHUNK_BYTES;
+        compute(2 * c, xbuf, b0);
+        if (2 * c + 2 < st1) issue(2 * c + 2, b0);
+        compute(2 * c + 1, xbuf, b1);
+        if (2 * c + 3 < st1) issue(2 * c + 3, b1);
+        if (c + 1 < c1) put_a(buf ^ 1);
+        __syncthreads();
+    }
+
+    const float* rscale = reinterpret_cast<const float*>(xa + xa_bytes);
+    if (S > 1) {
+        // publish this segment's partial tile sums, then the last arrival adds them
+        float* mine = part + ((size_t)sgi * gridDim.x + blockIdx.x) * (MM3_WAVES * TW * 64 * 4);
+#pragma unroll
+        for (int tw = 0; tw < TW; ++tw)
+            *reinterpret_cast<f32x4_t*>(mine + ((wave * TW + tw) * 64 + lane) * 4) = acc[tw];
+        __threadfence();
+        __syncthreads();
+        if (tid == 0) s_last = atomicAdd(&arrive[blockIdx.x], 1) == S - 1;
+        __syncthreads();
+        if (!s_last) return;
+        __threadfence();
+#pragma unroll
+        for (int tw = 0; tw < TW; ++tw) acc[tw] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        for (int q2 = 0; q2 < S; ++q2) {
+            const float* pp = part + ((size_t)q2 * gridDim.x + blockIdx.x) * (MM3_WAVES * TW * 64 * 4);
+#pragma unroll
+            for (int tw = 0; tw < TW; ++tw)
+                acc[tw] += __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(pp + ((wave * TW + tw) * 64 + lane) * 4));
+        }
+    }
+#pragma unroll
+    for (int tw = 0; tw < TW; ++tw) {
+        const long row = row_base + tw * 16 + j;
+        if (row < N) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = 4 * G + i;
+                if (m < M) Y[(size_t)m * ldy + row] = acc[tw][i] * rscale[m];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Generic kernel: any qtype, 1..MT rows of X, 2-byte alignment, any K % 32.
 // One wave per weight row (4 waves per workgroup), one block per lane step.
 // ---------------------------------------------------------------------------
@@ -1118,6 +1651,120 @@ int launch_m1b(const M1Prob* probs, int n, int wgs_per_cu, int waves, hipStream_
     return check_launch("qmv batched m1 kernel");
 }
 
+// M = 2..16 on the matrix cores (Q4_0, K % 64 == 0, 4-byte aligned rows).
+template <int WAVES, int TW>
+int launch_mm_t(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N, int K,
+                hipStream_t st) {
+    const long rows_wg = 16L * TW * WAVES;
+    const long grid = ((long)N + rows_wg - 1) / rows_wg;
+    if (grid > 0x7FFFFFFF) return fail(QMV_EINVAL, "N too large");
+    hipLaunchKernelGGL((k_mm<WAVES, TW>), dim3((unsigned)grid), dim3(WAVES * 64), 2 * MM_CHUNK_BYTES, st, W, ldw, X,
+                       ldx, Y, ldy, M, N, K);
+    return check_launch("qmv mfma kernel");
+}
+
+int launch_mm(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N, int K,
+              int waves, int tw, hipStream_t st) {
+    if (waves == 0) {
+        // enough workgroups to cover the chip; more rows per wave when there are plenty
+        const long tiles = ((long)N + 15) / 16;
+        waves = 4;
+        tw = tiles >= 4L * 4 * num_cus() ? 2 : 1;
+    }
+    if (waves == 4 && tw == 1) return launch_mm_t<4, 1>(W, ldw, X, ldx, Y, ldy, M, N, K, st);
+    if (waves == 4 && tw == 2) return launch_mm_t<4, 2>(W, ldw, X, ldx, Y, ldy, M, N, K, st);
+    if (waves == 8 && tw == 1) return launch_mm_t<8, 1>(W, ldw, X, ldx, Y, ldy, M, N, K, st);
+    if (waves == 8 && tw == 2) return launch_mm_t<8, 2>(W, ldw, X, ldx, Y, ldy, M, N, K, st);
+    return fail(QMV_EINVAL, "internal: no mfma kernel for waves=%d tw=%d", waves, tw);
+}
+
+// M = 2..16 with the activation pre-pass; returns QMV_EUNSUPPORTED (nothing
+// enqueued) when the scratch buffer cannot be allocated, so the caller can
+// fall back to the staging kernel.
+int launch_mm2(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N, int K,
+               int force_S, int force_tw, hipStream_t st) {
+    if (K > XP_KMAX) return QMV_EUNSUPPORTED;
+    const size_t bytes = (size_t)(K / 32) * 2048 + 64;
+    void* xa = nullptr;
+    if (hipMallocAsync(&xa, bytes, st) != hipSuccess || !xa) {
+        (void)hipGetLastError();
+        return QMV_EUNSUPPORTED;
+    }
+    hipLaunchKernelGGL(k_xprep, dim3(16), dim3(XP_THREADS), 0, st, X, ldx, M, K, (uint8_t*)xa, (int*)nullptr, 0);
+    int rc = check_launch("qmv activation pre-pass");
+    if (rc == QMV_OK) {
+        const long tiles = ((long)N + 15) / 16;
+        const int ncu = num_cus();
+        int tw = force_tw ? force_tw : (tiles >= 8L * ncu ? 2 : 1);
+        const long groups = (tiles + tw - 1) / tw;
+        const int P = K / 64;
+        int S = 1;
+        while (S < 8 && groups * S < 4L * ncu && (P + 2 * S - 1) / (2 * S) >= 4) S *= 2;
+        if (force_S) S = force_S;
+        MmPlan pl;
+        pl.S = S;
+        pl.seg = (P + S - 1) / S;
+        pl.WR = 8 / S > 0 ? (S >= 8 ? 1 : 8 / S) : 1;
+        if (pl.WR > 2 && groups < (long)ncu * pl.WR) pl.WR = 2;
+        const long grid = (groups + pl.WR - 1) / pl.WR;
+        if (tw == 2)
+            hipLaunchKernelGGL((k_mm2<2>), dim3((unsigned)grid), dim3(64 * pl.S * pl.WR), 0, st, W, ldw, (const uint8_t*)xa, Y,
+                               ldy, M, N, K, pl);
+        else
+            hipLaunchKernelGGL((k_mm2<1>), dim3((unsigned)grid), dim3(64 * pl.S * pl.WR), 0, st, W, ldw, (const uint8_t*)xa, Y,
+                               ldy, M, N, K, pl);
+        rc = check_launch("qmv mfma kernel");
+    }
+    if (hipFreeAsync(xa, st) != hipSuccess && rc == QMV_OK) rc = fail(QMV_EHIP, "qmv: hipFreeAsync failed");
+    return rc;
+}
+
+// M = 2..16: activation pre-pass + k_mm3. Returns QMV_EUNSUPPORTED (nothing
+// enqueued) when the shape is out of its range or scratch is unavailable.
+int launch_mm3(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N, int K,
+               int force_S, int force_tw, hipStream_t st) {
+    if (K > XP_KMAX) return QMV_EUNSUPPORTED;
+    const int ncu = num_cus();
+    const long tiles = ((long)N + 15) / 16;
+    const int tw = force_tw ? force_tw : (tiles >= 2L * MM3_WAVES * 2 * ncu ? 2 : 1);
+    const long groups = (tiles + (long)MM3_WAVES * tw - 1) / ((long)MM3_WAVES * tw);
+    const int nchunks = (K + MM_KC - 1) / MM_KC;
+    // Split-K across workgroups needs a device-wide release per workgroup,
+    // which costs far more than it saves on this chip: one segment by default.
+    int S = 1;
+    if (force_S) S = force_S;
+    S = S > nchunks ? nchunks : S;
+    const int cps = (nchunks + S - 1) / S;
+    S = (nchunks + cps - 1) / cps;
+    if (groups > 0x7FFFFFFF || S > 65535) return QMV_EUNSUPPORTED;
+    const size_t xa_bytes = (size_t)(K / 32) * 2048 + 64;
+    const size_t part_bytes = S > 1 ? (size_t)S * groups * MM3_WAVES * tw * 64 * 16 : 0;
+    const size_t arr_bytes = S > 1 ? (size_t)groups * 4 : 0;
+    const size_t off_part = (xa_bytes + 255) & ~(size_t)255;
+    const size_t off_arr = (off_part + part_bytes + 255) & ~(size_t)255;
+    void* scratch = nullptr;
+    if (hipMallocAsync(&scratch, off_arr + arr_bytes + 256, st) != hipSuccess || !scratch) {
+        (void)hipGetLastError();
+        return QMV_EUNSUPPORTED;
+    }
+    uint8_t* xa = (uint8_t*)scratch;
+    float* part = (float*)(xa + off_part);
+    int* arrive = (int*)(xa + off_arr);
+    hipLaunchKernelGGL(k_xprep, dim3(16), dim3(XP_THREADS), 0, st, X, ldx, M, K, xa, arrive, (int)(arr_bytes / 4));
+    int rc = check_launch("qmv activation pre-pass");
+    if (rc == QMV_OK) {
+        if (tw == 2)
+            hipLaunchKernelGGL((k_mm3<2>), dim3((unsigned)groups, (unsigned)S), dim3(MM3_WAVES * 64), 2 * MM_CHUNK_BYTES, st, W,
+                               ldw, (const uint8_t*)xa, Y, ldy, M, N, K, cps, part, arrive);
+        else
+            hipLaunchKernelGGL((k_mm3<1>), dim3((unsigned)groups, (unsigned)S), dim3(MM3_WAVES * 64), 2 * MM_CHUNK_BYTES, st, W,
+                               ldw, (const uint8_t*)xa, Y, ldy, M, N, K, cps, part, arrive);
+        rc = check_launch("qmv mfma kernel");
+    }
+    if (hipFreeAsync(scratch, st) != hipSuccess && rc == QMV_OK) rc = fail(QMV_EHIP, "qmv: hipFreeAsync failed");
+    return rc;
+}
+
 template <int QT>
 int launch_generic(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N,
                    int K, hipStream_t st) {
@@ -1169,6 +1816,13 @@ int dense(int qtype, const void* Wv, size_t ldw, const float* X, size_t ldx, flo
     if (fast_ok) {
         return qtype == QMV_Q4_0 ? launch_m1<QMV_Q4_0>(W, ldw, X, Y, N, K, st)
                                  : launch_m1<QMV_Q8_0>(W, ldw, X, Y, N, K, st);
+    }
+    const bool mm_ok = qtype == QMV_Q4_0 && M >= 2 && K > 0 && K % 64 == 0 && ((uintptr_t)W & 3) == 0 &&
+                       (ldw & 3) == 0 && ((uintptr_t)X & 3) == 0;
+    if (mm_ok) {
+        const int rc = launch_mm3(W, ldw, X, ldx, Y, ldy, M, N, K, 0, 0, st);
+        if (rc != QMV_EUNSUPPORTED) return rc;
+        return launch_mm(W, ldw, X, ldx, Y, ldy, M, N, K, 0, 0, st);
     }
     return qtype == QMV_Q4_0 ? launch_generic<QMV_Q4_0>(W, ldw, X, ldx, Y, ldy, M, N, K, st)
                              : launch_generic<QMV_Q8_0>(W, ldw, X, ldx, Y, ldy, M, N, K, st);
@@ -1380,6 +2034,21 @@ int qmv_probe_m1b(int qtype, int waves, int wgs_per_cu, int n, const void* const
     }
     return qtype == QMV_Q4_0 ? launch_m1b<QMV_Q4_0>(pr, n, wgs_per_cu, waves, (hipStream_t)stream)
                              : launch_m1b<QMV_Q8_0>(pr, n, wgs_per_cu, waves, (hipStream_t)stream);
+}
+
+int qmv_probe_mm(int waves, int tw, const void* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M,
+                 int N, int K, void* stream) {
+    return launch_mm((const uint8_t*)W, ldw, X, ldx, Y, ldy, M, N, K, waves, tw, (hipStream_t)stream);
+}
+
+int qmv_probe_mm2(int S, int tw, const void* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M,
+                  int N, int K, void* stream) {
+    return launch_mm2((const uint8_t*)W, ldw, X, ldx, Y, ldy, M, N, K, S, tw, (hipStream_t)stream);
+}
+
+int qmv_probe_mm3(int S, int tw, const void* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M,
+                  int N, int K, void* stream) {
+    return launch_mm3((const uint8_t*)W, ldw, X, ldx, Y, ldy, M, N, K, S, tw, (hipStream_t)stream);
 }
 #endif
 
