@@ -207,11 +207,29 @@ __device__ __forceinline__ void load_pair(const uint8_t* p, uint32_t* r) {
 // LDS layout of the staged activation row: 64 floats per pair of blocks,
 // padded to 68 so that lanes reading different pairs use different banks.
 constexpr int XS_PAIR = 68;
+constexpr int KMAX_STAGE = 15360;  // largest K staged into LDS by the M = 1 kernels
 
 __host__ __device__ constexpr size_t xs_bytes(int K) { return (size_t)(K / 64) * XS_PAIR * sizeof(float); }
 
+// NT threads copy x (K % 4 == 0, K <= 4 * NT * XCH) into the padded layout:
+// every thread first issues all of its 16-byte loads, then stores them, so
+// the copy costs one memory latency instead of one per element.
+template <int NT, int XCH>
 __device__ __forceinline__ void stage_x(float* xs, const float* __restrict__ x, int K) {
-    for (int k = threadIdx.x; k < K; k += blockDim.x) xs[(k >> 6) * XS_PAIR + (k & 63)] = x[k];
+    typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
+    const int nch = K >> 2;
+    f32x4u v[XCH];
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+        const int c = threadIdx.x + i * NT;
+        if (c < nch) v[i] = *reinterpret_cast<const f32x4u*>(x + 4 * c);
+    }
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+        const int c = threadIdx.x + i * NT;
+        if (c < nch)
+            *reinterpret_cast<float4*>(xs + (c >> 4) * XS_PAIR + 4 * (c & 15)) = make_float4(v[i].x, v[i].y, v[i].z, v[i].w);
+    }
 }
 
 // v + (v of another lane chosen by a DPP control); lanes outside row_mask
@@ -274,7 +292,7 @@ __device__ __forceinline__ void m1_stream(const uint8_t* __restrict__ W, size_t 
         }
     };
     issue(tile, 0);
-    stage_x(xs, x, K);
+    stage_x<WAVES * 64, (KMAX_STAGE / 4 + WAVES * 64 - 1) / (WAVES * 64)>(xs, x, K);
     __syncthreads();
     float tot[RPT];
 #pragma unroll
@@ -364,73 +382,156 @@ __device__ __forceinline__ float group_sum_dyn(float v, int lpr) {
 
 template <int QT, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void k_m1b(const M1Batch B) {
+    extern __shared__ __align__(16) float xs[];
+    int pi = 0;
+    while (pi + 1 < B.n && (int)blockIdx.x >= B.p[pi + 1].wg0) ++pi;
+    const uint8_t* W = B.p[pi].W;
+    const float* x = B.p[pi].x;
+    float* y = B.p[pi].y;
+    const size_t ldw = B.p[pi].ldw;
+    const int N = B.p[pi].N, K = B.p[pi].K;
+    const long lw = blockIdx.x - B.p[pi].wg0, nwg = B.p[pi].nwg;
+    constexpr float OS = PairTraits<QT>::OUT_SCALE;
+    switch (B.p[pi].lpr) {
+        case 64: m1_stream<QT, 64, 1, WAVES>(W, ldw, x, y, N, K, lw, nwg, OS, xs); break;
+        case 32: m1_stream<QT, 32, 1, WAVES>(W, ldw, x, y, N, K, lw, nwg, OS, xs); break;
+        case 16: m1_stream<QT, 16, 1, WAVES>(W, ldw, x, y, N, K, lw, nwg, OS, xs); break;
+        case 8: m1_stream<QT, 8, 1, WAVES>(W, ldw, x, y, N, K, lw, nwg, OS, xs); break;
+        default: m1_stream<QT, 4, 1, WAVES>(W, ldw, x, y, N, K, lw, nwg, OS, xs); break;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// M = 1 one-shot kernel, batched: every wave issues all of its weight loads
+// at once, so the whole product costs about one memory latency plus the
+// transfer time, and no weight load waits behind arithmetic or a barrier.
+//
+// Lanes: LPR lanes per row (G = 64 / LPR rows per row group); lane j of a
+// group owns ONE pair of blocks (64 activations) of the row, pair
+// sg * seg + j, where sg is the wave's segment of K. Rows with more than 64
+// pairs are cut into S segments handled by S waves of the workgroup, whose
+// partial sums meet in LDS (added in segment order). A row wave owns at most
+// MAXI consecutive row groups; all their pair loads (36 or 68 bytes per lane
+// each) are issued before anything waits. The activations are read in this
+// order: each thread loads its share of x first, then the weights; x goes
+// through LDS (once per workgroup) into each lane's registers (its own 64
+// values), and every weight pair is reduced as soon as it lands.
+// ---------------------------------------------------------------------------
+constexpr int MO_WAVES = 8;
+constexpr int MO_XCH = 8;  // float4 chunks of x per thread
+constexpr int MO_KMAX = MO_WAVES * 64 * MO_XCH * 4;
+
+struct OsProb {
+    const uint8_t* W;
+    const float* x;
+    float* y;
+    size_t ldw;
+    int N, K;
+    int lpr, S;  // lanes per row; K segments (waves) per row group
+    int wg0, nwg;
+};
+struct OsBatch {
+    OsProb p[MAXB];
+    int n;
+};
+
+template <int QT, int MAXI>
+__global__ __launch_bounds__(MO_WAVES * 64) void k_m1o(const OsBatch B) {
     using T = PairTraits<QT>;
     constexpr int DW = T::DW, PB = DW * 4;
+    typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
     extern __shared__ __align__(16) float xs[];
+    __shared__ float red[MO_WAVES][MAXI];
     int pi = 0;
     while (pi + 1 < B.n && (int)blockIdx.x >= B.p[pi + 1].wg0) ++pi;
     const uint8_t* __restrict__ W = B.p[pi].W;
     const float* __restrict__ x = B.p[pi].x;
     float* __restrict__ y = B.p[pi].y;
     const size_t ldw = B.p[pi].ldw;
-    const int N = B.p[pi].N, K = B.p[pi].K, LPR = B.p[pi].lpr;
-    const int lw = blockIdx.x - B.p[pi].wg0;
-    const long T_waves = (long)B.p[pi].nwg * WAVES;
+    const int N = B.p[pi].N, K = B.p[pi].K, LPR = B.p[pi].lpr, S = B.p[pi].S;
+    const int lw = blockIdx.x - B.p[pi].wg0, nwg = B.p[pi].nwg;
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int GROUPS = 64 / LPR;
-    const int g = lane / LPR, j = lane % LPR;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int sg = wave % S, rw = wave / S, R = MO_WAVES / S;
+    const int GR = 64 / LPR, g = lane / LPR, j = lane % LPR;
     const int P = K >> 6;
-    const int IPT = (P + LPR - 1) / LPR;
-    const long RG = ((long)N + GROUPS - 1) / GROUPS;
-    const long gw = (long)lw * WAVES + wave;
-    const long rg0 = RG * gw / T_waves, rg1 = RG * (gw + 1) / T_waves;
-    const long nitems = (rg1 - rg0) * IPT;
+    const int seg = (P + S - 1) / S;
+    const int p = sg * seg + j;
+    const bool active = j < seg && p < P;
+    const int pc = active ? p : P - 1;
+    const long RG = ((long)N + GR - 1) / GR;
+    const long TR = (long)nwg * R, gr = (long)lw * R + rw;
+    const long rg0 = RG * gr / TR, rg1 = RG * (gr + 1) / TR;
+    const int nr = (int)(rg1 - rg0);  // <= MAXI (host plan)
 
-    long irg = rg0;
-    int iit = 0;
-    long issued = 0;
-    auto issue = [&](uint32_t (&b)[DW]) {
-        if (issued < nitems) {
-            long row = irg * GROUPS + g;
-            row = row < N ? row : N - 1;
-            int p = j + iit * LPR;
-            p = p < P ? p : P - 1;
-            load_pair<DW>(W + row * ldw + (size_t)p * PB, b);
+    // 1. this thread's share of x
+    // (unconditional, clamped, so the compiler can count them and later
+    // wait for x alone while the weight loads stay in flight)
+    f32x4u xv[MO_XCH];
+    const int nch = K >> 2;
+#pragma unroll
+    for (int i = 0; i < MO_XCH; ++i) {
+        const int c = tid + i * MO_WAVES * 64;
+        xv[i] = *reinterpret_cast<const f32x4u*>(x + 4 * (c < nch ? c : nch - 1));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // 2. every weight pair this lane will use
+    // (branch-free: surplus slots reload the wave's last row group)
+    uint32_t b[MAXI][DW];
+    const int last = nr > 0 ? nr - 1 : 0;
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) {
+        long row = (rg0 + (i < last ? i : last)) * GR + g;
+        row = row < N ? row : N - 1;
+        load_pair<DW>(W + row * ldw + (size_t)pc * PB, b[i]);
+    }
+    // Nothing that needs weight data may be scheduled above the x staging.
+    __builtin_amdgcn_sched_barrier(0);
+    // 3. x into LDS (pairs padded to XS_PAIR floats), then this lane's pair;
+    // surplus chunks rewrite the last chunk's slot with the same values.
+#pragma unroll
+    for (int i = 0; i < MO_XCH; ++i) {
+        int c = tid + i * MO_WAVES * 64;
+        c = c < nch ? c : nch - 1;
+        const int k = 4 * c;
+        *reinterpret_cast<float4*>(xs + (k >> 6) * XS_PAIR + (k & 63)) = make_float4(xv[i].x, xv[i].y, xv[i].z, xv[i].w);
+    }
+    // LDS-only barrier: __syncthreads() would also wait for every weight load
+    // in flight (vmcnt(0)), which is exactly what this kernel avoids.
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    float4 xr[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) xr[i] = reinterpret_cast<const float4*>(xs + pc * XS_PAIR)[i];
+    // 4. reduce each pair as it lands
+    float v[MAXI];
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) {
+        const float d = T::dot(b[i], xr);
+        v[i] = group_sum_dyn(active ? d : 0.f, LPR);
+    }
+    if (S == 1) {
+        if (j == LPR - 1) {
+#pragma unroll
+            for (int i = 0; i < MAXI; ++i) {
+                const long row = (rg0 + i) * GR + g;
+                if (i < nr && row < N) y[row] = v[i] * T::OUT_SCALE;
+            }
         }
-        ++issued;
-        if (++iit == IPT) {
-            iit = 0;
-            ++irg;
-        }
-    };
-    uint32_t b0[DW], b1[DW];
-    issue(b0);
-    issue(b1);
-    stage_x(xs, x, K);
+        return;
+    }
+    if (lane == 63) {
+#pragma unroll
+        for (int i = 0; i < MAXI; ++i) red[wave][i] = v[i];
+    }
     __syncthreads();
-
-    long prg = rg0;
-    int pit = 0;
-    float tot = 0.f;
-    auto process = [&](const uint32_t (&r)[DW]) {
-        const int p = j + pit * LPR;
-        if (p < P) tot += T::dot(r, reinterpret_cast<const float4*>(xs + p * XS_PAIR));
-        if (++pit == IPT) {
-            const float sum = group_sum_dyn(tot, LPR);
-            const long row = prg * GROUPS + g;
-            if (j == LPR - 1 && row < N) y[row] = sum * T::OUT_SCALE;
-            tot = 0.f;
-            pit = 0;
-            ++prg;
-        }
-    };
-    for (long it = 0; it < nitems; it += 2) {
-        process(b0);
-        issue(b0);
-        if (it + 1 < nitems) {
-            process(b1);
-            issue(b1);
+    if (sg == 0 && lane == 63) {
+#pragma unroll
+        for (int i = 0; i < MAXI; ++i) {
+            float t = v[i];
+            for (int s2 = 1; s2 < S; ++s2) t += red[wave + s2][i];
+            const long row = rg0 + i;
+            if (i < nr && row < N) y[row] = t * T::OUT_SCALE;
         }
     }
 }
@@ -766,6 +867,256 @@ MhPlan make_mh_plan(int N, int K, int ncu, int target_waves_per_cu) {
     pl.seg = (P + S - 1) / S;
     pl.WR = S >= 8 ? 1 : 8 / S;
     return pl;
+}
+
+// ---------------------------------------------------------------------------
+// Q4_0 codes as matrix-core operands. One qs dword holds 8 codes: the low
+// nibbles of its bytes are block elements 4u..4u+3, the high nibbles elements
+// 16+4u..16+4u+3 (u = the dword's index in the block). q4_dec turns them
+// into eight exact fp16 values code - 8 in the order
+//   [4u, 4u+2, 4u+1, 4u+3, 16+4u, 16+4u+2, 16+4u+1, 16+4u+3].
+// A low nibble n as the low byte of an fp16 whose high byte is 0x64 reads as
+// 1024 + n; a high nibble left in bits 4..7 under the high byte 0x54 reads as
+// 64 + n. v_perm_b32 builds both pairs of a dword from the masked code bytes
+// and a register holding the two high bytes, and one packed fp16 add removes
+// the offset exactly: 2 AND, 4 v_perm_b32 and 4 v_pk_add_f16 per dword.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ half8_t q4_dec(uint32_t q) {
+    const half2_t blo = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    const half2_t bhi = {(_Float16)-72.0f, (_Float16)-72.0f};
+    const uint32_t EXPB = 0x5464u;  // byte 4 of {EXPB, v} = 0x64, byte 5 = 0x54
+    const uint32_t lo = q & 0x0F0F0F0Fu, hi = q & 0xF0F0F0F0u;
+    const half2_t t0 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(EXPB, lo, 0x04020400u)) + blo;
+    const half2_t t1 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(EXPB, lo, 0x04030401u)) + blo;
+    const half2_t t2 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(EXPB, hi, 0x05020500u)) + bhi;
+    const half2_t t3 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(EXPB, hi, 0x05030501u)) + bhi;
+    return (half8_t){t0[0], t0[1], t1[0], t1[1], t2[0], t2[1], t3[0], t3[1]};
+}
+
+// ---------------------------------------------------------------------------
+// M = 1 Q4_0 on the matrix cores, batched (one launch serves up to 16
+// independent products y_p = W_p x_p).
+//
+// A wave owns a tile of 16 weight rows (MFMA column n = lane % 16) and a
+// segment of each row's block pairs; lane group G = lane / 16 streams pair
+// p0 + 4t + G of row n at step t (36 bytes). For block R of that pair, MFMA u
+// (u = 0..3) takes qs dword u of the lane's block as its B slice G. The A
+// operand is block diagonal: row 4G holds the hi and row 4G + 1 the lo fp16
+// part of the eight activations that slice G multiplies, every other entry is
+// zero, so after the four MFMAs lane (G, n) holds in D rows 4G and 4G + 1 the
+// block's dot product for row n, and the block's scale is applied in fp32.
+// The multiply-adds run on the matrix cores; the vector ALUs only unpack
+// codes (about 1.3 instructions per weight).
+//
+// Activations: each workgroup converts its problem's x once, in one pass,
+// into LDS records laid out as the A operands read them (MQ_PAIR bytes per
+// pair of blocks: block R x dword u x {hi, lo} x 8 fp16, then the two blocks'
+// factors 2^-s, then padding that staggers consecutive pairs over the LDS
+// banks). Block b is scaled by the power of two 2^s that brings its largest
+// |x| into [2^14, 2^15) and split as x * 2^s = hi + lo; fp16 products are
+// exact in fp32 and hi + lo keeps 22 bits of every activation. One zero
+// record after the last pair stands in for pairs past the end of a row.
+//
+// Work split: a tile's pairs are cut into S segments (S waves per tile,
+// T = WAVES / S tiles per workgroup pass); segment partial sums meet in LDS
+// and are added in segment order, so results do not depend on timing. The
+// grid is persistent: workgroup w of a problem takes tile groups w, w + nwg,
+// ... Weight loads run two steps ahead of the arithmetic.
+// ---------------------------------------------------------------------------
+constexpr int MQ_PAIR = 288;
+constexpr int MQ_KMAX = 32768;
+
+__host__ __device__ constexpr size_t mq_lds_bytes(int K) { return (size_t)(K / 64 + 1) * MQ_PAIR; }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float v) {
+    const int t = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false);
+    return fmaxf(v, __builtin_bit_cast(float, t));
+}
+
+__device__ __forceinline__ uint32_t pack_h2(_Float16 a, _Float16 b) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// Converts x[0..K) (K % 64 == 0) into the A-operand records at xs. Four
+// consecutive threads share a block: thread u of it holds the activations of
+// qs dword u (elements 4u..4u+3 and 16+4u..16+4u+3). Ends without a barrier.
+__device__ __forceinline__ void stage_xq(uint8_t* xs, const float* __restrict__ x, int K) {
+    typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
+    const int nb = K >> 5;
+    for (int i = threadIdx.x; i < nb * 4; i += blockDim.x) {
+        const int b = i >> 2, u = i & 3;
+        const f32x4u l4 = *reinterpret_cast<const f32x4u*>(x + (size_t)b * 32 + 4 * u);
+        const f32x4u h4 = *reinterpret_cast<const f32x4u*>(x + (size_t)b * 32 + 16 + 4 * u);
+        const float v[8] = {l4.x, l4.z, l4.y, l4.w, h4.x, h4.z, h4.y, h4.w};
+        float m = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
+        m = dpp_max<0xB1>(m);  // quad_perm [1,0,3,2]
+        m = dpp_max<0x4E>(m);  // quad_perm [2,3,0,1]
+        int s = 0;
+        if (m > 0.f && m <= 3.4e38f) {
+            int ex;
+            frexpf(m, &ex);  // m in [2^(ex-1), 2^ex)
+            s = 15 - ex;
+            s = s > 126 ? 126 : (s < -126 ? -126 : s);
+        }
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            _Float16 h[2], l[2];
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const float a = ldexpf(v[2 * k + c], s);
+                h[c] = (_Float16)a;
+                float r = a - (float)h[c];
+                r = r == r ? r : 0.f;  // hi = +-inf or nan carries the value alone
+                l[c] = (_Float16)r;
+            }
+            hw[k] = pack_h2(h[0], h[1]);
+            lw[k] = pack_h2(l[0], l[1]);
+        }
+        uint8_t* rec = xs + (size_t)(b >> 1) * MQ_PAIR + (b & 1) * 128 + u * 32;
+        *reinterpret_cast<u32x4*>(rec) = (u32x4){hw[0], hw[1], hw[2], hw[3]};
+        *reinterpret_cast<u32x4*>(rec + 16) = (u32x4){lw[0], lw[1], lw[2], lw[3]};
+        if (u == 0) *reinterpret_cast<float*>(xs + (size_t)(b >> 1) * MQ_PAIR + 256 + (b & 1) * 4) = ldexpf(1.f, -s);
+    }
+    uint8_t* zr = xs + (size_t)(K >> 6) * MQ_PAIR;
+    for (int i = threadIdx.x; i < MQ_PAIR / 16; i += blockDim.x)
+        *reinterpret_cast<u32x4*>(zr + 16 * i) = (u32x4){0u, 0u, 0u, 0u};
+}
+
+struct MqProb {
+    const uint8_t* W;
+    const float* x;
+    float* y;
+    size_t ldw;
+    int N, K;
+    int S;     // segments per tile (divides WAVES)
+    int segP;  // pairs per segment
+    int wg0, nwg;
+};
+struct MqBatch {
+    MqProb p[MAXB];
+    int n;
+};
+
+template <int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void k_m1q(const MqBatch B) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    uint8_t* xs = smem;
+    __shared__ float red[2][WAVES][16];
+    int pi = 0;
+    while (pi + 1 < B.n && (int)blockIdx.x >= B.p[pi + 1].wg0) ++pi;
+    const uint8_t* __restrict__ W = B.p[pi].W;
+    const float* __restrict__ x = B.p[pi].x;
+    float* __restrict__ y = B.p[pi].y;
+    const size_t ldw = B.p[pi].ldw;
+    const int N = B.p[pi].N, K = B.p[pi].K, S = B.p[pi].S, segP = B.p[pi].segP;
+    const int lw = blockIdx.x - B.p[pi].wg0, nwg = B.p[pi].nwg;
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int G = lane >> 4, n = lane & 15;
+    const int T = WAVES / S;
+    const int ts = wave / S, sg = wave % S;
+    const int P = K >> 6;
+    const int p0 = sg * segP;
+    const int nsteps = (segP + 3) >> 2;
+    const long ntiles = ((long)N + 15) / 16;
+    const long ntg = (ntiles + T - 1) / T;
+    const long nk = lw < ntg ? (ntg - lw + nwg - 1) / nwg : 0;
+    const long nitems = nk * nsteps;  // the same for every wave of the workgroup
+    const bool a_lane = (n >> 2) == G && (n & 3) < 2;
+    const int a_off = (n & 1) * 16;  // hi or lo piece
+
+    long ik = 0;
+    int ist = 0;
+    long issued = 0;
+    auto issue = [&](uint32_t (&b)[9]) {
+        if (issued < nitems) {
+            const long tile = (lw + ik * nwg) * T + ts;
+            long row = tile * 16 + n;
+            row = row < N ? row : N - 1;
+            int p = p0 + 4 * ist + G;
+            p = p < P ? p : P - 1;
+            load_pair<9>(W + row * ldw + (size_t)p * 36, b);
+        }
+        ++issued;
+        if (++ist == nsteps) {
+            ist = 0;
+            ++ik;
+        }
+    };
+    uint32_t b0[9], b1[9];
+    issue(b0);
+    issue(b1);
+    stage_xq(xs, x, K);
+    __syncthreads();
+
+    half8_t a0[4], a1[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        a0[u] = (half8_t){0, 0, 0, 0, 0, 0, 0, 0};
+        a1[u] = a0[u];
+    }
+    float acc = 0.f;
+    long pk = 0;
+    int pst = 0, parity = 0;
+    auto process = [&](const uint32_t (&r)[9]) {
+        const int q = 4 * pst + G;
+        const int p = p0 + q;
+        const bool valid = q < segP && p < P;
+        const uint8_t* rec = xs + (size_t)(valid ? p : P) * MQ_PAIR;
+        if (a_lane) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                a0[u] = *reinterpret_cast<const half8_t*>(rec + u * 32 + a_off);
+                a1[u] = *reinterpret_cast<const half8_t*>(rec + 128 + u * 32 + a_off);
+            }
+        }
+        const float2 xsc = *reinterpret_cast<const float2*>(rec + 256);
+        f32x4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0[u], q4_dec(__builtin_amdgcn_alignbyte(r[u + 1], r[u], 2)),
+                                                        c0, 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1[u], q4_dec(r[5 + u]), c1, 0, 0, 0);
+        const float s0 = valid ? half_lo(r[0]) * xsc.x : 0.f;
+        const float s1 = valid ? half_hi(r[4]) * xsc.y : 0.f;
+        acc = fmaf(s0, c0[0] + c0[1], acc);
+        acc = fmaf(s1, c1[0] + c1[1], acc);
+        if (++pst == nsteps) {
+            float v = acc + __shfl_xor(acc, 16, 64);
+            v += __shfl_xor(v, 32, 64);
+            acc = 0.f;
+            const long tile = (lw + pk * nwg) * T + ts;
+            const long row = tile * 16 + n;
+            const bool ok = tile < ntiles && row < N;
+            if (S == 1) {
+                if (G == 0 && ok) y[row] = v;
+            } else {
+                if (G == 0) red[parity][wave][n] = v;
+                __syncthreads();
+                if (sg == 0 && G == 0 && ok) {
+                    float t = v;
+                    for (int s2 = 1; s2 < S; ++s2) t += red[parity][wave + s2][n];
+                    y[row] = t;
+                }
+                parity ^= 1;
+            }
+            pst = 0;
+            ++pk;
+        }
+    };
+    for (long it = 0; it < nitems; it += 2) {
+        process(b0);
+        issue(b0);
+        if (it + 1 < nitems) {
+            process(b1);
+            issue(b1);
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1519,7 +1870,7 @@ M1Cfg pick_m1(int N, int K) {
     c.lpr = pick_lpr(K / 64);
     c.rpt = 1;
     c.waves = 8;
-    c.wgs_per_cu = 4;
+    c.wgs_per_cu = 2;
     (void)N;
     return c;
 }
@@ -1615,6 +1966,7 @@ bool m1b_eligible(const uint8_t* W, size_t ldw, const float* x, int K) {
 template <int QT>
 int launch_m1b(const M1Prob* probs, int n, int wgs_per_cu, int waves, hipStream_t st) {
     if (waves == 0) waves = 8;
+    if (wgs_per_cu == 0) wgs_per_cu = 2;
     M1Batch B;
     B.n = 0;
     size_t lds = 0;
@@ -1622,33 +1974,172 @@ int launch_m1b(const M1Prob* probs, int n, int wgs_per_cu, int waves, hipStream_
     const int bb = block_bytes(QT);
     for (int i = 0; i < n; ++i) total += (double)probs[i].N * (probs[i].K / QK) * bb;
     for (int i = 0; i < n; ++i) lds = xs_bytes(probs[i].K) > lds ? xs_bytes(probs[i].K) : lds;
-    if (wgs_per_cu == 0) {
-        wgs_per_cu = (int)(LDS_PER_CU / (lds ? lds : 1));
-        const int cap = waves == 16 ? 2 : 3;
-        wgs_per_cu = wgs_per_cu < 1 ? 1 : (wgs_per_cu > cap ? cap : wgs_per_cu);
-    }
-    const long budget = (long)num_cus() * wgs_per_cu;
-    int wg = 0;
+    long per_cu = (long)(LDS_PER_CU / (lds ? lds : 1));
+    per_cu = per_cu < 1 ? 1 : (per_cu < wgs_per_cu ? per_cu : wgs_per_cu);
+    const long budget = (long)num_cus() * per_cu;
+    long wg = 0;
     for (int i = 0; i < n; ++i) {
         M1Prob q = probs[i];
-        q.lpr = m1b_lpr(q.K / 64);
-        const long groups = ((long)q.N + 64 / q.lpr - 1) / (64 / q.lpr);
+        q.lpr = pick_lpr(q.K / 64);
+        const long rows = (long)(64 / q.lpr) * waves;  // rows per tile
+        const long tiles = ((long)q.N + rows - 1) / rows;
         const double bytes = (double)q.N * (q.K / QK) * bb;
         long nwg = (long)(budget * bytes / total + 0.5);
-        const long useful = (groups + waves - 1) / waves;  // at least one row group per wave
-        nwg = nwg < 1 ? 1 : (nwg > useful ? useful : nwg);
-        q.wg0 = wg;
+        nwg = nwg < 1 ? 1 : (nwg > tiles ? tiles : nwg);
+        q.wg0 = (int)wg;
         q.nwg = (int)nwg;
-        wg += q.nwg;
+        wg += nwg;
         B.p[B.n++] = q;
     }
+    if (wg > 0x7FFFFFFF) return fail(QMV_EINVAL, "N too large");
     if (waves == 16)
-        hipLaunchKernelGGL((k_m1b<QT, 16>), dim3(wg), dim3(1024), lds, st, B);
+        hipLaunchKernelGGL((k_m1b<QT, 16>), dim3((unsigned)wg), dim3(1024), lds, st, B);
     else if (waves == 4)
-        hipLaunchKernelGGL((k_m1b<QT, 4>), dim3(wg), dim3(256), lds, st, B);
+        hipLaunchKernelGGL((k_m1b<QT, 4>), dim3((unsigned)wg), dim3(256), lds, st, B);
     else
-        hipLaunchKernelGGL((k_m1b<QT, 8>), dim3(wg), dim3(512), lds, st, B);
+        hipLaunchKernelGGL((k_m1b<QT, 8>), dim3((unsigned)wg), dim3(512), lds, st, B);
     return check_launch("qmv batched m1 kernel");
+}
+
+bool mo_eligible(const uint8_t* W, size_t ldw, const float* x, int K) {
+    return K > 0 && K % 64 == 0 && K <= MO_KMAX && ((uintptr_t)W & 3) == 0 && (ldw & 3) == 0 &&
+           ((uintptr_t)x & 3) == 0;
+}
+
+// Launch the one-shot M = 1 kernel over n problems (all mo_eligible).
+// Knobs (0 = default): MAXI (4 or 8), target waves per CU.
+template <int QT>
+int launch_m1o(const M1Prob* probs, int n, int maxi, int wpc, hipStream_t st) {
+    if (maxi == 0) maxi = 4;
+    if (wpc <= 0) wpc = 16;
+    const int ncu = num_cus();
+    const int bb = block_bytes(QT);
+    double total = 0;
+    for (int i = 0; i < n; ++i) total += (double)probs[i].N * (probs[i].K / QK) * bb;
+    OsBatch B;
+    B.n = 0;
+    long wg = 0;
+    size_t lds = 0;
+    for (int i = 0; i < n; ++i) {
+        OsProb q;
+        q.W = probs[i].W;
+        q.x = probs[i].x;
+        q.y = probs[i].y;
+        q.ldw = probs[i].ldw;
+        q.N = probs[i].N;
+        q.K = probs[i].K;
+        const int P = q.K / 64;
+        int S = 1;
+        while (S * 64 < P) S *= 2;
+        int lpr = 4;
+        if (S > 1) {
+            lpr = 64;
+        } else {
+            while (lpr < P) lpr *= 2;
+        }
+        q.lpr = lpr;
+        q.S = S;
+        const int R = MO_WAVES / S;
+        const long RG = ((long)q.N + 64 / lpr - 1) / (64 / lpr);
+        const long tr_min = (RG + maxi - 1) / maxi;
+        const double bytes = (double)q.N * (q.K / QK) * bb;
+        long tr = (long)((double)ncu * wpc / S * bytes / total + 0.5);
+        tr = tr > RG ? RG : tr;
+        tr = tr < tr_min ? tr_min : tr;
+        tr = tr < 1 ? 1 : tr;
+        const long nwg = (tr + R - 1) / R;
+        q.wg0 = (int)wg;
+        q.nwg = (int)nwg;
+        wg += nwg;
+        B.p[B.n++] = q;
+        const size_t l = xs_bytes(q.K);
+        lds = l > lds ? l : lds;
+    }
+    if (wg > 0x7FFFFFFF) return fail(QMV_EINVAL, "N too large");
+    if (maxi == 8)
+        hipLaunchKernelGGL((k_m1o<QT, 8>), dim3((unsigned)wg), dim3(MO_WAVES * 64), lds, st, B);
+    else
+        hipLaunchKernelGGL((k_m1o<QT, 4>), dim3((unsigned)wg), dim3(MO_WAVES * 64), lds, st, B);
+    return check_launch("qmv one-shot m1 kernel");
+}
+
+bool mq_eligible(const uint8_t* W, size_t ldw, const float* x, int K) {
+    return K > 0 && K % 64 == 0 && K <= MQ_KMAX && ((uintptr_t)W & 3) == 0 && (ldw & 3) == 0 &&
+           ((uintptr_t)x & 3) == 0;
+}
+
+// Segments per tile: enough (tile, segment) waves for target_waves, each
+// segment keeping at least 8 pairs (two steps), at most 16 segments.
+int mq_segments(long ntiles, int P, long target_waves) {
+    int S = 1;
+    while (S < 16 && ntiles * S < target_waves && (P + 2 * S - 1) / (2 * S) >= 8) S *= 2;
+    return S;
+}
+
+// Launch the block-diagonal matrix-core M = 1 kernel over n Q4_0 problems
+// (n <= MAXB, all mq_eligible). Tuning knobs (0 = default): target waves per
+// CU, workgroups per CU, forced segment count.
+int launch_m1q(const M1Prob* probs, int n, int target_wpc, int wgs_per_cu, int force_S, hipStream_t st) {
+    const int ncu = num_cus();
+    if (target_wpc <= 0) target_wpc = 12;
+    int S[MAXB];
+    long ntg[MAXB];
+    double bytes[MAXB], total = 0;
+    int waves = 8;
+    size_t lds = 0;
+    for (int i = 0; i < n; ++i) {
+        const long ntiles = ((long)probs[i].N + 15) / 16;
+        const int P = probs[i].K / 64;
+        S[i] = force_S ? force_S : mq_segments(ntiles, P, (long)ncu * target_wpc);
+        if (S[i] != 1 && S[i] != 2 && S[i] != 4 && S[i] != 8 && S[i] != 16)
+            return fail(QMV_EINVAL, "internal: segment count %d", S[i]);
+        waves = S[i] > waves ? S[i] : waves;
+        const size_t l = mq_lds_bytes(probs[i].K);
+        lds = l > lds ? l : lds;
+        bytes[i] = (double)probs[i].N * (probs[i].K / QK) * 18;
+        total += bytes[i];
+    }
+    long sum_ntg = 0;
+    for (int i = 0; i < n; ++i) {
+        const long ntiles = ((long)probs[i].N + 15) / 16;
+        const int T = waves / S[i];
+        ntg[i] = (ntiles + T - 1) / T;
+        sum_ntg += ntg[i];
+    }
+    const size_t red = 2 * (size_t)waves * 16 * sizeof(float);
+    if (wgs_per_cu <= 0) {
+        const long by_lds = (long)(LDS_PER_CU / (lds + red));
+        const long by_waves = 32 / waves;
+        wgs_per_cu = (int)(by_lds < by_waves ? by_lds : by_waves);
+        if (wgs_per_cu < 1) wgs_per_cu = 1;
+    }
+    const long budget = (long)ncu * wgs_per_cu;
+    MqBatch B;
+    B.n = 0;
+    long wg = 0;
+    for (int i = 0; i < n; ++i) {
+        MqProb q;
+        q.W = probs[i].W;
+        q.x = probs[i].x;
+        q.y = probs[i].y;
+        q.ldw = probs[i].ldw;
+        q.N = probs[i].N;
+        q.K = probs[i].K;
+        q.S = S[i];
+        q.segP = (q.K / 64 + S[i] - 1) / S[i];
+        long nwg = sum_ntg <= budget ? ntg[i] : (long)(budget * bytes[i] / total + 0.5);
+        nwg = nwg < 1 ? 1 : (nwg > ntg[i] ? ntg[i] : nwg);
+        q.wg0 = (int)wg;
+        q.nwg = (int)nwg;
+        wg += nwg;
+        B.p[B.n++] = q;
+    }
+    if (wg > 0x7FFFFFFF) return fail(QMV_EINVAL, "N too large");
+    if (waves == 16)
+        hipLaunchKernelGGL((k_m1q<16>), dim3((unsigned)wg), dim3(1024), lds, st, B);
+    else
+        hipLaunchKernelGGL((k_m1q<8>), dim3((unsigned)wg), dim3(512), lds, st, B);
+    return check_launch("qmv matrix-core m1 kernel");
 }
 
 // M = 2..16 on the matrix cores (Q4_0, K % 64 == 0, 4-byte aligned rows).
@@ -2019,6 +2510,39 @@ int qmv_probe_m1x(int qtype, int lpr, int rpt, int wr, int wgs_per_cu, const voi
 int qmv_probe_m1h(int target_wpc, int wgs_per_cu, int force_S, const void* W, size_t ldw, const float* X, float* Y,
                   int N, int K, void* stream) {
     return launch_m1h((const uint8_t*)W, ldw, X, Y, N, K, target_wpc, wgs_per_cu, force_S, (hipStream_t)stream);
+}
+
+int qmv_probe_m1o(int qtype, int maxi, int wpc, int n, const void* const* W, const size_t* ldw,
+                   const float* const* X, float* const* Y, const int* N, const int* K, void* stream) {
+    M1Prob p[MAXB];
+    if (n < 1 || n > MAXB) return fail(QMV_EINVAL, "n");
+    for (int i = 0; i < n; ++i) {
+        p[i].W = (const uint8_t*)W[i];
+        p[i].ldw = ldw[i];
+        p[i].x = X[i];
+        p[i].y = Y[i];
+        p[i].N = N[i];
+        p[i].K = K[i];
+        if (!mo_eligible(p[i].W, p[i].ldw, p[i].x, p[i].K)) return fail(QMV_EINVAL, "not eligible");
+    }
+    return qtype == QMV_Q4_0 ? launch_m1o<QMV_Q4_0>(p, n, maxi, wpc, (hipStream_t)stream)
+                             : launch_m1o<QMV_Q8_0>(p, n, maxi, wpc, (hipStream_t)stream);
+}
+
+int qmv_probe_m1q(int target_wpc, int wgs_per_cu, int force_S, int n, const void* const* W, const size_t* ldw,
+                   const float* const* X, float* const* Y, const int* N, const int* K, void* stream) {
+    M1Prob p[MAXB];
+    if (n < 1 || n > MAXB) return fail(QMV_EINVAL, "n");
+    for (int i = 0; i < n; ++i) {
+        p[i].W = (const uint8_t*)W[i];
+        p[i].ldw = ldw[i];
+        p[i].x = X[i];
+        p[i].y = Y[i];
+        p[i].N = N[i];
+        p[i].K = K[i];
+        if (!mq_eligible(p[i].W, p[i].ldw, p[i].x, p[i].K)) return fail(QMV_EINVAL, "not eligible");
+    }
+    return launch_m1q(p, n, target_wpc, wgs_per_cu, force_S, (hipStream_t)stream);
 }
 
 int qmv_probe_m1b(int qtype, int waves, int wgs_per_cu, int n, const void* const* W, const size_t* ldw,
