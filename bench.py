@@ -13,10 +13,15 @@ The weights of R distinct copies of the layer set are resident in HBM
 (10 copies = 1.23 GB, several times the 256 MB Infinity Cache) and steps
 rotate through them, so every step streams its weights from HBM.
 
+Each step is captured once per copy as a HIP graph (four kernel nodes) and
+the timed region replays the graphs back to back, so the figure is the GPU's
+time, not the host's launch rate.
+
 Output: one JSON line with the effective weight bandwidth (algorithmic
-weight bytes / wall time per step), the roofline of the qmv kernel (bytes of
-its launches / their summed duration, from HIP events around each launch)
-and the CPU oracle timed on a bounded sample of the same workload.
+weight bytes / wall time per step), the roofline of the qmv kernel (its
+algorithmic bytes per launch / its average launch duration over the timed
+region, which holds nothing but its launches) and the CPU oracle timed on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -74,40 +79,40 @@ def step_bytes():
     return sum(p.weight_bytes for p in synth.CONFIGS[1]["problems"])
 
 
-def time_steps(fn, sets, steps, warmup):
-    """Wall time of `steps` steps (each fn(set)) after `warmup` untimed ones."""
+def capture_steps(fn, sets):
+    """One HIP graph per copy of the layer set, each holding one step."""
     import torch
-    R = len(sets)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for s in sets:  # eager pass first: library set-up stays out of the graphs
+            fn(s)
+    torch.cuda.synchronize()
+    graphs = []
+    for s in sets:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            fn(s)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def time_graphs(graphs, steps, warmup):
+    """Wall time (s) of `steps` graph replays after `warmup` untimed ones,
+    bracketed by synchronizations and HIP events."""
+    import torch
+    R = len(graphs)
     for i in range(warmup):
-        fn(sets[i % R])
+        graphs[i % R].replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(steps):
-        fn(sets[i % R])
+        graphs[i % R].replay()
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / 1e3
-
-
-def launch_durations(sets, steps):
-    """Per-launch durations (s) of the grouped launches, from HIP events on
-    the launch stream around each launch, over `steps` steps."""
-    import torch
-
-    from block_quantized_weight_qmatmul_amd import qmv
-    R = len(sets)
-    evs = []
-    for i in range(steps):
-        s = sets[i % R]
-        for g in GROUPS:
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            qmv.qmv_batch("q4_0", [s[n] for n in g])
-            b.record()
-            evs.append((g, a, b))
-    torch.cuda.synchronize()
-    return [(g, a.elapsed_time(b) / 1e3) for g, a, b in evs]
 
 
 def m16_throughput(dev, reps=20):
@@ -285,23 +290,25 @@ def main():
         for g in GROUPS:
             qmv.qmv_batch("q4_0", [s[n] for n in g])
 
-    t = time_steps(grouped, sets, args.steps, args.warmup)
+    graphs = capture_steps(grouped, sets)
+    t = time_graphs(graphs, args.steps, args.warmup)
     ms_per_step = t / args.steps * 1e3
     value = nbytes * args.steps / t / 1e9
 
-    durs = launch_durations(sets, max(20, min(args.steps, 200)))
-    kern_bytes = {("q", "k", "v"): 9437184 + 2 * 2359296, ("o",): 9437184, ("gate", "up"): 2 * 33030144,
-                  ("down",): 33030144}
-    tot_b = sum(kern_bytes[g] for g, _ in durs)
-    tot_t = sum(d for _, d in durs)
-    achieved = tot_b / tot_t / 1e9
-    per_launch = tot_b / len(durs)
+    # Every launch in the timed region is the batched M = 1 kernel, so its
+    # average launch duration is the region's time over its launch count (the
+    # short gaps between dependent launches are included).
+    launches = args.steps * len(GROUPS)
+    per_launch = nbytes / len(GROUPS)
+    avg_launch = t / launches
+    achieved = per_launch / avg_launch / 1e9
     traffic = read_traffic(per_launch)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "k_m1b (qmv_batch, M=1)", "launches_per_step": len(GROUPS),
-                "avg_launch_us": round(tot_t / len(durs) * 1e6, 3),
+                "avg_launch_us": round(avg_launch * 1e6, 3),
                 "algorithmic_bytes_per_launch": round(per_launch)}
+    del graphs
 
     if args.probe_copy_mb:
         src = torch.empty(args.probe_copy_mb * 2**20 // 4, dtype=torch.float32, device=dev).uniform_()
@@ -313,10 +320,12 @@ def main():
 
     extra = {}
     if not args.no_extra:
-        t1 = time_steps(lambda s: qmv.qmv_batch("q4_0", [s[n] for n in ("q", "k", "v", "o", "gate", "up", "down")]),
-                        sets, args.steps, args.warmup)
-        t7 = time_steps(lambda s: [qmv.qmv_q4_0(s[n][0], s[n][1], s[n][2]) for n in
-                                   ("q", "k", "v", "o", "gate", "up", "down")], sets, args.steps, args.warmup)
+        names = ("q", "k", "v", "o", "gate", "up", "down")
+        g1 = capture_steps(lambda s: qmv.qmv_batch("q4_0", [s[n] for n in names]), sets)
+        t1 = time_graphs(g1, args.steps, args.warmup)
+        g7 = capture_steps(lambda s: [qmv.qmv_q4_0(s[n][0], s[n][1], s[n][2]) for n in names], sets)
+        t7 = time_graphs(g7, args.steps, args.warmup)
+        del g1, g7
         extra["layer_set_one_launch_GBps"] = round(nbytes * args.steps / t1 / 1e9, 1)
         extra["layer_set_seven_launches_GBps"] = round(nbytes * args.steps / t7 / 1e9, 1)
         extra["m16"] = m16_throughput(dev)
