@@ -8,17 +8,26 @@
 // in src/inference/models/gemma4/model.rs).
 //
 // Kernels
-//   * k_m1_<qtype>   — M = 1 mat-vec, the decode case. Bandwidth-bound: every
-//     weight byte is read from HBM once. Each lane streams whole pairs of
-//     blocks (36 B for Q4_0, 68 B for Q8_0; 4-byte aligned when rows are) with
-//     dwordx4 loads, LPR lanes cover one row, a wave covers 64/LPR rows at a
-//     time (RPT rows per lane for ILP and x reuse). The activation vector is
-//     staged once per workgroup into LDS (pairs padded to 68 floats so the LPR
-//     distinct lanes of a read hit distinct banks). Q4_0 codes are decoded with
-//     v_cvt_off_f32_i4 on (byte ^ 0x88): it yields (code - 8) / 16 exactly,
-//     so no -8 fold (and no cancellation) is needed; the 1/16 is undone once
-//     per output. Each row's partial sums are reduced across its LPR lanes by
-//     lane shuffles.
+//   * k_m1 / k_m1b   — M = 1 mat-vec (decode), one problem or a batch of up
+//     to 16 (k_m1b picks the problem by workgroup index and runs the same
+//     loop). Bandwidth-bound: every weight byte is read from HBM once. LPR
+//     lanes cover one row, each lane streaming whole pairs of blocks (36 B
+//     for Q4_0, 68 B for Q8_0) with dwordx4 loads, the next pair's loads in
+//     flight while one is decoded; with LPR = 64 a wave reads a contiguous row.
+//     The activation vector is staged once per workgroup into LDS (all 16-byte
+//     loads issued before the stores, pairs padded to 68 floats so the lanes
+//     of a read hit distinct banks). Q4_0 codes are decoded with
+//     v_cvt_off_f32_i4 on (byte ^ 0x88), which yields (code - 8) / 16 exactly;
+//     the 1/16 is undone once per output. A row's partial sums are reduced
+//     across its LPR lanes with DPP moves.
+//   * k_xprep + k_mm4 (+ k_mmred) — Q4_0 with M = 2..16 on the matrix cores
+//     (v_mfma_f32_16x16x32_f16): the activations are converted once per call
+//     into fp16 hi/lo operands, then 16-row weight tiles are contracted with
+//     them chunk by chunk; K is split over workgroups, and the segments summed
+//     by k_mmred, when the tiles alone cannot fill the chip.
+//   * k_mm           — the same contraction with the activations converted by
+//     each workgroup itself (no scratch memory), used when the call's scratch
+//     buffer cannot be allocated.
 //   * k_generic      — any qtype, 1..16 rows of X, any 2-byte alignment and
 //     any K: one wave per weight row, one block per lane per step, 2-byte
 //     loads. The fallback for shapes the fast kernels do not take.
@@ -27,7 +36,7 @@
 //     expert ("leader") gathers every pair selecting the same expert and
 //     streams that expert's rows once for all of them; other workgroups exit.
 //
-// All accumulation is fp32 with a fixed order (no atomics), so outputs are
+// All accumulation is fp32 in a fixed order (no atomics), so outputs are
 // bitwise reproducible run to run.
 
 #include <hip/hip_runtime.h>
@@ -367,19 +376,6 @@ struct M1Batch {
     int n;
 };
 
-template <int LPR>
-__device__ __forceinline__ float group_sum_rt(float v) { return lane_group_sum<LPR>(v); }
-
-__device__ __forceinline__ float group_sum_dyn(float v, int lpr) {
-    switch (lpr) {
-        case 64: return lane_group_sum<64>(v);
-        case 32: return lane_group_sum<32>(v);
-        case 16: return lane_group_sum<16>(v);
-        case 8: return lane_group_sum<8>(v);
-        default: return lane_group_sum<4>(v);
-    }
-}
-
 template <int QT, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void k_m1b(const M1Batch B) {
     extern __shared__ __align__(16) float xs[];
@@ -402,472 +398,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_m1b(const M1Batch B) {
 }
 
 // ---------------------------------------------------------------------------
-// M = 1 one-shot kernel, batched: every wave issues all of its weight loads
-// at once, so the whole product costs about one memory latency plus the
-// transfer time, and no weight load waits behind arithmetic or a barrier.
-//
-// Lanes: LPR lanes per row (G = 64 / LPR rows per row group); lane j of a
-// group owns ONE pair of blocks (64 activations) of the row, pair
-// sg * seg + j, where sg is the wave's segment of K. Rows with more than 64
-// pairs are cut into S segments handled by S waves of the workgroup, whose
-// partial sums meet in LDS (added in segment order). A row wave owns at most
-// MAXI consecutive row groups; all their pair loads (36 or 68 bytes per lane
-// each) are issued before anything waits. The activations are read in this
-// order: each thread loads its share of x first, then the weights; x goes
-// through LDS (once per workgroup) into each lane's registers (its own 64
-// values), and every weight pair is reduced as soon as it lands.
-// ---------------------------------------------------------------------------
-constexpr int MO_WAVES = 8;
-constexpr int MO_XCH = 8;  // float4 chunks of x per thread
-constexpr int MO_KMAX = MO_WAVES * 64 * MO_XCH * 4;
-
-struct OsProb {
-    const uint8_t* W;
-    const float* x;
-    float* y;
-    size_t ldw;
-    int N, K;
-    int lpr, S;  // lanes per row; K segments (waves) per row group
-    int wg0, nwg;
-};
-struct OsBatch {
-    OsProb p[MAXB];
-    int n;
-};
-
-template <int QT, int MAXI>
-__global__ __launch_bounds__(MO_WAVES * 64) void k_m1o(const OsBatch B) {
-    using T = PairTraits<QT>;
-    constexpr int DW = T::DW, PB = DW * 4;
-    typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
-    extern __shared__ __align__(16) float xs[];
-    __shared__ float red[MO_WAVES][MAXI];
-    int pi = 0;
-    while (pi + 1 < B.n && (int)blockIdx.x >= B.p[pi + 1].wg0) ++pi;
-    const uint8_t* __restrict__ W = B.p[pi].W;
-    const float* __restrict__ x = B.p[pi].x;
-    float* __restrict__ y = B.p[pi].y;
-    const size_t ldw = B.p[pi].ldw;
-    const int N = B.p[pi].N, K = B.p[pi].K, LPR = B.p[pi].lpr, S = B.p[pi].S;
-    const int lw = blockIdx.x - B.p[pi].wg0, nwg = B.p[pi].nwg;
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int sg = wave % S, rw = wave / S, R = MO_WAVES / S;
-    const int GR = 64 / LPR, g = lane / LPR, j = lane % LPR;
-    const int P = K >> 6;
-    const int seg = (P + S - 1) / S;
-    const int p = sg * seg + j;
-    const bool active = j < seg && p < P;
-    const int pc = active ? p : P - 1;
-    const long RG = ((long)N + GR - 1) / GR;
-    const long TR = (long)nwg * R, gr = (long)lw * R + rw;
-    const long rg0 = RG * gr / TR, rg1 = RG * (gr + 1) / TR;
-    const int nr = (int)(rg1 - rg0);  // <= MAXI (host plan)
-
-    // 1. this thread's share of x
-    // (unconditional, clamped, so the compiler can count them and later
-    // wait for x alone while the weight loads stay in flight)
-    f32x4u xv[MO_XCH];
-    const int nch = K >> 2;
-#pragma unroll
-    for (int i = 0; i < MO_XCH; ++i) {
-        const int c = tid + i * MO_WAVES * 64;
-        xv[i] = *reinterpret_cast<const f32x4u*>(x + 4 * (c < nch ? c : nch - 1));
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // 2. every weight pair this lane will use
-    // (branch-free: surplus slots reload the wave's last row group)
-    uint32_t b[MAXI][DW];
-    const int last = nr > 0 ? nr - 1 : 0;
-#pragma unroll
-    for (int i = 0; i < MAXI; ++i) {
-        long row = (rg0 + (i < last ? i : last)) * GR + g;
-        row = row < N ? row : N - 1;
-        load_pair<DW>(W + row * ldw + (size_t)pc * PB, b[i]);
-    }
-    // Nothing that needs weight data may be scheduled above the x staging.
-    __builtin_amdgcn_sched_barrier(0);
-    // 3. x into LDS (pairs padded to XS_PAIR floats), then this lane's pair;
-    // surplus chunks rewrite the last chunk's slot with the same values.
-#pragma unroll
-    for (int i = 0; i < MO_XCH; ++i) {
-        int c = tid + i * MO_WAVES * 64;
-        c = c < nch ? c : nch - 1;
-        const int k = 4 * c;
-        *reinterpret_cast<float4*>(xs + (k >> 6) * XS_PAIR + (k & 63)) = make_float4(xv[i].x, xv[i].y, xv[i].z, xv[i].w);
-    }
-    // LDS-only barrier: __syncthreads() would also wait for every weight load
-    // in flight (vmcnt(0)), which is exactly what this kernel avoids.
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    float4 xr[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) xr[i] = reinterpret_cast<const float4*>(xs + pc * XS_PAIR)[i];
-    // 4. reduce each pair as it lands
-    float v[MAXI];
-#pragma unroll
-    for (int i = 0; i < MAXI; ++i) {
-        const float d = T::dot(b[i], xr);
-        v[i] = group_sum_dyn(active ? d : 0.f, LPR);
-    }
-    if (S == 1) {
-        if (j == LPR - 1) {
-#pragma unroll
-            for (int i = 0; i < MAXI; ++i) {
-                const long row = (rg0 + i) * GR + g;
-                if (i < nr && row < N) y[row] = v[i] * T::OUT_SCALE;
-            }
-        }
-        return;
-    }
-    if (lane == 63) {
-#pragma unroll
-        for (int i = 0; i < MAXI; ++i) red[wave][i] = v[i];
-    }
-    __syncthreads();
-    if (sg == 0 && lane == 63) {
-#pragma unroll
-        for (int i = 0; i < MAXI; ++i) {
-            float t = v[i];
-            for (int s2 = 1; s2 < S; ++s2) t += red[wave + s2][i];
-            const long row = rg0 + i;
-            if (i < nr && row < N) y[row] = t * T::OUT_SCALE;
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// M = 1 x-stationary kernel.
-//
-// Every lane owns one pair of blocks (64 activations) of K for the whole
-// kernel and keeps those activations in registers; weight rows stream past.
-// A row's P = K/64 pairs are split into S segments of `seg` pairs; a wave
-// covers one segment of 64/LPR rows (LPR lanes per row, lane j of a row
-// group holding pair s*seg + j), RPT rows per lane per step. The S waves of
-// a segment group hold the same rows; their partial sums meet in LDS. The
-// workgroup has S * WR waves (WR row-waves per segment). Loads run two steps
-// ahead of the arithmetic.
-// ---------------------------------------------------------------------------
-struct XsPlan {
-    int S, seg, WR;
-};
-
-template <int QT, int LPR, int RPT>
-__global__ __launch_bounds__(512) void k_m1x(const uint8_t* __restrict__ W, size_t ldw, const float* __restrict__ x,
-                                              float* __restrict__ y, int N, int K, XsPlan plan, float out_scale) {
-    using T = PairTraits<QT>;
-    constexpr int DW = T::DW, PB = DW * 4;
-    constexpr int GROUPS = 64 / LPR;
-    __shared__ float red[2][8][GROUPS * RPT];  // [step parity][wave][row slot]
-    const int S = plan.S, seg = plan.seg, WR = plan.WR;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int s = wave % S, rw = wave / S;
-    const int g = lane / LPR, j = lane % LPR;
-    const int P = K >> 6;
-    const int pidx = s * seg + j;
-    const bool active = j < seg && pidx < P;
-    const int pc = active ? pidx : 0;
-    const int ROWS_STEP = WR * GROUPS * RPT;
-    const long nsteps = ((long)N + ROWS_STEP - 1) / ROWS_STEP;
-    const long lrow = (long)(rw * GROUPS + g) * RPT;
-
-    // This lane's 64 activations, kept in registers.
-    float4 xr[16];
-    {
-        const float4* xp = reinterpret_cast<const float4*>(x + (size_t)pc * 64);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) xr[i] = active ? xp[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    auto issue = [&](long step, uint32_t (&b)[RPT][DW]) {
-        const long row0 = step * ROWS_STEP + lrow;
-#pragma unroll
-        for (int r = 0; r < RPT; ++r) {
-            long rr = row0 + r;
-            rr = rr < N ? rr : N - 1;
-            load_pair<DW>(W + rr * ldw + (size_t)pc * PB, b[r]);
-        }
-    };
-    auto finish = [&](long step, const uint32_t (&b)[RPT][DW], int parity) {
-        float v[RPT];
-#pragma unroll
-        for (int r = 0; r < RPT; ++r) v[r] = active ? T::dot(b[r], xr) : 0.f;
-#pragma unroll
-        for (int r = 0; r < RPT; ++r) v[r] = lane_group_sum<LPR>(v[r]);
-        const long row0 = step * ROWS_STEP + lrow;
-        if (S == 1) {
-            if (j == LPR - 1) {
-#pragma unroll
-                for (int r = 0; r < RPT; ++r)
-                    if (row0 + r < N) y[row0 + r] = v[r] * out_scale;
-            }
-            return;
-        }
-        if (j == LPR - 1) {
-#pragma unroll
-            for (int r = 0; r < RPT; ++r) red[parity][wave][g * RPT + r] = v[r];
-        }
-        __syncthreads();
-        if (s == 0 && j == LPR - 1) {
-#pragma unroll
-            for (int r = 0; r < RPT; ++r) {
-                float acc = v[r];
-                for (int q = 1; q < S; ++q) acc += red[parity][wave + q][g * RPT + r];
-                if (row0 + r < N) y[row0 + r] = acc * out_scale;
-            }
-        }
-    };
-
-    long step = blockIdx.x;
-    if (step >= nsteps) return;  // uniform over the workgroup
-    const long stride = gridDim.x;
-    uint32_t ba[RPT][DW], bb[RPT][DW];
-    issue(step, ba);
-    if (step + stride < nsteps) issue(step + stride, bb);
-    int parity = 0;
-    while (true) {
-        finish(step, ba, parity);
-        parity ^= 1;
-        if (step + 2 * stride < nsteps) issue(step + 2 * stride, ba);
-        step += stride;
-        if (step >= nsteps) break;
-        finish(step, bb, parity);
-        parity ^= 1;
-        if (step + 2 * stride < nsteps) issue(step + 2 * stride, bb);
-        step += stride;
-        if (step >= nsteps) break;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// M = 1 Q4_0 kernel on the matrix cores (v_mfma_f32_16x16x32_f16).
-//
-// A wave owns a tile of 16 weight rows (MFMA columns j = lane % 16) and a
-// segment of each row's block pairs. Lane group G = lane / 16 streams pair
-// q = p0 + 4t + G of row j at step t (36 bytes, two blocks), so the four lane
-// groups each feed their own block into one of the four 8-wide k slices of
-// every MFMA: slice G of MFMA u carries qs dword u of the lane's block, i.e.
-// 8 codes, as exact fp16 values (code - 8). The A operand is block diagonal:
-// row 4G + 0 holds the hi fp16 part and row 4G + 1 the lo fp16 part of the
-// matching activations in slice G, every other entry is zero. After the four
-// MFMAs of a block, lane (G, j) holds that block's sums for row j in D rows
-// 4G (hi) and 4G + 1 (lo), so the fp16 block scale is applied in fp32 right
-// there: acc += d * (D[4G] + D[4G+1]).
-//
-// The activations are split once per workgroup (x * 2^s = hi + lo with hi,
-// lo fp16 and 2^s bringing max |x| into [2^14, 2^15)) and stored in LDS in
-// the order the A operands read them: per block 128 bytes = 4 dwords u x
-// {hi, lo} x 8 halves. Products of fp16 values are exact in fp32 and hi + lo
-// carries 22 bits of each activation, so the result is fp32-accurate.
+// Matrix-core operand types.
 // ---------------------------------------------------------------------------
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-// 8 codes of one qs dword -> fp16 (code - 8), in the element order
-// [4u+0, 4u+2, 4u+1, 4u+3, 20+4u-4.., ...] = lo nibbles of bytes 0,2,1,3 then
-// hi nibbles of bytes 0,2,1,3 (u = the dword's index within the block).
-__device__ __forceinline__ half8_t q4_codes_f16(uint32_t q) {
-    const uint32_t M = 0x000F000Fu, MAGIC = 0x64006400u;  // fp16 1024 + nibble
-    const half2_t bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-    const half2_t v0 = __builtin_bit_cast(half2_t, (q & M) | MAGIC) + bias;
-    const half2_t v1 = __builtin_bit_cast(half2_t, ((q >> 8) & M) | MAGIC) + bias;
-    const half2_t v2 = __builtin_bit_cast(half2_t, ((q >> 4) & M) | MAGIC) + bias;
-    const half2_t v3 = __builtin_bit_cast(half2_t, ((q >> 12) & M) | MAGIC) + bias;
-    half8_t r;
-    r[0] = v0[0]; r[1] = v0[1]; r[2] = v1[0]; r[3] = v1[1];
-    r[4] = v2[0]; r[5] = v2[1]; r[6] = v3[0]; r[7] = v3[1];
-    return r;
-}
-
-// Byte offset within a block's 128-byte LDS record of activation e (0..31),
-// piece p (0 = hi, 1 = lo); matches q4_codes_f16's element order.
-__device__ __forceinline__ int xh_offset(int e, int p) {
-    const int hi = e >> 4, kk = e & 15, u = kk >> 2, r = kk & 3;
-    const int pos = hi * 4 + ((r & 1) << 1 | (r >> 1));  // 0,2,1,3 -> 0,1,2,3 order
-    return u * 32 + p * 16 + pos * 2;
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
-}
-
-// Split x (K floats) into scaled fp16 hi/lo pairs in the MFMA A-operand
-// order. Returns the power-of-two exponent s (x was multiplied by 2^s).
-// Called by all threads of the workgroup; ends with a barrier.
-__device__ int stage_x_f16(uint8_t* xh, const float* __restrict__ x, int K, float* red) {
-    float m = 0.f;
-    for (int k = threadIdx.x; k < K; k += blockDim.x) m = fmaxf(m, fabsf(x[k]));
-    m = wave_max(m);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    if (lane == 0) red[wave] = m;
-    __syncthreads();
-    m = red[0];
-    for (int w = 1; w < nw; ++w) m = fmaxf(m, red[w]);
-    int s = 0;
-    if (m > 0.f && m <= 3.4e38f) {
-        int e;
-        frexpf(m, &e);  // m in [2^(e-1), 2^e)
-        s = 15 - e;
-        s = s > 126 ? 126 : (s < -126 ? -126 : s);
-    }
-    for (int k = threadIdx.x; k < K; k += blockDim.x) {
-        const float v = ldexpf(x[k], s);
-        const _Float16 h = (_Float16)v;
-        const _Float16 l = (_Float16)(v - (float)h);
-        uint8_t* rec = xh + (size_t)(k >> 5) * 128;
-        *reinterpret_cast<_Float16*>(rec + xh_offset(k & 31, 0)) = h;
-        *reinterpret_cast<_Float16*>(rec + xh_offset(k & 31, 1)) = l;
-    }
-    __syncthreads();
-    return s;
-}
-
-// Plan: tiles of 16 rows; each row's P pairs in S segments of `seg` pairs;
-// a workgroup has S * WR waves and works on WR tiles at a time.
-struct MhPlan {
-    int S, seg, WR;
-};
-
-__global__ __launch_bounds__(1024) void k_m1h(const uint8_t* __restrict__ W, size_t ldw, const float* __restrict__ x,
-                                              float* __restrict__ y, int N, int K, MhPlan plan, float out_scale) {
-    extern __shared__ __align__(16) uint8_t smem[];
-    __shared__ float red[2][16][16];  // [tile parity][wave][row]
-    const int S = plan.S, seg = plan.seg, WR = plan.WR;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int sgi = wave % S, rw = wave / S;
-    const int G = lane >> 4, j = lane & 15;
-    const int P = K >> 6;
-    const int p0 = sgi * seg;
-    const int p1 = p0 + seg < P ? p0 + seg : P;
-    const int nsteps = (seg + 3) >> 2;  // the same for every wave of the grid
-    const long ntiles = ((long)N + 15) / 16;
-    const long tstride = (long)gridDim.x * WR;
-    const long tile0 = (long)blockIdx.x * WR + rw;
-    // Every wave walks the same number of (tile, step) items so that the
-    // workgroup's barriers line up; items past the last tile are masked.
-    const long rounds = (ntiles + tstride - 1) / tstride;
-    const long nitems = rounds * nsteps;
-    // A-operand lanes: row i = lane % 16 with i / 4 == G and i % 4 < 2.
-    const bool a_lane = (j >> 2) == G && (j & 3) < 2;
-    const int a_piece = j & 1;
-
-    // Issue cursor (tile, step) runs two items ahead of the compute cursor.
-    long itile = tile0;
-    int istep = 0;
-    long issued = 0;
-    auto issue = [&](uint32_t (&b)[9]) {
-        if (issued < nitems) {
-            long row = itile * 16 + j;
-            row = row < N ? row : N - 1;
-            int q = p0 + 4 * istep + G;
-            q = q < p1 ? q : p1 - 1;
-            q = q > 0 ? q : 0;
-            load_pair<9>(W + row * ldw + (size_t)q * 36, b);
-        }
-        ++issued;
-        if (++istep == nsteps) {
-            istep = 0;
-            itile += tstride;
-        }
-    };
-
-    uint32_t b0[9], b1[9];
-    issue(b0);
-    issue(b1);
-    const int sx = stage_x_f16(smem, x, K, &red[0][0][0]);
-    const float yscale = ldexpf(out_scale, -sx);
-
-    half8_t a[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) a[u] = (half8_t){0, 0, 0, 0, 0, 0, 0, 0};
-    float acc = 0.f;
-    int parity = 0;
-    long ptile = tile0;
-    int pstep = 0;
-
-    auto process = [&](const uint32_t (&r)[9]) {
-        const bool tile_ok = ptile < ntiles;
-        const int q = p0 + 4 * pstep + G;
-        const bool valid = tile_ok && q < p1;
-#pragma unroll
-        for (int R = 0; R < 2; ++R) {
-            const int bk = 2 * q + R;
-            if (a_lane) {
-                const uint8_t* rec = smem + (size_t)(valid ? bk : 0) * 128 + a_piece * 16;
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const half8_t v = *reinterpret_cast<const half8_t*>(rec + u * 32);
-                    a[u] = valid ? v : (half8_t){0, 0, 0, 0, 0, 0, 0, 0};
-                }
-            }
-            uint32_t qd[4];
-            float d;
-            if (R == 0) {
-#pragma unroll
-                for (int u = 0; u < 4; ++u) qd[u] = __builtin_amdgcn_alignbyte(r[u + 1], r[u], 2);
-                d = half_lo(r[0]);
-            } else {
-#pragma unroll
-                for (int u = 0; u < 4; ++u) qd[u] = r[5 + u];
-                d = half_hi(r[4]);
-            }
-            f32x4_t c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[u], q4_codes_f16(qd[u]), c, 0, 0, 0);
-            if (valid) acc = fmaf(d, c[0] + c[1], acc);
-        }
-        if (pstep == nsteps - 1) {
-            // Sum the four lane groups (block slices) of each row.
-            float v = acc + __shfl_xor(acc, 16, 64);
-            v += __shfl_xor(v, 32, 64);
-            acc = 0.f;
-            const long row = ptile * 16 + j;
-            if (S == 1) {
-                if (tile_ok && G == 0 && row < N) y[row] = v * yscale;
-            } else {
-                if (G == 0) red[parity][wave][j] = v;
-                __syncthreads();
-                if (tile_ok && sgi == 0 && G == 0 && row < N) {
-                    float tot = v;
-                    for (int q2 = 1; q2 < S; ++q2) tot += red[parity][wave + q2][j];
-                    y[row] = tot * yscale;
-                }
-                parity ^= 1;
-            }
-            pstep = 0;
-            ptile += tstride;
-        } else {
-            ++pstep;
-        }
-    };
-
-    for (long it = 0; it < nitems; it += 2) {
-        process(b0);
-        issue(b0);
-        if (it + 1 < nitems) {
-            process(b1);
-            issue(b1);
-        }
-    }
-}
-
-MhPlan make_mh_plan(int N, int K, int ncu, int target_waves_per_cu) {
-    const int P = K / 64;
-    const long ntiles = ((long)N + 15) / 16;
-    // Segments: enough (tile, segment) waves to fill the chip, each at least
-    // 4 pairs per lane group step and at most 16 segments.
-    long want = (long)ncu * target_waves_per_cu;
-    int S = 1;
-    while (S < 16 && ntiles * S < want && (P + 2 * S - 1) / (2 * S) >= 4) S *= 2;
-    MhPlan pl;
-    pl.S = S;
-    pl.seg = (P + S - 1) / S;
-    pl.WR = S >= 8 ? 1 : 8 / S;
-    return pl;
-}
 
 // ---------------------------------------------------------------------------
 // Q4_0 codes as matrix-core operands. One qs dword holds 8 codes: the low
@@ -893,41 +428,6 @@ __device__ __forceinline__ half8_t q4_dec(uint32_t q) {
     return (half8_t){t0[0], t0[1], t1[0], t1[1], t2[0], t2[1], t3[0], t3[1]};
 }
 
-// ---------------------------------------------------------------------------
-// M = 1 Q4_0 on the matrix cores, batched (one launch serves up to 16
-// independent products y_p = W_p x_p).
-//
-// A wave owns a tile of 16 weight rows (MFMA column n = lane % 16) and a
-// segment of each row's block pairs; lane group G = lane / 16 streams pair
-// p0 + 4t + G of row n at step t (36 bytes). For block R of that pair, MFMA u
-// (u = 0..3) takes qs dword u of the lane's block as its B slice G. The A
-// operand is block diagonal: row 4G holds the hi and row 4G + 1 the lo fp16
-// part of the eight activations that slice G multiplies, every other entry is
-// zero, so after the four MFMAs lane (G, n) holds in D rows 4G and 4G + 1 the
-// block's dot product for row n, and the block's scale is applied in fp32.
-// The multiply-adds run on the matrix cores; the vector ALUs only unpack
-// codes (about 1.3 instructions per weight).
-//
-// Activations: each workgroup converts its problem's x once, in one pass,
-// into LDS records laid out as the A operands read them (MQ_PAIR bytes per
-// pair of blocks: block R x dword u x {hi, lo} x 8 fp16, then the two blocks'
-// factors 2^-s, then padding that staggers consecutive pairs over the LDS
-// banks). Block b is scaled by the power of two 2^s that brings its largest
-// |x| into [2^14, 2^15) and split as x * 2^s = hi + lo; fp16 products are
-// exact in fp32 and hi + lo keeps 22 bits of every activation. One zero
-// record after the last pair stands in for pairs past the end of a row.
-//
-// Work split: a tile's pairs are cut into S segments (S waves per tile,
-// T = WAVES / S tiles per workgroup pass); segment partial sums meet in LDS
-// and are added in segment order, so results do not depend on timing. The
-// grid is persistent: workgroup w of a problem takes tile groups w, w + nwg,
-// ... Weight loads run two steps ahead of the arithmetic.
-// ---------------------------------------------------------------------------
-constexpr int MQ_PAIR = 288;
-constexpr int MQ_KMAX = 32768;
-
-__host__ __device__ constexpr size_t mq_lds_bytes(int K) { return (size_t)(K / 64 + 1) * MQ_PAIR; }
-
 template <int CTRL>
 __device__ __forceinline__ float dpp_max(float v) {
     const int t = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false);
@@ -936,187 +436,6 @@ __device__ __forceinline__ float dpp_max(float v) {
 
 __device__ __forceinline__ uint32_t pack_h2(_Float16 a, _Float16 b) {
     return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
-}
-
-// Converts x[0..K) (K % 64 == 0) into the A-operand records at xs. Four
-// consecutive threads share a block: thread u of it holds the activations of
-// qs dword u (elements 4u..4u+3 and 16+4u..16+4u+3). Ends without a barrier.
-__device__ __forceinline__ void stage_xq(uint8_t* xs, const float* __restrict__ x, int K) {
-    typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
-    const int nb = K >> 5;
-    for (int i = threadIdx.x; i < nb * 4; i += blockDim.x) {
-        const int b = i >> 2, u = i & 3;
-        const f32x4u l4 = *reinterpret_cast<const f32x4u*>(x + (size_t)b * 32 + 4 * u);
-        const f32x4u h4 = *reinterpret_cast<const f32x4u*>(x + (size_t)b * 32 + 16 + 4 * u);
-        const float v[8] = {l4.x, l4.z, l4.y, l4.w, h4.x, h4.z, h4.y, h4.w};
-        float m = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
-        m = dpp_max<0xB1>(m);  // quad_perm [1,0,3,2]
-        m = dpp_max<0x4E>(m);  // quad_perm [2,3,0,1]
-        int s = 0;
-        if (m > 0.f && m <= 3.4e38f) {
-            int ex;
-            frexpf(m, &ex);  // m in [2^(ex-1), 2^ex)
-            s = 15 - ex;
-            s = s > 126 ? 126 : (s < -126 ? -126 : s);
-        }
-        uint32_t hw[4], lw[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            _Float16 h[2], l[2];
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const float a = ldexpf(v[2 * k + c], s);
-                h[c] = (_Float16)a;
-                float r = a - (float)h[c];
-                r = r == r ? r : 0.f;  // hi = +-inf or nan carries the value alone
-                l[c] = (_Float16)r;
-            }
-            hw[k] = pack_h2(h[0], h[1]);
-            lw[k] = pack_h2(l[0], l[1]);
-        }
-        uint8_t* rec = xs + (size_t)(b >> 1) * MQ_PAIR + (b & 1) * 128 + u * 32;
-        *reinterpret_cast<u32x4*>(rec) = (u32x4){hw[0], hw[1], hw[2], hw[3]};
-        *reinterpret_cast<u32x4*>(rec + 16) = (u32x4){lw[0], lw[1], lw[2], lw[3]};
-        if (u == 0) *reinterpret_cast<float*>(xs + (size_t)(b >> 1) * MQ_PAIR + 256 + (b & 1) * 4) = ldexpf(1.f, -s);
-    }
-    uint8_t* zr = xs + (size_t)(K >> 6) * MQ_PAIR;
-    for (int i = threadIdx.x; i < MQ_PAIR / 16; i += blockDim.x)
-        *reinterpret_cast<u32x4*>(zr + 16 * i) = (u32x4){0u, 0u, 0u, 0u};
-}
-
-struct MqProb {
-    const uint8_t* W;
-    const float* x;
-    float* y;
-    size_t ldw;
-    int N, K;
-    int S;     // segments per tile (divides WAVES)
-    int segP;  // pairs per segment
-    int wg0, nwg;
-};
-struct MqBatch {
-    MqProb p[MAXB];
-    int n;
-};
-
-template <int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void k_m1q(const MqBatch B) {
-    extern __shared__ __align__(16) uint8_t smem[];
-    uint8_t* xs = smem;
-    __shared__ float red[2][WAVES][16];
-    int pi = 0;
-    while (pi + 1 < B.n && (int)blockIdx.x >= B.p[pi + 1].wg0) ++pi;
-    const uint8_t* __restrict__ W = B.p[pi].W;
-    const float* __restrict__ x = B.p[pi].x;
-    float* __restrict__ y = B.p[pi].y;
-    const size_t ldw = B.p[pi].ldw;
-    const int N = B.p[pi].N, K = B.p[pi].K, S = B.p[pi].S, segP = B.p[pi].segP;
-    const int lw = blockIdx.x - B.p[pi].wg0, nwg = B.p[pi].nwg;
-
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int G = lane >> 4, n = lane & 15;
-    const int T = WAVES / S;
-    const int ts = wave / S, sg = wave % S;
-    const int P = K >> 6;
-    const int p0 = sg * segP;
-    const int nsteps = (segP + 3) >> 2;
-    const long ntiles = ((long)N + 15) / 16;
-    const long ntg = (ntiles + T - 1) / T;
-    const long nk = lw < ntg ? (ntg - lw + nwg - 1) / nwg : 0;
-    const long nitems = nk * nsteps;  // the same for every wave of the workgroup
-    const bool a_lane = (n >> 2) == G && (n & 3) < 2;
-    const int a_off = (n & 1) * 16;  // hi or lo piece
-
-    long ik = 0;
-    int ist = 0;
-    long issued = 0;
-    auto issue = [&](uint32_t (&b)[9]) {
-        if (issued < nitems) {
-            const long tile = (lw + ik * nwg) * T + ts;
-            long row = tile * 16 + n;
-            row = row < N ? row : N - 1;
-            int p = p0 + 4 * ist + G;
-            p = p < P ? p : P - 1;
-            load_pair<9>(W + row * ldw + (size_t)p * 36, b);
-        }
-        ++issued;
-        if (++ist == nsteps) {
-            ist = 0;
-            ++ik;
-        }
-    };
-    uint32_t b0[9], b1[9];
-    issue(b0);
-    issue(b1);
-    stage_xq(xs, x, K);
-    __syncthreads();
-
-    half8_t a0[4], a1[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        a0[u] = (half8_t){0, 0, 0, 0, 0, 0, 0, 0};
-        a1[u] = a0[u];
-    }
-    float acc = 0.f;
-    long pk = 0;
-    int pst = 0, parity = 0;
-    auto process = [&](const uint32_t (&r)[9]) {
-        const int q = 4 * pst + G;
-        const int p = p0 + q;
-        const bool valid = q < segP && p < P;
-        const uint8_t* rec = xs + (size_t)(valid ? p : P) * MQ_PAIR;
-        if (a_lane) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                a0[u] = *reinterpret_cast<const half8_t*>(rec + u * 32 + a_off);
-                a1[u] = *reinterpret_cast<const half8_t*>(rec + 128 + u * 32 + a_off);
-            }
-        }
-        const float2 xsc = *reinterpret_cast<const float2*>(rec + 256);
-        f32x4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-            c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0[u], q4_dec(__builtin_amdgcn_alignbyte(r[u + 1], r[u], 2)),
-                                                        c0, 0, 0, 0);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1[u], q4_dec(r[5 + u]), c1, 0, 0, 0);
-        const float s0 = valid ? half_lo(r[0]) * xsc.x : 0.f;
-        const float s1 = valid ? half_hi(r[4]) * xsc.y : 0.f;
-        acc = fmaf(s0, c0[0] + c0[1], acc);
-        acc = fmaf(s1, c1[0] + c1[1], acc);
-        if (++pst == nsteps) {
-            float v = acc + __shfl_xor(acc, 16, 64);
-            v += __shfl_xor(v, 32, 64);
-            acc = 0.f;
-            const long tile = (lw + pk * nwg) * T + ts;
-            const long row = tile * 16 + n;
-            const bool ok = tile < ntiles && row < N;
-            if (S == 1) {
-                if (G == 0 && ok) y[row] = v;
-            } else {
-                if (G == 0) red[parity][wave][n] = v;
-                __syncthreads();
-                if (sg == 0 && G == 0 && ok) {
-                    float t = v;
-                    for (int s2 = 1; s2 < S; ++s2) t += red[parity][wave + s2][n];
-                    y[row] = t;
-                }
-                parity ^= 1;
-            }
-            pst = 0;
-            ++pk;
-        }
-    };
-    for (long it = 0; it < nitems; it += 2) {
-        process(b0);
-        issue(b0);
-        if (it + 1 < nitems) {
-            process(b1);
-            issue(b1);
-        }
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1268,7 +587,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_mm(const uint8_t* __restrict__ W
                     const int blk = 2 * s2 + R;  // block index within the step
                     const half8_t ah = *reinterpret_cast<const half8_t*>(xa + blk * 2048);
                     const half8_t al = *reinterpret_cast<const half8_t*>(xa + blk * 2048 + 1024);
-                    const half8_t bq = q4_codes_f16(R ? v1[s2] : v0[s2]);
+                    const half8_t bq = q4_dec(R ? v1[s2] : v0[s2]);
                     f32x4_t cc = {0.f, 0.f, 0.f, 0.f};
                     cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bq, cc, 0, 0, 0);
                     cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bq, cc, 0, 0, 0);
@@ -1319,228 +638,142 @@ __global__ __launch_bounds__(WAVES * 64) void k_mm(const uint8_t* __restrict__ W
 }
 
 // ---------------------------------------------------------------------------
-// M = 2..16, second form: the activations are converted once per call by a
-// small pre-pass into a stream-ordered scratch buffer, already in A-operand
-// order, and every wave loads its A operands straight from there (L2
-// resident, 1 KB contiguous per block and piece), so the main kernel has no
-// LDS staging and no barriers in its K loop.
+// M = 2..16 with an activation pre-pass, second form (the default).
 //
-// Pre-pass (one workgroup per activation row m < 16): s_m = the power of two
-// that puts max_k |x[m, k]| in [2^14, 2^15) (fp16 range; rows past M are
-// zero), then x * 2^s_m = hi + lo with hi, lo fp16. Scratch layout per block
-// b: piece p (hi, lo) x row m x slice G x 8 halves = 2 KB, then 16 floats
-// with 2^-s_m.
+// Pre-pass (k_xprep): one wave per (chunk of MM_KC = 512 columns, activation
+// row m), one thread per (block, slice). Each row of a chunk is scaled by the
+// power of two 2^s that brings its largest |x| into [2^14, 2^15) and split as
+// x * 2^s = hi + lo (fp16), written in A-operand order: per block 2 KB =
+// piece (hi, lo) x row m (16, zero past M) x slice G x 8 fp16 in q4_dec
+// order; after all blocks, the factors 2^-s as float[nchunks][16]. Scaling
+// per chunk needs no reduction across the whole row, so the pre-pass is one
+// pass with no global synchronisation.
 //
-// Main kernel: a workgroup has S * WR waves; wave (s, rw) owns TW tiles of
-// 16 weight rows and the s-th of S segments of each row's block pairs; the S
-// partial sums meet in LDS once at the end.
+// Main kernel (k_mm4): the WAVES waves of a workgroup own WAVES * TW tiles
+// of 16 weight rows and walk the same range of K chunk by chunk; the
+// converted activations of a chunk (32 KB + its factors) are copied into LDS
+// once for all of them (double buffered). Latency is covered by distance: a
+// chunk's activations are fetched into registers two chunks before they are
+// used, and each wave's weight loads run four steps (two chunks) ahead. Each
+// block takes two MFMAs (hi, lo); the fp16 block scale is applied in fp32 to
+// the 16 x 16 partial, and the chunk's activation factors once per chunk.
+// When there are too few tiles to fill the chip, K is split over grid.y: each
+// segment writes its partial tile sums to scratch and k_mmred adds the
+// segments in order (deterministic, no cross-workgroup synchronisation).
 // ---------------------------------------------------------------------------
-// One workgroup per activation row m < 16 (1024 threads, up to XP_PER
-// elements per thread held in registers, so x is read once).
-constexpr int XP_THREADS = 1024, XP_PER = 16;
-constexpr int XP_KMAX = XP_THREADS * XP_PER;
 
-__global__ __launch_bounds__(XP_THREADS) void k_xprep(const float* __restrict__ X, size_t ldx, int M, int K,
-                                                      uint8_t* __restrict__ xa, int* __restrict__ zero_me,
-                                                      int n_zero) {
-    __shared__ float red[XP_THREADS / 64];
-    const int m = blockIdx.x;  // 0..15
-    for (int i = threadIdx.x; i < n_zero && m == 0; i += XP_THREADS) zero_me[i] = 0;
-    float v[XP_PER];
+__global__ __launch_bounds__(256) void k_xprep(const float* __restrict__ X, size_t ldx, int M, int K,
+                                               uint8_t* __restrict__ xa) {
+    typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
+    // block of 256 threads = (4 rows) x (16 blocks) x (4 slices) of one chunk
+    const int c = blockIdx.x, m = blockIdx.y * 4 + (threadIdx.x >> 6);
+    const int bl = (threadIdx.x >> 2) & 15, G = threadIdx.x & 3;
+    const int nb = K >> 5;
+    const int b = c * 16 + bl;
+    const bool ok = m < M && b < nb;
+    // elements 4G..4G+3 and 16+4G..19+4G of the block, in q4_dec order
+    f32x4u lo = {0.f, 0.f, 0.f, 0.f}, hi = lo;
+    if (ok) {
+        const float* src = X + (size_t)m * ldx + (size_t)b * 32 + 4 * G;
+        lo = *reinterpret_cast<const f32x4u*>(src);
+        hi = *reinterpret_cast<const f32x4u*>(src + 16);
+    }
+    const float v[8] = {lo.x, lo.z, lo.y, lo.w, hi.x, hi.z, hi.y, hi.w};
     float mx = 0.f;
 #pragma unroll
-    for (int e = 0; e < XP_PER; ++e) {
-        const int k = threadIdx.x + e * XP_THREADS;
-        v[e] = (m < M && k < K) ? X[(size_t)m * ldx + k] : 0.f;
-        mx = fmaxf(mx, fabsf(v[e]));
-    }
-    mx = wave_max(mx);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
-    __syncthreads();
-    mx = red[0];
-#pragma unroll
-    for (int w = 1; w < XP_THREADS / 64; ++w) mx = fmaxf(mx, red[w]);
-    int sh = 0;
+    for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(v[e]));
+    // largest |x| of the row's chunk: the 64 lanes of the wave
+    mx = dpp_max<0xB1>(mx);
+    mx = dpp_max<0x4E>(mx);
+    mx = dpp_max<0x141>(mx);
+    mx = dpp_max<0x140>(mx);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    int s = 0;
     if (mx > 0.f && mx <= 3.4e38f) {
         int ex;
         frexpf(mx, &ex);
-        sh = 15 - ex;
-        sh = sh > 126 ? 126 : (sh < -126 ? -126 : sh);
+        s = 15 - ex;
+        s = s > 126 ? 126 : (s < -126 ? -126 : s);
     }
-    const size_t nb = (size_t)K / 32;
-    if (threadIdx.x == 0) reinterpret_cast<float*>(xa + nb * 2048)[m] = ldexpf(1.f, -sh);
+    if ((threadIdx.x & 63) == 0 && m < 16) reinterpret_cast<float*>(xa + (size_t)nb * 2048)[c * 16 + m] = ldexpf(1.f, -s);
+    if (b >= nb || m >= 16) return;
+    uint32_t hw[4], lw[4];
 #pragma unroll
-    for (int e = 0; e < XP_PER; ++e) {
-        const int k = threadIdx.x + e * XP_THREADS;
-        if (k < K) {
-            const float t = ldexpf(v[e], sh);
-            const _Float16 h = (_Float16)t;
-            const _Float16 l = (_Float16)(t - (float)h);
-            const int el = k & 31, g = (el & 15) >> 2;
-            uint8_t* rec = xa + (size_t)(k >> 5) * 2048 + m * 64 + g * 16 + slice_pos(el) * 2;
-            *reinterpret_cast<_Float16*>(rec) = h;
-            *reinterpret_cast<_Float16*>(rec + 1024) = l;
+    for (int k = 0; k < 4; ++k) {
+        _Float16 h[2], l[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const float a = ldexpf(v[2 * k + q], s);
+            h[q] = (_Float16)a;
+            float r = a - (float)h[q];
+            r = r == r ? r : 0.f;  // hi = +-inf or nan carries the value alone
+            l[q] = (_Float16)r;
         }
+        hw[k] = pack_h2(h[0], h[1]);
+        lw[k] = pack_h2(l[0], l[1]);
     }
+    uint8_t* rec = xa + (size_t)b * 2048 + m * 64 + G * 16;
+    *reinterpret_cast<u32x4*>(rec) = (u32x4){hw[0], hw[1], hw[2], hw[3]};
+    *reinterpret_cast<u32x4*>(rec + 1024) = (u32x4){lw[0], lw[1], lw[2], lw[3]};
 }
 
-struct MmPlan {
-    int S, seg, WR;
-};
-
-template <int TW>
-__global__ __launch_bounds__(512) void k_mm2(const uint8_t* __restrict__ W, size_t ldw, const uint8_t* __restrict__ xa,
-                                             float* __restrict__ Y, size_t ldy, int M, int N, int K, MmPlan plan) {
-    __shared__ f32x4_t red[8][TW][64];
-    const int S = plan.S, seg = plan.seg;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int sgi = wave % S, rw = wave / S;
-    const int G = lane >> 4, j = lane & 15;
-    const int P = K >> 6;
-    const int p0 = sgi * seg;
-    const int p1 = p0 + seg < P ? p0 + seg : P;
-    const int nsteps = (seg + 3) >> 2;
-    const long row_base = ((long)blockIdx.x * plan.WR + rw) * 16 * TW;
-
-    auto issue = [&](int t, uint32_t (&b)[TW][9]) {
+// Y[m, n] = sum over the S segments (in order) of part[(s * M + m) * N + n].
+// All S loads are issued before the first add (S <= MM_SMAX).
+constexpr int MM_SMAX = 16;
+__global__ __launch_bounds__(256) void k_mmred(const float* __restrict__ part, int S, int M, int N,
+                                               float* __restrict__ Y, size_t ldy) {
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (long)M * N) return;
+    const int m = (int)(i / N), n = (int)(i % N);
+    float v[MM_SMAX];
 #pragma unroll
-        for (int tw = 0; tw < TW; ++tw) {
-            long row = row_base + tw * 16 + j;
-            row = row < N ? row : N - 1;
-            int q = p0 + 4 * t + G;
-            q = q < p1 ? q : p1 - 1;
-            q = q > 0 ? q : 0;
-            load_pair<9>(W + row * ldw + (size_t)q * 36, b[tw]);
-        }
-    };
-    f32x4_t acc[TW];
+    for (int s = 0; s < MM_SMAX; ++s) v[s] = s < S ? part[((size_t)s * M + m) * N + n] : 0.f;
+    float t = v[0];
 #pragma unroll
-    for (int tw = 0; tw < TW; ++tw) acc[tw] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-    const uint8_t* xl = xa + j * 64 + G * 16;  // this lane's A slice within a block record
-
-    auto compute = [&](int t, uint32_t (&r)[TW][9]) {
-        const int qbase = p0 + 4 * t;  // pair of lane group 0
-        uint32_t v0[TW][4], v1[TW][4], dd[TW][4];
-#pragma unroll
-        for (int tw = 0; tw < TW; ++tw) {
-            const bool valid = qbase + G < p1;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                v0[tw][u] = __builtin_amdgcn_alignbyte(r[tw][u + 1], r[tw][u], 2);
-                v1[tw][u] = r[tw][5 + u];
-            }
-            const uint32_t dpk = valid ? ((r[tw][0] & 0xFFFFu) | (r[tw][4] & 0xFFFF0000u)) : 0u;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) dd[tw][u] = dpk;
-            xpose4(v0[tw]);
-            xpose4(v1[tw]);
-            xpose4(dd[tw]);
-        }
-#pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) {
-#pragma unroll
-            for (int R = 0; R < 2; ++R) {
-                int blk = 2 * (qbase + s2) + R;  // global block index
-                blk = blk < 2 * P ? blk : 2 * P - 1;
-                const uint8_t* rec = xl + (size_t)blk * 2048;
-                const half8_t ah = *reinterpret_cast<const half8_t*>(rec);
-                const half8_t al = *reinterpret_cast<const half8_t*>(rec + 1024);
-#pragma unroll
-                for (int tw = 0; tw < TW; ++tw) {
-                    const half8_t bq = q4_codes_f16(R ? v1[tw][s2] : v0[tw][s2]);
-                    f32x4_t cc = {0.f, 0.f, 0.f, 0.f};
-                    cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bq, cc, 0, 0, 0);
-                    cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bq, cc, 0, 0, 0);
-                    const float d = R ? half_hi(dd[tw][s2]) : half_lo(dd[tw][s2]);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[tw][i] = fmaf(d, cc[i], acc[tw][i]);
-                }
-            }
-        }
-    };
-
-    uint32_t b0[TW][9], b1[TW][9];
-    if (nsteps > 0) issue(0, b0);
-    if (nsteps > 1) issue(1, b1);
-    for (int t = 0; t < nsteps; t += 2) {
-        compute(t, b0);
-        if (t + 2 < nsteps) issue(t + 2, b0);
-        if (t + 1 < nsteps) {
-            compute(t + 1, b1);
-            if (t + 3 < nsteps) issue(t + 3, b1);
-        }
-    }
-    const float* rscale = reinterpret_cast<const float*>(xa + (size_t)(K / 32) * 2048);
-    if (S > 1) {
-#pragma unroll
-        for (int tw = 0; tw < TW; ++tw) red[wave][tw][lane] = acc[tw];
-        __syncthreads();
-        if (sgi != 0) return;
-        for (int q2 = 1; q2 < S; ++q2)
-#pragma unroll
-            for (int tw = 0; tw < TW; ++tw) acc[tw] += red[wave + q2][tw][lane];
-    }
-#pragma unroll
-    for (int tw = 0; tw < TW; ++tw) {
-        const long row = row_base + tw * 16 + j;
-        if (row < N) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int m = 4 * G + i;
-                if (m < M) Y[(size_t)m * ldy + row] = acc[tw][i] * rscale[m];
-            }
-        }
-    }
+    for (int s = 1; s < MM_SMAX; ++s)
+        if (s < S) t += v[s];
+    Y[(size_t)m * ldy + n] = t;
 }
 
-// ---------------------------------------------------------------------------
-// M = 2..16, third form: the eight waves of a workgroup work on eight
-// different 16-row tiles (TW tiles each) over the same K range, so they share
-// the A operands, which are copied chunk by chunk (512 columns = 32 KB) from
-// the converted activations into double-buffered LDS: the next chunk is
-// loaded into registers while the current one is consumed and written to the
-// other buffer before the one barrier per chunk. K is split over
-// grid.y workgroups when there are too few tiles to fill the chip; their
-// partial sums go to scratch and the last workgroup of a tile group (by an
-// atomic arrival count) adds them in segment order, so the result does not
-// depend on timing.
-// ---------------------------------------------------------------------------
-constexpr int MM3_WAVES = 8;
-
-template <int TW>
-__global__ __launch_bounds__(MM3_WAVES * 64) void k_mm3(const uint8_t* __restrict__ W, size_t ldw,
-                                                        const uint8_t* __restrict__ xa, float* __restrict__ Y,
-                                                        size_t ldy, int M, int N, int K, int chunks_per_seg,
-                                                        float* __restrict__ part, int* __restrict__ arrive) {
-    extern __shared__ __align__(16) uint8_t smem[];  // 2 x 32 KB A chunks
-    __shared__ int s_last;
+template <int WAVES, int TW>
+__global__ __launch_bounds__(WAVES * 64) void k_mm4(const uint8_t* __restrict__ W, size_t ldw,
+                                                    const uint8_t* __restrict__ xa, float* __restrict__ Y,
+                                                    size_t ldy, int M, int N, int K, int chunks_per_seg,
+                                                    float* __restrict__ part) {
+    extern __shared__ __align__(16) uint8_t smem[];  // 2 chunks of A operands
+    __shared__ __align__(16) float sfac[2][16];      // their activation factors
+    constexpr int NT = WAVES * 64;
+    constexpr int AV = MM_CHUNK_BYTES / (NT * 16);  // 16-byte A pieces per thread per chunk
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
     const int G = lane >> 4, j = lane & 15;
     const int P = K >> 6;
     const int nchunks = (K + MM_KC - 1) / MM_KC;
-    const int S = gridDim.y, sgi = blockIdx.y;
+    const int sgi = blockIdx.y;
     const int c0 = sgi * chunks_per_seg;
     const int c1 = c0 + chunks_per_seg < nchunks ? c0 + chunks_per_seg : nchunks;
-    const long row_base = ((long)blockIdx.x * MM3_WAVES + wave) * 16 * TW;
+    const long row_base = ((long)blockIdx.x * WAVES + wave) * 16 * TW;
     const size_t xa_bytes = (size_t)(K / 32) * 2048;
+    const float* __restrict__ fac = reinterpret_cast<const float*>(xa + xa_bytes);
 
-    // A chunk c: 16 blocks x 2 KB, contiguous in xa; 512 threads x 4 x 16 B.
     typedef uint32_t u32x4a __attribute__((ext_vector_type(4)));
-    u32x4a stg[4];
-    auto fetch_a = [&](int c) {
+    u32x4a stg[2][AV];
+    float fst[2];
+    auto fetch_a = [&](int c, int set) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            size_t off = (size_t)c * MM_CHUNK_BYTES + (size_t)(i * MM3_WAVES * 64 + tid) * 16;
+        for (int i = 0; i < AV; ++i) {
+            size_t off = (size_t)c * MM_CHUNK_BYTES + (size_t)(i * NT + tid) * 16;
             off = off < xa_bytes ? off : 0;  // the tail of the last chunk is never read
-            stg[i] = *reinterpret_cast<const u32x4a*>(xa + off);
+            stg[set][i] = *reinterpret_cast<const u32x4a*>(xa + off);
         }
+        fst[set] = fac[c * 16 + (tid & 15)];
     };
-    auto put_a = [&](int buf) {
+    auto put_a = [&](int buf, int set) __attribute__((always_inline)) {
+        uint8_t* dst = smem + buf * MM_CHUNK_BYTES;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<u32x4a*>(smem + buf * MM_CHUNK_BYTES + (i * MM3_WAVES * 64 + tid) * 16) = stg[i];
+        for (int i = 0; i < AV; ++i) *reinterpret_cast<u32x4a*>(dst + (i * NT + tid) * 16) = stg[set][i];
+        if (tid < 16) sfac[buf][tid] = fst[set];
     };
-
     auto issue = [&](int step, uint32_t (&b)[TW][9]) {
 #pragma unroll
         for (int tw = 0; tw < TW; ++tw) {
@@ -1551,13 +784,14 @@ __global__ __launch_bounds__(MM3_WAVES * 64) void k_mm3(const uint8_t* __restric
             load_pair<9>(W + row * ldw + (size_t)q * 36, b[tw]);
         }
     };
-    f32x4_t acc[TW];
+    f32x4_t acc[TW], cacc[TW];
 #pragma unroll
-    for (int tw = 0; tw < TW; ++tw) acc[tw] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-
+    for (int tw = 0; tw < TW; ++tw) {
+        acc[tw] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        cacc[tw] = acc[tw];
+    }
     auto compute = [&](int step, const uint8_t* xbuf, uint32_t (&r)[TW][9]) {
-        const int qbase = step * 4;
-        const bool valid = qbase + G < P;
+        const bool valid = step * 4 + G < P;
         uint32_t v0[TW][4], v1[TW][4], dd[TW][4];
 #pragma unroll
         for (int tw = 0; tw < TW; ++tw) {
@@ -1583,61 +817,74 @@ __global__ __launch_bounds__(MM3_WAVES * 64) void k_mm3(const uint8_t* __restric
                 const half8_t al = *reinterpret_cast<const half8_t*>(rec + 1024);
 #pragma unroll
                 for (int tw = 0; tw < TW; ++tw) {
-                    const half8_t bq = q4_codes_f16(R ? v1[tw][s2] : v0[tw][s2]);
+                    const half8_t bq = q4_dec(R ? v1[tw][s2] : v0[tw][s2]);
                     f32x4_t cc = {0.f, 0.f, 0.f, 0.f};
                     cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bq, cc, 0, 0, 0);
                     cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bq, cc, 0, 0, 0);
                     const float d = R ? half_hi(dd[tw][s2]) : half_lo(dd[tw][s2]);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[tw][i] = fmaf(d, cc[i], acc[tw][i]);
+                    for (int i = 0; i < 4; ++i) cacc[tw][i] = fmaf(d, cc[i], cacc[tw][i]);
                 }
             }
         }
     };
-
-    // Two steps (256 columns each) per chunk; W loads two steps ahead.
-    uint32_t b0[TW][9], b1[TW][9];
-    const int st0 = c0 * 2, st1 = c1 * 2;
-    if (st0 < st1) {
-        issue(st0, b0);
-        issue(st0 + 1, b1);
-        fetch_a(c0);
-        put_a(0);
-    }
-    __syncthreads();
-    for (int c = c0; c < c1; ++c) {
-        const int buf = (c - c0) & 1;
-        if (c + 1 < c1) fetch_a(c + 1);
-        const uint8_t* xbuf = smem + buf * MM_CHUNK_BYTES;
-        compute(2 * c, xbuf, b0);
-        if (2 * c + 2 < st1) issue(2 * c + 2, b0);
-        compute(2 * c + 1, xbuf, b1);
-        if (2 * c + 3 < st1) issue(2 * c + 3, b1);
-        if (c + 1 < c1) put_a(buf ^ 1);
-        __syncthreads();
-    }
-
-    const float* rscale = reinterpret_cast<const float*>(xa + xa_bytes);
-    if (S > 1) {
-        // publish this segment's partial tile sums, then the last arrival adds them
-        float* mine = part + ((size_t)sgi * gridDim.x + blockIdx.x) * (MM3_WAVES * TW * 64 * 4);
+    auto fold = [&](int buf) {
+        const float4 f = *reinterpret_cast<const float4*>(&sfac[buf][4 * G]);
+        const float fv[4] = {f.x, f.y, f.z, f.w};
 #pragma unroll
         for (int tw = 0; tw < TW; ++tw)
-            *reinterpret_cast<f32x4_t*>(mine + ((wave * TW + tw) * 64 + lane) * 4) = acc[tw];
-        __threadfence();
-        __syncthreads();
-        if (tid == 0) s_last = atomicAdd(&arrive[blockIdx.x], 1) == S - 1;
-        __syncthreads();
-        if (!s_last) return;
-        __threadfence();
 #pragma unroll
-        for (int tw = 0; tw < TW; ++tw) acc[tw] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-        for (int q2 = 0; q2 < S; ++q2) {
-            const float* pp = part + ((size_t)q2 * gridDim.x + blockIdx.x) * (MM3_WAVES * TW * 64 * 4);
+            for (int i = 0; i < 4; ++i) {
+                acc[tw][i] = fmaf(fv[i], cacc[tw][i], acc[tw][i]);
+                cacc[tw][i] = 0.f;
+            }
+    };
+
+    // Weight steps (256 columns each) run four ahead in a ring of buffers.
+    uint32_t b0[TW][9], b1[TW][9], b2[TW][9], b3[TW][9];
+    const int st0 = 2 * c0, st1 = 2 * c1;
+    if (st0 < st1) issue(st0, b0);
+    if (st0 + 1 < st1) issue(st0 + 1, b1);
+    if (st0 + 2 < st1) issue(st0 + 2, b2);
+    if (st0 + 3 < st1) issue(st0 + 3, b3);
+    if (c0 < c1) {
+        fetch_a(c0, 0);
+        put_a(0, 0);
+    }
+    if (c0 + 1 < c1) fetch_a(c0 + 1, 1);
+    __syncthreads();
+    // chunk c is in LDS buffer (c - c0) & 1; register set (c - c0) & 1 is free
+    // once chunk c is in LDS and takes chunk c + 2.
+    auto body = [&](int c, auto BUF, uint32_t (&ba)[TW][9], uint32_t (&bb)[TW][9]) __attribute__((always_inline)) {
+        constexpr int buf = decltype(BUF)::value;
+        if (c + 2 < c1) fetch_a(c + 2, buf);
+        const uint8_t* xbuf = smem + buf * MM_CHUNK_BYTES;
+        compute(2 * c, xbuf, ba);
+        if (2 * c + 4 < st1) issue(2 * c + 4, ba);
+        compute(2 * c + 1, xbuf, bb);
+        if (2 * c + 5 < st1) issue(2 * c + 5, bb);
+        fold(buf);
+        if (c + 1 < c1) put_a(buf ^ 1, buf ^ 1);
+        __syncthreads();
+    };
+    for (int c = c0; c < c1; c += 2) {
+        body(c, std::integral_constant<int, 0>{}, b0, b1);
+        if (c + 1 < c1) body(c + 1, std::integral_constant<int, 1>{}, b2, b3);
+    }
+
+    if (gridDim.y > 1) {
 #pragma unroll
-            for (int tw = 0; tw < TW; ++tw)
-                acc[tw] += __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(pp + ((wave * TW + tw) * 64 + lane) * 4));
+        for (int tw = 0; tw < TW; ++tw) {
+            const long row = row_base + tw * 16 + j;
+            if (row < N) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int m = 4 * G + i;
+                    if (m < M) part[((size_t)sgi * M + m) * N + row] = acc[tw][i];
+                }
+            }
         }
+        return;
     }
 #pragma unroll
     for (int tw = 0; tw < TW; ++tw) {
@@ -1646,7 +893,7 @@ __global__ __launch_bounds__(MM3_WAVES * 64) void k_mm3(const uint8_t* __restric
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int m = 4 * G + i;
-                if (m < M) Y[(size_t)m * ldy + row] = acc[tw][i] * rscale[m];
+                if (m < M) Y[(size_t)m * ldy + row] = acc[tw][i];
             }
         }
     }
@@ -1901,61 +1148,6 @@ int launch_m1(const uint8_t* W, size_t ldw, const float* X, float* Y, int N, int
 }
 
 // Plan for the x-stationary kernel: lanes per row and K segments.
-struct M1xCfg {
-    int lpr, rpt, wr, wgs_per_cu;
-};
-
-XsPlan make_plan(int P, int lpr, int wr) {
-    XsPlan pl;
-    pl.S = (P + lpr - 1) / lpr;
-    pl.seg = (P + pl.S - 1) / pl.S;
-    pl.WR = wr;
-    while (pl.S * pl.WR > 8 && pl.WR > 1) --pl.WR;
-    return pl;
-}
-
-template <int QT, int LPR, int RPT>
-int launch_m1x_t(const uint8_t* W, size_t ldw, const float* X, float* Y, int N, int K, int wr, int wgs_per_cu,
-                 float out_scale, hipStream_t st) {
-    const XsPlan pl = make_plan(K / 64, LPR, wr);
-    if (pl.S > 8) return fail(QMV_EINVAL, "internal: K=%d too long for the x-stationary kernel", K);
-    const int rows_step = pl.WR * (64 / LPR) * RPT;
-    const long nsteps = ((long)N + rows_step - 1) / rows_step;
-    long grid = (long)num_cus() * wgs_per_cu;
-    grid = grid < nsteps ? grid : nsteps;
-    hipLaunchKernelGGL((k_m1x<QT, LPR, RPT>), dim3((unsigned)grid), dim3(64 * pl.S * pl.WR), 0, st, W, ldw, X, Y, N,
-                       K, pl, out_scale);
-    return check_launch("qmv m1x kernel");
-}
-
-int launch_m1h(const uint8_t* W, size_t ldw, const float* X, float* Y, int N, int K, int target_wpc, int wgs_per_cu,
-               int force_S, hipStream_t st) {
-    const int ncu = num_cus();
-    MhPlan pl = make_mh_plan(N, K, ncu, target_wpc);
-    if (force_S > 0) {
-        pl.S = force_S;
-        pl.seg = (K / 64 + force_S - 1) / force_S;
-        pl.WR = force_S >= 8 ? 1 : 8 / force_S;
-    }
-    const long ntiles = ((long)N + 15) / 16;
-    long grid = (long)ncu * wgs_per_cu;
-    const long need = (ntiles + pl.WR - 1) / pl.WR;
-    grid = grid < need ? grid : need;
-    const size_t lds = (size_t)(K / 32) * 128;
-    hipLaunchKernelGGL(k_m1h, dim3((unsigned)grid), dim3(64 * pl.S * pl.WR), lds, st, W, ldw, X, Y, N, K, pl, 1.0f);
-    return check_launch("qmv m1h kernel");
-}
-
-// Lanes per row for the batched kernel: favour more rows in flight (more
-// waves) over lane utilisation, since these products are latency-bound: the
-// largest power of two not above 4/3 of the pairs per row.
-int m1b_lpr(int P) {
-    int l = 64;
-    while (l > 4 && 3 * l > 4 * P) l >>= 1;
-    return l;
-}
-
-// Problems a batched M = 1 launch can take (checked by the caller).
 bool m1b_eligible(const uint8_t* W, size_t ldw, const float* x, int K) {
     return K > 0 && K % 64 == 0 && K <= KMAX_FAST && ((uintptr_t)W & 3) == 0 && (ldw & 3) == 0 &&
            ((uintptr_t)x & 3) == 0;
@@ -2001,147 +1193,6 @@ int launch_m1b(const M1Prob* probs, int n, int wgs_per_cu, int waves, hipStream_
     return check_launch("qmv batched m1 kernel");
 }
 
-bool mo_eligible(const uint8_t* W, size_t ldw, const float* x, int K) {
-    return K > 0 && K % 64 == 0 && K <= MO_KMAX && ((uintptr_t)W & 3) == 0 && (ldw & 3) == 0 &&
-           ((uintptr_t)x & 3) == 0;
-}
-
-// Launch the one-shot M = 1 kernel over n problems (all mo_eligible).
-// Knobs (0 = default): MAXI (4 or 8), target waves per CU.
-template <int QT>
-int launch_m1o(const M1Prob* probs, int n, int maxi, int wpc, hipStream_t st) {
-    if (maxi == 0) maxi = 4;
-    if (wpc <= 0) wpc = 16;
-    const int ncu = num_cus();
-    const int bb = block_bytes(QT);
-    double total = 0;
-    for (int i = 0; i < n; ++i) total += (double)probs[i].N * (probs[i].K / QK) * bb;
-    OsBatch B;
-    B.n = 0;
-    long wg = 0;
-    size_t lds = 0;
-    for (int i = 0; i < n; ++i) {
-        OsProb q;
-        q.W = probs[i].W;
-        q.x = probs[i].x;
-        q.y = probs[i].y;
-        q.ldw = probs[i].ldw;
-        q.N = probs[i].N;
-        q.K = probs[i].K;
-        const int P = q.K / 64;
-        int S = 1;
-        while (S * 64 < P) S *= 2;
-        int lpr = 4;
-        if (S > 1) {
-            lpr = 64;
-        } else {
-            while (lpr < P) lpr *= 2;
-        }
-        q.lpr = lpr;
-        q.S = S;
-        const int R = MO_WAVES / S;
-        const long RG = ((long)q.N + 64 / lpr - 1) / (64 / lpr);
-        const long tr_min = (RG + maxi - 1) / maxi;
-        const double bytes = (double)q.N * (q.K / QK) * bb;
-        long tr = (long)((double)ncu * wpc / S * bytes / total + 0.5);
-        tr = tr > RG ? RG : tr;
-        tr = tr < tr_min ? tr_min : tr;
-        tr = tr < 1 ? 1 : tr;
-        const long nwg = (tr + R - 1) / R;
-        q.wg0 = (int)wg;
-        q.nwg = (int)nwg;
-        wg += nwg;
-        B.p[B.n++] = q;
-        const size_t l = xs_bytes(q.K);
-        lds = l > lds ? l : lds;
-    }
-    if (wg > 0x7FFFFFFF) return fail(QMV_EINVAL, "N too large");
-    if (maxi == 8)
-        hipLaunchKernelGGL((k_m1o<QT, 8>), dim3((unsigned)wg), dim3(MO_WAVES * 64), lds, st, B);
-    else
-        hipLaunchKernelGGL((k_m1o<QT, 4>), dim3((unsigned)wg), dim3(MO_WAVES * 64), lds, st, B);
-    return check_launch("qmv one-shot m1 kernel");
-}
-
-bool mq_eligible(const uint8_t* W, size_t ldw, const float* x, int K) {
-    return K > 0 && K % 64 == 0 && K <= MQ_KMAX && ((uintptr_t)W & 3) == 0 && (ldw & 3) == 0 &&
-           ((uintptr_t)x & 3) == 0;
-}
-
-// Segments per tile: enough (tile, segment) waves for target_waves, each
-// segment keeping at least 8 pairs (two steps), at most 16 segments.
-int mq_segments(long ntiles, int P, long target_waves) {
-    int S = 1;
-    while (S < 16 && ntiles * S < target_waves && (P + 2 * S - 1) / (2 * S) >= 8) S *= 2;
-    return S;
-}
-
-// Launch the block-diagonal matrix-core M = 1 kernel over n Q4_0 problems
-// (n <= MAXB, all mq_eligible). Tuning knobs (0 = default): target waves per
-// CU, workgroups per CU, forced segment count.
-int launch_m1q(const M1Prob* probs, int n, int target_wpc, int wgs_per_cu, int force_S, hipStream_t st) {
-    const int ncu = num_cus();
-    if (target_wpc <= 0) target_wpc = 12;
-    int S[MAXB];
-    long ntg[MAXB];
-    double bytes[MAXB], total = 0;
-    int waves = 8;
-    size_t lds = 0;
-    for (int i = 0; i < n; ++i) {
-        const long ntiles = ((long)probs[i].N + 15) / 16;
-        const int P = probs[i].K / 64;
-        S[i] = force_S ? force_S : mq_segments(ntiles, P, (long)ncu * target_wpc);
-        if (S[i] != 1 && S[i] != 2 && S[i] != 4 && S[i] != 8 && S[i] != 16)
-            return fail(QMV_EINVAL, "internal: segment count %d", S[i]);
-        waves = S[i] > waves ? S[i] : waves;
-        const size_t l = mq_lds_bytes(probs[i].K);
-        lds = l > lds ? l : lds;
-        bytes[i] = (double)probs[i].N * (probs[i].K / QK) * 18;
-        total += bytes[i];
-    }
-    long sum_ntg = 0;
-    for (int i = 0; i < n; ++i) {
-        const long ntiles = ((long)probs[i].N + 15) / 16;
-        const int T = waves / S[i];
-        ntg[i] = (ntiles + T - 1) / T;
-        sum_ntg += ntg[i];
-    }
-    const size_t red = 2 * (size_t)waves * 16 * sizeof(float);
-    if (wgs_per_cu <= 0) {
-        const long by_lds = (long)(LDS_PER_CU / (lds + red));
-        const long by_waves = 32 / waves;
-        wgs_per_cu = (int)(by_lds < by_waves ? by_lds : by_waves);
-        if (wgs_per_cu < 1) wgs_per_cu = 1;
-    }
-    const long budget = (long)ncu * wgs_per_cu;
-    MqBatch B;
-    B.n = 0;
-    long wg = 0;
-    for (int i = 0; i < n; ++i) {
-        MqProb q;
-        q.W = probs[i].W;
-        q.x = probs[i].x;
-        q.y = probs[i].y;
-        q.ldw = probs[i].ldw;
-        q.N = probs[i].N;
-        q.K = probs[i].K;
-        q.S = S[i];
-        q.segP = (q.K / 64 + S[i] - 1) / S[i];
-        long nwg = sum_ntg <= budget ? ntg[i] : (long)(budget * bytes[i] / total + 0.5);
-        nwg = nwg < 1 ? 1 : (nwg > ntg[i] ? ntg[i] : nwg);
-        q.wg0 = (int)wg;
-        q.nwg = (int)nwg;
-        wg += nwg;
-        B.p[B.n++] = q;
-    }
-    if (wg > 0x7FFFFFFF) return fail(QMV_EINVAL, "N too large");
-    if (waves == 16)
-        hipLaunchKernelGGL((k_m1q<16>), dim3((unsigned)wg), dim3(1024), lds, st, B);
-    else
-        hipLaunchKernelGGL((k_m1q<8>), dim3((unsigned)wg), dim3(512), lds, st, B);
-    return check_launch("qmv matrix-core m1 kernel");
-}
-
 // M = 2..16 on the matrix cores (Q4_0, K % 64 == 0, 4-byte aligned rows).
 template <int WAVES, int TW>
 int launch_mm_t(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N, int K,
@@ -2169,88 +1220,55 @@ int launch_mm(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y
     return fail(QMV_EINVAL, "internal: no mfma kernel for waves=%d tw=%d", waves, tw);
 }
 
-// M = 2..16 with the activation pre-pass; returns QMV_EUNSUPPORTED (nothing
-// enqueued) when the scratch buffer cannot be allocated, so the caller can
-// fall back to the staging kernel.
-int launch_mm2(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N, int K,
-               int force_S, int force_tw, hipStream_t st) {
-    if (K > XP_KMAX) return QMV_EUNSUPPORTED;
-    const size_t bytes = (size_t)(K / 32) * 2048 + 64;
-    void* xa = nullptr;
-    if (hipMallocAsync(&xa, bytes, st) != hipSuccess || !xa) {
-        (void)hipGetLastError();
-        return QMV_EUNSUPPORTED;
-    }
-    hipLaunchKernelGGL(k_xprep, dim3(16), dim3(XP_THREADS), 0, st, X, ldx, M, K, (uint8_t*)xa, (int*)nullptr, 0);
-    int rc = check_launch("qmv activation pre-pass");
-    if (rc == QMV_OK) {
-        const long tiles = ((long)N + 15) / 16;
-        const int ncu = num_cus();
-        int tw = force_tw ? force_tw : (tiles >= 8L * ncu ? 2 : 1);
-        const long groups = (tiles + tw - 1) / tw;
-        const int P = K / 64;
-        int S = 1;
-        while (S < 8 && groups * S < 4L * ncu && (P + 2 * S - 1) / (2 * S) >= 4) S *= 2;
-        if (force_S) S = force_S;
-        MmPlan pl;
-        pl.S = S;
-        pl.seg = (P + S - 1) / S;
-        pl.WR = 8 / S > 0 ? (S >= 8 ? 1 : 8 / S) : 1;
-        if (pl.WR > 2 && groups < (long)ncu * pl.WR) pl.WR = 2;
-        const long grid = (groups + pl.WR - 1) / pl.WR;
-        if (tw == 2)
-            hipLaunchKernelGGL((k_mm2<2>), dim3((unsigned)grid), dim3(64 * pl.S * pl.WR), 0, st, W, ldw, (const uint8_t*)xa, Y,
-                               ldy, M, N, K, pl);
-        else
-            hipLaunchKernelGGL((k_mm2<1>), dim3((unsigned)grid), dim3(64 * pl.S * pl.WR), 0, st, W, ldw, (const uint8_t*)xa, Y,
-                               ldy, M, N, K, pl);
-        rc = check_launch("qmv mfma kernel");
-    }
-    if (hipFreeAsync(xa, st) != hipSuccess && rc == QMV_OK) rc = fail(QMV_EHIP, "qmv: hipFreeAsync failed");
-    return rc;
-}
-
-// M = 2..16: activation pre-pass + k_mm3. Returns QMV_EUNSUPPORTED (nothing
-// enqueued) when the shape is out of its range or scratch is unavailable.
-int launch_mm3(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N, int K,
-               int force_S, int force_tw, hipStream_t st) {
-    if (K > XP_KMAX) return QMV_EUNSUPPORTED;
+// M = 2..16: activation pre-pass + k_mm4 (+ k_mmred when K is split).
+// Returns QMV_EUNSUPPORTED (nothing enqueued) when the scratch buffer cannot
+// be had, so the caller can fall back to the kernel that needs none.
+// Knobs (0 = default): segments of K, waves per workgroup (4 or 8).
+int launch_mm4(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N, int K,
+               int force_S, int force_waves, hipStream_t st) {
     const int ncu = num_cus();
     const long tiles = ((long)N + 15) / 16;
-    const int tw = force_tw ? force_tw : (tiles >= 2L * MM3_WAVES * 2 * ncu ? 2 : 1);
-    const long groups = (tiles + (long)MM3_WAVES * tw - 1) / ((long)MM3_WAVES * tw);
+    const int waves = force_waves ? force_waves : 8;
+    if (waves != 4 && waves != 8) return fail(QMV_EINVAL, "internal: waves=%d", waves);
+    const long groups = (tiles + waves - 1) / waves;
     const int nchunks = (K + MM_KC - 1) / MM_KC;
-    // Split-K across workgroups needs a device-wide release per workgroup,
-    // which costs far more than it saves on this chip: one segment by default.
+    // Split K only when the tile groups fill less than half the chip: the
+    // reduction launch costs more than a partly idle chip otherwise.
     int S = 1;
+    if (2 * groups <= ncu)
+        while (S < nchunks && S < MM_SMAX && groups * S < ncu) S *= 2;
     if (force_S) S = force_S;
     S = S > nchunks ? nchunks : S;
+    S = S > MM_SMAX ? MM_SMAX : S;
     const int cps = (nchunks + S - 1) / S;
     S = (nchunks + cps - 1) / cps;
     if (groups > 0x7FFFFFFF || S > 65535) return QMV_EUNSUPPORTED;
-    const size_t xa_bytes = (size_t)(K / 32) * 2048 + 64;
-    const size_t part_bytes = S > 1 ? (size_t)S * groups * MM3_WAVES * tw * 64 * 16 : 0;
-    const size_t arr_bytes = S > 1 ? (size_t)groups * 4 : 0;
+    const size_t xa_bytes = (size_t)(K / 32) * 2048 + (size_t)nchunks * 64;
     const size_t off_part = (xa_bytes + 255) & ~(size_t)255;
-    const size_t off_arr = (off_part + part_bytes + 255) & ~(size_t)255;
+    const size_t part_bytes = S > 1 ? (size_t)S * M * N * sizeof(float) : 0;
     void* scratch = nullptr;
-    if (hipMallocAsync(&scratch, off_arr + arr_bytes + 256, st) != hipSuccess || !scratch) {
+    if (hipMallocAsync(&scratch, off_part + part_bytes, st) != hipSuccess || !scratch) {
         (void)hipGetLastError();
         return QMV_EUNSUPPORTED;
     }
     uint8_t* xa = (uint8_t*)scratch;
-    float* part = (float*)(xa + off_part);
-    int* arrive = (int*)(xa + off_arr);
-    hipLaunchKernelGGL(k_xprep, dim3(16), dim3(XP_THREADS), 0, st, X, ldx, M, K, xa, arrive, (int)(arr_bytes / 4));
+    float* part = S > 1 ? (float*)(xa + off_part) : nullptr;
+    hipLaunchKernelGGL(k_xprep, dim3((unsigned)nchunks, 4), dim3(256), 0, st, X, ldx, M, K, xa);
     int rc = check_launch("qmv activation pre-pass");
     if (rc == QMV_OK) {
-        if (tw == 2)
-            hipLaunchKernelGGL((k_mm3<2>), dim3((unsigned)groups, (unsigned)S), dim3(MM3_WAVES * 64), 2 * MM_CHUNK_BYTES, st, W,
-                               ldw, (const uint8_t*)xa, Y, ldy, M, N, K, cps, part, arrive);
+        if (waves == 4)
+            hipLaunchKernelGGL((k_mm4<4, 1>), dim3((unsigned)groups, (unsigned)S), dim3(256), 2 * MM_CHUNK_BYTES, st, W,
+                               ldw, (const uint8_t*)xa, Y, ldy, M, N, K, cps, part);
         else
-            hipLaunchKernelGGL((k_mm3<1>), dim3((unsigned)groups, (unsigned)S), dim3(MM3_WAVES * 64), 2 * MM_CHUNK_BYTES, st, W,
-                               ldw, (const uint8_t*)xa, Y, ldy, M, N, K, cps, part, arrive);
+            hipLaunchKernelGGL((k_mm4<8, 1>), dim3((unsigned)groups, (unsigned)S), dim3(512), 2 * MM_CHUNK_BYTES, st, W,
+                               ldw, (const uint8_t*)xa, Y, ldy, M, N, K, cps, part);
         rc = check_launch("qmv mfma kernel");
+    }
+    if (rc == QMV_OK && S > 1) {
+        const long n = (long)M * N;
+        hipLaunchKernelGGL(k_mmred, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, (const float*)part, S, M, N, Y,
+                           ldy);
+        rc = check_launch("qmv split-K reduction");
     }
     if (hipFreeAsync(scratch, st) != hipSuccess && rc == QMV_OK) rc = fail(QMV_EHIP, "qmv: hipFreeAsync failed");
     return rc;
@@ -2311,7 +1329,7 @@ int dense(int qtype, const void* Wv, size_t ldw, const float* X, size_t ldx, flo
     const bool mm_ok = qtype == QMV_Q4_0 && M >= 2 && K > 0 && K % 64 == 0 && ((uintptr_t)W & 3) == 0 &&
                        (ldw & 3) == 0 && ((uintptr_t)X & 3) == 0;
     if (mm_ok) {
-        const int rc = launch_mm3(W, ldw, X, ldx, Y, ldy, M, N, K, 0, 0, st);
+        const int rc = launch_mm4(W, ldw, X, ldx, Y, ldy, M, N, K, 0, 0, st);
         if (rc != QMV_EUNSUPPORTED) return rc;
         return launch_mm(W, ldw, X, ldx, Y, ldy, M, N, K, 0, 0, st);
     }
@@ -2493,58 +1511,6 @@ int qmv_probe_m1(int qtype, int lpr, int rpt, int waves, int wgs_per_cu, const v
     return fail(QMV_EINVAL, "probe: no variant");
 }
 
-int qmv_probe_m1x(int qtype, int lpr, int rpt, int wr, int wgs_per_cu, const void* W, size_t ldw, const float* X,
-                  float* Y, int N, int K, void* stream) {
-    hipStream_t st = (hipStream_t)stream;
-    const uint8_t* w = (const uint8_t*)W;
-    const float sc = qtype == QMV_Q4_0 ? 16.f : 1.f;
-#define QMV_P(QT, L, R) \
-    if (qtype == QT && lpr == L && rpt == R) return launch_m1x_t<QT, L, R>(w, ldw, X, Y, N, K, wr, wgs_per_cu, sc, st);
-#define QMV_PQ(QT) QMV_P(QT, 64, 1) QMV_P(QT, 64, 2) QMV_P(QT, 32, 1) QMV_P(QT, 32, 2) QMV_P(QT, 16, 1) QMV_P(QT, 16, 2)
-    QMV_PQ(QMV_Q4_0) QMV_PQ(QMV_Q8_0)
-#undef QMV_PQ
-#undef QMV_P
-    return fail(QMV_EINVAL, "probe: no variant");
-}
-
-int qmv_probe_m1h(int target_wpc, int wgs_per_cu, int force_S, const void* W, size_t ldw, const float* X, float* Y,
-                  int N, int K, void* stream) {
-    return launch_m1h((const uint8_t*)W, ldw, X, Y, N, K, target_wpc, wgs_per_cu, force_S, (hipStream_t)stream);
-}
-
-int qmv_probe_m1o(int qtype, int maxi, int wpc, int n, const void* const* W, const size_t* ldw,
-                   const float* const* X, float* const* Y, const int* N, const int* K, void* stream) {
-    M1Prob p[MAXB];
-    if (n < 1 || n > MAXB) return fail(QMV_EINVAL, "n");
-    for (int i = 0; i < n; ++i) {
-        p[i].W = (const uint8_t*)W[i];
-        p[i].ldw = ldw[i];
-        p[i].x = X[i];
-        p[i].y = Y[i];
-        p[i].N = N[i];
-        p[i].K = K[i];
-        if (!mo_eligible(p[i].W, p[i].ldw, p[i].x, p[i].K)) return fail(QMV_EINVAL, "not eligible");
-    }
-    return qtype == QMV_Q4_0 ? launch_m1o<QMV_Q4_0>(p, n, maxi, wpc, (hipStream_t)stream)
-                             : launch_m1o<QMV_Q8_0>(p, n, maxi, wpc, (hipStream_t)stream);
-}
-
-int qmv_probe_m1q(int target_wpc, int wgs_per_cu, int force_S, int n, const void* const* W, const size_t* ldw,
-                   const float* const* X, float* const* Y, const int* N, const int* K, void* stream) {
-    M1Prob p[MAXB];
-    if (n < 1 || n > MAXB) return fail(QMV_EINVAL, "n");
-    for (int i = 0; i < n; ++i) {
-        p[i].W = (const uint8_t*)W[i];
-        p[i].ldw = ldw[i];
-        p[i].x = X[i];
-        p[i].y = Y[i];
-        p[i].N = N[i];
-        p[i].K = K[i];
-        if (!mq_eligible(p[i].W, p[i].ldw, p[i].x, p[i].K)) return fail(QMV_EINVAL, "not eligible");
-    }
-    return launch_m1q(p, n, target_wpc, wgs_per_cu, force_S, (hipStream_t)stream);
-}
-
 int qmv_probe_m1b(int qtype, int waves, int wgs_per_cu, int n, const void* const* W, const size_t* ldw,
                   const float* const* X, float* const* Y, const int* N, const int* K, void* stream) {
     M1Prob pr[MAXB];
@@ -2565,14 +1531,9 @@ int qmv_probe_mm(int waves, int tw, const void* W, size_t ldw, const float* X, s
     return launch_mm((const uint8_t*)W, ldw, X, ldx, Y, ldy, M, N, K, waves, tw, (hipStream_t)stream);
 }
 
-int qmv_probe_mm2(int S, int tw, const void* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M,
+int qmv_probe_mm4(int S, int waves, const void* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M,
                   int N, int K, void* stream) {
-    return launch_mm2((const uint8_t*)W, ldw, X, ldx, Y, ldy, M, N, K, S, tw, (hipStream_t)stream);
-}
-
-int qmv_probe_mm3(int S, int tw, const void* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M,
-                  int N, int K, void* stream) {
-    return launch_mm3((const uint8_t*)W, ldw, X, ldx, Y, ldy, M, N, K, S, tw, (hipStream_t)stream);
+    return launch_mm4((const uint8_t*)W, ldw, X, ldx, Y, ldy, M, N, K, S, waves, (hipStream_t)stream);
 }
 #endif
 

@@ -33,10 +33,12 @@
  *    library never synchronizes; each call only enqueues work on `stream`
  *    (a hipStream_t; NULL = the null stream) and returns. The only memory it
  *    takes is for the dense Q4_0 calls with M >= 2: a stream-ordered scratch
- *    buffer of K/32 * 2 KiB + 64 bytes (the activations converted to the
- *    matrix-core operand layout), taken with hipMallocAsync and released with
- *    hipFreeAsync on `stream` within the same call. If it cannot be had, the
- *    call falls back to a kernel that needs no scratch.
+ *    buffer, taken with hipMallocAsync and released with hipFreeAsync on
+ *    `stream` within the same call, of K/32 * 2 KiB + ceil(K/512) * 64 bytes
+ *    (the activations converted to the matrix-core operand layout) plus, when
+ *    K is split over up to 16 workgroups per tile, 4 * S * M * N bytes of
+ *    partial sums. If it cannot be had, the call falls back to a kernel that
+ *    needs no scratch.
  *  - Arguments are validated on the host before any HIP call. A rejected call
  *    launches nothing, returns a negative status and sets a thread-local
  *    message readable with qmv_last_error().

@@ -170,6 +170,36 @@ def test_multi_row_x_with_strides(qtype, M):
     assert np.all(np.isnan(y[:, N:]))  # the row padding of Y is left alone
 
 
+@pytest.mark.parametrize("M", [5, 16])
+@pytest.mark.parametrize("N,K", [(64, 5120), (4100, 2112), (300, 1088), (27, 64)])
+def test_multi_row_split_k_and_ragged_chunks(M, N, K):
+    """Q4_0, M >= 2: few tiles (K split over workgroups and summed by a second
+    launch), K not a multiple of the 512-column chunk, N not a multiple of 16."""
+    W = synth.make_weights("q4_0", N, K, cfg=94, part=M)
+    X = synth.make_x(M, K, cfg=94, part=M)
+    check("q4_0", W, X, f"M={M} N={N} K={K}")
+
+
+def test_multi_row_dynamic_range_per_chunk():
+    """Activations spanning 2^-58..2^58 with a different scale in every row
+    and every 512-column chunk."""
+    M, N, K = 16, 384, 3072
+    W = synth.make_weights("q4_0", N, K, cfg=93)
+    r = np.random.default_rng(93)
+    X = synth.make_x(M, K, cfg=93) * np.exp(r.uniform(-40, 40, (M, K)))
+    X *= np.exp(r.uniform(-20, 20, (M, K // 512, 1))).repeat(512, axis=2).reshape(M, K)
+    check("q4_0", W, X.astype(np.float32), "dynamic range M=16")
+
+
+def test_multi_row_deterministic_bitwise():
+    M, N, K = 16, 200, 5120  # K split over several workgroups
+    W = synth.make_weights("q4_0", N, K, cfg=92)
+    X = synth.make_x(M, K, cfg=92)
+    y1, _ = run("q4_0", W, X)
+    y2, _ = run("q4_0", W, X)
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
 def test_k_zero_writes_zeros_and_empty_calls_do_nothing():
     Y = torch.full((3, 10), 7.0, dtype=torch.float32, device=DEV)
     W = torch.zeros((10, 2), dtype=torch.uint8, device=DEV)
