@@ -459,7 +459,7 @@ __device__ __forceinline__ uint32_t pack_h2(_Float16 a, _Float16 b) {
 // partial sums are added to the accumulator.
 // ---------------------------------------------------------------------------
 constexpr int MM_KC = 512;                        // activation columns per staged chunk
-constexpr int MM_CHUNK_BYTES = (MM_KC / 32) * 2 * 1024;  // blocks x {hi, lo} x 16 rows x 4 slices x 16 B
+constexpr int MM_CHUNK_BYTES = (MM_KC / 32) * 2 * 1024;  // blocks x {hi, lo} x 4 slices x 16 rows x 16 B
 
 // 4 x 4 transpose across the four 16-lane rows: on entry lane row R holds
 // v[c] = element (R, c); on exit it holds v[c] = element (c, R).
@@ -525,7 +525,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_mm(const uint8_t* __restrict__ W
                 const _Float16 h = (_Float16)xv;
                 const _Float16 l = (_Float16)(xv - (float)h);
                 const int el = e0 + e, g = (el & 15) >> 2;
-                uint8_t* rec = dst + (size_t)blk * 2048 + m * 64 + g * 16 + slice_pos(el) * 2;
+                uint8_t* rec = dst + (size_t)blk * 2048 + g * 256 + m * 16 + slice_pos(el) * 2;
                 *reinterpret_cast<_Float16*>(rec) = h;
                 *reinterpret_cast<_Float16*>(rec + 1024) = l;
             }
@@ -561,7 +561,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_mm(const uint8_t* __restrict__ W
 
     auto compute = [&](int step, uint32_t (&r)[TW][9]) {
         const int c = step / steps_per_chunk, buf = c & 1;
-        const uint8_t* xa = smem + buf * MM_CHUNK_BYTES + (step % steps_per_chunk) * 8 * 2048 + j * 64 + G * 16;
+        const uint8_t* xa = smem + buf * MM_CHUNK_BYTES + (step % steps_per_chunk) * 8 * 2048 + G * 256 + j * 16;
         const int q = step * 4 + G;
         const bool valid = q < P;
 #pragma unroll
@@ -644,8 +644,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_mm(const uint8_t* __restrict__ W
 // row m), one thread per (block, slice). Each row of a chunk is scaled by the
 // power of two 2^s that brings its largest |x| into [2^14, 2^15) and split as
 // x * 2^s = hi + lo (fp16), written in A-operand order: per block 2 KB =
-// piece (hi, lo) x row m (16, zero past M) x slice G x 8 fp16 in q4_dec
-// order; after all blocks, the factors 2^-s as float[nchunks][16]. Scaling
+// piece (hi, lo) x slice G x row m (16, zero past M) x 8 fp16 in q4_dec
+// order (slice-major, so the 16 lanes of one 16-byte LDS read cover all 64
+// banks once); after all blocks, the factors 2^-s as float[nchunks][16]. Scaling
 // per chunk needs no reduction across the whole row, so the pre-pass is one
 // pass with no global synchronisation.
 //
@@ -713,7 +714,7 @@ __global__ __launch_bounds__(256) void k_xprep(const float* __restrict__ X, size
         hw[k] = pack_h2(h[0], h[1]);
         lw[k] = pack_h2(l[0], l[1]);
     }
-    uint8_t* rec = xa + (size_t)b * 2048 + m * 64 + G * 16;
+    uint8_t* rec = xa + (size_t)b * 2048 + G * 256 + m * 16;
     *reinterpret_cast<u32x4*>(rec) = (u32x4){hw[0], hw[1], hw[2], hw[3]};
     *reinterpret_cast<u32x4*>(rec + 1024) = (u32x4){lw[0], lw[1], lw[2], lw[3]};
 }
@@ -807,7 +808,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_mm4(const uint8_t* __restrict__ 
             xpose4(v1[tw]);
             xpose4(dd[tw]);
         }
-        const uint8_t* xl = xbuf + (step & 1) * 8 * 2048 + j * 64 + G * 16;
+        const uint8_t* xl = xbuf + (step & 1) * 8 * 2048 + G * 256 + j * 16;
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) {
 #pragma unroll
@@ -990,7 +991,137 @@ __global__ __launch_bounds__(256) void k_generic(const uint8_t* __restrict__ W, 
 //  * otherwise gather every pair q >= p with ids[q] == e (in order) and
 //    compute their rows of this tile, streaming expert e's rows once.
 // ---------------------------------------------------------------------------
+// Decoded weights of one pair of blocks, for reuse against several
+// activation vectors: w[0..31] block 0, w[32..63] block 1, as (code - 8) / 16
+// (Q4_0) or code (Q8_0); d0, d1 the block scales.
+template <int QT>
+__device__ __forceinline__ void decode_pair(const uint32_t* r, float* w, float& d0, float& d1) {
+    if constexpr (QT == QMV_Q4_0) {
+        uint32_t u[9], u4[9];
+#pragma unroll
+        for (int i = 0; i < 9; ++i) {
+            u[i] = r[i] ^ 0x88888888u;
+            u4[i] = u[i] >> 4;
+        }
+        unroll<0, 2>([&](auto R) {
+            constexpr int QB = R ? 20 : 2;
+            unroll<0, 16>([&](auto I) {
+                constexpr int t = QB + I;
+                w[32 * R + I] = nib<t % 4>(u[t / 4]);
+                w[32 * R + 16 + I] = nib<t % 4>(u4[t / 4]);
+            });
+        });
+        d0 = half_lo(r[0]);
+        d1 = half_hi(r[4]);
+    } else {
+        unroll<0, 2>([&](auto R) {
+            constexpr int QB = R ? 36 : 2;
+            unroll<0, 32>([&](auto I) {
+                constexpr int t = QB + I;
+                w[32 * R + I] = sbyte<t % 4>(r[t / 4]);
+            });
+        });
+        d0 = half_lo(r[0]);
+        d1 = half_hi(r[8]);
+    }
+}
+
+// m1_stream for nx <= MX activation vectors at once (the expert-indexed
+// product when several (token, slot) pairs select one expert): each weight
+// pair is loaded and decoded once and multiplied into every vector. The nx
+// vectors x[i] (rows of X at xoff[i]) are staged into LDS one after another;
+// results go to y[i][row] * out_scale.
+template <int QT, int LPR, int WAVES, int MX>
+__device__ __forceinline__ void m1_stream_mx(const uint8_t* __restrict__ W, size_t ldw, const float* __restrict__ X,
+                                             const size_t* xoff, float* const* y, int nx, int N, int K,
+                                             long first_tile, long tile_stride, float out_scale, float* xs) {
+    using T = PairTraits<QT>;
+    constexpr int DW = T::DW, PB = DW * 4;
+    constexpr int GROUPS = 64 / LPR;
+    constexpr int ROWS = GROUPS * WAVES;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane / LPR, j = lane % LPR;
+    const int P = K >> 6;
+    const int IPT = (P + LPR - 1) / LPR;
+    const long ntiles = ((long)N + ROWS - 1) / ROWS;
+    const long lrow = (long)(wave * GROUPS + g);
+    const size_t xstride = (size_t)P * XS_PAIR;  // floats per staged vector
+    long tile = first_tile;
+    if (tile >= ntiles) return;  // uniform over the workgroup
+    int it = 0;
+    uint32_t nxt[DW];
+    auto issue = [&](long tl, int i) {
+        long row = tl * ROWS + lrow;
+        row = row < N ? row : N - 1;
+        int p = j + i * LPR;
+        p = p < P ? p : P - 1;
+        load_pair<DW>(W + row * ldw + (size_t)p * PB, nxt);
+    };
+    issue(tile, 0);
+#pragma unroll
+    for (int i = 0; i < MX; ++i)
+        if (i < nx)
+            stage_x<WAVES * 64, (KMAX_STAGE / 4 + WAVES * 64 - 1) / (WAVES * 64)>(xs + i * xstride, X + xoff[i], K);
+    __syncthreads();
+    float tot[MX];
+#pragma unroll
+    for (int i = 0; i < MX; ++i) tot[i] = 0.f;
+    while (true) {
+        uint32_t cur[DW];
+#pragma unroll
+        for (int d = 0; d < DW; ++d) cur[d] = nxt[d];
+        const int p = j + it * LPR;
+        int it2 = it + 1;
+        long tile2 = tile;
+        if (it2 == IPT) {
+            it2 = 0;
+            tile2 += tile_stride;
+        }
+        const bool more = tile2 < ntiles;
+        if (more) issue(tile2, it2);
+        if (p < P) {
+            float w[64], d0, d1;
+            decode_pair<QT>(cur, w, d0, d1);
+#pragma unroll
+            for (int i = 0; i < MX; ++i) {
+                if (i < nx) {
+                    const float4* xv = reinterpret_cast<const float4*>(xs + i * xstride + p * XS_PAIR);
+                    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        const float4 a = xv[q], b = xv[8 + q];
+                        s0 = fmaf(w[4 * q], a.x, s0);
+                        s0 = fmaf(w[4 * q + 1], a.y, s0);
+                        s0 = fmaf(w[4 * q + 2], a.z, s0);
+                        s0 = fmaf(w[4 * q + 3], a.w, s0);
+                        s1 = fmaf(w[32 + 4 * q], b.x, s1);
+                        s1 = fmaf(w[32 + 4 * q + 1], b.y, s1);
+                        s1 = fmaf(w[32 + 4 * q + 2], b.z, s1);
+                        s1 = fmaf(w[32 + 4 * q + 3], b.w, s1);
+                    }
+                    tot[i] += fmaf(d1, s1, d0 * s0);
+                }
+            }
+        }
+        if (it == IPT - 1) {
+            const long row = tile * ROWS + lrow;
+#pragma unroll
+            for (int i = 0; i < MX; ++i) {
+                if (i < nx) {
+                    const float sum = lane_group_sum<LPR>(tot[i]);
+                    if (j == LPR - 1 && row < N) y[i][row] = sum * out_scale;
+                }
+                tot[i] = 0.f;
+            }
+        }
+        if (!more) break;
+        tile = tile2;
+        it = it2;
+    }
+}
+
 constexpr int ID_MAX_LIST = 1024;  // pairs one leader can serve in one pass
+constexpr int ID_MX = 8;           // activation vectors streamed together
 
 template <int QT, int LPR, int RPT, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void k_id(const uint8_t* __restrict__ W, size_t estride, size_t ldw,
@@ -998,7 +1129,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_id(const uint8_t* __restrict__ W
                                                    const uint32_t* __restrict__ ids, int n_pairs, int top_k,
                                                    float* __restrict__ Y, size_t ldy, int N, int K,
                                                    const float* __restrict__ escale, int* __restrict__ err_flag,
-                                                   int fast) {
+                                                   int fast, int mxcap) {
     constexpr int GROUPS = 64 / LPR;
     constexpr int ROWS_PER_WG = GROUPS * RPT * WAVES;
     __shared__ int s_list[ID_MAX_LIST];
@@ -1040,11 +1171,29 @@ __global__ __launch_bounds__(WAVES * 64) void k_id(const uint8_t* __restrict__ W
     const int count = s_count;
     const uint8_t* We = W + (size_t)e * estride;
 
-    if (count == 1 && fast) {
-        const int t = p / top_k;
+    if (fast) {
         const float sc = (escale ? escale[e] : 1.f) * PairTraits<QT>::OUT_SCALE;
-        m1_stream<QT, LPR, RPT, WAVES>(We, ldw, X + (size_t)t * ldx, Y + (size_t)p * ldy, N, K, blockIdx.x,
-                                       gridDim.x, sc, xs);
+        if (count == 1) {
+            const int t = p / top_k;
+            m1_stream<QT, LPR, RPT, WAVES>(We, ldw, X + (size_t)t * ldx, Y + (size_t)p * ldy, N, K, blockIdx.x,
+                                           gridDim.x, sc, xs);
+            return;
+        }
+        // Several pairs: each weight pair is read once for up to mxcap of them.
+        const int served = count < ID_MAX_LIST ? count : ID_MAX_LIST;
+        for (int c0 = 0; c0 < served; c0 += mxcap) {
+            const int nx = served - c0 < mxcap ? served - c0 : mxcap;
+            size_t xoff[ID_MX];
+            float* yp[ID_MX];
+#pragma unroll
+            for (int i = 0; i < ID_MX; ++i) {
+                const int q = s_list[c0 + (i < nx ? i : nx - 1)];
+                xoff[i] = (size_t)(q / top_k) * ldx;
+                yp[i] = Y + (size_t)q * ldy;
+            }
+            if (c0 > 0) __syncthreads();  // the previous vectors' LDS reads are done
+            m1_stream_mx<QT, LPR, WAVES, ID_MX>(We, ldw, X, xoff, yp, nx, N, K, blockIdx.x, gridDim.x, sc, xs);
+        }
         return;
     }
     // General case: one wave per row, up to 16 pairs per pass.
@@ -1345,9 +1494,16 @@ int launch_id_t(const uint8_t* W, size_t es, size_t ldw, int E, const float* X, 
     constexpr int ROWS_PER_WG = (64 / LPR) * RPT * WAVES;
     const long tiles = ((long)N + ROWS_PER_WG - 1) / ROWS_PER_WG;
     if (tiles > 0x7FFFFFFF) return fail(QMV_EINVAL, "qmv_id: N too large");
-    const size_t lds = fast ? xs_bytes(K) : 0;
+    // LDS for up to ID_MX staged vectors, within 64 KiB
+    int mxcap = 1;
+    if (fast) {
+        const size_t one = xs_bytes(K);
+        mxcap = (int)(65536 / (one ? one : 1));
+        mxcap = mxcap < 1 ? 1 : (mxcap > ID_MX ? ID_MX : mxcap);
+    }
+    const size_t lds = fast ? (size_t)mxcap * xs_bytes(K) : 0;
     hipLaunchKernelGGL((k_id<QT, LPR, RPT, WAVES>), dim3((unsigned)tiles, (unsigned)n_pairs), dim3(WAVES * 64), lds,
-                       st, W, es, ldw, E, X, ldx, ids, n_pairs, top_k, Y, ldy, N, K, sc, err, fast);
+                       st, W, es, ldw, E, X, ldx, ids, n_pairs, top_k, Y, ldy, N, K, sc, err, fast, mxcap);
     return check_launch("qmv_id kernel");
 }
 

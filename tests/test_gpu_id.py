@@ -116,6 +116,23 @@ def test_small_random_stack_against_oracle(qtype):
     assert_within_tol(y, yo, a, qtype)
 
 
+@pytest.mark.parametrize("qtype", ["q4_0", "q8_0"])
+@pytest.mark.parametrize("K", [2816, 704])
+def test_one_expert_serving_many_pairs(qtype, K):
+    """Slot 0 of all 24 tokens picks expert 3: its weights are streamed once
+    for several passes of staged activation rows; every pair's own token row
+    and output row must be used."""
+    E, T, N = 16, 24, 136
+    W = synth.make_weights(qtype, E * N, K, cfg=96, part=K).reshape(E, N, -1)
+    X = synth.make_x(T, K, cfg=96, part=K)
+    r = np.random.default_rng(K)
+    ids = np.stack([np.full(T, 3), r.integers(0, E, T)], axis=1).astype(np.uint32)
+    sc = synth.expert_scale(E, cfg=96)
+    y, _, _ = run_id(qtype, W, X, ids, N, K, escale=sc)
+    yo, a = oracle.qmv_id(qtype, W, X, ids, N, K, sc)
+    assert_within_tol(y, yo, a, f"{qtype} K={K}")
+
+
 def test_out_of_range_id_gives_nan_row_and_sets_flag():
     E, N, K = 8, 64, 256
     W = synth.make_weights("q4_0", E * N, K, cfg=81).reshape(E, N, -1)
