@@ -115,37 +115,83 @@ def time_graphs(graphs, steps, warmup):
     return e0.elapsed_time(e1) / 1e3
 
 
-def m16_throughput(dev, reps=20):
+def m16_throughput(dev, steps=40):
     """Config 3 (Q4_0, M = 16, K = 5120, N in {5120, 1024, 27648}): GB/s over
-    rotated copies."""
+    4 rotated copies, eager launches (these calls take stream-ordered scratch
+    memory, which graph capture would replace by the kernel that needs none)."""
     import torch
 
     from block_quantized_weight_qmatmul_amd import qmv, synth
     probs = synth.CONFIGS[3]["problems"]
-    R = 4
-    data = []
-    for r in range(R):
+    sets = []
+    for r in range(4):
+        s = []
         for part, p in enumerate(probs):
             W = torch.from_numpy(synth.make_weights("q4_0", p.N, p.K, cfg=3, copy=r, part=part)).to(dev)
             X = torch.from_numpy(synth.make_x(p.M, p.K, cfg=3, copy=r, part=part)).to(dev)
-            data.append((W, X, torch.empty((p.M, p.N), device=dev)))
+            s.append((W, X, torch.empty((p.M, p.N), device=dev)))
+        sets.append(s)
     nbytes = sum(p.weight_bytes for p in probs)
 
-    def step(r):
-        for W, X, Y in data[r * len(probs):(r + 1) * len(probs)]:
-            qmv.qmv_q4_0(W, X, Y)
-    for r in range(R):
-        step(r)
+    # raw C-ABI calls with the arguments prepared once, so that the host keeps
+    # ahead of the GPU
+    st = torch.cuda.current_stream().cuda_stream
+    args = [[(W.data_ptr(), W.stride(0), X.data_ptr(), X.stride(0), Y.data_ptr(), Y.stride(0), p.M, p.N, p.K)
+             for (W, X, Y), p in zip(s, probs)] for s in sets]
+
+    def step(a):
+        for W, ldw, X, ldx, Y, ldy, M, N, K in a:
+            if qmv.raw_qmv(qmv.QMV_Q4_0, W, ldw, X, ldx, Y, ldy, M, N, K, st) != 0:
+                raise RuntimeError(qmv.last_error())
+    for a in args:
+        step(a)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for i in range(reps):
-        step(i % R)
+    for i in range(steps):
+        step(args[i % 4])
     e1.record()
     torch.cuda.synchronize()
-    t = e0.elapsed_time(e1) / 1e3 / reps
-    return {"workload": "q4_0_m16_k5120_n5120_1024_27648", "weight_bytes": nbytes, "us_per_set": round(t * 1e6, 2),
-            "GBps": round(nbytes / t / 1e9, 1), "pct_hbm_peak": round(100 * nbytes / t / 1e9 / HBM_PEAK_GBS, 2)}
+    t = e0.elapsed_time(e1) / 1e3 / steps
+    return {"workload": "q4_0_m16_k5120_n5120_1024_27648", "weight_bytes": nbytes, "timing": "eager",
+            "us_per_set": round(t * 1e6, 2), "GBps": round(nbytes / t / 1e9, 1),
+            "pct_hbm_peak": round(100 * nbytes / t / 1e9 / HBM_PEAK_GBS, 2)}
+
+
+def moe_throughput(dev, T, steps=40):
+    """Config 4 (Q4_0 MoE, 128 experts, top-8, hidden 2816, expert
+    intermediate 704): the gate_up and down id calls for T tokens, graph
+    replays over rotated stacks (16 for T = 1, 4 for T = 32). GB/s counts the
+    weights of the distinct selected experts (each streamed once per call)."""
+    import numpy as np
+    import torch
+
+    from block_quantized_weight_qmatmul_amd import qmv, synth
+    R = 16 if T == 1 else 4
+    gu, dn = synth.moe_calls(T)
+    sets, nbytes = [], 0
+    for r in range(R):
+        d = synth.moe_inputs(T, copy=r)
+        dd = {k: torch.from_numpy(np.ascontiguousarray(v)).to(dev) for k, v in d.items()}
+        dd["ids"] = dd["ids"].to(torch.int32).contiguous()
+        dd["Y_gu"] = torch.empty(T * gu.top_k, gu.N, device=dev)
+        dd["Y_dn"] = torch.empty(T * gu.top_k, dn.N, device=dev)
+        nexp = synth.distinct(d["ids"])
+        nbytes += nexp * (gu.N * (gu.K // 32) + dn.N * (dn.K // 32)) * 18
+        sets.append(dd)
+    nbytes /= R
+
+    def step(dd):
+        qmv.qmv_id("q4_0", dd["W_gate_up"], dd["X_gate_up"], dd["ids"], dd["Y_gu"], gu.N, gu.K,
+                   expert_scale=dd["expert_scale"])
+        qmv.qmv_id("q4_0", dd["W_down"], dd["X_down"], dd["ids"].view(-1, 1), dd["Y_dn"], dn.N, dn.K,
+                   expert_scale=dd["expert_scale"])
+    graphs = capture_steps(step, sets)
+    t = time_graphs(graphs, steps, 4) / steps
+    del graphs
+    return {"workload": f"q4_0_moe_e128_top8_h2816_i704_t{T}", "weight_bytes_per_step": round(nbytes),
+            "us_per_step": round(t * 1e6, 2), "GBps": round(nbytes / t / 1e9, 1),
+            "pct_hbm_peak": round(100 * nbytes / t / 1e9 / HBM_PEAK_GBS, 2)}
 
 
 def cpu_baseline(target_s: float):
@@ -329,6 +375,8 @@ def main():
         extra["layer_set_one_launch_GBps"] = round(nbytes * args.steps / t1 / 1e9, 1)
         extra["layer_set_seven_launches_GBps"] = round(nbytes * args.steps / t7 / 1e9, 1)
         extra["m16"] = m16_throughput(dev)
+        extra["moe_t1"] = moe_throughput(dev, 1)
+        extra["moe_t32"] = moe_throughput(dev, 32)
     del sets
     torch.cuda.empty_cache()
 

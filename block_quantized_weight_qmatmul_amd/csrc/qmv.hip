@@ -1371,7 +1371,8 @@ int launch_mm(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y
 
 // M = 2..16: activation pre-pass + k_mm4 (+ k_mmred when K is split).
 // Returns QMV_EUNSUPPORTED (nothing enqueued) when the scratch buffer cannot
-// be had, so the caller can fall back to the kernel that needs none.
+// be had or the stream is being captured, so the caller can fall back to the
+// kernel that needs none.
 // Knobs (0 = default): segments of K, waves per workgroup (4 or 8).
 int launch_mm4(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N, int K,
                int force_S, int force_waves, hipStream_t st) {
@@ -1392,6 +1393,14 @@ int launch_mm4(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* 
     const int cps = (nchunks + S - 1) / S;
     S = (nchunks + cps - 1) / cps;
     if (groups > 0x7FFFFFFF || S > 65535) return QMV_EUNSUPPORTED;
+    // No stream-ordered allocation while the stream is being captured into a
+    // graph: the caller then gets the kernel that needs no scratch.
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cap) != hipSuccess) {
+        (void)hipGetLastError();
+        return QMV_EUNSUPPORTED;
+    }
+    if (cap != hipStreamCaptureStatusNone) return QMV_EUNSUPPORTED;
     const size_t xa_bytes = (size_t)(K / 32) * 2048 + (size_t)nchunks * 64;
     const size_t off_part = (xa_bytes + 255) & ~(size_t)255;
     const size_t part_bytes = S > 1 ? (size_t)S * M * N * sizeof(float) : 0;

@@ -37,8 +37,9 @@
  *    `stream` within the same call, of K/32 * 2 KiB + ceil(K/512) * 64 bytes
  *    (the activations converted to the matrix-core operand layout) plus, when
  *    K is split over up to 16 workgroups per tile, 4 * S * M * N bytes of
- *    partial sums. If it cannot be had, the call falls back to a kernel that
- *    needs no scratch.
+ *    partial sums. If it cannot be had, or if `stream` is being captured into
+ *    a HIP graph, the call uses a (slower) kernel that needs no scratch, so
+ *    every call can be captured.
  *  - Arguments are validated on the host before any HIP call. A rejected call
  *    launches nothing, returns a negative status and sets a thread-local
  *    message readable with qmv_last_error().

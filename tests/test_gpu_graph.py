@@ -1,0 +1,103 @@
+"""Calls captured into a HIP graph and replayed (needs an MI355X).
+
+Every call can be captured: under capture, the dense Q4_0 call with M >= 2
+uses the kernel that needs no scratch memory (no stream-ordered allocation
+is recorded). Each replay is checked against the oracle (and, where the same
+kernel runs eagerly, bit for bit against the eager result), with eager work
+and synchronisations between replays.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from block_quantized_weight_qmatmul_amd import qmv, synth
+from helpers import assert_within_tol
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def test_graph_replays_dense_and_batch():
+    cases = [(1, 300, 4096), (16, 64, 5120), (7, 700, 1088)]  # M = 1; M = 16 few tiles; ragged chunks
+    data = []
+    for i, (M, N, K) in enumerate(cases):
+        W = synth.make_weights("q4_0", N, K, cfg=91, part=i)
+        X = synth.make_x(M, K, cfg=91, part=i)
+        data.append((W, X, torch.from_numpy(W).to(DEV), torch.from_numpy(X).to(DEV),
+                     torch.full((M, N), np.nan, dtype=torch.float32, device=DEV)))
+    # batch of two M = 1 problems
+    Wb = [synth.make_weights("q4_0", 256, 2048, cfg=91, part=10 + k) for k in range(2)]
+    xb = synth.make_x(1, 2048, cfg=91, part=10)[0]
+    Wbd = [torch.from_numpy(w).to(DEV) for w in Wb]
+    xbd = torch.from_numpy(xb).to(DEV)
+    ybd = [torch.full((256,), np.nan, dtype=torch.float32, device=DEV) for _ in range(2)]
+
+    def calls():
+        for _, _, Wd, Xd, Yd in data:
+            qmv.qmv_q4_0(Wd, Xd, Yd)
+        qmv.qmv_batch("q4_0", [(Wbd[k], xbd, ybd[k]) for k in range(2)])
+
+    # eager reference for the M = 1 and batch calls (same kernels as in the graph)
+    calls()
+    torch.cuda.synchronize()
+    eager_m1 = data[0][4].cpu().numpy().copy()
+    eager_b = [y.cpu().numpy().copy() for y in ybd]
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        calls()
+    torch.cuda.synchronize()
+
+    first = None
+    for rep in range(3):
+        for _, _, _, _, Yd in data:
+            Yd.fill_(np.nan)  # eager work between replays
+        for y in ybd:
+            y.fill_(np.nan)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        outs = [d[4].cpu().numpy().copy() for d in data]
+        for (W, X, _, _, _), y, (M, N, K) in zip(data, outs, cases):
+            yo, a = oracle.qmv("q4_0", W, X)
+            assert_within_tol(y, yo, a, f"replay {rep} M={M} N={N} K={K}")
+        assert np.array_equal(outs[0].view(np.uint32), eager_m1.view(np.uint32))
+        for k in range(2):
+            assert np.array_equal(ybd[k].cpu().numpy().view(np.uint32), eager_b[k].view(np.uint32))
+        if first is None:
+            first = outs
+        else:
+            for a_, b_ in zip(first, outs):
+                assert np.array_equal(a_.view(np.uint32), b_.view(np.uint32))
+
+
+def test_graph_replays_id():
+    E, T, N, K = 16, 6, 96, 704
+    W = synth.make_weights("q4_0", E * N, K, cfg=90).reshape(E, N, -1)
+    X = synth.make_x(T, K, cfg=90)
+    ids = synth.router_topk(T, E, 4, cfg=90)
+    Wd, Xd = torch.from_numpy(W).to(DEV), torch.from_numpy(X).to(DEV)
+    idd = torch.from_numpy(ids.astype(np.int32)).to(DEV)
+    Y = torch.full((T * 4, N), np.nan, dtype=torch.float32, device=DEV)
+    qmv.qmv_id("q4_0", Wd, Xd, idd, Y, N, K)
+    torch.cuda.synchronize()
+    eager = Y.cpu().numpy().copy()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        qmv.qmv_id("q4_0", Wd, Xd, idd, Y, N, K)
+    torch.cuda.synchronize()
+    yo, a = oracle.qmv_id("q4_0", W, X, ids, N, K)
+    for rep in range(3):
+        Y.fill_(np.nan)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        y = Y.cpu().numpy()
+        assert np.array_equal(y.view(np.uint32), eager.view(np.uint32))
+        assert_within_tol(y, yo, a, f"id replay {rep}")
