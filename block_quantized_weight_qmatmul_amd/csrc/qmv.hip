@@ -45,6 +45,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+#include <vector>
+
 #include "qmv.h"
 
 namespace {
@@ -1369,10 +1372,52 @@ int launch_mm(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y
     return fail(QMV_EINVAL, "internal: no mfma kernel for waves=%d tw=%d", waves, tw);
 }
 
-// M = 2..16: activation pre-pass + k_mm4 (+ k_mmred when K is split).
-// Returns QMV_EUNSUPPORTED (nothing enqueued) when the scratch buffer cannot
-// be had or the stream is being captured, so the caller can fall back to the
-// kernel that needs none.
+// Scratch for the M >= 2 calls, one buffer per (device, stream), reused by
+// the calls that stream orders one after another and kept until the process
+// ends; a call that needs more releases the old buffer and takes a larger one,
+// both in stream order on that stream. Returns nullptr if none can be had.
+// The caller holds g_scratch_mu until its kernels are enqueued, so a buffer
+// is never released ahead of work already handed out on the same stream.
+struct StreamScratch {
+    int dev;
+    hipStream_t st;
+    void* p;
+    size_t n;
+};
+std::mutex g_scratch_mu;
+std::vector<StreamScratch> g_scratch;
+
+void* stream_scratch(hipStream_t st, size_t n) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    StreamScratch* e = nullptr;
+    for (auto& c : g_scratch)
+        if (c.dev == dev && c.st == st) e = &c;
+    if (e && e->n >= n) return e->p;
+    const size_t want = (n + ((size_t)1 << 20) - 1) & ~(((size_t)1 << 20) - 1);  // whole MiB
+    void* p = nullptr;
+    if (hipMallocAsync(&p, want, st) != hipSuccess || !p) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    if (e) {
+        if (hipFreeAsync(e->p, st) != hipSuccess) (void)hipGetLastError();
+        e->p = p;
+        e->n = want;
+    } else {
+        g_scratch.push_back({dev, st, p, want});
+    }
+    return p;
+}
+
+// M = 2..16: activation pre-pass + k_mm4 (+ k_mmred when K is split), with
+// the stream's scratch buffer. Returns QMV_EUNSUPPORTED (nothing enqueued)
+// when the buffer cannot be had or the stream is being captured (a graph
+// must not hold a buffer that later eager calls on the stream reuse), so the
+// caller can fall back to the kernel that needs none.
 // Knobs (0 = default): segments of K, waves per workgroup (4 or 8).
 int launch_mm4(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N, int K,
                int force_S, int force_waves, hipStream_t st) {
@@ -1404,11 +1449,9 @@ int launch_mm4(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* 
     const size_t xa_bytes = (size_t)(K / 32) * 2048 + (size_t)nchunks * 64;
     const size_t off_part = (xa_bytes + 255) & ~(size_t)255;
     const size_t part_bytes = S > 1 ? (size_t)S * M * N * sizeof(float) : 0;
-    void* scratch = nullptr;
-    if (hipMallocAsync(&scratch, off_part + part_bytes, st) != hipSuccess || !scratch) {
-        (void)hipGetLastError();
-        return QMV_EUNSUPPORTED;
-    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    void* scratch = stream_scratch(st, off_part + part_bytes);
+    if (!scratch) return QMV_EUNSUPPORTED;
     uint8_t* xa = (uint8_t*)scratch;
     float* part = S > 1 ? (float*)(xa + off_part) : nullptr;
     hipLaunchKernelGGL(k_xprep, dim3((unsigned)nchunks, 4), dim3(256), 0, st, X, ldx, M, K, xa);
@@ -1428,7 +1471,6 @@ int launch_mm4(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* 
                            ldy);
         rc = check_launch("qmv split-K reduction");
     }
-    if (hipFreeAsync(scratch, st) != hipSuccess && rc == QMV_OK) rc = fail(QMV_EHIP, "qmv: hipFreeAsync failed");
     return rc;
 }
 

@@ -32,14 +32,17 @@
  *  - All array arguments are DEVICE pointers, owned by the caller. The
  *    library never synchronizes; each call only enqueues work on `stream`
  *    (a hipStream_t; NULL = the null stream) and returns. The only memory it
- *    takes is for the dense Q4_0 calls with M >= 2: a stream-ordered scratch
- *    buffer, taken with hipMallocAsync and released with hipFreeAsync on
- *    `stream` within the same call, of K/32 * 2 KiB + ceil(K/512) * 64 bytes
- *    (the activations converted to the matrix-core operand layout) plus, when
- *    K is split over up to 16 workgroups per tile, 4 * S * M * N bytes of
- *    partial sums. If it cannot be had, or if `stream` is being captured into
- *    a HIP graph, the call uses a (slower) kernel that needs no scratch, so
- *    every call can be captured.
+ *    takes is for the dense Q4_0 calls with M >= 2: a scratch buffer per
+ *    (device, stream), taken with hipMallocAsync on that stream at the first
+ *    call that needs it (grown the same way, old buffer released with
+ *    hipFreeAsync in stream order) and kept until the process ends; a call
+ *    needs K/32 * 2 KiB + ceil(K/512) * 64 bytes (the activations converted
+ *    to the matrix-core operand layout) plus, when K is split over up to 16
+ *    workgroups per tile, 4 * S * M * N bytes of partial sums, rounded up to
+ *    whole MiB. If it cannot be had, or if `stream` is being captured into a
+ *    HIP graph, the call uses a (slower) kernel that needs no scratch, so
+ *    every call can be captured. Calls on one stream are ordered by the
+ *    stream and share its buffer safely.
  *  - Arguments are validated on the host before any HIP call. A rejected call
  *    launches nothing, returns a negative status and sets a thread-local
  *    message readable with qmv_last_error().
