@@ -58,6 +58,14 @@ def _load():
         lib.oracle_qmv.argtypes = [I, P, S, P, S, I, I, I, P, P, S, I]
         lib.oracle_qmv_id.restype = I
         lib.oracle_qmv_id.argtypes = [I, P, S, S, I, P, S, P, I, I, P, I, I, P, P, S, I]
+        lib.oracle_qmv_id_swiglu.restype = I
+        lib.oracle_qmv_id_swiglu.argtypes = [I, P, S, S, I, P, S, P, I, I, P, I, I, P, P, S, I]
+        lib.oracle_silu.restype = D
+        lib.oracle_silu.argtypes = [D]
+        lib.oracle_swiglu.restype = I
+        lib.oracle_swiglu.argtypes = [P, S, I, I, P, S]
+        lib.oracle_moe_wsum.restype = I
+        lib.oracle_moe_wsum.argtypes = [P, P, S, P, I, I, I, P, P, S]
         lib.oracle_max_threads.restype = I
         _lib = lib
     return _lib
@@ -131,6 +139,88 @@ def qmv_id(qtype, W: np.ndarray, X: np.ndarray, ids: np.ndarray, N: int, K: int,
     if rc != 0:
         raise ValueError(f"oracle_qmv_id failed ({rc})")
     return Y, A
+
+
+def silu(z: float) -> float:
+    """silu(z) = z / (1 + exp(-z)) in fp64."""
+    return _load().oracle_silu(float(z))
+
+
+def swiglu(G: np.ndarray, I: Optional[int] = None) -> np.ndarray:
+    """H[r, i] = silu(G[r, i]) * G[r, I + i] in fp64; G fp32 [rows, >= 2I] (gate half first)."""
+    G = np.ascontiguousarray(G, dtype=np.float32)
+    if G.ndim == 1:
+        G = G[None, :]
+    rows, ldg = G.shape
+    I = ldg // 2 if I is None else I
+    H = np.empty((rows, I), dtype=np.float64)
+    if _load().oracle_swiglu(_ptr(G), ldg, rows, I, _ptr(H), I) != 0:
+        raise ValueError("bad arguments")
+    return H
+
+
+def qmv_id_swiglu(qtype, W: np.ndarray, G: np.ndarray, ids: np.ndarray, N: int, K: int,
+                  expert_scale: Optional[np.ndarray] = None, nthreads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+    """Expert-indexed product over SwiGLU rows: X[t] = silu(G[t, :K]) * G[t, K:2K].
+
+    W uint8 [E, N, ldw]; G fp32 [n_tokens, >= 2K]; ids uint32 [n_tokens, top_k].
+    Returns (Y, A) fp64 [n_tokens*top_k, N]."""
+    W = np.ascontiguousarray(W, dtype=np.uint8)
+    G = np.ascontiguousarray(G, dtype=np.float32)
+    ids = np.ascontiguousarray(ids, dtype=np.uint32)
+    if ids.ndim == 1:
+        ids = ids[:, None]
+    E, Nw, ldw = W.shape
+    n_tokens, top_k = ids.shape
+    if G.shape[0] != n_tokens:
+        raise ValueError("G rows must equal n_tokens")
+    es = None if expert_scale is None else np.ascontiguousarray(expert_scale, dtype=np.float32)
+    P = n_tokens * top_k
+    Y = np.empty((P, N), dtype=np.float64)
+    A = np.empty((P, N), dtype=np.float64)
+    rc = _load().oracle_qmv_id_swiglu(_qt(qtype), _ptr(W), Nw * ldw, ldw, E, _ptr(G), G.shape[1], _ptr(ids),
+                                      n_tokens, top_k, None if es is None else _ptr(es), N, K,
+                                      _ptr(Y), _ptr(A), N, nthreads)
+    if rc != 0:
+        raise ValueError(f"oracle_qmv_id_swiglu failed ({rc})")
+    return Y, A
+
+
+def moe_wsum(Y: np.ndarray, w: np.ndarray, top_k: int, YA: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """out[t, n] = sum_s w[t*top_k + s] * Y[t*top_k + s, n] in slot order (fp64).
+
+    Y fp64 [n_tokens*top_k, N]; w fp32 [n_tokens*top_k]. Returns (out, A) fp64
+    [n_tokens, N]; A = sum_s |w| * YA when YA is given, else sum_s |w * Y|."""
+    Y = np.ascontiguousarray(Y, dtype=np.float64)
+    w = np.ascontiguousarray(w, dtype=np.float32).reshape(-1)
+    P, N = Y.shape
+    if P % top_k or w.size != P:
+        raise ValueError("Y rows and w must hold n_tokens*top_k entries")
+    T = P // top_k
+    YA = None if YA is None else np.ascontiguousarray(YA, dtype=np.float64)
+    out = np.empty((T, N), dtype=np.float64)
+    A = np.empty((T, N), dtype=np.float64)
+    rc = _load().oracle_moe_wsum(_ptr(Y), None if YA is None else _ptr(YA), N, _ptr(w), T, top_k, N,
+                                 _ptr(out), _ptr(A), N)
+    if rc != 0:
+        raise ValueError(f"oracle_moe_wsum failed ({rc})")
+    return out, A
+
+
+def moe_down(qtype, W: np.ndarray, G: np.ndarray, ids: np.ndarray, w: np.ndarray, N: int, K: int,
+             expert_scale: Optional[np.ndarray] = None, nthreads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+    """The MoE down half of one layer: SwiGLU of each slot's gate_up row, the
+    expert-indexed down product, then the routing-weighted sum over slots.
+
+    G fp32 [n_tokens*top_k, >= 2K] (row t*top_k + s is slot s of token t);
+    ids uint32 [n_tokens, top_k]; w fp32 [n_tokens, top_k]. Returns (out, A)
+    fp64 [n_tokens, N]."""
+    ids = np.ascontiguousarray(ids, dtype=np.uint32)
+    if ids.ndim == 1:
+        ids = ids[None, :]
+    top_k = ids.shape[1]
+    Y, YA = qmv_id_swiglu(qtype, W, G, ids.reshape(-1, 1), N, K, expert_scale=expert_scale, nthreads=nthreads)
+    return moe_wsum(Y, np.asarray(w, dtype=np.float32).reshape(-1), top_k, YA=YA)
 
 
 def max_threads() -> int:

@@ -46,7 +46,14 @@
  * routing weights of the weighted sum that follows; since that sum is linear,
  * scaling the id output row is the same product).
  *
- * Every function returns 0 on success and a negative value on bad arguments.
+ * MoE steps around the expert-indexed product (same page, blocks B12 and
+ * B14): SwiGLU of the gate_up rows, silu(gate) * up, which becomes the down
+ * projection's activation rows, and the routing-weighted sum of the down
+ * rows over each token's top_k slots. Composed in that order (gate_up id,
+ * SwiGLU, down id, weighted sum) they are the MoE feed-forward of one layer.
+ *
+ * Every function returns 0 on success and a negative value on bad arguments
+ * (oracle_silu returns its value).
  */
 #include <math.h>
 #include <stddef.h>
@@ -121,6 +128,18 @@ static void dot_row(const double* w, const float* x, int K, double* y, double* a
     if (a) *a = m;
 }
 
+/* The same sum for an fp64 activation row. */
+static void dot_row_f64(const double* w, const double* x, int K, double* y, double* a) {
+    double s = 0.0, m = 0.0;
+    for (int k = 0; k < K; ++k) {
+        double p = w[k] * x[k];
+        s += p;
+        m += fabs(p);
+    }
+    *y = s;
+    if (a) *a = m;
+}
+
 static void set_threads(int nthreads) {
 #ifdef _OPENMP
     if (nthreads > 0) omp_set_num_threads(nthreads);
@@ -170,10 +189,10 @@ int oracle_qmv(int qtype, const uint8_t* W, size_t ldw, const float* X, size_t l
  * sc = expert_scale[e] when expert_scale is given, else 1.
  * A receives |sc| * sum_k |w_e[n][k] * X[t*ldx + k]|.
  */
-int oracle_qmv_id(int qtype, const uint8_t* W, size_t expert_stride, size_t ldw, int n_experts,
-                  const float* X, size_t ldx, const uint32_t* ids, int n_tokens, int top_k,
-                  const float* expert_scale, int N, int K, double* Y, double* A, size_t ldy,
-                  int nthreads) {
+static int qmv_id_core(int qtype, const uint8_t* W, size_t expert_stride, size_t ldw, int n_experts,
+                       const float* X, const double* Xd, size_t ldx, const uint32_t* ids, int n_tokens,
+                       int top_k, const float* expert_scale, int N, int K, double* Y, double* A, size_t ldy,
+                       int nthreads) {
     int bb = block_bytes(qtype);
     if (bb < 0 || n_experts <= 0 || n_tokens < 0 || top_k <= 0 || N < 0 || K <= 0 || K % ORACLE_QK) return -1;
     if (ldw < (size_t)(K / ORACLE_QK) * bb || ldx < (size_t)K || ldy < (size_t)N) return -1;
@@ -199,7 +218,10 @@ int oracle_qmv_id(int qtype, const uint8_t* W, size_t expert_stride, size_t ldw,
                     const uint8_t* row = W + (size_t)e * expert_stride + (size_t)n * ldw;
                     double y, a;
                     oracle_dequant_row(qtype, row, K, w);
-                    dot_row(w, X + (size_t)t * ldx, K, &y, &a);
+                    if (Xd)
+                        dot_row_f64(w, Xd + (size_t)t * ldx, K, &y, &a);
+                    else
+                        dot_row(w, X + (size_t)t * ldx, K, &y, &a);
                     Y[(size_t)p * ldy + n] = sc * y;
                     if (A) A[(size_t)p * ldy + n] = fabs(sc) * a;
                 }
@@ -208,6 +230,95 @@ int oracle_qmv_id(int qtype, const uint8_t* W, size_t expert_stride, size_t ldw,
         }
     }
     return err;
+}
+
+int oracle_qmv_id(int qtype, const uint8_t* W, size_t expert_stride, size_t ldw, int n_experts,
+                  const float* X, size_t ldx, const uint32_t* ids, int n_tokens, int top_k,
+                  const float* expert_scale, int N, int K, double* Y, double* A, size_t ldy,
+                  int nthreads) {
+    if (!X) return -1;
+    return qmv_id_core(qtype, W, expert_stride, ldw, n_experts, X, NULL, ldx, ids, n_tokens, top_k,
+                       expert_scale, N, K, Y, A, ldy, nthreads);
+}
+
+/*
+ * SiLU, the sigmoid-weighted linear unit: silu(z) = z * sigmoid(z)
+ * = z / (1 + e^(-z)). For z below about -709, e^(-z) overflows to +Inf and
+ * the quotient is -0, the limit; NaN propagates.
+ */
+double oracle_silu(double z) {
+    return z / (1.0 + exp(-z));
+}
+
+/*
+ * SwiGLU over rows of a gate_up product (the `moe_swiglu_batch_encode` step,
+ * block B12 of `MlxModelWeights::encode_one_layer` on the hf2q page
+ * `src/inference/models/gemma4/gpu_full_attn.rs`; the same page set writes the
+ * dense form as down(silu(gate(x)) * up(x)) in the doc of its drafter MLP).
+ * Row r of G holds 2*I values: the gate half in [0, I), the up half in
+ * [I, 2I). The pages never say which half comes first; gate first is the
+ * order the buffer name `gate_up` gives.
+ *   H[r*ldh + i] = silu(G[r*ldg + i]) * G[r*ldg + I + i],  i < I,
+ * all in fp64 from the fp32 inputs.
+ */
+int oracle_swiglu(const float* G, size_t ldg, int rows, int I, double* H, size_t ldh) {
+    if (rows < 0 || I < 0 || ldg < (size_t)2 * I || ldh < (size_t)I) return -1;
+    for (int r = 0; r < rows; ++r)
+        for (int i = 0; i < I; ++i) {
+            const float* g = G + (size_t)r * ldg;
+            H[(size_t)r * ldh + i] = oracle_silu((double)g[i]) * (double)g[I + i];
+        }
+    return 0;
+}
+
+/*
+ * Expert-indexed product whose activation rows are the SwiGLU of gate_up
+ * rows (the down projection of the MoE block, B13 after B12): the
+ * expert-indexed product above with X[t] = H[t], H = oracle_swiglu(G) over
+ * n_tokens rows of 2*K values (row stride ldg).
+ */
+int oracle_qmv_id_swiglu(int qtype, const uint8_t* W, size_t expert_stride, size_t ldw, int n_experts,
+                         const float* G, size_t ldg, const uint32_t* ids, int n_tokens, int top_k,
+                         const float* expert_scale, int N, int K, double* Y, double* A, size_t ldy,
+                         int nthreads) {
+    if (!G || n_tokens < 0 || K <= 0 || ldg < (size_t)2 * K) return -1;
+    double* H = (double*)malloc(sizeof(double) * (size_t)K * (size_t)(n_tokens > 0 ? n_tokens : 1));
+    if (!H) return -2;
+    int rc = oracle_swiglu(G, ldg, n_tokens, K, H, (size_t)K);
+    if (rc == 0)
+        rc = qmv_id_core(qtype, W, expert_stride, ldw, n_experts, NULL, H, (size_t)K, ids, n_tokens, top_k,
+                         expert_scale, N, K, Y, A, ldy, nthreads);
+    free(H);
+    return rc;
+}
+
+/*
+ * Routing-weighted sum over the top_k slots of each token (the
+ * `moe_weighted_sum_encode` step, block B14 of `encode_one_layer` on the same
+ * page; its weights are the routing weights that the routing step has
+ * already multiplied by the per-expert scale):
+ *   out[t*ldo + n] = sum_{s < top_k} w[t*top_k + s] * Y[(t*top_k + s)*ldy + n],
+ * summed in slot order in fp64. A (nullable) receives
+ * sum_s |w[t*top_k + s]| * YA[(t*top_k + s)*ldy + n] when YA is given (the
+ * magnitudes of the rows' own sums), else sum_s |w * Y|.
+ */
+int oracle_moe_wsum(const double* Y, const double* YA, size_t ldy, const float* w, int n_tokens, int top_k,
+                    int N, double* out, double* A, size_t ldo) {
+    if (n_tokens < 0 || top_k <= 0 || N < 0 || ldy < (size_t)N || ldo < (size_t)N) return -1;
+    for (int t = 0; t < n_tokens; ++t)
+        for (int n = 0; n < N; ++n) {
+            double s = 0.0, m = 0.0;
+            for (int k = 0; k < top_k; ++k) {
+                size_t p = (size_t)t * top_k + k;
+                double wk = (double)w[p];
+                double y = Y[p * ldy + n];
+                s += wk * y;
+                m += YA ? fabs(wk) * YA[p * ldy + n] : fabs(wk * y);
+            }
+            out[(size_t)t * ldo + n] = s;
+            if (A) A[(size_t)t * ldo + n] = m;
+        }
+    return 0;
 }
 
 int oracle_max_threads(void) {

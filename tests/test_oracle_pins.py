@@ -315,3 +315,119 @@ def test_dense_rejects_bad_shapes():
         oracle.qmv("q4_0", W, np.ones((1, 33), np.float32), K=33)
     with pytest.raises(ValueError):
         oracle.qmv("q4_0", W, np.ones((1, 64), np.float32))  # row shorter than K/32 blocks
+
+
+# --------------------------------------------------------------------------
+# MoE steps around the expert-indexed call: SwiGLU and the weighted sum.
+# --------------------------------------------------------------------------
+def _silu_tanh(z):
+    """silu through the identity z * sigmoid(z) = (z / 2) * (1 + tanh(z / 2))."""
+    z = np.asarray(z, dtype=np.float64)
+    return 0.5 * z * (1.0 + np.tanh(0.5 * z))
+
+
+def test_silu_closed_forms_limits_and_odd_part():
+    assert oracle.silu(0.0) == 0.0
+    assert abs(oracle.silu(1.0) - 0.5 * (1.0 + math.tanh(0.5))) <= 2.0 ** -52
+    assert abs(oracle.silu(-1.0) - (-0.5) * (1.0 - math.tanh(0.5))) <= 2.0 ** -53
+    # silu(z) = z * (1 - e^-z / (1 + e^-z)); at z = 40 the correction is
+    # 4.2e-18, below half an ulp of 40, so the rounded value is 40 exactly.
+    assert oracle.silu(40.0) == 40.0
+    # e^800 overflows: the value is the limit, -0 (sign kept).
+    v = oracle.silu(-800.0)
+    assert v == 0.0 and math.copysign(1.0, v) == -1.0
+    assert math.isnan(oracle.silu(float("nan")))
+    zs = np.linspace(-30.0, 30.0, 1201)
+    for z in zs:
+        s_pos, s_neg = oracle.silu(z), oracle.silu(-z)
+        # silu(z) - silu(-z) = z (sigmoid(z) + sigmoid(-z) = 1)
+        assert abs((s_pos - s_neg) - z) <= 4 * 2.0 ** -52 * max(1.0, abs(z))
+        assert abs(s_pos - _silu_tanh(z)) <= 8 * 2.0 ** -52 * max(1.0, abs(z))
+
+
+def test_swiglu_gate_is_the_first_half_of_each_row():
+    G = np.array([[1.0, 2.0, 2.0, 1.0],
+                  [0.0, 5.0, 7.0, -3.0],
+                  [-2.0, 0.5, 0.0, 4.0]], dtype=np.float32)
+    H = oracle.swiglu(G)
+    want = np.array([[_silu_tanh(1.0) * 2.0, _silu_tanh(2.0) * 1.0],
+                     [0.0, _silu_tanh(5.0) * -3.0],
+                     [_silu_tanh(-2.0) * 0.0, _silu_tanh(0.5) * 4.0]])
+    assert np.allclose(H, want, rtol=1e-15, atol=0)
+    # swapped halves would give silu(2) * 1 = 1.7616 in place of silu(1) * 2 = 1.4621
+    assert abs(H[0, 0] - 1.4621171572600098) < 1e-15
+    assert H[1, 0] == 0.0 and H[2, 0] == 0.0
+
+
+@pytest.mark.parametrize("qtype", ["q4_0", "q8_0"])
+def test_id_swiglu_with_saturated_gates_equals_id_on_scaled_up_rows(qtype):
+    """Gate 40 gives silu = 40 exactly and gate -800 gives -0, so the SwiGLU
+    rows are 40 * up (or 0) exactly; the product must then equal the pinned
+    expert-indexed call on those rows bit for bit."""
+    from block_quantized_weight_qmatmul_amd import synth
+    E, N, K, T, k = 6, 12, 128, 3, 2
+    W = synth.make_weights(qtype, E * N, K, cfg=95).reshape(E, N, -1)
+    r = np.random.default_rng(95)
+    up = r.integers(-100, 101, (T, K)).astype(np.float32)
+    mask = r.random((T, K)) < 0.6
+    gate = np.where(mask, 40.0, -800.0).astype(np.float32)
+    G = np.concatenate([gate, up], axis=1)
+    ids = np.array([[5, 1], [2, 2], [0, 4]], dtype=np.uint32)
+    sc = np.array([0.5, 1.25, 2.0, 1.0, 0.75, 1.5], dtype=np.float32)
+    Y, A = oracle.qmv_id_swiglu(qtype, W, G, ids, N, K, expert_scale=sc)
+    X = np.where(mask, 40.0 * up, 0.0).astype(np.float32)
+    Yr, Ar = oracle.qmv_id(qtype, W, X, ids, N, K, expert_scale=sc)
+    assert np.array_equal(Y, Yr) and np.array_equal(A, Ar)
+
+
+def test_weighted_sum_hand_derived_values():
+    # two tokens, three slots, two columns; row p of Y is [2p + 1, 2p + 2]
+    Y = np.arange(1, 13, dtype=np.float64).reshape(6, 2)
+    w = np.array([0.5, 0.25, 2.0, 1.0, -1.0, 0.125], dtype=np.float32)
+    out, A = oracle.moe_wsum(Y, w, 3)
+    # token 0: 0.5*[1,2] + 0.25*[3,4] + 2*[5,6]; token 1: [7,8] - [9,10] + [11,12]/8
+    assert np.array_equal(out, [[11.25, 14.0], [-0.625, -0.5]])
+    assert np.array_equal(A, [[11.25, 14.0], [17.375, 19.5]])
+    out1, _ = oracle.moe_wsum(Y, np.array([0, 1, 0, 0, 0, 1], np.float32), 3)
+    assert np.array_equal(out1, [[3.0, 4.0], [11.0, 12.0]])
+
+
+@pytest.mark.parametrize("qtype", ["q4_0", "q8_0"])
+def test_moe_down_composition_against_numpy_brute_force(qtype):
+    """SwiGLU -> expert-indexed down -> weighted sum, against a numpy fp64
+    evaluation that decodes the blocks itself and takes silu through tanh."""
+    from block_quantized_weight_qmatmul_amd import synth
+    E, N, K, T, k = 7, 10, 96, 3, 3
+    W = synth.make_weights(qtype, E * N, K, cfg=94).reshape(E, N, -1)
+    r = np.random.default_rng(94)
+    G = (r.standard_normal((T * k, 2 * K)) * 2).astype(np.float32)
+    ids = np.array([[6, 0, 3], [3, 3, 1], [2, 5, 4]], dtype=np.uint32)
+    w = r.random((T, k)).astype(np.float32)
+    sc = r.uniform(0.5, 1.5, E).astype(np.float32)
+    out, A = oracle.moe_down(qtype, W, G, ids, w, N, K, expert_scale=sc)
+
+    bb = oracle.BLOCK_BYTES[oracle.QTYPES[qtype]]
+
+    def deq(mat):
+        blk = mat.reshape(N, K // 32, bb)
+        d = blk[:, :, 0:2].copy().view("<f2").astype(np.float64)[:, :, 0]
+        if qtype == "q4_0":
+            lo = (blk[:, :, 2:] & 0x0F).astype(np.int64) - 8
+            hi = (blk[:, :, 2:] >> 4).astype(np.int64) - 8
+            c = np.concatenate([lo, hi], axis=2)
+        else:
+            c = blk[:, :, 2:].view(np.int8).astype(np.int64)
+        return (c * d[:, :, None]).reshape(N, K)
+
+    for t in range(T):
+        want = np.zeros(N)
+        mag = np.zeros(N)
+        for s in range(k):
+            g = G[t * k + s].astype(np.float64)
+            h = _silu_tanh(g[:K]) * g[K:]
+            e = int(ids[t, s])
+            prod = deq(W[e]) * h[None, :]
+            want += float(w[t, s]) * float(sc[e]) * prod.sum(axis=1)
+            mag += abs(float(w[t, s]) * float(sc[e])) * np.abs(prod).sum(axis=1)
+        assert np.all(np.abs(out[t] - want) <= 1e-12 * mag + 1e-300), t
+        assert np.allclose(A[t], mag, rtol=1e-12, atol=0)
