@@ -158,11 +158,17 @@ def m16_throughput(dev, steps=40):
             "pct_hbm_peak": round(100 * nbytes / t / 1e9 / HBM_PEAK_GBS, 2)}
 
 
-def moe_throughput(dev, T, steps=40):
+def moe_throughput(dev, T, steps=40, mode="id"):
     """Config 4 (Q4_0 MoE, 128 experts, top-8, hidden 2816, expert
-    intermediate 704): the gate_up and down id calls for T tokens, graph
-    replays over rotated stacks (16 for T = 1, 4 for T = 32). GB/s counts the
-    weights of the distinct selected experts (each streamed once per call)."""
+    intermediate 704) for T tokens, graph replays over rotated stacks (16 for
+    T = 1, 4 for T = 32). GB/s counts the weights of the distinct selected
+    experts (each streamed once per call).
+
+    mode "id": the gate_up and down id calls alone (down fed a synthetic x).
+    mode "ffn_fused": the MoE FFN of the tokens: gate_up id, then the
+    one-launch down half (SwiGLU + down + weighted sum), 2 launches.
+    mode "ffn_two_call": gate_up id, SwiGLU-fed down id, weighted sum,
+    3 launches."""
     import numpy as np
     import torch
 
@@ -176,6 +182,7 @@ def moe_throughput(dev, T, steps=40):
         dd["ids"] = dd["ids"].to(torch.int32).contiguous()
         dd["Y_gu"] = torch.empty(T * gu.top_k, gu.N, device=dev)
         dd["Y_dn"] = torch.empty(T * gu.top_k, dn.N, device=dev)
+        dd["out"] = torch.empty(T, dn.N, device=dev)
         nexp = synth.distinct(d["ids"])
         nbytes += nexp * (gu.N * (gu.K // 32) + dn.N * (dn.K // 32)) * 18
         sets.append(dd)
@@ -183,15 +190,24 @@ def moe_throughput(dev, T, steps=40):
 
     def step(dd):
         qmv.qmv_id("q4_0", dd["W_gate_up"], dd["X_gate_up"], dd["ids"], dd["Y_gu"], gu.N, gu.K,
-                   expert_scale=dd["expert_scale"])
-        qmv.qmv_id("q4_0", dd["W_down"], dd["X_down"], dd["ids"].view(-1, 1), dd["Y_dn"], dn.N, dn.K,
-                   expert_scale=dd["expert_scale"])
+                   expert_scale=None if mode != "id" else dd["expert_scale"])
+        if mode == "id":
+            qmv.qmv_id("q4_0", dd["W_down"], dd["X_down"], dd["ids"].view(-1, 1), dd["Y_dn"], dn.N, dn.K,
+                       expert_scale=dd["expert_scale"])
+        elif mode == "ffn_fused":
+            qmv.qmv_moe_down("q4_0", dd["W_down"], dd["Y_gu"], dd["ids"], dd["weights"], dd["out"], dn.N, dn.K,
+                             expert_scale=dd["expert_scale"])
+        else:
+            qmv.qmv_id_swiglu("q4_0", dd["W_down"], dd["Y_gu"], dd["ids"].view(-1, 1), dd["Y_dn"], dn.N, dn.K,
+                              expert_scale=dd["expert_scale"])
+            qmv.qmv_moe_wsum(dd["Y_dn"], dd["weights"], dd["out"], gu.top_k)
     graphs = capture_steps(step, sets)
     t = time_graphs(graphs, steps, 4) / steps
     del graphs
-    return {"workload": f"q4_0_moe_e128_top8_h2816_i704_t{T}", "weight_bytes_per_step": round(nbytes),
-            "us_per_step": round(t * 1e6, 2), "GBps": round(nbytes / t / 1e9, 1),
-            "pct_hbm_peak": round(100 * nbytes / t / 1e9 / HBM_PEAK_GBS, 2)}
+    launches = {"id": 2, "ffn_fused": 2, "ffn_two_call": 3}[mode]
+    return {"workload": f"q4_0_moe_e128_top8_h2816_i704_t{T}", "mode": mode, "launches": launches,
+            "weight_bytes_per_step": round(nbytes), "us_per_step": round(t * 1e6, 2),
+            "GBps": round(nbytes / t / 1e9, 1), "pct_hbm_peak": round(100 * nbytes / t / 1e9 / HBM_PEAK_GBS, 2)}
 
 
 def cpu_baseline(target_s: float):
@@ -377,6 +393,10 @@ def main():
         extra["m16"] = m16_throughput(dev)
         extra["moe_t1"] = moe_throughput(dev, 1)
         extra["moe_t32"] = moe_throughput(dev, 32)
+        extra["moe_ffn_t1_fused"] = moe_throughput(dev, 1, mode="ffn_fused")
+        extra["moe_ffn_t1_two_call"] = moe_throughput(dev, 1, mode="ffn_two_call")
+        extra["moe_ffn_t32_two_call"] = moe_throughput(dev, 32, mode="ffn_two_call")
+        extra["moe_ffn_t32_fused"] = moe_throughput(dev, 32, mode="ffn_fused")
     del sets
     torch.cuda.empty_cache()
 

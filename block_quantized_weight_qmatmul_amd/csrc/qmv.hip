@@ -244,6 +244,45 @@ __device__ __forceinline__ void stage_x(float* xs, const float* __restrict__ x, 
     }
 }
 
+// SiLU, z * sigmoid(z) = z / (1 + e^-z), in fp32. Below z = -88.7 e^-z
+// overflows and the quotient is -0, the limit; NaN propagates.
+__device__ __forceinline__ float silu_f(float z) { return z / (1.f + expf(-z)); }
+
+// rows SwiGLU rows into the padded LDS layout, one after another (row r at
+// xs + r * xstride): row r of the source holds 2K values at g + r * ldg, the
+// gate half first, and its staged row is silu(gate) * up. NT threads, four
+// 16-byte chunks of each half in flight per thread.
+template <int NT>
+__device__ __forceinline__ void stage_swiglu(float* xs, size_t xstride, const float* __restrict__ g, size_t ldg,
+                                             int rows, int K) {
+    typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
+    const int nch = K >> 2;
+    const int total = rows * nch;
+    for (int c0 = threadIdx.x; c0 < total; c0 += 4 * NT) {
+        f32x4u a[4], b[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = c0 + i * NT;
+            if (c < total) {
+                const int r = c / nch, cc = c - r * nch;
+                const float* src = g + (size_t)r * ldg + 4 * cc;
+                a[i] = *reinterpret_cast<const f32x4u*>(src);
+                b[i] = *reinterpret_cast<const f32x4u*>(src + K);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = c0 + i * NT;
+            if (c < total) {
+                const int r = c / nch, cc = c - r * nch;
+                *reinterpret_cast<float4*>(xs + (size_t)r * xstride + (cc >> 4) * XS_PAIR + 4 * (cc & 15)) =
+                    make_float4(silu_f(a[i].x) * b[i].x, silu_f(a[i].y) * b[i].y, silu_f(a[i].z) * b[i].z,
+                                silu_f(a[i].w) * b[i].w);
+            }
+        }
+    }
+}
+
 // v + (v of another lane chosen by a DPP control); lanes outside row_mask
 // add 0.
 template <int CTRL, int ROW_MASK = 0xF>
@@ -272,9 +311,10 @@ __device__ __forceinline__ float lane_group_sum(float v) {
 // group takes pairs j, j + LPR, ... of that row; each step is one pair of
 // RPT rows, and the loads of the next step are issued before the current one
 // is decoded (one step of register prefetch). The activation row x is staged
-// into LDS after the first loads are in flight. Each row's sum is reduced over
-// its lane group and written to y[row] * out_scale.
-template <int QT, int LPR, int RPT, int WAVES>
+// into LDS after the first loads are in flight (with SW, x holds 2K values and
+// the staged row is their SwiGLU). Each row's sum is reduced over its lane
+// group and written to y[row] * out_scale.
+template <int QT, int LPR, int RPT, int WAVES, bool SW = false>
 __device__ __forceinline__ void m1_stream(const uint8_t* __restrict__ W, size_t ldw, const float* __restrict__ x,
                                           float* __restrict__ y, int N, int K, long first_tile, long tile_stride,
                                           float out_scale, float* xs) {
@@ -304,7 +344,10 @@ __device__ __forceinline__ void m1_stream(const uint8_t* __restrict__ W, size_t 
         }
     };
     issue(tile, 0);
-    stage_x<WAVES * 64, (KMAX_STAGE / 4 + WAVES * 64 - 1) / (WAVES * 64)>(xs, x, K);
+    if constexpr (SW)
+        stage_swiglu<WAVES * 64>(xs, 0, x, 0, 1, K);
+    else
+        stage_x<WAVES * 64, (KMAX_STAGE / 4 + WAVES * 64 - 1) / (WAVES * 64)>(xs, x, K);
     __syncthreads();
     float tot[RPT];
 #pragma unroll
@@ -938,7 +981,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // y_m = sum over row `wr` (K/32 blocks) of w * X[xrow[m]], m < M; lane-partial.
-template <int QT, int MT>
+// With SW the rows of X hold 2K values and the activation is their SwiGLU,
+// silu(X[k]) * X[K + k].
+template <int QT, int MT, bool SW = false>
 __device__ __forceinline__ void generic_row(const uint8_t* __restrict__ wr, const float* __restrict__ X,
                                             const size_t* xoff, int M, int K, int lane, float* acc) {
     constexpr int BB = block_bytes(QT);
@@ -952,11 +997,12 @@ __device__ __forceinline__ void generic_row(const uint8_t* __restrict__ wr, cons
         for (int m = 0; m < MT; ++m) {
             if (m < M) {
                 const float* xp = X + xoff[m] + (size_t)b * QK;
+                auto xv = [&](int i) { return SW ? silu_f(xp[i]) * xp[K + i] : xp[i]; };
                 float s0 = 0.f, s1 = 0.f;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    s0 = fmaf(c[i], xp[i], s0);
-                    s1 = fmaf(c[16 + i], xp[16 + i], s1);
+                    s0 = fmaf(c[i], xv(i), s0);
+                    s1 = fmaf(c[16 + i], xv(16 + i), s1);
                 }
                 acc[m] = fmaf(d, s0 + s1, acc[m]);
             }
@@ -993,6 +1039,8 @@ __global__ __launch_bounds__(256) void k_generic(const uint8_t* __restrict__ W, 
 //    covers p too).
 //  * otherwise gather every pair q >= p with ids[q] == e (in order) and
 //    compute their rows of this tile, streaming expert e's rows once.
+// With SW the rows of X hold 2K values, gate then up, and the activation of
+// token t is silu(gate) * up (the MoE down projection after SwiGLU).
 // ---------------------------------------------------------------------------
 // Decoded weights of one pair of blocks, for reuse against several
 // activation vectors: w[0..31] block 0, w[32..63] block 1, as (code - 8) / 16
@@ -1032,9 +1080,9 @@ __device__ __forceinline__ void decode_pair(const uint32_t* r, float* w, float& 
 // m1_stream for nx <= MX activation vectors at once (the expert-indexed
 // product when several (token, slot) pairs select one expert): each weight
 // pair is loaded and decoded once and multiplied into every vector. The nx
-// vectors x[i] (rows of X at xoff[i]) are staged into LDS one after another;
-// results go to y[i][row] * out_scale.
-template <int QT, int LPR, int WAVES, int MX>
+// vectors x[i] (rows of X at xoff[i], or their SwiGLU with SW) are staged
+// into LDS one after another; results go to y[i][row] * out_scale.
+template <int QT, int LPR, int WAVES, int MX, bool SW = false>
 __device__ __forceinline__ void m1_stream_mx(const uint8_t* __restrict__ W, size_t ldw, const float* __restrict__ X,
                                              const size_t* xoff, float* const* y, int nx, int N, int K,
                                              long first_tile, long tile_stride, float out_scale, float* xs) {
@@ -1062,9 +1110,14 @@ __device__ __forceinline__ void m1_stream_mx(const uint8_t* __restrict__ W, size
     };
     issue(tile, 0);
 #pragma unroll
-    for (int i = 0; i < MX; ++i)
-        if (i < nx)
-            stage_x<WAVES * 64, (KMAX_STAGE / 4 + WAVES * 64 - 1) / (WAVES * 64)>(xs + i * xstride, X + xoff[i], K);
+    for (int i = 0; i < MX; ++i) {
+        if (i < nx) {
+            if constexpr (SW)
+                stage_swiglu<WAVES * 64>(xs + i * xstride, 0, X + xoff[i], 0, 1, K);
+            else
+                stage_x<WAVES * 64, (KMAX_STAGE / 4 + WAVES * 64 - 1) / (WAVES * 64)>(xs + i * xstride, X + xoff[i], K);
+        }
+    }
     __syncthreads();
     float tot[MX];
 #pragma unroll
@@ -1126,7 +1179,7 @@ __device__ __forceinline__ void m1_stream_mx(const uint8_t* __restrict__ W, size
 constexpr int ID_MAX_LIST = 1024;  // pairs one leader can serve in one pass
 constexpr int ID_MX = 8;           // activation vectors streamed together
 
-template <int QT, int LPR, int RPT, int WAVES>
+template <int QT, int LPR, int RPT, int WAVES, bool SW>
 __global__ __launch_bounds__(WAVES * 64) void k_id(const uint8_t* __restrict__ W, size_t estride, size_t ldw,
                                                    int n_experts, const float* __restrict__ X, size_t ldx,
                                                    const uint32_t* __restrict__ ids, int n_pairs, int top_k,
@@ -1178,8 +1231,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_id(const uint8_t* __restrict__ W
         const float sc = (escale ? escale[e] : 1.f) * PairTraits<QT>::OUT_SCALE;
         if (count == 1) {
             const int t = p / top_k;
-            m1_stream<QT, LPR, RPT, WAVES>(We, ldw, X + (size_t)t * ldx, Y + (size_t)p * ldy, N, K, blockIdx.x,
-                                           gridDim.x, sc, xs);
+            m1_stream<QT, LPR, RPT, WAVES, SW>(We, ldw, X + (size_t)t * ldx, Y + (size_t)p * ldy, N, K, blockIdx.x,
+                                               gridDim.x, sc, xs);
             return;
         }
         // Several pairs: each weight pair is read once for up to mxcap of them.
@@ -1195,7 +1248,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_id(const uint8_t* __restrict__ W
                 yp[i] = Y + (size_t)q * ldy;
             }
             if (c0 > 0) __syncthreads();  // the previous vectors' LDS reads are done
-            m1_stream_mx<QT, LPR, WAVES, ID_MX>(We, ldw, X, xoff, yp, nx, N, K, blockIdx.x, gridDim.x, sc, xs);
+            m1_stream_mx<QT, LPR, WAVES, ID_MX, SW>(We, ldw, X, xoff, yp, nx, N, K, blockIdx.x, gridDim.x, sc, xs);
         }
         return;
     }
@@ -1210,7 +1263,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_id(const uint8_t* __restrict__ W
         for (int m = 0; m < 16; ++m) xoff[m] = (size_t)(s_list[c0 + (m < M ? m : 0)] / top_k) * ldx;
         for (long n = tile_row0 + wave; n < tile_row0 + ROWS_PER_WG && n < N; n += WAVES) {
             float acc[16];
-            generic_row<QT, 16>(We + n * ldw, X, xoff, M, K, lane, acc);
+            generic_row<QT, 16, SW>(We + n * ldw, X, xoff, M, K, lane, acc);
 #pragma unroll
             for (int m = 0; m < 16; ++m) {
                 if (m < M) {
@@ -1222,6 +1275,121 @@ __global__ __launch_bounds__(WAVES * 64) void k_id(const uint8_t* __restrict__ W
     }
     // The host launches at most ID_MAX_LIST pairs at a time, so the list
     // always holds every pair of this launch that selects e.
+}
+
+// ---------------------------------------------------------------------------
+// Routing-weighted sum over slots: out[t][n] = sum_s w[t*top_k + s] *
+// Y[t*top_k + s][n], accumulated in slot order with one fma per slot.
+// One thread per output element; the grid covers tokens x column tiles.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_wsum(const float* __restrict__ Y, size_t ldy, const float* __restrict__ wts,
+                                              int top_k, int N, long col_tiles, float* __restrict__ out, size_t ldo) {
+    const long t = (long)blockIdx.x / col_tiles;
+    const long n = ((long)blockIdx.x - t * col_tiles) * 256 + threadIdx.x;
+    if (n >= N) return;
+    const float* yp = Y + (size_t)t * top_k * ldy + n;
+    const float* wp = wts + (size_t)t * top_k;
+    float acc = 0.f;
+    for (int s = 0; s < top_k; ++s) acc = fmaf(wp[s], yp[(size_t)s * ldy], acc);
+    out[(size_t)t * ldo + n] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// MoE down half of one token in one launch: SwiGLU of each slot's gate_up
+// row, the down product of the slot's expert, and the weighted sum over
+// slots. grid = (row tiles of R = 64 / LPR rows, tokens). Every slot's
+// SwiGLU row is staged into LDS first; wave w then streams rows
+// row0 .. row0 + R - 1 of the experts of slots w, w + WAVES, ... (LPR lanes
+// per row, one step of register prefetch across slots) and puts each row's
+// sum times expert_scale[e] into red[s][r]. Thread r < R then writes
+// out[t][row0 + r] = sum_s w_s * red[s][r] in slot order. An id outside
+// [0, n_experts) makes the token's rows NaN and sets *err_flag.
+// Requires K % 64 == 0, top_k <= MD_MAX_TOPK, 4-byte aligned W, ldw and
+// expert stride, and top_k staged rows within the LDS the host grants.
+// ---------------------------------------------------------------------------
+constexpr int MD_MAX_TOPK = 64;
+
+template <int QT, int LPR, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void k_moe_down(const uint8_t* __restrict__ W, size_t estride, size_t ldw,
+                                                         int n_experts, const float* __restrict__ G, size_t ldg,
+                                                         const uint32_t* __restrict__ ids,
+                                                         const float* __restrict__ wts, int top_k,
+                                                         float* __restrict__ out, size_t ldo, int N, int K,
+                                                         const float* __restrict__ escale, int* __restrict__ err_flag) {
+    using T = PairTraits<QT>;
+    constexpr int DW = T::DW, PB = DW * 4;
+    constexpr int R = 64 / LPR;
+    __shared__ float red[MD_MAX_TOPK][R];
+    extern __shared__ __align__(16) float xs[];
+
+    const long t = blockIdx.y;
+    const long row0 = (long)blockIdx.x * R;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane / LPR, j = lane % LPR;
+    const int P = K >> 6;
+    const int IPT = (P + LPR - 1) / LPR;
+    const size_t xstride = (size_t)P * XS_PAIR;
+    const uint32_t* tids = ids + t * top_k;
+    long row = row0 + g;
+    row = row < N ? row : N - 1;
+
+    uint32_t nxt[DW];
+    // This lane's row of slot sl's expert; an id out of range reads expert 0
+    // (in bounds) and its result is replaced by NaN.
+    auto base = [&](int sl) {
+        uint32_t e = tids[sl];
+        e = e < (uint32_t)n_experts ? e : 0u;
+        return W + (size_t)e * estride + (size_t)row * ldw;
+    };
+    auto issue = [&](const uint8_t* b, int i) {
+        int p = j + i * LPR;
+        p = p < P ? p : P - 1;
+        load_pair<DW>(b + (size_t)p * PB, nxt);
+    };
+    int s = wave, it = 0;
+    const uint8_t* bn = W;
+    if (s < top_k) {
+        bn = base(s);
+        issue(bn, 0);
+    }
+    stage_swiglu<WAVES * 64>(xs, xstride, G + (size_t)t * top_k * ldg, ldg, top_k, K);
+    __syncthreads();
+    float tot = 0.f;
+    while (s < top_k) {  // uniform over the wave
+        uint32_t cur[DW];
+#pragma unroll
+        for (int d = 0; d < DW; ++d) cur[d] = nxt[d];
+        int it2 = it + 1, s2 = s;
+        if (it2 == IPT) {
+            it2 = 0;
+            s2 += WAVES;
+            if (s2 < top_k) bn = base(s2);
+        }
+        if (s2 < top_k) issue(bn, it2);
+        const int p = j + it * LPR;
+        if (p < P) tot += T::dot(cur, reinterpret_cast<const float4*>(xs + (size_t)s * xstride + p * XS_PAIR));
+        if (it == IPT - 1) {
+            const uint32_t e = tids[s];
+            const bool ok = e < (uint32_t)n_experts;
+            const float sc = T::OUT_SCALE * (escale && ok ? escale[e] : 1.f);
+            const float sum = lane_group_sum<LPR>(tot) * sc;
+            if (j == LPR - 1) red[s][g] = ok ? sum : __builtin_nanf("");
+            if (!ok && lane == 0 && err_flag) *err_flag = 1;
+            tot = 0.f;
+        }
+        s = s2;
+        it = it2;
+    }
+    __syncthreads();
+    if (threadIdx.x < R) {
+        const long r = row0 + threadIdx.x;
+        if (r < N) {
+            const float* wp = wts + t * top_k;
+            float acc = 0.f;
+            for (int k = 0; k < top_k; ++k) acc = fmaf(wp[k], red[k][threadIdx.x], acc);
+            out[(size_t)t * ldo + r] = acc;
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1537,7 +1705,7 @@ int dense(int qtype, const void* Wv, size_t ldw, const float* X, size_t ldx, flo
                              : launch_generic<QMV_Q8_0>(W, ldw, X, ldx, Y, ldy, M, N, K, st);
 }
 
-template <int QT, int LPR, int RPT>
+template <int QT, int LPR, int RPT, bool SW>
 int launch_id_t(const uint8_t* W, size_t es, size_t ldw, int E, const float* X, size_t ldx, const uint32_t* ids,
                 int n_pairs, int top_k, float* Y, size_t ldy, int N, int K, const float* sc, int* err, int fast,
                 hipStream_t st) {
@@ -1553,23 +1721,136 @@ int launch_id_t(const uint8_t* W, size_t es, size_t ldw, int E, const float* X, 
         mxcap = mxcap < 1 ? 1 : (mxcap > ID_MX ? ID_MX : mxcap);
     }
     const size_t lds = fast ? (size_t)mxcap * xs_bytes(K) : 0;
-    hipLaunchKernelGGL((k_id<QT, LPR, RPT, WAVES>), dim3((unsigned)tiles, (unsigned)n_pairs), dim3(WAVES * 64), lds,
+    hipLaunchKernelGGL((k_id<QT, LPR, RPT, WAVES, SW>), dim3((unsigned)tiles, (unsigned)n_pairs), dim3(WAVES * 64), lds,
                        st, W, es, ldw, E, X, ldx, ids, n_pairs, top_k, Y, ldy, N, K, sc, err, fast, mxcap);
     return check_launch("qmv_id kernel");
 }
 
-template <int QT>
+template <int QT, bool SW>
 int launch_id(const uint8_t* W, size_t es, size_t ldw, int E, const float* X, size_t ldx, const uint32_t* ids,
               int n_pairs, int top_k, float* Y, size_t ldy, int N, int K, const float* sc, int* err, int fast,
               hipStream_t st) {
     const int lpr = fast ? pick_lpr(K / 64) : 64;
 #define QMV_ID_CASE(L) \
-    if (lpr == L) return launch_id_t<QT, L, 1>(W, es, ldw, E, X, ldx, ids, n_pairs, top_k, Y, ldy, N, K, sc, err, fast, st);
+    if (lpr == L) return launch_id_t<QT, L, 1, SW>(W, es, ldw, E, X, ldx, ids, n_pairs, top_k, Y, ldy, N, K, sc, err, fast, st);
     QMV_ID_CASE(64) QMV_ID_CASE(32) QMV_ID_CASE(16) QMV_ID_CASE(8) QMV_ID_CASE(4)
 #undef QMV_ID_CASE
     return fail(QMV_EINVAL, "internal: no id kernel for lpr=%d", lpr);
 }
 
+// Shared by qmv_id (SW = false: X rows hold K values) and qmv_id_swiglu
+// (SW = true: X rows hold 2K values, gate then up). `fn` names the entry point
+// in error messages.
+template <bool SW>
+int id_common(const char* fn, int qtype, const void* Wv, size_t expert_stride_bytes, size_t ldw_bytes, int n_experts,
+              const float* X, size_t ldx, const uint32_t* ids, int n_tokens, int top_k, float* Y, size_t ldy, int N,
+              int K, const float* expert_scale, int* err_flag, void* stream) {
+    if (qtype != QMV_Q4_0 && qtype != QMV_Q8_0) return fail(QMV_EUNSUPPORTED, "%s: qtype %d not supported", fn, qtype);
+    const int bb = block_bytes(qtype);
+    if (n_experts <= 0) return fail(QMV_EINVAL, "%s: n_experts=%d must be > 0", fn, n_experts);
+    if (top_k <= 0) return fail(QMV_EINVAL, "%s: top_k=%d must be > 0", fn, top_k);
+    if (n_tokens < 0) return fail(QMV_EINVAL, "%s: n_tokens=%d < 0", fn, n_tokens);
+    if (N < 0) return fail(QMV_EINVAL, "%s: N=%d < 0", fn, N);
+    if (K < 0 || K % QK) return fail(QMV_EINVAL, "%s: K=%d is not a non-negative multiple of 32", fn, K);
+    if (top_k > ID_MAX_LIST) return fail(QMV_EUNSUPPORTED, "%s: top_k=%d exceeds %d", fn, top_k, ID_MAX_LIST);
+    if ((long)n_tokens * top_k > 0x7FFFFFFFL) return fail(QMV_EINVAL, "%s: n_tokens*top_k overflows", fn);
+    if (n_tokens == 0 || N == 0) return QMV_OK;
+    if (!Wv || !X || !ids || !Y) return fail(QMV_EINVAL, "%s: NULL W, X, ids or Y", fn);
+    const size_t row = (size_t)(K / QK) * bb;
+    if (ldw_bytes < row) return fail(QMV_EINVAL, "%s: ldw_bytes=%zu < K/32*%d=%zu", fn, ldw_bytes, bb, row);
+    if ((size_t)N > SIZE_MAX / (ldw_bytes ? ldw_bytes : 1)) return fail(QMV_EINVAL, "%s: N*ldw overflows", fn);
+    if (expert_stride_bytes < (size_t)N * ldw_bytes)
+        return fail(QMV_EINVAL, "%s: expert_stride_bytes=%zu < N*ldw_bytes=%zu", fn, expert_stride_bytes,
+                    (size_t)N * ldw_bytes);
+    if (ldx < (size_t)(SW ? 2 : 1) * K)
+        return fail(QMV_EINVAL, "%s: ldx=%zu < %s=%d", fn, ldx, SW ? "2K" : "K", (SW ? 2 : 1) * K);
+    if (ldy < (size_t)N) return fail(QMV_EINVAL, "%s: ldy=%zu < N=%d", fn, ldy, N);
+    if (((uintptr_t)Wv & 1) || (ldw_bytes & 1) || (expert_stride_bytes & 1))
+        return fail(QMV_EALIGN, "%s: W, ldw_bytes and expert_stride_bytes must be 2-byte aligned", fn);
+    if (((uintptr_t)X & 3) || ((uintptr_t)Y & 3) || ((uintptr_t)ids & 3) || ((uintptr_t)expert_scale & 3) ||
+        ((uintptr_t)err_flag & 3))
+        return fail(QMV_EALIGN, "%s: X, Y, ids, expert_scale and err_flag must be 4-byte aligned", fn);
+    const int n_pairs = n_tokens * top_k;
+    const size_t ybytes = ((size_t)(n_pairs - 1) * ldy + N) * 4;
+    const size_t wbytes = (size_t)(n_experts - 1) * expert_stride_bytes + (size_t)(N - 1) * ldw_bytes + row;
+    const size_t xbytes = ((size_t)(n_tokens - 1) * ldx + (size_t)(SW ? 2 : 1) * K) * 4;
+    if (overlaps(Y, ybytes, Wv, K ? wbytes : 0) || overlaps(Y, ybytes, X, K ? xbytes : 0) ||
+        overlaps(Y, ybytes, ids, (size_t)n_pairs * 4) ||
+        overlaps(Y, ybytes, expert_scale, expert_scale ? (size_t)n_experts * 4 : 0) ||
+        overlaps(Y, ybytes, err_flag, err_flag ? 4 : 0))
+        return fail(QMV_EINVAL, "%s: Y overlaps another argument", fn);
+
+    hipStream_t st = (hipStream_t)stream;
+    const uint8_t* W = (const uint8_t*)Wv;
+    const int fast = K > 0 && K % 64 == 0 && K <= KMAX_FAST_ID && ((uintptr_t)W & 3) == 0 && (ldw_bytes & 3) == 0 &&
+                     (expert_stride_bytes & 3) == 0;
+    // A leader gathers at most ID_MAX_LIST pairs, so a call is split into
+    // launches over whole tokens holding at most that many pairs each.
+    const int tok_per_launch = ID_MAX_LIST / top_k;
+    for (int t0 = 0; t0 < n_tokens; t0 += tok_per_launch) {
+        const int nt = n_tokens - t0 < tok_per_launch ? n_tokens - t0 : tok_per_launch;
+        const size_t p0 = (size_t)t0 * top_k;
+        const float* Xs = X + (size_t)t0 * ldx;
+        const uint32_t* is = ids + p0;
+        float* Ys = Y + p0 * ldy;
+        const int rc = qtype == QMV_Q4_0
+                           ? launch_id<QMV_Q4_0, SW>(W, expert_stride_bytes, ldw_bytes, n_experts, Xs, ldx, is, nt * top_k,
+                                                 top_k, Ys, ldy, N, K, expert_scale, err_flag, fast, st)
+                           : launch_id<QMV_Q8_0, SW>(W, expert_stride_bytes, ldw_bytes, n_experts, Xs, ldx, is, nt * top_k,
+                                                 top_k, Ys, ldy, N, K, expert_scale, err_flag, fast, st);
+        if (rc) return rc;
+    }
+    return QMV_OK;
+}
+
+
+template <int QT, int LPR, int WAVES>
+int launch_moe_down_t(const uint8_t* W, size_t es, size_t ldw, int E, const float* G, size_t ldg, const uint32_t* ids,
+                      const float* wts, int n_tokens, int top_k, float* out, size_t ldo, int N, int K,
+                      const float* sc, int* err, hipStream_t st) {
+    constexpr int R = 64 / LPR;
+    const long tiles = ((long)N + R - 1) / R;
+    if (tiles > 0x7FFFFFFF) return fail(QMV_EINVAL, "qmv_moe_down: N too large");
+    const size_t lds = (size_t)top_k * xs_bytes(K);
+    // grid.y is limited to 65535: launch over slices of the tokens.
+    for (int t0 = 0; t0 < n_tokens; t0 += 65535) {
+        const int nt = n_tokens - t0 < 65535 ? n_tokens - t0 : 65535;
+        hipLaunchKernelGGL((k_moe_down<QT, LPR, WAVES>), dim3((unsigned)tiles, (unsigned)nt), dim3(WAVES * 64), lds, st,
+                           W, es, ldw, E, G + (size_t)t0 * top_k * ldg, ldg, ids + (size_t)t0 * top_k,
+                           wts + (size_t)t0 * top_k, top_k, out + (size_t)t0 * ldo, ldo, N, K, sc, err);
+        const int rc = check_launch("qmv_moe_down kernel");
+        if (rc) return rc;
+    }
+    return QMV_OK;
+}
+
+template <int QT, int WAVES>
+int launch_moe_down_w(const uint8_t* W, size_t es, size_t ldw, int E, const float* G, size_t ldg, const uint32_t* ids,
+                      const float* wts, int n_tokens, int top_k, float* out, size_t ldo, int N, int K,
+                      const float* sc, int* err, hipStream_t st) {
+    const int lpr = pick_lpr(K / 64);
+#define QMV_MD_CASE(L)                                                                                            \
+    if (lpr == L)                                                                                                 \
+        return launch_moe_down_t<QT, L, WAVES>(W, es, ldw, E, G, ldg, ids, wts, n_tokens, top_k, out, ldo, N, K, sc, \
+                                               err, st);
+    QMV_MD_CASE(64) QMV_MD_CASE(32) QMV_MD_CASE(16) QMV_MD_CASE(8) QMV_MD_CASE(4)
+#undef QMV_MD_CASE
+    return fail(QMV_EINVAL, "internal: no moe_down kernel for lpr=%d", lpr);
+}
+
+// Waves per workgroup: one per slot up to 8.
+template <int QT>
+int launch_moe_down(const uint8_t* W, size_t es, size_t ldw, int E, const float* G, size_t ldg, const uint32_t* ids,
+                    const float* wts, int n_tokens, int top_k, float* out, size_t ldo, int N, int K, const float* sc,
+                    int* err, hipStream_t st) {
+    if (top_k <= 2)
+        return launch_moe_down_w<QT, 2>(W, es, ldw, E, G, ldg, ids, wts, n_tokens, top_k, out, ldo, N, K, sc, err, st);
+    if (top_k <= 4)
+        return launch_moe_down_w<QT, 4>(W, es, ldw, E, G, ldg, ids, wts, n_tokens, top_k, out, ldo, N, K, sc, err, st);
+    return launch_moe_down_w<QT, 8>(W, es, ldw, E, G, ldg, ids, wts, n_tokens, top_k, out, ldo, N, K, sc, err, st);
+}
+
+constexpr size_t MD_LDS_MAX = 64 * 1024;  // staged SwiGLU rows of one token
 }  // namespace
 
 extern "C" {
@@ -1587,61 +1868,93 @@ int qmv_q8_0(const void* W, size_t ldw_bytes, const float* X, size_t ldx, float*
 int qmv_id(int qtype, const void* Wv, size_t expert_stride_bytes, size_t ldw_bytes, int n_experts, const float* X,
            size_t ldx, const uint32_t* ids, int n_tokens, int top_k, float* Y, size_t ldy, int N, int K,
            const float* expert_scale, int* err_flag, void* stream) {
-    if (qtype != QMV_Q4_0 && qtype != QMV_Q8_0) return fail(QMV_EUNSUPPORTED, "qmv_id: qtype %d not supported", qtype);
-    const int bb = block_bytes(qtype);
-    if (n_experts <= 0) return fail(QMV_EINVAL, "qmv_id: n_experts=%d must be > 0", n_experts);
-    if (top_k <= 0) return fail(QMV_EINVAL, "qmv_id: top_k=%d must be > 0", top_k);
-    if (n_tokens < 0) return fail(QMV_EINVAL, "qmv_id: n_tokens=%d < 0", n_tokens);
-    if (N < 0) return fail(QMV_EINVAL, "qmv_id: N=%d < 0", N);
-    if (K < 0 || K % QK) return fail(QMV_EINVAL, "qmv_id: K=%d is not a non-negative multiple of 32", K);
-    if (top_k > ID_MAX_LIST) return fail(QMV_EUNSUPPORTED, "qmv_id: top_k=%d exceeds %d", top_k, ID_MAX_LIST);
-    if ((long)n_tokens * top_k > 0x7FFFFFFFL) return fail(QMV_EINVAL, "qmv_id: n_tokens*top_k overflows");
-    if (n_tokens == 0 || N == 0) return QMV_OK;
-    if (!Wv || !X || !ids || !Y) return fail(QMV_EINVAL, "qmv_id: NULL W, X, ids or Y");
-    const size_t row = (size_t)(K / QK) * bb;
-    if (ldw_bytes < row) return fail(QMV_EINVAL, "qmv_id: ldw_bytes=%zu < K/32*%d=%zu", ldw_bytes, bb, row);
-    if ((size_t)N > SIZE_MAX / (ldw_bytes ? ldw_bytes : 1)) return fail(QMV_EINVAL, "qmv_id: N*ldw overflows");
-    if (expert_stride_bytes < (size_t)N * ldw_bytes)
-        return fail(QMV_EINVAL, "qmv_id: expert_stride_bytes=%zu < N*ldw_bytes=%zu", expert_stride_bytes,
-                    (size_t)N * ldw_bytes);
-    if (ldx < (size_t)K) return fail(QMV_EINVAL, "qmv_id: ldx=%zu < K=%d", ldx, K);
-    if (ldy < (size_t)N) return fail(QMV_EINVAL, "qmv_id: ldy=%zu < N=%d", ldy, N);
-    if (((uintptr_t)Wv & 1) || (ldw_bytes & 1) || (expert_stride_bytes & 1))
-        return fail(QMV_EALIGN, "qmv_id: W, ldw_bytes and expert_stride_bytes must be 2-byte aligned");
-    if (((uintptr_t)X & 3) || ((uintptr_t)Y & 3) || ((uintptr_t)ids & 3) || ((uintptr_t)expert_scale & 3) ||
-        ((uintptr_t)err_flag & 3))
-        return fail(QMV_EALIGN, "qmv_id: X, Y, ids, expert_scale and err_flag must be 4-byte aligned");
-    const int n_pairs = n_tokens * top_k;
-    const size_t ybytes = ((size_t)(n_pairs - 1) * ldy + N) * 4;
-    const size_t wbytes = (size_t)(n_experts - 1) * expert_stride_bytes + (size_t)(N - 1) * ldw_bytes + row;
-    const size_t xbytes = ((size_t)(n_tokens - 1) * ldx + K) * 4;
-    if (overlaps(Y, ybytes, Wv, K ? wbytes : 0) || overlaps(Y, ybytes, X, K ? xbytes : 0) ||
-        overlaps(Y, ybytes, ids, (size_t)n_pairs * 4) ||
-        overlaps(Y, ybytes, expert_scale, expert_scale ? (size_t)n_experts * 4 : 0) ||
-        overlaps(Y, ybytes, err_flag, err_flag ? 4 : 0))
-        return fail(QMV_EINVAL, "qmv_id: Y overlaps another argument");
+    return id_common<false>("qmv_id", qtype, Wv, expert_stride_bytes, ldw_bytes, n_experts, X, ldx, ids, n_tokens,
+                            top_k, Y, ldy, N, K, expert_scale, err_flag, stream);
+}
 
-    hipStream_t st = (hipStream_t)stream;
+int qmv_id_swiglu(int qtype, const void* Wv, size_t expert_stride_bytes, size_t ldw_bytes, int n_experts,
+                  const float* G, size_t ldg, const uint32_t* ids, int n_tokens, int top_k, float* Y, size_t ldy,
+                  int N, int K, const float* expert_scale, int* err_flag, void* stream) {
+    return id_common<true>("qmv_id_swiglu", qtype, Wv, expert_stride_bytes, ldw_bytes, n_experts, G, ldg, ids,
+                           n_tokens, top_k, Y, ldy, N, K, expert_scale, err_flag, stream);
+}
+
+int qmv_moe_wsum(const float* Y, size_t ldy, const float* weights, int n_tokens, int top_k, int N, float* out,
+                 size_t ldo, void* stream) {
+    if (n_tokens < 0) return fail(QMV_EINVAL, "qmv_moe_wsum: n_tokens=%d < 0", n_tokens);
+    if (top_k <= 0) return fail(QMV_EINVAL, "qmv_moe_wsum: top_k=%d must be > 0", top_k);
+    if (N < 0) return fail(QMV_EINVAL, "qmv_moe_wsum: N=%d < 0", N);
+    if ((long)n_tokens * top_k > 0x7FFFFFFFL) return fail(QMV_EINVAL, "qmv_moe_wsum: n_tokens*top_k overflows");
+    if (n_tokens == 0 || N == 0) return QMV_OK;
+    if (!Y || !weights || !out) return fail(QMV_EINVAL, "qmv_moe_wsum: NULL Y, weights or out");
+    if (ldy < (size_t)N) return fail(QMV_EINVAL, "qmv_moe_wsum: ldy=%zu < N=%d", ldy, N);
+    if (ldo < (size_t)N) return fail(QMV_EINVAL, "qmv_moe_wsum: ldo=%zu < N=%d", ldo, N);
+    if (((uintptr_t)Y & 3) || ((uintptr_t)weights & 3) || ((uintptr_t)out & 3))
+        return fail(QMV_EALIGN, "qmv_moe_wsum: Y, weights and out must be 4-byte aligned");
+    const size_t P = (size_t)n_tokens * top_k;
+    const size_t obytes = ((size_t)(n_tokens - 1) * ldo + N) * 4;
+    if (overlaps(out, obytes, Y, ((P - 1) * ldy + N) * 4) || overlaps(out, obytes, weights, P * 4))
+        return fail(QMV_EINVAL, "qmv_moe_wsum: out overlaps another argument");
+    const long col_tiles = ((long)N + 255) / 256;
+    if ((long)n_tokens * col_tiles > 0x7FFFFFFFL) return fail(QMV_EINVAL, "qmv_moe_wsum: too many tokens x columns");
+    hipLaunchKernelGGL(k_wsum, dim3((unsigned)(n_tokens * col_tiles)), dim3(256), 0, (hipStream_t)stream, Y, ldy,
+                       weights, top_k, N, col_tiles, out, ldo);
+    return check_launch("qmv_moe_wsum kernel");
+}
+
+int qmv_moe_down(int qtype, const void* Wv, size_t expert_stride_bytes, size_t ldw_bytes, int n_experts,
+                 const float* G, size_t ldg, const uint32_t* ids, const float* weights, int n_tokens, int top_k,
+                 float* out, size_t ldo, int N, int K, const float* expert_scale, int* err_flag, void* stream) {
+    if (qtype != QMV_Q4_0 && qtype != QMV_Q8_0)
+        return fail(QMV_EUNSUPPORTED, "qmv_moe_down: qtype %d not supported", qtype);
+    const int bb = block_bytes(qtype);
+    if (n_experts <= 0) return fail(QMV_EINVAL, "qmv_moe_down: n_experts=%d must be > 0", n_experts);
+    if (top_k <= 0) return fail(QMV_EINVAL, "qmv_moe_down: top_k=%d must be > 0", top_k);
+    if (n_tokens < 0) return fail(QMV_EINVAL, "qmv_moe_down: n_tokens=%d < 0", n_tokens);
+    if (N < 0) return fail(QMV_EINVAL, "qmv_moe_down: N=%d < 0", N);
+    if (K < 0 || K % QK) return fail(QMV_EINVAL, "qmv_moe_down: K=%d is not a non-negative multiple of 32", K);
+    if ((long)n_tokens * top_k > 0x7FFFFFFFL) return fail(QMV_EINVAL, "qmv_moe_down: n_tokens*top_k overflows");
+    if (n_tokens == 0 || N == 0) return QMV_OK;
+    if (!Wv || !G || !ids || !weights || !out) return fail(QMV_EINVAL, "qmv_moe_down: NULL W, G, ids, weights or out");
+    if (K == 0)
+        return fail(QMV_EUNSUPPORTED, "qmv_moe_down: K=0 (qmv_id_swiglu + qmv_moe_wsum cover empty rows)");
+    const size_t row = (size_t)(K / QK) * bb;
+    if (ldw_bytes < row) return fail(QMV_EINVAL, "qmv_moe_down: ldw_bytes=%zu < K/32*%d=%zu", ldw_bytes, bb, row);
+    if ((size_t)N > SIZE_MAX / ldw_bytes) return fail(QMV_EINVAL, "qmv_moe_down: N*ldw overflows");
+    if (expert_stride_bytes < (size_t)N * ldw_bytes)
+        return fail(QMV_EINVAL, "qmv_moe_down: expert_stride_bytes=%zu < N*ldw_bytes=%zu", expert_stride_bytes,
+                    (size_t)N * ldw_bytes);
+    if (ldg < (size_t)2 * K) return fail(QMV_EINVAL, "qmv_moe_down: ldg=%zu < 2K=%d", ldg, 2 * K);
+    if (ldo < (size_t)N) return fail(QMV_EINVAL, "qmv_moe_down: ldo=%zu < N=%d", ldo, N);
+    if (((uintptr_t)G & 3) || ((uintptr_t)out & 3) || ((uintptr_t)ids & 3) || ((uintptr_t)weights & 3) ||
+        ((uintptr_t)expert_scale & 3) || ((uintptr_t)err_flag & 3))
+        return fail(QMV_EALIGN, "qmv_moe_down: G, out, ids, weights, expert_scale and err_flag must be 4-byte aligned");
+    if (K % 64 || ((uintptr_t)Wv & 3) || (ldw_bytes & 3) || (expert_stride_bytes & 3))
+        return fail(QMV_EUNSUPPORTED,
+                    "qmv_moe_down: needs K %% 64 == 0 and 4-byte aligned W, ldw_bytes and expert_stride_bytes "
+                    "(qmv_id_swiglu + qmv_moe_wsum cover the rest)");
+    if (top_k > MD_MAX_TOPK || (size_t)top_k * xs_bytes(K) > MD_LDS_MAX)
+        return fail(QMV_EUNSUPPORTED,
+                    "qmv_moe_down: top_k=%d rows of K=%d do not fit the staging limit (top_k <= %d, top_k*K <= %d); "
+                    "qmv_id_swiglu + qmv_moe_wsum cover the rest",
+                    top_k, K, MD_MAX_TOPK, (int)(MD_LDS_MAX / xs_bytes(64)) * 64);
+    const size_t P = (size_t)n_tokens * top_k;
+    const size_t obytes = ((size_t)(n_tokens - 1) * ldo + N) * 4;
+    const size_t wbytes = (size_t)(n_experts - 1) * expert_stride_bytes + (size_t)(N - 1) * ldw_bytes + row;
+    const size_t gbytes = ((P - 1) * ldg + 2 * (size_t)K) * 4;
+    if (overlaps(out, obytes, Wv, wbytes) || overlaps(out, obytes, G, gbytes) || overlaps(out, obytes, ids, P * 4) ||
+        overlaps(out, obytes, weights, P * 4) ||
+        overlaps(out, obytes, expert_scale, expert_scale ? (size_t)n_experts * 4 : 0) ||
+        overlaps(out, obytes, err_flag, err_flag ? 4 : 0))
+        return fail(QMV_EINVAL, "qmv_moe_down: out overlaps another argument");
     const uint8_t* W = (const uint8_t*)Wv;
-    const int fast = K > 0 && K % 64 == 0 && K <= KMAX_FAST_ID && ((uintptr_t)W & 3) == 0 && (ldw_bytes & 3) == 0 &&
-                     (expert_stride_bytes & 3) == 0;
-    // A leader gathers at most ID_MAX_LIST pairs, so a call is split into
-    // launches over whole tokens holding at most that many pairs each.
-    const int tok_per_launch = ID_MAX_LIST / top_k;
-    for (int t0 = 0; t0 < n_tokens; t0 += tok_per_launch) {
-        const int nt = n_tokens - t0 < tok_per_launch ? n_tokens - t0 : tok_per_launch;
-        const size_t p0 = (size_t)t0 * top_k;
-        const float* Xs = X + (size_t)t0 * ldx;
-        const uint32_t* is = ids + p0;
-        float* Ys = Y + p0 * ldy;
-        const int rc = qtype == QMV_Q4_0
-                           ? launch_id<QMV_Q4_0>(W, expert_stride_bytes, ldw_bytes, n_experts, Xs, ldx, is, nt * top_k,
-                                                 top_k, Ys, ldy, N, K, expert_scale, err_flag, fast, st)
-                           : launch_id<QMV_Q8_0>(W, expert_stride_bytes, ldw_bytes, n_experts, Xs, ldx, is, nt * top_k,
-                                                 top_k, Ys, ldy, N, K, expert_scale, err_flag, fast, st);
-        if (rc) return rc;
-    }
-    return QMV_OK;
+    hipStream_t st = (hipStream_t)stream;
+    return qtype == QMV_Q4_0 ? launch_moe_down<QMV_Q4_0>(W, expert_stride_bytes, ldw_bytes, n_experts, G, ldg, ids,
+                                                         weights, n_tokens, top_k, out, ldo, N, K, expert_scale,
+                                                         err_flag, st)
+                             : launch_moe_down<QMV_Q8_0>(W, expert_stride_bytes, ldw_bytes, n_experts, G, ldg, ids,
+                                                         weights, n_tokens, top_k, out, ldo, N, K, expert_scale,
+                                                         err_flag, st);
 }
 
 int qmv_batch(int qtype, const qmv_problem* problems, int n_problems, void* stream) {

@@ -52,6 +52,12 @@ def lib() -> ctypes.CDLL:
             f.argtypes = [P, S, P, S, P, S, I, I, I, P]
         L.qmv_id.restype = I
         L.qmv_id.argtypes = [I, P, S, S, I, P, S, P, I, I, P, S, I, I, P, P, P]
+        L.qmv_id_swiglu.restype = I
+        L.qmv_id_swiglu.argtypes = [I, P, S, S, I, P, S, P, I, I, P, S, I, I, P, P, P]
+        L.qmv_moe_wsum.restype = I
+        L.qmv_moe_wsum.argtypes = [P, S, P, I, I, I, P, S, P]
+        L.qmv_moe_down.restype = I
+        L.qmv_moe_down.argtypes = [I, P, S, S, I, P, S, P, P, I, I, P, S, I, I, P, P, P]
         L.qmv_batch.restype = I
         L.qmv_batch.argtypes = [I, ctypes.POINTER(Problem), I, P]
         L.qmv_last_error.restype = ctypes.c_char_p
@@ -94,6 +100,22 @@ def raw_qmv_id(qtype, W, expert_stride, ldw, n_experts, X, ldx, ids, n_tokens, t
                expert_scale=0, err_flag=0, stream=0) -> int:
     return lib().qmv_id(qtype, W, expert_stride, ldw, n_experts, X, ldx, ids, n_tokens, top_k, Y, ldy, N, K,
                         expert_scale, err_flag, stream)
+
+
+def raw_qmv_id_swiglu(qtype, W, expert_stride, ldw, n_experts, G, ldg, ids, n_tokens, top_k, Y, ldy, N, K,
+                      expert_scale=0, err_flag=0, stream=0) -> int:
+    return lib().qmv_id_swiglu(qtype, W, expert_stride, ldw, n_experts, G, ldg, ids, n_tokens, top_k, Y, ldy, N, K,
+                               expert_scale, err_flag, stream)
+
+
+def raw_qmv_moe_wsum(Y, ldy, weights, n_tokens, top_k, N, out, ldo, stream=0) -> int:
+    return lib().qmv_moe_wsum(Y, ldy, weights, n_tokens, top_k, N, out, ldo, stream)
+
+
+def raw_qmv_moe_down(qtype, W, expert_stride, ldw, n_experts, G, ldg, ids, weights, n_tokens, top_k, out, ldo, N, K,
+                     expert_scale=0, err_flag=0, stream=0) -> int:
+    return lib().qmv_moe_down(qtype, W, expert_stride, ldw, n_experts, G, ldg, ids, weights, n_tokens, top_k, out,
+                              ldo, N, K, expert_scale, err_flag, stream)
 
 
 def raw_qmv_batch(qtype: int, problems, stream: int = 0) -> int:
@@ -150,6 +172,62 @@ def qmv_id(qtype, W, X, ids, Y, N: int, K: int, expert_scale=None, err_flag=None
     st = raw_qmv_id(q, _ptr(W), W.stride(0), W.stride(1), W.shape[0], _ptr(X), X.stride(0), _ptr(ids2),
                     n_tokens, top_k, _ptr(Y), Y.stride(0), N, K, _ptr(expert_scale), _ptr(err_flag),
                     _stream(stream))
+    _check(st)
+
+
+def _stack(W):
+    if W.dim() != 3 or W.stride(2) != 1:
+        raise ValueError("W must be a 3-D uint8 tensor [E, N, ldw] with contiguous rows")
+
+
+def qmv_id_swiglu(qtype, W, G, ids, Y, N: int, K: int, expert_scale=None, err_flag=None, stream=None) -> None:
+    """qmv_id on the SwiGLU of gate_up rows (see include/qmv.h).
+
+    W: uint8 [E, N, ldw]; G: fp32 [n_tokens, >= 2K] (gate half first);
+    ids: [n_tokens, top_k] (or [n_tokens]); Y: fp32 [n_tokens * top_k, N].
+    """
+    q = QTYPES[qtype] if isinstance(qtype, str) else int(qtype)
+    _stack(W)
+    ids2 = ids if ids.dim() == 2 else ids.view(-1, 1)
+    if not ids2.is_contiguous():
+        raise ValueError("ids must be contiguous")
+    n_tokens, top_k = ids2.shape
+    st = raw_qmv_id_swiglu(q, _ptr(W), W.stride(0), W.stride(1), W.shape[0], _ptr(G), G.stride(0), _ptr(ids2),
+                           n_tokens, top_k, _ptr(Y), Y.stride(0), N, K, _ptr(expert_scale), _ptr(err_flag),
+                           _stream(stream))
+    _check(st)
+
+
+def qmv_moe_wsum(Y, weights, out, top_k: int, stream=None) -> None:
+    """out[t] = sum_s weights[t*top_k + s] * Y[t*top_k + s] (see include/qmv.h).
+
+    Y: fp32 [n_tokens * top_k, N]; weights: fp32 contiguous [n_tokens * top_k]
+    (any shape); out: fp32 [n_tokens, N]."""
+    if not weights.is_contiguous() or Y.stride(1) != 1 or out.stride(1) != 1:
+        raise ValueError("weights must be contiguous; Y and out need unit inner stride")
+    n_tokens, N = out.shape
+    if Y.shape[0] != n_tokens * top_k or Y.shape[1] != N or weights.numel() != n_tokens * top_k:
+        raise ValueError("Y must be [n_tokens*top_k, N] and weights hold n_tokens*top_k values")
+    _check(raw_qmv_moe_wsum(_ptr(Y), Y.stride(0), _ptr(weights), n_tokens, top_k, N, _ptr(out), out.stride(0),
+                            _stream(stream)))
+
+
+def qmv_moe_down(qtype, W, G, ids, weights, out, N: int, K: int, expert_scale=None, err_flag=None,
+                 stream=None) -> None:
+    """SwiGLU + expert-indexed down product + weighted sum, one launch (see include/qmv.h).
+
+    W: uint8 [E, N, ldw]; G: fp32 [n_tokens * top_k, >= 2K]; ids: [n_tokens, top_k];
+    weights: fp32 contiguous [n_tokens, top_k]; out: fp32 [n_tokens, N]."""
+    q = QTYPES[qtype] if isinstance(qtype, str) else int(qtype)
+    _stack(W)
+    if ids.dim() != 2 or not ids.is_contiguous() or not weights.is_contiguous():
+        raise ValueError("ids must be a contiguous [n_tokens, top_k] tensor and weights contiguous")
+    n_tokens, top_k = ids.shape
+    if weights.numel() != n_tokens * top_k:
+        raise ValueError("weights must hold n_tokens*top_k values")
+    st = raw_qmv_moe_down(q, _ptr(W), W.stride(0), W.stride(1), W.shape[0], _ptr(G), G.stride(0), _ptr(ids),
+                          _ptr(weights), n_tokens, top_k, _ptr(out), out.stride(0), N, K, _ptr(expert_scale),
+                          _ptr(err_flag), _stream(stream))
     _check(st)
 
 

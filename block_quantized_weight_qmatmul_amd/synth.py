@@ -23,7 +23,8 @@ round-to-nearest-even cast.
 
 Seeds: ``numpy.random.default_rng([20261202, cfg, copy, tensor, part])``
 with tensor ids 0 = scales, 1 = codes, 2 = activations, 3 = router logits,
-4 = per-expert scale; ``part`` tells apart several matrices of one config.
+4 = per-expert scale, 5 = gate_up rows, 6 = routing weights; ``part`` tells
+apart several matrices of one config.
 """
 from __future__ import annotations
 
@@ -34,7 +35,7 @@ import numpy as np
 
 ROOT_SEED = 20261202
 
-T_SCALE, T_CODES, T_X, T_LOGITS, T_ESCALE = 0, 1, 2, 3, 4
+T_SCALE, T_CODES, T_X, T_LOGITS, T_ESCALE, T_GATE_UP, T_RWEIGHT = 0, 1, 2, 3, 4, 5, 6
 
 QK = 32  # weights per block
 BLOCK_BYTES = {"q4_0": 18, "q8_0": 34}
@@ -109,6 +110,30 @@ def router_topk(T: int, n_experts: int, top_k: int, cfg: int, copy: int = 0, par
 def expert_scale(n_experts: int, cfg: int, copy: int = 0, part: int = 0) -> np.ndarray:
     """Per-expert fp32 scale drawn from U[0.5, 1.5]."""
     return rng(cfg, copy, T_ESCALE, part).uniform(0.5, 1.5, size=n_experts).astype(np.float32)
+
+
+# Standard deviation of one gate_up output for N(0,1) activations over
+# K = 2816 inputs, Q4_0 codes uniform over 0..15 and d ~ U[0.001, 0.02]:
+# E[(c - 8)^2] = 344/16 = 21.5, E[d^2] = (0.02^3 - 0.001^3) / (3 * 0.019)
+# = 1.403e-4, so sqrt(2816 * 21.5 * 1.403e-4) = 2.91.
+GATE_UP_STD = 2.9
+
+
+def gate_up_rows(rows: int, inter: int, cfg: int, copy: int = 0, part: int = 0,
+                 std: float = GATE_UP_STD) -> np.ndarray:
+    """Stand-in gate_up outputs ``[rows, 2 * inter]`` fp32 drawn from N(0, std^2).
+
+    Row p holds the gate half then the up half of one (token, slot) pair.
+    """
+    r = rng(cfg, copy, T_GATE_UP, part)
+    return (r.standard_normal((rows, 2 * inter), dtype=np.float64) * std).astype(np.float32)
+
+
+def routing_weights(T: int, top_k: int, cfg: int, copy: int = 0, part: int = 0) -> np.ndarray:
+    """Routing weights ``[T, top_k]`` fp32: U[0, 1) draws divided by their
+    per-token sum (positive, summing to 1 over a token's slots)."""
+    u = rng(cfg, copy, T_RWEIGHT, part).random((T, top_k)) + 1e-3
+    return (u / u.sum(axis=1, keepdims=True)).astype(np.float32)
 
 
 # ---------------------------------------------------------------------------
@@ -187,7 +212,9 @@ def moe_inputs(T: int, copy: int = 0, cfg: int = 4):
 
     Returns a dict with the stacked gate_up and down weights (uint8
     [E, N, row_bytes]), the gate_up input X [T, hidden], the down input
-    [T*top_k, inter], ids [T, top_k] and the per-expert scale [E].
+    [T*top_k, inter], ids [T, top_k], the per-expert scale [E], stand-in
+    gate_up output rows G_down [T*top_k, 2*inter] for the SwiGLU-fed down
+    calls and the routing weights [T, top_k].
     """
     gu, dn = moe_calls(T)
     E = MOE["n_experts"]
@@ -198,4 +225,6 @@ def moe_inputs(T: int, copy: int = 0, cfg: int = 4):
         "X_down": make_x(T * MOE["top_k"], dn.K, cfg, copy, part=1),
         "ids": router_topk(T, E, MOE["top_k"], cfg, copy),
         "expert_scale": expert_scale(E, cfg, copy),
+        "G_down": gate_up_rows(T * MOE["top_k"], dn.K, cfg, copy),
+        "weights": routing_weights(T, MOE["top_k"], cfg, copy),
     }

@@ -19,6 +19,9 @@
  *    expert_stride, ggml_type }` (gpu_full_attn.rs, MoE blocks B11 gate_up and
  *    B13 down); stacked weights `[n_experts, N, packed_K]` with a byte stride
  *    per expert (model.rs, `MlxMoeWeights`).
+ *  - The MoE steps on either side of the down call in the same function:
+ *    SwiGLU of the gate_up rows (B12, `moe_swiglu_batch_encode`) and the
+ *    routing-weighted sum over slots (B14, `moe_weighted_sum_encode`).
  *
  * Block formats (32 weights per block):
  *   Q4_0, 18 bytes: binary16 scale d (little-endian), then 16 bytes where
@@ -141,6 +144,77 @@ int qmv_id(int qtype, const void* W, size_t expert_stride_bytes, size_t ldw_byte
            const float* X, size_t ldx, const uint32_t* ids, int n_tokens, int top_k,
            float* Y, size_t ldy, int N, int K, const float* expert_scale, int* err_flag,
            void* stream);
+
+/*
+ * qmv_id_swiglu — the MoE down projection fed by SwiGLU: qmv_id with
+ *   X[t, k] = silu(G[t, k]) * G[t, K + k],   silu(z) = z / (1 + e^-z),
+ * so that the SwiGLU step between the gate_up and down calls (block B12,
+ * `moe_swiglu_batch_encode`, of `encode_one_layer`) runs inside the down call
+ * (block B13) and its result never goes to memory. Row t of G is a gate_up
+ * output row: 2K values, the gate half first (the pages do not order the
+ * halves; gate first follows the buffer name `gate_up`).
+ *
+ *  G, ldg   device fp32 [n_tokens, 2K], row stride ldg >= 2K, 4-byte aligned.
+ *  Every other argument, the result layout, NaN rows for bad ids and the
+ *  error behaviour are those of qmv_id. For the pages' down form pass the
+ *  gate_up output rows with (n_tokens = T*k, top_k = 1).
+ * In fp32, silu(z) for z < -88.7 is -0 (e^-z overflows), against a true
+ * value below 1e-36 in size.
+ */
+int qmv_id_swiglu(int qtype, const void* W, size_t expert_stride_bytes, size_t ldw_bytes, int n_experts,
+                  const float* G, size_t ldg, const uint32_t* ids, int n_tokens, int top_k,
+                  float* Y, size_t ldy, int N, int K, const float* expert_scale, int* err_flag,
+                  void* stream);
+
+/*
+ * qmv_moe_wsum — routing-weighted sum over each token's slots (block B14,
+ * `moe_weighted_sum_encode`, of `encode_one_layer`):
+ *   out[t, n] = sum_{s<top_k} weights[t*top_k + s] * Y[t*top_k + s, n],
+ * accumulated in slot order (s = 0 first) with one fp32 fma per slot.
+ * The pages pass routing weights already multiplied by the per-expert scale;
+ * pass those, or plain weights with the scale applied by qmv_id's
+ * expert_scale (the sum is linear, so both give the same value).
+ *
+ *  Y, ldy     device fp32 [n_tokens*top_k, N], row stride ldy >= N.
+ *  weights    device fp32 [n_tokens*top_k].
+ *  n_tokens   >= 0 (0: nothing to do).   top_k > 0.   N >= 0.
+ *  out, ldo   device fp32 [n_tokens, N], row stride ldo >= N; overwritten,
+ *             must not overlap Y or weights.
+ * All pointers 4-byte aligned. Returns QMV_OK or a negative status.
+ */
+int qmv_moe_wsum(const float* Y, size_t ldy, const float* weights, int n_tokens, int top_k, int N,
+                 float* out, size_t ldo, void* stream);
+
+/*
+ * qmv_moe_down — the down half of the MoE block in one launch: SwiGLU of each
+ * slot's gate_up row (B12), the expert-indexed down product (B13) and the
+ * routing-weighted sum (B14):
+ *   out[t, n] = sum_{s<top_k} weights[p] * sc_e * sum_{k<K} w_e[n, k] *
+ *               silu(G[p, k]) * G[p, K + k],      p = t*top_k + s, e = ids[p],
+ * with w_e and sc_e as in qmv_id, and the slot sum in slot order.
+ *
+ *  G, ldg     device fp32 [n_tokens*top_k, 2K]: the gate_up id output, row p
+ *             for slot s of token t; ldg >= 2K.
+ *  ids        device uint32 [n_tokens*top_k].
+ *  weights    device fp32 [n_tokens*top_k] routing weights.
+ *  out, ldo   device fp32 [n_tokens, N], ldo >= N; overwritten, must not
+ *             overlap any input.
+ *  W, expert_stride_bytes, ldw_bytes, n_experts, N, K, expert_scale: as qmv_id.
+ *  err_flag   as qmv_id: a bad id makes the token's outputs NaN.
+ * Each token reads the rows of its own top_k experts, so tokens that share
+ * an expert read it again: this is the form for decode, one or a few tokens
+ * with distinct experts. With many tokens, qmv_id_swiglu (each selected
+ * expert read once per call) followed by qmv_moe_wsum reads less.
+ * Supported: K a positive multiple of 64, top_k <= 64, top_k * K within
+ * 64 KiB of staged rows (top_k * K <= 15360), W, ldw_bytes and
+ * expert_stride_bytes 4-byte aligned; other shapes return QMV_EUNSUPPORTED
+ * (qmv_id_swiglu + qmv_moe_wsum compute them). Returns QMV_OK or a negative
+ * status.
+ */
+int qmv_moe_down(int qtype, const void* W, size_t expert_stride_bytes, size_t ldw_bytes, int n_experts,
+                 const float* G, size_t ldg, const uint32_t* ids, const float* weights, int n_tokens,
+                 int top_k, float* out, size_t ldo, int N, int K, const float* expert_scale,
+                 int* err_flag, void* stream);
 
 /*
  * qmv_batch — several independent M = 1 products in one launch:

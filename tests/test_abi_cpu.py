@@ -26,7 +26,8 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert {"qmv_q4_0", "qmv_q8_0", "qmv_id", "qmv_batch", "qmv_last_error"} <= set(names)
+    assert {"qmv_q4_0", "qmv_q8_0", "qmv_id", "qmv_id_swiglu", "qmv_moe_wsum", "qmv_moe_down", "qmv_batch",
+            "qmv_last_error"} <= set(names)
     L = ctypes.CDLL(qmv.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -133,3 +134,77 @@ def test_batch_bad_qtype_and_empty():
     assert qmv.raw_qmv_batch(5, [_bp()]) == qmv.QMV_EUNSUPPORTED
     assert qmv.raw_qmv_batch(Q4, []) == qmv.QMV_OK
     assert qmv.raw_qmv_batch(Q8, [_bp(N=0, W=0, x=0, ldw=34 * 4)]) == qmv.QMV_OK  # N = 0: nothing to launch
+
+
+def _sw(**kw):
+    a = dict(qtype=Q4, W=W, es=18 * 16, ldw=18, E=4, G=X, ldg=64, ids=0x40000000, nt=1, k=2, Y=Y, ldy=16,
+             N=16, K=32, sc=0, err=0)
+    a.update(kw)
+    return qmv.raw_qmv_id_swiglu(a["qtype"], a["W"], a["es"], a["ldw"], a["E"], a["G"], a["ldg"], a["ids"], a["nt"],
+                                 a["k"], a["Y"], a["ldy"], a["N"], a["K"], a["sc"], a["err"])
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(ldg=63), qmv.QMV_EINVAL, "qmv_id_swiglu: ldx=63 < 2K=64"),
+    (dict(qtype=3), qmv.QMV_EUNSUPPORTED, "qmv_id_swiglu: qtype"),
+    (dict(G=X + 2), qmv.QMV_EALIGN, "4-byte"),
+    (dict(Y=X + 4 * 60), qmv.QMV_EINVAL, "overlaps"),  # Y inside G's second half
+    (dict(K=48), qmv.QMV_EINVAL, "K=48"),
+])
+def test_id_swiglu_argument_checks(kw, status, msg):
+    assert _sw(**kw) == status
+    assert msg in qmv.last_error()
+
+
+def _ws(**kw):
+    a = dict(Y=Y, ldy=16, w=0x40000000, nt=2, k=4, N=16, out=0x50000000, ldo=16)
+    a.update(kw)
+    return qmv.raw_qmv_moe_wsum(a["Y"], a["ldy"], a["w"], a["nt"], a["k"], a["N"], a["out"], a["ldo"])
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(k=0), qmv.QMV_EINVAL, "top_k"),
+    (dict(nt=-1), qmv.QMV_EINVAL, "n_tokens"),
+    (dict(N=-1), qmv.QMV_EINVAL, "N=-1"),
+    (dict(ldy=15), qmv.QMV_EINVAL, "ldy"),
+    (dict(ldo=15), qmv.QMV_EINVAL, "ldo"),
+    (dict(w=0), qmv.QMV_EINVAL, "NULL"),
+    (dict(out=Y + 4 * 16 * 7), qmv.QMV_EINVAL, "overlaps"),  # out starts in Y's last row
+    (dict(out=0x50000002), qmv.QMV_EALIGN, "4-byte"),
+])
+def test_moe_wsum_argument_checks(kw, status, msg):
+    assert _ws(**kw) == status
+    assert msg in qmv.last_error()
+
+
+def _md(**kw):
+    a = dict(qtype=Q4, W=W, es=36 * 16, ldw=36, E=4, G=X, ldg=128, ids=0x40000000, w=0x48000000, nt=1, k=8,
+             out=Y, ldo=16, N=16, K=64, sc=0, err=0)
+    a.update(kw)
+    return qmv.raw_qmv_moe_down(a["qtype"], a["W"], a["es"], a["ldw"], a["E"], a["G"], a["ldg"], a["ids"], a["w"],
+                                a["nt"], a["k"], a["out"], a["ldo"], a["N"], a["K"], a["sc"], a["err"])
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(qtype=3), qmv.QMV_EUNSUPPORTED, "qtype"),
+    (dict(K=32, ldw=18, es=18 * 16, ldg=64), qmv.QMV_EUNSUPPORTED, "K % 64"),
+    (dict(K=0), qmv.QMV_EUNSUPPORTED, "K=0"),
+    (dict(k=65), qmv.QMV_EUNSUPPORTED, "staging limit"),
+    (dict(k=16, K=1024, ldw=18 * 32, es=18 * 32 * 16, ldg=2048), qmv.QMV_EUNSUPPORTED, "staging limit"),
+    (dict(ldg=127), qmv.QMV_EINVAL, "ldg"),
+    (dict(ldo=15), qmv.QMV_EINVAL, "ldo"),
+    (dict(w=0), qmv.QMV_EINVAL, "NULL"),
+    (dict(es=36 * 15), qmv.QMV_EINVAL, "expert_stride"),
+    (dict(ldw=38, es=38 * 16), qmv.QMV_EUNSUPPORTED, "4-byte aligned W"),
+    (dict(w=0x48000002), qmv.QMV_EALIGN, "4-byte"),
+    (dict(out=X + 4 * 100), qmv.QMV_EINVAL, "overlaps"),
+])
+def test_moe_down_argument_checks(kw, status, msg):
+    assert _md(**kw) == status
+    assert msg in qmv.last_error()
+
+
+def test_moe_empty_calls_are_no_ops():
+    assert qmv.raw_qmv_moe_wsum(0, 0, 0, 0, 8, 16, 0, 0) == qmv.QMV_OK
+    assert qmv.raw_qmv_moe_down(Q4, 0, 0, 0, 4, 0, 0, 0, 0, 0, 8, 0, 0, 16, 64) == qmv.QMV_OK
+    assert qmv.raw_qmv_id_swiglu(Q4, 0, 0, 0, 4, 0, 0, 0, 0, 2, 0, 0, 16, 32) == qmv.QMV_OK

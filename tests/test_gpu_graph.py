@@ -101,3 +101,52 @@ def test_graph_replays_id():
         y = Y.cpu().numpy()
         assert np.array_equal(y.view(np.uint32), eager.view(np.uint32))
         assert_within_tol(y, yo, a, f"id replay {rep}")
+
+
+def test_graph_replays_moe_ffn():
+    """One MoE FFN token in a graph: gate_up id, then the one-launch down half;
+    and the two-call down half (SwiGLU-fed id, weighted sum) beside it."""
+    E, T, k, H, I = 16, 2, 4, 512, 192
+    Wgu = synth.make_weights("q4_0", E * 2 * I, H, cfg=89, part=0).reshape(E, 2 * I, -1)
+    Wdn = synth.make_weights("q4_0", E * H, I, cfg=89, part=1).reshape(E, H, -1)
+    X = synth.make_x(T, H, cfg=89)
+    ids = synth.router_topk(T, E, k, cfg=89)
+    w = synth.routing_weights(T, k, cfg=89)
+    sc = synth.expert_scale(E, cfg=89)
+    d = {n: torch.from_numpy(np.ascontiguousarray(v)).to(DEV)
+         for n, v in dict(Wgu=Wgu, Wdn=Wdn, X=X, ids=ids.astype(np.int32), w=w, sc=sc).items()}
+    G = torch.full((T * k, 2 * I), np.nan, dtype=torch.float32, device=DEV)
+    out1 = torch.full((T, H), np.nan, dtype=torch.float32, device=DEV)
+    Yd = torch.full((T * k, H), np.nan, dtype=torch.float32, device=DEV)
+    out2 = torch.full((T, H), np.nan, dtype=torch.float32, device=DEV)
+
+    def calls():
+        qmv.qmv_id("q4_0", d["Wgu"], d["X"], d["ids"], G, 2 * I, H)
+        qmv.qmv_moe_down("q4_0", d["Wdn"], G, d["ids"], d["w"], out1, H, I, expert_scale=d["sc"])
+        qmv.qmv_id_swiglu("q4_0", d["Wdn"], G, d["ids"].view(-1, 1), Yd, H, I, expert_scale=d["sc"])
+        qmv.qmv_moe_wsum(Yd, d["w"], out2, k)
+
+    calls()
+    torch.cuda.synchronize()
+    eager = [t.cpu().numpy().copy() for t in (G, out1, out2)]
+    # the down half against the oracle, fed the gate_up rows the GPU produced
+    ref, a = oracle.moe_down("q4_0", Wdn, eager[0], ids, w, H, I, expert_scale=sc)
+    assert_within_tol(eager[1], ref, a, "eager one-launch")
+    assert_within_tol(eager[2], ref, a, "eager two-call")
+    gu, ga = oracle.qmv_id("q4_0", Wgu, X, ids, 2 * I, H)
+    assert_within_tol(eager[0], gu, ga, "eager gate_up")
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        calls()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (G, out1, Yd, out2):
+            t.fill_(np.nan)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for t, e, name in zip((G, out1, out2), eager, ("gate_up", "one-launch", "two-call")):
+            assert np.array_equal(t.cpu().numpy().view(np.uint32), e.view(np.uint32)), f"replay {rep} {name}"
