@@ -244,6 +244,35 @@ __device__ __forceinline__ void stage_x(float* xs, const float* __restrict__ x, 
     }
 }
 
+// stage_x in two halves, so that other loads can be issued between them:
+// stage_x_load issues this thread's 16-byte loads of x into v, stage_x_store
+// writes them to the padded layout.
+typedef float f32x4u_t __attribute__((ext_vector_type(4), aligned(4)));
+template <int NT, int XCH>
+__device__ __forceinline__ void stage_x_load(f32x4u_t (&v)[XCH], const float* __restrict__ x, int K) {
+    const int nch = K >> 2;
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+        const int c = threadIdx.x + i * NT;
+        if (c < nch) v[i] = *reinterpret_cast<const f32x4u_t*>(x + 4 * c);
+    }
+}
+template <int NT, int XCH>
+__device__ __forceinline__ void stage_x_store(float* xs, const f32x4u_t (&v)[XCH], int K) {
+    const int nch = K >> 2;
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+        const int c = threadIdx.x + i * NT;
+        if (c < nch)
+            *reinterpret_cast<float4*>(xs + (c >> 4) * XS_PAIR + 4 * (c & 15)) = make_float4(v[i].x, v[i].y, v[i].z, v[i].w);
+    }
+}
+
+// Workgroup barrier over LDS only: waits for this thread's LDS operations but
+// not for its outstanding global loads (__syncthreads waits for those too,
+// which would drain the weight loads already in flight).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // SiLU, z * sigmoid(z) = z / (1 + e^-z), in fp32. Below z = -88.7 e^-z
 // overflows and the quotient is -0, the limit; NaN propagates.
 __device__ __forceinline__ float silu_f(float z) { return z / (1.f + expf(-z)); }
@@ -343,12 +372,20 @@ __device__ __forceinline__ void m1_stream(const uint8_t* __restrict__ W, size_t 
             load_pair<DW>(W + rr * ldw + (size_t)p * PB, nxt[r]);
         }
     };
-    issue(tile, 0);
-    if constexpr (SW)
+    if constexpr (SW) {
+        issue(tile, 0);
         stage_swiglu<WAVES * 64>(xs, 0, x, 0, 1, K);
-    else
-        stage_x<WAVES * 64, (KMAX_STAGE / 4 + WAVES * 64 - 1) / (WAVES * 64)>(xs, x, K);
-    __syncthreads();
+        __syncthreads();
+    } else {
+        // x loads first, then the first weight loads: waiting for x before
+        // the LDS stores then leaves the weight loads in flight.
+        constexpr int XCH = (KMAX_STAGE / 4 + WAVES * 64 - 1) / (WAVES * 64);
+        f32x4u_t xv[XCH];
+        stage_x_load<WAVES * 64, XCH>(xv, x, K);
+        issue(tile, 0);
+        stage_x_store<WAVES * 64, XCH>(xs, xv, K);
+        lds_barrier();
+    }
     float tot[RPT];
 #pragma unroll
     for (int r = 0; r < RPT; ++r) tot[r] = 0.f;
@@ -1705,11 +1742,10 @@ int dense(int qtype, const void* Wv, size_t ldw, const float* X, size_t ldx, flo
                              : launch_generic<QMV_Q8_0>(W, ldw, X, ldx, Y, ldy, M, N, K, st);
 }
 
-template <int QT, int LPR, int RPT, bool SW>
+template <int QT, int LPR, int RPT, bool SW, int WAVES = 4>
 int launch_id_t(const uint8_t* W, size_t es, size_t ldw, int E, const float* X, size_t ldx, const uint32_t* ids,
                 int n_pairs, int top_k, float* Y, size_t ldy, int N, int K, const float* sc, int* err, int fast,
                 hipStream_t st) {
-    constexpr int WAVES = 4;
     constexpr int ROWS_PER_WG = (64 / LPR) * RPT * WAVES;
     const long tiles = ((long)N + ROWS_PER_WG - 1) / ROWS_PER_WG;
     if (tiles > 0x7FFFFFFF) return fail(QMV_EINVAL, "qmv_id: N too large");
@@ -2054,6 +2090,41 @@ int qmv_probe_mm(int waves, int tw, const void* W, size_t ldw, const float* X, s
 int qmv_probe_mm4(int S, int waves, const void* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M,
                   int N, int K, void* stream) {
     return launch_mm4((const uint8_t*)W, ldw, X, ldx, Y, ldy, M, N, K, S, waves, (hipStream_t)stream);
+}
+
+// Expert-indexed product (fast path, no SwiGLU) with a forced lanes-per-row
+// and wave count.
+int qmv_probe_id(int qtype, int lpr, int waves, const void* W, size_t es, size_t ldw, int E, const float* X,
+                 size_t ldx, const uint32_t* ids, int n_tokens, int top_k, float* Y, size_t ldy, int N, int K,
+                 const float* sc, void* stream) {
+    hipStream_t st = (hipStream_t)stream;
+    const uint8_t* w = (const uint8_t*)W;
+    const int np = n_tokens * top_k;
+#define QMV_P(QT, L, WV)                            \
+    if (qtype == QT && lpr == L && waves == WV) \
+        return launch_id_t<QT, L, 1, false, WV>(w, es, ldw, E, X, ldx, ids, np, top_k, Y, ldy, N, K, sc, nullptr, 1, st);
+#define QMV_PW(QT, WV) QMV_P(QT, 64, WV) QMV_P(QT, 32, WV) QMV_P(QT, 16, WV) QMV_P(QT, 8, WV) QMV_P(QT, 4, WV)
+    QMV_PW(QMV_Q4_0, 4) QMV_PW(QMV_Q4_0, 8) QMV_PW(QMV_Q4_0, 2)
+#undef QMV_PW
+#undef QMV_P
+    return fail(QMV_EINVAL, "probe: no variant");
+}
+
+// One-launch MoE down half with a forced lanes-per-row and wave count.
+int qmv_probe_moe_down(int qtype, int lpr, int waves, const void* W, size_t es, size_t ldw, int E, const float* G,
+                       size_t ldg, const uint32_t* ids, const float* wts, int n_tokens, int top_k, float* out,
+                       size_t ldo, int N, int K, const float* sc, void* stream) {
+    hipStream_t st = (hipStream_t)stream;
+    const uint8_t* w = (const uint8_t*)W;
+#define QMV_P(QT, L, WV)                            \
+    if (qtype == QT && lpr == L && waves == WV) \
+        return launch_moe_down_t<QT, L, WV>(w, es, ldw, E, G, ldg, ids, wts, n_tokens, top_k, out, ldo, N, K, sc, \
+                                            nullptr, st);
+#define QMV_PW(QT, WV) QMV_P(QT, 64, WV) QMV_P(QT, 32, WV) QMV_P(QT, 16, WV) QMV_P(QT, 8, WV) QMV_P(QT, 4, WV)
+    QMV_PW(QMV_Q4_0, 8) QMV_PW(QMV_Q4_0, 4)
+#undef QMV_PW
+#undef QMV_P
+    return fail(QMV_EINVAL, "probe: no variant");
 }
 #endif
 
