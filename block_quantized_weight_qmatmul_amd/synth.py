@@ -38,8 +38,9 @@ ROOT_SEED = 20261202
 T_SCALE, T_CODES, T_X, T_LOGITS, T_ESCALE, T_GATE_UP, T_RWEIGHT = 0, 1, 2, 3, 4, 5, 6
 
 QK = 32  # weights per block
-BLOCK_BYTES = {"q4_0": 18, "q8_0": 34}
-QTYPE_ID = {"q4_0": 2, "q8_0": 8}  # GGML type numbers for Q4_0 and Q8_0
+BLOCK_BYTES = {"q4_0": 18, "q8_0": 34, "q6_k": 210}
+BLOCK_ELEMS = {"q4_0": 32, "q8_0": 32, "q6_k": 256}
+QTYPE_ID = {"q4_0": 2, "q8_0": 8, "q6_k": 14}  # GGML type numbers
 
 # Scale ranges and code ranges the workloads draw from.
 Q4_0_D_RANGE = (0.001, 0.02)
@@ -51,9 +52,10 @@ def rng(cfg: int, copy: int, tensor: int, part: int = 0) -> np.random.Generator:
 
 
 def row_bytes(qtype: str, K: int) -> int:
-    if K % QK:
-        raise ValueError(f"K={K} is not a multiple of {QK}")
-    return K // QK * BLOCK_BYTES[qtype]
+    qk = BLOCK_ELEMS[qtype]
+    if K % qk:
+        raise ValueError(f"K={K} is not a multiple of {qk}")
+    return K // qk * BLOCK_BYTES[qtype]
 
 
 def _scales_f16_bytes(r: np.random.Generator, shape, lo: float, hi: float) -> np.ndarray:
@@ -69,6 +71,8 @@ def make_weights(qtype: str, N: int, K: int, cfg: int, copy: int = 0, part: int 
     Bytes past the dense row length (when ``ldw`` exceeds it) are filled with
     0xA5 so that a reader that strays into the row padding gets garbage.
     """
+    if qtype == "q6_k":
+        return _make_q6_k(N, K, cfg, copy, part, d_range, ldw)
     bb = BLOCK_BYTES[qtype]
     nb = K // QK
     dense = row_bytes(qtype, K)
@@ -84,6 +88,33 @@ def make_weights(qtype: str, N: int, K: int, cfg: int, copy: int = 0, part: int 
         blocks[..., 2:] = rc.integers(0, 256, size=(N, nb, bb - 2), dtype=np.uint8)
     else:
         blocks[..., 2:] = rc.integers(-127, 128, size=(N, nb, bb - 2)).astype(np.int8).view(np.uint8)
+    if ldw == dense:
+        return blocks.reshape(N, dense)
+    out = np.full((N, ldw), 0xA5, dtype=np.uint8)
+    out[:, :dense] = blocks.reshape(N, dense)
+    return out
+
+
+Q6_K_D_RANGE = (1e-5, 5e-5)
+
+
+def _make_q6_k(N, K, cfg, copy, part, d_range, ldw):
+    """Q6_K rows: per 256-weight super-block, 192 bytes of code bits drawn
+    uniformly (so every 6-bit code is uniform over 0..63), 16 int8 sub-block
+    scales uniform over -128..127, and a binary16 scale d ~ U(d_range)
+    (default 1e-5..5e-5, mostly binary16 subnormals, as small super-block
+    scales are). Padding bytes past the dense row are 0xA5."""
+    nb = K // 256
+    dense = nb * 210
+    ldw = dense if ldw is None else ldw
+    if ldw < dense:
+        raise ValueError("ldw smaller than a dense row")
+    d_range = Q6_K_D_RANGE if d_range is None else d_range
+    blocks = np.empty((N, nb, 210), dtype=np.uint8)
+    rc = rng(cfg, copy, T_CODES, part)
+    blocks[..., 0:192] = rc.integers(0, 256, size=(N, nb, 192), dtype=np.uint8)
+    blocks[..., 192:208] = rc.integers(-128, 128, size=(N, nb, 16)).astype(np.int8).view(np.uint8)
+    blocks[..., 208:210] = _scales_f16_bytes(rng(cfg, copy, T_SCALE, part), (N, nb), *d_range)
     if ldw == dense:
         return blocks.reshape(N, dense)
     out = np.full((N, ldw), 0xA5, dtype=np.uint8)

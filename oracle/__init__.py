@@ -27,9 +27,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "qmv_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-Q4_0, Q8_0 = 2, 8
-QTYPES = {"q4_0": Q4_0, "q8_0": Q8_0}
-BLOCK_BYTES = {Q4_0: 18, Q8_0: 34}
+Q4_0, Q8_0, Q6_K = 2, 8, 14
+QTYPES = {"q4_0": Q4_0, "q8_0": Q8_0, "q6_k": Q6_K}
+BLOCK_BYTES = {Q4_0: 18, Q8_0: 34, Q6_K: 210}
+BLOCK_ELEMS = {Q4_0: 32, Q8_0: 32, Q6_K: 256}
 
 _lib = None
 
@@ -86,7 +87,7 @@ def f16_to_f64(bits: int) -> float:
 def dequant_row(qtype, row: np.ndarray, K: int) -> np.ndarray:
     row = np.ascontiguousarray(row, dtype=np.uint8)
     q = _qt(qtype)
-    if row.size < K // 32 * BLOCK_BYTES[q]:
+    if row.size < K // BLOCK_ELEMS[q] * BLOCK_BYTES[q]:
         raise ValueError("row too short")
     out = np.empty(K, dtype=np.float64)
     if _load().oracle_dequant_row(q, _ptr(row), K, _ptr(out)) != 0:

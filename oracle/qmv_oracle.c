@@ -35,6 +35,12 @@
  *   The scale is decoded exactly from its IEEE 754 binary16 bit pattern:
  *   subnormals kept, signed zero kept, Inf/NaN propagate.
  *
+ *   Q6_K (210 B per 256 weights): the format of the lm_head the pages load
+ *   natively (`lm_head_q6k` in `MlxModelWeights`, model.rs: gemma4's
+ *   token_embd.weight as Q6_K [2816, 262144] = 605 MB, which fixes 210 bytes
+ *   per 256 weights). The pages name the format only; the layout read here is
+ *   the GGML k-quant Q6_K super-block, written out at decode_superblock_q6_k.
+ *
  * Expert-indexed variant (the `quantized_matmul_id_ggml` calls in
  * `MlxModelWeights::encode_one_layer` on the hf2q page
  * `src/inference/models/gemma4/gpu_full_attn.rs`, MoE blocks B11 and B13,
@@ -65,8 +71,10 @@
 #endif
 
 #define ORACLE_QK 32
+#define ORACLE_QK_K 256
 #define ORACLE_Q4_0 2
 #define ORACLE_Q8_0 8
+#define ORACLE_Q6_K 14
 
 /* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
 double oracle_f16_to_f64(uint16_t h) {
@@ -87,7 +95,38 @@ double oracle_f16_to_f64(uint16_t h) {
 static int block_bytes(int qtype) {
     if (qtype == ORACLE_Q4_0) return 18;
     if (qtype == ORACLE_Q8_0) return 34;
+    if (qtype == ORACLE_Q6_K) return 210;
     return -1;
+}
+
+/* Weights per block: 32, or 256 for the super-block format. */
+static int block_elems(int qtype) { return qtype == ORACLE_Q6_K ? ORACLE_QK_K : ORACLE_QK; }
+
+/*
+ * Q6_K super-block (210 bytes, 256 weights), the GGML k-quant 6-bit format:
+ *   bytes   0..127  ql: low 4 bits of the codes
+ *   bytes 128..191  qh: high 2 bits of the codes
+ *   bytes 192..207  16 int8 sub-block scales, one per 16 weights
+ *   bytes 208..209  binary16 super-block scale d (low byte first)
+ * Weight i (0..255): half h = i / 128 and r = i % 128, quarter g = r / 32,
+ * l = r % 32. Its low 4 bits are the low (g < 2) or high (g >= 2) nibble of
+ * ql[64h + 32(g % 2) + l]; its high 2 bits are bits 2g, 2g + 1 of
+ * qh[32h + l]; code q = low + 16 * high (0..63); its scale is
+ * scales[8h + 2g + l / 16]; w = d * scale * (q - 32).
+ */
+static void decode_superblock_q6_k(const uint8_t* b, double* out) {
+    const uint8_t* ql = b;
+    const uint8_t* qh = b + 128;
+    const int8_t* sc = (const int8_t*)(b + 192);
+    double d = oracle_f16_to_f64((uint16_t)(b[208] | (b[209] << 8)));
+    for (int i = 0; i < ORACLE_QK_K; ++i) {
+        int h = i / 128, r = i % 128, g = r / 32, l = r % 32;
+        int byte = ql[64 * h + 32 * (g % 2) + l];
+        int low = g < 2 ? (byte & 0x0F) : (byte >> 4);
+        int high = (qh[32 * h + l] >> (2 * g)) & 3;
+        int q = low + 16 * high;
+        out[i] = d * (double)sc[8 * h + 2 * g + l / 16] * (double)(q - 32);
+    }
 }
 
 /* Decode one 32-element block into out[0..32). */
@@ -109,11 +148,16 @@ static void decode_block(int qtype, const uint8_t* b, double* out) {
     }
 }
 
-/* Dequantize one row of K weights (K % 32 == 0) into w[0..K). */
+/* Dequantize one row of K weights (K a multiple of the block size) into w[0..K). */
 int oracle_dequant_row(int qtype, const uint8_t* row, int K, double* w) {
-    int bb = block_bytes(qtype);
-    if (bb < 0 || K <= 0 || K % ORACLE_QK) return -1;
-    for (int b = 0; b < K / ORACLE_QK; ++b) decode_block(qtype, row + (size_t)b * bb, w + (size_t)b * ORACLE_QK);
+    int bb = block_bytes(qtype), qk = block_elems(qtype);
+    if (bb < 0 || K <= 0 || K % qk) return -1;
+    for (int b = 0; b < K / qk; ++b) {
+        if (qtype == ORACLE_Q6_K)
+            decode_superblock_q6_k(row + (size_t)b * bb, w + (size_t)b * qk);
+        else
+            decode_block(qtype, row + (size_t)b * bb, w + (size_t)b * qk);
+    }
     return 0;
 }
 
@@ -156,9 +200,9 @@ static void set_threads(int nthreads) {
  */
 int oracle_qmv(int qtype, const uint8_t* W, size_t ldw, const float* X, size_t ldx,
                int M, int N, int K, double* Y, double* A, size_t ldy, int nthreads) {
-    int bb = block_bytes(qtype);
-    if (bb < 0 || M < 0 || N < 0 || K <= 0 || K % ORACLE_QK) return -1;
-    if (ldw < (size_t)(K / ORACLE_QK) * bb || ldx < (size_t)K || ldy < (size_t)N) return -1;
+    int bb = block_bytes(qtype), qk = block_elems(qtype);
+    if (bb < 0 || M < 0 || N < 0 || K <= 0 || K % qk) return -1;
+    if (ldw < (size_t)(K / qk) * bb || ldx < (size_t)K || ldy < (size_t)N) return -1;
     set_threads(nthreads);
     int err = 0;
 #pragma omp parallel
@@ -193,9 +237,9 @@ static int qmv_id_core(int qtype, const uint8_t* W, size_t expert_stride, size_t
                        const float* X, const double* Xd, size_t ldx, const uint32_t* ids, int n_tokens,
                        int top_k, const float* expert_scale, int N, int K, double* Y, double* A, size_t ldy,
                        int nthreads) {
-    int bb = block_bytes(qtype);
-    if (bb < 0 || n_experts <= 0 || n_tokens < 0 || top_k <= 0 || N < 0 || K <= 0 || K % ORACLE_QK) return -1;
-    if (ldw < (size_t)(K / ORACLE_QK) * bb || ldx < (size_t)K || ldy < (size_t)N) return -1;
+    int bb = block_bytes(qtype), qk = block_elems(qtype);
+    if (bb < 0 || n_experts <= 0 || n_tokens < 0 || top_k <= 0 || N < 0 || K <= 0 || K % qk) return -1;
+    if (ldw < (size_t)(K / qk) * bb || ldx < (size_t)K || ldy < (size_t)N) return -1;
     if (expert_stride < (size_t)N * ldw) return -1;
     int P = n_tokens * top_k;
     for (int p = 0; p < P; ++p)

@@ -431,3 +431,95 @@ def test_moe_down_composition_against_numpy_brute_force(qtype):
             mag += abs(float(w[t, s]) * float(sc[e])) * np.abs(prod).sum(axis=1)
         assert np.all(np.abs(out[t] - want) <= 1e-12 * mag + 1e-300), t
         assert np.allclose(A[t], mag, rtol=1e-12, atol=0)
+
+
+# --------------------------------------------------------------------------
+# Q6_K super-blocks (256 weights, 210 bytes).
+# --------------------------------------------------------------------------
+def _enc_q6_k(codes, scales, d_bits):
+    """Lay out 256 six-bit codes, 16 int8 scales and a binary16 scale the way
+    the GGML Q6_K super-block stores them, walking the storage bytes: ql byte
+    64h + 32p + l holds code 128h + 32p + l in its low nibble and code
+    128h + 32(p + 2) + l in its high nibble; qh byte 32h + l holds bits 4..5
+    of codes 128h + 32g + l at bit 2g (g = 0..3)."""
+    b = bytearray(210)
+    for h in range(2):
+        for p in range(2):
+            for l in range(32):
+                lo = codes[128 * h + 32 * p + l] & 15
+                hi = codes[128 * h + 32 * (p + 2) + l] & 15
+                b[64 * h + 32 * p + l] = lo | (hi << 4)
+        for l in range(32):
+            b[128 + 32 * h + l] = sum(((codes[128 * h + 32 * g + l] >> 4) & 3) << (2 * g) for g in range(4))
+    b[192:208] = bytes(s & 0xFF for s in scales)
+    b[208], b[209] = d_bits & 0xFF, d_bits >> 8
+    return bytes(b)
+
+
+def test_q6_k_lm_head_size_closed_form():
+    # the pages: token_embd.weight as Q6_K [2816, 262144] is 605 MB
+    from block_quantized_weight_qmatmul_amd import synth
+    assert 262144 * (2816 // 256) * 210 == 605_552_640
+    assert synth.row_bytes("q6_k", 2816) == 2310
+    with pytest.raises(ValueError):
+        oracle.dequant_row("q6_k", np.zeros(210, np.uint8), 128)  # K not a multiple of 256
+
+
+def test_q6_k_hand_built_super_blocks():
+    """Every code at every position, signed scales including -128, and
+    normal, subnormal and negative super-block scales: weight i must be
+    d * scale[i // 16] * (code_i - 32)."""
+    r = np.random.default_rng(61)
+    for trial, d_bits in enumerate([0x3C00, 0x3800, 0x0001, 0x03FF, 0xC400, 0x0000, 0x7BFF]):
+        codes = [int(c) for c in r.permutation(np.repeat(np.arange(64), 4))]  # every code, 4 times
+        scales = [int(v) for v in r.integers(-128, 128, 16)]
+        scales[trial % 16] = -128
+        raw = np.frombuffer(_enc_q6_k(codes, scales, d_bits), dtype=np.uint8)
+        w = oracle.dequant_row("q6_k", raw, 256)
+        d = float(np.array(d_bits, dtype=np.uint16).view(np.float16))
+        want = np.array([d * scales[i // 16] * (codes[i] - 32) for i in range(256)])
+        assert np.array_equal(w, want), trial
+
+
+def test_q6_k_constant_codes_and_one_hot():
+    raw = np.frombuffer(_enc_q6_k([33] * 256, [1] * 16, 0x3C00), dtype=np.uint8)
+    W = np.tile(raw, (3, 2))  # 3 rows of K = 512
+    x = np.random.default_rng(62).standard_normal((1, 512)).astype(np.float32)
+    Y, A = oracle.qmv("q6_k", W, x)
+    assert np.all(np.abs(Y[0] - math.fsum(x[0].astype(np.float64))) <= 512 * 2.0 ** -53 * A[0])
+    from block_quantized_weight_qmatmul_amd import synth
+    Wr = synth.make_weights("q6_k", 5, 512, cfg=62)
+    for k in (0, 1, 127, 128, 255, 256, 300, 511):
+        e = np.zeros((1, 512), np.float32)
+        e[0, k] = 1.0
+        Y, _ = oracle.qmv("q6_k", Wr, e)
+        for n in range(5):
+            assert Y[0, n] == oracle.dequant_row("q6_k", Wr[n], 512)[k]
+
+
+def test_q6_k_brute_force_tiny_shapes_against_exact_rationals():
+    r = np.random.default_rng(63)
+    for K in (256, 512):
+        N, M = 3, 2
+        rows, dense = [], []
+        for n in range(N):
+            raw, vals = b"", []
+            for sb in range(K // 256):
+                codes = [int(c) for c in r.integers(0, 64, 256)]
+                scales = [int(c) for c in r.integers(-128, 128, 16)]
+                d_bits = [0x0123, 0x3555, 0x8C00][(n + sb) % 3]
+                raw += _enc_q6_k(codes, scales, d_bits)
+                d = _f16_fraction(d_bits)
+                vals += [d * scales[i // 16] * (codes[i] - 32) for i in range(256)]
+            rows.append(np.frombuffer(raw, dtype=np.uint8))
+            dense.append(vals)
+        W = np.stack(rows)
+        X = r.standard_normal((M, K)).astype(np.float32)
+        Y, A = oracle.qmv("q6_k", W, X)
+        for m in range(M):
+            for n in range(N):
+                prods = [dense[n][k] * Fraction(float(X[m, k])) for k in range(K)]
+                exact, mag = sum(prods), sum(abs(p) for p in prods)
+                bound = Fraction(K * 2.0 ** -53 * float(mag))
+                assert abs(Fraction(Y[m, n]) - exact) <= bound
+                assert abs(Fraction(A[m, n]) - mag) <= bound
