@@ -210,6 +210,25 @@ def moe_throughput(dev, T, steps=40, mode="id"):
             "GBps": round(nbytes / t / 1e9, 1), "pct_hbm_peak": round(100 * nbytes / t / 1e9 / HBM_PEAK_GBS, 2)}
 
 
+def lm_head_q6k_throughput(dev, steps=20):
+    """The pages' lm_head as Q6_K: [2816 -> 262144] (605.6 MB), one token
+    (M = 1), graph replays of one copy (it is larger than the chip's last-level
+    cache, so every replay streams it from HBM)."""
+    import torch
+
+    from block_quantized_weight_qmatmul_amd import qmv, synth
+    N, K = 262144, 2816
+    W = torch.from_numpy(synth.make_weights("q6_k", N, K, cfg=5)).to(dev)
+    X = torch.from_numpy(synth.make_x(1, K, cfg=5)[0]).to(dev)
+    Y = torch.empty(N, device=dev)
+    nbytes = N * synth.row_bytes("q6_k", K)
+    graphs = capture_steps(lambda s: qmv.qmv_q6_k(s[0], s[1], s[2]), [(W, X, Y)])
+    t = time_graphs(graphs, steps, 3) / steps
+    del graphs, W
+    return {"workload": "q6_k_m1_lm_head_2816x262144", "weight_bytes": nbytes, "us_per_call": round(t * 1e6, 2),
+            "GBps": round(nbytes / t / 1e9, 1), "pct_hbm_peak": round(100 * nbytes / t / 1e9 / HBM_PEAK_GBS, 2)}
+
+
 def cpu_baseline(target_s: float):
     """The CPU oracle (fp64, OpenMP over rows) timed on a bounded sample of
     the layer set: the first rows of every projection, sized to take about
@@ -397,6 +416,7 @@ def main():
         extra["moe_ffn_t1_two_call"] = moe_throughput(dev, 1, mode="ffn_two_call")
         extra["moe_ffn_t32_two_call"] = moe_throughput(dev, 32, mode="ffn_two_call")
         extra["moe_ffn_t32_fused"] = moe_throughput(dev, 32, mode="ffn_fused")
+        extra["lm_head_q6_k"] = lm_head_q6k_throughput(dev)
     del sets
     torch.cuda.empty_cache()
 

@@ -1430,6 +1430,230 @@ __global__ __launch_bounds__(WAVES * 64) void k_moe_down(const uint8_t* __restri
 }
 
 // ---------------------------------------------------------------------------
+// Q6_K (GGML k-quant 6-bit super-blocks: 256 weights in 210 bytes).
+// Super-block layout: ql[128] low 4 bits, qh[64] high 2 bits, 16 int8
+// sub-block scales, binary16 d. Weight i: h = i / 128, r = i % 128,
+// g = r / 32, l = r % 32; low bits = nibble (g / 2) of ql[64h + 32(g % 2) + l],
+// high bits = bits 2g..2g+1 of qh[32h + l], q = low | high << 4, scale =
+// scales[i / 16], w = d * scale * (q - 32).
+//
+// The kernel's unit is half a super-block (128 weights: 64 ql bytes, 32 qh
+// bytes, 8 scales, and d): lanes take units as the Q4_0 kernels take pairs.
+// Rows of an odd number of super-blocks are only 2-byte aligned; the loads
+// use 2-byte aligned vector types, which gfx950 serves as unaligned global
+// loads. sum (q - 32) x = sum q x - 32 sum x per 16-weight group, with the
+// group sums of x computed once when x is staged.
+// ---------------------------------------------------------------------------
+constexpr int Q6_SB_BYTES = 210;
+constexpr int Q6_UNIT_DW = 27;   // 16 ql + 8 qh + 2 scale dwords + d
+constexpr int XS_Q6 = 132;       // LDS floats per staged unit (128 + 4 pad)
+constexpr int KMAX_Q6 = 16384;   // largest K the Q6_K kernel stages
+
+__host__ __device__ constexpr size_t q6_xs_bytes(int K) {
+    return ((size_t)(K / 128) * XS_Q6 + (size_t)(K / 16)) * sizeof(float);
+}
+
+// Registers of unit h (0 or 1) of the super-block at sb.
+__device__ __forceinline__ void load_q6_unit(const uint8_t* sb, int h, uint32_t* r) {
+    typedef uint32_t u32x4a2 __attribute__((ext_vector_type(4), aligned(2)));
+    typedef uint32_t u32x2a2 __attribute__((ext_vector_type(2), aligned(2)));
+    const u32x4a2* ql = reinterpret_cast<const u32x4a2*>(sb + 64 * h);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const u32x4a2 v = ql[i];
+        r[4 * i] = v.x, r[4 * i + 1] = v.y, r[4 * i + 2] = v.z, r[4 * i + 3] = v.w;
+    }
+    const u32x4a2* qh = reinterpret_cast<const u32x4a2*>(sb + 128 + 32 * h);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const u32x4a2 v = qh[i];
+        r[16 + 4 * i] = v.x, r[17 + 4 * i] = v.y, r[18 + 4 * i] = v.z, r[19 + 4 * i] = v.w;
+    }
+    const u32x2a2 sc = *reinterpret_cast<const u32x2a2*>(sb + 192 + 8 * h);
+    r[24] = sc.x;
+    r[25] = sc.y;
+    r[26] = *reinterpret_cast<const uint16_t*>(sb + 208);
+}
+
+// Stage nx rows of x (row i at X + xoff[i]) for the Q6_K kernel: row i's
+// unit u at xs + i * xstride + u * XS_Q6, and the sum of each 16-weight group
+// j at gs + i * gstride + j. One thread per group of 16; loads are issued
+// by stage_q6_load, and stored (with the sums) by stage_q6_store, so that
+// weight loads can be issued between the two.
+template <int NT, int GCH, int MX>
+struct Q6Stage {
+    f32x4u_t v[MX][GCH][4];
+    __device__ __forceinline__ void load(const float* __restrict__ X, const size_t* xoff, int nx, int K) {
+        const int ng = K >> 4;
+#pragma unroll
+        for (int i = 0; i < MX; ++i) {
+            if (i < nx) {
+#pragma unroll
+                for (int c = 0; c < GCH; ++c) {
+                    const int grp = threadIdx.x + c * NT;
+                    if (grp < ng) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            v[i][c][q] = *reinterpret_cast<const f32x4u_t*>(X + xoff[i] + 16 * grp + 4 * q);
+                    }
+                }
+            }
+        }
+    }
+    __device__ __forceinline__ void store(float* xs, size_t xstride, float* gs, size_t gstride, int nx, int K) {
+        const int ng = K >> 4;
+#pragma unroll
+        for (int i = 0; i < MX; ++i) {
+            if (i < nx) {
+#pragma unroll
+                for (int c = 0; c < GCH; ++c) {
+                    const int grp = threadIdx.x + c * NT;
+                    if (grp < ng) {
+                        float* dst = xs + i * xstride + (grp >> 3) * XS_Q6 + 16 * (grp & 7);
+                        float sum = 0.f;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const f32x4u_t t = v[i][c][q];
+                            *reinterpret_cast<float4*>(dst + 4 * q) = make_float4(t.x, t.y, t.z, t.w);
+                            sum += (t.x + t.y) + (t.z + t.w);
+                        }
+                        gs[i * gstride + grp] = sum;
+                    }
+                }
+            }
+        }
+    }
+};
+
+// tot[i] += dot of one unit (registers r) with staged row i (xs_i = its
+// unit's 128 values, gs_i = its 8 group sums), for i < nx.
+template <int MX>
+__device__ __forceinline__ void q6_unit_dot(const uint32_t* r, const float* xs, size_t xstride, const float* gs,
+                                            size_t gstride, int nx, float* tot) {
+    const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)(r[26] & 0xFFFFu));
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+#pragma unroll
+        for (int is = 0; is < 2; ++is) {
+            float acc[MX];
+#pragma unroll
+            for (int i = 0; i < MX; ++i) acc[i] = 0.f;
+#pragma unroll
+            for (int mm = 0; mm < 4; ++mm) {
+                const int m = 4 * is + mm;
+                const uint32_t lw = (g & 1) ? r[8 + m] : r[m];
+                const uint32_t nib = (g < 2) ? (lw & 0x0F0F0F0Fu) : ((lw >> 4) & 0x0F0F0F0Fu);
+                const uint32_t q = r[16 + m];
+                const uint32_t hq = g == 0 ? (q << 4) : g == 1 ? (q << 2) : g == 2 ? q : (q >> 2);
+                const uint32_t c = (hq & 0x30303030u) | nib;
+                const float c0 = (float)(c & 0xFF), c1 = (float)((c >> 8) & 0xFF);
+                const float c2 = (float)((c >> 16) & 0xFF), c3 = (float)(c >> 24);
+#pragma unroll
+                for (int i = 0; i < MX; ++i) {
+                    if (i < nx) {
+                        const float4 xv = *reinterpret_cast<const float4*>(xs + i * xstride + 32 * g + 4 * m);
+                        acc[i] = fmaf(c0, xv.x, acc[i]);
+                        acc[i] = fmaf(c1, xv.y, acc[i]);
+                        acc[i] = fmaf(c2, xv.z, acc[i]);
+                        acc[i] = fmaf(c3, xv.w, acc[i]);
+                    }
+                }
+            }
+            const int j = 2 * g + is;
+            const float sc = (float)(int8_t)(r[24 + (j >> 2)] >> (8 * (j & 3)));
+#pragma unroll
+            for (int i = 0; i < MX; ++i)
+                if (i < nx) tot[i] = fmaf(sc * d, fmaf(-32.f, gs[i * gstride + j], acc[i]), tot[i]);
+        }
+    }
+}
+
+// Persistent M <= MX kernel: tiles of ROWS = (64 / LPR) * WAVES rows, tiles
+// blockIdx.x, blockIdx.x + gridDim.x, ...; lane j of a row's LPR lanes takes
+// units j, j + LPR, ... of the row, one step of register prefetch; row sums
+// reduced over the lane group. Needs K % 256 == 0, 0 < K <= KMAX_Q6.
+template <int LPR, int WAVES, int MX>
+__global__ __launch_bounds__(WAVES * 64) void k_q6k(const uint8_t* __restrict__ W, size_t ldw,
+                                                     const float* __restrict__ X, size_t ldx, float* __restrict__ Y,
+                                                     size_t ldy, int nx, int N, int K) {
+    constexpr int GROUPS = 64 / LPR;
+    constexpr int ROWS = GROUPS * WAVES;
+    constexpr int NT = WAVES * 64;
+    constexpr int GCH = (KMAX_Q6 / 16 + NT - 1) / NT;
+    extern __shared__ __align__(16) float xs[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane / LPR, j = lane % LPR;
+    const int U = K >> 7;
+    const int IPT = (U + LPR - 1) / LPR;
+    const long ntiles = ((long)N + ROWS - 1) / ROWS;
+    const long lrow = (long)(wave * GROUPS + g);
+    const size_t xstride = (size_t)U * XS_Q6;
+    float* gs = xs + (size_t)nx * xstride;
+    const size_t gstride = (size_t)(K >> 4);
+
+    long tile = blockIdx.x;
+    if (tile >= ntiles) return;  // uniform over the workgroup
+    int it = 0;
+    uint32_t nxt[Q6_UNIT_DW];
+    auto issue = [&](long tl, int i) {
+        long row = tl * ROWS + lrow;
+        row = row < N ? row : N - 1;
+        int u = j + i * LPR;
+        u = u < U ? u : U - 1;
+        load_q6_unit(W + (size_t)row * ldw + (size_t)(u >> 1) * Q6_SB_BYTES, u & 1, nxt);
+    };
+    if constexpr (MX == 1) {
+        // x loads first, then the first weight loads (see m1_stream)
+        const size_t xo = 0;
+        Q6Stage<NT, GCH, 1> stg;
+        stg.load(X, &xo, 1, K);
+        issue(tile, 0);
+        stg.store(xs, 0, gs, 0, 1, K);
+    } else {
+        issue(tile, 0);
+        for (int i = 0; i < nx; ++i) {
+            const size_t xo = (size_t)i * ldx;
+            Q6Stage<NT, GCH, 1> stg;
+            stg.load(X, &xo, 1, K);
+            stg.store(xs + i * xstride, 0, gs + i * gstride, 0, 1, K);
+        }
+    }
+    lds_barrier();
+    float tot[MX];
+#pragma unroll
+    for (int i = 0; i < MX; ++i) tot[i] = 0.f;
+    while (true) {
+        uint32_t cur[Q6_UNIT_DW];
+#pragma unroll
+        for (int d = 0; d < Q6_UNIT_DW; ++d) cur[d] = nxt[d];
+        const int u = j + it * LPR;
+        int it2 = it + 1;
+        long tile2 = tile;
+        if (it2 == IPT) {
+            it2 = 0;
+            tile2 += gridDim.x;
+        }
+        const bool more = tile2 < ntiles;
+        if (more) issue(tile2, it2);
+        if (u < U) q6_unit_dot<MX>(cur, xs + (size_t)u * XS_Q6, xstride, gs + 8 * u, gstride, nx, tot);
+        if (it == IPT - 1) {
+            const long row = tile * ROWS + lrow;
+#pragma unroll
+            for (int i = 0; i < MX; ++i) {
+                if (i < nx) {
+                    const float sum = lane_group_sum<LPR>(tot[i]);
+                    if (j == LPR - 1 && row < N) Y[(size_t)i * ldy + row] = sum;
+                }
+                tot[i] = 0.f;
+            }
+        }
+        if (!more) break;
+        tile = tile2;
+        it = it2;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
 constexpr int KMAX_FAST = 15360;     // x staged in <= 64 KiB of LDS
@@ -1887,6 +2111,39 @@ int launch_moe_down(const uint8_t* W, size_t es, size_t ldw, int E, const float*
 }
 
 constexpr size_t MD_LDS_MAX = 64 * 1024;  // staged SwiGLU rows of one token
+
+template <int LPR, int WAVES, int MX>
+int launch_q6k_t(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int nx, int N, int K,
+                 int wgs_per_cu, hipStream_t st) {
+    constexpr int ROWS = (64 / LPR) * WAVES;
+    const long tiles = ((long)N + ROWS - 1) / ROWS;
+    long nwg = (long)num_cus() * (wgs_per_cu > 0 ? wgs_per_cu : 2);
+    nwg = nwg < tiles ? nwg : tiles;
+    const size_t lds = (size_t)nx * q6_xs_bytes(K);
+    hipLaunchKernelGGL((k_q6k<LPR, WAVES, MX>), dim3((unsigned)nwg), dim3(WAVES * 64), lds, st, W, ldw, X, ldx, Y, ldy,
+                       nx, N, K);
+    return check_launch("qmv_q6_k kernel");
+}
+
+// Rows of X in launches of up to 4 (one launch when M = 1).
+int launch_q6k(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N, int K,
+               int lpr, int wgs_per_cu, hipStream_t st) {
+    if (lpr <= 0) lpr = pick_lpr(K / 128);
+    for (int m0 = 0; m0 < M; m0 += 4) {
+        const int nx = M - m0 < 4 ? M - m0 : 4;
+        const float* Xm = X + (size_t)m0 * ldx;
+        float* Ym = Y + (size_t)m0 * ldy;
+        int rc = QMV_EINVAL;
+#define QMV_Q6_CASE(L)                                                                                   \
+    if (lpr == L)                                                                                        \
+        rc = nx == 1 ? launch_q6k_t<L, 8, 1>(W, ldw, Xm, ldx, Ym, ldy, 1, N, K, wgs_per_cu, st)          \
+                     : launch_q6k_t<L, 8, 4>(W, ldw, Xm, ldx, Ym, ldy, nx, N, K, wgs_per_cu, st);
+        QMV_Q6_CASE(64) QMV_Q6_CASE(32) QMV_Q6_CASE(16) QMV_Q6_CASE(8) QMV_Q6_CASE(4)
+#undef QMV_Q6_CASE
+        if (rc) return rc == QMV_EINVAL ? fail(QMV_EINVAL, "internal: no Q6_K kernel for lpr=%d", lpr) : rc;
+    }
+    return QMV_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -1913,6 +2170,36 @@ int qmv_id_swiglu(int qtype, const void* Wv, size_t expert_stride_bytes, size_t 
                   int N, int K, const float* expert_scale, int* err_flag, void* stream) {
     return id_common<true>("qmv_id_swiglu", qtype, Wv, expert_stride_bytes, ldw_bytes, n_experts, G, ldg, ids,
                            n_tokens, top_k, Y, ldy, N, K, expert_scale, err_flag, stream);
+}
+
+int qmv_q6_k(const void* Wv, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N, int K,
+             void* stream) {
+    const char* name = "qmv_q6_k";
+    if (M < 0 || M > QMV_MAX_M) return fail(QMV_EUNSUPPORTED, "%s: M=%d outside 0..%d", name, M, QMV_MAX_M);
+    if (N < 0) return fail(QMV_EINVAL, "%s: N=%d < 0", name, N);
+    if (K < 0 || K % 256) return fail(QMV_EINVAL, "%s: K=%d is not a non-negative multiple of 256", name, K);
+    if (M == 0 || N == 0) return QMV_OK;
+    if (!Wv && K > 0) return fail(QMV_EINVAL, "%s: W is NULL", name);
+    if (!X && K > 0) return fail(QMV_EINVAL, "%s: X is NULL", name);
+    if (!Y) return fail(QMV_EINVAL, "%s: Y is NULL", name);
+    if (K > KMAX_Q6) return fail(QMV_EUNSUPPORTED, "%s: K=%d exceeds %d", name, K, KMAX_Q6);
+    const size_t row = (size_t)(K / 256) * Q6_SB_BYTES;
+    if (ldw < row) return fail(QMV_EINVAL, "%s: ldw_bytes=%zu < K/256*210=%zu", name, ldw, row);
+    if (M > 1 && ldx < (size_t)K) return fail(QMV_EINVAL, "%s: ldx=%zu < K=%d", name, ldx, K);
+    if (M > 1 && ldy < (size_t)N) return fail(QMV_EINVAL, "%s: ldy=%zu < N=%d", name, ldy, N);
+    if (((uintptr_t)Wv & 1) || (ldw & 1)) return fail(QMV_EALIGN, "%s: W and ldw_bytes must be 2-byte aligned", name);
+    if (((uintptr_t)X & 3) || ((uintptr_t)Y & 3)) return fail(QMV_EALIGN, "%s: X and Y must be 4-byte aligned", name);
+    if (M == 1) ldx = (size_t)K, ldy = (size_t)N;
+    if ((size_t)N > (SIZE_MAX - row) / (ldw ? ldw : 1)) return fail(QMV_EINVAL, "%s: N*ldw overflows", name);
+    const size_t wbytes = K ? (size_t)(N - 1) * ldw + row : 0;
+    const size_t xbytes = K ? ((size_t)(M - 1) * ldx + K) * 4 : 0;
+    const size_t ybytes = ((size_t)(M - 1) * ldy + N) * 4;
+    if (overlaps(Y, ybytes, Wv, wbytes) || overlaps(Y, ybytes, X, xbytes))
+        return fail(QMV_EINVAL, "%s: Y overlaps W or X", name);
+    hipStream_t st = (hipStream_t)stream;
+    if (K == 0)  // empty sums: the generic kernel reads no weights and writes zeros
+        return launch_generic<QMV_Q4_0>((const uint8_t*)Wv, ldw, X, ldx, Y, ldy, M, N, 0, st);
+    return launch_q6k((const uint8_t*)Wv, ldw, X, ldx, Y, ldy, M, N, K, 0, 0, st);
 }
 
 int qmv_moe_wsum(const float* Y, size_t ldy, const float* weights, int n_tokens, int top_k, int N, float* out,
@@ -2108,6 +2395,12 @@ int qmv_probe_id(int qtype, int lpr, int waves, const void* W, size_t es, size_t
 #undef QMV_PW
 #undef QMV_P
     return fail(QMV_EINVAL, "probe: no variant");
+}
+
+// Q6_K with a forced lanes-per-row and workgroups per compute unit.
+int qmv_probe_q6k(int lpr, int wgs_per_cu, const void* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy,
+                  int M, int N, int K, void* stream) {
+    return launch_q6k((const uint8_t*)W, ldw, X, ldx, Y, ldy, M, N, K, lpr, wgs_per_cu, (hipStream_t)stream);
 }
 
 // One-launch MoE down half with a forced lanes-per-row and wave count.

@@ -2,8 +2,9 @@
  * qmv.h — block-quantized weight mat-vec on AMD Instinct MI355X (gfx950).
  *
  * y = W x for weights stored as GGML-style 32-element blocks (Q4_0, Q8_0)
- * against fp32 activations, for 1 to 16 activation rows, plus the
- * expert-indexed variant over a stack of per-expert weight matrices.
+ * or 256-element super-blocks (Q6_K) against fp32 activations, for 1 to 16
+ * activation rows, plus the expert-indexed variant over a stack of
+ * per-expert weight matrices and the MoE steps around it.
  *
  * Source of the operations: the hf2q 0.1.1 pages.
  *  - Dense call: `dispatch_qmatmul(session, registry, device, x, &MlxQWeight,
@@ -77,6 +78,7 @@ extern "C" {
 /* Weight types (GGML type numbers). */
 #define QMV_Q4_0 2
 #define QMV_Q8_0 8
+#define QMV_Q6_K 14
 
 #define QMV_MAX_M 16
 
@@ -105,6 +107,31 @@ int qmv_q4_0(const void* W, size_t ldw_bytes, const float* X, size_t ldx, float*
  * qmv_q8_0 — as qmv_q4_0 with Q8_0 blocks (34 bytes): ldw_bytes >= K/32*34.
  */
 int qmv_q8_0(const void* W, size_t ldw_bytes, const float* X, size_t ldx, float* Y, size_t ldy,
+             int M, int N, int K, void* stream);
+
+/*
+ * qmv_q6_k — as qmv_q4_0 with Q6_K super-blocks: 256 weights in 210 bytes.
+ *
+ * The pages load the lm_head natively in this format (`lm_head_q6k` of
+ * `MlxModelWeights` in model.rs: gemma4's token_embd.weight as Q6_K
+ * [2816, 262144] = 605 MB, dispatched through `dispatch_qmatmul`). They name
+ * the format but do not lay it out; the layout taken is the GGML k-quant
+ * Q6_K super-block:
+ *   bytes   0..127  ql, low 4 bits of the 6-bit codes
+ *   bytes 128..191  qh, high 2 bits
+ *   bytes 192..207  16 int8 scales, scale j for weights 16j..16j+15
+ *   bytes 208..209  binary16 d
+ * Weight i: h = i/128, r = i%128, g = r/32, l = r%32; low bits = nibble g/2
+ * (0 = low) of ql[64h + 32(g%2) + l]; high bits = bits 2g, 2g+1 of
+ * qh[32h + l]; code q = low | high << 4; w = d * scale[i/16] * (q - 32).
+ *
+ *  K          a non-negative multiple of 256, at most 16384.
+ *  ldw_bytes  >= K/256 * 210, even; W 2-byte aligned (rows of an odd number
+ *             of super-blocks are 2-byte aligned, and are read as such).
+ *  Other arguments as qmv_q4_0 (M 0..16; activation rows are processed in
+ *  launches of up to 4, each reading the weights once).
+ */
+int qmv_q6_k(const void* W, size_t ldw_bytes, const float* X, size_t ldx, float* Y, size_t ldy,
              int M, int N, int K, void* stream);
 
 /*

@@ -26,8 +26,8 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert {"qmv_q4_0", "qmv_q8_0", "qmv_id", "qmv_id_swiglu", "qmv_moe_wsum", "qmv_moe_down", "qmv_batch",
-            "qmv_last_error"} <= set(names)
+    assert {"qmv_q4_0", "qmv_q8_0", "qmv_q6_k", "qmv_id", "qmv_id_swiglu", "qmv_moe_wsum", "qmv_moe_down",
+            "qmv_batch", "qmv_last_error"} <= set(names)
     L = ctypes.CDLL(qmv.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -208,3 +208,22 @@ def test_moe_empty_calls_are_no_ops():
     assert qmv.raw_qmv_moe_wsum(0, 0, 0, 0, 8, 16, 0, 0) == qmv.QMV_OK
     assert qmv.raw_qmv_moe_down(Q4, 0, 0, 0, 4, 0, 0, 0, 0, 0, 8, 0, 0, 16, 64) == qmv.QMV_OK
     assert qmv.raw_qmv_id_swiglu(Q4, 0, 0, 0, 4, 0, 0, 0, 0, 2, 0, 0, 16, 32) == qmv.QMV_OK
+
+
+Q6 = qmv.QMV_Q6_K
+
+
+@pytest.mark.parametrize("args,status,msg", [
+    ((Q6, W, 210, X, 256, Y, 16, 17, 16, 256), qmv.QMV_EUNSUPPORTED, "M=17"),
+    ((Q6, W, 210, X, 256, Y, 16, 1, 16, 128), qmv.QMV_EINVAL, "multiple of 256"),
+    ((Q6, W, 208, X, 256, Y, 16, 1, 16, 256), qmv.QMV_EINVAL, "ldw_bytes"),
+    ((Q6, W, 211, X, 256, Y, 16, 1, 16, 256), qmv.QMV_EALIGN, "2-byte"),
+    ((Q6, W + 1, 210, X, 256, Y, 16, 1, 16, 256), qmv.QMV_EALIGN, "2-byte"),
+    ((Q6, W, 210 * 64, X, 16384, Y, 16, 1, 16, 16640), qmv.QMV_EUNSUPPORTED, "exceeds"),
+    ((Q6, W, 210, X, 256, W + 8, 16, 1, 16, 256), qmv.QMV_EINVAL, "overlaps"),
+    ((Q6, W, 210, X, 255, Y, 16, 2, 16, 256), qmv.QMV_EINVAL, "ldx"),
+])
+def test_q6k_argument_checks(args, status, msg):
+    q, *rest = args
+    assert qmv.raw_qmv(q, *rest) == status
+    assert msg in qmv.last_error()

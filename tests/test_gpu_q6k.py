@@ -1,0 +1,106 @@
+"""GPU parity of qmv_q6_k (Q6_K super-blocks) against the CPU oracle.
+
+Shapes cover every lanes-per-row choice (K/128 units per row: 2, 4, 22, 32,
+128), rows of an odd number of super-blocks (2-byte aligned rows), padded
+row strides, ragged N, M = 1..16 (launches of up to 4 rows), the lm_head
+shape [262144, 2816] on sampled rows, and one-hot activations, where the
+result is a single rounding of the exact weight.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from block_quantized_weight_qmatmul_amd import qmv, synth
+from helpers import assert_within_tol
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def run(W, X, N, K, ldy=None):
+    M = X.shape[0]
+    Yfull = torch.full((M, ldy or N), np.nan, dtype=torch.float32, device=DEV)
+    Y = Yfull[:, :N]
+    Wd = torch.from_numpy(np.ascontiguousarray(W)).to(DEV)
+    Xd = torch.from_numpy(np.ascontiguousarray(X)).to(DEV)
+    qmv.qmv_q6_k(Wd, Xd if M > 1 else Xd[0], Y if M > 1 else Y[0], K=K)
+    torch.cuda.synchronize()
+    return Y.cpu().numpy(), Yfull.cpu().numpy()
+
+
+@pytest.mark.parametrize("N,K", [(300, 2816), (1000, 256), (77, 512), (2050, 4096), (64, 16384), (1, 2816)])
+def test_q6k_m1_against_oracle(N, K):
+    W = synth.make_weights("q6_k", N, K, cfg=60, part=K)
+    X = synth.make_x(1, K, cfg=60, part=K)
+    y, _ = run(W, X, N, K)
+    yo, a = oracle.qmv("q6_k", W, X)
+    print("ratio", assert_within_tol(y, yo, a, f"N={N} K={K}"))
+
+
+@pytest.mark.parametrize("M", [2, 3, 4, 5, 16])
+def test_q6k_multi_row(M):
+    N, K = 700, 2816
+    W = synth.make_weights("q6_k", N, K, cfg=61, part=M)
+    X = synth.make_x(M, K, cfg=61, part=M)
+    y, full = run(W, X, N, K, ldy=N + 3)
+    yo, a = oracle.qmv("q6_k", W, X)
+    assert_within_tol(y, yo, a, f"M={M}")
+    assert np.all(np.isnan(full[:, N:]))
+
+
+def test_q6k_padded_rows_and_wide_scale_range():
+    N, K = 333, 1280
+    ldw = synth.row_bytes("q6_k", K) + 6
+    W = synth.make_weights("q6_k", N, K, cfg=62, ldw=ldw, d_range=(1e-3, 3.0))
+    X = synth.make_x(1, K, cfg=62)
+    y, _ = run(W, X, N, K)
+    yo, a = oracle.qmv("q6_k", W[:, :ldw], X)
+    assert_within_tol(y, yo, a, "padded")
+
+
+def test_q6k_one_hot_is_one_rounding_of_the_weight():
+    N, K = 96, 2816
+    W = synth.make_weights("q6_k", N, K, cfg=63)
+    ks = [0, 1, 15, 16, 127, 128, 255, 256, 1000, 2815]
+    X = np.zeros((len(ks), K), np.float32)
+    for i, k in enumerate(ks):
+        X[i, k] = 1.0
+    y, _ = run(W, X, N, K)
+    for i, k in enumerate(ks):
+        want = np.array([oracle.dequant_row("q6_k", W[n], K)[k] for n in range(N)]).astype(np.float32)
+        assert np.array_equal(y[i], want), k
+
+
+def test_q6k_lm_head_shape_sampled_rows():
+    """The pages' lm_head: Q6_K [2816 -> 262144], one token."""
+    N, K = 262144, 2816
+    W = synth.make_weights("q6_k", N, K, cfg=5)
+    X = synth.make_x(1, K, cfg=5)
+    y, _ = run(W, X, N, K)
+    rows = np.unique(np.r_[0, 1, N - 1, np.random.default_rng(5).integers(0, N, 400)])
+    yo, a = oracle.qmv("q6_k", W[rows], X)
+    print("ratio", assert_within_tol(y[:, rows], yo, a, "lm_head"))
+    assert np.isfinite(y).all()
+
+
+def test_q6k_k0_zero_and_m0_noop():
+    Y = torch.full((2, 8), 5.0, device=DEV)
+    W = torch.zeros((8, 2), dtype=torch.uint8, device=DEV)
+    qmv.qmv_q6_k(W, torch.zeros((2, 0), device=DEV), Y, K=0)
+    torch.cuda.synchronize()
+    assert torch.all(Y == 0.0)
+    Y.fill_(5.0)
+    qmv.qmv_q6_k(W, torch.zeros((0, 256), device=DEV), Y[:0], K=256)
+    torch.cuda.synchronize()
+    assert torch.all(Y == 5.0)
+
+
+def test_q6k_deterministic():
+    N, K = 4096, 2816
+    W = synth.make_weights("q6_k", N, K, cfg=64)
+    X = synth.make_x(1, K, cfg=64)
+    y1, _ = run(W, X, N, K)
+    y2, _ = run(W, X, N, K)
+    assert np.array_equal(y1, y2)
