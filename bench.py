@@ -336,9 +336,38 @@ def summarize(stats_dir, fetch_dir, write_dir, cmd_note):
     print(text)
 
 
+def summarize_trace(trace_csv, out_name, title, kernels, cmd_note):
+    """Per-kernel median durations from a rocprofv3 kernel-trace CSV for the
+    kernels whose names contain one of `kernels` (comma-separated), grouped
+    by launch shape, written to profiles/<out_name>."""
+    import csv
+    import statistics
+    if os.path.basename(out_name) != out_name:
+        raise ValueError("out_name must be a file name inside profiles/")
+    groups = {}
+    for r in csv.DictReader(open(trace_csv)):
+        name = r["Kernel_Name"].replace("void (anonymous namespace)::", "").replace("(anonymous namespace)::", "")
+        short = name.split("(")[0]
+        if not any(k in short for k in kernels.split(",")):
+            continue
+        key = (short, int(r["Grid_Size_X"]), int(r["Grid_Size_Y"]), int(r["Workgroup_Size_X"]))
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = [f"# {title}", f"# command: {cmd_note}", "# per-kernel durations from the kernel trace (median over calls)",
+             f"#   {'kernel':34s} {'grid_x(threads)':>15s} {'grid_y':>6s} {'wg':>4s} {'calls':>6s} {'median_us':>10s}"]
+    for (k, gx, gy, wg), v in sorted(groups.items()):
+        lines.append(f"  {k:34s} {gx:15d} {gy:6d} {wg:4d} {len(v):6d} {statistics.median(v):10.2f}")
+    text = "\n".join(lines) + "\n"
+    with open(os.path.join(ROOT, "profiles", out_name), "w") as f:
+        f.write(text)
+    print(text)
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize":
         summarize(sys.argv[2], sys.argv[3], sys.argv[4], " ".join(sys.argv[5:]))
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-trace":
+        summarize_trace(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], " ".join(sys.argv[6:]))
         return
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)

@@ -72,7 +72,7 @@ extern "C" {
 #define QMV_OK 0
 #define QMV_EINVAL (-1)       /* bad shape, stride, pointer or overlap */
 #define QMV_EALIGN (-2)       /* misaligned pointer or stride */
-#define QMV_EUNSUPPORTED (-3) /* unsupported qtype, or M outside 0..16 */
+#define QMV_EUNSUPPORTED (-3) /* unsupported qtype or shape (M outside 0..16, limits stated per call) */
 #define QMV_EHIP (-4)         /* the HIP runtime reported a launch error */
 
 /* Weight types (GGML type numbers). */
