@@ -13,9 +13,9 @@ The weights of R distinct copies of the layer set are resident in HBM
 (10 copies = 1.23 GB, several times the 256 MB Infinity Cache) and steps
 rotate through them, so every step streams its weights from HBM.
 
-Each step is captured once per copy as a HIP graph (four kernel nodes) and
-the timed region replays the graphs back to back, so the figure is the GPU's
-time, not the host's launch rate.
+Consecutive steps (one per copy, in turn) are captured together into one
+HIP graph of 10 steps (40 kernel nodes) and the timed region replays it, so
+the figure is the GPU's time, not the host's launch or replay rate.
 
 Output: one JSON line with the effective weight bandwidth (algorithmic
 weight bytes / wall time per step), the roofline of the qmv kernel (its
@@ -79,39 +79,44 @@ def step_bytes():
     return sum(p.weight_bytes for p in synth.CONFIGS[1]["problems"])
 
 
-def capture_steps(fn, sets):
-    """One HIP graph per copy of the layer set, each holding one step."""
+def time_steps(fn, sets, steps, warmup):
+    """Wall time (s) of exactly `steps` steps after at least `warmup` untimed
+    ones, bracketed by synchronizations and HIP events. Step i runs on
+    sets[i % len(sets)]. Consecutive steps are captured together into HIP
+    graphs of at least 8 steps, so each replay keeps the GPU busy long enough
+    that the host's replay cost stays out of the timed region (one small graph
+    per step measures the host, not the kernels)."""
     import torch
+    R = len(sets)
+    chunk = R * ((8 + R - 1) // R)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
         for s in sets:  # eager pass first: library set-up stays out of the graphs
             fn(s)
     torch.cuda.synchronize()
-    graphs = []
-    for s in sets:
+
+    def build(n):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=side):
-            fn(s)
-        graphs.append(g)
+            for i in range(n):
+                fn(sets[i % R])
+        return g
+    full = build(chunk)
+    part = build(steps % chunk) if steps % chunk else None
     torch.cuda.synchronize()
-    return graphs
-
-
-def time_graphs(graphs, steps, warmup):
-    """Wall time (s) of `steps` graph replays after `warmup` untimed ones,
-    bracketed by synchronizations and HIP events."""
-    import torch
-    R = len(graphs)
-    for i in range(warmup):
-        graphs[i % R].replay()
+    for _ in range((warmup + chunk - 1) // chunk):
+        full.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for i in range(steps):
-        graphs[i % R].replay()
+    for _ in range(steps // chunk):
+        full.replay()
+    if part is not None:
+        part.replay()
     e1.record()
     torch.cuda.synchronize()
+    del full, part
     return e0.elapsed_time(e1) / 1e3
 
 
@@ -160,9 +165,9 @@ def m16_throughput(dev, steps=40):
 
 def moe_throughput(dev, T, steps=40, mode="id"):
     """Config 4 (Q4_0 MoE, 128 experts, top-8, hidden 2816, expert
-    intermediate 704) for T tokens, graph replays over rotated stacks (16 for
-    T = 1, 4 for T = 32). GB/s counts the weights of the distinct selected
-    experts (each streamed once per call).
+    intermediate 704) for T tokens over rotated stacks (16 for T = 1, 4 for
+    T = 32), several steps per graph replay. GB/s counts the weights of the
+    distinct selected experts (the bytes a call must read at least).
 
     mode "id": the gate_up and down id calls alone (down fed a synthetic x).
     mode "ffn_fused": the MoE FFN of the tokens: gate_up id, then the
@@ -201,9 +206,7 @@ def moe_throughput(dev, T, steps=40, mode="id"):
             qmv.qmv_id_swiglu("q4_0", dd["W_down"], dd["Y_gu"], dd["ids"].view(-1, 1), dd["Y_dn"], dn.N, dn.K,
                               expert_scale=dd["expert_scale"])
             qmv.qmv_moe_wsum(dd["Y_dn"], dd["weights"], dd["out"], gu.top_k)
-    graphs = capture_steps(step, sets)
-    t = time_graphs(graphs, steps, 4) / steps
-    del graphs
+    t = time_steps(step, sets, steps, 4) / steps
     launches = {"id": 2, "ffn_fused": 2, "ffn_two_call": 3}[mode]
     return {"workload": f"q4_0_moe_e128_top8_h2816_i704_t{T}", "mode": mode, "launches": launches,
             "weight_bytes_per_step": round(nbytes), "us_per_step": round(t * 1e6, 2),
@@ -212,7 +215,7 @@ def moe_throughput(dev, T, steps=40, mode="id"):
 
 def lm_head_q6k_throughput(dev, steps=20):
     """The pages' lm_head as Q6_K: [2816 -> 262144] (605.6 MB), one token
-    (M = 1), graph replays of one copy (it is larger than the chip's last-level
+    (M = 1), replays of a graph of 8 calls on one copy (it is larger than the chip's last-level
     cache, so every replay streams it from HBM)."""
     import torch
 
@@ -222,11 +225,34 @@ def lm_head_q6k_throughput(dev, steps=20):
     X = torch.from_numpy(synth.make_x(1, K, cfg=5)[0]).to(dev)
     Y = torch.empty(N, device=dev)
     nbytes = N * synth.row_bytes("q6_k", K)
-    graphs = capture_steps(lambda s: qmv.qmv_q6_k(s[0], s[1], s[2]), [(W, X, Y)])
-    t = time_graphs(graphs, steps, 3) / steps
-    del graphs, W
+    t = time_steps(lambda s: qmv.qmv_q6_k(s[0], s[1], s[2]), [(W, X, Y)], steps, 3) / steps
+    del W
     return {"workload": "q6_k_m1_lm_head_2816x262144", "weight_bytes": nbytes, "us_per_call": round(t * 1e6, 2),
             "GBps": round(nbytes / t / 1e9, 1), "pct_hbm_peak": round(100 * nbytes / t / 1e9 / HBM_PEAK_GBS, 2)}
+
+
+def moe_q6k_gate_up_throughput(dev, steps=40):
+    """The gate_up id call of one token over Q6_K experts (the pages' production
+    MoE stores gate_up experts as Q6_K): 128 experts [1408, 2816], top-8. One
+    stack (416 MB, larger than the last-level cache) and 16 routing sets
+    replayed in turn; GB/s counts the 8 selected experts' bytes."""
+    import numpy as np
+    import torch
+
+    from block_quantized_weight_qmatmul_amd import qmv, synth
+    E, N, K, k = 128, 1408, 2816, 8
+    W = torch.from_numpy(synth.make_weights("q6_k", E * N, K, cfg=4, part=7).reshape(E, N, -1)).to(dev)
+    X = torch.from_numpy(synth.make_x(1, K, cfg=4, part=7)).to(dev)
+    sets = []
+    for r in range(16):
+        ids = torch.from_numpy(synth.router_topk(1, E, k, cfg=4, copy=r, part=7).astype(np.int32)).to(dev)
+        sets.append((ids, torch.empty(k, N, device=dev)))
+    nbytes = k * N * synth.row_bytes("q6_k", K)
+    t = time_steps(lambda s: qmv.qmv_id("q6_k", W, X, s[0], s[1], N, K), sets, steps, 4) / steps
+    del W
+    return {"workload": "q6_k_moe_gate_up_e128_top8_h2816_n1408_t1", "weight_bytes_per_call": nbytes,
+            "us_per_call": round(t * 1e6, 2), "GBps": round(nbytes / t / 1e9, 1),
+            "pct_hbm_peak": round(100 * nbytes / t / 1e9 / HBM_PEAK_GBS, 2)}
 
 
 def cpu_baseline(target_s: float):
@@ -400,8 +426,7 @@ def main():
         for g in GROUPS:
             qmv.qmv_batch("q4_0", [s[n] for n in g])
 
-    graphs = capture_steps(grouped, sets)
-    t = time_graphs(graphs, args.steps, args.warmup)
+    t = time_steps(grouped, sets, args.steps, args.warmup)
     ms_per_step = t / args.steps * 1e3
     value = nbytes * args.steps / t / 1e9
 
@@ -418,7 +443,6 @@ def main():
                 "kernel": "k_m1b (qmv_batch, M=1)", "launches_per_step": len(GROUPS),
                 "avg_launch_us": round(avg_launch * 1e6, 3),
                 "algorithmic_bytes_per_launch": round(per_launch)}
-    del graphs
 
     if args.probe_copy_mb:
         src = torch.empty(args.probe_copy_mb * 2**20 // 4, dtype=torch.float32, device=dev).uniform_()
@@ -431,11 +455,9 @@ def main():
     extra = {}
     if not args.no_extra:
         names = ("q", "k", "v", "o", "gate", "up", "down")
-        g1 = capture_steps(lambda s: qmv.qmv_batch("q4_0", [s[n] for n in names]), sets)
-        t1 = time_graphs(g1, args.steps, args.warmup)
-        g7 = capture_steps(lambda s: [qmv.qmv_q4_0(s[n][0], s[n][1], s[n][2]) for n in names], sets)
-        t7 = time_graphs(g7, args.steps, args.warmup)
-        del g1, g7
+        t1 = time_steps(lambda s: qmv.qmv_batch("q4_0", [s[n] for n in names]), sets, args.steps, args.warmup)
+        t7 = time_steps(lambda s: [qmv.qmv_q4_0(s[n][0], s[n][1], s[n][2]) for n in names], sets, args.steps,
+                        args.warmup)
         extra["layer_set_one_launch_GBps"] = round(nbytes * args.steps / t1 / 1e9, 1)
         extra["layer_set_seven_launches_GBps"] = round(nbytes * args.steps / t7 / 1e9, 1)
         extra["m16"] = m16_throughput(dev)
@@ -446,6 +468,7 @@ def main():
         extra["moe_ffn_t32_two_call"] = moe_throughput(dev, 32, mode="ffn_two_call")
         extra["moe_ffn_t32_fused"] = moe_throughput(dev, 32, mode="ffn_fused")
         extra["lm_head_q6_k"] = lm_head_q6k_throughput(dev)
+        extra["moe_q6_k_gate_up_t1"] = moe_q6k_gate_up_throughput(dev)
     del sets
     torch.cuda.empty_cache()
 

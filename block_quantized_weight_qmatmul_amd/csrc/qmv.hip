@@ -1899,6 +1899,66 @@ __global__ __launch_bounds__(WAVES * 64) void k_q6k(const uint8_t* __restrict__ 
     }
 }
 
+// Expert-indexed Q6_K product: one workgroup per (tile of ROWS rows, pair
+// p); expert ids[p]'s rows against activation row p / top_k. Pairs are not
+// grouped by expert (each reads its expert's rows): the form for decode,
+// where a token's experts are distinct. An id outside [0, n_experts) gives
+// NaN rows and sets *err_flag.
+template <int LPR, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void k_id_q6(const uint8_t* __restrict__ W, size_t estride, size_t ldw,
+                                                      int n_experts, const float* __restrict__ X, size_t ldx,
+                                                      const uint32_t* __restrict__ ids, int top_k,
+                                                      float* __restrict__ Y, size_t ldy, int N, int K,
+                                                      const float* __restrict__ escale, int* __restrict__ err_flag) {
+    constexpr int GROUPS = 64 / LPR;
+    constexpr int ROWS = GROUPS * WAVES;
+    constexpr int NT = WAVES * 64;
+    constexpr int GCH = (KMAX_Q6 / 16 + NT - 1) / NT;
+    extern __shared__ __align__(16) float xs[];
+    const int p = blockIdx.y;
+    const uint32_t e = ids[p];
+    const long row0 = (long)blockIdx.x * ROWS;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane / LPR, j = lane % LPR;
+    const int U = K >> 7;
+    const int IPT = (U + LPR - 1) / LPR;
+    if (e >= (uint32_t)n_experts) {  // uniform over the workgroup
+        for (long n = row0 + tid; n < row0 + ROWS && n < N; n += NT) Y[(size_t)p * ldy + n] = __builtin_nanf("");
+        if (tid == 0 && err_flag) *err_flag = 1;
+        return;
+    }
+    const uint8_t* We = W + (size_t)e * estride;
+    const long row = row0 + wave * GROUPS + g;
+    const long rowc = row < N ? row : N - 1;
+    float* gs = xs + (size_t)U * XS_Q6;
+    uint32_t nxt[Q6_UNIT_DW];
+    auto issue = [&](int i) {
+        int u = j + i * LPR;
+        u = u < U ? u : U - 1;
+        load_q6_unit(We + (size_t)rowc * ldw + (size_t)(u >> 1) * Q6_SB_BYTES, u & 1, nxt);
+    };
+    {
+        // x loads first, then the first weight loads (see m1_stream)
+        const size_t xo = (size_t)(p / top_k) * ldx;
+        Q6Stage<NT, GCH, 1> stg;
+        stg.load(X, &xo, 1, K);
+        issue(0);
+        stg.store(xs, 0, gs, 0, 1, K);
+    }
+    lds_barrier();
+    float tot = 0.f;
+    for (int it = 0; it < IPT; ++it) {
+        uint32_t cur[Q6_UNIT_DW];
+#pragma unroll
+        for (int d = 0; d < Q6_UNIT_DW; ++d) cur[d] = nxt[d];
+        if (it + 1 < IPT) issue(it + 1);
+        const int u = j + it * LPR;
+        if (u < U) q6_unit_dot<1>(cur, xs + (size_t)u * XS_Q6, 0, gs + 8 * u, 0, 1, &tot);
+    }
+    const float sum = lane_group_sum<LPR>(tot) * (escale ? escale[e] : 1.f);
+    if (j == LPR - 1 && row < N) Y[(size_t)p * ldy + row] = sum;
+}
+
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
@@ -2335,6 +2395,10 @@ int launch_id(const uint8_t* W, size_t es, size_t ldw, int E, const float* X, si
     return fail(QMV_EINVAL, "internal: no id kernel for lpr=%d", lpr);
 }
 
+int launch_id_q6(const uint8_t* W, size_t es, size_t ldw, int E, const float* X, size_t ldx, const uint32_t* ids,
+                 int n_pairs, int top_k, float* Y, size_t ldy, int N, int K, const float* sc, int* err,
+                 hipStream_t st);
+
 // Shared by qmv_id (SW = false: X rows hold K values) and qmv_id_swiglu
 // (SW = true: X rows hold 2K values, gate then up). `fn` names the entry point
 // in error messages.
@@ -2342,19 +2406,23 @@ template <bool SW>
 int id_common(const char* fn, int qtype, const void* Wv, size_t expert_stride_bytes, size_t ldw_bytes, int n_experts,
               const float* X, size_t ldx, const uint32_t* ids, int n_tokens, int top_k, float* Y, size_t ldy, int N,
               int K, const float* expert_scale, int* err_flag, void* stream) {
-    if (qtype != QMV_Q4_0 && qtype != QMV_Q8_0) return fail(QMV_EUNSUPPORTED, "%s: qtype %d not supported", fn, qtype);
-    const int bb = block_bytes(qtype);
+    const bool q6 = qtype == QMV_Q6_K;
+    if (qtype != QMV_Q4_0 && qtype != QMV_Q8_0 && !(q6 && !SW))
+        return fail(QMV_EUNSUPPORTED, "%s: qtype %d not supported", fn, qtype);
+    const int bb = q6 ? Q6_SB_BYTES : block_bytes(qtype);
+    const int qk = q6 ? 256 : QK;
     if (n_experts <= 0) return fail(QMV_EINVAL, "%s: n_experts=%d must be > 0", fn, n_experts);
     if (top_k <= 0) return fail(QMV_EINVAL, "%s: top_k=%d must be > 0", fn, top_k);
     if (n_tokens < 0) return fail(QMV_EINVAL, "%s: n_tokens=%d < 0", fn, n_tokens);
     if (N < 0) return fail(QMV_EINVAL, "%s: N=%d < 0", fn, N);
-    if (K < 0 || K % QK) return fail(QMV_EINVAL, "%s: K=%d is not a non-negative multiple of 32", fn, K);
+    if (K < 0 || K % qk) return fail(QMV_EINVAL, "%s: K=%d is not a non-negative multiple of %d", fn, K, qk);
+    if (q6 && K > KMAX_Q6) return fail(QMV_EUNSUPPORTED, "%s: K=%d exceeds %d for Q6_K", fn, K, KMAX_Q6);
     if (top_k > ID_MAX_LIST) return fail(QMV_EUNSUPPORTED, "%s: top_k=%d exceeds %d", fn, top_k, ID_MAX_LIST);
     if ((long)n_tokens * top_k > 0x7FFFFFFFL) return fail(QMV_EINVAL, "%s: n_tokens*top_k overflows", fn);
     if (n_tokens == 0 || N == 0) return QMV_OK;
     if (!Wv || !X || !ids || !Y) return fail(QMV_EINVAL, "%s: NULL W, X, ids or Y", fn);
-    const size_t row = (size_t)(K / QK) * bb;
-    if (ldw_bytes < row) return fail(QMV_EINVAL, "%s: ldw_bytes=%zu < K/32*%d=%zu", fn, ldw_bytes, bb, row);
+    const size_t row = (size_t)(K / qk) * bb;
+    if (ldw_bytes < row) return fail(QMV_EINVAL, "%s: ldw_bytes=%zu < K/%d*%d=%zu", fn, ldw_bytes, qk, bb, row);
     if ((size_t)N > SIZE_MAX / (ldw_bytes ? ldw_bytes : 1)) return fail(QMV_EINVAL, "%s: N*ldw overflows", fn);
     if (expert_stride_bytes < (size_t)N * ldw_bytes)
         return fail(QMV_EINVAL, "%s: expert_stride_bytes=%zu < N*ldw_bytes=%zu", fn, expert_stride_bytes,
@@ -2379,6 +2447,10 @@ int id_common(const char* fn, int qtype, const void* Wv, size_t expert_stride_by
 
     hipStream_t st = (hipStream_t)stream;
     const uint8_t* W = (const uint8_t*)Wv;
+    if (q6 && K > 0)
+        return launch_id_q6(W, expert_stride_bytes, ldw_bytes, n_experts, X, ldx, ids, n_tokens * top_k, top_k, Y,
+                            ldy, N, K, expert_scale, err_flag, st);
+    // (K = 0 of any type: the generic kernel reads no weights and writes zeros)
     const int fast = K > 0 && K % 64 == 0 && K <= KMAX_FAST_ID && ((uintptr_t)W & 3) == 0 && (ldw_bytes & 3) == 0 &&
                      (expert_stride_bytes & 3) == 0;
     // Up to 64 pairs (decode and short batches): stream all pairs' rows as
@@ -2476,6 +2548,38 @@ int launch_q6k_t(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float
     hipLaunchKernelGGL((k_q6k<LPR, WAVES, MX>), dim3((unsigned)nwg), dim3(WAVES * 64), lds, st, W, ldw, X, ldx, Y, ldy,
                        nx, N, K);
     return check_launch("qmv_q6_k kernel");
+}
+
+template <int LPR>
+int launch_id_q6_t(const uint8_t* W, size_t es, size_t ldw, int E, const float* X, size_t ldx, const uint32_t* ids,
+                   int n_pairs, int top_k, float* Y, size_t ldy, int N, int K, const float* sc, int* err,
+                   hipStream_t st) {
+    constexpr int WAVES = 4;
+    constexpr int ROWS = (64 / LPR) * WAVES;
+    const long tiles = ((long)N + ROWS - 1) / ROWS;
+    if (tiles > 0x7FFFFFFF) return fail(QMV_EINVAL, "qmv_id: N too large");
+    // grid.y holds at most 65535 pairs: launches over whole tokens
+    const int per = (65535 / top_k) * top_k;
+    for (int p0 = 0; p0 < n_pairs; p0 += per) {
+        const int np = n_pairs - p0 < per ? n_pairs - p0 : per;
+        hipLaunchKernelGGL((k_id_q6<LPR, WAVES>), dim3((unsigned)tiles, (unsigned)np), dim3(WAVES * 64),
+                           q6_xs_bytes(K), st, W, es, ldw, E, X + (size_t)(p0 / top_k) * ldx, ldx, ids + p0, top_k,
+                           Y + (size_t)p0 * ldy, ldy, N, K, sc, err);
+        const int rc = check_launch("qmv_id Q6_K kernel");
+        if (rc) return rc;
+    }
+    return QMV_OK;
+}
+
+int launch_id_q6(const uint8_t* W, size_t es, size_t ldw, int E, const float* X, size_t ldx, const uint32_t* ids,
+                 int n_pairs, int top_k, float* Y, size_t ldy, int N, int K, const float* sc, int* err,
+                 hipStream_t st) {
+    const int lpr = pick_lpr_q6(K / 128);
+#define QMV_IDQ6_CASE(L) \
+    if (lpr == L) return launch_id_q6_t<L>(W, es, ldw, E, X, ldx, ids, n_pairs, top_k, Y, ldy, N, K, sc, err, st);
+    QMV_IDQ6_CASE(64) QMV_IDQ6_CASE(32) QMV_IDQ6_CASE(16) QMV_IDQ6_CASE(8) QMV_IDQ6_CASE(4)
+#undef QMV_IDQ6_CASE
+    return fail(QMV_EINVAL, "internal: no Q6_K id kernel for lpr=%d", lpr);
 }
 
 // Rows of X in launches of up to 4 (one launch when M = 1).

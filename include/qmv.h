@@ -147,7 +147,10 @@ int qmv_q6_k(const void* W, size_t ldw_bytes, const float* X, size_t ldx, float*
  * per token; the down form flattens the slots: (n_tokens = T*k, top_k = 1)
  * with one X row per slot.
  *
- *  qtype                QMV_Q4_0 or QMV_Q8_0.
+ *  qtype                QMV_Q4_0, QMV_Q8_0 or QMV_Q6_K (the pages' production MoE
+ *                       stores the gate_up experts as Q6_K; K a multiple of 256,
+ *                       at most 16384; each (token, slot) pair reads its expert's
+ *                       rows, with no grouping of pairs by expert).
  *  W                    device, stacked weights, 2-byte aligned.
  *  expert_stride_bytes  >= N * ldw_bytes, even.
  *  ldw_bytes            row stride within an expert, >= K/32 * block bytes, even.
@@ -163,8 +166,11 @@ int qmv_q6_k(const void* W, size_t ldw_bytes, const float* X, size_t ldx, float*
  *                       input: its output row is filled with NaN and, when
  *                       err_flag is given, 1 is stored to *err_flag (the
  *                       library never clears it; the caller zeroes it).
- * Each selected expert's weights are read from memory once per call, however
- * many (token, slot) pairs select it.
+ * Reads (Q4_0, Q8_0): with more than 64 (token, slot) pairs, each selected
+ * expert's weights are read from memory once per call, however many pairs
+ * select it; with up to 64 pairs (decode-sized calls) every pair reads its
+ * expert's rows, which is faster at that size although an expert selected by
+ * several pairs is then read once per pair.
  * Returns QMV_OK or a negative status.
  */
 int qmv_id(int qtype, const void* W, size_t expert_stride_bytes, size_t ldw_bytes, int n_experts,
@@ -182,6 +188,7 @@ int qmv_id(int qtype, const void* W, size_t expert_stride_bytes, size_t ldw_byte
  * halves; gate first follows the buffer name `gate_up`).
  *
  *  G, ldg   device fp32 [n_tokens, 2K], row stride ldg >= 2K, 4-byte aligned.
+ *  qtype    QMV_Q4_0 or QMV_Q8_0 (QMV_Q6_K returns QMV_EUNSUPPORTED).
  *  Every other argument, the result layout, NaN rows for bad ids and the
  *  error behaviour are those of qmv_id. For the pages' down form pass the
  *  gate_up output rows with (n_tokens = T*k, top_k = 1).

@@ -95,6 +95,9 @@ def _id(**kw):
     (dict(err=0x50000001), qmv.QMV_EALIGN, "4-byte"),
     (dict(Y=W + 18 * 20), qmv.QMV_EINVAL, "overlaps"),
     (dict(Y=0x40000000 - 4), qmv.QMV_EINVAL, "overlaps"),
+    (dict(qtype=qmv.QMV_Q6_K), qmv.QMV_EINVAL, "multiple of 256"),
+    (dict(qtype=qmv.QMV_Q6_K, K=256, ldw=208, es=210 * 16, ldx=256), qmv.QMV_EINVAL, "ldw_bytes"),
+    (dict(qtype=qmv.QMV_Q6_K, K=16640, ldw=210 * 65, es=210 * 65 * 16, ldx=16640), qmv.QMV_EUNSUPPORTED, "Q6_K"),
 ])
 def test_id_argument_checks(kw, status, msg):
     assert _id(**kw) == status
@@ -150,6 +153,7 @@ def _sw(**kw):
     (dict(G=X + 2), qmv.QMV_EALIGN, "4-byte"),
     (dict(Y=X + 4 * 60), qmv.QMV_EINVAL, "overlaps"),  # Y inside G's second half
     (dict(K=48), qmv.QMV_EINVAL, "K=48"),
+    (dict(qtype=qmv.QMV_Q6_K, K=256, ldw=210, es=210 * 16, ldg=512), qmv.QMV_EUNSUPPORTED, "qtype 14"),
 ])
 def test_id_swiglu_argument_checks(kw, status, msg):
     assert _sw(**kw) == status

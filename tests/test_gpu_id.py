@@ -175,3 +175,37 @@ def test_deterministic_bitwise():
     y1, _, _ = run_id("q4_0", inp["W_gate_up"], inp["X_gate_up"], inp["ids"], call.N, call.K)
     y2, _, _ = run_id("q4_0", inp["W_gate_up"], inp["X_gate_up"], inp["ids"], call.N, call.K)
     assert np.array_equal(y1, y2)
+
+
+# --------------------------------------------------------------------------
+# Q6_K experts (the pages' production MoE keeps gate_up experts as Q6_K).
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("K,N", [(2816, 1408), (512, 300), (256, 77)])
+def test_q6k_stack_against_oracle(K, N):
+    E, T = 12, 5
+    W = synth.make_weights("q6_k", E * N, K, cfg=83, part=K).reshape(E, N, -1)
+    X = synth.make_x(T, K, cfg=83, part=K)
+    ids = np.array([[0, 11, 2], [2, 2, 1], [4, 0, 3], [5, 5, 5], [11, 3, 0]], dtype=np.uint32)
+    sc = synth.expert_scale(E, cfg=83)
+    y, _, _ = run_id("q6_k", W, X, ids, N, K, escale=sc)
+    yo, a = oracle.qmv_id("q6_k", W, X, ids, N, K, sc)
+    assert_within_tol(y, yo, a, f"q6_k K={K}")
+
+
+def test_q6k_moe_gate_up_t1_and_bad_id():
+    """The gate_up call of one token, 128 Q6_K experts [1408, 2816], top-8;
+    then an out-of-range id gives a NaN row and sets the flag."""
+    E, N, K = 128, 1408, 2816
+    W = synth.make_weights("q6_k", E * N, K, cfg=84).reshape(E, N, -1)
+    X = synth.make_x(1, K, cfg=84)
+    ids = synth.router_topk(1, E, 8, cfg=84)
+    sc = synth.expert_scale(E, cfg=84)
+    y, _, _ = run_id("q6_k", W, X, ids, N, K, escale=sc)
+    yo, a = oracle.qmv_id("q6_k", W, X, ids, N, K, sc)
+    print("ratio", assert_within_tol(y, yo, a, "q6_k gate_up T=1"))
+    bad = ids.copy()
+    bad[0, 3] = 128
+    y2, flag, _ = run_id("q6_k", W, X, bad, N, K, escale=sc, err=True)
+    assert flag == 1 and np.all(np.isnan(y2[3]))
+    keep = [0, 1, 2, 4, 5, 6, 7]
+    assert np.array_equal(y2[keep], y[keep])
