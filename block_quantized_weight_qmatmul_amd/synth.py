@@ -38,9 +38,9 @@ ROOT_SEED = 20261202
 T_SCALE, T_CODES, T_X, T_LOGITS, T_ESCALE, T_GATE_UP, T_RWEIGHT = 0, 1, 2, 3, 4, 5, 6
 
 QK = 32  # weights per block
-BLOCK_BYTES = {"q4_0": 18, "q8_0": 34, "q6_k": 210}
-BLOCK_ELEMS = {"q4_0": 32, "q8_0": 32, "q6_k": 256}
-QTYPE_ID = {"q4_0": 2, "q8_0": 8, "q6_k": 14}  # GGML type numbers
+BLOCK_BYTES = {"q4_0": 18, "q8_0": 34, "q5_k": 176, "q6_k": 210}
+BLOCK_ELEMS = {"q4_0": 32, "q8_0": 32, "q5_k": 256, "q6_k": 256}
+QTYPE_ID = {"q4_0": 2, "q8_0": 8, "q5_k": 13, "q6_k": 14}  # GGML type numbers
 
 # Scale ranges and code ranges the workloads draw from.
 Q4_0_D_RANGE = (0.001, 0.02)
@@ -73,6 +73,8 @@ def make_weights(qtype: str, N: int, K: int, cfg: int, copy: int = 0, part: int 
     """
     if qtype == "q6_k":
         return _make_q6_k(N, K, cfg, copy, part, d_range, ldw)
+    if qtype == "q5_k":
+        return _make_q5_k(N, K, cfg, copy, part, ldw)
     bb = BLOCK_BYTES[qtype]
     nb = K // QK
     dense = row_bytes(qtype, K)
@@ -115,6 +117,32 @@ def _make_q6_k(N, K, cfg, copy, part, d_range, ldw):
     blocks[..., 0:192] = rc.integers(0, 256, size=(N, nb, 192), dtype=np.uint8)
     blocks[..., 192:208] = rc.integers(-128, 128, size=(N, nb, 16)).astype(np.int8).view(np.uint8)
     blocks[..., 208:210] = _scales_f16_bytes(rng(cfg, copy, T_SCALE, part), (N, nb), *d_range)
+    if ldw == dense:
+        return blocks.reshape(N, dense)
+    out = np.full((N, ldw), 0xA5, dtype=np.uint8)
+    out[:, :dense] = blocks.reshape(N, dense)
+    return out
+
+
+Q5_K_D_RANGE = (2e-5, 8e-5)
+Q5_K_DMIN_RANGE = (2e-4, 1e-3)
+
+
+def _make_q5_k(N, K, cfg, copy, part, ldw):
+    """Q5_K rows: per 256-weight super-block, binary16 d ~ U[2e-5, 8e-5] and
+    dmin ~ U[2e-4, 1e-3], and the 172 other bytes (packed 6-bit scales and
+    minimums, code bits) drawn uniformly, so every 6-bit scale and minimum and
+    every 5-bit code is uniform. Padding bytes past the dense row are 0xA5."""
+    nb = K // 256
+    dense = nb * 176
+    ldw = dense if ldw is None else ldw
+    if ldw < dense:
+        raise ValueError("ldw smaller than a dense row")
+    blocks = np.empty((N, nb, 176), dtype=np.uint8)
+    rs = rng(cfg, copy, T_SCALE, part)
+    blocks[..., 0:2] = _scales_f16_bytes(rs, (N, nb), *Q5_K_D_RANGE)
+    blocks[..., 2:4] = _scales_f16_bytes(rs, (N, nb), *Q5_K_DMIN_RANGE)
+    blocks[..., 4:] = rng(cfg, copy, T_CODES, part).integers(0, 256, size=(N, nb, 172), dtype=np.uint8)
     if ldw == dense:
         return blocks.reshape(N, dense)
     out = np.full((N, ldw), 0xA5, dtype=np.uint8)

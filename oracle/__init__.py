@@ -27,10 +27,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "qmv_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-Q4_0, Q8_0, Q6_K = 2, 8, 14
-QTYPES = {"q4_0": Q4_0, "q8_0": Q8_0, "q6_k": Q6_K}
-BLOCK_BYTES = {Q4_0: 18, Q8_0: 34, Q6_K: 210}
-BLOCK_ELEMS = {Q4_0: 32, Q8_0: 32, Q6_K: 256}
+Q4_0, Q8_0, Q5_K, Q6_K = 2, 8, 13, 14
+QTYPES = {"q4_0": Q4_0, "q8_0": Q8_0, "q5_k": Q5_K, "q6_k": Q6_K}
+BLOCK_BYTES = {Q4_0: 18, Q8_0: 34, Q5_K: 176, Q6_K: 210}
+BLOCK_ELEMS = {Q4_0: 32, Q8_0: 32, Q5_K: 256, Q6_K: 256}
 
 _lib = None
 

@@ -41,6 +41,12 @@
  *   per 256 weights). The pages name the format only; the layout read here is
  *   the GGML k-quant Q6_K super-block, written out at decode_superblock_q6_k.
  *
+ *   Q5_K (176 B per 256 weights): the format of the dense FFN gate, up and
+ *   router projections of the pages' production model (the B9 comment in
+ *   `encode_one_layer`: "Q5_K 2816->5760 x 2 + 2816->128"). Named only; the
+ *   layout read here is the GGML k-quant Q5_K super-block, written out at
+ *   decode_superblock_q5_k.
+ *
  * Expert-indexed variant (the `quantized_matmul_id_ggml` calls in
  * `MlxModelWeights::encode_one_layer` on the hf2q page
  * `src/inference/models/gemma4/gpu_full_attn.rs`, MoE blocks B11 and B13,
@@ -74,6 +80,7 @@
 #define ORACLE_QK_K 256
 #define ORACLE_Q4_0 2
 #define ORACLE_Q8_0 8
+#define ORACLE_Q5_K 13
 #define ORACLE_Q6_K 14
 
 /* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
@@ -96,11 +103,53 @@ static int block_bytes(int qtype) {
     if (qtype == ORACLE_Q4_0) return 18;
     if (qtype == ORACLE_Q8_0) return 34;
     if (qtype == ORACLE_Q6_K) return 210;
+    if (qtype == ORACLE_Q5_K) return 176;
     return -1;
 }
 
-/* Weights per block: 32, or 256 for the super-block format. */
-static int block_elems(int qtype) { return qtype == ORACLE_Q6_K ? ORACLE_QK_K : ORACLE_QK; }
+/* Weights per block: 32, or 256 for the super-block formats. */
+static int block_elems(int qtype) {
+    return (qtype == ORACLE_Q6_K || qtype == ORACLE_Q5_K) ? ORACLE_QK_K : ORACLE_QK;
+}
+
+/*
+ * Q5_K super-block (176 bytes, 256 weights), the GGML k-quant 5-bit format:
+ *   bytes   0..1    binary16 d (scale of the sub-block scales)
+ *   bytes   2..3    binary16 dmin (scale of the sub-block minimums)
+ *   bytes   4..15   eight 6-bit sub-block scales and eight 6-bit minimums
+ *   bytes  16..47   qh: bit j of qh[l] is the high bit of weight 32j + l
+ *   bytes  48..175  qs: low 4 bits; sub-blocks 2i and 2i+1 share
+ *                   qs[32i .. 32i+31], 2i in the low nibbles, 2i+1 in the high
+ * Sub-block j (weights 32j .. 32j+31), with s = bytes 4..15:
+ *   j < 4:  scale = s[j] & 63,                     min = s[j+4] & 63
+ *   j >= 4: scale = (s[j+4] & 15) | (s[j-4] >> 6) << 4,
+ *           min   = (s[j+4] >> 4) | (s[j] >> 6) << 4
+ * Weight 32j + l: q = nibble of qs[32(j/2) + l] (low if j even) + 16 * bit j
+ * of qh[l]; w = d * scale * q - dmin * min.
+ */
+static void decode_superblock_q5_k(const uint8_t* b, double* out) {
+    double d = oracle_f16_to_f64((uint16_t)(b[0] | (b[1] << 8)));
+    double dmin = oracle_f16_to_f64((uint16_t)(b[2] | (b[3] << 8)));
+    const uint8_t* s = b + 4;
+    const uint8_t* qh = b + 16;
+    const uint8_t* qs = b + 48;
+    for (int j = 0; j < 8; ++j) {
+        int sc, mn;
+        if (j < 4) {
+            sc = s[j] & 63;
+            mn = s[j + 4] & 63;
+        } else {
+            sc = (s[j + 4] & 15) | ((s[j - 4] >> 6) << 4);
+            mn = (s[j + 4] >> 4) | ((s[j] >> 6) << 4);
+        }
+        for (int l = 0; l < 32; ++l) {
+            int byte = qs[32 * (j / 2) + l];
+            int low = (j % 2 == 0) ? (byte & 15) : (byte >> 4);
+            int q = low + 16 * ((qh[l] >> j) & 1);
+            out[32 * j + l] = d * (double)sc * (double)q - dmin * (double)mn;
+        }
+    }
+}
 
 /*
  * Q6_K super-block (210 bytes, 256 weights), the GGML k-quant 6-bit format:
@@ -155,6 +204,8 @@ int oracle_dequant_row(int qtype, const uint8_t* row, int K, double* w) {
     for (int b = 0; b < K / qk; ++b) {
         if (qtype == ORACLE_Q6_K)
             decode_superblock_q6_k(row + (size_t)b * bb, w + (size_t)b * qk);
+        else if (qtype == ORACLE_Q5_K)
+            decode_superblock_q5_k(row + (size_t)b * bb, w + (size_t)b * qk);
         else
             decode_block(qtype, row + (size_t)b * bb, w + (size_t)b * qk);
     }

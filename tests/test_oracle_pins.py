@@ -523,3 +523,82 @@ def test_q6_k_brute_force_tiny_shapes_against_exact_rationals():
                 bound = Fraction(K * 2.0 ** -53 * float(mag))
                 assert abs(Fraction(Y[m, n]) - exact) <= bound
                 assert abs(Fraction(A[m, n]) - mag) <= bound
+
+
+# --------------------------------------------------------------------------
+# Q5_K super-blocks (256 weights, 176 bytes).
+# --------------------------------------------------------------------------
+def _enc_q5_k(codes, scales, mins, d_bits, dmin_bits):
+    """Lay out 256 five-bit codes, eight 6-bit scales and minimums and the two
+    binary16 scales the way the GGML Q5_K super-block stores them, walking
+    the storage bytes: scale byte k (k < 4) = scale k | (scale k+4 >> 4) << 6;
+    byte 4+k = min k | (min k+4 >> 4) << 6; byte 8+k = (scale k+4 & 15) |
+    (min k+4 & 15) << 4; qh byte l holds bit 4 of code 32j + l at bit j; qs
+    byte 32i + l = (code 64i + l & 15) | (code 64i + 32 + l & 15) << 4."""
+    b = bytearray(176)
+    b[0], b[1], b[2], b[3] = d_bits & 0xFF, d_bits >> 8, dmin_bits & 0xFF, dmin_bits >> 8
+    for k in range(4):
+        b[4 + k] = scales[k] | ((scales[k + 4] >> 4) << 6)
+        b[8 + k] = mins[k] | ((mins[k + 4] >> 4) << 6)
+        b[12 + k] = (scales[k + 4] & 15) | ((mins[k + 4] & 15) << 4)
+    for l in range(32):
+        b[16 + l] = sum(((codes[32 * j + l] >> 4) & 1) << j for j in range(8))
+    for i in range(4):
+        for l in range(32):
+            b[48 + 32 * i + l] = (codes[64 * i + l] & 15) | ((codes[64 * i + 32 + l] & 15) << 4)
+    return bytes(b)
+
+
+def _q5_want(codes, scales, mins, d_bits, dmin_bits):
+    d = Fraction(float(np.array(d_bits, dtype=np.uint16).view(np.float16)))
+    dm = Fraction(float(np.array(dmin_bits, dtype=np.uint16).view(np.float16)))
+    return [d * scales[i // 32] * codes[i] - dm * mins[i // 32] for i in range(256)]
+
+
+def test_q5_k_hand_built_super_blocks():
+    """Every code 0..31 eight times, every 6-bit scale and minimum value over
+    the trials (high 2 bits included), normal, subnormal, negative and zero
+    scales: weight i must be d * scale[i // 32] * q_i - dmin * min[i // 32]."""
+    r = np.random.default_rng(71)
+    pairs = [(0x3C00, 0x3800), (0x0001, 0x03FF), (0xC000, 0x2E66), (0x1234, 0x0000), (0x7BFF, 0x8001)]
+    for trial, (db, mb) in enumerate(pairs * 2):
+        codes = [int(c) for c in r.permutation(np.repeat(np.arange(32), 8))]
+        scales = [int(v) for v in r.integers(0, 64, 8)]
+        mins = [int(v) for v in r.integers(0, 64, 8)]
+        scales[trial % 8], mins[(trial + 3) % 8] = 63, 63
+        raw = np.frombuffer(_enc_q5_k(codes, scales, mins, db, mb), dtype=np.uint8)
+        w = oracle.dequant_row("q5_k", raw, 256)
+        want = [float(v) for v in _q5_want(codes, scales, mins, db, mb)]
+        assert np.array_equal(w, np.array(want)), trial
+
+
+def test_q5_k_brute_force_and_one_hot():
+    r = np.random.default_rng(72)
+    K, N = 512, 3
+    rows, dense = [], []
+    for n in range(N):
+        raw, vals = b"", []
+        for sb in range(K // 256):
+            codes = [int(c) for c in r.integers(0, 32, 256)]
+            scales = [int(c) for c in r.integers(0, 64, 8)]
+            mins = [int(c) for c in r.integers(0, 64, 8)]
+            db, mb = [(0x2A00, 0x1F00), (0x0040, 0x0123), (0x3555, 0x3000)][(n + sb) % 3]
+            raw += _enc_q5_k(codes, scales, mins, db, mb)
+            vals += _q5_want(codes, scales, mins, db, mb)
+        rows.append(np.frombuffer(raw, dtype=np.uint8))
+        dense.append(vals)
+    W = np.stack(rows)
+    X = r.standard_normal((2, K)).astype(np.float32)
+    Y, A = oracle.qmv("q5_k", W, X)
+    for m in range(2):
+        for n in range(N):
+            prods = [dense[n][k] * Fraction(float(X[m, k])) for k in range(K)]
+            exact, mag = sum(prods), sum(abs(p) for p in prods)
+            bound = Fraction(K * 2.0 ** -53 * float(mag))
+            assert abs(Fraction(Y[m, n]) - exact) <= bound
+            assert abs(Fraction(A[m, n]) - mag) <= bound
+    for k in (0, 31, 32, 255, 256, 511):
+        e = np.zeros((1, K), np.float32)
+        e[0, k] = 1.0
+        Y, _ = oracle.qmv("q5_k", W, e)
+        assert all(Y[0, n] == float(dense[n][k]) for n in range(N))
