@@ -255,6 +255,28 @@ def moe_q6k_gate_up_throughput(dev, steps=40):
             "pct_hbm_peak": round(100 * nbytes / t / 1e9 / HBM_PEAK_GBS, 2)}
 
 
+def q5k_b9_throughput(dev, steps=48):
+    """The pages' B9 group in Q5_K at M = 1: FFN gate and up 2816 -> 5760 and
+    the router 2816 -> 128, three calls per step, 16 rotated copies (361 MB,
+    larger than the last-level cache)."""
+    import torch
+
+    from block_quantized_weight_qmatmul_amd import qmv, synth
+    shapes = [("gate", 5760), ("up", 5760), ("router", 128)]
+    K = 2816
+    sets = []
+    for r in range(16):
+        x = torch.from_numpy(synth.make_x(1, K, cfg=6, copy=r)[0]).to(dev)
+        sets.append([(torch.from_numpy(synth.make_weights("q5_k", n, K, cfg=6, copy=r, part=i)).to(dev), x,
+                      torch.empty(n, device=dev)) for i, (_, n) in enumerate(shapes)])
+    nbytes = sum(n for _, n in shapes) * synth.row_bytes("q5_k", K)
+    t = time_steps(lambda s: [qmv.qmv_q5_k(W, x, y) for W, x, y in s], sets, steps, 4) / steps
+    del sets
+    return {"workload": "q5_k_m1_b9_gate_up_2816x5760_router_2816x128", "weight_bytes_per_step": nbytes,
+            "launches": 3, "us_per_step": round(t * 1e6, 2), "GBps": round(nbytes / t / 1e9, 1),
+            "pct_hbm_peak": round(100 * nbytes / t / 1e9 / HBM_PEAK_GBS, 2)}
+
+
 def cpu_baseline(target_s: float):
     """The CPU oracle (fp64, OpenMP over rows) timed on a bounded sample of
     the layer set: the first rows of every projection, sized to take about
@@ -469,6 +491,7 @@ def main():
         extra["moe_ffn_t32_fused"] = moe_throughput(dev, 32, mode="ffn_fused")
         extra["lm_head_q6_k"] = lm_head_q6k_throughput(dev)
         extra["moe_q6_k_gate_up_t1"] = moe_q6k_gate_up_throughput(dev)
+        extra["q5_k_b9_group"] = q5k_b9_throughput(dev)
     del sets
     torch.cuda.empty_cache()
 

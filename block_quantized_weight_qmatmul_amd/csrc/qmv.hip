@@ -1814,11 +1814,113 @@ __device__ __forceinline__ void q6_unit_dot(const uint32_t* r, const float* xs, 
     }
 }
 
-// Persistent M <= MX kernel: tiles of ROWS = (64 / LPR) * WAVES rows, tiles
-// blockIdx.x, blockIdx.x + gridDim.x, ...; lane j of a row's LPR lanes takes
-// units j, j + LPR, ... of the row, one step of register prefetch; row sums
-// reduced over the lane group. Needs K % 256 == 0, 0 < K <= KMAX_Q6.
-template <int LPR, int WAVES, int MX>
+// ---------------------------------------------------------------------------
+// Q5_K (GGML k-quant 5-bit super-blocks: 256 weights in 176 bytes): d, dmin
+// (binary16), 12 bytes of eight 6-bit sub-block scales and minimums, qh[32]
+// (bit j of qh[l] = high bit of weight 32j + l), qs[128] (sub-blocks 2i, 2i+1
+// in the low / high nibbles of qs[32i + l]). w = d * scale_j * q - dmin * min_j.
+// The unit is again half a super-block: sub-blocks 4h .. 4h+3 (qs[64h ..
+// 64h+63], all of qh, the 12 scale bytes, d and dmin).
+// ---------------------------------------------------------------------------
+constexpr int Q5_SB_BYTES = 176;
+constexpr int Q5_UNIT_DW = 28;  // 16 qs + 8 qh + 3 scale dwords + d, dmin
+
+__device__ __forceinline__ void load_q5_unit(const uint8_t* sb, int h, uint32_t* r) {
+    typedef uint32_t u32x4a2 __attribute__((ext_vector_type(4), aligned(2)));
+    typedef uint32_t u32x2a2 __attribute__((ext_vector_type(2), aligned(2)));
+    typedef uint32_t u32a2 __attribute__((aligned(2)));
+    const u32x4a2* qs = reinterpret_cast<const u32x4a2*>(sb + 48 + 64 * h);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const u32x4a2 v = qs[i];
+        r[4 * i] = v.x, r[4 * i + 1] = v.y, r[4 * i + 2] = v.z, r[4 * i + 3] = v.w;
+    }
+    const u32x4a2* qh = reinterpret_cast<const u32x4a2*>(sb + 16);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const u32x4a2 v = qh[i];
+        r[16 + 4 * i] = v.x, r[17 + 4 * i] = v.y, r[18 + 4 * i] = v.z, r[19 + 4 * i] = v.w;
+    }
+    const u32x2a2 sc = *reinterpret_cast<const u32x2a2*>(sb + 4);
+    r[24] = sc.x;
+    r[25] = sc.y;
+    r[26] = *reinterpret_cast<const u32a2*>(sb + 12);
+    r[27] = *reinterpret_cast<const u32a2*>(sb);  // d (low half), dmin (high half)
+}
+
+// tot[i] += dot of Q5_K unit h (registers r) with staged row i.
+template <int MX>
+__device__ __forceinline__ void q5_unit_dot(const uint32_t* r, int h, const float* xs, size_t xstride,
+                                            const float* gs, size_t gstride, int nx, float* tot) {
+    const float d = half_lo(r[27]), dmin = half_hi(r[27]);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {  // sub-block j = 4h + jj
+        // scale bytes jj, jj + 4, jj + 8 hold sub-blocks jj and jj + 4
+        const uint32_t a = (r[24] >> (8 * jj)) & 0xFF, b = (r[25] >> (8 * jj)) & 0xFF;
+        const uint32_t c = (r[26] >> (8 * jj)) & 0xFF;
+        const uint32_t scj = h ? ((c & 15) | ((a >> 6) << 4)) : (a & 63);
+        const uint32_t mnj = h ? ((c >> 4) | ((b >> 6) << 4)) : (b & 63);
+        const int j = 4 * h + jj;
+        float acc[MX];
+#pragma unroll
+        for (int i = 0; i < MX; ++i) acc[i] = 0.f;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const uint32_t w = r[8 * (jj >> 1) + m];
+            const uint32_t nib = (jj & 1) ? ((w >> 4) & 0x0F0F0F0Fu) : (w & 0x0F0F0F0Fu);
+            const uint32_t cq = nib | (((r[16 + m] >> j) & 0x01010101u) << 4);
+            const float c0 = (float)(cq & 0xFF), c1 = (float)((cq >> 8) & 0xFF);
+            const float c2 = (float)((cq >> 16) & 0xFF), c3 = (float)(cq >> 24);
+#pragma unroll
+            for (int i = 0; i < MX; ++i) {
+                if (i < nx) {
+                    const float4 xv = *reinterpret_cast<const float4*>(xs + i * xstride + 32 * jj + 4 * m);
+                    acc[i] = fmaf(c0, xv.x, acc[i]);
+                    acc[i] = fmaf(c1, xv.y, acc[i]);
+                    acc[i] = fmaf(c2, xv.z, acc[i]);
+                    acc[i] = fmaf(c3, xv.w, acc[i]);
+                }
+            }
+        }
+        const float dsc = d * (float)scj, dmn = dmin * (float)mnj;
+#pragma unroll
+        for (int i = 0; i < MX; ++i) {
+            if (i < nx) {
+                const float sx = gs[i * gstride + 2 * jj] + gs[i * gstride + 2 * jj + 1];
+                tot[i] = fmaf(dsc, acc[i], fmaf(-dmn, sx, tot[i]));
+            }
+        }
+    }
+}
+
+// The two super-block formats, for the kernels below.
+struct FmtQ6K {
+    static constexpr int SB = Q6_SB_BYTES, DW = Q6_UNIT_DW;
+    static constexpr const char* NAME = "Q6_K";
+    __device__ static void load(const uint8_t* sb, int h, uint32_t* r) { load_q6_unit(sb, h, r); }
+    template <int MX>
+    __device__ static void dot(const uint32_t* r, int, const float* xs, size_t xstride, const float* gs,
+                               size_t gstride, int nx, float* tot) {
+        q6_unit_dot<MX>(r, xs, xstride, gs, gstride, nx, tot);
+    }
+};
+struct FmtQ5K {
+    static constexpr int SB = Q5_SB_BYTES, DW = Q5_UNIT_DW;
+    static constexpr const char* NAME = "Q5_K";
+    __device__ static void load(const uint8_t* sb, int h, uint32_t* r) { load_q5_unit(sb, h, r); }
+    template <int MX>
+    __device__ static void dot(const uint32_t* r, int h, const float* xs, size_t xstride, const float* gs,
+                               size_t gstride, int nx, float* tot) {
+        q5_unit_dot<MX>(r, h, xs, xstride, gs, gstride, nx, tot);
+    }
+};
+
+// Persistent M <= MX kernel for a super-block format F: tiles of ROWS =
+// (64 / LPR) * WAVES rows, tiles blockIdx.x, blockIdx.x + gridDim.x, ...;
+// lane j of a row's LPR lanes takes units j, j + LPR, ... of the row, one
+// step of register prefetch; row sums reduced over the lane group. Needs
+// K % 256 == 0, 0 < K <= KMAX_Q6.
+template <class F, int LPR, int WAVES, int MX>
 __global__ __launch_bounds__(WAVES * 64) void k_q6k(const uint8_t* __restrict__ W, size_t ldw,
                                                      const float* __restrict__ X, size_t ldx, float* __restrict__ Y,
                                                      size_t ldy, int nx, int N, int K) {
@@ -1840,13 +1942,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_q6k(const uint8_t* __restrict__ 
     long tile = blockIdx.x;
     if (tile >= ntiles) return;  // uniform over the workgroup
     int it = 0;
-    uint32_t nxt[Q6_UNIT_DW];
+    uint32_t nxt[F::DW];
     auto issue = [&](long tl, int i) {
         long row = tl * ROWS + lrow;
         row = row < N ? row : N - 1;
         int u = j + i * LPR;
         u = u < U ? u : U - 1;
-        load_q6_unit(W + (size_t)row * ldw + (size_t)(u >> 1) * Q6_SB_BYTES, u & 1, nxt);
+        F::load(W + (size_t)row * ldw + (size_t)(u >> 1) * F::SB, u & 1, nxt);
     };
     if constexpr (MX == 1) {
         // x loads first, then the first weight loads (see m1_stream)
@@ -1869,9 +1971,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_q6k(const uint8_t* __restrict__ 
 #pragma unroll
     for (int i = 0; i < MX; ++i) tot[i] = 0.f;
     while (true) {
-        uint32_t cur[Q6_UNIT_DW];
+        uint32_t cur[F::DW];
 #pragma unroll
-        for (int d = 0; d < Q6_UNIT_DW; ++d) cur[d] = nxt[d];
+        for (int d = 0; d < F::DW; ++d) cur[d] = nxt[d];
         const int u = j + it * LPR;
         int it2 = it + 1;
         long tile2 = tile;
@@ -1881,7 +1983,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_q6k(const uint8_t* __restrict__ 
         }
         const bool more = tile2 < ntiles;
         if (more) issue(tile2, it2);
-        if (u < U) q6_unit_dot<MX>(cur, xs + (size_t)u * XS_Q6, xstride, gs + 8 * u, gstride, nx, tot);
+        if (u < U) F::template dot<MX>(cur, u & 1, xs + (size_t)u * XS_Q6, xstride, gs + 8 * u, gstride, nx, tot);
         if (it == IPT - 1) {
             const long row = tile * ROWS + lrow;
 #pragma unroll
@@ -1899,12 +2001,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_q6k(const uint8_t* __restrict__ 
     }
 }
 
-// Expert-indexed Q6_K product: one workgroup per (tile of ROWS rows, pair
+// Expert-indexed super-block (Q6_K, Q5_K) product: one workgroup per (tile of ROWS rows, pair
 // p); expert ids[p]'s rows against activation row p / top_k. Pairs are not
 // grouped by expert (each reads its expert's rows): the form for decode,
 // where a token's experts are distinct. An id outside [0, n_experts) gives
 // NaN rows and sets *err_flag.
-template <int LPR, int WAVES>
+template <class F, int LPR, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void k_id_q6(const uint8_t* __restrict__ W, size_t estride, size_t ldw,
                                                       int n_experts, const float* __restrict__ X, size_t ldx,
                                                       const uint32_t* __restrict__ ids, int top_k,
@@ -1931,11 +2033,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_id_q6(const uint8_t* __restrict_
     const long row = row0 + wave * GROUPS + g;
     const long rowc = row < N ? row : N - 1;
     float* gs = xs + (size_t)U * XS_Q6;
-    uint32_t nxt[Q6_UNIT_DW];
+    uint32_t nxt[F::DW];
     auto issue = [&](int i) {
         int u = j + i * LPR;
         u = u < U ? u : U - 1;
-        load_q6_unit(We + (size_t)rowc * ldw + (size_t)(u >> 1) * Q6_SB_BYTES, u & 1, nxt);
+        F::load(We + (size_t)rowc * ldw + (size_t)(u >> 1) * F::SB, u & 1, nxt);
     };
     {
         // x loads first, then the first weight loads (see m1_stream)
@@ -1948,12 +2050,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_id_q6(const uint8_t* __restrict_
     lds_barrier();
     float tot = 0.f;
     for (int it = 0; it < IPT; ++it) {
-        uint32_t cur[Q6_UNIT_DW];
+        uint32_t cur[F::DW];
 #pragma unroll
-        for (int d = 0; d < Q6_UNIT_DW; ++d) cur[d] = nxt[d];
+        for (int d = 0; d < F::DW; ++d) cur[d] = nxt[d];
         if (it + 1 < IPT) issue(it + 1);
         const int u = j + it * LPR;
-        if (u < U) q6_unit_dot<1>(cur, xs + (size_t)u * XS_Q6, 0, gs + 8 * u, 0, 1, &tot);
+        if (u < U) F::template dot<1>(cur, u & 1, xs + (size_t)u * XS_Q6, 0, gs + 8 * u, 0, 1, &tot);
     }
     const float sum = lane_group_sum<LPR>(tot) * (escale ? escale[e] : 1.f);
     if (j == LPR - 1 && row < N) Y[(size_t)p * ldy + row] = sum;
@@ -2396,7 +2498,7 @@ int launch_id(const uint8_t* W, size_t es, size_t ldw, int E, const float* X, si
 }
 
 int launch_id_q6(const uint8_t* W, size_t es, size_t ldw, int E, const float* X, size_t ldx, const uint32_t* ids,
-                 int n_pairs, int top_k, float* Y, size_t ldy, int N, int K, const float* sc, int* err,
+                 int n_pairs, int top_k, float* Y, size_t ldy, int N, int K, const float* sc, int* err, int qtype,
                  hipStream_t st);
 
 // Shared by qmv_id (SW = false: X rows hold K values) and qmv_id_swiglu
@@ -2406,17 +2508,17 @@ template <bool SW>
 int id_common(const char* fn, int qtype, const void* Wv, size_t expert_stride_bytes, size_t ldw_bytes, int n_experts,
               const float* X, size_t ldx, const uint32_t* ids, int n_tokens, int top_k, float* Y, size_t ldy, int N,
               int K, const float* expert_scale, int* err_flag, void* stream) {
-    const bool q6 = qtype == QMV_Q6_K;
+    const bool q6 = qtype == QMV_Q6_K || qtype == QMV_Q5_K;  // super-block formats
     if (qtype != QMV_Q4_0 && qtype != QMV_Q8_0 && !(q6 && !SW))
         return fail(QMV_EUNSUPPORTED, "%s: qtype %d not supported", fn, qtype);
-    const int bb = q6 ? Q6_SB_BYTES : block_bytes(qtype);
+    const int bb = qtype == QMV_Q6_K ? Q6_SB_BYTES : qtype == QMV_Q5_K ? Q5_SB_BYTES : block_bytes(qtype);
     const int qk = q6 ? 256 : QK;
     if (n_experts <= 0) return fail(QMV_EINVAL, "%s: n_experts=%d must be > 0", fn, n_experts);
     if (top_k <= 0) return fail(QMV_EINVAL, "%s: top_k=%d must be > 0", fn, top_k);
     if (n_tokens < 0) return fail(QMV_EINVAL, "%s: n_tokens=%d < 0", fn, n_tokens);
     if (N < 0) return fail(QMV_EINVAL, "%s: N=%d < 0", fn, N);
     if (K < 0 || K % qk) return fail(QMV_EINVAL, "%s: K=%d is not a non-negative multiple of %d", fn, K, qk);
-    if (q6 && K > KMAX_Q6) return fail(QMV_EUNSUPPORTED, "%s: K=%d exceeds %d for Q6_K", fn, K, KMAX_Q6);
+    if (q6 && K > KMAX_Q6) return fail(QMV_EUNSUPPORTED, "%s: K=%d exceeds %d for Q6_K and Q5_K", fn, K, KMAX_Q6);
     if (top_k > ID_MAX_LIST) return fail(QMV_EUNSUPPORTED, "%s: top_k=%d exceeds %d", fn, top_k, ID_MAX_LIST);
     if ((long)n_tokens * top_k > 0x7FFFFFFFL) return fail(QMV_EINVAL, "%s: n_tokens*top_k overflows", fn);
     if (n_tokens == 0 || N == 0) return QMV_OK;
@@ -2449,7 +2551,7 @@ int id_common(const char* fn, int qtype, const void* Wv, size_t expert_stride_by
     const uint8_t* W = (const uint8_t*)Wv;
     if (q6 && K > 0)
         return launch_id_q6(W, expert_stride_bytes, ldw_bytes, n_experts, X, ldx, ids, n_tokens * top_k, top_k, Y,
-                            ldy, N, K, expert_scale, err_flag, st);
+                            ldy, N, K, expert_scale, err_flag, qtype, st);
     // (K = 0 of any type: the generic kernel reads no weights and writes zeros)
     const int fast = K > 0 && K % 64 == 0 && K <= KMAX_FAST_ID && ((uintptr_t)W & 3) == 0 && (ldw_bytes & 3) == 0 &&
                      (expert_stride_bytes & 3) == 0;
@@ -2537,7 +2639,7 @@ int launch_moe_down(const uint8_t* W, size_t es, size_t ldw, int E, const float*
 
 constexpr size_t MD_LDS_MAX = 64 * 1024;  // staged SwiGLU rows of one token
 
-template <int LPR, int WAVES, int MX>
+template <class F, int LPR, int WAVES, int MX>
 int launch_q6k_t(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int nx, int N, int K,
                  int wgs_per_cu, hipStream_t st) {
     constexpr int ROWS = (64 / LPR) * WAVES;
@@ -2545,12 +2647,12 @@ int launch_q6k_t(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float
     long nwg = (long)num_cus() * (wgs_per_cu > 0 ? wgs_per_cu : 2);
     nwg = nwg < tiles ? nwg : tiles;
     const size_t lds = (size_t)nx * q6_xs_bytes(K);
-    hipLaunchKernelGGL((k_q6k<LPR, WAVES, MX>), dim3((unsigned)nwg), dim3(WAVES * 64), lds, st, W, ldw, X, ldx, Y, ldy,
-                       nx, N, K);
-    return check_launch("qmv_q6_k kernel");
+    hipLaunchKernelGGL((k_q6k<F, LPR, WAVES, MX>), dim3((unsigned)nwg), dim3(WAVES * 64), lds, st, W, ldw, X, ldx, Y,
+                       ldy, nx, N, K);
+    return check_launch("super-block kernel");
 }
 
-template <int LPR>
+template <class F, int LPR>
 int launch_id_q6_t(const uint8_t* W, size_t es, size_t ldw, int E, const float* X, size_t ldx, const uint32_t* ids,
                    int n_pairs, int top_k, float* Y, size_t ldy, int N, int K, const float* sc, int* err,
                    hipStream_t st) {
@@ -2562,30 +2664,44 @@ int launch_id_q6_t(const uint8_t* W, size_t es, size_t ldw, int E, const float* 
     const int per = (65535 / top_k) * top_k;
     for (int p0 = 0; p0 < n_pairs; p0 += per) {
         const int np = n_pairs - p0 < per ? n_pairs - p0 : per;
-        hipLaunchKernelGGL((k_id_q6<LPR, WAVES>), dim3((unsigned)tiles, (unsigned)np), dim3(WAVES * 64),
+        hipLaunchKernelGGL((k_id_q6<F, LPR, WAVES>), dim3((unsigned)tiles, (unsigned)np), dim3(WAVES * 64),
                            q6_xs_bytes(K), st, W, es, ldw, E, X + (size_t)(p0 / top_k) * ldx, ldx, ids + p0, top_k,
                            Y + (size_t)p0 * ldy, ldy, N, K, sc, err);
-        const int rc = check_launch("qmv_id Q6_K kernel");
+        const int rc = check_launch("qmv_id super-block kernel");
         if (rc) return rc;
     }
     return QMV_OK;
 }
 
-int launch_id_q6(const uint8_t* W, size_t es, size_t ldw, int E, const float* X, size_t ldx, const uint32_t* ids,
+template <class F>
+int launch_id_kq(const uint8_t* W, size_t es, size_t ldw, int E, const float* X, size_t ldx, const uint32_t* ids,
                  int n_pairs, int top_k, float* Y, size_t ldy, int N, int K, const float* sc, int* err,
                  hipStream_t st) {
     const int lpr = pick_lpr_q6(K / 128);
 #define QMV_IDQ6_CASE(L) \
-    if (lpr == L) return launch_id_q6_t<L>(W, es, ldw, E, X, ldx, ids, n_pairs, top_k, Y, ldy, N, K, sc, err, st);
+    if (lpr == L) return launch_id_q6_t<F, L>(W, es, ldw, E, X, ldx, ids, n_pairs, top_k, Y, ldy, N, K, sc, err, st);
     QMV_IDQ6_CASE(64) QMV_IDQ6_CASE(32) QMV_IDQ6_CASE(16) QMV_IDQ6_CASE(8) QMV_IDQ6_CASE(4)
 #undef QMV_IDQ6_CASE
-    return fail(QMV_EINVAL, "internal: no Q6_K id kernel for lpr=%d", lpr);
+    return fail(QMV_EINVAL, "internal: no super-block id kernel for lpr=%d", lpr);
+}
+
+int launch_id_q6(const uint8_t* W, size_t es, size_t ldw, int E, const float* X, size_t ldx, const uint32_t* ids,
+                 int n_pairs, int top_k, float* Y, size_t ldy, int N, int K, const float* sc, int* err, int qtype,
+                 hipStream_t st) {
+    return qtype == QMV_Q5_K ? launch_id_kq<FmtQ5K>(W, es, ldw, E, X, ldx, ids, n_pairs, top_k, Y, ldy, N, K, sc, err, st)
+                             : launch_id_kq<FmtQ6K>(W, es, ldw, E, X, ldx, ids, n_pairs, top_k, Y, ldy, N, K, sc, err, st);
 }
 
 // Rows of X in launches of up to 4 (one launch when M = 1).
+template <class F>
 int launch_q6k(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N, int K,
                int lpr, int wgs_per_cu, hipStream_t st) {
-    if (lpr <= 0) lpr = pick_lpr_q6(K / 128);
+    if (lpr <= 0) {
+        // widen the lane groups of short calls until every compute unit has
+        // a tile (5760 rows at 8 lanes per row are 90 tiles of 64 rows)
+        lpr = pick_lpr_q6(K / 128);
+        while (lpr < 64 && ((long)N + (64 / lpr) * 8 - 1) / ((64 / lpr) * 8) < num_cus()) lpr *= 2;
+    }
     for (int m0 = 0; m0 < M; m0 += 4) {
         const int nx = M - m0 < 4 ? M - m0 : 4;
         const float* Xm = X + (size_t)m0 * ldx;
@@ -2593,14 +2709,45 @@ int launch_q6k(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* 
         int rc = QMV_EINVAL;
 #define QMV_Q6_CASE(L)                                                                                   \
     if (lpr == L)                                                                                        \
-        rc = nx == 1 ? launch_q6k_t<L, 8, 1>(W, ldw, Xm, ldx, Ym, ldy, 1, N, K, wgs_per_cu, st)          \
-                     : launch_q6k_t<L, 8, 4>(W, ldw, Xm, ldx, Ym, ldy, nx, N, K, wgs_per_cu, st);
+        rc = nx == 1 ? launch_q6k_t<F, L, 8, 1>(W, ldw, Xm, ldx, Ym, ldy, 1, N, K, wgs_per_cu, st)       \
+                     : launch_q6k_t<F, L, 8, 4>(W, ldw, Xm, ldx, Ym, ldy, nx, N, K, wgs_per_cu, st);
         QMV_Q6_CASE(64) QMV_Q6_CASE(32) QMV_Q6_CASE(16) QMV_Q6_CASE(8) QMV_Q6_CASE(4)
 #undef QMV_Q6_CASE
-        if (rc) return rc == QMV_EINVAL ? fail(QMV_EINVAL, "internal: no Q6_K kernel for lpr=%d", lpr) : rc;
+        if (rc) return rc == QMV_EINVAL ? fail(QMV_EINVAL, "internal: no super-block kernel for lpr=%d", lpr) : rc;
     }
     return QMV_OK;
 }
+// Dense call of a super-block format (shared by qmv_q5_k and qmv_q6_k).
+template <class F>
+int kq_dense(const char* name, const void* Wv, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M,
+             int N, int K, void* stream) {
+    if (M < 0 || M > QMV_MAX_M) return fail(QMV_EUNSUPPORTED, "%s: M=%d outside 0..%d", name, M, QMV_MAX_M);
+    if (N < 0) return fail(QMV_EINVAL, "%s: N=%d < 0", name, N);
+    if (K < 0 || K % 256) return fail(QMV_EINVAL, "%s: K=%d is not a non-negative multiple of 256", name, K);
+    if (M == 0 || N == 0) return QMV_OK;
+    if (!Wv && K > 0) return fail(QMV_EINVAL, "%s: W is NULL", name);
+    if (!X && K > 0) return fail(QMV_EINVAL, "%s: X is NULL", name);
+    if (!Y) return fail(QMV_EINVAL, "%s: Y is NULL", name);
+    if (K > KMAX_Q6) return fail(QMV_EUNSUPPORTED, "%s: K=%d exceeds %d", name, K, KMAX_Q6);
+    const size_t row = (size_t)(K / 256) * F::SB;
+    if (ldw < row) return fail(QMV_EINVAL, "%s: ldw_bytes=%zu < K/256*%d=%zu", name, ldw, F::SB, row);
+    if (M > 1 && ldx < (size_t)K) return fail(QMV_EINVAL, "%s: ldx=%zu < K=%d", name, ldx, K);
+    if (M > 1 && ldy < (size_t)N) return fail(QMV_EINVAL, "%s: ldy=%zu < N=%d", name, ldy, N);
+    if (((uintptr_t)Wv & 1) || (ldw & 1)) return fail(QMV_EALIGN, "%s: W and ldw_bytes must be 2-byte aligned", name);
+    if (((uintptr_t)X & 3) || ((uintptr_t)Y & 3)) return fail(QMV_EALIGN, "%s: X and Y must be 4-byte aligned", name);
+    if (M == 1) ldx = (size_t)K, ldy = (size_t)N;
+    if ((size_t)N > (SIZE_MAX - row) / (ldw ? ldw : 1)) return fail(QMV_EINVAL, "%s: N*ldw overflows", name);
+    const size_t wbytes = K ? (size_t)(N - 1) * ldw + row : 0;
+    const size_t xbytes = K ? ((size_t)(M - 1) * ldx + K) * 4 : 0;
+    const size_t ybytes = ((size_t)(M - 1) * ldy + N) * 4;
+    if (overlaps(Y, ybytes, Wv, wbytes) || overlaps(Y, ybytes, X, xbytes))
+        return fail(QMV_EINVAL, "%s: Y overlaps W or X", name);
+    hipStream_t st = (hipStream_t)stream;
+    if (K == 0)  // empty sums: the generic kernel reads no weights and writes zeros
+        return launch_generic<QMV_Q4_0>((const uint8_t*)Wv, ldw, X, ldx, Y, ldy, M, N, 0, st);
+    return launch_q6k<F>((const uint8_t*)Wv, ldw, X, ldx, Y, ldy, M, N, K, 0, 0, st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -2629,34 +2776,14 @@ int qmv_id_swiglu(int qtype, const void* Wv, size_t expert_stride_bytes, size_t 
                            n_tokens, top_k, Y, ldy, N, K, expert_scale, err_flag, stream);
 }
 
+int qmv_q5_k(const void* Wv, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N, int K,
+             void* stream) {
+    return kq_dense<FmtQ5K>("qmv_q5_k", Wv, ldw, X, ldx, Y, ldy, M, N, K, stream);
+}
+
 int qmv_q6_k(const void* Wv, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N, int K,
              void* stream) {
-    const char* name = "qmv_q6_k";
-    if (M < 0 || M > QMV_MAX_M) return fail(QMV_EUNSUPPORTED, "%s: M=%d outside 0..%d", name, M, QMV_MAX_M);
-    if (N < 0) return fail(QMV_EINVAL, "%s: N=%d < 0", name, N);
-    if (K < 0 || K % 256) return fail(QMV_EINVAL, "%s: K=%d is not a non-negative multiple of 256", name, K);
-    if (M == 0 || N == 0) return QMV_OK;
-    if (!Wv && K > 0) return fail(QMV_EINVAL, "%s: W is NULL", name);
-    if (!X && K > 0) return fail(QMV_EINVAL, "%s: X is NULL", name);
-    if (!Y) return fail(QMV_EINVAL, "%s: Y is NULL", name);
-    if (K > KMAX_Q6) return fail(QMV_EUNSUPPORTED, "%s: K=%d exceeds %d", name, K, KMAX_Q6);
-    const size_t row = (size_t)(K / 256) * Q6_SB_BYTES;
-    if (ldw < row) return fail(QMV_EINVAL, "%s: ldw_bytes=%zu < K/256*210=%zu", name, ldw, row);
-    if (M > 1 && ldx < (size_t)K) return fail(QMV_EINVAL, "%s: ldx=%zu < K=%d", name, ldx, K);
-    if (M > 1 && ldy < (size_t)N) return fail(QMV_EINVAL, "%s: ldy=%zu < N=%d", name, ldy, N);
-    if (((uintptr_t)Wv & 1) || (ldw & 1)) return fail(QMV_EALIGN, "%s: W and ldw_bytes must be 2-byte aligned", name);
-    if (((uintptr_t)X & 3) || ((uintptr_t)Y & 3)) return fail(QMV_EALIGN, "%s: X and Y must be 4-byte aligned", name);
-    if (M == 1) ldx = (size_t)K, ldy = (size_t)N;
-    if ((size_t)N > (SIZE_MAX - row) / (ldw ? ldw : 1)) return fail(QMV_EINVAL, "%s: N*ldw overflows", name);
-    const size_t wbytes = K ? (size_t)(N - 1) * ldw + row : 0;
-    const size_t xbytes = K ? ((size_t)(M - 1) * ldx + K) * 4 : 0;
-    const size_t ybytes = ((size_t)(M - 1) * ldy + N) * 4;
-    if (overlaps(Y, ybytes, Wv, wbytes) || overlaps(Y, ybytes, X, xbytes))
-        return fail(QMV_EINVAL, "%s: Y overlaps W or X", name);
-    hipStream_t st = (hipStream_t)stream;
-    if (K == 0)  // empty sums: the generic kernel reads no weights and writes zeros
-        return launch_generic<QMV_Q4_0>((const uint8_t*)Wv, ldw, X, ldx, Y, ldy, M, N, 0, st);
-    return launch_q6k((const uint8_t*)Wv, ldw, X, ldx, Y, ldy, M, N, K, 0, 0, st);
+    return kq_dense<FmtQ6K>("qmv_q6_k", Wv, ldw, X, ldx, Y, ldy, M, N, K, stream);
 }
 
 int qmv_moe_wsum(const float* Y, size_t ldy, const float* weights, int n_tokens, int top_k, int N, float* out,
@@ -2874,7 +3001,7 @@ int qmv_probe_idv(int qtype, int sw, int lpr, int wgs_per_cu, int deep, const vo
 // Q6_K with a forced lanes-per-row and workgroups per compute unit.
 int qmv_probe_q6k(int lpr, int wgs_per_cu, const void* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy,
                   int M, int N, int K, void* stream) {
-    return launch_q6k((const uint8_t*)W, ldw, X, ldx, Y, ldy, M, N, K, lpr, wgs_per_cu, (hipStream_t)stream);
+    return launch_q6k<FmtQ6K>((const uint8_t*)W, ldw, X, ldx, Y, ldy, M, N, K, lpr, wgs_per_cu, (hipStream_t)stream);
 }
 
 // One-launch MoE down half with a forced lanes-per-row and wave count.

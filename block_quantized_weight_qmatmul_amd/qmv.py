@@ -15,10 +15,10 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libqmv.so")
 
 QMV_OK, QMV_EINVAL, QMV_EALIGN, QMV_EUNSUPPORTED, QMV_EHIP = 0, -1, -2, -3, -4
-QMV_Q4_0, QMV_Q8_0, QMV_Q6_K = 2, 8, 14
+QMV_Q4_0, QMV_Q8_0, QMV_Q5_K, QMV_Q6_K = 2, 8, 13, 14
 QMV_MAX_M = 16
-BLOCK_BYTES = {QMV_Q4_0: 18, QMV_Q8_0: 34, QMV_Q6_K: 210}
-QTYPES = {"q4_0": QMV_Q4_0, "q8_0": QMV_Q8_0, "q6_k": QMV_Q6_K}
+BLOCK_BYTES = {QMV_Q4_0: 18, QMV_Q8_0: 34, QMV_Q5_K: 176, QMV_Q6_K: 210}
+QTYPES = {"q4_0": QMV_Q4_0, "q8_0": QMV_Q8_0, "q5_k": QMV_Q5_K, "q6_k": QMV_Q6_K}
 
 QMV_MAX_BATCH = 16
 
@@ -46,7 +46,7 @@ def lib() -> ctypes.CDLL:
                                "or python -m block_quantized_weight_qmatmul_amd.build")
         L = ctypes.CDLL(LIB_PATH)
         P, S, I = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
-        for name in ("qmv_q4_0", "qmv_q8_0", "qmv_q6_k"):
+        for name in ("qmv_q4_0", "qmv_q8_0", "qmv_q5_k", "qmv_q6_k"):
             f = getattr(L, name)
             f.restype = I
             f.argtypes = [P, S, P, S, P, S, I, I, I, P]
@@ -92,7 +92,7 @@ def _stream(stream) -> int:
 # ---------------------------------------------------------------------------
 def raw_qmv(qtype: int, W: int, ldw: int, X: int, ldx: int, Y: int, ldy: int, M: int, N: int, K: int,
             stream: int = 0) -> int:
-    f = {QMV_Q4_0: lib().qmv_q4_0, QMV_Q8_0: lib().qmv_q8_0, QMV_Q6_K: lib().qmv_q6_k}[qtype]
+    f = {QMV_Q4_0: lib().qmv_q4_0, QMV_Q8_0: lib().qmv_q8_0, QMV_Q5_K: lib().qmv_q5_k, QMV_Q6_K: lib().qmv_q6_k}[qtype]
     return f(W, ldw, X, ldx, Y, ldy, M, N, K, stream)
 
 
@@ -158,6 +158,11 @@ def qmv_q8_0(W, X, Y, K: Optional[int] = None, stream=None) -> None:
 def qmv_q6_k(W, X, Y, K: Optional[int] = None, stream=None) -> None:
     """Y = deq(W) @ X per row, Q6_K super-blocks (see include/qmv.h)."""
     _dense(QMV_Q6_K, W, X, Y, K, stream)
+
+
+def qmv_q5_k(W, X, Y, K: Optional[int] = None, stream=None) -> None:
+    """Y = deq(W) @ X per row, Q5_K super-blocks (see include/qmv.h)."""
+    _dense(QMV_Q5_K, W, X, Y, K, stream)
 
 
 def qmv_id(qtype, W, X, ids, Y, N: int, K: int, expert_scale=None, err_flag=None, stream=None) -> None:

@@ -2,7 +2,7 @@
  * qmv.h — block-quantized weight mat-vec on AMD Instinct MI355X (gfx950).
  *
  * y = W x for weights stored as GGML-style 32-element blocks (Q4_0, Q8_0)
- * or 256-element super-blocks (Q6_K) against fp32 activations, for 1 to 16
+ * or 256-element super-blocks (Q6_K, Q5_K) against fp32 activations, for 1 to 16
  * activation rows, plus the expert-indexed variant over a stack of
  * per-expert weight matrices and the MoE steps around it.
  *
@@ -78,6 +78,7 @@ extern "C" {
 /* Weight types (GGML type numbers). */
 #define QMV_Q4_0 2
 #define QMV_Q8_0 8
+#define QMV_Q5_K 13
 #define QMV_Q6_K 14
 
 #define QMV_MAX_M 16
@@ -135,6 +136,29 @@ int qmv_q6_k(const void* W, size_t ldw_bytes, const float* X, size_t ldx, float*
              int M, int N, int K, void* stream);
 
 /*
+ * qmv_q5_k — as qmv_q6_k with Q5_K super-blocks: 256 weights in 176 bytes.
+ *
+ * The pages' production model keeps its dense FFN gate, up and router
+ * projections in this format (the comment on the B9 dispatch group of
+ * `encode_one_layer`: "Q5_K 2816->5760 x 2 + 2816->128"). Named only; the
+ * layout taken is the GGML k-quant Q5_K super-block:
+ *   bytes   0..1    binary16 d        bytes 2..3  binary16 dmin
+ *   bytes   4..15   eight 6-bit sub-block scales and minimums, packed: for
+ *                   sub-block j < 4 scale = s[j] & 63, min = s[j+4] & 63; for
+ *                   j >= 4 scale = (s[j+4] & 15) | (s[j-4] >> 6) << 4,
+ *                   min = (s[j+4] >> 4) | (s[j] >> 6) << 4   (s = bytes 4..15)
+ *   bytes  16..47   qh: bit j of qh[l] is bit 4 of the code of weight 32j + l
+ *   bytes  48..175  qs: the low 4 bits; sub-blocks 2i and 2i+1 in the low and
+ *                   high nibbles of qs[32i + l]
+ * w = d * scale_j * q - dmin * min_j for weight 32j + l.
+ *  K          a non-negative multiple of 256, at most 16384.
+ *  ldw_bytes  >= K/256 * 176, even; W 2-byte aligned.
+ *  Other arguments as qmv_q4_0 (M 0..16, launches of up to 4 rows).
+ */
+int qmv_q5_k(const void* W, size_t ldw_bytes, const float* X, size_t ldx, float* Y, size_t ldy,
+             int M, int N, int K, void* stream);
+
+/*
  * qmv_id — expert-indexed product over a stack of weight matrices.
  *
  * For t < n_tokens and s < top_k, with p = t*top_k + s and e = ids[p]:
@@ -147,10 +171,11 @@ int qmv_q6_k(const void* W, size_t ldw_bytes, const float* X, size_t ldx, float*
  * per token; the down form flattens the slots: (n_tokens = T*k, top_k = 1)
  * with one X row per slot.
  *
- *  qtype                QMV_Q4_0, QMV_Q8_0 or QMV_Q6_K (the pages' production MoE
- *                       stores the gate_up experts as Q6_K; K a multiple of 256,
- *                       at most 16384; each (token, slot) pair reads its expert's
- *                       rows, with no grouping of pairs by expert).
+ *  qtype                QMV_Q4_0, QMV_Q8_0, QMV_Q6_K or QMV_Q5_K (the pages'
+ *                       production MoE stores the gate_up experts as Q6_K; for the
+ *                       super-block types K is a multiple of 256, at most 16384,
+ *                       and each (token, slot) pair reads its expert's rows, with
+ *                       no grouping of pairs by expert).
  *  W                    device, stacked weights, 2-byte aligned.
  *  expert_stride_bytes  >= N * ldw_bytes, even.
  *  ldw_bytes            row stride within an expert, >= K/32 * block bytes, even.
@@ -188,7 +213,7 @@ int qmv_id(int qtype, const void* W, size_t expert_stride_bytes, size_t ldw_byte
  * halves; gate first follows the buffer name `gate_up`).
  *
  *  G, ldg   device fp32 [n_tokens, 2K], row stride ldg >= 2K, 4-byte aligned.
- *  qtype    QMV_Q4_0 or QMV_Q8_0 (QMV_Q6_K returns QMV_EUNSUPPORTED).
+ *  qtype    QMV_Q4_0 or QMV_Q8_0 (the super-block types return QMV_EUNSUPPORTED).
  *  Every other argument, the result layout, NaN rows for bad ids and the
  *  error behaviour are those of qmv_id. For the pages' down form pass the
  *  gate_up output rows with (n_tokens = T*k, top_k = 1).

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert {"qmv_q4_0", "qmv_q8_0", "qmv_q6_k", "qmv_id", "qmv_id_swiglu", "qmv_moe_wsum", "qmv_moe_down",
+    assert {"qmv_q4_0", "qmv_q8_0", "qmv_q5_k", "qmv_q6_k", "qmv_id", "qmv_id_swiglu", "qmv_moe_wsum", "qmv_moe_down",
             "qmv_batch", "qmv_last_error"} <= set(names)
     L = ctypes.CDLL(qmv.LIB_PATH)
     for n in names:
@@ -228,6 +228,22 @@ Q6 = qmv.QMV_Q6_K
     ((Q6, W, 210, X, 255, Y, 16, 2, 16, 256), qmv.QMV_EINVAL, "ldx"),
 ])
 def test_q6k_argument_checks(args, status, msg):
+    q, *rest = args
+    assert qmv.raw_qmv(q, *rest) == status
+    assert msg in qmv.last_error()
+
+
+Q5 = qmv.QMV_Q5_K
+
+
+@pytest.mark.parametrize("args,status,msg", [
+    ((Q5, W, 176, X, 256, Y, 16, 1, 16, 128), qmv.QMV_EINVAL, "multiple of 256"),
+    ((Q5, W, 174, X, 256, Y, 16, 1, 16, 256), qmv.QMV_EINVAL, "K/256*176"),
+    ((Q5, W + 1, 176, X, 256, Y, 16, 1, 16, 256), qmv.QMV_EALIGN, "2-byte"),
+    ((Q5, W, 176, X, 256, W + 8, 16, 1, 16, 256), qmv.QMV_EINVAL, "overlaps"),
+    ((Q5, W, 176 * 65, X, 16640, Y, 16, 1, 16, 16640), qmv.QMV_EUNSUPPORTED, "exceeds"),
+])
+def test_q5k_argument_checks(args, status, msg):
     q, *rest = args
     assert qmv.raw_qmv(q, *rest) == status
     assert msg in qmv.last_error()
