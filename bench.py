@@ -277,6 +277,52 @@ def q5k_b9_throughput(dev, steps=48):
             "pct_hbm_peak": round(100 * nbytes / t / 1e9 / HBM_PEAK_GBS, 2)}
 
 
+def prefill_throughput(dev, M=512, steps=10):
+    """Prefill-sized product (qmv_gemm): M = 512 activation rows through the
+    Q4_0 FFN gate matrix 4096 -> 14336 (33 MB), eager raw calls (the M >= 2
+    path takes stream-ordered scratch). Beside it, the pages' F16-shadow route
+    timed on the same shape: an fp16 GEMM of dequantized weights through
+    torch.matmul (hipBLASLt) -- timing only, its fp16 activations do not meet
+    the parity tolerance."""
+    import torch
+
+    from block_quantized_weight_qmatmul_amd import qmv, synth
+    N, K = 14336, 4096
+    W = torch.from_numpy(synth.make_weights("q4_0", N, K, cfg=8)).to(dev)
+    X = torch.from_numpy(synth.make_x(M, K, cfg=8)).to(dev)
+    Y = torch.empty((M, N), device=dev)
+    st = torch.cuda.current_stream().cuda_stream
+    args = (qmv.QMV_Q4_0, W.data_ptr(), W.stride(0), X.data_ptr(), X.stride(0), Y.data_ptr(), Y.stride(0), M, N, K, st)
+
+    def run():
+        if qmv.raw_qmv_gemm(*args) != 0:
+            raise RuntimeError(qmv.last_error())
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3 / steps
+    Wt = torch.randn((K, N), device=dev, dtype=torch.float16)  # the shadow's shape and dtype
+    Xh = X.to(torch.float16)
+    Yh = torch.matmul(Xh, Wt)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        torch.matmul(Xh, Wt, out=Yh)
+    e1.record()
+    torch.cuda.synchronize()
+    t16 = e0.elapsed_time(e1) / 1e3 / steps
+    flops = 2.0 * M * N * K
+    del W, X, Y, Wt, Xh, Yh
+    return {"workload": f"q4_0_prefill_m{M}_4096x14336", "timing": "eager", "us_per_call": round(t * 1e6, 1),
+            "TFLOPs": round(flops / t / 1e12, 1), "pct_fp16_mfma_peak": round(100 * flops / t / 2.5e15, 2),
+            "f16_shadow_us": round(t16 * 1e6, 1), "f16_shadow_TFLOPs": round(flops / t16 / 1e12, 1)}
+
+
 def cpu_baseline(target_s: float):
     """The CPU oracle (fp64, OpenMP over rows) timed on a bounded sample of
     the layer set: the first rows of every projection, sized to take about
@@ -492,6 +538,7 @@ def main():
         extra["lm_head_q6_k"] = lm_head_q6k_throughput(dev)
         extra["moe_q6_k_gate_up_t1"] = moe_q6k_gate_up_throughput(dev)
         extra["q5_k_b9_group"] = q5k_b9_throughput(dev)
+        extra["prefill_m512"] = prefill_throughput(dev)
     del sets
     torch.cuda.empty_cache()
 

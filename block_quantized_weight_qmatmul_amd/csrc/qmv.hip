@@ -2786,6 +2786,52 @@ int qmv_q6_k(const void* Wv, size_t ldw, const float* X, size_t ldx, float* Y, s
     return kq_dense<FmtQ6K>("qmv_q6_k", Wv, ldw, X, ldx, Y, ldy, M, N, K, stream);
 }
 
+int qmv_gemm(int qtype, const void* Wv, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N,
+             int K, void* stream) {
+    const char* name = "qmv_gemm";
+    const bool kq = qtype == QMV_Q6_K || qtype == QMV_Q5_K;
+    if (qtype != QMV_Q4_0 && qtype != QMV_Q8_0 && !kq)
+        return fail(QMV_EUNSUPPORTED, "%s: qtype %d not supported", name, qtype);
+    const int qk = kq ? 256 : QK;
+    const int bb = qtype == QMV_Q6_K ? Q6_SB_BYTES : qtype == QMV_Q5_K ? Q5_SB_BYTES : block_bytes(qtype);
+    if (M < 0) return fail(QMV_EINVAL, "%s: M=%d < 0", name, M);
+    if (N < 0) return fail(QMV_EINVAL, "%s: N=%d < 0", name, N);
+    if (K < 0 || K % qk) return fail(QMV_EINVAL, "%s: K=%d is not a non-negative multiple of %d", name, K, qk);
+    if (M == 0 || N == 0) return QMV_OK;
+    if ((!Wv || !X) && K > 0) return fail(QMV_EINVAL, "%s: W or X is NULL", name);
+    if (!Y) return fail(QMV_EINVAL, "%s: Y is NULL", name);
+    const size_t row = (size_t)(K / qk) * bb;
+    if (ldw < row) return fail(QMV_EINVAL, "%s: ldw_bytes=%zu < K/%d*%d=%zu", name, ldw, qk, bb, row);
+    if (M > 1 && ldx < (size_t)K) return fail(QMV_EINVAL, "%s: ldx=%zu < K=%d", name, ldx, K);
+    if (M > 1 && ldy < (size_t)N) return fail(QMV_EINVAL, "%s: ldy=%zu < N=%d", name, ldy, N);
+    if (((uintptr_t)Wv & 1) || (ldw & 1)) return fail(QMV_EALIGN, "%s: W and ldw_bytes must be 2-byte aligned", name);
+    if (((uintptr_t)X & 3) || ((uintptr_t)Y & 3)) return fail(QMV_EALIGN, "%s: X and Y must be 4-byte aligned", name);
+    if (M == 1) ldx = (size_t)K, ldy = (size_t)N;
+    if ((size_t)N > (SIZE_MAX - row) / (ldw ? ldw : 1)) return fail(QMV_EINVAL, "%s: N*ldw overflows", name);
+    if ((size_t)M > (SIZE_MAX / 4 - (size_t)N) / (ldy ? ldy : 1)) return fail(QMV_EINVAL, "%s: M*ldy overflows", name);
+    const size_t wbytes = K ? (size_t)(N - 1) * ldw + row : 0;
+    const size_t xbytes = K ? ((size_t)(M - 1) * ldx + K) * 4 : 0;
+    const size_t ybytes = ((size_t)(M - 1) * ldy + N) * 4;
+    if (overlaps(Y, ybytes, Wv, wbytes) || overlaps(Y, ybytes, X, xbytes))
+        return fail(QMV_EINVAL, "%s: Y overlaps W or X", name);
+    // Blocks of up to 16 activation rows, each through the dense call of its
+    // type (matrix cores for Q4_0); every block reads the weights once.
+    for (int m0 = 0; m0 < M; m0 += QMV_MAX_M) {
+        const int mb = M - m0 < QMV_MAX_M ? M - m0 : QMV_MAX_M;
+        const float* Xm = X + (size_t)m0 * ldx;
+        float* Ym = Y + (size_t)m0 * ldy;
+        int rc;
+        if (qtype == QMV_Q6_K)
+            rc = kq_dense<FmtQ6K>(name, Wv, ldw, Xm, ldx, Ym, ldy, mb, N, K, stream);
+        else if (qtype == QMV_Q5_K)
+            rc = kq_dense<FmtQ5K>(name, Wv, ldw, Xm, ldx, Ym, ldy, mb, N, K, stream);
+        else
+            rc = dense(qtype, Wv, ldw, Xm, ldx, Ym, ldy, mb, N, K, stream);
+        if (rc) return rc;
+    }
+    return QMV_OK;
+}
+
 int qmv_moe_wsum(const float* Y, size_t ldy, const float* weights, int n_tokens, int top_k, int N, float* out,
                  size_t ldo, void* stream) {
     if (n_tokens < 0) return fail(QMV_EINVAL, "qmv_moe_wsum: n_tokens=%d < 0", n_tokens);

@@ -58,6 +58,8 @@ def lib() -> ctypes.CDLL:
         L.qmv_moe_wsum.argtypes = [P, S, P, I, I, I, P, S, P]
         L.qmv_moe_down.restype = I
         L.qmv_moe_down.argtypes = [I, P, S, S, I, P, S, P, P, I, I, P, S, I, I, P, P, P]
+        L.qmv_gemm.restype = I
+        L.qmv_gemm.argtypes = [I, P, S, P, S, P, S, I, I, I, P]
         L.qmv_batch.restype = I
         L.qmv_batch.argtypes = [I, ctypes.POINTER(Problem), I, P]
         L.qmv_last_error.restype = ctypes.c_char_p
@@ -163,6 +165,26 @@ def qmv_q6_k(W, X, Y, K: Optional[int] = None, stream=None) -> None:
 def qmv_q5_k(W, X, Y, K: Optional[int] = None, stream=None) -> None:
     """Y = deq(W) @ X per row, Q5_K super-blocks (see include/qmv.h)."""
     _dense(QMV_Q5_K, W, X, Y, K, stream)
+
+
+def raw_qmv_gemm(qtype: int, W: int, ldw: int, X: int, ldx: int, Y: int, ldy: int, M: int, N: int, K: int,
+                 stream: int = 0) -> int:
+    return lib().qmv_gemm(qtype, W, ldw, X, ldx, Y, ldy, M, N, K, stream)
+
+
+def qmv_gemm(qtype, W, X, Y, K: Optional[int] = None, stream=None) -> None:
+    """Y = deq(W) @ X per row for any number of rows M (see include/qmv.h).
+
+    W: uint8 [N, ldw]; X: fp32 [M, K]; Y: fp32 [M, N]."""
+    q = QTYPES[qtype] if isinstance(qtype, str) else int(qtype)
+    if W.dim() != 2 or W.stride(1) != 1 or X.dim() != 2 or Y.dim() != 2:
+        raise ValueError("W [N, ldw], X [M, K] and Y [M, N] must be 2-D")
+    M, N = Y.shape
+    K = X.shape[1] if K is None else K
+    if X.shape[0] != M or W.shape[0] != N or X.stride(1) != 1 or Y.stride(1) != 1:
+        raise ValueError("X [M, K] and Y [M, N] need unit inner stride and matching M, N")
+    _check(raw_qmv_gemm(q, _ptr(W), W.stride(0), _ptr(X), X.stride(0), _ptr(Y), Y.stride(0), M, N, K,
+                        _stream(stream)))
 
 
 def qmv_id(qtype, W, X, ids, Y, N: int, K: int, expert_scale=None, err_flag=None, stream=None) -> None:

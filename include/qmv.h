@@ -159,6 +159,29 @@ int qmv_q5_k(const void* W, size_t ldw_bytes, const float* X, size_t ldx, float*
              int M, int N, int K, void* stream);
 
 /*
+ * qmv_gemm — Y = deq(W) X^T for any number of activation rows M (prefill):
+ * the product of qmv_q4_0 / qmv_q8_0 / qmv_q5_k / qmv_q6_k without the
+ * M <= 16 limit.
+ *
+ * The pages route m > 8 through an F16 shadow of the weights (the F16 shadow
+ * population pass of the gemma4 model page: every attention and dense-MLP
+ * quantized weight pre-dequantized to F16 after load, so that
+ * `dispatch_qmatmul` takes an F16-input matmul for m > 8; about 1 GB extra,
+ * +16% prefill at 2K tokens). Here the weights
+ * stay block-quantized: the rows of X go in blocks of 16 through the dense
+ * call of the type (matrix cores for Q4_0), each block reading the weights
+ * once, so the weight traffic is ceil(M/16) times that of one call.
+ *
+ *  qtype   QMV_Q4_0, QMV_Q8_0, QMV_Q5_K or QMV_Q6_K.
+ *  M       >= 0 (0: nothing to do); other arguments and rules as qmv_q4_0
+ *          (qmv_q6_k / qmv_q5_k for the super-block types). With M > 16 and
+ *          Q4_0 the call takes the per-stream scratch of qmv_q4_0's M >= 2
+ *          path, once per block of rows, in stream order.
+ */
+int qmv_gemm(int qtype, const void* W, size_t ldw_bytes, const float* X, size_t ldx, float* Y, size_t ldy,
+             int M, int N, int K, void* stream);
+
+/*
  * qmv_id — expert-indexed product over a stack of weight matrices.
  *
  * For t < n_tokens and s < top_k, with p = t*top_k + s and e = ids[p]:

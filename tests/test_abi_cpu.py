@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert {"qmv_q4_0", "qmv_q8_0", "qmv_q5_k", "qmv_q6_k", "qmv_id", "qmv_id_swiglu", "qmv_moe_wsum", "qmv_moe_down",
+    assert {"qmv_q4_0", "qmv_q8_0", "qmv_q5_k", "qmv_q6_k", "qmv_gemm", "qmv_id", "qmv_id_swiglu", "qmv_moe_wsum", "qmv_moe_down",
             "qmv_batch", "qmv_last_error"} <= set(names)
     L = ctypes.CDLL(qmv.LIB_PATH)
     for n in names:
@@ -247,3 +247,20 @@ def test_q5k_argument_checks(args, status, msg):
     q, *rest = args
     assert qmv.raw_qmv(q, *rest) == status
     assert msg in qmv.last_error()
+
+
+@pytest.mark.parametrize("args,status,msg", [
+    ((5, W, 18 * 4, X, 128, Y, 16, 40, 16, 128), qmv.QMV_EUNSUPPORTED, "qtype"),
+    ((Q4, W, 18 * 4, X, 128, Y, 16, -1, 16, 128), qmv.QMV_EINVAL, "M=-1"),
+    ((Q4, W, 18 * 4, X, 127, Y, 16, 40, 16, 128), qmv.QMV_EINVAL, "ldx"),
+    ((Q4, W, 18 * 4, X, 128, Y, 15, 40, 16, 128), qmv.QMV_EINVAL, "ldy"),
+    ((Q4, W, 18 * 4, X, 128, X + 4 * 128 * 39, 16, 40, 16, 128), qmv.QMV_EINVAL, "overlaps"),
+    ((qmv.QMV_Q6_K, W, 210, X, 256, Y, 16, 40, 16, 128), qmv.QMV_EINVAL, "multiple of 256"),
+])
+def test_gemm_argument_checks(args, status, msg):
+    assert qmv.raw_qmv_gemm(*args) == status
+    assert msg in qmv.last_error()
+
+
+def test_gemm_empty_is_a_no_op():
+    assert qmv.raw_qmv_gemm(Q4, 0, 0, 0, 0, 0, 0, 0, 16, 128) == qmv.QMV_OK

@@ -1,0 +1,59 @@
+"""GPU parity of qmv_gemm (any number of activation rows) against the oracle.
+
+M spans one and several 16-row blocks with ragged tails; every weight type;
+a prefill shape (M = 256 rows of a 4096 x 4096 Q4_0 matrix) on sampled rows.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from block_quantized_weight_qmatmul_amd import qmv, synth
+from helpers import assert_within_tol
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def run(qtype, W, X, N, ldy=None):
+    M = X.shape[0]
+    Yfull = torch.full((M, ldy or N), np.nan, dtype=torch.float32, device=DEV)
+    Y = Yfull[:, :N]
+    qmv.qmv_gemm(qtype, torch.from_numpy(W).to(DEV), torch.from_numpy(X).to(DEV), Y)
+    torch.cuda.synchronize()
+    return Y.cpu().numpy(), Yfull.cpu().numpy()
+
+
+@pytest.mark.parametrize("qtype,M,N,K", [("q4_0", 17, 300, 1088), ("q4_0", 33, 129, 4096), ("q4_0", 100, 64, 512),
+                                         ("q8_0", 40, 200, 1024), ("q6_k", 20, 150, 2816), ("q5_k", 21, 150, 2816),
+                                         ("q4_0", 5, 77, 96)])
+def test_gemm_against_oracle(qtype, M, N, K):
+    W = synth.make_weights(qtype, N, K, cfg=90, part=M)
+    X = synth.make_x(M, K, cfg=90, part=M)
+    y, full = run(qtype, W, X, N, ldy=N + 2)
+    yo, a = oracle.qmv(qtype, W, X)
+    assert_within_tol(y, yo, a, f"{qtype} M={M}")
+    assert np.all(np.isnan(full[:, N:]))
+
+
+def test_gemm_prefill_shape_sampled_rows():
+    M, N, K = 256, 4096, 4096
+    W = synth.make_weights("q4_0", N, K, cfg=91)
+    X = synth.make_x(M, K, cfg=91)
+    y, _ = run("q4_0", W, X, N)
+    rows = np.unique(np.r_[0, N - 1, np.random.default_rng(91).integers(0, N, 120)])
+    yo, a = oracle.qmv("q4_0", W[rows], X)
+    print("ratio", assert_within_tol(y[:, rows], yo, a, "prefill"))
+
+
+def test_gemm_matches_dense_call_on_each_block():
+    """Rows 16..31 of a 40-row call equal a 16-row dense call on those rows."""
+    N, K = 256, 1024
+    W = synth.make_weights("q4_0", N, K, cfg=92)
+    X = synth.make_x(40, K, cfg=92)
+    y, _ = run("q4_0", W, X, N)
+    Y16 = torch.empty((16, N), device=DEV)
+    qmv.qmv_q4_0(torch.from_numpy(W).to(DEV), torch.from_numpy(X[16:32].copy()).to(DEV), Y16)
+    torch.cuda.synchronize()
+    assert np.array_equal(y[16:32], Y16.cpu().numpy())
