@@ -777,10 +777,16 @@ __global__ __launch_bounds__(WAVES * 64) void k_mm(const uint8_t* __restrict__ W
 // ---------------------------------------------------------------------------
 
 __global__ __launch_bounds__(256) void k_xprep(const float* __restrict__ X, size_t ldx, int M, int K,
-                                               uint8_t* __restrict__ xa) {
+                                               uint8_t* __restrict__ xa, size_t xa_stride) {
     typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
-    // block of 256 threads = (4 rows) x (16 blocks) x (4 slices) of one chunk
-    const int c = blockIdx.x, m = blockIdx.y * 4 + (threadIdx.x >> 6);
+    // block of 256 threads = (4 rows) x (16 blocks) x (4 slices) of one chunk;
+    // grid.y = 4 per block of 16 activation rows, whose records are xa_stride
+    // bytes apart
+    const int mb = blockIdx.y >> 2;
+    X += (size_t)mb * 16 * ldx;
+    M -= mb * 16;
+    xa += (size_t)mb * xa_stride;
+    const int c = blockIdx.x, m = (blockIdx.y & 3) * 4 + (threadIdx.x >> 6);
     const int bl = (threadIdx.x >> 2) & 15, G = threadIdx.x & 3;
     const int nb = K >> 5;
     const int b = c * 16 + bl;
@@ -854,7 +860,15 @@ template <int WAVES, int TW>
 __global__ __launch_bounds__(WAVES * 64) void k_mm4(const uint8_t* __restrict__ W, size_t ldw,
                                                     const uint8_t* __restrict__ xa, float* __restrict__ Y,
                                                     size_t ldy, int M, int N, int K, int chunks_per_seg,
-                                                    float* __restrict__ part) {
+                                                    float* __restrict__ part, int mblocks, size_t xa_stride) {
+    // blocks of 16 activation rows: block mb of tile group g is workgroup
+    // g * mblocks + mb, so the workgroups that read the same weights run
+    // side by side and share them through L2
+    const int mb = blockIdx.x % mblocks;
+    const int grp = blockIdx.x / mblocks;
+    xa += (size_t)mb * xa_stride;
+    Y += (size_t)mb * 16 * ldy;
+    M = M - mb * 16 < 16 ? M - mb * 16 : 16;
     extern __shared__ __align__(16) uint8_t smem[];  // 2 chunks of A operands
     __shared__ __align__(16) float sfac[2][16];      // their activation factors
     constexpr int NT = WAVES * 64;
@@ -866,7 +880,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_mm4(const uint8_t* __restrict__ 
     const int sgi = blockIdx.y;
     const int c0 = sgi * chunks_per_seg;
     const int c1 = c0 + chunks_per_seg < nchunks ? c0 + chunks_per_seg : nchunks;
-    const long row_base = ((long)blockIdx.x * WAVES + wave) * 16 * TW;
+    const long row_base = ((long)grp * WAVES + wave) * 16 * TW;
     const size_t xa_bytes = (size_t)(K / 32) * 2048;
     const float* __restrict__ fac = reinterpret_cast<const float*>(xa + xa_bytes);
 
@@ -2268,25 +2282,29 @@ void* stream_scratch(hipStream_t st, size_t n) {
 // must not hold a buffer that later eager calls on the stream reuse), so the
 // caller can fall back to the kernel that needs none.
 // Knobs (0 = default): segments of K, waves per workgroup (4 or 8).
+// Any M: blocks of 16 activation rows side by side in one launch (each block's
+// workgroups read the weights; neighbours share them through L2).
 int launch_mm4(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N, int K,
                int force_S, int force_waves, hipStream_t st) {
     const int ncu = num_cus();
     const long tiles = ((long)N + 15) / 16;
     const int waves = force_waves ? force_waves : 8;
     if (waves != 4 && waves != 8) return fail(QMV_EINVAL, "internal: waves=%d", waves);
+    const int mblocks = (M + 15) / 16;
     const long groups = (tiles + waves - 1) / waves;
     const int nchunks = (K + MM_KC - 1) / MM_KC;
     // Split K only when the tile groups fill less than half the chip: the
     // reduction launch costs more than a partly idle chip otherwise.
+    // (Only for one block of rows: the partial sums are laid out per call.)
     int S = 1;
-    if (2 * groups <= ncu)
+    if (mblocks == 1 && 2 * groups <= ncu)
         while (S < nchunks && S < MM_SMAX && groups * S < ncu) S *= 2;
-    if (force_S) S = force_S;
+    if (force_S && mblocks == 1) S = force_S;
     S = S > nchunks ? nchunks : S;
     S = S > MM_SMAX ? MM_SMAX : S;
     const int cps = (nchunks + S - 1) / S;
     S = (nchunks + cps - 1) / cps;
-    if (groups > 0x7FFFFFFF || S > 65535) return QMV_EUNSUPPORTED;
+    if (groups * mblocks > 0x7FFFFFFF || S > 65535 || 4L * mblocks > 65535) return QMV_EUNSUPPORTED;
     // No stream-ordered allocation while the stream is being captured into a
     // graph: the caller then gets the kernel that needs no scratch.
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
@@ -2296,22 +2314,26 @@ int launch_mm4(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* 
     }
     if (cap != hipStreamCaptureStatusNone) return QMV_EUNSUPPORTED;
     const size_t xa_bytes = (size_t)(K / 32) * 2048 + (size_t)nchunks * 64;
-    const size_t off_part = (xa_bytes + 255) & ~(size_t)255;
+    const size_t xa_stride = (xa_bytes + 255) & ~(size_t)255;
+    const size_t off_part = xa_stride * mblocks;
     const size_t part_bytes = S > 1 ? (size_t)S * M * N * sizeof(float) : 0;
     std::lock_guard<std::mutex> lock(g_scratch_mu);
     void* scratch = stream_scratch(st, off_part + part_bytes);
     if (!scratch) return QMV_EUNSUPPORTED;
     uint8_t* xa = (uint8_t*)scratch;
     float* part = S > 1 ? (float*)(xa + off_part) : nullptr;
-    hipLaunchKernelGGL(k_xprep, dim3((unsigned)nchunks, 4), dim3(256), 0, st, X, ldx, M, K, xa);
+    hipLaunchKernelGGL(k_xprep, dim3((unsigned)nchunks, (unsigned)(4 * mblocks)), dim3(256), 0, st, X, ldx, M, K, xa,
+                       xa_stride);
     int rc = check_launch("qmv activation pre-pass");
     if (rc == QMV_OK) {
         if (waves == 4)
-            hipLaunchKernelGGL((k_mm4<4, 1>), dim3((unsigned)groups, (unsigned)S), dim3(256), 2 * MM_CHUNK_BYTES, st, W,
-                               ldw, (const uint8_t*)xa, Y, ldy, M, N, K, cps, part);
+            hipLaunchKernelGGL((k_mm4<4, 1>), dim3((unsigned)(groups * mblocks), (unsigned)S), dim3(256),
+                               2 * MM_CHUNK_BYTES, st, W, ldw, (const uint8_t*)xa, Y, ldy, M, N, K, cps, part, mblocks,
+                               xa_stride);
         else
-            hipLaunchKernelGGL((k_mm4<8, 1>), dim3((unsigned)groups, (unsigned)S), dim3(512), 2 * MM_CHUNK_BYTES, st, W,
-                               ldw, (const uint8_t*)xa, Y, ldy, M, N, K, cps, part);
+            hipLaunchKernelGGL((k_mm4<8, 1>), dim3((unsigned)(groups * mblocks), (unsigned)S), dim3(512),
+                               2 * MM_CHUNK_BYTES, st, W, ldw, (const uint8_t*)xa, Y, ldy, M, N, K, cps, part, mblocks,
+                               xa_stride);
         rc = check_launch("qmv mfma kernel");
     }
     if (rc == QMV_OK && S > 1) {
@@ -2814,6 +2836,13 @@ int qmv_gemm(int qtype, const void* Wv, size_t ldw, const float* X, size_t ldx, 
     const size_t ybytes = ((size_t)(M - 1) * ldy + N) * 4;
     if (overlaps(Y, ybytes, Wv, wbytes) || overlaps(Y, ybytes, X, xbytes))
         return fail(QMV_EINVAL, "%s: Y overlaps W or X", name);
+    // Q4_0: every block of 16 rows in one matrix-core launch (blocks that
+    // read the same weights run side by side and share them through L2).
+    if (qtype == QMV_Q4_0 && M > QMV_MAX_M && K > 0 && K % 64 == 0 && ((uintptr_t)Wv & 3) == 0 && (ldw & 3) == 0) {
+        const int rc = launch_mm4((const uint8_t*)Wv, ldw, X, ldx, Y, ldy, M, N, K, 0, 0, (hipStream_t)stream);
+        if (rc != QMV_EUNSUPPORTED) return rc;
+        // under graph capture (no scratch) the blocks go through the dense call
+    }
     // Blocks of up to 16 activation rows, each through the dense call of its
     // type (matrix cores for Q4_0); every block reads the weights once.
     for (int m0 = 0; m0 < M; m0 += QMV_MAX_M) {
