@@ -150,6 +150,27 @@ def _make_q5_k(N, K, cfg, copy, part, ldw):
     return out
 
 
+def _bf16_rne(values) -> np.ndarray:
+    """fp32 values -> bf16 bit patterns, round to nearest even."""
+    u = np.asarray(values, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def make_affine4(N: int, K: int, cfg: int, copy: int = 0, part: int = 0):
+    """MLX affine 4-bit rows with groups of 32: (Wq uint32 [N, K/8], scales
+    and biases as bf16 bit patterns uint16 [N, K/32]). Codes uniform over
+    0..15 (uniform words), scales ~ U[0.002, 0.02] and biases ~ U[-0.16,
+    -0.016] as fp32 rounded to bf16 (nearest even), so weights scale*q + bias
+    straddle zero as affine-quantized weights do."""
+    if K % 32:
+        raise ValueError(f"K={K} is not a multiple of 32")
+    wq = rng(cfg, copy, T_CODES, part).integers(0, 2 ** 32, size=(N, K // 8), dtype=np.uint64).astype(np.uint32)
+    r = rng(cfg, copy, T_SCALE, part)
+    sc = _bf16_rne(r.uniform(0.002, 0.02, size=(N, K // 32)))
+    bi = _bf16_rne(r.uniform(-0.16, -0.016, size=(N, K // 32)))
+    return wq, sc, bi
+
+
 def make_x(M: int, K: int, cfg: int, copy: int = 0, part: int = 0) -> np.ndarray:
     """Activations ``[M, K]`` fp32 drawn from N(0, 1)."""
     return rng(cfg, copy, T_X, part).standard_normal((M, K), dtype=np.float64).astype(np.float32)

@@ -67,6 +67,12 @@ def _load():
         lib.oracle_swiglu.argtypes = [P, S, I, I, P, S]
         lib.oracle_moe_wsum.restype = I
         lib.oracle_moe_wsum.argtypes = [P, P, S, P, I, I, I, P, P, S]
+        lib.oracle_bf16_to_f64.restype = D
+        lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.oracle_dequant_affine4_row.restype = I
+        lib.oracle_dequant_affine4_row.argtypes = [P, P, P, I, P]
+        lib.oracle_qmv_affine4.restype = I
+        lib.oracle_qmv_affine4.argtypes = [P, S, P, P, S, P, S, I, I, I, P, P, S, I]
         lib.oracle_max_threads.restype = I
         _lib = lib
     return _lib
@@ -222,6 +228,46 @@ def moe_down(qtype, W: np.ndarray, G: np.ndarray, ids: np.ndarray, w: np.ndarray
     top_k = ids.shape[1]
     Y, YA = qmv_id_swiglu(qtype, W, G, ids.reshape(-1, 1), N, K, expert_scale=expert_scale, nthreads=nthreads)
     return moe_wsum(Y, np.asarray(w, dtype=np.float32).reshape(-1), top_k, YA=YA)
+
+
+def bf16_to_f64(bits: int) -> float:
+    return _load().oracle_bf16_to_f64(int(bits) & 0xFFFF)
+
+
+def dequant_affine4_row(wq: np.ndarray, scales: np.ndarray, biases: np.ndarray, K: int) -> np.ndarray:
+    """Affine 4-bit row: uint32 words (code j at bits 4j), bf16 bit patterns of
+    the group-of-32 scales and biases. Returns fp64 [K]."""
+    wq = np.ascontiguousarray(wq, dtype=np.uint32)
+    sc = np.ascontiguousarray(scales, dtype=np.uint16)
+    bi = np.ascontiguousarray(biases, dtype=np.uint16)
+    if wq.size < K // 8 or sc.size < K // 32 or bi.size < K // 32:
+        raise ValueError("row too short")
+    out = np.empty(K, dtype=np.float64)
+    if _load().oracle_dequant_affine4_row(_ptr(wq), _ptr(sc), _ptr(bi), K, _ptr(out)) != 0:
+        raise ValueError("bad arguments")
+    return out
+
+
+def qmv_affine4(Wq: np.ndarray, S: np.ndarray, B: np.ndarray, X: np.ndarray, nthreads: int = 0):
+    """Y, A for affine 4-bit rows: Wq uint32 [N, >= K/8], S, B uint16 (bf16) [N, >= K/32],
+    X fp32 [M, K]. Returns fp64 [M, N] each."""
+    Wq = np.ascontiguousarray(Wq, dtype=np.uint32)
+    S = np.ascontiguousarray(S, dtype=np.uint16)
+    B = np.ascontiguousarray(B, dtype=np.uint16)
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    if X.ndim == 1:
+        X = X[None, :]
+    M, K = X.shape
+    N = Wq.shape[0]
+    if S.shape != B.shape or S.shape[0] != N:
+        raise ValueError("scales and biases must be [N, groups]")
+    Y = np.empty((M, N), dtype=np.float64)
+    A = np.empty((M, N), dtype=np.float64)
+    rc = _load().oracle_qmv_affine4(_ptr(Wq), Wq.shape[1], _ptr(S), _ptr(B), S.shape[1], _ptr(X), K, M, N, K,
+                                    _ptr(Y), _ptr(A), N, nthreads)
+    if rc != 0:
+        raise ValueError(f"oracle_qmv_affine4 failed ({rc})")
+    return Y, A
 
 
 def max_threads() -> int:

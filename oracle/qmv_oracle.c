@@ -416,6 +416,63 @@ int oracle_moe_wsum(const double* Y, const double* YA, size_t ldy, const float* 
     return 0;
 }
 
+/*
+ * MLX affine 4-bit weights with groups of 32 (the DWQ MoE stacks of the
+ * gemma4 model page: each row's codes packed eight to a 32-bit word, code j
+ * of a word in bits 4j..4j+3, and one bf16 scale and one bf16 bias per group
+ * of 32 weights, in arrays of their own). The pages name the format affine
+ * and store a bias beside each scale; the reading taken is the affine
+ * dequantization w = scale * q + bias, q = 0..15.
+ *   Wq     row n at Wq + n*ldw (ldw in 32-bit words, >= K/8)
+ *   S, B   row n's scales and biases at S + n*lds, B + n*lds (>= K/32), bf16
+ * bf16 is the upper half of an IEEE binary32; it is decoded exactly.
+ */
+double oracle_bf16_to_f64(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+int oracle_dequant_affine4_row(const uint32_t* wq, const uint16_t* sc, const uint16_t* bi, int K, double* w) {
+    if (K <= 0 || K % 32) return -1;
+    for (int k = 0; k < K; ++k) {
+        int q = (int)((wq[k / 8] >> (4 * (k % 8))) & 15);
+        w[k] = oracle_bf16_to_f64(sc[k / 32]) * (double)q + oracle_bf16_to_f64(bi[k / 32]);
+    }
+    return 0;
+}
+
+/*
+ * Y[m*ldy + n] = sum_k w[n][k] * X[m*ldx + k] for affine 4-bit rows; A
+ * (nullable) receives sum_k |w x|. Same index order and fp64 as oracle_qmv.
+ */
+int oracle_qmv_affine4(const uint32_t* Wq, size_t ldw, const uint16_t* S, const uint16_t* B, size_t lds,
+                       const float* X, size_t ldx, int M, int N, int K, double* Y, double* A, size_t ldy,
+                       int nthreads) {
+    if (M < 0 || N < 0 || K <= 0 || K % 32) return -1;
+    if (ldw < (size_t)K / 8 || lds < (size_t)K / 32 || ldx < (size_t)K || ldy < (size_t)N) return -1;
+    set_threads(nthreads);
+    int err = 0;
+#pragma omp parallel
+    {
+        double* w = (double*)malloc(sizeof(double) * (size_t)K);
+        if (!w) {
+#pragma omp atomic write
+            err = -2;
+        } else {
+#pragma omp for schedule(static)
+            for (int n = 0; n < N; ++n) {
+                oracle_dequant_affine4_row(Wq + (size_t)n * ldw, S + (size_t)n * lds, B + (size_t)n * lds, K, w);
+                for (int m = 0; m < M; ++m)
+                    dot_row(w, X + (size_t)m * ldx, K, &Y[(size_t)m * ldy + n], A ? &A[(size_t)m * ldy + n] : NULL);
+            }
+            free(w);
+        }
+    }
+    return err;
+}
+
 int oracle_max_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

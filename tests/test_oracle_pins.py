@@ -602,3 +602,68 @@ def test_q5_k_brute_force_and_one_hot():
         e[0, k] = 1.0
         Y, _ = oracle.qmv("q5_k", W, e)
         assert all(Y[0, n] == float(dense[n][k]) for n in range(N))
+
+
+# --------------------------------------------------------------------------
+# MLX affine 4-bit, groups of 32 (codes eight to a 32-bit word, bf16 scale and
+# bias per group).
+# --------------------------------------------------------------------------
+def _pack_words(codes):
+    """codes [..., K] in 0..15 -> uint32 words [..., K/8], code j of a word in bits 4j."""
+    c = np.asarray(codes, dtype=np.uint32).reshape(*np.shape(codes)[:-1], -1, 8)
+    return np.bitwise_or.reduce(c << (4 * np.arange(8, dtype=np.uint32)), axis=-1).astype(np.uint32)
+
+
+def _bf16_bits(values):
+    """Truncate fp32 values to bf16 bit patterns (exactly representable inputs are kept)."""
+    return (np.asarray(values, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_bf16_decode_all_patterns():
+    bits = np.arange(65536, dtype=np.uint32)
+    want = (bits << 16).view(np.float32).astype(np.float64)
+    got = np.array([oracle.bf16_to_f64(int(b)) for b in bits])
+    same = (got == want) | (np.isnan(got) & np.isnan(want))
+    assert same.all()
+
+
+def test_affine4_hand_built_rows():
+    """Every code at every position of a word; scales and biases exactly
+    representable in bf16 (signs, powers of two, subnormal): weight k must be
+    scale[k // 32] * code_k + bias[k // 32]."""
+    r = np.random.default_rng(81)
+    K = 256
+    for trial in range(6):
+        codes = np.array([(k * 5 + k // 8 + trial) % 16 for k in range(K)])
+        sc = np.array([0.5, -0.25, 3.0, 1.0 / 1024, -6.0, 2.0 ** -130, 0.75, 96.0], dtype=np.float32)[r.permutation(8)]
+        bi = np.array([-1.0, 0.125, 0.0, -3.5, 2.0, -0.0, 7.0, 2.0 ** -128], dtype=np.float32)[r.permutation(8)]
+        w = oracle.dequant_affine4_row(_pack_words(codes), _bf16_bits(sc), _bf16_bits(bi), K)
+        want = [Fraction(float(sc[k // 32])) * int(codes[k]) + Fraction(float(bi[k // 32])) for k in range(K)]
+        assert np.array_equal(w, np.array([float(v) for v in want])), trial
+
+
+def test_affine4_brute_force_and_one_hot():
+    r = np.random.default_rng(82)
+    N, K = 3, 128
+    codes = r.integers(0, 16, (N, K))
+    sc = _bf16_bits(r.uniform(-0.05, 0.05, (N, K // 32)))
+    bi = _bf16_bits(r.uniform(-0.3, 0.3, (N, K // 32)))
+    Wq = _pack_words(codes)
+    X = r.standard_normal((2, K)).astype(np.float32)
+    Y, A = oracle.qmv_affine4(Wq, sc, bi, X)
+    scf = (sc.astype(np.uint32) << 16).view(np.float32)
+    bif = (bi.astype(np.uint32) << 16).view(np.float32)
+    for m in range(2):
+        for n in range(N):
+            prods = [(Fraction(float(scf[n, k // 32])) * int(codes[n, k]) + Fraction(float(bif[n, k // 32])))
+                     * Fraction(float(X[m, k])) for k in range(K)]
+            exact, mag = sum(prods), sum(abs(p) for p in prods)
+            bound = Fraction(K * 2.0 ** -53 * float(mag))
+            assert abs(Fraction(Y[m, n]) - exact) <= bound
+            assert abs(Fraction(A[m, n]) - mag) <= bound
+    for k in (0, 7, 8, 31, 32, 127):
+        e = np.zeros((1, K), np.float32)
+        e[0, k] = 1.0
+        Y, _ = oracle.qmv_affine4(Wq, sc, bi, e)
+        for n in range(N):
+            assert Y[0, n] == float(scf[n, k // 32]) * int(codes[n, k]) + float(bif[n, k // 32])
