@@ -323,6 +323,43 @@ def prefill_throughput(dev, M=512, steps=10):
             "f16_shadow_us": round(t16 * 1e6, 1), "f16_shadow_TFLOPs": round(flops / t16 / 1e12, 1)}
 
 
+def moe_affine4_throughput(dev, steps=48):
+    """MoE decode over MLX affine 4-bit expert stacks (the pages' DWQ stacks:
+    groups of 32, bf16 scale and bias): 128 experts, gate_up [1408, 2816] and
+    down [2816, 704], one token, top-8 -- the gate_up id call and the down id
+    call (8 activation rows, one slot each). One stack pair (about 475 MB,
+    larger than the last-level cache) and 16 routing sets in turn; GB/s counts
+    the 8 selected experts' bytes (codes, scales and biases)."""
+    import numpy as np
+    import torch
+
+    from block_quantized_weight_qmatmul_amd import qmv, synth
+    E, H, I, k = 128, 2816, 704, 8
+
+    def stack(N, K, part):
+        wq, sc, bi = synth.make_affine4(E * N, K, cfg=4, part=part)
+        return tuple(torch.from_numpy(a.reshape(E, N, -1).view(dt)).to(dev)
+                     for a, dt in ((wq, np.int32), (sc, np.int16), (bi, np.int16)))
+    gu, dn = stack(2 * I, H, 8), stack(H, I, 9)
+    X = torch.from_numpy(synth.make_x(1, H, cfg=4, part=8)).to(dev)
+    Xd = torch.from_numpy(synth.make_x(k, I, cfg=4, part=9)).to(dev)
+    sets = []
+    for r in range(16):
+        ids = torch.from_numpy(synth.router_topk(1, E, k, cfg=4, copy=r, part=8).astype(np.int32)).to(dev)
+        sets.append((ids, torch.empty(k, 2 * I, device=dev), torch.empty(k, H, device=dev)))
+
+    def step(s):
+        qmv.qmv_affine4_id(*gu, X, s[0], s[1], 2 * I, H)
+        qmv.qmv_affine4_id(*dn, Xd, s[0].view(-1, 1), s[2], H, I)
+    per_expert = (2 * I * H // 2 + 2 * I * (H // 32) * 4) + (H * I // 2 + H * (I // 32) * 4)
+    nbytes = k * per_expert
+    t = time_steps(step, sets, steps, 4) / steps
+    del gu, dn
+    return {"workload": "affine4_g32_moe_e128_top8_h2816_i704_t1", "launches": 2, "weight_bytes_per_step": nbytes,
+            "us_per_step": round(t * 1e6, 2), "GBps": round(nbytes / t / 1e9, 1),
+            "pct_hbm_peak": round(100 * nbytes / t / 1e9 / HBM_PEAK_GBS, 2)}
+
+
 def cpu_baseline(target_s: float):
     """The CPU oracle (fp64, OpenMP over rows) timed on a bounded sample of
     the layer set: the first rows of every projection, sized to take about
@@ -539,6 +576,7 @@ def main():
         extra["moe_q6_k_gate_up_t1"] = moe_q6k_gate_up_throughput(dev)
         extra["q5_k_b9_group"] = q5k_b9_throughput(dev)
         extra["prefill_m512"] = prefill_throughput(dev)
+        extra["moe_affine4_t1"] = moe_affine4_throughput(dev)
     del sets
     torch.cuda.empty_cache()
 

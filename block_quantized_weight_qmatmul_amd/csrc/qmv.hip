@@ -1710,7 +1710,7 @@ constexpr int XS_Q6 = 132;       // LDS floats per staged unit (128 + 4 pad)
 constexpr int KMAX_Q6 = 16384;   // largest K the Q6_K kernel stages
 
 __host__ __device__ constexpr size_t q6_xs_bytes(int K) {
-    return ((size_t)(K / 128) * XS_Q6 + (size_t)(K / 16)) * sizeof(float);
+    return ((size_t)((K + 127) / 128) * XS_Q6 + (size_t)(K / 16)) * sizeof(float);
 }
 
 // Registers of unit h (0 or 1) of the super-block at sb.
@@ -1907,25 +1907,124 @@ __device__ __forceinline__ void q5_unit_dot(const uint32_t* r, int h, const floa
     }
 }
 
-// The two super-block formats, for the kernels below.
+// ---------------------------------------------------------------------------
+// MLX affine 4-bit, groups of 32: a row's codes eight to a 32-bit word (code j
+// in bits 4j), and one bf16 scale and one bf16 bias per group in arrays of
+// their own; w = scale * q + bias. The unit is four groups (128 weights: 16
+// code words, 4 scales, 4 biases); the last unit of a row whose K is not a
+// multiple of 128 holds K % 128 weights and reads nothing past them.
+// ---------------------------------------------------------------------------
+constexpr int A4_UNIT_DW = 20;  // 16 code words + 2 scale dwords + 2 bias dwords
+
+__device__ __forceinline__ void load_a4_unit(const uint8_t* wrow, const uint16_t* srow, const uint16_t* brow, int u,
+                                             int K, uint32_t* r) {
+    const int g0 = 4 * u, ng = K >> 5;  // groups of this unit: g0 .. g0 + 3, valid below ng
+    const u32x4* wq = reinterpret_cast<const u32x4*>(wrow) + g0;
+    uint16_t sv[4], bv[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        sv[g] = 0;
+        bv[g] = 0;
+        if (g0 + g < ng) {
+            v = wq[g];
+            sv[g] = srow[g0 + g];
+            bv[g] = brow[g0 + g];
+        }
+        r[4 * g] = v.x, r[4 * g + 1] = v.y, r[4 * g + 2] = v.z, r[4 * g + 3] = v.w;
+    }
+    r[16] = sv[0] | (uint32_t)sv[1] << 16;
+    r[17] = sv[2] | (uint32_t)sv[3] << 16;
+    r[18] = bv[0] | (uint32_t)bv[1] << 16;
+    r[19] = bv[2] | (uint32_t)bv[3] << 16;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+
+// tot[i] += dot of affine unit u (registers r) with staged row i; groups at
+// or past K (the tail of a row's last unit) contribute nothing.
+template <int MX>
+__device__ __forceinline__ void a4_unit_dot(const uint32_t* r, int u, int K, const float* xs, size_t xstride,
+                                            const float* gs, size_t gstride, int nx, float* tot) {
+    const int ng = K >> 5;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        if (4 * u + g >= ng) break;
+        float acc[MX];
+#pragma unroll
+        for (int i = 0; i < MX; ++i) acc[i] = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {  // weights 8w .. 8w+7 of the group
+            const uint32_t q = r[4 * g + w];
+            const uint32_t ev = q & 0x0F0F0F0Fu, od = (q >> 4) & 0x0F0F0F0Fu;  // even, odd weights
+            const float c0 = (float)(ev & 0xFF), c2 = (float)((ev >> 8) & 0xFF);
+            const float c4 = (float)((ev >> 16) & 0xFF), c6 = (float)(ev >> 24);
+            const float c1 = (float)(od & 0xFF), c3 = (float)((od >> 8) & 0xFF);
+            const float c5 = (float)((od >> 16) & 0xFF), c7 = (float)(od >> 24);
+#pragma unroll
+            for (int i = 0; i < MX; ++i) {
+                if (i < nx) {
+                    const float* xp = xs + i * xstride + 32 * g + 8 * w;
+                    const float4 a = *reinterpret_cast<const float4*>(xp);
+                    const float4 b = *reinterpret_cast<const float4*>(xp + 4);
+                    acc[i] = fmaf(c0, a.x, acc[i]);
+                    acc[i] = fmaf(c1, a.y, acc[i]);
+                    acc[i] = fmaf(c2, a.z, acc[i]);
+                    acc[i] = fmaf(c3, a.w, acc[i]);
+                    acc[i] = fmaf(c4, b.x, acc[i]);
+                    acc[i] = fmaf(c5, b.y, acc[i]);
+                    acc[i] = fmaf(c6, b.z, acc[i]);
+                    acc[i] = fmaf(c7, b.w, acc[i]);
+                }
+            }
+        }
+        const float sc = (g & 1) ? bf16_hi(r[16 + (g >> 1)]) : bf16_lo(r[16 + (g >> 1)]);
+        const float bi = (g & 1) ? bf16_hi(r[18 + (g >> 1)]) : bf16_lo(r[18 + (g >> 1)]);
+#pragma unroll
+        for (int i = 0; i < MX; ++i)
+            if (i < nx) tot[i] = fmaf(sc, acc[i], fmaf(bi, gs[i * gstride + 2 * g] + gs[i * gstride + 2 * g + 1], tot[i]));
+    }
+}
+
+// The weight formats of the unit kernels below: units per row, the registers
+// of unit u of a row (wrow: the row's bytes; srow, brow: its separate scales
+// and biases, affine format only), and the unit's dot product.
 struct FmtQ6K {
-    static constexpr int SB = Q6_SB_BYTES, DW = Q6_UNIT_DW;
-    static constexpr const char* NAME = "Q6_K";
-    __device__ static void load(const uint8_t* sb, int h, uint32_t* r) { load_q6_unit(sb, h, r); }
+    static constexpr int DW = Q6_UNIT_DW, SB = Q6_SB_BYTES;
+    __host__ __device__ static constexpr int units(int K) { return K >> 7; }
+    __device__ static void load(const uint8_t* wrow, const uint16_t*, const uint16_t*, int u, int, uint32_t* r) {
+        load_q6_unit(wrow + (size_t)(u >> 1) * Q6_SB_BYTES, u & 1, r);
+    }
     template <int MX>
-    __device__ static void dot(const uint32_t* r, int, const float* xs, size_t xstride, const float* gs,
+    __device__ static void dot(const uint32_t* r, int, int, const float* xs, size_t xstride, const float* gs,
                                size_t gstride, int nx, float* tot) {
         q6_unit_dot<MX>(r, xs, xstride, gs, gstride, nx, tot);
     }
 };
 struct FmtQ5K {
-    static constexpr int SB = Q5_SB_BYTES, DW = Q5_UNIT_DW;
-    static constexpr const char* NAME = "Q5_K";
-    __device__ static void load(const uint8_t* sb, int h, uint32_t* r) { load_q5_unit(sb, h, r); }
+    static constexpr int DW = Q5_UNIT_DW, SB = Q5_SB_BYTES;
+    __host__ __device__ static constexpr int units(int K) { return K >> 7; }
+    __device__ static void load(const uint8_t* wrow, const uint16_t*, const uint16_t*, int u, int, uint32_t* r) {
+        load_q5_unit(wrow + (size_t)(u >> 1) * Q5_SB_BYTES, u & 1, r);
+    }
     template <int MX>
-    __device__ static void dot(const uint32_t* r, int h, const float* xs, size_t xstride, const float* gs,
+    __device__ static void dot(const uint32_t* r, int u, int, const float* xs, size_t xstride, const float* gs,
                                size_t gstride, int nx, float* tot) {
-        q5_unit_dot<MX>(r, h, xs, xstride, gs, gstride, nx, tot);
+        q5_unit_dot<MX>(r, u & 1, xs, xstride, gs, gstride, nx, tot);
+    }
+};
+struct FmtA4 {
+    static constexpr int DW = A4_UNIT_DW;
+    __host__ __device__ static constexpr int units(int K) { return (K + 127) >> 7; }
+    __device__ static void load(const uint8_t* wrow, const uint16_t* srow, const uint16_t* brow, int u, int K,
+                                uint32_t* r) {
+        load_a4_unit(wrow, srow, brow, u, K, r);
+    }
+    template <int MX>
+    __device__ static void dot(const uint32_t* r, int u, int K, const float* xs, size_t xstride, const float* gs,
+                               size_t gstride, int nx, float* tot) {
+        a4_unit_dot<MX>(r, u, K, xs, xstride, gs, gstride, nx, tot);
     }
 };
 
@@ -1937,7 +2036,8 @@ struct FmtQ5K {
 template <class F, int LPR, int WAVES, int MX>
 __global__ __launch_bounds__(WAVES * 64) void k_q6k(const uint8_t* __restrict__ W, size_t ldw,
                                                      const float* __restrict__ X, size_t ldx, float* __restrict__ Y,
-                                                     size_t ldy, int nx, int N, int K) {
+                                                     size_t ldy, int nx, int N, int K, const uint16_t* __restrict__ S,
+                                                     const uint16_t* __restrict__ Bz, size_t lds) {
     constexpr int GROUPS = 64 / LPR;
     constexpr int ROWS = GROUPS * WAVES;
     constexpr int NT = WAVES * 64;
@@ -1945,7 +2045,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_q6k(const uint8_t* __restrict__ 
     extern __shared__ __align__(16) float xs[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane / LPR, j = lane % LPR;
-    const int U = K >> 7;
+    const int U = F::units(K);
     const int IPT = (U + LPR - 1) / LPR;
     const long ntiles = ((long)N + ROWS - 1) / ROWS;
     const long lrow = (long)(wave * GROUPS + g);
@@ -1962,7 +2062,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_q6k(const uint8_t* __restrict__ 
         row = row < N ? row : N - 1;
         int u = j + i * LPR;
         u = u < U ? u : U - 1;
-        F::load(W + (size_t)row * ldw + (size_t)(u >> 1) * F::SB, u & 1, nxt);
+        F::load(W + (size_t)row * ldw, S + (size_t)row * lds, Bz + (size_t)row * lds, u, K, nxt);
     };
     if constexpr (MX == 1) {
         // x loads first, then the first weight loads (see m1_stream)
@@ -1997,7 +2097,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_q6k(const uint8_t* __restrict__ 
         }
         const bool more = tile2 < ntiles;
         if (more) issue(tile2, it2);
-        if (u < U) F::template dot<MX>(cur, u & 1, xs + (size_t)u * XS_Q6, xstride, gs + 8 * u, gstride, nx, tot);
+        if (u < U) F::template dot<MX>(cur, u, K, xs + (size_t)u * XS_Q6, xstride, gs + 8 * u, gstride, nx, tot);
         if (it == IPT - 1) {
             const long row = tile * ROWS + lrow;
 #pragma unroll
@@ -2025,7 +2125,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_id_q6(const uint8_t* __restrict_
                                                       int n_experts, const float* __restrict__ X, size_t ldx,
                                                       const uint32_t* __restrict__ ids, int top_k,
                                                       float* __restrict__ Y, size_t ldy, int N, int K,
-                                                      const float* __restrict__ escale, int* __restrict__ err_flag) {
+                                                      const float* __restrict__ escale, int* __restrict__ err_flag,
+                                                      const uint16_t* __restrict__ S, const uint16_t* __restrict__ Bz,
+                                                      size_t s_estride, size_t lds) {
     constexpr int GROUPS = 64 / LPR;
     constexpr int ROWS = GROUPS * WAVES;
     constexpr int NT = WAVES * 64;
@@ -2036,7 +2138,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_id_q6(const uint8_t* __restrict_
     const long row0 = (long)blockIdx.x * ROWS;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane / LPR, j = lane % LPR;
-    const int U = K >> 7;
+    const int U = F::units(K);
     const int IPT = (U + LPR - 1) / LPR;
     if (e >= (uint32_t)n_experts) {  // uniform over the workgroup
         for (long n = row0 + tid; n < row0 + ROWS && n < N; n += NT) Y[(size_t)p * ldy + n] = __builtin_nanf("");
@@ -2051,7 +2153,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_id_q6(const uint8_t* __restrict_
     auto issue = [&](int i) {
         int u = j + i * LPR;
         u = u < U ? u : U - 1;
-        F::load(We + (size_t)rowc * ldw + (size_t)(u >> 1) * F::SB, u & 1, nxt);
+        F::load(We + (size_t)rowc * ldw, S + (size_t)e * s_estride + (size_t)rowc * lds,
+                Bz + (size_t)e * s_estride + (size_t)rowc * lds, u, K, nxt);
     };
     {
         // x loads first, then the first weight loads (see m1_stream)
@@ -2069,7 +2172,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_id_q6(const uint8_t* __restrict_
         for (int d = 0; d < F::DW; ++d) cur[d] = nxt[d];
         if (it + 1 < IPT) issue(it + 1);
         const int u = j + it * LPR;
-        if (u < U) F::template dot<1>(cur, u & 1, xs + (size_t)u * XS_Q6, 0, gs + 8 * u, 0, 1, &tot);
+        if (u < U) F::template dot<1>(cur, u, K, xs + (size_t)u * XS_Q6, 0, gs + 8 * u, 0, 1, &tot);
     }
     const float sum = lane_group_sum<LPR>(tot) * (escale ? escale[e] : 1.f);
     if (j == LPR - 1 && row < N) Y[(size_t)p * ldy + row] = sum;
@@ -2661,23 +2764,32 @@ int launch_moe_down(const uint8_t* W, size_t es, size_t ldw, int E, const float*
 
 constexpr size_t MD_LDS_MAX = 64 * 1024;  // staged SwiGLU rows of one token
 
+// Separate per-group scales and biases of the affine format (unused by the
+// super-block formats): row n's at S + n * lds, expert e's block s_estride
+// elements after expert e - 1's.
+struct AuxArgs {
+    const uint16_t* S = nullptr;
+    const uint16_t* B = nullptr;
+    size_t lds = 0, s_estride = 0;
+};
+
 template <class F, int LPR, int WAVES, int MX>
 int launch_q6k_t(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int nx, int N, int K,
-                 int wgs_per_cu, hipStream_t st) {
+                 int wgs_per_cu, hipStream_t st, const AuxArgs& ax) {
     constexpr int ROWS = (64 / LPR) * WAVES;
     const long tiles = ((long)N + ROWS - 1) / ROWS;
     long nwg = (long)num_cus() * (wgs_per_cu > 0 ? wgs_per_cu : 2);
     nwg = nwg < tiles ? nwg : tiles;
     const size_t lds = (size_t)nx * q6_xs_bytes(K);
     hipLaunchKernelGGL((k_q6k<F, LPR, WAVES, MX>), dim3((unsigned)nwg), dim3(WAVES * 64), lds, st, W, ldw, X, ldx, Y,
-                       ldy, nx, N, K);
+                       ldy, nx, N, K, ax.S, ax.B, ax.lds);
     return check_launch("super-block kernel");
 }
 
 template <class F, int LPR>
 int launch_id_q6_t(const uint8_t* W, size_t es, size_t ldw, int E, const float* X, size_t ldx, const uint32_t* ids,
                    int n_pairs, int top_k, float* Y, size_t ldy, int N, int K, const float* sc, int* err,
-                   hipStream_t st) {
+                   hipStream_t st, const AuxArgs& ax) {
     constexpr int WAVES = 4;
     constexpr int ROWS = (64 / LPR) * WAVES;
     const long tiles = ((long)N + ROWS - 1) / ROWS;
@@ -2688,7 +2800,7 @@ int launch_id_q6_t(const uint8_t* W, size_t es, size_t ldw, int E, const float* 
         const int np = n_pairs - p0 < per ? n_pairs - p0 : per;
         hipLaunchKernelGGL((k_id_q6<F, LPR, WAVES>), dim3((unsigned)tiles, (unsigned)np), dim3(WAVES * 64),
                            q6_xs_bytes(K), st, W, es, ldw, E, X + (size_t)(p0 / top_k) * ldx, ldx, ids + p0, top_k,
-                           Y + (size_t)p0 * ldy, ldy, N, K, sc, err);
+                           Y + (size_t)p0 * ldy, ldy, N, K, sc, err, ax.S, ax.B, ax.s_estride, ax.lds);
         const int rc = check_launch("qmv_id super-block kernel");
         if (rc) return rc;
     }
@@ -2698,10 +2810,11 @@ int launch_id_q6_t(const uint8_t* W, size_t es, size_t ldw, int E, const float* 
 template <class F>
 int launch_id_kq(const uint8_t* W, size_t es, size_t ldw, int E, const float* X, size_t ldx, const uint32_t* ids,
                  int n_pairs, int top_k, float* Y, size_t ldy, int N, int K, const float* sc, int* err,
-                 hipStream_t st) {
-    const int lpr = pick_lpr_q6(K / 128);
-#define QMV_IDQ6_CASE(L) \
-    if (lpr == L) return launch_id_q6_t<F, L>(W, es, ldw, E, X, ldx, ids, n_pairs, top_k, Y, ldy, N, K, sc, err, st);
+                 hipStream_t st, const AuxArgs& ax = AuxArgs{}) {
+    const int lpr = pick_lpr_q6(F::units(K));
+#define QMV_IDQ6_CASE(L)                                                                                            \
+    if (lpr == L)                                                                                                   \
+        return launch_id_q6_t<F, L>(W, es, ldw, E, X, ldx, ids, n_pairs, top_k, Y, ldy, N, K, sc, err, st, ax);
     QMV_IDQ6_CASE(64) QMV_IDQ6_CASE(32) QMV_IDQ6_CASE(16) QMV_IDQ6_CASE(8) QMV_IDQ6_CASE(4)
 #undef QMV_IDQ6_CASE
     return fail(QMV_EINVAL, "internal: no super-block id kernel for lpr=%d", lpr);
@@ -2717,11 +2830,11 @@ int launch_id_q6(const uint8_t* W, size_t es, size_t ldw, int E, const float* X,
 // Rows of X in launches of up to 4 (one launch when M = 1).
 template <class F>
 int launch_q6k(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N, int K,
-               int lpr, int wgs_per_cu, hipStream_t st) {
+               int lpr, int wgs_per_cu, hipStream_t st, const AuxArgs& ax = AuxArgs{}) {
     if (lpr <= 0) {
         // widen the lane groups of short calls until every compute unit has
         // a tile (5760 rows at 8 lanes per row are 90 tiles of 64 rows)
-        lpr = pick_lpr_q6(K / 128);
+        lpr = pick_lpr_q6(F::units(K));
         while (lpr < 64 && ((long)N + (64 / lpr) * 8 - 1) / ((64 / lpr) * 8) < num_cus()) lpr *= 2;
     }
     for (int m0 = 0; m0 < M; m0 += 4) {
@@ -2731,8 +2844,8 @@ int launch_q6k(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* 
         int rc = QMV_EINVAL;
 #define QMV_Q6_CASE(L)                                                                                   \
     if (lpr == L)                                                                                        \
-        rc = nx == 1 ? launch_q6k_t<F, L, 8, 1>(W, ldw, Xm, ldx, Ym, ldy, 1, N, K, wgs_per_cu, st)       \
-                     : launch_q6k_t<F, L, 8, 4>(W, ldw, Xm, ldx, Ym, ldy, nx, N, K, wgs_per_cu, st);
+        rc = nx == 1 ? launch_q6k_t<F, L, 8, 1>(W, ldw, Xm, ldx, Ym, ldy, 1, N, K, wgs_per_cu, st, ax)   \
+                     : launch_q6k_t<F, L, 8, 4>(W, ldw, Xm, ldx, Ym, ldy, nx, N, K, wgs_per_cu, st, ax);
         QMV_Q6_CASE(64) QMV_Q6_CASE(32) QMV_Q6_CASE(16) QMV_Q6_CASE(8) QMV_Q6_CASE(4)
 #undef QMV_Q6_CASE
         if (rc) return rc == QMV_EINVAL ? fail(QMV_EINVAL, "internal: no super-block kernel for lpr=%d", lpr) : rc;
@@ -2859,6 +2972,79 @@ int qmv_gemm(int qtype, const void* Wv, size_t ldw, const float* X, size_t ldx, 
         if (rc) return rc;
     }
     return QMV_OK;
+}
+
+int qmv_affine4(const uint32_t* Wq, size_t ldw, const uint16_t* scales, const uint16_t* biases, size_t lds,
+                const float* X, size_t ldx, float* Y, size_t ldy, int M, int N, int K, void* stream) {
+    const char* name = "qmv_affine4";
+    if (M < 0 || M > QMV_MAX_M) return fail(QMV_EUNSUPPORTED, "%s: M=%d outside 0..%d", name, M, QMV_MAX_M);
+    if (N < 0) return fail(QMV_EINVAL, "%s: N=%d < 0", name, N);
+    if (K < 0 || K % 32) return fail(QMV_EINVAL, "%s: K=%d is not a non-negative multiple of 32", name, K);
+    if (M == 0 || N == 0) return QMV_OK;
+    if (K == 0) return fail(QMV_EUNSUPPORTED, "%s: K=0", name);
+    if (K > KMAX_Q6) return fail(QMV_EUNSUPPORTED, "%s: K=%d exceeds %d", name, K, KMAX_Q6);
+    if (!Wq || !scales || !biases || !X || !Y) return fail(QMV_EINVAL, "%s: NULL argument", name);
+    if (ldw < (size_t)K / 8) return fail(QMV_EINVAL, "%s: ldw=%zu words < K/8=%d", name, ldw, K / 8);
+    if (lds < (size_t)K / 32) return fail(QMV_EINVAL, "%s: lds=%zu < K/32=%d", name, lds, K / 32);
+    if (M > 1 && ldx < (size_t)K) return fail(QMV_EINVAL, "%s: ldx=%zu < K=%d", name, ldx, K);
+    if (M > 1 && ldy < (size_t)N) return fail(QMV_EINVAL, "%s: ldy=%zu < N=%d", name, ldy, N);
+    if (((uintptr_t)Wq & 3) || ((uintptr_t)X & 3) || ((uintptr_t)Y & 3) || ((uintptr_t)scales & 1) ||
+        ((uintptr_t)biases & 1))
+        return fail(QMV_EALIGN, "%s: Wq, X and Y must be 4-byte aligned, scales and biases 2-byte", name);
+    if (M == 1) ldx = (size_t)K, ldy = (size_t)N;
+    if ((size_t)N > SIZE_MAX / 4 / (ldw > lds ? ldw : lds)) return fail(QMV_EINVAL, "%s: N*ldw overflows", name);
+    const size_t ybytes = ((size_t)(M - 1) * ldy + N) * 4;
+    const size_t sbytes = ((size_t)(N - 1) * lds + K / 32) * 2;
+    if (overlaps(Y, ybytes, Wq, ((size_t)(N - 1) * ldw + K / 8) * 4) || overlaps(Y, ybytes, X, ((size_t)(M - 1) * ldx + K) * 4) ||
+        overlaps(Y, ybytes, scales, sbytes) || overlaps(Y, ybytes, biases, sbytes))
+        return fail(QMV_EINVAL, "%s: Y overlaps an input", name);
+    AuxArgs ax;
+    ax.S = scales, ax.B = biases, ax.lds = lds;
+    return launch_q6k<FmtA4>((const uint8_t*)Wq, ldw * 4, X, ldx, Y, ldy, M, N, K, 0, 0, (hipStream_t)stream, ax);
+}
+
+int qmv_affine4_id(const uint32_t* Wq, size_t expert_stride_words, size_t ldw, const uint16_t* scales,
+                   const uint16_t* biases, size_t expert_stride_groups, size_t lds, int n_experts, const float* X,
+                   size_t ldx, const uint32_t* ids, int n_tokens, int top_k, float* Y, size_t ldy, int N, int K,
+                   const float* expert_scale, int* err_flag, void* stream) {
+    const char* name = "qmv_affine4_id";
+    if (n_experts <= 0) return fail(QMV_EINVAL, "%s: n_experts=%d must be > 0", name, n_experts);
+    if (top_k <= 0) return fail(QMV_EINVAL, "%s: top_k=%d must be > 0", name, top_k);
+    if (n_tokens < 0) return fail(QMV_EINVAL, "%s: n_tokens=%d < 0", name, n_tokens);
+    if (N < 0) return fail(QMV_EINVAL, "%s: N=%d < 0", name, N);
+    if (K < 0 || K % 32) return fail(QMV_EINVAL, "%s: K=%d is not a non-negative multiple of 32", name, K);
+    if ((long)n_tokens * top_k > 0x7FFFFFFFL) return fail(QMV_EINVAL, "%s: n_tokens*top_k overflows", name);
+    if (n_tokens == 0 || N == 0) return QMV_OK;
+    if (K == 0) return fail(QMV_EUNSUPPORTED, "%s: K=0", name);
+    if (K > KMAX_Q6) return fail(QMV_EUNSUPPORTED, "%s: K=%d exceeds %d", name, K, KMAX_Q6);
+    if (!Wq || !scales || !biases || !X || !ids || !Y) return fail(QMV_EINVAL, "%s: NULL argument", name);
+    if (ldw < (size_t)K / 8) return fail(QMV_EINVAL, "%s: ldw=%zu words < K/8=%d", name, ldw, K / 8);
+    if (lds < (size_t)K / 32) return fail(QMV_EINVAL, "%s: lds=%zu < K/32=%d", name, lds, K / 32);
+    if ((size_t)N > SIZE_MAX / 4 / (ldw > lds ? ldw : lds)) return fail(QMV_EINVAL, "%s: N*ldw overflows", name);
+    if (expert_stride_words < (size_t)N * ldw)
+        return fail(QMV_EINVAL, "%s: expert_stride_words=%zu < N*ldw", name, expert_stride_words);
+    if (expert_stride_groups < (size_t)N * lds)
+        return fail(QMV_EINVAL, "%s: expert_stride_groups=%zu < N*lds", name, expert_stride_groups);
+    if (ldx < (size_t)K) return fail(QMV_EINVAL, "%s: ldx=%zu < K=%d", name, ldx, K);
+    if (ldy < (size_t)N) return fail(QMV_EINVAL, "%s: ldy=%zu < N=%d", name, ldy, N);
+    if (((uintptr_t)Wq & 3) || ((uintptr_t)X & 3) || ((uintptr_t)Y & 3) || ((uintptr_t)ids & 3) ||
+        ((uintptr_t)expert_scale & 3) || ((uintptr_t)err_flag & 3) || ((uintptr_t)scales & 1) ||
+        ((uintptr_t)biases & 1))
+        return fail(QMV_EALIGN, "%s: Wq, X, Y, ids, expert_scale, err_flag 4-byte, scales and biases 2-byte", name);
+    const int n_pairs = n_tokens * top_k;
+    const size_t ybytes = ((size_t)(n_pairs - 1) * ldy + N) * 4;
+    const size_t wbytes = ((size_t)(n_experts - 1) * expert_stride_words + (size_t)(N - 1) * ldw + K / 8) * 4;
+    const size_t sbytes = ((size_t)(n_experts - 1) * expert_stride_groups + (size_t)(N - 1) * lds + K / 32) * 2;
+    if (overlaps(Y, ybytes, Wq, wbytes) || overlaps(Y, ybytes, X, ((size_t)(n_tokens - 1) * ldx + K) * 4) ||
+        overlaps(Y, ybytes, scales, sbytes) || overlaps(Y, ybytes, biases, sbytes) ||
+        overlaps(Y, ybytes, ids, (size_t)n_pairs * 4) ||
+        overlaps(Y, ybytes, expert_scale, expert_scale ? (size_t)n_experts * 4 : 0) ||
+        overlaps(Y, ybytes, err_flag, err_flag ? 4 : 0))
+        return fail(QMV_EINVAL, "%s: Y overlaps another argument", name);
+    AuxArgs ax;
+    ax.S = scales, ax.B = biases, ax.lds = lds, ax.s_estride = expert_stride_groups;
+    return launch_id_kq<FmtA4>((const uint8_t*)Wq, expert_stride_words * 4, ldw * 4, n_experts, X, ldx, ids, n_pairs,
+                               top_k, Y, ldy, N, K, expert_scale, err_flag, (hipStream_t)stream, ax);
 }
 
 int qmv_moe_wsum(const float* Y, size_t ldy, const float* weights, int n_tokens, int top_k, int N, float* out,

@@ -58,6 +58,10 @@ def lib() -> ctypes.CDLL:
         L.qmv_moe_wsum.argtypes = [P, S, P, I, I, I, P, S, P]
         L.qmv_moe_down.restype = I
         L.qmv_moe_down.argtypes = [I, P, S, S, I, P, S, P, P, I, I, P, S, I, I, P, P, P]
+        L.qmv_affine4.restype = I
+        L.qmv_affine4.argtypes = [P, S, P, P, S, P, S, P, S, I, I, I, P]
+        L.qmv_affine4_id.restype = I
+        L.qmv_affine4_id.argtypes = [P, S, S, P, P, S, S, I, P, S, P, I, I, P, S, I, I, P, P, P]
         L.qmv_gemm.restype = I
         L.qmv_gemm.argtypes = [I, P, S, P, S, P, S, I, I, I, P]
         L.qmv_batch.restype = I
@@ -185,6 +189,36 @@ def qmv_gemm(qtype, W, X, Y, K: Optional[int] = None, stream=None) -> None:
         raise ValueError("X [M, K] and Y [M, N] need unit inner stride and matching M, N")
     _check(raw_qmv_gemm(q, _ptr(W), W.stride(0), _ptr(X), X.stride(0), _ptr(Y), Y.stride(0), M, N, K,
                         _stream(stream)))
+
+
+def raw_qmv_affine4(Wq, ldw, S, B, lds, X, ldx, Y, ldy, M, N, K, stream=0) -> int:
+    return lib().qmv_affine4(Wq, ldw, S, B, lds, X, ldx, Y, ldy, M, N, K, stream)
+
+
+def qmv_affine4(Wq, S, B, X, Y, stream=None) -> None:
+    """Affine 4-bit product (see include/qmv.h): Wq int32/uint32 [N, >= K/8],
+    S, B int16/uint16 bf16 bit patterns [N, >= K/32], X fp32 [M, K] or [K],
+    Y fp32 [M, N] or [N]."""
+    x2 = X if X.dim() == 2 else X.view(1, -1)
+    y2 = Y if Y.dim() == 2 else Y.view(1, -1)
+    M, K = x2.shape
+    N = Wq.shape[0]
+    if Wq.stride(1) != 1 or S.stride(1) != 1 or B.stride(1) != 1 or S.stride(0) != B.stride(0):
+        raise ValueError("Wq, S and B need contiguous rows; S and B one row stride")
+    _check(raw_qmv_affine4(_ptr(Wq), Wq.stride(0), _ptr(S), _ptr(B), S.stride(0), _ptr(x2), x2.stride(0), _ptr(y2),
+                           y2.stride(0), M, N, K, _stream(stream)))
+
+
+def qmv_affine4_id(Wq, S, B, X, ids, Y, N: int, K: int, expert_scale=None, err_flag=None, stream=None) -> None:
+    """Expert-indexed affine 4-bit product: Wq [E, N, >= K/8] words, S, B [E, N, >= K/32]
+    bf16 bit patterns, X fp32 [n_tokens, K], ids [n_tokens, top_k], Y fp32 [n_tokens*top_k, N]."""
+    ids2 = ids if ids.dim() == 2 else ids.view(-1, 1)
+    n_tokens, top_k = ids2.shape
+    if S.stride() != B.stride() or Wq.stride(2) != 1 or S.stride(2) != 1 or not ids2.is_contiguous():
+        raise ValueError("S and B need one layout, contiguous rows; ids contiguous")
+    _check(lib().qmv_affine4_id(_ptr(Wq), Wq.stride(0), Wq.stride(1), _ptr(S), _ptr(B), S.stride(0), S.stride(1),
+                                Wq.shape[0], _ptr(X), X.stride(0), _ptr(ids2), n_tokens, top_k, _ptr(Y), Y.stride(0),
+                                N, K, _ptr(expert_scale), _ptr(err_flag), _stream(stream)))
 
 
 def qmv_id(qtype, W, X, ids, Y, N: int, K: int, expert_scale=None, err_flag=None, stream=None) -> None:

@@ -182,6 +182,39 @@ int qmv_gemm(int qtype, const void* W, size_t ldw_bytes, const float* X, size_t 
              int M, int N, int K, void* stream);
 
 /*
+ * qmv_affine4 — Y = deq(W) X^T for MLX affine 4-bit weights, groups of 32.
+ *
+ * The gemma4 model page builds its DWQ MoE stacks this way: each row's codes
+ * packed eight to a 32-bit word, code j of a word in bits 4j..4j+3, and one
+ * bf16 scale and one bf16 bias per group of 32 weights in arrays of their
+ * own (the `MlxAffineMoeStack` weight, scales and biases buffers, bits = 4,
+ * group_size = 32). The pages call the format affine and store a bias per
+ * group; the dequantization taken is w = scale * q + bias, q = 0..15.
+ *
+ *  Wq       device uint32, row n at Wq + n*ldw (ldw in words, >= K/8),
+ *           4-byte aligned.
+ *  scales, biases  device bf16 bit patterns, row n at + n*lds (lds >= K/32),
+ *           2-byte aligned.
+ *  K        a positive multiple of 32, at most 16384 (rows need not hold a
+ *           multiple of 128 weights).
+ *  Other arguments as qmv_q4_0 (M 0..16).
+ */
+int qmv_affine4(const uint32_t* Wq, size_t ldw, const uint16_t* scales, const uint16_t* biases, size_t lds,
+                const float* X, size_t ldx, float* Y, size_t ldy, int M, int N, int K, void* stream);
+
+/*
+ * qmv_affine4_id — the expert-indexed product (qmv_id's mapping and error
+ * behaviour) over stacked affine 4-bit experts: expert e's words start at
+ * Wq + e*expert_stride_words, its scales and biases at
+ * + e*expert_stride_groups. Each (token, slot) pair reads its expert's rows.
+ */
+int qmv_affine4_id(const uint32_t* Wq, size_t expert_stride_words, size_t ldw, const uint16_t* scales,
+                   const uint16_t* biases, size_t expert_stride_groups, size_t lds, int n_experts,
+                   const float* X, size_t ldx, const uint32_t* ids, int n_tokens, int top_k,
+                   float* Y, size_t ldy, int N, int K, const float* expert_scale, int* err_flag,
+                   void* stream);
+
+/*
  * qmv_id — expert-indexed product over a stack of weight matrices.
  *
  * For t < n_tokens and s < top_k, with p = t*top_k + s and e = ids[p]:

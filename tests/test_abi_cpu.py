@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert {"qmv_q4_0", "qmv_q8_0", "qmv_q5_k", "qmv_q6_k", "qmv_gemm", "qmv_id", "qmv_id_swiglu", "qmv_moe_wsum", "qmv_moe_down",
+    assert {"qmv_q4_0", "qmv_q8_0", "qmv_q5_k", "qmv_q6_k", "qmv_gemm", "qmv_affine4", "qmv_affine4_id", "qmv_id", "qmv_id_swiglu", "qmv_moe_wsum", "qmv_moe_down",
             "qmv_batch", "qmv_last_error"} <= set(names)
     L = ctypes.CDLL(qmv.LIB_PATH)
     for n in names:
@@ -264,3 +264,26 @@ def test_gemm_argument_checks(args, status, msg):
 
 def test_gemm_empty_is_a_no_op():
     assert qmv.raw_qmv_gemm(Q4, 0, 0, 0, 0, 0, 0, 0, 16, 128) == qmv.QMV_OK
+
+
+def _a4(**kw):
+    a = dict(Wq=W, ldw=88, S=X, B=X + 4096, lds=22, X=Y, ldx=704, Y=0x40000000, ldy=16, M=1, N=16, K=704)
+    a.update(kw)
+    return qmv.raw_qmv_affine4(a["Wq"], a["ldw"], a["S"], a["B"], a["lds"], a["X"], a["ldx"], a["Y"], a["ldy"],
+                               a["M"], a["N"], a["K"])
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(K=700), qmv.QMV_EINVAL, "multiple of 32"),
+    (dict(ldw=87), qmv.QMV_EINVAL, "ldw"),
+    (dict(lds=21), qmv.QMV_EINVAL, "lds"),
+    (dict(M=17), qmv.QMV_EUNSUPPORTED, "M=17"),
+    (dict(K=16416, ldw=2052, lds=513, ldx=16416), qmv.QMV_EUNSUPPORTED, "exceeds"),
+    (dict(Wq=W + 2), qmv.QMV_EALIGN, "aligned"),
+    (dict(S=X + 1), qmv.QMV_EALIGN, "aligned"),
+    (dict(Y=X + 8), qmv.QMV_EINVAL, "overlaps"),
+    (dict(B=0), qmv.QMV_EINVAL, "NULL"),
+])
+def test_affine4_argument_checks(kw, status, msg):
+    assert _a4(**kw) == status
+    assert msg in qmv.last_error()
