@@ -422,7 +422,7 @@ def summarize(stats_dir, fetch_dir, write_dir, cmd_note):
     out = []
     stats = rows(stats_dir, "*kernel_stats.csv")
     for r in stats:
-        if "k_m1b" in r["Name"] or "copy" in r["Name"].lower() or "k_generic" in r["Name"]:
+        if "k_m1" in r["Name"] or "copy" in r["Name"].lower() or "k_generic" in r["Name"]:
             out.append(f"{r['Name'][:90]:90s} calls={r['Calls']:>6s} avg_ns={float(r['AverageNs']):10.1f} "
                        f"min_ns={float(r['MinNs']):10.1f} max_ns={float(r['MaxNs']):10.1f}")
 
@@ -432,7 +432,7 @@ def summarize(stats_dir, fetch_dir, write_dir, cmd_note):
             if r["Counter_Name"] != name:
                 continue
             k = r["Kernel_Name"]
-            if "k_m1b" in k:
+            if "k_m1" in k:
                 per["qmv"].append(float(r["Counter_Value"]))
             elif "MulFunctor" in k or "copyBuffer" in k:
                 per["copy"].append(float(r["Counter_Value"]))
@@ -462,7 +462,7 @@ def summarize(stats_dir, fetch_dir, write_dir, cmd_note):
             json.dump(res, f, indent=1)
     text = "\n".join([f"# qmv decode-layer set (Q4_0, M=1, hidden 4096), kernel source {kernel_hash()}",
                       f"# command: {cmd_note}", *out]) + "\n"
-    with open(os.path.join(ROOT, "profiles", "k_m1b_decode_layer_h4096.txt"), "w") as f:
+    with open(os.path.join(ROOT, "profiles", "k_m1c_decode_layer_h4096.txt"), "w") as f:
         f.write(text)
     print(text)
 
@@ -545,7 +545,7 @@ def main():
     traffic = read_traffic(per_launch)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "k_m1b (qmv_batch, M=1)", "launches_per_step": len(GROUPS),
+                "kernel": "k_m1c (qmv_batch, M=1)", "launches_per_step": len(GROUPS),
                 "avg_launch_us": round(avg_launch * 1e6, 3),
                 "algorithmic_bytes_per_launch": round(per_launch)}
 

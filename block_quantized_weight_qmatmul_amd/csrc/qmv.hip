@@ -20,6 +20,9 @@
 //     v_cvt_off_f32_i4 on (byte ^ 0x88), which yields (code - 8) / 16 exactly;
 //     the 1/16 is undone once per output. A row's partial sums are reduced
 //     across its LPR lanes with DPP moves.
+//   * k_m1c          — the batched M = 1 call when all problems share x and K
+//     (a layer's Q/K/V, its gate/up): their rows form one virtual matrix of
+//     tiles that every workgroup strides through, so the work is even.
 //   * k_xprep + k_mm4 (+ k_mmred) — Q4_0 with M = 2..16 on the matrix cores
 //     (v_mfma_f32_16x16x32_f16): the activations are converted once per call
 //     into fp16 hi/lo operands, then 16-row weight tiles are contracted with
@@ -507,6 +510,112 @@ __global__ __launch_bounds__(WAVES * 64) void k_m1b(const M1Batch B) {
         case 16: m1_stream<QT, 16, 1, WAVES>(W, ldw, x, y, N, K, lw, nwg, OS, xs); break;
         case 8: m1_stream<QT, 8, 1, WAVES>(W, ldw, x, y, N, K, lw, nwg, OS, xs); break;
         default: m1_stream<QT, 4, 1, WAVES>(W, ldw, x, y, N, K, lw, nwg, OS, xs); break;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Batched M = 1 kernel for problems that share one activation vector (the
+// Q/K/V projections of a layer, or its FFN gate and up): the rows of all
+// problems form one virtual matrix of tiles (problem p owns global tiles
+// t0[p] .. t0[p+1]-1; a tile never spans two problems) and every workgroup
+// takes tiles blockIdx.x, blockIdx.x + gridDim.x, ... of it, so the work is
+// spread evenly whatever the problems' sizes, and x is staged once per
+// workgroup. The loop is m1_stream's with one row per lane group.
+// ---------------------------------------------------------------------------
+struct M1Cat {
+    const uint8_t* W[MAXB];
+    float* y[MAXB];
+    size_t ldw[MAXB];
+    int N[MAXB];
+    long t0[MAXB + 1];
+    const float* x;
+    int K, n;
+};
+
+template <int QT, int LPR, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void k_m1c(const M1Cat C) {
+    extern __shared__ __align__(16) float xs[];
+    using T = PairTraits<QT>;
+    constexpr int DW = T::DW, PB = DW * 4;
+    constexpr int GROUPS = 64 / LPR;
+    constexpr int ROWS = GROUPS * WAVES;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane / LPR, j = lane % LPR;
+    const int K = C.K;
+    const int P = K >> 6;
+    const int IPT = (P + LPR - 1) / LPR;
+    const long ntiles = C.t0[C.n];
+    const long lrow = (long)(wave * GROUPS + g);
+    const long stride = gridDim.x;
+    long tile = blockIdx.x;
+    if (tile >= ntiles) return;  // uniform over the workgroup
+    // The parameters of the problem whose tile is being loaded (i*) and of
+    // the one whose tile is being summed (s*) live in registers; the kernel
+    // arguments are read again only when the loaded tile crosses into the
+    // next problem.
+    int ip = 0;
+    while (tile >= C.t0[ip + 1]) ++ip;
+    const uint8_t* iW = C.W[ip];
+    size_t ildw = C.ldw[ip];
+    int iN = C.N[ip];
+    long it0 = C.t0[ip], inext = C.t0[ip + 1];
+    float* sy = C.y[ip];
+    int sN = iN;
+    long st0 = it0;
+    int it = 0;
+    uint32_t nxt[DW];
+    auto issue = [&](long tl, int i) {
+        const long row = (tl - it0) * ROWS + lrow;
+        const long rr = row < iN ? row : iN - 1;
+        int p = j + i * LPR;
+        p = p < P ? p : P - 1;
+        load_pair<DW>(iW + rr * ildw + (size_t)p * PB, nxt);
+    };
+    {
+        constexpr int XCH = (KMAX_STAGE / 4 + WAVES * 64 - 1) / (WAVES * 64);
+        f32x4u_t xv[XCH];
+        stage_x_load<WAVES * 64, XCH>(xv, C.x, K);
+        issue(tile, 0);
+        stage_x_store<WAVES * 64, XCH>(xs, xv, K);
+        lds_barrier();
+    }
+    float tot = 0.f;
+    while (true) {
+        uint32_t cur[DW];
+#pragma unroll
+        for (int d = 0; d < DW; ++d) cur[d] = nxt[d];
+        const int p = j + it * LPR;
+        int it2 = it + 1;
+        long tile2 = tile;
+        if (it2 == IPT) {
+            it2 = 0;
+            tile2 += stride;
+            if (tile2 >= inext && tile2 < ntiles) {
+                while (tile2 >= C.t0[ip + 1]) ++ip;
+                iW = C.W[ip];
+                ildw = C.ldw[ip];
+                iN = C.N[ip];
+                it0 = C.t0[ip];
+                inext = C.t0[ip + 1];
+            }
+        }
+        const bool more = tile2 < ntiles;
+        if (more) issue(tile2, it2);
+        if (p < P) tot += T::dot(cur, reinterpret_cast<const float4*>(xs + p * XS_PAIR));
+        if (it == IPT - 1) {
+            const long row = (tile - st0) * ROWS + lrow;
+            const float sum = lane_group_sum<LPR>(tot);
+            if (j == LPR - 1 && row < sN) sy[row] = sum * T::OUT_SCALE;
+            tot = 0.f;
+        }
+        if (!more) break;
+        if (it2 == 0) {  // the next step starts the tile just issued
+            sy = C.y[ip];
+            sN = iN;
+            st0 = it0;
+        }
+        tile = tile2;
+        it = it2;
     }
 }
 
@@ -2273,10 +2382,52 @@ bool m1b_eligible(const uint8_t* W, size_t ldw, const float* x, int K) {
 
 // Launch the batched M = 1 kernel over n problems (n <= MAXB), all eligible.
 // wgs_per_cu and waves are tuning knobs (0 = default).
+template <int QT, int LPR>
+int launch_m1c_t(const M1Cat& C, long tiles, int wgs_per_cu, hipStream_t st) {
+    const size_t lds = xs_bytes(C.K);
+    long per_cu = (long)(LDS_PER_CU / (lds ? lds : 1));
+    per_cu = per_cu < 1 ? 1 : (per_cu < wgs_per_cu ? per_cu : wgs_per_cu);
+    long grid = (long)num_cus() * per_cu;
+    grid = grid < tiles ? grid : tiles;
+    hipLaunchKernelGGL((k_m1c<QT, LPR, 8>), dim3((unsigned)grid), dim3(512), lds, st, C);
+    return check_launch("qmv shared-input batched m1 kernel");
+}
+
+// Problems that share x and K: one virtual matrix of 8-row tiles (k_m1c).
+template <int QT>
+int launch_m1c(const M1Prob* probs, int n, int wgs_per_cu, hipStream_t st) {
+    M1Cat C;
+    C.x = probs[0].x;
+    C.K = probs[0].K;
+    C.n = n;
+    const int lpr = pick_lpr(C.K / 64);
+    const long rows = (long)(64 / lpr) * 8;
+    C.t0[0] = 0;
+    for (int i = 0; i < n; ++i) {
+        C.W[i] = probs[i].W;
+        C.y[i] = probs[i].y;
+        C.ldw[i] = probs[i].ldw;
+        C.N[i] = probs[i].N;
+        C.t0[i + 1] = C.t0[i] + ((long)probs[i].N + rows - 1) / rows;
+    }
+    const long tiles = C.t0[n];
+    if (tiles > 0x7FFFFFFF) return fail(QMV_EINVAL, "N too large");
+    switch (lpr) {
+        case 64: return launch_m1c_t<QT, 64>(C, tiles, wgs_per_cu, st);
+        case 32: return launch_m1c_t<QT, 32>(C, tiles, wgs_per_cu, st);
+        case 16: return launch_m1c_t<QT, 16>(C, tiles, wgs_per_cu, st);
+        case 8: return launch_m1c_t<QT, 8>(C, tiles, wgs_per_cu, st);
+        default: return launch_m1c_t<QT, 4>(C, tiles, wgs_per_cu, st);
+    }
+}
+
 template <int QT>
 int launch_m1b(const M1Prob* probs, int n, int wgs_per_cu, int waves, hipStream_t st) {
     if (waves == 0) waves = 8;
     if (wgs_per_cu == 0) wgs_per_cu = 2;
+    bool shared = waves == 8;
+    for (int i = 1; i < n; ++i) shared = shared && probs[i].x == probs[0].x && probs[i].K == probs[0].K;
+    if (shared) return launch_m1c<QT>(probs, n, wgs_per_cu, st);
     M1Batch B;
     B.n = 0;
     size_t lds = 0;

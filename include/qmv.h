@@ -339,7 +339,9 @@ int qmv_moe_down(int qtype, const void* W, size_t expert_stride_bytes, size_t ld
  * encode Q, K and V (which share one input) as one concurrent group, and
  * the FFN gate, up and router as another (`encode_one_layer`, the barrier
  * groups before the first and the ninth block of dispatches). Problems may
- * share x; their outputs must not overlap each other or any W or x.
+ * share x; their outputs must not overlap each other or any W or x. When
+ * every problem reads the same x pointer with the same K, their rows are
+ * streamed as one matrix (the results equal the single calls' bit for bit).
  *
  *  qtype        QMV_Q4_0 or QMV_Q8_0 (all problems of a batch have one type).
  *  problems     HOST array of n_problems descriptors, read during the call.

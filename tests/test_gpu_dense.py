@@ -247,6 +247,42 @@ def test_batch_decode_layer_set_against_oracle(qtype):
         assert_within_tol(y.cpu().numpy()[None, :], yo, a, f"batch {p.name}")
 
 
+SHARED_GROUPS = {
+    # name: (K, [N per problem]) -- every problem of a group reads one x
+    "qkv_h4096": (4096, [4096, 1024, 1024]),
+    "gate_up_h4096": (4096, [14336, 14336]),
+    "ragged_k2816": (2816, [5, 300, 13, 1, 64, 7]),
+    "sixteen_k704": (704, [3 + 17 * i for i in range(16)]),
+    "down_k14336": (14336, [1000, 24]),
+}
+
+
+@pytest.mark.parametrize("qtype", ["q4_0", "q8_0"])
+@pytest.mark.parametrize("group", sorted(SHARED_GROUPS))
+def test_batch_shared_input_groups(qtype, group):
+    """Problems that share one x (a layer's Q/K/V, its gate/up) stream as one
+    virtual matrix of row tiles; ragged row counts end tiles early, a tile
+    never spans two problems."""
+    K, Ns = SHARED_GROUPS[group]
+    X = synth.make_x(1, K, cfg=81, part=0)
+    xd = torch.from_numpy(X[0]).to(DEV)
+    host, dev = [], []
+    for i, N in enumerate(Ns):
+        W = synth.make_weights(qtype, N, K, cfg=81, part=i + 1)
+        host.append(W)
+        dev.append((torch.from_numpy(W).to(DEV), xd, torch.full((N,), np.nan, device=DEV)))
+    qmv.qmv_batch(qtype, dev)
+    torch.cuda.synchronize()
+    for i, (W, (_, _, y)) in enumerate(zip(host, dev)):
+        yo, a = oracle.qmv(qtype, W, X)
+        assert_within_tol(y.cpu().numpy()[None, :], yo, a, f"{group} problem {i}")
+        # the same rows through the single-problem call, bit for bit
+        ys = torch.full((W.shape[0],), np.nan, device=DEV)
+        FN[qtype](dev[i][0], xd[None, :], ys[None, :])
+        torch.cuda.synchronize()
+        assert torch.equal(ys, y), f"{group} problem {i}: batch differs from the single call"
+
+
 def test_batch_mixed_fast_and_fallback_problems():
     """Problems the fast kernel takes and ones it does not (odd blocks per
     row, 2-byte row stride, K = 0) in one call."""
