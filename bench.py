@@ -163,6 +163,35 @@ def m16_throughput(dev, steps=40):
             "pct_hbm_peak": round(100 * nbytes / t / 1e9 / HBM_PEAK_GBS, 2)}
 
 
+def dense_m1_throughput(dev, cfg, steps=400):
+    """One-problem M = 1 calls of a dense config (0: Q4_0 2048 -> 2048; 2:
+    Q8_0 4096 -> 14336 and 14336 -> 4096), each timed on its own: a step is
+    one call, steps rotate over enough device copies of the weights to fill
+    >= 1.1 GB (beyond the Infinity Cache), several steps per graph replay.
+    The copies hold one seeded weight tensor each (the data does not change
+    the time; distinct buffers keep every call streaming from HBM)."""
+    import torch
+
+    from block_quantized_weight_qmatmul_amd import qmv, synth
+    fn = {"q4_0": qmv.qmv_q4_0, "q8_0": qmv.qmv_q8_0}
+    out = {"workload": synth.CONFIGS[cfg]["name"]}
+    for part, p in enumerate(synth.CONFIGS[cfg]["problems"]):
+        W, X = synth.dense_inputs(cfg, p, part)
+        R = max(4, -(-int(1.1e9) // p.weight_bytes))
+        Wd = torch.from_numpy(W).to(dev)
+        Xd = torch.from_numpy(X).to(dev)
+        sets = [(Wd if r == 0 else Wd.clone(), Xd if r == 0 else Xd.clone(), torch.empty((1, p.N), device=dev))
+                for r in range(R)]
+        t = time_steps(lambda s: fn[p.qtype](s[0], s[1], s[2]), sets, steps, 2 * R)
+        us = t / steps * 1e6
+        out[p.name] = {"N": p.N, "K": p.K, "weight_bytes": p.weight_bytes, "rotated_copies": R,
+                       "us_per_call": round(us, 2), "GBps": round(p.weight_bytes / us / 1e3, 1),
+                       "pct_hbm_peak": round(100 * p.weight_bytes / us / 1e3 / HBM_PEAK_GBS, 2)}
+        del sets, Wd, Xd
+        torch.cuda.empty_cache()
+    return out
+
+
 def moe_throughput(dev, T, steps=40, mode="id"):
     """Config 4 (Q4_0 MoE, 128 experts, top-8, hidden 2816, expert
     intermediate 704) for T tokens over rotated stacks (16 for T = 1, 4 for
@@ -565,6 +594,8 @@ def main():
                         args.warmup)
         extra["layer_set_one_launch_GBps"] = round(nbytes * args.steps / t1 / 1e9, 1)
         extra["layer_set_seven_launches_GBps"] = round(nbytes * args.steps / t7 / 1e9, 1)
+        extra["q4_0_m1_2048x2048"] = dense_m1_throughput(dev, 0)
+        extra["q8_0_m1"] = dense_m1_throughput(dev, 2)
         extra["m16"] = m16_throughput(dev)
         extra["moe_t1"] = moe_throughput(dev, 1)
         extra["moe_t32"] = moe_throughput(dev, 32)
