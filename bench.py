@@ -79,6 +79,28 @@ def step_bytes():
     return sum(p.weight_bytes for p in synth.CONFIGS[1]["problems"])
 
 
+def fused_layer_set_throughput(sets, args):
+    """The layer-set step with Q/K/V stored as one [6144, 4096] matrix and
+    gate/up as one [28672, 4096] matrix (a loader may concatenate weights that
+    share an input): four single-matrix calls per step. Returns GB/s."""
+    import torch
+
+    from block_quantized_weight_qmatmul_amd import qmv
+    fused = []
+    for s in sets:
+        qkv = torch.cat([s["q"][0], s["k"][0], s["v"][0]])
+        gu = torch.cat([s["gate"][0], s["up"][0]])
+        fused.append({"qkv": (qkv, s["q"][1][None, :], torch.empty((1, qkv.shape[0]), device=qkv.device)),
+                      "o": (s["o"][0], s["o"][1][None, :], s["o"][2][None, :]),
+                      "gu": (gu, s["gate"][1][None, :], torch.empty((1, gu.shape[0]), device=gu.device)),
+                      "down": (s["down"][0], s["down"][1][None, :], s["down"][2][None, :])})
+    t = time_steps(lambda f: [qmv.qmv_q4_0(*f[n]) for n in ("qkv", "o", "gu", "down")], fused, args.steps,
+                   args.warmup)
+    del fused
+    torch.cuda.empty_cache()
+    return step_bytes() * args.steps / t / 1e9
+
+
 def time_steps(fn, sets, steps, warmup):
     """Wall time (s) of exactly `steps` steps after at least `warmup` untimed
     ones, bracketed by synchronizations and HIP events. Step i runs on
@@ -593,6 +615,7 @@ def main():
         t7 = time_steps(lambda s: [qmv.qmv_q4_0(s[n][0], s[n][1], s[n][2]) for n in names], sets, args.steps,
                         args.warmup)
         extra["layer_set_one_launch_GBps"] = round(nbytes * args.steps / t1 / 1e9, 1)
+        extra["layer_set_fused_qkv_gate_up_GBps"] = round(fused_layer_set_throughput(sets, args), 1)
         extra["layer_set_seven_launches_GBps"] = round(nbytes * args.steps / t7 / 1e9, 1)
         extra["q4_0_m1_2048x2048"] = dense_m1_throughput(dev, 0)
         extra["q8_0_m1"] = dense_m1_throughput(dev, 2)
