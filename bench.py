@@ -37,6 +37,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+WARMUP_S = 0.3  # minimum untimed warm-up per measurement, seconds
 METRIC = "effective weight GB/s and % of HBM peak, Q4_0 qmatmul at M=1 and M=16"
 KERNEL_SRC = os.path.join(ROOT, "block_quantized_weight_qmatmul_amd", "csrc", "qmv.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qmv_decode_layer_h4096.json")
@@ -101,6 +102,21 @@ def fused_layer_set_throughput(sets, args):
     return step_bytes() * args.steps / t / 1e9
 
 
+def warm_eager(fn):
+    """Call fn (which queues GPU work) until WARMUP_S seconds have passed,
+    synchronizing every few calls, so the GPU runs at its working clocks when
+    an eager timed region starts."""
+    import torch
+    t_end = time.perf_counter() + WARMUP_S
+    n = 0
+    while time.perf_counter() < t_end:
+        fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def time_steps(fn, sets, steps, warmup):
     """Wall time (s) of exactly `steps` steps after at least `warmup` untimed
     ones, bracketed by synchronizations and HIP events. Step i runs on
@@ -127,8 +143,17 @@ def time_steps(fn, sets, steps, warmup):
     full = build(chunk)
     part = build(steps % chunk) if steps % chunk else None
     torch.cuda.synchronize()
-    for _ in range((warmup + chunk - 1) // chunk):
+    # At least `warmup` steps, and at least WARMUP_S seconds of them: a GPU
+    # that has been idle runs the first ~0.1 s of work at lower clocks (the
+    # same 200 timed steps measured 6-8% slower after 20 warm-up steps than
+    # after 2000).
+    t_end = time.perf_counter() + WARMUP_S
+    n = 0
+    while n < (warmup + chunk - 1) // chunk or time.perf_counter() < t_end:
         full.replay()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -173,6 +198,12 @@ def m16_throughput(dev, steps=40):
     for a in args:
         step(a)
     torch.cuda.synchronize()
+    ctr = [0]
+
+    def nxt():
+        step(args[ctr[0] % 4])
+        ctr[0] += 1
+    warm_eager(nxt)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(steps):
@@ -350,6 +381,7 @@ def prefill_throughput(dev, M=512, steps=10):
             raise RuntimeError(qmv.last_error())
     run()
     torch.cuda.synchronize()
+    warm_eager(run)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(steps):
@@ -361,6 +393,7 @@ def prefill_throughput(dev, M=512, steps=10):
     Xh = X.to(torch.float16)
     Yh = torch.matmul(Xh, Wt)
     torch.cuda.synchronize()
+    warm_eager(lambda: torch.matmul(Xh, Wt, out=Yh))
     e0.record()
     for _ in range(steps):
         torch.matmul(Xh, Wt, out=Yh)
