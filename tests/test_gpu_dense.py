@@ -254,6 +254,9 @@ SHARED_GROUPS = {
     "ragged_k2816": (2816, [5, 300, 13, 1, 64, 7]),
     "sixteen_k704": (704, [3 + 17 * i for i in range(16)]),
     "down_k14336": (14336, [1000, 24]),
+    # row strides padded by 12 bytes (4-byte aligned) and by 2 bytes (the
+    # second problem then takes the generic kernel, the others the fast one)
+    "padded_k4096": (4096, [(100, 12), (37, 2), (513, 0)]),
 }
 
 
@@ -268,7 +271,8 @@ def test_batch_shared_input_groups(qtype, group):
     xd = torch.from_numpy(X[0]).to(DEV)
     host, dev = [], []
     for i, N in enumerate(Ns):
-        W = synth.make_weights(qtype, N, K, cfg=81, part=i + 1)
+        N, pad = N if isinstance(N, tuple) else (N, 0)
+        W = synth.make_weights(qtype, N, K, cfg=81, part=i + 1, ldw=synth.row_bytes(qtype, K) + pad)
         host.append(W)
         dev.append((torch.from_numpy(W).to(DEV), xd, torch.full((N,), np.nan, device=DEV)))
     qmv.qmv_batch(qtype, dev)
