@@ -2542,7 +2542,9 @@ int launch_mm4(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* 
                int force_S, int force_waves, hipStream_t st) {
     const int ncu = num_cus();
     const long tiles = ((long)N + 15) / 16;
-    const int waves = force_waves ? force_waves : 8;
+    // Few tiles (N <= 2048): 4-wave workgroups, twice as many of them
+    // (N = 1024, M = 16: 11.6 vs 13.9 us per call).
+    const int waves = force_waves ? force_waves : (tiles <= 128 ? 4 : 8);
     if (waves != 4 && waves != 8) return fail(QMV_EINVAL, "internal: waves=%d", waves);
     const int mblocks = (M + 15) / 16;
     const long groups = (tiles + waves - 1) / waves;
