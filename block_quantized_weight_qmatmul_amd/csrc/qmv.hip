@@ -563,28 +563,41 @@ __global__ __launch_bounds__(WAVES * 64) void k_m1c(const M1Cat C) {
     int sN = iN;
     long st0 = it0;
     int it = 0;
-    uint32_t nxt[DW];
-    auto issue = [&](long tl, int i) {
+    // Two register buffers take turns: the next step's loads go into one
+    // while the other is decoded, with no copy between them. The last step
+    // is decoded on a path of its own, so that on every other step the wait
+    // before the decode counts exactly the loads issued after it.
+    uint32_t bufA[DW], bufB[DW];
+    auto issue = [&](long tl, int i, uint32_t (&b)[DW]) {
         const long row = (tl - it0) * ROWS + lrow;
         const long rr = row < iN ? row : iN - 1;
         int p = j + i * LPR;
         p = p < P ? p : P - 1;
-        load_pair<DW>(iW + rr * ildw + (size_t)p * PB, nxt);
+        load_pair<DW>(iW + rr * ildw + (size_t)p * PB, b);
     };
     {
         constexpr int XCH = (KMAX_STAGE / 4 + WAVES * 64 - 1) / (WAVES * 64);
         f32x4u_t xv[XCH];
         stage_x_load<WAVES * 64, XCH>(xv, C.x, K);
-        issue(tile, 0);
+        issue(tile, 0, bufA);
         stage_x_store<WAVES * 64, XCH>(xs, xv, K);
         lds_barrier();
     }
     float tot = 0.f;
-    while (true) {
-        uint32_t cur[DW];
-#pragma unroll
-        for (int d = 0; d < DW; ++d) cur[d] = nxt[d];
+    // decode the current step from `cb`; write the row at the end of a tile
+    auto consume = [&](const uint32_t (&cb)[DW]) {
         const int p = j + it * LPR;
+        if (p < P) tot += T::dot(cb, reinterpret_cast<const float4*>(xs + p * XS_PAIR));
+        if (it == IPT - 1) {
+            const long row = (tile - st0) * ROWS + lrow;
+            const float sum = lane_group_sum<LPR>(tot);
+            if (j == LPR - 1 && row < sN) sy[row] = sum * T::OUT_SCALE;
+            tot = 0.f;
+        }
+    };
+    // One step: issue the next step into `nb` and decode `cb`; false after
+    // the last step.
+    auto step = [&](uint32_t (&cb)[DW], uint32_t (&nb)[DW]) -> bool {
         int it2 = it + 1;
         long tile2 = tile;
         if (it2 == IPT) {
@@ -599,16 +612,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_m1c(const M1Cat C) {
                 inext = C.t0[ip + 1];
             }
         }
-        const bool more = tile2 < ntiles;
-        if (more) issue(tile2, it2);
-        if (p < P) tot += T::dot(cur, reinterpret_cast<const float4*>(xs + p * XS_PAIR));
-        if (it == IPT - 1) {
-            const long row = (tile - st0) * ROWS + lrow;
-            const float sum = lane_group_sum<LPR>(tot);
-            if (j == LPR - 1 && row < sN) sy[row] = sum * T::OUT_SCALE;
-            tot = 0.f;
+        if (tile2 >= ntiles) {
+            consume(cb);
+            return false;
         }
-        if (!more) break;
+        issue(tile2, it2, nb);
+        consume(cb);
         if (it2 == 0) {  // the next step starts the tile just issued
             sy = C.y[ip];
             sN = iN;
@@ -616,6 +625,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_m1c(const M1Cat C) {
         }
         tile = tile2;
         it = it2;
+        return true;
+    };
+    while (step(bufA, bufB) && step(bufB, bufA)) {
     }
 }
 
@@ -2335,20 +2347,6 @@ int pick_lpr_q6(int U) {
     return 4;
 }
 
-struct M1Cfg {
-    int lpr, rpt, waves, wgs_per_cu;
-};
-
-M1Cfg pick_m1(int N, int K) {
-    M1Cfg c;
-    c.lpr = pick_lpr(K / 64);
-    c.rpt = 1;
-    c.waves = 8;
-    c.wgs_per_cu = 2;
-    (void)N;
-    return c;
-}
-
 template <int QT, int LPR, int RPT, int WAVES>
 int launch_m1_t(const uint8_t* W, size_t ldw, const float* X, float* Y, int N, int K, int wgs_per_cu,
                 hipStream_t st) {
@@ -2364,14 +2362,19 @@ int launch_m1_t(const uint8_t* W, size_t ldw, const float* X, float* Y, int N, i
     return check_launch("qmv m1 kernel");
 }
 
+// One M = 1 product: k_m1 with 8 waves, two workgroups per CU and the lane
+// width of the row length. (As a batch of one through k_m1c the 2 MB call
+// of 2048 x 2048 took 3.8 instead of 3.3 us: its larger kernel-argument
+// block is read before anything else starts.)
 template <int QT>
 int launch_m1(const uint8_t* W, size_t ldw, const float* X, float* Y, int N, int K, hipStream_t st) {
-    const M1Cfg c = pick_m1(N, K);
-#define QMV_M1_CASE(L, R, WV) \
-    if (c.lpr == L && c.rpt == R && c.waves == WV) return launch_m1_t<QT, L, R, WV>(W, ldw, X, Y, N, K, c.wgs_per_cu, st);
-    QMV_M1_CASE(64, 1, 8) QMV_M1_CASE(32, 1, 8) QMV_M1_CASE(16, 1, 8) QMV_M1_CASE(8, 1, 8) QMV_M1_CASE(4, 1, 8)
-#undef QMV_M1_CASE
-    return fail(QMV_EINVAL, "internal: no m1 kernel for lpr=%d rpt=%d waves=%d", c.lpr, c.rpt, c.waves);
+    switch (pick_lpr(K / 64)) {
+        case 64: return launch_m1_t<QT, 64, 1, 8>(W, ldw, X, Y, N, K, 2, st);
+        case 32: return launch_m1_t<QT, 32, 1, 8>(W, ldw, X, Y, N, K, 2, st);
+        case 16: return launch_m1_t<QT, 16, 1, 8>(W, ldw, X, Y, N, K, 2, st);
+        case 8: return launch_m1_t<QT, 8, 1, 8>(W, ldw, X, Y, N, K, 2, st);
+        default: return launch_m1_t<QT, 4, 1, 8>(W, ldw, X, Y, N, K, 2, st);
+    }
 }
 
 // Plan for the x-stationary kernel: lanes per row and K segments.
