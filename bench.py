@@ -44,8 +44,16 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qmv_decode_layer_h4096.js
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the kernel source's code: comments and blank space are left
+    out, so that the committed counter figures stay attached to the code they
+    were taken on and a comment edit does not orphan them."""
+    import re
+    with open(KERNEL_SRC, encoding="utf-8") as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    src = " ".join(src.split())
+    return hashlib.sha256(src.encode()).hexdigest()[:16]
 
 
 def build_layer_sets(R, dev):

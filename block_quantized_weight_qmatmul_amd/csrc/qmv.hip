@@ -520,7 +520,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_m1b(const M1Batch B) {
 // t0[p] .. t0[p+1]-1; a tile never spans two problems) and every workgroup
 // takes tiles blockIdx.x, blockIdx.x + gridDim.x, ... of it, so the work is
 // spread evenly whatever the problems' sizes, and x is staged once per
-// workgroup. The loop is m1_stream's with one row per lane group.
+// workgroup. The loop is m1_stream's with one row per lane group, except
+// that its two register buffers take turns instead of being copied.
 // ---------------------------------------------------------------------------
 struct M1Cat {
     const uint8_t* W[MAXB];
