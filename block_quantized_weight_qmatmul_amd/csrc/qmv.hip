@@ -2178,23 +2178,24 @@ __global__ __launch_bounds__(WAVES * 64) void k_q6k(const uint8_t* __restrict__ 
     long tile = blockIdx.x;
     if (tile >= ntiles) return;  // uniform over the workgroup
     int it = 0;
-    uint32_t nxt[F::DW];
-    auto issue = [&](long tl, int i) {
+    // two register buffers in turn (see k_m1c)
+    uint32_t bufA[F::DW], bufB[F::DW];
+    auto issue = [&](long tl, int i, uint32_t (&b)[F::DW]) {
         long row = tl * ROWS + lrow;
         row = row < N ? row : N - 1;
         int u = j + i * LPR;
         u = u < U ? u : U - 1;
-        F::load(W + (size_t)row * ldw, S + (size_t)row * lds, Bz + (size_t)row * lds, u, K, nxt);
+        F::load(W + (size_t)row * ldw, S + (size_t)row * lds, Bz + (size_t)row * lds, u, K, b);
     };
     if constexpr (MX == 1) {
         // x loads first, then the first weight loads (see m1_stream)
         const size_t xo = 0;
         Q6Stage<NT, GCH, 1> stg;
         stg.load(X, &xo, 1, K);
-        issue(tile, 0);
+        issue(tile, 0, bufA);
         stg.store(xs, 0, gs, 0, 1, K);
     } else {
-        issue(tile, 0);
+        issue(tile, 0, bufA);
         for (int i = 0; i < nx; ++i) {
             const size_t xo = (size_t)i * ldx;
             Q6Stage<NT, GCH, 1> stg;
@@ -2206,20 +2207,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_q6k(const uint8_t* __restrict__ 
     float tot[MX];
 #pragma unroll
     for (int i = 0; i < MX; ++i) tot[i] = 0.f;
-    while (true) {
-        uint32_t cur[F::DW];
-#pragma unroll
-        for (int d = 0; d < F::DW; ++d) cur[d] = nxt[d];
+    auto consume = [&](const uint32_t (&cb)[F::DW]) {
         const int u = j + it * LPR;
-        int it2 = it + 1;
-        long tile2 = tile;
-        if (it2 == IPT) {
-            it2 = 0;
-            tile2 += gridDim.x;
-        }
-        const bool more = tile2 < ntiles;
-        if (more) issue(tile2, it2);
-        if (u < U) F::template dot<MX>(cur, u, K, xs + (size_t)u * XS_Q6, xstride, gs + 8 * u, gstride, nx, tot);
+        if (u < U) F::template dot<MX>(cb, u, K, xs + (size_t)u * XS_Q6, xstride, gs + 8 * u, gstride, nx, tot);
         if (it == IPT - 1) {
             const long row = tile * ROWS + lrow;
 #pragma unroll
@@ -2231,9 +2221,25 @@ __global__ __launch_bounds__(WAVES * 64) void k_q6k(const uint8_t* __restrict__ 
                 tot[i] = 0.f;
             }
         }
-        if (!more) break;
+    };
+    auto step = [&](uint32_t (&cb)[F::DW], uint32_t (&nb)[F::DW]) -> bool {
+        int it2 = it + 1;
+        long tile2 = tile;
+        if (it2 == IPT) {
+            it2 = 0;
+            tile2 += gridDim.x;
+        }
+        if (tile2 >= ntiles) {  // the last step, on a path of its own
+            consume(cb);
+            return false;
+        }
+        issue(tile2, it2, nb);
+        consume(cb);
         tile = tile2;
         it = it2;
+        return true;
+    };
+    while (step(bufA, bufB) && step(bufB, bufA)) {
     }
 }
 
