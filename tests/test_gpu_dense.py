@@ -257,6 +257,9 @@ SHARED_GROUPS = {
     # row strides padded by 12 bytes (4-byte aligned) and by 2 bytes (the
     # second problem then takes the generic kernel, the others the fast one)
     "padded_k4096": (4096, [(100, 12), (37, 2), (513, 0)]),
+    # more 8-row tiles (1027) than workgroups: a workgroup's stride jumps
+    # from the second problem over the three one-tile problems to the last
+    "stride_skips_k4096": (4096, [4096, 8, 8, 8, 4096]),
 }
 
 
