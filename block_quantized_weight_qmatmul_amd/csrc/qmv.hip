@@ -394,19 +394,23 @@ __device__ __forceinline__ void m1_stream(const uint8_t* __restrict__ W, size_t 
     long tile = first_tile;
     if (tile >= ntiles) return;  // uniform over the workgroup
     int it = 0;
-    uint32_t nxt[RPT][DW];
-    auto issue = [&](long tl, int i) {
+    // Two register buffers take turns: the next step's loads go into one
+    // while the other is decoded, with no copy between them; the last step
+    // is decoded on a path of its own, so that the wait before every other
+    // decode counts exactly the loads issued after it.
+    uint32_t bufA[RPT][DW], bufB[RPT][DW];
+    auto issue = [&](long tl, int i, uint32_t (&b)[RPT][DW]) {
         const long row0 = tl * ROWS + lrow;
         int p = j + i * LPR;
         p = p < P ? p : P - 1;
 #pragma unroll
         for (int r = 0; r < RPT; ++r) {
             const long rr = row0 + r < N ? row0 + r : N - 1;
-            load_pair<DW>(W + rr * ldw + (size_t)p * PB, nxt[r]);
+            load_pair<DW>(W + rr * ldw + (size_t)p * PB, b[r]);
         }
     };
     if constexpr (SW) {
-        issue(tile, 0);
+        issue(tile, 0, bufA);
         stage_swiglu<WAVES * 64>(xs, 0, x, 0, 1, K);
         __syncthreads();
     } else {
@@ -415,32 +419,19 @@ __device__ __forceinline__ void m1_stream(const uint8_t* __restrict__ W, size_t 
         constexpr int XCH = (KMAX_STAGE / 4 + WAVES * 64 - 1) / (WAVES * 64);
         f32x4u_t xv[XCH];
         stage_x_load<WAVES * 64, XCH>(xv, x, K);
-        issue(tile, 0);
+        issue(tile, 0, bufA);
         stage_x_store<WAVES * 64, XCH>(xs, xv, K);
         lds_barrier();
     }
     float tot[RPT];
 #pragma unroll
     for (int r = 0; r < RPT; ++r) tot[r] = 0.f;
-    while (true) {
-        uint32_t cur[RPT][DW];
-#pragma unroll
-        for (int r = 0; r < RPT; ++r)
-#pragma unroll
-            for (int d = 0; d < DW; ++d) cur[r][d] = nxt[r][d];
+    auto consume = [&](const uint32_t (&cb)[RPT][DW]) {
         const int p = j + it * LPR;
-        int it2 = it + 1;
-        long tile2 = tile;
-        if (it2 == IPT) {
-            it2 = 0;
-            tile2 += tile_stride;
-        }
-        const bool more = tile2 < ntiles;
-        if (more) issue(tile2, it2);
         if (p < P) {
             const float4* xv = reinterpret_cast<const float4*>(xs + p * XS_PAIR);
 #pragma unroll
-            for (int r = 0; r < RPT; ++r) tot[r] += T::dot(cur[r], xv);
+            for (int r = 0; r < RPT; ++r) tot[r] += T::dot(cb[r], xv);
         }
         if (it == IPT - 1) {
             const long row0 = tile * ROWS + lrow;
@@ -451,9 +442,25 @@ __device__ __forceinline__ void m1_stream(const uint8_t* __restrict__ W, size_t 
                 tot[r] = 0.f;
             }
         }
-        if (!more) break;
+    };
+    auto step = [&](uint32_t (&cb)[RPT][DW], uint32_t (&nb)[RPT][DW]) -> bool {
+        int it2 = it + 1;
+        long tile2 = tile;
+        if (it2 == IPT) {
+            it2 = 0;
+            tile2 += tile_stride;
+        }
+        if (tile2 >= ntiles) {
+            consume(cb);
+            return false;
+        }
+        issue(tile2, it2, nb);
+        consume(cb);
         tile = tile2;
         it = it2;
+        return true;
+    };
+    while (step(bufA, bufB) && step(bufB, bufA)) {
     }
 }
 
