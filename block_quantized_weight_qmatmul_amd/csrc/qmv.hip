@@ -1536,11 +1536,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_idv(const uint8_t* __restrict__ 
     auto wrow = [&](int n, uint32_t e) {
         return W + (size_t)(e < (uint32_t)n_experts ? e : 0u) * estride + (size_t)n * ldw;
     };
-    uint32_t nxt[DW];
-    auto issue = [&](const uint8_t* wr, int i) {
+    // two register buffers in turn (see m1_stream)
+    uint32_t bufA[DW], bufB[DW];
+    auto issue = [&](const uint8_t* wr, int i, uint32_t (&b)[DW]) {
         int pp = j + i * LPR;
         pp = pp < P ? pp : P - 1;
-        load_pair<DW>(wr + (size_t)pp * PB, nxt);
+        load_pair<DW>(wr + (size_t)pp * PB, b);
     };
 
     int p, n;
@@ -1552,17 +1553,17 @@ __global__ __launch_bounds__(WAVES * 64) void k_idv(const uint8_t* __restrict__ 
             f32x4u_t xv[XCH];
             stage_x_load<NT, XCH>(xv, X, K);
             rowinfo(tile, p, n, e);
-            issue(wrow(n, e), 0);
+            issue(wrow(n, e), 0, bufA);
             stage_x_store<NT, XCH>(xs, xv, K);
         } else {
             rowinfo(tile, p, n, e);
-            issue(wrow(n, e), 0);
+            issue(wrow(n, e), 0, bufA);
             for (int r = 0; r < n_xrows; ++r)
                 stage_x<NT, (KMAX_STAGE / 4 + NT - 1) / NT>(xs + r * xstride, X + (size_t)r * ldx, K);
         }
     } else {
         rowinfo(tile, p, n, e);
-        issue(wrow(n, e), 0);
+        issue(wrow(n, e), 0, bufA);
         stage_swiglu<NT>(xs, xstride, X, ldx, n_xrows, K);
     }
     // each pair's scale, needed first at the end of the first tile
@@ -1571,26 +1572,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_idv(const uint8_t* __restrict__ 
 
     int it = 0;
     float tot = 0.f;
-    while (true) {
-        uint32_t cur[DW];
-#pragma unroll
-        for (int d = 0; d < DW; ++d) cur[d] = nxt[d];
+    auto consume = [&](const uint32_t (&cb)[DW]) {
         const int pp = j + it * LPR;
-        int it2 = it + 1, tile2 = tile;
-        int p2 = p, n2 = n;
-        uint32_t e2 = e;
-        if (it2 == IPT) {
-            it2 = 0;
-            tile2 += gridDim.x;
-        }
-        const bool more = tile2 < ntiles;
-        if (more) {
-            if (tile2 != tile) rowinfo(tile2, p2, n2, e2);
-            issue(wrow(n2, e2), it2);
-        }
         if (pp < P) {
             const float* xr = xs + (size_t)(p / top_k) * xstride + pp * XS_PAIR;
-            tot += T::dot(cur, reinterpret_cast<const float4*>(xr));
+            tot += T::dot(cb, reinterpret_cast<const float4*>(xr));
         }
         if (it == IPT - 1) {
             const float sc = __shfl(scq, p, 64) * T::OUT_SCALE;
@@ -1603,12 +1589,30 @@ __global__ __launch_bounds__(WAVES * 64) void k_idv(const uint8_t* __restrict__ 
             }
             tot = 0.f;
         }
-        if (!more) break;
+    };
+    auto step = [&](uint32_t (&cb)[DW], uint32_t (&nb)[DW]) -> bool {
+        int it2 = it + 1, tile2 = tile;
+        int p2 = p, n2 = n;
+        uint32_t e2 = e;
+        if (it2 == IPT) {
+            it2 = 0;
+            tile2 += gridDim.x;
+        }
+        if (tile2 >= ntiles) {  // the last step, on a path of its own
+            consume(cb);
+            return false;
+        }
+        if (tile2 != tile) rowinfo(tile2, p2, n2, e2);
+        issue(wrow(n2, e2), it2, nb);
+        consume(cb);
         tile = tile2;
         it = it2;
         p = p2;
         n = n2;
         e = e2;
+        return true;
+    };
+    while (step(bufA, bufB) && step(bufB, bufA)) {
     }
 }
 
