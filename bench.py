@@ -321,6 +321,24 @@ def lm_head_q6k_throughput(dev, steps=20):
             "GBps": round(nbytes / t / 1e9, 1), "pct_hbm_peak": round(100 * nbytes / t / 1e9 / HBM_PEAK_GBS, 2)}
 
 
+def lm_head_q8_throughput(dev, steps=20):
+    """The pages' lm_head re-quantized to Q8_0: [2816 -> 262144] (784.3 MB),
+    one token, replays of a graph of 8 calls on one copy (larger than the
+    chip's last-level cache, so every call streams it from HBM)."""
+    import torch
+
+    from block_quantized_weight_qmatmul_amd import qmv, synth
+    N, K = 262144, 2816
+    W = torch.from_numpy(synth.make_weights("q8_0", N, K, cfg=5)).to(dev)
+    X = torch.from_numpy(synth.make_x(1, K, cfg=5)).to(dev)
+    Y = torch.empty((1, N), device=dev)
+    nbytes = N * synth.row_bytes("q8_0", K)
+    t = time_steps(lambda s: qmv.qmv_q8_0(s[0], s[1], s[2]), [(W, X, Y)], steps, 3) / steps
+    del W
+    return {"workload": "q8_0_m1_lm_head_2816x262144", "weight_bytes": nbytes, "us_per_call": round(t * 1e6, 2),
+            "GBps": round(nbytes / t / 1e9, 1), "pct_hbm_peak": round(100 * nbytes / t / 1e9 / HBM_PEAK_GBS, 2)}
+
+
 def moe_q6k_gate_up_throughput(dev, steps=40):
     """The gate_up id call of one token over Q6_K experts (the pages' production
     MoE stores gate_up experts as Q6_K): 128 experts [1408, 2816], top-8. One
@@ -668,6 +686,7 @@ def main():
         extra["moe_ffn_t32_two_call"] = moe_throughput(dev, 32, mode="ffn_two_call")
         extra["moe_ffn_t32_fused"] = moe_throughput(dev, 32, mode="ffn_fused")
         extra["lm_head_q6_k"] = lm_head_q6k_throughput(dev)
+        extra["lm_head_q8_0"] = lm_head_q8_throughput(dev)
         extra["moe_q6_k_gate_up_t1"] = moe_q6k_gate_up_throughput(dev)
         extra["q5_k_b9_group"] = q5k_b9_throughput(dev)
         extra["prefill_m512"] = prefill_throughput(dev)

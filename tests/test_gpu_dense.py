@@ -130,6 +130,16 @@ def test_ragged_shapes(qtype, N, K):
 
 
 @pytest.mark.parametrize("qtype", ["q4_0", "q8_0"])
+@pytest.mark.parametrize("N,K", [(32768, 1024), (33001, 2816), (40000, 8192)])
+def test_m1_large_matrices_narrow_lane_groups(qtype, N, K):
+    """Large M = 1 calls take 16 lanes per row (N >= 32768, 1024 <= K <= 8192);
+    a ragged last tile included."""
+    W = synth.make_weights(qtype, N, K, cfg=96, part=N % 97)
+    X = synth.make_x(1, K, cfg=96, part=K)
+    check(qtype, W, X, f"{qtype} N={N} K={K}")
+
+
+@pytest.mark.parametrize("qtype", ["q4_0", "q8_0"])
 @pytest.mark.parametrize("pad", [2, 4, 64])
 def test_padded_row_stride(qtype, pad):
     N, K = 515, 1024
