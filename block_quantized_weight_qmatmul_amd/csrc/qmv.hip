@@ -530,18 +530,23 @@ __global__ __launch_bounds__(WAVES * 64) void k_m1b(const M1Batch B) {
 // workgroup. The loop is m1_stream's with one row per lane group, except
 // that its two register buffers take turns instead of being copied.
 // ---------------------------------------------------------------------------
+// The problem table is sized for at most MAXP problems (1, 4 or 16): a
+// kernel-argument block read before the first load is issued costs a small
+// launch time in proportion to its size (a batch of one through the 16-entry
+// table took 3.8 instead of 3.3 us on a 2 MB matrix).
+template <int MAXP>
 struct M1Cat {
-    const uint8_t* W[MAXB];
-    float* y[MAXB];
-    size_t ldw[MAXB];
-    int N[MAXB];
-    long t0[MAXB + 1];
+    const uint8_t* W[MAXP];
+    float* y[MAXP];
+    size_t ldw[MAXP];
+    int N[MAXP];
+    long t0[MAXP + 1];
     const float* x;
     int K, n;
 };
 
-template <int QT, int LPR, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void k_m1c(const M1Cat C) {
+template <int QT, int LPR, int WAVES, int MAXP>
+__global__ __launch_bounds__(WAVES * 64) void k_m1c(const M1Cat<MAXP> C) {
     extern __shared__ __align__(16) float xs[];
     using T = PairTraits<QT>;
     constexpr int DW = T::DW, PB = DW * 4;
@@ -562,7 +567,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_m1c(const M1Cat C) {
     // arguments are read again only when the loaded tile crosses into the
     // next problem.
     int ip = 0;
-    while (tile >= C.t0[ip + 1]) ++ip;
+    if constexpr (MAXP > 1)
+        while (ip + 1 < C.n && tile >= C.t0[ip + 1]) ++ip;
     const uint8_t* iW = C.W[ip];
     size_t ildw = C.ldw[ip];
     int iN = C.N[ip];
@@ -611,13 +617,15 @@ __global__ __launch_bounds__(WAVES * 64) void k_m1c(const M1Cat C) {
         if (it2 == IPT) {
             it2 = 0;
             tile2 += stride;
-            if (tile2 >= inext && tile2 < ntiles) {
-                while (tile2 >= C.t0[ip + 1]) ++ip;
-                iW = C.W[ip];
-                ildw = C.ldw[ip];
-                iN = C.N[ip];
-                it0 = C.t0[ip];
-                inext = C.t0[ip + 1];
+            if constexpr (MAXP > 1) {
+                if (tile2 >= inext && tile2 < ntiles) {
+                    while (ip + 1 < C.n && tile2 >= C.t0[ip + 1]) ++ip;
+                    iW = C.W[ip];
+                    ildw = C.ldw[ip];
+                    iN = C.N[ip];
+                    it0 = C.t0[ip];
+                    inext = C.t0[ip + 1];
+                }
             }
         }
         if (tile2 >= ntiles) {
@@ -2409,21 +2417,22 @@ bool m1b_eligible(const uint8_t* W, size_t ldw, const float* x, int K) {
 
 // Launch the batched M = 1 kernel over n problems (n <= MAXB), all eligible.
 // wgs_per_cu and waves are tuning knobs (0 = default).
-template <int QT, int LPR>
-int launch_m1c_t(const M1Cat& C, long tiles, int wgs_per_cu, hipStream_t st) {
+template <int QT, int LPR, int MAXP>
+int launch_m1c_t(const M1Cat<MAXP>& C, long tiles, int wgs_per_cu, hipStream_t st) {
     const size_t lds = xs_bytes(C.K);
     long per_cu = (long)(LDS_PER_CU / (lds ? lds : 1));
     per_cu = per_cu < 1 ? 1 : (per_cu < wgs_per_cu ? per_cu : wgs_per_cu);
     long grid = (long)num_cus() * per_cu;
     grid = grid < tiles ? grid : tiles;
-    hipLaunchKernelGGL((k_m1c<QT, LPR, 8>), dim3((unsigned)grid), dim3(512), lds, st, C);
+    hipLaunchKernelGGL((k_m1c<QT, LPR, 8, MAXP>), dim3((unsigned)grid), dim3(512), lds, st, C);
     return check_launch("qmv shared-input batched m1 kernel");
 }
 
-// Problems that share x and K: one virtual matrix of 8-row tiles (k_m1c).
-template <int QT>
-int launch_m1c(const M1Prob* probs, int n, int wgs_per_cu, hipStream_t st) {
-    M1Cat C;
+// Problems that share x and K: one virtual matrix of 8-row tiles (k_m1c),
+// with a problem table of MAXP >= n entries.
+template <int QT, int MAXP>
+int launch_m1c_n(const M1Prob* probs, int n, int wgs_per_cu, hipStream_t st) {
+    M1Cat<MAXP> C;
     C.x = probs[0].x;
     C.K = probs[0].K;
     C.n = n;
@@ -2440,12 +2449,19 @@ int launch_m1c(const M1Prob* probs, int n, int wgs_per_cu, hipStream_t st) {
     const long tiles = C.t0[n];
     if (tiles > 0x7FFFFFFF) return fail(QMV_EINVAL, "N too large");
     switch (lpr) {
-        case 64: return launch_m1c_t<QT, 64>(C, tiles, wgs_per_cu, st);
-        case 32: return launch_m1c_t<QT, 32>(C, tiles, wgs_per_cu, st);
-        case 16: return launch_m1c_t<QT, 16>(C, tiles, wgs_per_cu, st);
-        case 8: return launch_m1c_t<QT, 8>(C, tiles, wgs_per_cu, st);
-        default: return launch_m1c_t<QT, 4>(C, tiles, wgs_per_cu, st);
+        case 64: return launch_m1c_t<QT, 64, MAXP>(C, tiles, wgs_per_cu, st);
+        case 32: return launch_m1c_t<QT, 32, MAXP>(C, tiles, wgs_per_cu, st);
+        case 16: return launch_m1c_t<QT, 16, MAXP>(C, tiles, wgs_per_cu, st);
+        case 8: return launch_m1c_t<QT, 8, MAXP>(C, tiles, wgs_per_cu, st);
+        default: return launch_m1c_t<QT, 4, MAXP>(C, tiles, wgs_per_cu, st);
     }
+}
+
+template <int QT>
+int launch_m1c(const M1Prob* probs, int n, int wgs_per_cu, hipStream_t st) {
+    if (n <= 1) return launch_m1c_n<QT, 1>(probs, n, wgs_per_cu, st);
+    if (n <= 4) return launch_m1c_n<QT, 4>(probs, n, wgs_per_cu, st);
+    return launch_m1c_n<QT, MAXB>(probs, n, wgs_per_cu, st);
 }
 
 template <int QT>
