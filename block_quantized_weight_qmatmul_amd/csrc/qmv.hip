@@ -204,11 +204,7 @@ __device__ __forceinline__ void load_pair(const uint8_t* p, uint32_t* r) {
     const u32x4* v = reinterpret_cast<const u32x4*>(p);
 #pragma unroll
     for (int i = 0; i < DW / 4; ++i) {
-#ifdef QMV_LOAD_NT
-        u32x4 t = __builtin_nontemporal_load(v + i);
-#else
         u32x4 t = v[i];
-#endif
         r[4 * i + 0] = t.x;
         r[4 * i + 1] = t.y;
         r[4 * i + 2] = t.z;
@@ -3377,106 +3373,6 @@ int qmv_batch(int qtype, const qmv_problem* problems, int n_problems, void* stre
 
 const char* qmv_last_error(void) { return g_err; }
 
-#ifdef QMV_PROBE
-// Tuning entries, built only into a separate probe library.
-int qmv_probe_m1(int qtype, int lpr, int rpt, int waves, int wgs_per_cu, const void* W, size_t ldw, const float* X,
-                 float* Y, int N, int K, void* stream) {
-    hipStream_t st = (hipStream_t)stream;
-    const uint8_t* w = (const uint8_t*)W;
-#define QMV_P(QT, L, R, WV)                            \
-    if (qtype == QT && lpr == L && rpt == R && waves == WV) \
-        return launch_m1_t<QT, L, R, WV>(w, ldw, X, Y, N, K, wgs_per_cu, st);
-#define QMV_PW(QT, WV) QMV_P(QT, 64, 1, WV) QMV_P(QT, 64, 2, WV) QMV_P(QT, 32, 1, WV) QMV_P(QT, 32, 2, WV) \
-    QMV_P(QT, 16, 1, WV) QMV_P(QT, 16, 2, WV)
-    QMV_PW(QMV_Q4_0, 4) QMV_PW(QMV_Q4_0, 8) QMV_PW(QMV_Q4_0, 16)
-    QMV_PW(QMV_Q8_0, 4) QMV_PW(QMV_Q8_0, 8) QMV_PW(QMV_Q8_0, 16)
-#undef QMV_PW
-#undef QMV_P
-    return fail(QMV_EINVAL, "probe: no variant");
-}
 
-int qmv_probe_m1b(int qtype, int waves, int wgs_per_cu, int n, const void* const* W, const size_t* ldw,
-                  const float* const* X, float* const* Y, const int* N, const int* K, void* stream) {
-    M1Prob pr[MAXB];
-    for (int i = 0; i < n && i < MAXB; ++i) {
-        pr[i].W = (const uint8_t*)W[i];
-        pr[i].x = X[i];
-        pr[i].y = Y[i];
-        pr[i].ldw = ldw[i];
-        pr[i].N = N[i];
-        pr[i].K = K[i];
-    }
-    return qtype == QMV_Q4_0 ? launch_m1b<QMV_Q4_0>(pr, n, wgs_per_cu, waves, (hipStream_t)stream)
-                             : launch_m1b<QMV_Q8_0>(pr, n, wgs_per_cu, waves, (hipStream_t)stream);
-}
-
-int qmv_probe_mm(int waves, int tw, const void* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M,
-                 int N, int K, void* stream) {
-    return launch_mm((const uint8_t*)W, ldw, X, ldx, Y, ldy, M, N, K, waves, tw, (hipStream_t)stream);
-}
-
-int qmv_probe_mm4(int S, int waves, const void* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M,
-                  int N, int K, void* stream) {
-    return launch_mm4((const uint8_t*)W, ldw, X, ldx, Y, ldy, M, N, K, S, waves, (hipStream_t)stream);
-}
-
-// Expert-indexed product (fast path, no SwiGLU) with a forced lanes-per-row
-// and wave count.
-int qmv_probe_id(int qtype, int lpr, int waves, const void* W, size_t es, size_t ldw, int E, const float* X,
-                 size_t ldx, const uint32_t* ids, int n_tokens, int top_k, float* Y, size_t ldy, int N, int K,
-                 const float* sc, void* stream) {
-    hipStream_t st = (hipStream_t)stream;
-    const uint8_t* w = (const uint8_t*)W;
-    const int np = n_tokens * top_k;
-#define QMV_P(QT, L, WV)                            \
-    if (qtype == QT && lpr == L && waves == WV) \
-        return launch_id_t<QT, L, 1, false, WV>(w, es, ldw, E, X, ldx, ids, np, top_k, Y, ldy, N, K, sc, nullptr, 1, st);
-#define QMV_PW(QT, WV) QMV_P(QT, 64, WV) QMV_P(QT, 32, WV) QMV_P(QT, 16, WV) QMV_P(QT, 8, WV) QMV_P(QT, 4, WV)
-    QMV_PW(QMV_Q4_0, 4) QMV_PW(QMV_Q4_0, 8) QMV_PW(QMV_Q4_0, 2)
-#undef QMV_PW
-#undef QMV_P
-    return fail(QMV_EINVAL, "probe: no variant");
-}
-
-// Few-pairs expert-indexed kernel with forced lanes-per-row and workgroups
-// per compute unit (n_tokens rows of X or, with sw, of SwiGLU input).
-int qmv_probe_idv(int qtype, int sw, int lpr, int wgs_per_cu, int deep, const void* W, size_t es, size_t ldw, int E,
-                  const float* X, size_t ldx, const uint32_t* ids, int n_tokens, int top_k, float* Y, size_t ldy, int N,
-                  int K, const float* sc, void* stream) {
-    hipStream_t st = (hipStream_t)stream;
-    const uint8_t* w = (const uint8_t*)W;
-    const int np = n_tokens * top_k;
-    if (qtype == QMV_Q4_0 && sw)
-        return launch_idv<QMV_Q4_0, true>(w, es, ldw, E, X, ldx, ids, np, top_k, n_tokens, Y, ldy, N, K, sc, nullptr,
-                                          lpr, wgs_per_cu, deep, st);
-    if (qtype == QMV_Q4_0)
-        return launch_idv<QMV_Q4_0, false>(w, es, ldw, E, X, ldx, ids, np, top_k, n_tokens, Y, ldy, N, K, sc, nullptr,
-                                           lpr, wgs_per_cu, deep, st);
-    return fail(QMV_EINVAL, "probe: no variant");
-}
-
-// Q6_K with a forced lanes-per-row and workgroups per compute unit.
-int qmv_probe_q6k(int lpr, int wgs_per_cu, const void* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy,
-                  int M, int N, int K, void* stream) {
-    return launch_q6k<FmtQ6K>((const uint8_t*)W, ldw, X, ldx, Y, ldy, M, N, K, lpr, wgs_per_cu, (hipStream_t)stream);
-}
-
-// One-launch MoE down half with a forced lanes-per-row and wave count.
-int qmv_probe_moe_down(int qtype, int lpr, int waves, const void* W, size_t es, size_t ldw, int E, const float* G,
-                       size_t ldg, const uint32_t* ids, const float* wts, int n_tokens, int top_k, float* out,
-                       size_t ldo, int N, int K, const float* sc, void* stream) {
-    hipStream_t st = (hipStream_t)stream;
-    const uint8_t* w = (const uint8_t*)W;
-#define QMV_P(QT, L, WV)                            \
-    if (qtype == QT && lpr == L && waves == WV) \
-        return launch_moe_down_t<QT, L, WV>(w, es, ldw, E, G, ldg, ids, wts, n_tokens, top_k, out, ldo, N, K, sc, \
-                                            nullptr, st);
-#define QMV_PW(QT, WV) QMV_P(QT, 64, WV) QMV_P(QT, 32, WV) QMV_P(QT, 16, WV) QMV_P(QT, 8, WV) QMV_P(QT, 4, WV)
-    QMV_PW(QMV_Q4_0, 8) QMV_PW(QMV_Q4_0, 4)
-#undef QMV_PW
-#undef QMV_P
-    return fail(QMV_EINVAL, "probe: no variant");
-}
-#endif
 
 }  // extern "C"

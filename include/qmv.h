@@ -140,7 +140,7 @@ int qmv_q6_k(const void* W, size_t ldw_bytes, const float* X, size_t ldx, float*
  *
  * The pages' production model keeps its dense FFN gate, up and router
  * projections in this format (the comment on the B9 dispatch group of
- * `encode_one_layer`: "Q5_K 2816->5760 x 2 + 2816->128"). Named only; the
+ * `encode_one_layer`: Q5_K projections from 2816 to 5760, twice, plus a 2816 to 128 router). Named only; the
  * layout taken is the GGML k-quant Q5_K super-block:
  *   bytes   0..1    binary16 d        bytes 2..3  binary16 dmin
  *   bytes   4..15   eight 6-bit sub-block scales and minimums, packed: for

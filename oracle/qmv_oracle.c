@@ -26,7 +26,7 @@
  *   Any int8 decodes as-is, -128 included.
  *
  *   Q4_0 (18 B): the pages name the format (the `MlxMoeWeights` doc calls
- *   the weights "GGML block format"; a `qwen3-vl-2b-q4_0.gguf` model is
+ *   the weights as kept in the GGML block layout; a `qwen3-vl-2b-q4_0.gguf` model is
  *   named in `MlxMoeWeights::dense_placeholder`) but never lay it out. The
  *   reading taken here is the GGML Q4_0 block: bytes 0,1 = binary16 scale
  *   (low byte first); byte 2+j (j < 16) holds element j in its low nibble and
@@ -43,7 +43,7 @@
  *
  *   Q5_K (176 B per 256 weights): the format of the dense FFN gate, up and
  *   router projections of the pages' production model (the B9 comment in
- *   `encode_one_layer`: "Q5_K 2816->5760 x 2 + 2816->128"). Named only; the
+ *   `encode_one_layer`: Q5_K projections from 2816 to 5760, twice, plus a 2816 to 128 router). Named only; the
  *   layout read here is the GGML k-quant Q5_K super-block, written out at
  *   decode_superblock_q5_k.
  *

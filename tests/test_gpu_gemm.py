@@ -1,7 +1,7 @@
 """GPU parity of qmv_gemm (any number of activation rows) against the oracle.
 
 M spans one and several 16-row blocks with ragged tails; every weight type;
-a prefill shape (M = 256 rows of a 4096 x 4096 Q4_0 matrix) on sampled rows.
+a prefill shape (M = 256 rows of a 4096 x 4096 Q4_0 matrix), every output element.
 """
 import numpy as np
 import pytest
@@ -38,14 +38,13 @@ def test_gemm_against_oracle(qtype, M, N, K):
     assert np.all(np.isnan(full[:, N:]))
 
 
-def test_gemm_prefill_shape_sampled_rows():
+def test_gemm_prefill_shape_full():
     M, N, K = 256, 4096, 4096
     W = synth.make_weights("q4_0", N, K, cfg=91)
     X = synth.make_x(M, K, cfg=91)
     y, _ = run("q4_0", W, X, N)
-    rows = np.unique(np.r_[0, N - 1, np.random.default_rng(91).integers(0, N, 120)])
-    yo, a = oracle.qmv("q4_0", W[rows], X)
-    print("ratio", assert_within_tol(y[:, rows], yo, a, "prefill"))
+    yo, a = oracle.qmv("q4_0", W, X)
+    print("ratio", assert_within_tol(y, yo, a, "prefill"))
 
 
 def test_gemm_row_blocks_agree_with_the_16_row_call_and_repeat_bitwise():

@@ -94,11 +94,8 @@ def test_moe_t1_full(call_idx):
 
 
 @pytest.mark.parametrize("call_idx", [0, 1])
-def test_moe_t32_sampled(call_idx):
-    r = np.random.default_rng(32 + call_idx)
-    N = synth.moe_calls(32)[call_idx].N
-    rows = np.unique(np.r_[0, N - 1, r.integers(0, N, 160)])
-    print("ratio", _moe_check(32, call_idx, sample_rows=rows))
+def test_moe_t32_full(call_idx):
+    print("ratio", _moe_check(32, call_idx))
 
 
 def test_moe_without_expert_scale():

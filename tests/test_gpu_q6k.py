@@ -3,7 +3,7 @@
 Shapes cover every lanes-per-row choice (K/128 units per row: 2, 4, 22, 32,
 128), rows of an odd number of super-blocks (2-byte aligned rows), padded
 row strides, ragged N, M = 1..16 (launches of up to 4 rows), the lm_head
-shape [262144, 2816] on sampled rows, and one-hot activations, where the
+shape [262144, 2816] in full, and one-hot activations, where the
 result is a single rounding of the exact weight.
 """
 import numpy as np
@@ -73,15 +73,14 @@ def test_q6k_one_hot_is_one_rounding_of_the_weight():
         assert np.array_equal(y[i], want), k
 
 
-def test_q6k_lm_head_shape_sampled_rows():
-    """The pages' lm_head: Q6_K [2816 -> 262144], one token."""
+def test_q6k_lm_head_shape_full():
+    """The pages' lm_head: Q6_K [2816 -> 262144], one token, every output."""
     N, K = 262144, 2816
     W = synth.make_weights("q6_k", N, K, cfg=5)
     X = synth.make_x(1, K, cfg=5)
     y, _ = run(W, X, N, K)
-    rows = np.unique(np.r_[0, 1, N - 1, np.random.default_rng(5).integers(0, N, 400)])
-    yo, a = oracle.qmv("q6_k", W[rows], X)
-    print("ratio", assert_within_tol(y[:, rows], yo, a, "lm_head"))
+    yo, a = oracle.qmv("q6_k", W, X)
+    print("ratio", assert_within_tol(y, yo, a, "lm_head"))
     assert np.isfinite(y).all()
 
 
