@@ -175,53 +175,36 @@ def time_steps(fn, sets, steps, warmup):
     return e0.elapsed_time(e1) / 1e3
 
 
-def m16_throughput(dev, steps=40):
-    """Config 3 (Q4_0, M = 16, K = 5120, N in {5120, 1024, 27648}): GB/s over
-    4 rotated copies, eager launches (these calls take stream-ordered scratch
-    memory, which graph capture would replace by the kernel that needs none)."""
+def m16_throughput(dev, qtype="q4_0", steps=40):
+    """Config 3 (M = 16, K = 5120, N in {5120, 1024, 27648}; Q4_0, or the same
+    shapes in Q8_0): each matrix timed on its own, graph-timed over enough
+    rotated device copies to stream at least 1.07 GB per sweep (R = 73, 365
+    and 14 copies in Q4_0), several calls per graph replay. The set figure is
+    the three matrices' bytes over the sum of their times."""
     import torch
 
     from block_quantized_weight_qmatmul_amd import qmv, synth
-    probs = synth.CONFIGS[3]["problems"]
-    sets = []
-    for r in range(4):
-        s = []
-        for part, p in enumerate(probs):
-            W = torch.from_numpy(synth.make_weights("q4_0", p.N, p.K, cfg=3, copy=r, part=part)).to(dev)
-            X = torch.from_numpy(synth.make_x(p.M, p.K, cfg=3, copy=r, part=part)).to(dev)
-            s.append((W, X, torch.empty((p.M, p.N), device=dev)))
-        sets.append(s)
-    nbytes = sum(p.weight_bytes for p in probs)
-
-    # raw C-ABI calls with the arguments prepared once, so that the host keeps
-    # ahead of the GPU
-    st = torch.cuda.current_stream().cuda_stream
-    args = [[(W.data_ptr(), W.stride(0), X.data_ptr(), X.stride(0), Y.data_ptr(), Y.stride(0), p.M, p.N, p.K)
-             for (W, X, Y), p in zip(s, probs)] for s in sets]
-
-    def step(a):
-        for W, ldw, X, ldx, Y, ldy, M, N, K in a:
-            if qmv.raw_qmv(qmv.QMV_Q4_0, W, ldw, X, ldx, Y, ldy, M, N, K, st) != 0:
-                raise RuntimeError(qmv.last_error())
-    for a in args:
-        step(a)
-    torch.cuda.synchronize()
-    ctr = [0]
-
-    def nxt():
-        step(args[ctr[0] % 4])
-        ctr[0] += 1
-    warm_eager(nxt)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(steps):
-        step(args[i % 4])
-    e1.record()
-    torch.cuda.synchronize()
-    t = e0.elapsed_time(e1) / 1e3 / steps
-    return {"workload": "q4_0_m16_k5120_n5120_1024_27648", "weight_bytes": nbytes, "timing": "eager",
-            "us_per_set": round(t * 1e6, 2), "GBps": round(nbytes / t / 1e9, 1),
-            "pct_hbm_peak": round(100 * nbytes / t / 1e9 / HBM_PEAK_GBS, 2)}
+    fn = {"q4_0": qmv.qmv_q4_0, "q8_0": qmv.qmv_q8_0}[qtype]
+    out, tot_b, tot_t = {"workload": f"{qtype}_m16_k5120_n5120_1024_27648", "timing": "graph"}, 0, 0.0
+    for part, p in enumerate(synth.CONFIGS[3]["problems"]):
+        W = synth.make_weights(qtype, p.N, p.K, cfg=3, part=part)
+        X = synth.make_x(p.M, p.K, cfg=3, part=part)
+        nb = W.nbytes
+        R = max(4, -(-int(1.07e9) // nb))
+        Wd, Xd = torch.from_numpy(W).to(dev), torch.from_numpy(X).to(dev)
+        sets = [(Wd if r == 0 else Wd.clone(), Xd, torch.empty((p.M, p.N), device=dev)) for r in range(R)]
+        n = max(steps, R)
+        t = time_steps(lambda s: fn(s[0], s[1], s[2]), sets, n, R) / n
+        out[f"n{p.N}"] = {"weight_bytes": nb, "rotated_copies": R, "us_per_call": round(t * 1e6, 2),
+                          "GBps": round(nb / t / 1e9, 1), "pct_hbm_peak": round(100 * nb / t / 1e9 / HBM_PEAK_GBS, 2),
+                          "TFLOPs": round(2.0 * p.M * p.N * p.K / t / 1e12, 2)}
+        tot_b += nb
+        tot_t += t
+        del sets, Wd, Xd
+        torch.cuda.empty_cache()
+    out.update({"weight_bytes": tot_b, "us_per_set": round(tot_t * 1e6, 2), "GBps": round(tot_b / tot_t / 1e9, 1),
+                "pct_hbm_peak": round(100 * tot_b / tot_t / 1e9 / HBM_PEAK_GBS, 2)})
+    return out
 
 
 def dense_m1_throughput(dev, cfg, steps=400):
@@ -679,6 +662,7 @@ def main():
         extra["q4_0_m1_2048x2048"] = dense_m1_throughput(dev, 0)
         extra["q8_0_m1"] = dense_m1_throughput(dev, 2)
         extra["m16"] = m16_throughput(dev)
+        extra["m16_q8_0"] = m16_throughput(dev, "q8_0")
         extra["moe_t1"] = moe_throughput(dev, 1)
         extra["moe_t32"] = moe_throughput(dev, 32)
         extra["moe_ffn_t1_fused"] = moe_throughput(dev, 1, mode="ffn_fused")

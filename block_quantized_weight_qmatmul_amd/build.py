@@ -6,27 +6,45 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "qmv.hip")
+SRCS = [os.path.join(PKG, "csrc", f) for f in ("qmv.hip", "qmv_mq.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqmv.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
+FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          # keep packed fp32 VALU ops out of the generated code
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
 def build(out: str = LIB, extra: list[str] | None = None, quiet: bool = True) -> str:
-    """Compile csrc/qmv.hip into ``out`` (atomically replaced)."""
-    tmp = out + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, *(extra or []), "-I", INCLUDE, SRC, "-o", tmp]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + r.stdout + r.stderr)
-    if not quiet:
-        print(" ".join(cmd))
-    os.replace(tmp, out)
+    """Compile csrc/*.hip into ``out`` (atomically replaced): each source to an
+    object file in parallel, then one link."""
+    objs, procs = [], []
+    for src in SRCS:
+        obj = os.path.join(PKG, "csrc", os.path.basename(src) + ".o.tmp%d" % os.getpid())
+        cmd = [HIPCC, *FLAGS, "-c", *(extra or []), "-I", INCLUDE, src, "-o", obj]
+        procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+        objs.append(obj)
+    try:
+        for cmd, p in procs:
+            o, e = p.communicate()
+            if p.returncode != 0:
+                raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + o + e)
+            if not quiet:
+                print(" ".join(cmd))
+        tmp = out + ".tmp%d" % os.getpid()
+        cmd = [HIPCC, *FLAGS, "-shared", *objs, "-o", tmp]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("hipcc link failed:\n" + r.stdout + r.stderr)
+        if not quiet:
+            print(" ".join(cmd))
+        os.replace(tmp, out)
+    finally:
+        for obj in objs:
+            if os.path.exists(obj):
+                os.remove(obj)
     return out
 
 

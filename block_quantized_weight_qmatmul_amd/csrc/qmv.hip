@@ -23,14 +23,8 @@
 //   * k_m1c          — the batched M = 1 call when all problems share x and K
 //     (a layer's Q/K/V, its gate/up): their rows form one virtual matrix of
 //     tiles that every workgroup strides through, so the work is even.
-//   * k_xprep + k_mm4 (+ k_mmred) — Q4_0 with M = 2..16 on the matrix cores
-//     (v_mfma_f32_16x16x32_f16): the activations are converted once per call
-//     into fp16 hi/lo operands, then 16-row weight tiles are contracted with
-//     them chunk by chunk; K is split over workgroups, and the segments summed
-//     by k_mmred, when the tiles alone cannot fill the chip.
-//   * k_mm           — the same contraction with the activations converted by
-//     each workgroup itself (no scratch memory), used when the call's scratch
-//     buffer cannot be allocated.
+//   * k_mq (qmv_mq.hip) — Q4_0 and Q8_0 with M = 2..16 (and each 16-row
+//     block of a prefill) on the matrix cores, one launch, no scratch memory.
 //   * k_generic      — any qtype, 1..16 rows of X, any 2-byte alignment and
 //     any K: one wave per weight row, one block per lane per step, 2-byte
 //     loads. The fallback for shapes the fast kernels do not take.
@@ -48,16 +42,12 @@
 #include <stdio.h>
 #include <string.h>
 
-#include <mutex>
-#include <vector>
 
 #include "qmv.h"
+#include "qmv_internal.h"
 
-namespace {
+namespace qmvi {
 
-// ---------------------------------------------------------------------------
-// Error reporting
-// ---------------------------------------------------------------------------
 thread_local char g_err[512] = "";
 
 int fail(int code, const char* fmt, ...) {
@@ -74,6 +64,24 @@ int check_launch(const char* what) {
     return QMV_OK;
 }
 
+// Compute units of the current device (cached per device id).
+int num_cus() {
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < 64 && cache[dev] > 0) return cache[dev];
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    if (dev < 64) cache[dev] = n;
+    return n;
+}
+
+}  // namespace qmvi
+
+namespace {
+
+using namespace qmvi;
+
 constexpr int QK = 32;
 
 __host__ __device__ constexpr int block_bytes(int qtype) { return qtype == QMV_Q4_0 ? 18 : 34; }
@@ -81,14 +89,6 @@ __host__ __device__ constexpr int block_bytes(int qtype) { return qtype == QMV_Q
 // ---------------------------------------------------------------------------
 // Device helpers
 // ---------------------------------------------------------------------------
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4), aligned(4)));
-
-__device__ __forceinline__ float half_lo(uint32_t w) {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
-}
-__device__ __forceinline__ float half_hi(uint32_t w) {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
-}
 
 // (code - 8) / 16 for the low nibble of byte B of w, where w already holds
 // the code bytes XORed with 0x88 (v_cvt_off_f32_i4 reads bits [3:0] as a
@@ -199,21 +199,6 @@ struct PairTraits<QMV_Q8_0> {
     __device__ static float dot(const uint32_t* r, const float4* xv) { return q8_pair(r, xv); }
 };
 
-template <int DW>
-__device__ __forceinline__ void load_pair(const uint8_t* p, uint32_t* r) {
-    const u32x4* v = reinterpret_cast<const u32x4*>(p);
-#pragma unroll
-    for (int i = 0; i < DW / 4; ++i) {
-        u32x4 t = v[i];
-        r[4 * i + 0] = t.x;
-        r[4 * i + 1] = t.y;
-        r[4 * i + 2] = t.z;
-        r[4 * i + 3] = t.w;
-    }
-    if constexpr (DW % 4) {
-        r[DW - 1] = reinterpret_cast<const uint32_t*>(p)[DW - 1];
-    }
-}
 
 // LDS layout of the staged activation row: 64 floats per pair of blocks,
 // padded to 68 so that lanes reading different pairs use different banks.
@@ -267,10 +252,6 @@ __device__ __forceinline__ void stage_x_store(float* xs, const f32x4u_t (&v)[XCH
     }
 }
 
-// Workgroup barrier over LDS only: waits for this thread's LDS operations but
-// not for its outstanding global loads (__syncthreads waits for those too,
-// which would drain the weight loads already in flight).
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // rows rows of x (row r at x + r * ldx, K values) into the padded layout, row
 // r at xs + r * xstride; four 16-byte chunks in flight per thread (fewer
@@ -640,523 +621,6 @@ __global__ __launch_bounds__(WAVES * 64) void k_m1c(const M1Cat<MAXP> C) {
         return true;
     };
     while (step(bufA, bufB) && step(bufB, bufA)) {
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Matrix-core operand types.
-// ---------------------------------------------------------------------------
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-// ---------------------------------------------------------------------------
-// Q4_0 codes as matrix-core operands. One qs dword holds 8 codes: the low
-// nibbles of its bytes are block elements 4u..4u+3, the high nibbles elements
-// 16+4u..16+4u+3 (u = the dword's index in the block). q4_dec turns them
-// into eight exact fp16 values code - 8 in the order
-//   [4u, 4u+2, 4u+1, 4u+3, 16+4u, 16+4u+2, 16+4u+1, 16+4u+3].
-// A low nibble n as the low byte of an fp16 whose high byte is 0x64 reads as
-// 1024 + n; a high nibble left in bits 4..7 under the high byte 0x54 reads as
-// 64 + n. v_perm_b32 builds both pairs of a dword from the masked code bytes
-// and a register holding the two high bytes, and one packed fp16 add removes
-// the offset exactly: 2 AND, 4 v_perm_b32 and 4 v_pk_add_f16 per dword.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ half8_t q4_dec(uint32_t q) {
-    const half2_t blo = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-    const half2_t bhi = {(_Float16)-72.0f, (_Float16)-72.0f};
-    const uint32_t EXPB = 0x5464u;  // byte 4 of {EXPB, v} = 0x64, byte 5 = 0x54
-    const uint32_t lo = q & 0x0F0F0F0Fu, hi = q & 0xF0F0F0F0u;
-    const half2_t t0 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(EXPB, lo, 0x04020400u)) + blo;
-    const half2_t t1 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(EXPB, lo, 0x04030401u)) + blo;
-    const half2_t t2 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(EXPB, hi, 0x05020500u)) + bhi;
-    const half2_t t3 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(EXPB, hi, 0x05030501u)) + bhi;
-    return (half8_t){t0[0], t0[1], t1[0], t1[1], t2[0], t2[1], t3[0], t3[1]};
-}
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_max(float v) {
-    const int t = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false);
-    return fmaxf(v, __builtin_bit_cast(float, t));
-}
-
-__device__ __forceinline__ uint32_t pack_h2(_Float16 a, _Float16 b) {
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
-}
-
-// ---------------------------------------------------------------------------
-// M = 2..16 kernel on the matrix cores (v_mfma_f32_16x16x32_f16).
-//
-// One MFMA multiplies 16 activation rows (A, padded with zero rows) by one
-// block of 16 weight rows (B): lane (G, j) of B supplies qs dword G of the
-// block of weight row j as 8 exact fp16 codes (code - 8). Every lane streams
-// whole 36-byte block pairs (pair 4t + G of its row at step t), so after the
-// loads each of the four lane groups holds different blocks; two 4 x 4
-// transposes across the four 16-lane rows (v_permlane16_swap, then
-// v_permlane32_swap) hand lane group G dword G of all eight blocks of the
-// step, and the same transposes gather the eight block scales. Each block
-// takes two MFMAs (x split into fp16 hi + lo), and the fp16 block scale is
-// applied in fp32 to the 16 x 16 partial: acc += d[row, block] * D.
-//
-// Activations are staged per chunk of 512 columns into LDS (double
-// buffered), already split into hi/lo and ordered as the A operands read
-// them; each activation row of a chunk is scaled by a power of two that puts
-// its largest magnitude in [2^14, 2^15) (fp16 range), undone when the chunk's
-// partial sums are added to the accumulator.
-// ---------------------------------------------------------------------------
-constexpr int MM_KC = 512;                        // activation columns per staged chunk
-constexpr int MM_CHUNK_BYTES = (MM_KC / 32) * 2 * 1024;  // blocks x {hi, lo} x 4 slices x 16 rows x 16 B
-
-// 4 x 4 transpose across the four 16-lane rows: on entry lane row R holds
-// v[c] = element (R, c); on exit it holds v[c] = element (c, R).
-__device__ __forceinline__ void xpose4(uint32_t* v) {
-    auto a = __builtin_amdgcn_permlane16_swap(v[0], v[1], false, false);
-    auto b = __builtin_amdgcn_permlane16_swap(v[2], v[3], false, false);
-    auto c = __builtin_amdgcn_permlane32_swap(a[0], b[0], false, false);
-    auto d = __builtin_amdgcn_permlane32_swap(a[1], b[1], false, false);
-    v[0] = c[0];
-    v[2] = c[1];
-    v[1] = d[0];
-    v[3] = d[1];
-}
-
-// Position (in halves) of block element e within its 8-half A/B slice.
-__device__ __forceinline__ int slice_pos(int e) {
-    const int r = e & 3;
-    return ((e >> 4) << 2) + ((r & 1) << 1 | (r >> 1));
-}
-
-template <int WAVES, int TW>
-__global__ __launch_bounds__(WAVES * 64) void k_mm(const uint8_t* __restrict__ W, size_t ldw,
-                                                   const float* __restrict__ X, size_t ldx, float* __restrict__ Y,
-                                                   size_t ldy, int M, int N, int K) {
-    extern __shared__ __align__(16) uint8_t smem[];   // 2 activation chunks
-    __shared__ float s_scale[2][16];                 // per chunk buffer: 2^-s for each activation row
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int G = lane >> 4, j = lane & 15;
-    const int P = K >> 6;
-    const int nchunks = (K + MM_KC - 1) / MM_KC;
-    const long row_base = ((long)blockIdx.x * WAVES + wave) * 16 * TW;
-
-    // ---- activation staging: thread t covers 16 columns of one row ----
-    auto stage = [&](int c, int buf) {
-        uint8_t* dst = smem + buf * MM_CHUNK_BYTES;
-        const int t = threadIdx.x;
-        for (int base = 0; base < 16 * 32; base += WAVES * 64) {
-            const int u = base + t;             // 0..511: row m = u / 32, columns (u % 32) * 16 ..
-            const int m = u >> 5, c0 = (u & 31) * 16;
-            float v[16];
-            float mx = 0.f;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int k = c * MM_KC + c0 + e;
-                v[e] = (m < M && k < K) ? X[(size_t)m * ldx + k] : 0.f;
-                mx = fmaxf(mx, fabsf(v[e]));
-            }
-            // max over the 32 threads of this row (a half wave)
-#pragma unroll
-            for (int off = 16; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 32));
-            int sh = 0;
-            if (mx > 0.f && mx <= 3.4e38f) {
-                int ex;
-                frexpf(mx, &ex);
-                sh = 15 - ex;
-                sh = sh > 126 ? 126 : (sh < -126 ? -126 : sh);
-            }
-            if ((u & 31) == 0) s_scale[buf][m] = ldexpf(1.f, -sh);
-            const int blk = c0 >> 5, e0 = c0 & 31;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const float xv = ldexpf(v[e], sh);
-                const _Float16 h = (_Float16)xv;
-                const _Float16 l = (_Float16)(xv - (float)h);
-                const int el = e0 + e, g = (el & 15) >> 2;
-                uint8_t* rec = dst + (size_t)blk * 2048 + g * 256 + m * 16 + slice_pos(el) * 2;
-                *reinterpret_cast<_Float16*>(rec) = h;
-                *reinterpret_cast<_Float16*>(rec + 1024) = l;
-            }
-        }
-    };
-
-    // ---- weight loads: one pair per lane per tile per step ----
-    const int steps_per_chunk = MM_KC / 256;
-    const int nsteps = nchunks * steps_per_chunk;
-    auto issue = [&](int step, uint32_t (&b)[TW][9]) {
-#pragma unroll
-        for (int tw = 0; tw < TW; ++tw) {
-            long row = row_base + tw * 16 + j;
-            row = row < N ? row : N - 1;
-            int q = step * 4 + G;
-            q = q < P ? q : P - 1;
-            load_pair<9>(W + row * ldw + (size_t)q * 36, b[tw]);
-        }
-    };
-
-    uint32_t b0[TW][9], b1[TW][9];
-    issue(0, b0);
-    if (nsteps > 1) issue(1, b1);
-    stage(0, 0);
-    __syncthreads();
-
-    f32x4_t acc[TW], cacc[TW];
-#pragma unroll
-    for (int tw = 0; tw < TW; ++tw) {
-        acc[tw] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-        cacc[tw] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-    }
-
-    auto compute = [&](int step, uint32_t (&r)[TW][9]) {
-        const int c = step / steps_per_chunk, buf = c & 1;
-        const uint8_t* xa = smem + buf * MM_CHUNK_BYTES + (step % steps_per_chunk) * 8 * 2048 + G * 256 + j * 16;
-        const int q = step * 4 + G;
-        const bool valid = q < P;
-#pragma unroll
-        for (int tw = 0; tw < TW; ++tw) {
-            // qs dwords of this lane's two blocks, then hand out slices
-            uint32_t v0[4], v1[4], dd[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                v0[u] = __builtin_amdgcn_alignbyte(r[tw][u + 1], r[tw][u], 2);
-                v1[u] = r[tw][5 + u];
-            }
-            // both block scales (fp16) packed in one dword; zero for pairs past K
-            const uint32_t dpk = valid ? ((r[tw][0] & 0xFFFFu) | (r[tw][4] & 0xFFFF0000u)) : 0u;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) dd[u] = dpk;
-            xpose4(v0);
-            xpose4(v1);
-            xpose4(dd);  // dd[s] = scales of lane group s's pair
-#pragma unroll
-            for (int s2 = 0; s2 < 4; ++s2) {
-#pragma unroll
-                for (int R = 0; R < 2; ++R) {
-                    const int blk = 2 * s2 + R;  // block index within the step
-                    const half8_t ah = *reinterpret_cast<const half8_t*>(xa + blk * 2048);
-                    const half8_t al = *reinterpret_cast<const half8_t*>(xa + blk * 2048 + 1024);
-                    const half8_t bq = q4_dec(R ? v1[s2] : v0[s2]);
-                    f32x4_t cc = {0.f, 0.f, 0.f, 0.f};
-                    cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bq, cc, 0, 0, 0);
-                    cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bq, cc, 0, 0, 0);
-                    const float d = R ? half_hi(dd[s2]) : half_lo(dd[s2]);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) cacc[tw][i] = fmaf(d, cc[i], cacc[tw][i]);
-                }
-            }
-        }
-        if ((step + 1) % steps_per_chunk == 0 || step + 1 == nsteps) {
-            // fold this chunk's partial sums with the chunk's activation scales
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float sc = s_scale[buf][4 * G + i];
-#pragma unroll
-                for (int tw = 0; tw < TW; ++tw) {
-                    acc[tw][i] = fmaf(sc, cacc[tw][i], acc[tw][i]);
-                    cacc[tw][i] = 0.f;
-                }
-            }
-        }
-    };
-
-    for (int step = 0; step < nsteps; step += 2) {
-        // stage the next chunk while this one is consumed
-        const int c = step / steps_per_chunk;
-        if (step % steps_per_chunk == 0 && c + 1 < nchunks) stage(c + 1, (c + 1) & 1);
-        compute(step, b0);
-        if (step + 2 < nsteps) issue(step + 2, b0);
-        if (step + 1 < nsteps) {
-            compute(step + 1, b1);
-            if (step + 3 < nsteps) issue(step + 3, b1);
-        }
-        if ((step + 2) % steps_per_chunk == 0) __syncthreads();  // chunk c consumed, c + 1 staged
-    }
-    // lane (G, j) holds rows 4G..4G+3 of activation rows, weight row j of each tile
-#pragma unroll
-    for (int tw = 0; tw < TW; ++tw) {
-        const long row = row_base + tw * 16 + j;
-        if (row < N) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int m = 4 * G + i;
-                if (m < M) Y[(size_t)m * ldy + row] = acc[tw][i];
-            }
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// M = 2..16 with an activation pre-pass, second form (the default).
-//
-// Pre-pass (k_xprep): one wave per (chunk of MM_KC = 512 columns, activation
-// row m), one thread per (block, slice). Each row of a chunk is scaled by the
-// power of two 2^s that brings its largest |x| into [2^14, 2^15) and split as
-// x * 2^s = hi + lo (fp16), written in A-operand order: per block 2 KB =
-// piece (hi, lo) x slice G x row m (16, zero past M) x 8 fp16 in q4_dec
-// order (slice-major, so the 16 lanes of one 16-byte LDS read cover all 64
-// banks once); after all blocks, the factors 2^-s as float[nchunks][16]. Scaling
-// per chunk needs no reduction across the whole row, so the pre-pass is one
-// pass with no global synchronisation.
-//
-// Main kernel (k_mm4): the WAVES waves of a workgroup own WAVES * TW tiles
-// of 16 weight rows and walk the same range of K chunk by chunk; the
-// converted activations of a chunk (32 KB + its factors) are copied into LDS
-// once for all of them (double buffered). Latency is covered by distance: a
-// chunk's activations are fetched into registers two chunks before they are
-// used, and each wave's weight loads run four steps (two chunks) ahead. Each
-// block takes two MFMAs (hi, lo); the fp16 block scale is applied in fp32 to
-// the 16 x 16 partial, and the chunk's activation factors once per chunk.
-// When there are too few tiles to fill the chip, K is split over grid.y: each
-// segment writes its partial tile sums to scratch and k_mmred adds the
-// segments in order (deterministic, no cross-workgroup synchronisation).
-// ---------------------------------------------------------------------------
-
-__global__ __launch_bounds__(256) void k_xprep(const float* __restrict__ X, size_t ldx, int M, int K,
-                                               uint8_t* __restrict__ xa, size_t xa_stride) {
-    typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
-    // block of 256 threads = (4 rows) x (16 blocks) x (4 slices) of one chunk;
-    // grid.y = 4 per block of 16 activation rows, whose records are xa_stride
-    // bytes apart
-    const int mb = blockIdx.y >> 2;
-    X += (size_t)mb * 16 * ldx;
-    M -= mb * 16;
-    xa += (size_t)mb * xa_stride;
-    const int c = blockIdx.x, m = (blockIdx.y & 3) * 4 + (threadIdx.x >> 6);
-    const int bl = (threadIdx.x >> 2) & 15, G = threadIdx.x & 3;
-    const int nb = K >> 5;
-    const int b = c * 16 + bl;
-    const bool ok = m < M && b < nb;
-    // elements 4G..4G+3 and 16+4G..19+4G of the block, in q4_dec order
-    f32x4u lo = {0.f, 0.f, 0.f, 0.f}, hi = lo;
-    if (ok) {
-        const float* src = X + (size_t)m * ldx + (size_t)b * 32 + 4 * G;
-        lo = *reinterpret_cast<const f32x4u*>(src);
-        hi = *reinterpret_cast<const f32x4u*>(src + 16);
-    }
-    const float v[8] = {lo.x, lo.z, lo.y, lo.w, hi.x, hi.z, hi.y, hi.w};
-    float mx = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(v[e]));
-    // largest |x| of the row's chunk: the 64 lanes of the wave
-    mx = dpp_max<0xB1>(mx);
-    mx = dpp_max<0x4E>(mx);
-    mx = dpp_max<0x141>(mx);
-    mx = dpp_max<0x140>(mx);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    int s = 0;
-    if (mx > 0.f && mx <= 3.4e38f) {
-        int ex;
-        frexpf(mx, &ex);
-        s = 15 - ex;
-        s = s > 126 ? 126 : (s < -126 ? -126 : s);
-    }
-    if ((threadIdx.x & 63) == 0 && m < 16) reinterpret_cast<float*>(xa + (size_t)nb * 2048)[c * 16 + m] = ldexpf(1.f, -s);
-    if (b >= nb || m >= 16) return;
-    uint32_t hw[4], lw[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        _Float16 h[2], l[2];
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const float a = ldexpf(v[2 * k + q], s);
-            h[q] = (_Float16)a;
-            float r = a - (float)h[q];
-            r = r == r ? r : 0.f;  // hi = +-inf or nan carries the value alone
-            l[q] = (_Float16)r;
-        }
-        hw[k] = pack_h2(h[0], h[1]);
-        lw[k] = pack_h2(l[0], l[1]);
-    }
-    uint8_t* rec = xa + (size_t)b * 2048 + G * 256 + m * 16;
-    *reinterpret_cast<u32x4*>(rec) = (u32x4){hw[0], hw[1], hw[2], hw[3]};
-    *reinterpret_cast<u32x4*>(rec + 1024) = (u32x4){lw[0], lw[1], lw[2], lw[3]};
-}
-
-// Y[m, n] = sum over the S segments (in order) of part[(s * M + m) * N + n].
-// All S loads are issued before the first add (S <= MM_SMAX).
-constexpr int MM_SMAX = 16;
-__global__ __launch_bounds__(256) void k_mmred(const float* __restrict__ part, int S, int M, int N,
-                                               float* __restrict__ Y, size_t ldy) {
-    const long i = (long)blockIdx.x * 256 + threadIdx.x;
-    if (i >= (long)M * N) return;
-    const int m = (int)(i / N), n = (int)(i % N);
-    float v[MM_SMAX];
-#pragma unroll
-    for (int s = 0; s < MM_SMAX; ++s) v[s] = s < S ? part[((size_t)s * M + m) * N + n] : 0.f;
-    float t = v[0];
-#pragma unroll
-    for (int s = 1; s < MM_SMAX; ++s)
-        if (s < S) t += v[s];
-    Y[(size_t)m * ldy + n] = t;
-}
-
-template <int WAVES, int TW>
-__global__ __launch_bounds__(WAVES * 64) void k_mm4(const uint8_t* __restrict__ W, size_t ldw,
-                                                    const uint8_t* __restrict__ xa, float* __restrict__ Y,
-                                                    size_t ldy, int M, int N, int K, int chunks_per_seg,
-                                                    float* __restrict__ part, int mblocks, size_t xa_stride) {
-    // blocks of 16 activation rows: block mb of tile group g is workgroup
-    // g * mblocks + mb, so the workgroups that read the same weights run
-    // side by side and share them through L2
-    const int mb = blockIdx.x % mblocks;
-    const int grp = blockIdx.x / mblocks;
-    xa += (size_t)mb * xa_stride;
-    Y += (size_t)mb * 16 * ldy;
-    M = M - mb * 16 < 16 ? M - mb * 16 : 16;
-    extern __shared__ __align__(16) uint8_t smem[];  // 2 chunks of A operands
-    __shared__ __align__(16) float sfac[2][16];      // their activation factors
-    constexpr int NT = WAVES * 64;
-    constexpr int AV = MM_CHUNK_BYTES / (NT * 16);  // 16-byte A pieces per thread per chunk
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
-    const int G = lane >> 4, j = lane & 15;
-    const int P = K >> 6;
-    const int nchunks = (K + MM_KC - 1) / MM_KC;
-    const int sgi = blockIdx.y;
-    const int c0 = sgi * chunks_per_seg;
-    const int c1 = c0 + chunks_per_seg < nchunks ? c0 + chunks_per_seg : nchunks;
-    const long row_base = ((long)grp * WAVES + wave) * 16 * TW;
-    const size_t xa_bytes = (size_t)(K / 32) * 2048;
-    const float* __restrict__ fac = reinterpret_cast<const float*>(xa + xa_bytes);
-
-    typedef uint32_t u32x4a __attribute__((ext_vector_type(4)));
-    u32x4a stg[2][AV];
-    float fst[2];
-    auto fetch_a = [&](int c, int set) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < AV; ++i) {
-            size_t off = (size_t)c * MM_CHUNK_BYTES + (size_t)(i * NT + tid) * 16;
-            off = off < xa_bytes ? off : 0;  // the tail of the last chunk is never read
-            stg[set][i] = *reinterpret_cast<const u32x4a*>(xa + off);
-        }
-        fst[set] = fac[c * 16 + (tid & 15)];
-    };
-    auto put_a = [&](int buf, int set) __attribute__((always_inline)) {
-        uint8_t* dst = smem + buf * MM_CHUNK_BYTES;
-#pragma unroll
-        for (int i = 0; i < AV; ++i) *reinterpret_cast<u32x4a*>(dst + (i * NT + tid) * 16) = stg[set][i];
-        if (tid < 16) sfac[buf][tid] = fst[set];
-    };
-    auto issue = [&](int step, uint32_t (&b)[TW][9]) {
-#pragma unroll
-        for (int tw = 0; tw < TW; ++tw) {
-            long row = row_base + tw * 16 + j;
-            row = row < N ? row : N - 1;
-            int q = step * 4 + G;
-            q = q < P ? q : P - 1;
-            load_pair<9>(W + row * ldw + (size_t)q * 36, b[tw]);
-        }
-    };
-    f32x4_t acc[TW], cacc[TW];
-#pragma unroll
-    for (int tw = 0; tw < TW; ++tw) {
-        acc[tw] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-        cacc[tw] = acc[tw];
-    }
-    auto compute = [&](int step, const uint8_t* xbuf, uint32_t (&r)[TW][9]) {
-        const bool valid = step * 4 + G < P;
-        uint32_t v0[TW][4], v1[TW][4], dd[TW][4];
-#pragma unroll
-        for (int tw = 0; tw < TW; ++tw) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                v0[tw][u] = __builtin_amdgcn_alignbyte(r[tw][u + 1], r[tw][u], 2);
-                v1[tw][u] = r[tw][5 + u];
-            }
-            const uint32_t dpk = valid ? ((r[tw][0] & 0xFFFFu) | (r[tw][4] & 0xFFFF0000u)) : 0u;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) dd[tw][u] = dpk;
-            xpose4(v0[tw]);
-            xpose4(v1[tw]);
-            xpose4(dd[tw]);
-        }
-        const uint8_t* xl = xbuf + (step & 1) * 8 * 2048 + G * 256 + j * 16;
-#pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) {
-#pragma unroll
-            for (int R = 0; R < 2; ++R) {
-                const uint8_t* rec = xl + (2 * s2 + R) * 2048;
-                const half8_t ah = *reinterpret_cast<const half8_t*>(rec);
-                const half8_t al = *reinterpret_cast<const half8_t*>(rec + 1024);
-#pragma unroll
-                for (int tw = 0; tw < TW; ++tw) {
-                    const half8_t bq = q4_dec(R ? v1[tw][s2] : v0[tw][s2]);
-                    f32x4_t cc = {0.f, 0.f, 0.f, 0.f};
-                    cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bq, cc, 0, 0, 0);
-                    cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bq, cc, 0, 0, 0);
-                    const float d = R ? half_hi(dd[tw][s2]) : half_lo(dd[tw][s2]);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) cacc[tw][i] = fmaf(d, cc[i], cacc[tw][i]);
-                }
-            }
-        }
-    };
-    auto fold = [&](int buf) {
-        const float4 f = *reinterpret_cast<const float4*>(&sfac[buf][4 * G]);
-        const float fv[4] = {f.x, f.y, f.z, f.w};
-#pragma unroll
-        for (int tw = 0; tw < TW; ++tw)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc[tw][i] = fmaf(fv[i], cacc[tw][i], acc[tw][i]);
-                cacc[tw][i] = 0.f;
-            }
-    };
-
-    // Weight steps (256 columns each) run four ahead in a ring of buffers.
-    uint32_t b0[TW][9], b1[TW][9], b2[TW][9], b3[TW][9];
-    const int st0 = 2 * c0, st1 = 2 * c1;
-    if (st0 < st1) issue(st0, b0);
-    if (st0 + 1 < st1) issue(st0 + 1, b1);
-    if (st0 + 2 < st1) issue(st0 + 2, b2);
-    if (st0 + 3 < st1) issue(st0 + 3, b3);
-    if (c0 < c1) {
-        fetch_a(c0, 0);
-        put_a(0, 0);
-    }
-    if (c0 + 1 < c1) fetch_a(c0 + 1, 1);
-    __syncthreads();
-    // chunk c is in LDS buffer (c - c0) & 1; register set (c - c0) & 1 is free
-    // once chunk c is in LDS and takes chunk c + 2.
-    auto body = [&](int c, auto BUF, uint32_t (&ba)[TW][9], uint32_t (&bb)[TW][9]) __attribute__((always_inline)) {
-        constexpr int buf = decltype(BUF)::value;
-        if (c + 2 < c1) fetch_a(c + 2, buf);
-        const uint8_t* xbuf = smem + buf * MM_CHUNK_BYTES;
-        compute(2 * c, xbuf, ba);
-        if (2 * c + 4 < st1) issue(2 * c + 4, ba);
-        compute(2 * c + 1, xbuf, bb);
-        if (2 * c + 5 < st1) issue(2 * c + 5, bb);
-        fold(buf);
-        if (c + 1 < c1) put_a(buf ^ 1, buf ^ 1);
-        __syncthreads();
-    };
-    for (int c = c0; c < c1; c += 2) {
-        body(c, std::integral_constant<int, 0>{}, b0, b1);
-        if (c + 1 < c1) body(c + 1, std::integral_constant<int, 1>{}, b2, b3);
-    }
-
-    if (gridDim.y > 1) {
-#pragma unroll
-        for (int tw = 0; tw < TW; ++tw) {
-            const long row = row_base + tw * 16 + j;
-            if (row < N) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int m = 4 * G + i;
-                    if (m < M) part[((size_t)sgi * M + m) * N + row] = acc[tw][i];
-                }
-            }
-        }
-        return;
-    }
-#pragma unroll
-    for (int tw = 0; tw < TW; ++tw) {
-        const long row = row_base + tw * 16 + j;
-        if (row < N) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int m = 4 * G + i;
-                if (m < M) Y[(size_t)m * ldy + row] = acc[tw][i];
-            }
-        }
     }
 }
 
@@ -2329,17 +1793,6 @@ constexpr int KMAX_FAST_ID = 14336;  // same, next to the id kernel's pair list
 
 constexpr size_t LDS_PER_CU = 160 * 1024;  // gfx950
 
-// Compute units of the current device (cached per device id).
-int num_cus() {
-    static int cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-    if (dev < 64 && cache[dev] > 0) return cache[dev];
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    if (dev < 64) cache[dev] = n;
-    return n;
-}
 
 // Lanes per row: the largest power of two (<= 64) whose lane utilisation
 // P / (LPR * ceil(P / LPR)) is within 5% of the best one, so long rows keep
@@ -2501,145 +1954,6 @@ int launch_m1b(const M1Prob* probs, int n, int wgs_per_cu, int waves, hipStream_
     return check_launch("qmv batched m1 kernel");
 }
 
-// M = 2..16 on the matrix cores (Q4_0, K % 64 == 0, 4-byte aligned rows).
-template <int WAVES, int TW>
-int launch_mm_t(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N, int K,
-                hipStream_t st) {
-    const long rows_wg = 16L * TW * WAVES;
-    const long grid = ((long)N + rows_wg - 1) / rows_wg;
-    if (grid > 0x7FFFFFFF) return fail(QMV_EINVAL, "N too large");
-    hipLaunchKernelGGL((k_mm<WAVES, TW>), dim3((unsigned)grid), dim3(WAVES * 64), 2 * MM_CHUNK_BYTES, st, W, ldw, X,
-                       ldx, Y, ldy, M, N, K);
-    return check_launch("qmv mfma kernel");
-}
-
-int launch_mm(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N, int K,
-              int waves, int tw, hipStream_t st) {
-    if (waves == 0) {
-        // enough workgroups to cover the chip; more rows per wave when there are plenty
-        const long tiles = ((long)N + 15) / 16;
-        waves = 4;
-        tw = tiles >= 4L * 4 * num_cus() ? 2 : 1;
-    }
-    if (waves == 4 && tw == 1) return launch_mm_t<4, 1>(W, ldw, X, ldx, Y, ldy, M, N, K, st);
-    if (waves == 4 && tw == 2) return launch_mm_t<4, 2>(W, ldw, X, ldx, Y, ldy, M, N, K, st);
-    if (waves == 8 && tw == 1) return launch_mm_t<8, 1>(W, ldw, X, ldx, Y, ldy, M, N, K, st);
-    if (waves == 8 && tw == 2) return launch_mm_t<8, 2>(W, ldw, X, ldx, Y, ldy, M, N, K, st);
-    return fail(QMV_EINVAL, "internal: no mfma kernel for waves=%d tw=%d", waves, tw);
-}
-
-// Scratch for the M >= 2 calls, one buffer per (device, stream), reused by
-// the calls that stream orders one after another and kept until the process
-// ends; a call that needs more releases the old buffer and takes a larger one,
-// both in stream order on that stream. Returns nullptr if none can be had.
-// The caller holds g_scratch_mu until its kernels are enqueued, so a buffer
-// is never released ahead of work already handed out on the same stream.
-struct StreamScratch {
-    int dev;
-    hipStream_t st;
-    void* p;
-    size_t n;
-};
-std::mutex g_scratch_mu;
-std::vector<StreamScratch> g_scratch;
-
-void* stream_scratch(hipStream_t st, size_t n) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) {
-        (void)hipGetLastError();
-        return nullptr;
-    }
-    StreamScratch* e = nullptr;
-    for (auto& c : g_scratch)
-        if (c.dev == dev && c.st == st) e = &c;
-    if (e && e->n >= n) return e->p;
-    const size_t want = (n + ((size_t)1 << 20) - 1) & ~(((size_t)1 << 20) - 1);  // whole MiB
-    void* p = nullptr;
-    if (hipMallocAsync(&p, want, st) != hipSuccess || !p) {
-        (void)hipGetLastError();
-        return nullptr;
-    }
-    if (e) {
-        if (hipFreeAsync(e->p, st) != hipSuccess) (void)hipGetLastError();
-        e->p = p;
-        e->n = want;
-    } else {
-        g_scratch.push_back({dev, st, p, want});
-    }
-    return p;
-}
-
-// M = 2..16: activation pre-pass + k_mm4 (+ k_mmred when K is split), with
-// the stream's scratch buffer. Returns QMV_EUNSUPPORTED (nothing enqueued)
-// when the buffer cannot be had or the stream is being captured (a graph
-// must not hold a buffer that later eager calls on the stream reuse), so the
-// caller can fall back to the kernel that needs none.
-// Knobs (0 = default): segments of K, waves per workgroup (4 or 8).
-// Any M: blocks of 16 activation rows side by side in one launch (each block's
-// workgroups read the weights; neighbours share them through L2).
-int launch_mm4(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N, int K,
-               int force_S, int force_waves, hipStream_t st) {
-    const int ncu = num_cus();
-    const long tiles = ((long)N + 15) / 16;
-    // Few tiles (N <= 2048): 4-wave workgroups, twice as many of them
-    // (N = 1024, M = 16: 11.6 vs 13.9 us per call).
-    const int waves = force_waves ? force_waves : (tiles <= 128 ? 4 : 8);
-    if (waves != 4 && waves != 8) return fail(QMV_EINVAL, "internal: waves=%d", waves);
-    const int mblocks = (M + 15) / 16;
-    const long groups = (tiles + waves - 1) / waves;
-    const int nchunks = (K + MM_KC - 1) / MM_KC;
-    // Split K only when the tile groups fill less than half the chip: the
-    // reduction launch costs more than a partly idle chip otherwise.
-    // (Only for one block of rows: the partial sums are laid out per call.)
-    int S = 1;
-    if (mblocks == 1 && 2 * groups <= ncu)
-        while (S < nchunks && S < MM_SMAX && groups * S < ncu) S *= 2;
-    if (force_S && mblocks == 1) S = force_S;
-    S = S > nchunks ? nchunks : S;
-    S = S > MM_SMAX ? MM_SMAX : S;
-    const int cps = (nchunks + S - 1) / S;
-    S = (nchunks + cps - 1) / cps;
-    if (groups * mblocks > 0x7FFFFFFF || S > 65535 || 4L * mblocks > 65535) return QMV_EUNSUPPORTED;
-    // No stream-ordered allocation while the stream is being captured into a
-    // graph: the caller then gets the kernel that needs no scratch.
-    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(st, &cap) != hipSuccess) {
-        (void)hipGetLastError();
-        return QMV_EUNSUPPORTED;
-    }
-    if (cap != hipStreamCaptureStatusNone) return QMV_EUNSUPPORTED;
-    const size_t xa_bytes = (size_t)(K / 32) * 2048 + (size_t)nchunks * 64;
-    const size_t xa_stride = (xa_bytes + 255) & ~(size_t)255;
-    const size_t off_part = xa_stride * mblocks;
-    const size_t part_bytes = S > 1 ? (size_t)S * M * N * sizeof(float) : 0;
-    std::lock_guard<std::mutex> lock(g_scratch_mu);
-    void* scratch = stream_scratch(st, off_part + part_bytes);
-    if (!scratch) return QMV_EUNSUPPORTED;
-    uint8_t* xa = (uint8_t*)scratch;
-    float* part = S > 1 ? (float*)(xa + off_part) : nullptr;
-    hipLaunchKernelGGL(k_xprep, dim3((unsigned)nchunks, (unsigned)(4 * mblocks)), dim3(256), 0, st, X, ldx, M, K, xa,
-                       xa_stride);
-    int rc = check_launch("qmv activation pre-pass");
-    if (rc == QMV_OK) {
-        if (waves == 4)
-            hipLaunchKernelGGL((k_mm4<4, 1>), dim3((unsigned)(groups * mblocks), (unsigned)S), dim3(256),
-                               2 * MM_CHUNK_BYTES, st, W, ldw, (const uint8_t*)xa, Y, ldy, M, N, K, cps, part, mblocks,
-                               xa_stride);
-        else
-            hipLaunchKernelGGL((k_mm4<8, 1>), dim3((unsigned)(groups * mblocks), (unsigned)S), dim3(512),
-                               2 * MM_CHUNK_BYTES, st, W, ldw, (const uint8_t*)xa, Y, ldy, M, N, K, cps, part, mblocks,
-                               xa_stride);
-        rc = check_launch("qmv mfma kernel");
-    }
-    if (rc == QMV_OK && S > 1) {
-        const long n = (long)M * N;
-        hipLaunchKernelGGL(k_mmred, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, (const float*)part, S, M, N, Y,
-                           ldy);
-        rc = check_launch("qmv split-K reduction");
-    }
-    return rc;
-}
-
 template <int QT>
 int launch_generic(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N,
                    int K, hipStream_t st) {
@@ -2692,13 +2006,8 @@ int dense(int qtype, const void* Wv, size_t ldw, const float* X, size_t ldx, flo
         return qtype == QMV_Q4_0 ? launch_m1<QMV_Q4_0>(W, ldw, X, Y, N, K, st)
                                  : launch_m1<QMV_Q8_0>(W, ldw, X, Y, N, K, st);
     }
-    const bool mm_ok = qtype == QMV_Q4_0 && M >= 2 && K > 0 && K % 64 == 0 && ((uintptr_t)W & 3) == 0 &&
-                       (ldw & 3) == 0 && ((uintptr_t)X & 3) == 0;
-    if (mm_ok) {
-        const int rc = launch_mm4(W, ldw, X, ldx, Y, ldy, M, N, K, 0, 0, st);
-        if (rc != QMV_EUNSUPPORTED) return rc;
-        return launch_mm(W, ldw, X, ldx, Y, ldy, M, N, K, 0, 0, st);
-    }
+    const bool mq_ok = M >= 2 && K > 0 && K % 64 == 0 && ((uintptr_t)W & 3) == 0 && (ldw & 3) == 0;
+    if (mq_ok) return launch_mq(qtype, W, ldw, X, ldx, Y, ldy, M, N, K, 0, 0, st);
     return qtype == QMV_Q4_0 ? launch_generic<QMV_Q4_0>(W, ldw, X, ldx, Y, ldy, M, N, K, st)
                              : launch_generic<QMV_Q8_0>(W, ldw, X, ldx, Y, ldy, M, N, K, st);
 }
@@ -3141,13 +2450,11 @@ int qmv_gemm(int qtype, const void* Wv, size_t ldw, const float* X, size_t ldx, 
     const size_t ybytes = ((size_t)(M - 1) * ldy + N) * 4;
     if (overlaps(Y, ybytes, Wv, wbytes) || overlaps(Y, ybytes, X, xbytes))
         return fail(QMV_EINVAL, "%s: Y overlaps W or X", name);
-    // Q4_0: every block of 16 rows in one matrix-core launch (blocks that
-    // read the same weights run side by side and share them through L2).
-    if (qtype == QMV_Q4_0 && M > QMV_MAX_M && K > 0 && K % 64 == 0 && ((uintptr_t)Wv & 3) == 0 && (ldw & 3) == 0) {
-        const int rc = launch_mm4((const uint8_t*)Wv, ldw, X, ldx, Y, ldy, M, N, K, 0, 0, (hipStream_t)stream);
-        if (rc != QMV_EUNSUPPORTED) return rc;
-        // under graph capture (no scratch) the blocks go through the dense call
-    }
+    // Q4_0 and Q8_0: every block of 16 rows in one matrix-core launch (blocks
+    // that read the same weights run side by side and share them through L2).
+    if ((qtype == QMV_Q4_0 || qtype == QMV_Q8_0) && M > QMV_MAX_M && K > 0 && K % 64 == 0 &&
+        ((uintptr_t)Wv & 3) == 0 && (ldw & 3) == 0)
+        return launch_mq(qtype, (const uint8_t*)Wv, ldw, X, ldx, Y, ldy, M, N, K, 0, 0, (hipStream_t)stream);
     // Blocks of up to 16 activation rows, each through the dense call of its
     // type (matrix cores for Q4_0); every block reads the weights once.
     for (int m0 = 0; m0 < M; m0 += QMV_MAX_M) {

@@ -1,0 +1,425 @@
+// qmv_mq.hip — Q4_0 / Q8_0 products with 2..16 activation rows on the matrix
+// cores of gfx950 (v_mfma_f32_16x16x32_bf16): the batched-verify shape of the
+// hf2q pages (several tokens through one `dispatch_qmatmul`, m > 1), and each
+// 16-row block of a prefill. One launch per call; the kernel needs no memory
+// beyond the caller's inputs and outputs, so a call can be captured into a
+// HIP graph as it is.
+//
+// The product per block of 32 weights: Y[m, n] += d[n] * sum_k c[n, k] X[m, k]
+// with c the integer code (Q4_0: code - 8, Q8_0: the int8 code). One MFMA
+// multiplies 16 activation rows (A) by one block of 16 weight rows (B) and
+// returns the 16 x 16 block sums; the fp16 block scale d is applied in fp32
+// to them and they are added to the running sums.
+//
+// Operands:
+//  * B: the codes as bf16, exact (Q4_0: (code - 8) / 16 from
+//    v_cvt_off_f32_i4 on code ^ 8, the 1/16 undone on output; Q8_0: the int8
+//    code). Lanes load whole 36-byte (Q4_0) or 68-byte (Q8_0) block pairs of
+//    their weight row; two 4 x 4 transposes across the wave's 16-lane rows
+//    hand every lane its MFMA slice of each of the step's 8 blocks.
+//  * A: each fp32 activation x split into two bf16, x = hi + lo + r with
+//    hi = bf16(x), lo = bf16(x - hi) (round to nearest even, |r| <= 2^-16 |x|
+//    for every finite x within the bf16 range: bf16 keeps the fp32 exponent,
+//    so no activation row needs scaling and no value can fall out of range).
+//    A finite x beyond the largest bf16 takes hi = x rounded toward zero
+//    (|r| <= 2^-15 |x|); an infinity or NaN keeps its value in hi, lo = 0. Each workgroup converts the
+//    activation columns of the step it is about to use into LDS, one step
+//    ahead, from registers loaded one step before that.
+//
+// Work split: a tile is 16 weight rows. A workgroup owns WAVES / KS tiles;
+// the KS waves of a tile take its steps (8 blocks = 256 columns) in turn,
+// so all waves of the workgroup work on the same KS consecutive steps
+// (one "round") at a time, and their partial sums are added in a fixed order
+// through LDS at the end (no atomics: bitwise reproducible). Each wave keeps
+// the weight loads of its next four rounds in flight.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "qmv.h"
+#include "qmv_internal.h"
+
+namespace qmvi {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4a_t __attribute__((ext_vector_type(4), aligned(4)));
+
+constexpr int MQ_STEP_BYTES = 8 * 2048;  // A operands of one step: 8 blocks x {hi, lo} x 4 slices x 16 rows x 16 B
+
+template <int QT>
+struct MqFmt;
+// Q4_0: a pair of blocks is 36 bytes (9 dwords). The MFMA slice G of a block
+// is qs dword G: its low nibbles are elements 4G..4G+3, its high nibbles
+// elements 16+4G..16+4G+3, in that order.
+template <>
+struct MqFmt<QMV_Q4_0> {
+    static constexpr int DW = 9;
+    static constexpr float OUT_SCALE = 16.f;
+    __host__ __device__ static constexpr int xoff(int G, int h) { return 16 * h + 4 * G; }
+};
+// Q8_0: a pair is 68 bytes (17 dwords). Slice G of a block = codes 8G..8G+7.
+template <>
+struct MqFmt<QMV_Q8_0> {
+    static constexpr int DW = 17;
+    static constexpr float OUT_SCALE = 1.f;
+    __host__ __device__ static constexpr int xoff(int G, int h) { return 8 * G + 4 * h; }
+};
+
+// Two fp32 whose low 16 bits are zero (exact bf16 values) as a bf16 pair.
+__device__ __forceinline__ uint32_t pack_bf16_exact(float a, float b) {
+    return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, a), 0x07060302u);
+}
+
+// (code - 8) / 16 for the low nibble of byte B of w, where w holds code
+// bytes XORed with 0x88 (v_cvt_off_f32_i4 reads bits [3:0] as a signed
+// 4-bit value and divides by 16).
+template <int B>
+__device__ __forceinline__ float nib(uint32_t w) {
+    float r;
+    if constexpr (B == 0) {
+        r = __builtin_amdgcn_cvt_off_f32_i4((int)w);
+    } else if constexpr (B == 1) {
+        asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(r) : "v"(w));
+    } else if constexpr (B == 2) {
+        asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(r) : "v"(w));
+    } else {
+        asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(r) : "v"(w));
+    }
+    return r;
+}
+
+// Q4_0 slice: one qs dword -> 8 bf16 (code - 8) / 16, elements
+// 4G, 4G+1, 4G+2, 4G+3, 16+4G, 16+4G+1, 16+4G+2, 16+4G+3.
+__device__ __forceinline__ bf16x8_t dec_q4(uint32_t q) {
+    const uint32_t u = q ^ 0x88888888u, u4 = u >> 4;
+    const uint32_t p0 = pack_bf16_exact(nib<0>(u), nib<1>(u));
+    const uint32_t p1 = pack_bf16_exact(nib<2>(u), nib<3>(u));
+    const uint32_t p2 = pack_bf16_exact(nib<0>(u4), nib<1>(u4));
+    const uint32_t p3 = pack_bf16_exact(nib<2>(u4), nib<3>(u4));
+    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(bf16x8_t, (u32x4v){p0, p1, p2, p3});
+}
+
+// Q8_0 slice: two code dwords -> 8 bf16 int8 codes, in byte order.
+__device__ __forceinline__ bf16x8_t dec_q8(uint32_t a, uint32_t b) {
+    auto sb = [](uint32_t w, int k) { return (float)(int8_t)(w >> (8 * k)); };
+    const uint32_t p0 = pack_bf16_exact(sb(a, 0), sb(a, 1));
+    const uint32_t p1 = pack_bf16_exact(sb(a, 2), sb(a, 3));
+    const uint32_t p2 = pack_bf16_exact(sb(b, 0), sb(b, 1));
+    const uint32_t p3 = pack_bf16_exact(sb(b, 2), sb(b, 3));
+    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(bf16x8_t, (u32x4v){p0, p1, p2, p3});
+}
+
+// Eight activations -> A operand record: hi (4 dwords) and lo (4 dwords).
+constexpr float BF16_MAX = 0x1.fcp127f;  // largest finite bf16 (0x7F7F)
+__device__ __forceinline__ void split_bf16(const float (&v)[8], uint32_t (&hw)[4], uint32_t (&lw)[4]) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    // All eight finite and below the largest bf16: the common case, taken by
+    // the whole wave or not at all.
+    bool ok = true;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ok = ok && fabsf(v[e]) < BF16_MAX;
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(!ok) == 0, 1)) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const bf16x2 h = {(__bf16)v[2 * k], (__bf16)v[2 * k + 1]};
+            const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+            const float r0 = v[2 * k] - __builtin_bit_cast(float, hb << 16);
+            const float r1 = v[2 * k + 1] - __builtin_bit_cast(float, hb & 0xFFFF0000u);
+            const bf16x2 l = {(__bf16)r0, (__bf16)r1};
+            hw[k] = hb;
+            lw[k] = __builtin_bit_cast(uint32_t, l);
+        }
+    } else {
+        // per element: as above below the largest bf16; a larger finite x
+        // takes hi = x rounded toward zero (finite) and lo = bf16(x - hi); an
+        // infinity keeps its value in hi and a NaN stays a NaN, with lo = 0
+        uint16_t h[8], l[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float x = v[e];
+            const uint32_t xb = __builtin_bit_cast(uint32_t, x);
+            if (fabsf(x) < BF16_MAX) {
+                const __bf16 hx = (__bf16)x;
+                h[e] = __builtin_bit_cast(uint16_t, hx);
+                l[e] = __builtin_bit_cast(uint16_t, (__bf16)(x - (float)hx));
+            } else if (fabsf(x) <= 0x1.fffffep127f) {
+                h[e] = (uint16_t)(xb >> 16);
+                l[e] = __builtin_bit_cast(uint16_t, (__bf16)(x - __builtin_bit_cast(float, xb & 0xFFFF0000u)));
+            } else {
+                h[e] = (uint16_t)((xb >> 16) | (x != x ? 0x0040u : 0u));
+                l[e] = 0;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            hw[k] = h[2 * k] | ((uint32_t)h[2 * k + 1] << 16);
+            lw[k] = l[2 * k] | ((uint32_t)l[2 * k + 1] << 16);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The kernel. grid.x = (tile groups) * mblocks, the 16-row block of X / Y
+// fastest, so the workgroups that read one weight tile run side by side.
+// ---------------------------------------------------------------------------
+template <int QT, int WAVES, int KS>
+__global__ __launch_bounds__(WAVES * 64) void k_mq(const uint8_t* __restrict__ W, size_t ldw,
+                                                   const float* __restrict__ X, size_t ldx, float* __restrict__ Y,
+                                                   size_t ldy, int M, int N, int K, int mblocks) {
+    using F = MqFmt<QT>;
+    constexpr int DW = F::DW, PB = 4 * DW;
+    constexpr int NT = WAVES * 64;
+    constexpr int TWG = WAVES / KS;            // tiles per workgroup
+    constexpr int REC = 512 * KS;              // A records (16 B hi + 16 B lo) per round
+    constexpr int RPT = (REC + NT - 1) / NT;   // records per thread
+    // activation register sets in flight (fewer with the 68-byte Q8_0 pairs)
+    constexpr int XS = (QT == QMV_Q8_0 && RPT <= 2) ? 2 : RPT <= 4 ? 4 : 2;
+    constexpr int ROUND_BYTES = KS * MQ_STEP_BYTES;
+    extern __shared__ __align__(16) uint8_t smem[];  // A operands of two rounds
+
+    const int mb = blockIdx.x % mblocks;
+    const long grp = blockIdx.x / mblocks;
+    X += (size_t)mb * 16 * ldx;
+    Y += (size_t)mb * 16 * ldy;
+    const int Mb = M - mb * 16 < 16 ? M - mb * 16 : 16;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int G = lane >> 4, j = lane & 15;
+    const int tw = wave / KS, sp = wave % KS;
+    const long row0 = (grp * TWG + tw) * 16;
+    const int P = K >> 6;             // block pairs per row
+    const int S = (P + 3) >> 2;       // steps per row
+    const int nb = K >> 5;            // blocks per row
+    const int rounds = (S + KS - 1) / KS;
+    long wr = row0 + j;
+    wr = wr < N ? wr : N - 1;
+    const uint8_t* __restrict__ wrow = W + wr * ldw;
+
+    // ---- weights: the pair 4t + G of this lane's row, t = this wave's step of round r
+    auto issue = [&](int r, uint32_t (&b)[DW]) __attribute__((always_inline)) {
+        int q = (r * KS + sp) * 4 + G;
+        q = q < P ? q : P - 1;  // past the row end: the last pair again (not used)
+        load_pair<DW>(wrow + (size_t)q * PB, b);
+    };
+    // ---- activations. Record rho of a round = (step in round, block, slice
+    // G, row m) with rho = tid + i * NT: every record of a thread has the
+    // thread's own (G, m) = (lane / 16, lane % 16) and block (wave + i * WAVES)
+    // of the round. Every lane loads from a valid address (rows past M and
+    // blocks past K clamped), so the loads carry no branch and the wait before
+    // their use counts exactly the loads issued after them; such records are
+    // stored as zeros.
+    const bool mok = j < Mb;
+    const float* __restrict__ xb = X + (size_t)(mok ? j : Mb - 1) * ldx + F::xoff(G, 0);
+    constexpr int XD = F::xoff(0, 1) - F::xoff(0, 0);  // second 4-float run of a record
+    auto fetch_x = [&](int r, f32x4a_t (&xr)[RPT][2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            int blk = r * 8 * KS + wave + i * WAVES;
+            blk = blk < nb ? blk : nb - 1;
+            const float* src = xb + (size_t)blk * 32;
+            xr[i][0] = *reinterpret_cast<const f32x4a_t*>(src);
+            xr[i][1] = *reinterpret_cast<const f32x4a_t*>(src + XD);
+        }
+    };
+    auto put_x = [&](int r, int buf, const f32x4a_t (&xr)[RPT][2]) __attribute__((always_inline)) {
+        uint8_t* base = smem + buf * ROUND_BYTES + wave * 2048 + lane * 16;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            uint8_t* rec = base + i * WAVES * 2048;
+            u32x4 hi = {0u, 0u, 0u, 0u}, lo = hi;
+            if (mok && r * 8 * KS + wave + i * WAVES < nb) {
+                const float v[8] = {xr[i][0].x, xr[i][0].y, xr[i][0].z, xr[i][0].w,
+                                    xr[i][1].x, xr[i][1].y, xr[i][1].z, xr[i][1].w};
+                uint32_t hw[4], lw[4];
+                split_bf16(v, hw, lw);
+                hi = (u32x4){hw[0], hw[1], hw[2], hw[3]};
+                lo = (u32x4){lw[0], lw[1], lw[2], lw[3]};
+            }
+            *reinterpret_cast<u32x4*>(rec) = hi;
+            *reinterpret_cast<u32x4*>(rec + 1024) = lo;
+        }
+    };
+
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    // ---- one step: 8 blocks of the tile (2 per lane group, pair 4t + c for lane group c)
+    auto compute = [&](int r, const uint32_t (&b)[DW]) __attribute__((always_inline)) {
+        const int t = r * KS + sp;
+        const bool valid = t * 4 + G < P;
+        const uint8_t* xa = smem + (r & 1) * ROUND_BYTES + sp * MQ_STEP_BYTES + G * 256 + j * 16;
+        // both block scales of this lane's pair in one dword; zero past K
+        uint32_t dd[4];
+        const uint32_t dpk = valid ? ((b[0] & 0xFFFFu) | (QT == QMV_Q4_0 ? (b[4] & 0xFFFF0000u) : (b[8] & 0xFFFF0000u))) : 0u;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dd[c] = dpk;
+        xpose4(dd);  // dd[c] = scales of lane group c's pair
+        // B slices of the step's 8 blocks: slice of block 2c + R in bq_src(c, R)
+        uint32_t v0[4], v1[4], w0[4], w1[4];
+        if constexpr (QT == QMV_Q4_0) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                v0[u] = __builtin_amdgcn_alignbyte(b[u + 1], b[u], 2);
+                v1[u] = b[5 + u];
+            }
+            xpose4(v0);  // v0[c] = qs dword G of the first block of pair c
+            xpose4(v1);
+        } else {
+            // block 0 codes at bytes 2..33 (dwords 0..8, shifted by 2), block 1 at 36..67 (dwords 9..16)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                v0[u] = __builtin_amdgcn_alignbyte(b[2 * u + 1], b[2 * u], 2);
+                w0[u] = __builtin_amdgcn_alignbyte(b[2 * u + 2], b[2 * u + 1], 2);
+                v1[u] = b[9 + 2 * u];
+                w1[u] = b[10 + 2 * u];
+            }
+            xpose4(v0);  // v0[c] = code dword 2G of the first block of pair c
+            xpose4(w0);  //          w0[c]: code dword 2G + 1
+            xpose4(v1);
+            xpose4(w1);
+        }
+        // A operands one block ahead of the one being multiplied
+        bf16x8_t ah[2], al[2];
+        ah[0] = *reinterpret_cast<const bf16x8_t*>(xa);
+        al[0] = *reinterpret_cast<const bf16x8_t*>(xa + 1024);
+#pragma unroll
+        for (int blk = 0; blk < 8; ++blk) {
+            const int c = blk >> 1, R = blk & 1;
+            if (blk + 1 < 8) {
+                ah[(blk + 1) & 1] = *reinterpret_cast<const bf16x8_t*>(xa + (blk + 1) * 2048);
+                al[(blk + 1) & 1] = *reinterpret_cast<const bf16x8_t*>(xa + (blk + 1) * 2048 + 1024);
+            }
+            bf16x8_t bq;
+            if constexpr (QT == QMV_Q4_0)
+                bq = dec_q4(R ? v1[c] : v0[c]);
+            else
+                bq = R ? dec_q8(v1[c], w1[c]) : dec_q8(v0[c], w0[c]);
+            f32x4_t cc = {0.f, 0.f, 0.f, 0.f};
+            cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[blk & 1], bq, cc, 0, 0, 0);
+            cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[blk & 1], bq, cc, 0, 0, 0);
+            const float d = R ? half_hi(dd[c]) : half_lo(dd[c]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = fmaf(d, cc[i], acc[i]);
+        }
+    };
+
+    // ---- pipeline: weights four rounds ahead; activations converted one
+    // round ahead, from
+    // registers loaded XS rounds before that (XS register sets, X(k) in set
+    // k % XS). Loads past the last round read valid addresses and are not
+    // used, so that no load is conditional (a conditional load makes the
+    // compiler wait for all loads).
+    f32x4a_t xr[XS][RPT][2];
+    uint32_t b0[DW], b1[DW], b2[DW], b3[DW];
+    fetch_x(0, xr[0]);  // before the weight loads: waiting for it leaves them in flight
+    issue(0, b0);
+    issue(1, b1);
+    issue(2, b2);
+    issue(3, b3);
+    put_x(0, 0, xr[0]);
+#pragma unroll
+    for (int k = 1; k <= XS; ++k) fetch_x(k, xr[k % XS]);
+    lds_barrier();
+    // round r: its step, the weights of round r + 4, the activations of
+    // round r + 1 into LDS and those of round r + 1 + XS into the freed set
+    auto body = [&](int r, uint32_t (&bb)[DW], auto SET) __attribute__((always_inline)) {
+        constexpr int xs = decltype(SET)::value;
+        compute(r, bb);
+        issue(r + 4, bb);
+        put_x(r + 1, (r + 1) & 1, xr[xs]);
+        fetch_x(r + 1 + XS, xr[xs]);
+        lds_barrier();
+        // rounds stay apart: no work of the next round is hoisted above the
+        // barrier (it would only hold registers)
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    using S1 = std::integral_constant<int, 1 % XS>;
+    using S2 = std::integral_constant<int, 2 % XS>;
+    using S3 = std::integral_constant<int, 3 % XS>;
+    using S0 = std::integral_constant<int, 0>;
+    // Whole groups of four rounds in the loop, the rest after it: every path
+    // into the loop's first round then has the same loads in flight.
+    int r = 0;
+    for (; r + 4 <= rounds; r += 4) {
+        body(r, b0, S1{});
+        body(r + 1, b1, S2{});
+        body(r + 2, b2, S3{});
+        body(r + 3, b3, S0{});
+    }
+    if (r < rounds) body(r, b0, S1{});
+    if (r + 1 < rounds) body(r + 1, b1, S2{});
+    if (r + 2 < rounds) body(r + 2, b2, S3{});
+
+    // ---- the KS partial sums of a tile, added in order sp = 0, 1, ...
+    // lane (G, j) holds activation rows 4G..4G+3 of weight row j
+    if constexpr (KS > 1) {
+        f32x4_t* red = reinterpret_cast<f32x4_t*>(smem);  // [tile][sp - 1][lane]
+        if (sp > 0) red[(tw * (KS - 1) + sp - 1) * 64 + lane] = acc;
+        lds_barrier();
+        if (sp > 0) return;
+#pragma unroll
+        for (int s = 1; s < KS; ++s) {
+            const f32x4_t o = red[(tw * (KS - 1) + s - 1) * 64 + lane];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] += o[i];
+        }
+    }
+    const long row = row0 + j;
+    if (row < N) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = 4 * G + i;
+            if (m < Mb) Y[(size_t)m * ldy + row] = acc[i] * F::OUT_SCALE;
+        }
+    }
+}
+
+template <int QT, int WAVES, int KS>
+int launch_mq_t(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N, int K,
+                hipStream_t st) {
+    constexpr int TWG = WAVES / KS;
+    const long tiles = ((long)N + 15) / 16;
+    const long groups = (tiles + TWG - 1) / TWG;
+    const long mblocks = ((long)M + 15) / 16;
+    if (groups * mblocks > 0x7FFFFFFF) return fail(QMV_EINVAL, "N too large");
+    const size_t lds = (size_t)2 * KS * MQ_STEP_BYTES;
+    hipLaunchKernelGGL((k_mq<QT, WAVES, KS>), dim3((unsigned)(groups * mblocks)), dim3(WAVES * 64), lds, st, W, ldw,
+                       X, ldx, Y, ldy, M, N, K, (int)mblocks);
+    return check_launch("qmv matrix-core kernel");
+}
+
+template <int QT>
+int launch_mq_q(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N, int K,
+                int waves, int ks, hipStream_t st) {
+    if (waves == 0) {
+        // Many tiles: one wave per tile over all of K, eight tiles per
+        // workgroup (the activation conversion shared by 128 weight rows).
+        // Fewer tiles: two tiles per workgroup, each split over two waves
+        // (graph-timed, M = 16, K = 5120: N = 27648 33 us; N = 5120 and 1024
+        // 24 us, where every workgroup still reads and converts all of X).
+        const long tiles = ((long)N + 15) / 16;
+        if (tiles >= 4L * num_cus()) {
+            waves = 8;
+            ks = 1;
+        } else {
+            waves = 4;
+            ks = 2;
+        }
+    }
+    if (waves == 8 && ks == 1) return launch_mq_t<QT, 8, 1>(W, ldw, X, ldx, Y, ldy, M, N, K, st);
+    if (waves == 4 && ks == 2) return launch_mq_t<QT, 4, 2>(W, ldw, X, ldx, Y, ldy, M, N, K, st);
+
+    return fail(QMV_EINVAL, "internal: no matrix-core kernel for waves=%d ks=%d", waves, ks);
+}
+
+}  // namespace
+
+int launch_mq(int qtype, const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N,
+              int K, int waves, int ks, hipStream_t st) {
+    return qtype == QMV_Q4_0 ? launch_mq_q<QMV_Q4_0>(W, ldw, X, ldx, Y, ldy, M, N, K, waves, ks, st)
+                             : launch_mq_q<QMV_Q8_0>(W, ldw, X, ldx, Y, ldy, M, N, K, waves, ks, st);
+}
+
+}  // namespace qmvi

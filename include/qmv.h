@@ -34,26 +34,24 @@
  *
  * Conventions for every entry point:
  *  - All array arguments are DEVICE pointers, owned by the caller. The
- *    library never synchronizes; each call only enqueues work on `stream`
- *    (a hipStream_t; NULL = the null stream) and returns. The only memory it
- *    takes is for the dense Q4_0 calls with M >= 2: a scratch buffer per
- *    (device, stream), taken with hipMallocAsync on that stream at the first
- *    call that needs it (grown the same way, old buffer released with
- *    hipFreeAsync in stream order) and kept until the process ends; a call
- *    needs K/32 * 2 KiB + ceil(K/512) * 64 bytes (the activations converted
- *    to the matrix-core operand layout) plus, when K is split over up to 16
- *    workgroups per tile, 4 * S * M * N bytes of partial sums, rounded up to
- *    whole MiB. If it cannot be had, or if `stream` is being captured into a
- *    HIP graph, the call uses a (slower) kernel that needs no scratch, so
- *    every call can be captured. Calls on one stream are ordered by the
- *    stream and share its buffer safely.
+ *    library never synchronizes and never allocates or frees memory: each
+ *    call only enqueues kernels on `stream` (a hipStream_t; NULL = the null
+ *    stream) that read the inputs and write the outputs, and returns. Every
+ *    call can therefore be captured into a HIP graph as it is.
  *  - Arguments are validated on the host before any HIP call. A rejected call
  *    launches nothing, returns a negative status and sets a thread-local
  *    message readable with qmv_last_error().
  *  - Y is overwritten (not accumulated into) and must not overlap W, X, the
  *    ids or the scales.
  *  - Results: each output element is an fp32 sum whose error against the
- *    exact value is far below 1e-4 * sum_k |w_k x_k| + 1e-6. Runs on the same
+ *    exact value is below 1e-4 * sum_k |w_k x_k| + 1e-6. With M >= 2 the
+ *    Q4_0 / Q8_0 products run on the matrix cores with each activation
+ *    split into two bf16 (x = hi + lo, relative error at most 2^-16, the
+ *    fp32 exponent range kept), so that bound holds for every finite input
+ *    whose block sums stay within the fp32 range: the code sum of a block,
+ *    sum_k c_k x_k (c = code - 8 or the int8 code), is formed before the
+ *    block scale is applied, which is always in range for |x| < 2^116.
+ *    Non-finite activations propagate as in exact arithmetic (inf * 0 = NaN). Runs on the same
  *    inputs and the same device give bitwise-identical outputs (no atomics).
  *  - Calls are reentrant; concurrent calls on different streams are safe as
  *    long as their outputs do not overlap.
@@ -168,15 +166,15 @@ int qmv_q5_k(const void* W, size_t ldw_bytes, const float* X, size_t ldx, float*
  * quantized weight pre-dequantized to F16 after load, so that
  * `dispatch_qmatmul` takes an F16-input matmul for m > 8; about 1 GB extra,
  * +16% prefill at 2K tokens). Here the weights
- * stay block-quantized: the rows of X go in blocks of 16 through the dense
- * call of the type (matrix cores for Q4_0), each block reading the weights
- * once, so the weight traffic is ceil(M/16) times that of one call.
+ * stay block-quantized: the rows of X go in blocks of 16 through the
+ * product of the type (matrix cores for Q4_0 and Q8_0), each block reading
+ * the weights, so the weight traffic is up to ceil(M/16) times that of one
+ * call (blocks that read a weight tile run side by side and share it in L2).
  *
  *  qtype   QMV_Q4_0, QMV_Q8_0, QMV_Q5_K or QMV_Q6_K.
  *  M       >= 0 (0: nothing to do); other arguments and rules as qmv_q4_0
- *          (qmv_q6_k / qmv_q5_k for the super-block types). With M > 16 and
- *          Q4_0 the call takes the per-stream scratch of qmv_q4_0's M >= 2
- *          path, once per block of rows, in stream order.
+ *          (qmv_q6_k / qmv_q5_k for the super-block types). Q4_0 and Q8_0
+ *          take all blocks of 16 rows in one matrix-core launch.
  */
 int qmv_gemm(int qtype, const void* W, size_t ldw_bytes, const float* X, size_t ldx, float* Y, size_t ldy,
              int M, int N, int K, void* stream);

@@ -200,29 +200,84 @@ def test_multi_row_x_with_strides(qtype, M):
     assert np.all(np.isnan(y[:, N:]))  # the row padding of Y is left alone
 
 
+@pytest.mark.parametrize("qtype", ["q4_0", "q8_0"])
 @pytest.mark.parametrize("M", [5, 16])
-@pytest.mark.parametrize("N,K", [(64, 5120), (4100, 2112), (300, 1088), (27, 64)])
-def test_multi_row_split_k_and_ragged_chunks(M, N, K):
-    """Q4_0, M >= 2: few tiles (K split over workgroups and summed by a second
-    launch), K not a multiple of the 512-column chunk, N not a multiple of 16."""
-    W = synth.make_weights("q4_0", N, K, cfg=94, part=M)
+@pytest.mark.parametrize("N,K", [(64, 5120), (4100, 2112), (300, 1088), (27, 64), (16400, 704), (65552, 256)])
+def test_multi_row_launch_shapes_and_ragged_steps(qtype, M, N, K):
+    """M >= 2 on the matrix cores: few tiles (K split over 4 or 2 waves of a
+    tile), many tiles (one wave per tile, workgroups of 4 and 8 waves), K not
+    a multiple of the 256-column step, N not a multiple of 16."""
+    W = synth.make_weights(qtype, N, K, cfg=94, part=M)
     X = synth.make_x(M, K, cfg=94, part=M)
-    check("q4_0", W, X, f"M={M} N={N} K={K}")
+    check(qtype, W, X, f"{qtype} M={M} N={N} K={K}")
 
 
-def test_multi_row_dynamic_range_per_chunk():
-    """Activations spanning 2^-58..2^58 with a different scale in every row
-    and every 512-column chunk."""
+@pytest.mark.parametrize("qtype", ["q4_0", "q8_0"])
+def test_multi_row_dynamic_range(qtype):
+    """Activations spanning e^-60..e^60 (about 2^-87..2^87), a different
+    scale in every row and every 512 columns."""
     M, N, K = 16, 384, 3072
-    W = synth.make_weights("q4_0", N, K, cfg=93)
+    W = synth.make_weights(qtype, N, K, cfg=93)
     r = np.random.default_rng(93)
     X = synth.make_x(M, K, cfg=93) * np.exp(r.uniform(-40, 40, (M, K)))
     X *= np.exp(r.uniform(-20, 20, (M, K // 512, 1))).repeat(512, axis=2).reshape(M, K)
-    check("q4_0", W, X.astype(np.float32), "dynamic range M=16")
+    check(qtype, W, X.astype(np.float32), "dynamic range M=16")
+
+
+@pytest.mark.parametrize("outlier", [1e9, 1e10, 1e30, 3.3e38])
+def test_multi_row_outlier_on_a_zero_weight(outlier):
+    """One huge activation on a column whose weights are all exactly zero
+    (code 8): the other columns must keep their full precision, so the
+    result meets the tolerance built from the small terms alone."""
+    M, N, K = 16, 96, 2048
+    W = synth.make_weights("q4_0", N, K, cfg=88)
+    col = 517
+    blk = W.reshape(N, K // 32, 18)
+    q = blk[:, col // 32, 2 + (col % 32) % 16]
+    blk[:, col // 32, 2 + (col % 32) % 16] = (q & 0x0F) | 0x80 if col % 32 >= 16 else (q & 0xF0) | 0x08
+    X = synth.make_x(M, K, cfg=88)
+    X[:, col] = np.float32(outlier)
+    X[3, col + 1] = np.float32(outlier)  # one row also has it on a nonzero weight
+    r = check("q4_0", W, X, f"outlier {outlier:g}")
+    print(f"outlier {outlier:g}: max ratio {r:.3g}")
+
+
+@pytest.mark.parametrize("qtype", ["q4_0", "q8_0"])
+@pytest.mark.parametrize("M", [1, 16])
+def test_non_finite_activations_propagate(qtype, M):
+    """x = +inf at one column: y is +-inf where that column's weight is
+    nonzero (sign of the weight) and NaN where it is zero (0 * inf); a NaN in
+    x makes its row NaN; in Q4_0 a finite x beyond the largest bf16 (3.39e38)
+    is an ordinary value (in Q8_0 the unscaled block sum, up to 127 |x|,
+    would leave the fp32 range: the stated limit is |x| < 2^116)."""
+    N, K = 200, 1024
+    W = synth.make_weights(qtype, N, K, cfg=87)
+    deq = np.stack([oracle.dequant_row(qtype, W[n], K) for n in range(N)])
+    X = synth.make_x(M, K, cfg=87) * np.float32(1e-3)
+    k_inf = 300
+    X[0, k_inf] = np.inf
+    if M > 1:
+        X[1, 5] = np.nan
+        if qtype == "q4_0":
+            X[2, 700] = np.float32(3.395e38)
+            X[3, 701] = np.float32(-3.4e38)
+        else:
+            X[2, 700] = np.float32(2.0**115)
+            X[3, 701] = np.float32(-(2.0**115))
+    y, _ = run(qtype, W, X)
+    w = deq[:, k_inf]
+    assert np.array_equal(np.isnan(y[0]), w == 0), "NaN exactly where the weight is zero"
+    nz = w != 0
+    assert np.all(np.isinf(y[0][nz])) and np.array_equal(np.sign(y[0][nz]), np.sign(w[nz]))
+    if M > 1:
+        assert np.all(np.isnan(y[1]))
+        rows = [m for m in range(M) if m not in (0, 1)]
+        yo, a = oracle.qmv(qtype, W, X[rows])
+        assert_within_tol(y[rows], yo, a, f"{qtype} finite rows")
 
 
 def test_multi_row_deterministic_bitwise():
-    M, N, K = 16, 200, 5120  # K split over several workgroups
+    M, N, K = 16, 200, 5120  # K split over the waves of a tile
     W = synth.make_weights("q4_0", N, K, cfg=92)
     X = synth.make_x(M, K, cfg=92)
     y1, _ = run("q4_0", W, X)

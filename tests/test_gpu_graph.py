@@ -1,9 +1,8 @@
 """Calls captured into a HIP graph and replayed (needs an MI355X).
 
-Every call can be captured: under capture, the dense Q4_0 call with M >= 2
-uses the kernel that needs no scratch memory (no stream-ordered allocation
-is recorded). Each replay is checked against the oracle (and, where the same
-kernel runs eagerly, bit for bit against the eager result), with eager work
+Every call can be captured as it is: the library allocates nothing, so a
+captured call runs the same kernels as an eager one. Each replay is checked
+against the oracle and bit for bit against the eager result, with eager work
 and synchronisations between replays.
 """
 import numpy as np
@@ -20,7 +19,9 @@ DEV = "cuda:0"
 
 
 def test_graph_replays_dense_and_batch():
-    cases = [(1, 300, 4096), (16, 64, 5120), (7, 700, 1088)]  # M = 1; M = 16 few tiles; ragged chunks
+    # M = 1; M = 16 with few tiles (K split over the waves of a tile); ragged
+    # steps; M = 16 at N = 27648, K = 5120 (one wave per tile over all of K)
+    cases = [(1, 300, 4096), (16, 64, 5120), (7, 700, 1088), (16, 27648, 5120)]
     data = []
     for i, (M, N, K) in enumerate(cases):
         W = synth.make_weights("q4_0", N, K, cfg=91, part=i)
@@ -39,11 +40,12 @@ def test_graph_replays_dense_and_batch():
             qmv.qmv_q4_0(Wd, Xd, Yd)
         qmv.qmv_batch("q4_0", [(Wbd[k], xbd, ybd[k]) for k in range(2)])
 
-    # eager reference for the M = 1 and batch calls (same kernels as in the graph)
+    # eager reference (the same kernels as in the graph)
     calls()
     torch.cuda.synchronize()
-    eager_m1 = data[0][4].cpu().numpy().copy()
+    eager = [d[4].cpu().numpy().copy() for d in data]
     eager_b = [y.cpu().numpy().copy() for y in ybd]
+    refs = [oracle.qmv("q4_0", W, X) for W, X, _, _, _ in data]
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -62,10 +64,9 @@ def test_graph_replays_dense_and_batch():
         g.replay()
         torch.cuda.synchronize()
         outs = [d[4].cpu().numpy().copy() for d in data]
-        for (W, X, _, _, _), y, (M, N, K) in zip(data, outs, cases):
-            yo, a = oracle.qmv("q4_0", W, X)
+        for y, e, (yo, a), (M, N, K) in zip(outs, eager, refs, cases):
             assert_within_tol(y, yo, a, f"replay {rep} M={M} N={N} K={K}")
-        assert np.array_equal(outs[0].view(np.uint32), eager_m1.view(np.uint32))
+            assert np.array_equal(y.view(np.uint32), e.view(np.uint32)), f"replay {rep} M={M} N={N}: not the eager bits"
         for k in range(2):
             assert np.array_equal(ybd[k].cpu().numpy().view(np.uint32), eager_b[k].view(np.uint32))
         if first is None:
