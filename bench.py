@@ -175,17 +175,22 @@ def time_steps(fn, sets, steps, warmup):
     return e0.elapsed_time(e1) / 1e3
 
 
-def m16_throughput(dev, qtype="q4_0", steps=40):
+def m16_throughput(dev, qtype="q4_0", steps=40, workspace=True):
     """Config 3 (M = 16, K = 5120, N in {5120, 1024, 27648}; Q4_0, or the same
     shapes in Q8_0): each matrix timed on its own, graph-timed over enough
     rotated device copies to stream at least 1.07 GB per sweep (R = 73, 365
-    and 14 copies in Q4_0), several calls per graph replay. The set figure is
-    the three matrices' bytes over the sum of their times."""
+    and 14 copies in Q4_0), several calls per graph replay. With `workspace`
+    the calls go through qmv_ws with a workspace of qmv_ws_bytes() bytes
+    allocated once beforehand (the matrices with few rows then split K over
+    workgroups); without, through qmv_q4_0 / qmv_q8_0. The set figure is the
+    three matrices' bytes over the sum of their times."""
     import torch
 
     from block_quantized_weight_qmatmul_amd import qmv, synth
     fn = {"q4_0": qmv.qmv_q4_0, "q8_0": qmv.qmv_q8_0}[qtype]
-    out, tot_b, tot_t = {"workload": f"{qtype}_m16_k5120_n5120_1024_27648", "timing": "graph"}, 0, 0.0
+    out = {"workload": f"{qtype}_m16_k5120_n5120_1024_27648", "timing": "graph",
+           "entry": "qmv_ws" if workspace else f"qmv_{qtype}"}
+    tot_b, tot_t = 0, 0.0
     for part, p in enumerate(synth.CONFIGS[3]["problems"]):
         W = synth.make_weights(qtype, p.N, p.K, cfg=3, part=part)
         X = synth.make_x(p.M, p.K, cfg=3, part=part)
@@ -193,14 +198,20 @@ def m16_throughput(dev, qtype="q4_0", steps=40):
         R = max(4, -(-int(1.07e9) // nb))
         Wd, Xd = torch.from_numpy(W).to(dev), torch.from_numpy(X).to(dev)
         sets = [(Wd if r == 0 else Wd.clone(), Xd, torch.empty((p.M, p.N), device=dev)) for r in range(R)]
+        wsb = qmv.ws_bytes(qtype, p.M, p.N, p.K)
+        ws = torch.empty(max(256, wsb), dtype=torch.uint8, device=dev) if workspace else None
         n = max(steps, R)
-        t = time_steps(lambda s: fn(s[0], s[1], s[2]), sets, n, R) / n
-        out[f"n{p.N}"] = {"weight_bytes": nb, "rotated_copies": R, "us_per_call": round(t * 1e6, 2),
-                          "GBps": round(nb / t / 1e9, 1), "pct_hbm_peak": round(100 * nb / t / 1e9 / HBM_PEAK_GBS, 2),
+        if workspace:
+            t = time_steps(lambda s: qmv.qmv_ws(qtype, s[0], s[1], s[2], ws), sets, n, R) / n
+        else:
+            t = time_steps(lambda s: fn(s[0], s[1], s[2]), sets, n, R) / n
+        out[f"n{p.N}"] = {"weight_bytes": nb, "rotated_copies": R, "workspace_bytes": wsb if workspace else 0,
+                          "us_per_call": round(t * 1e6, 2), "GBps": round(nb / t / 1e9, 1),
+                          "pct_hbm_peak": round(100 * nb / t / 1e9 / HBM_PEAK_GBS, 2),
                           "TFLOPs": round(2.0 * p.M * p.N * p.K / t / 1e12, 2)}
         tot_b += nb
         tot_t += t
-        del sets, Wd, Xd
+        del sets, Wd, Xd, ws
         torch.cuda.empty_cache()
     out.update({"weight_bytes": tot_b, "us_per_set": round(tot_t * 1e6, 2), "GBps": round(tot_b / tot_t / 1e9, 1),
                 "pct_hbm_peak": round(100 * tot_b / tot_t / 1e9 / HBM_PEAK_GBS, 2)})
@@ -662,6 +673,7 @@ def main():
         extra["q4_0_m1_2048x2048"] = dense_m1_throughput(dev, 0)
         extra["q8_0_m1"] = dense_m1_throughput(dev, 2)
         extra["m16"] = m16_throughput(dev)
+        extra["m16_no_workspace"] = m16_throughput(dev, workspace=False)
         extra["m16_q8_0"] = m16_throughput(dev, "q8_0")
         extra["moe_t1"] = moe_throughput(dev, 1)
         extra["moe_t32"] = moe_throughput(dev, 32)

@@ -1973,9 +1973,12 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     return na && nb && pa < pb + nb && pb < pa + na;
 }
 
+// The dense product (qmv_q4_0 / qmv_q8_0 / qmv_ws): validation, then the
+// kernel for the shape. ws: an optional caller workspace for M >= 2
+// (ws_bytes of it), overlap-checked like the outputs.
 int dense(int qtype, const void* Wv, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N, int K,
-          void* stream) {
-    const char* name = qtype == QMV_Q4_0 ? "qmv_q4_0" : "qmv_q8_0";
+          void* stream, void* ws = nullptr, size_t ws_bytes = 0, const char* name = nullptr) {
+    if (!name) name = qtype == QMV_Q4_0 ? "qmv_q4_0" : "qmv_q8_0";
     const int bb = block_bytes(qtype);
     if (M < 0 || M > QMV_MAX_M) return fail(QMV_EUNSUPPORTED, "%s: M=%d outside 0..%d", name, M, QMV_MAX_M);
     if (N < 0) return fail(QMV_EINVAL, "%s: N=%d < 0", name, N);
@@ -1997,6 +2000,9 @@ int dense(int qtype, const void* Wv, size_t ldw, const float* X, size_t ldx, flo
     const size_t ybytes = ((size_t)(M - 1) * ldy + N) * 4;
     if (overlaps(Y, ybytes, Wv, wbytes) || overlaps(Y, ybytes, X, xbytes))
         return fail(QMV_EINVAL, "%s: Y overlaps W or X", name);
+    if (ws && (((uintptr_t)ws & 255) || overlaps(ws, ws_bytes, Y, ybytes) || overlaps(ws, ws_bytes, Wv, wbytes) ||
+               overlaps(ws, ws_bytes, X, xbytes)))
+        return fail(QMV_EINVAL, "%s: the workspace must be 256-byte aligned and not overlap W, X or Y", name);
 
     hipStream_t st = (hipStream_t)stream;
     const uint8_t* W = (const uint8_t*)Wv;
@@ -2007,7 +2013,7 @@ int dense(int qtype, const void* Wv, size_t ldw, const float* X, size_t ldx, flo
                                  : launch_m1<QMV_Q8_0>(W, ldw, X, Y, N, K, st);
     }
     const bool mq_ok = M >= 2 && K > 0 && K % 64 == 0 && ((uintptr_t)W & 3) == 0 && (ldw & 3) == 0;
-    if (mq_ok) return launch_mq(qtype, W, ldw, X, ldx, Y, ldy, M, N, K, 0, 0, st);
+    if (mq_ok) return launch_mq(qtype, W, ldw, X, ldx, Y, ldy, M, N, K, ws, ws ? ws_bytes : 0, 0, 0, 0, st);
     return qtype == QMV_Q4_0 ? launch_generic<QMV_Q4_0>(W, ldw, X, ldx, Y, ldy, M, N, K, st)
                              : launch_generic<QMV_Q8_0>(W, ldw, X, ldx, Y, ldy, M, N, K, st);
 }
@@ -2398,6 +2404,22 @@ int qmv_q8_0(const void* W, size_t ldw_bytes, const float* X, size_t ldx, float*
     return dense(QMV_Q8_0, W, ldw_bytes, X, ldx, Y, ldy, M, N, K, stream);
 }
 
+size_t qmv_ws_bytes(int qtype, int M, int N, int K) {
+    if ((qtype != QMV_Q4_0 && qtype != QMV_Q8_0) || M < 2 || M > QMV_MAX_M || N <= 0 || K <= 0 || K % 64) return 0;
+    return mq_ws_bytes(M, N, K);
+}
+
+int qmv_ws(int qtype, const void* W, size_t ldw_bytes, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N,
+           int K, void* workspace, size_t workspace_bytes, void* stream) {
+    if (qtype != QMV_Q4_0 && qtype != QMV_Q8_0) return fail(QMV_EUNSUPPORTED, "qmv_ws: qtype %d not supported", qtype);
+    const size_t need = qmv_ws_bytes(qtype, M, N, K);
+    if (workspace && workspace_bytes < need)
+        return fail(QMV_EINVAL, "qmv_ws: workspace_bytes=%zu < %zu needed for M=%d N=%d K=%d", workspace_bytes, need, M,
+                    N, K);
+    return dense(qtype, W, ldw_bytes, X, ldx, Y, ldy, M, N, K, stream, workspace, workspace ? workspace_bytes : 0,
+                 "qmv_ws");
+}
+
 int qmv_id(int qtype, const void* Wv, size_t expert_stride_bytes, size_t ldw_bytes, int n_experts, const float* X,
            size_t ldx, const uint32_t* ids, int n_tokens, int top_k, float* Y, size_t ldy, int N, int K,
            const float* expert_scale, int* err_flag, void* stream) {
@@ -2454,7 +2476,8 @@ int qmv_gemm(int qtype, const void* Wv, size_t ldw, const float* X, size_t ldx, 
     // that read the same weights run side by side and share them through L2).
     if ((qtype == QMV_Q4_0 || qtype == QMV_Q8_0) && M > QMV_MAX_M && K > 0 && K % 64 == 0 &&
         ((uintptr_t)Wv & 3) == 0 && (ldw & 3) == 0)
-        return launch_mq(qtype, (const uint8_t*)Wv, ldw, X, ldx, Y, ldy, M, N, K, 0, 0, (hipStream_t)stream);
+        return launch_mq(qtype, (const uint8_t*)Wv, ldw, X, ldx, Y, ldy, M, N, K, nullptr, 0, 0, 0, 0,
+                         (hipStream_t)stream);
     // Blocks of up to 16 activation rows, each through the dense call of its
     // type (matrix cores for Q4_0); every block reads the weights once.
     for (int m0 = 0; m0 < M; m0 += QMV_MAX_M) {

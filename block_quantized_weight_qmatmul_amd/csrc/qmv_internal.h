@@ -24,14 +24,18 @@ QMV_HIDDEN int check_launch(const char* what);
 // Compute units of the current device.
 QMV_HIDDEN int num_cus();
 
-// Matrix-core products with 1..QMV_MAX_M activation rows per block of 16
-// (qmv_mq.hip). Requirements, checked by the caller: qtype Q4_0 or Q8_0,
-// K > 0 and K % 64 == 0, W and ldw 4-byte aligned, X and Y 4-byte aligned,
-// M >= 1 (any number of 16-row blocks). waves / ks = 0 pick the launch shape
-// from N; otherwise they force it (waves per workgroup, and the number of
-// waves that split K within a workgroup for one tile).
+// Matrix-core products (qmv_mq.hip), any number of activation rows in blocks
+// of 16. Requirements, checked by the caller: qtype Q4_0 or Q8_0, K > 0 and
+// K % 64 == 0, W and ldw 4-byte aligned, X and Y 4-byte aligned, M >= 1.
+// ws / ws_bytes: a caller workspace the call may use for K-segment partial
+// sums (NULL / 0: none; the call then needs no memory beyond X, W and Y).
+// waves = 0 picks the launch shape; otherwise waves, ks and S force it
+// (tuning).
 QMV_HIDDEN int launch_mq(int qtype, const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy,
-                         int M, int N, int K, int waves, int ks, hipStream_t st);
+                         int M, int N, int K, void* ws, size_t ws_bytes, int waves, int ks, int S, hipStream_t st);
+// Workspace bytes launch_mq would use for M, N, K given unlimited room (0 if
+// it would not split K).
+QMV_HIDDEN size_t mq_ws_bytes(int M, int N, int K);
 
 // ---------------------------------------------------------------------------
 // Device helpers

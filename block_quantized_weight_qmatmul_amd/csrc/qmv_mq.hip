@@ -170,7 +170,8 @@ __device__ __forceinline__ void split_bf16(const float (&v)[8], uint32_t (&hw)[4
 template <int QT, int WAVES, int KS>
 __global__ __launch_bounds__(WAVES * 64) void k_mq(const uint8_t* __restrict__ W, size_t ldw,
                                                    const float* __restrict__ X, size_t ldx, float* __restrict__ Y,
-                                                   size_t ldy, int M, int N, int K, int mblocks) {
+                                                   size_t ldy, int M, int N, int K, int mblocks, int seg_rounds,
+                                                   float* __restrict__ part) {
     using F = MqFmt<QT>;
     constexpr int DW = F::DW, PB = 4 * DW;
     constexpr int NT = WAVES * 64;
@@ -178,7 +179,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_mq(const uint8_t* __restrict__ W
     constexpr int REC = 512 * KS;              // A records (16 B hi + 16 B lo) per round
     constexpr int RPT = (REC + NT - 1) / NT;   // records per thread
     // activation register sets in flight (fewer with the 68-byte Q8_0 pairs)
-    constexpr int XS = (QT == QMV_Q8_0 && RPT <= 2) ? 2 : RPT <= 4 ? 4 : 2;
+    constexpr int XS = ((QT == QMV_Q8_0 || WAVES % 4 != 0) && RPT <= 2) ? 2 : RPT <= 4 ? 4 : 2;
     constexpr int ROUND_BYTES = KS * MQ_STEP_BYTES;
     extern __shared__ __align__(16) uint8_t smem[];  // A operands of two rounds
 
@@ -195,13 +196,17 @@ __global__ __launch_bounds__(WAVES * 64) void k_mq(const uint8_t* __restrict__ W
     const int S = (P + 3) >> 2;       // steps per row
     const int nb = K >> 5;            // blocks per row
     const int rounds = (S + KS - 1) / KS;
+    // K segment blockIdx.y: rounds r0 .. r0 + nr - 1 (all of them with one segment)
+    const int r0 = blockIdx.y * seg_rounds;
+    const int nr = (rounds - r0 < seg_rounds ? rounds - r0 : seg_rounds);
     long wr = row0 + j;
     wr = wr < N ? wr : N - 1;
     const uint8_t* __restrict__ wrow = W + wr * ldw;
 
-    // ---- weights: the pair 4t + G of this lane's row, t = this wave's step of round r
+    // ---- weights: the pair 4t + G of this lane's row, t = this wave's step
+    // of round r0 + r (r counts the rounds of this workgroup's K segment)
     auto issue = [&](int r, uint32_t (&b)[DW]) __attribute__((always_inline)) {
-        int q = (r * KS + sp) * 4 + G;
+        int q = ((r0 + r) * KS + sp) * 4 + G;
         q = q < P ? q : P - 1;  // past the row end: the last pair again (not used)
         load_pair<DW>(wrow + (size_t)q * PB, b);
     };
@@ -218,7 +223,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_mq(const uint8_t* __restrict__ W
     auto fetch_x = [&](int r, f32x4a_t (&xr)[RPT][2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
-            int blk = r * 8 * KS + wave + i * WAVES;
+            int blk = (r0 + r) * 8 * KS + wave + i * WAVES;
             blk = blk < nb ? blk : nb - 1;
             const float* src = xb + (size_t)blk * 32;
             xr[i][0] = *reinterpret_cast<const f32x4a_t*>(src);
@@ -229,9 +234,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_mq(const uint8_t* __restrict__ W
         uint8_t* base = smem + buf * ROUND_BYTES + wave * 2048 + lane * 16;
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
+            if ((8 * KS) % WAVES != 0 && wave + i * WAVES >= 8 * KS) continue;  // past the round's blocks
             uint8_t* rec = base + i * WAVES * 2048;
             u32x4 hi = {0u, 0u, 0u, 0u}, lo = hi;
-            if (mok && r * 8 * KS + wave + i * WAVES < nb) {
+            if (mok && (r0 + r) * 8 * KS + wave + i * WAVES < nb) {
                 const float v[8] = {xr[i][0].x, xr[i][0].y, xr[i][0].z, xr[i][0].w,
                                     xr[i][1].x, xr[i][1].y, xr[i][1].z, xr[i][1].w};
                 uint32_t hw[4], lw[4];
@@ -247,7 +253,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_mq(const uint8_t* __restrict__ W
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     // ---- one step: 8 blocks of the tile (2 per lane group, pair 4t + c for lane group c)
     auto compute = [&](int r, const uint32_t (&b)[DW]) __attribute__((always_inline)) {
-        const int t = r * KS + sp;
+        const int t = (r0 + r) * KS + sp;
         const bool valid = t * 4 + G < P;
         const uint8_t* xa = smem + (r & 1) * ROUND_BYTES + sp * MQ_STEP_BYTES + G * 256 + j * 16;
         // both block scales of this lane's pair in one dword; zero past K
@@ -342,15 +348,15 @@ __global__ __launch_bounds__(WAVES * 64) void k_mq(const uint8_t* __restrict__ W
     // Whole groups of four rounds in the loop, the rest after it: every path
     // into the loop's first round then has the same loads in flight.
     int r = 0;
-    for (; r + 4 <= rounds; r += 4) {
+    for (; r + 4 <= nr; r += 4) {
         body(r, b0, S1{});
         body(r + 1, b1, S2{});
         body(r + 2, b2, S3{});
         body(r + 3, b3, S0{});
     }
-    if (r < rounds) body(r, b0, S1{});
-    if (r + 1 < rounds) body(r + 1, b1, S2{});
-    if (r + 2 < rounds) body(r + 2, b2, S3{});
+    if (r < nr) body(r, b0, S1{});
+    if (r + 1 < nr) body(r + 1, b1, S2{});
+    if (r + 2 < nr) body(r + 2, b2, S3{});
 
     // ---- the KS partial sums of a tile, added in order sp = 0, 1, ...
     // lane (G, j) holds activation rows 4G..4G+3 of weight row j
@@ -368,58 +374,126 @@ __global__ __launch_bounds__(WAVES * 64) void k_mq(const uint8_t* __restrict__ W
     }
     const long row = row0 + j;
     if (row < N) {
+        // with K segments: partial sums part[segment][m][n] (M rows of N), summed by k_mqred
+        float* dst = part ? part + ((size_t)blockIdx.y * M + (size_t)mb * 16) * N + row : Y + row;
+        const size_t ld = part ? (size_t)N : ldy;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int m = 4 * G + i;
-            if (m < Mb) Y[(size_t)m * ldy + row] = acc[i] * F::OUT_SCALE;
+            if (m < Mb) dst[(size_t)m * ld] = acc[i] * F::OUT_SCALE;
         }
     }
+}
+
+// Y[m, n] = the S partial sums part[s][m][n] added in segment order.
+__global__ __launch_bounds__(256) void k_mqred(const float* __restrict__ part, int S, int M, int N,
+                                               float* __restrict__ Y, size_t ldy) {
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (long)M * N) return;
+    const size_t mn = (size_t)M * N;
+    const float* p = part + i;
+    float t = p[0];
+    int s = 1;
+    for (; s + 4 <= S; s += 4) {  // four loads in flight, added in order
+        const float a = p[s * mn], b = p[(s + 1) * mn], c = p[(s + 2) * mn], d = p[(s + 3) * mn];
+        t = (((t + a) + b) + c) + d;
+    }
+    for (; s < S; ++s) t += p[s * mn];
+    Y[(size_t)(i / N) * ldy + (size_t)(i % N)] = t;
+}
+
+// Launch plan: workgroup shape and K segments (S = 1: no segments, no workspace).
+struct MqPlan {
+    int waves, ks, S, seg_rounds;
+    size_t ws_bytes;
+};
+
+// ws_cap: the most workspace bytes the call may use (0: none, scratch-free).
+MqPlan plan_mq(int M, int N, int K, size_t ws_cap) {
+    const long tiles = ((long)N + 15) / 16;
+    const long ncu = num_cus();
+    const long mblocks = ((long)M + 15) / 16;
+    const int steps = ((K >> 6) + 3) >> 2;
+    MqPlan p{8, 1, 1, steps, 0};
+    if (tiles * mblocks >= 4 * ncu) return p;  // one wave per tile fills the chip
+    // Few tiles. Without a workspace: two tiles per workgroup, each split over
+    // two waves, every workgroup reading and converting all of X. With one:
+    // four tiles per workgroup and K cut into segments of whole steps over
+    // grid.y, so that about one workgroup per compute unit each reads and
+    // converts only its segment of X; the partial sums go to the workspace
+    // and a second launch adds them in segment order (M = 16, K = 5120,
+    // graph-timed: N = 5120 17 us with 3 segments, N = 1024 11 us with 10).
+    const long groups = ((tiles + 3) / 4) * mblocks;
+    long S = (ncu + groups / 2) / groups;  // about one workgroup per compute unit
+    S = S < steps ? S : steps;
+    const size_t per_seg = (size_t)M * N * sizeof(float);
+    if (ws_cap / per_seg < (size_t)S) S = (long)(ws_cap / per_seg);
+    if (S < 2) {
+        p.waves = 4;
+        p.ks = 2;
+        p.seg_rounds = (steps + 1) / 2;
+        return p;
+    }
+    const int seg = (int)((steps + S - 1) / S);
+    p.waves = 4;
+    p.ks = 1;
+    p.seg_rounds = seg;
+    p.S = (steps + seg - 1) / seg;
+    p.ws_bytes = (size_t)p.S * per_seg;
+    return p;
 }
 
 template <int QT, int WAVES, int KS>
 int launch_mq_t(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N, int K,
-                hipStream_t st) {
+                int S, int seg_rounds, float* part, hipStream_t st) {
     constexpr int TWG = WAVES / KS;
     const long tiles = ((long)N + 15) / 16;
     const long groups = (tiles + TWG - 1) / TWG;
     const long mblocks = ((long)M + 15) / 16;
-    if (groups * mblocks > 0x7FFFFFFF) return fail(QMV_EINVAL, "N too large");
+    if (groups * mblocks > 0x7FFFFFFF || S > 65535) return fail(QMV_EINVAL, "N too large");
     const size_t lds = (size_t)2 * KS * MQ_STEP_BYTES;
-    hipLaunchKernelGGL((k_mq<QT, WAVES, KS>), dim3((unsigned)(groups * mblocks)), dim3(WAVES * 64), lds, st, W, ldw,
-                       X, ldx, Y, ldy, M, N, K, (int)mblocks);
-    return check_launch("qmv matrix-core kernel");
+    hipLaunchKernelGGL((k_mq<QT, WAVES, KS>), dim3((unsigned)(groups * mblocks), (unsigned)S), dim3(WAVES * 64), lds,
+                       st, W, ldw, X, ldx, Y, ldy, M, N, K, (int)mblocks, seg_rounds, S > 1 ? part : nullptr);
+    int rc = check_launch("qmv matrix-core kernel");
+    if (rc == QMV_OK && S > 1) {
+        const long n = (long)M * N;
+        hipLaunchKernelGGL(k_mqred, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, (const float*)part, S, M, N, Y,
+                           ldy);
+        rc = check_launch("qmv matrix-core partial-sum launch");
+    }
+    return rc;
 }
 
 template <int QT>
 int launch_mq_q(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N, int K,
-                int waves, int ks, hipStream_t st) {
-    if (waves == 0) {
-        // Many tiles: one wave per tile over all of K, eight tiles per
-        // workgroup (the activation conversion shared by 128 weight rows).
-        // Fewer tiles: two tiles per workgroup, each split over two waves
-        // (graph-timed, M = 16, K = 5120: N = 27648 33 us; N = 5120 and 1024
-        // 24 us, where every workgroup still reads and converts all of X).
-        const long tiles = ((long)N + 15) / 16;
-        if (tiles >= 4L * num_cus()) {
-            waves = 8;
-            ks = 1;
-        } else {
-            waves = 4;
-            ks = 2;
-        }
-    }
-    if (waves == 8 && ks == 1) return launch_mq_t<QT, 8, 1>(W, ldw, X, ldx, Y, ldy, M, N, K, st);
-    if (waves == 4 && ks == 2) return launch_mq_t<QT, 4, 2>(W, ldw, X, ldx, Y, ldy, M, N, K, st);
-
-    return fail(QMV_EINVAL, "internal: no matrix-core kernel for waves=%d ks=%d", waves, ks);
+                const MqPlan& p, float* part, hipStream_t st) {
+    const int S = p.S, sr = p.seg_rounds;
+    if (p.waves == 8 && p.ks == 1) return launch_mq_t<QT, 8, 1>(W, ldw, X, ldx, Y, ldy, M, N, K, S, sr, part, st);
+    if (p.waves == 4 && p.ks == 1) return launch_mq_t<QT, 4, 1>(W, ldw, X, ldx, Y, ldy, M, N, K, S, sr, part, st);
+    if (p.waves == 4 && p.ks == 2) return launch_mq_t<QT, 4, 2>(W, ldw, X, ldx, Y, ldy, M, N, K, S, sr, part, st);
+    return fail(QMV_EINVAL, "internal: no matrix-core kernel for waves=%d ks=%d", p.waves, p.ks);
 }
 
 }  // namespace
 
+size_t mq_ws_bytes(int M, int N, int K) { return M >= 2 && N > 0 && K > 0 ? plan_mq(M, N, K, SIZE_MAX).ws_bytes : 0; }
+
 int launch_mq(int qtype, const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N,
-              int K, int waves, int ks, hipStream_t st) {
-    return qtype == QMV_Q4_0 ? launch_mq_q<QMV_Q4_0>(W, ldw, X, ldx, Y, ldy, M, N, K, waves, ks, st)
-                             : launch_mq_q<QMV_Q8_0>(W, ldw, X, ldx, Y, ldy, M, N, K, waves, ks, st);
+              int K, void* ws, size_t ws_bytes, int waves, int ks, int S, hipStream_t st) {
+    MqPlan p = plan_mq(M, N, K, ws ? ws_bytes : 0);
+    if (waves) {  // a forced shape (tuning): S segments of K when given workspace allows
+        const int steps = ((K >> 6) + 3) >> 2;
+        const int rounds = (steps + ks - 1) / ks;
+        p.waves = waves;
+        p.ks = ks;
+        S = S < 1 ? 1 : (S > rounds ? rounds : S);
+        p.seg_rounds = (rounds + S - 1) / S;
+        p.S = (rounds + p.seg_rounds - 1) / p.seg_rounds;
+        p.ws_bytes = p.S > 1 ? (size_t)p.S * M * N * sizeof(float) : 0;
+        if (p.ws_bytes > (ws ? ws_bytes : 0)) return fail(QMV_EINVAL, "internal: workspace too small for S=%d", S);
+    }
+    return qtype == QMV_Q4_0 ? launch_mq_q<QMV_Q4_0>(W, ldw, X, ldx, Y, ldy, M, N, K, p, (float*)ws, st)
+                             : launch_mq_q<QMV_Q8_0>(W, ldw, X, ldx, Y, ldy, M, N, K, p, (float*)ws, st);
 }
 
 }  // namespace qmvi

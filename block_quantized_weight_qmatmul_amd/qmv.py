@@ -66,10 +66,18 @@ def lib() -> ctypes.CDLL:
         L.qmv_gemm.argtypes = [I, P, S, P, S, P, S, I, I, I, P]
         L.qmv_batch.restype = I
         L.qmv_batch.argtypes = [I, ctypes.POINTER(Problem), I, P]
+        L.qmv_ws.restype = I
+        L.qmv_ws.argtypes = [I, P, S, P, S, P, S, I, I, I, P, S, P]
+        L.qmv_ws_bytes.restype = S
+        L.qmv_ws_bytes.argtypes = [I, I, I, I]
         L.qmv_last_error.restype = ctypes.c_char_p
         L.qmv_last_error.argtypes = []
         _lib = L
     return _lib
+
+
+def _qt(qtype) -> int:
+    return QTYPES[qtype] if isinstance(qtype, str) else int(qtype)
 
 
 def last_error() -> str:
@@ -100,6 +108,16 @@ def raw_qmv(qtype: int, W: int, ldw: int, X: int, ldx: int, Y: int, ldy: int, M:
             stream: int = 0) -> int:
     f = {QMV_Q4_0: lib().qmv_q4_0, QMV_Q8_0: lib().qmv_q8_0, QMV_Q5_K: lib().qmv_q5_k, QMV_Q6_K: lib().qmv_q6_k}[qtype]
     return f(W, ldw, X, ldx, Y, ldy, M, N, K, stream)
+
+
+def raw_qmv_ws(qtype: int, W: int, ldw: int, X: int, ldx: int, Y: int, ldy: int, M: int, N: int, K: int,
+               ws: int, ws_bytes: int, stream: int = 0) -> int:
+    return lib().qmv_ws(qtype, W, ldw, X, ldx, Y, ldy, M, N, K, ws, ws_bytes, stream)
+
+
+def ws_bytes(qtype, M: int, N: int, K: int) -> int:
+    """Workspace bytes qmv_ws uses for these sizes (0: it would not split K)."""
+    return int(lib().qmv_ws_bytes(_qt(qtype), M, N, K))
 
 
 def raw_qmv_id(qtype, W, expert_stride, ldw, n_experts, X, ldx, ids, n_tokens, top_k, Y, ldy, N, K,
@@ -149,6 +167,23 @@ def _dense(qtype: int, W, X, Y, K: Optional[int], stream) -> None:
     st = raw_qmv(qtype, _ptr(W), W.stride(0), _ptr(x2), x2.stride(0), _ptr(y2), y2.stride(0), M, N, K,
                  _stream(stream))
     _check(st)
+
+
+def qmv_ws(qtype, W, X, Y, workspace, K: Optional[int] = None, stream=None) -> None:
+    """qmv_q4_0 / qmv_q8_0 with a caller workspace (a uint8 device tensor of at
+    least ws_bytes(qtype, M, N, K) bytes, or None) -- see include/qmv.h."""
+    if W.dim() != 2 or W.stride(1) != 1:
+        raise ValueError("W must be a 2-D uint8 tensor with contiguous rows")
+    x2 = X if X.dim() == 2 else X.view(1, -1)
+    y2 = Y if Y.dim() == 2 else Y.view(1, -1)
+    M, N = x2.shape[0], W.shape[0]
+    if K is None:
+        K = x2.shape[1]
+    if x2.stride(1) != 1 or y2.stride(1) != 1 or y2.shape[0] != M or y2.shape[1] != N:
+        raise ValueError("X [M, K] and Y [M, N] need unit inner stride and matching M, N")
+    nb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(raw_qmv_ws(_qt(qtype), _ptr(W), W.stride(0), _ptr(x2), x2.stride(0), _ptr(y2), y2.stride(0), M, N, K,
+                      _ptr(workspace), nb, _stream(stream)))
 
 
 def qmv_q4_0(W, X, Y, K: Optional[int] = None, stream=None) -> None:

@@ -109,6 +109,37 @@ int qmv_q8_0(const void* W, size_t ldw_bytes, const float* X, size_t ldx, float*
              int M, int N, int K, void* stream);
 
 /*
+ * qmv_ws — the qmv_q4_0 / qmv_q8_0 product (qtype QMV_Q4_0 or QMV_Q8_0) with
+ * a caller-provided workspace, for the batched-verify calls of few output
+ * rows (M >= 2, N below about 16K). The pages allocate every activation and
+ * scratch buffer once at load and only encode work into them (model.rs,
+ * `alloc_activation_buffers`; gpu_full_attn.rs, `encode_one_layer`); a
+ * workspace of qmv_ws_bytes() bytes taken the same way lets such a call cut
+ * K into segments over more compute units: each segment writes fp32 partial
+ * sums into the workspace and a second launch adds them in segment order
+ * (bitwise reproducible). Without it every workgroup must read and convert
+ * all of X.
+ *
+ *  workspace        device, 256-byte aligned, owned by the caller, not
+ *                   overlapping W, X or Y; NULL = none (the call is then
+ *                   qmv_q4_0 / qmv_q8_0).
+ *  workspace_bytes  its size; at least qmv_ws_bytes(qtype, M, N, K) when
+ *                   workspace is not NULL (QMV_EINVAL otherwise).
+ *  Other arguments and rules as qmv_q4_0. The workspace needs no
+ *  initialisation; calls that use the same workspace must be ordered (one
+ *  stream, or events), as its contents are overwritten by every call.
+ */
+int qmv_ws(int qtype, const void* W, size_t ldw_bytes, const float* X, size_t ldx, float* Y, size_t ldy,
+           int M, int N, int K, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * qmv_ws_bytes — the workspace qmv_ws uses for these arguments: 0 when it
+ * would not split K (M = 1, many output rows, K % 64 != 0, other qtypes),
+ * else S * M * N * 4 bytes for S segments.
+ */
+size_t qmv_ws_bytes(int qtype, int M, int N, int K);
+
+/*
  * qmv_q6_k — as qmv_q4_0 with Q6_K super-blocks: 256 weights in 210 bytes.
  *
  * The pages load the lm_head natively in this format (`lm_head_q6k` of

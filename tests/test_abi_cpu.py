@@ -27,7 +27,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     names = declared_functions()
     assert {"qmv_q4_0", "qmv_q8_0", "qmv_q5_k", "qmv_q6_k", "qmv_gemm", "qmv_affine4", "qmv_affine4_id", "qmv_id", "qmv_id_swiglu", "qmv_moe_wsum", "qmv_moe_down",
-            "qmv_batch", "qmv_last_error"} <= set(names)
+            "qmv_batch", "qmv_ws", "qmv_ws_bytes", "qmv_last_error"} <= set(names)
     L = ctypes.CDLL(qmv.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -61,6 +61,34 @@ def test_dense_argument_checks(args, status, msg):
     q, *rest = args
     assert qmv.raw_qmv(q, *rest) == status
     assert msg in qmv.last_error()
+
+
+WS = 0x50000000
+
+
+@pytest.mark.parametrize("args,status,msg", [
+    ((Q4, W, 18 * 160, X, 5120, Y, 1024, 16, 1024, 5120, WS, 1000), qmv.QMV_EINVAL, "workspace_bytes=1000"),
+    ((Q4, W, 18 * 160, X, 5120, Y, 1024, 16, 1024, 5120, WS + 16, 1 << 26), qmv.QMV_EINVAL, "256-byte aligned"),
+    ((Q4, W, 18 * 160, X, 5120, Y, 1024, 16, 1024, 5120, Y + 256, 1 << 26), qmv.QMV_EINVAL, "not overlap"),
+    ((qmv.QMV_Q6_K, W, 18 * 160, X, 5120, Y, 1024, 16, 1024, 5120, WS, 1 << 26), qmv.QMV_EUNSUPPORTED, "qtype"),
+    ((Q4, W, 18 * 160, X, 5120, Y, 1024, 17, 1024, 5120, WS, 1 << 26), qmv.QMV_EUNSUPPORTED, "M=17"),
+])
+def test_ws_argument_checks(args, status, msg):
+    q, *rest = args
+    assert qmv.raw_qmv_ws(q, *rest) == status
+    assert msg in qmv.last_error()
+
+
+def test_ws_bytes_query():
+    """Partial sums of S K segments, S * M * N * 4 bytes, for calls with few
+    output rows; 0 where the call does not split K."""
+    n = qmv.ws_bytes("q4_0", 16, 1024, 5120)
+    assert n > 0 and n % (16 * 1024 * 4) == 0 and n // (16 * 1024 * 4) <= 5120 // 256
+    assert qmv.ws_bytes("q8_0", 16, 5120, 5120) % (16 * 5120 * 4) == 0
+    assert qmv.ws_bytes("q4_0", 1, 1024, 5120) == 0          # M = 1
+    assert qmv.ws_bytes("q4_0", 16, 1024, 5120 + 32) == 0     # K % 64 != 0 (generic kernel)
+    assert qmv.ws_bytes("q6_k", 16, 1024, 5120) == 0
+    assert qmv.ws_bytes("q4_0", 17, 1024, 5120) == 0
 
 
 def test_empty_calls_are_no_ops_without_touching_memory():
