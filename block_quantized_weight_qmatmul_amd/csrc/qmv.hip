@@ -42,6 +42,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 
 #include "qmv.h"
 #include "qmv_internal.h"
@@ -2392,6 +2395,47 @@ int kq_dense(const char* name, const void* Wv, size_t ldw, const float* X, size_
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Static scratch for qmv_ws_static: the K-segment partial sums of qmv_ws kept
+// in the library's own device memory (one copy per GPU, held until the
+// process ends), for callers that cannot allocate. Its device address is
+// looked up once per device (hipGetSymbolAddress, with that device current);
+// host code passes that address to the kernels, never the symbol itself.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[QMV_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::atomic<void*> g_scratch_ptr[MAX_DEVICES];
+std::mutex g_scratch_mu;
+
+// The current device's address of `scratch` (nullptr and the error message
+// set if it cannot be had).
+void* static_scratch(const char* name) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) {
+        (void)hipGetLastError();
+        fail(QMV_EHIP, "%s: no current device (or device id >= %d)", name, MAX_DEVICES);
+        return nullptr;
+    }
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            fail(QMV_EHIP, "%s: hipGetSymbolAddress(scratch) failed on device %d: %s", name, dev,
+                 hipGetErrorString(e));
+            return nullptr;
+        }
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+}  // namespace
+
 extern "C" {
 
 int qmv_q4_0(const void* W, size_t ldw_bytes, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N, int K,
@@ -2418,6 +2462,22 @@ int qmv_ws(int qtype, const void* W, size_t ldw_bytes, const float* X, size_t ld
                     N, K);
     return dense(qtype, W, ldw_bytes, X, ldx, Y, ldy, M, N, K, stream, workspace, workspace ? workspace_bytes : 0,
                  "qmv_ws");
+}
+
+int qmv_ws_static(int qtype, const void* W, size_t ldw_bytes, const float* X, size_t ldx, float* Y, size_t ldy, int M,
+                  int N, int K, void* stream) {
+    if (qtype != QMV_Q4_0 && qtype != QMV_Q8_0)
+        return fail(QMV_EUNSUPPORTED, "qmv_ws_static: qtype %d not supported", qtype);
+    const size_t need = qmv_ws_bytes(qtype, M, N, K);
+    if (need > (size_t)QMV_STATIC_SCRATCH_BYTES)
+        return fail(QMV_EINVAL,
+                    "qmv_ws_static: M=%d N=%d K=%d needs %zu bytes of scratch, more than the static %d; use qmv_ws "
+                    "with a workspace",
+                    M, N, K, need, QMV_STATIC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if (need > 0 && !(ws = static_scratch("qmv_ws_static"))) return QMV_EHIP;
+    return dense(qtype, W, ldw_bytes, X, ldx, Y, ldy, M, N, K, stream, ws, ws ? (size_t)QMV_STATIC_SCRATCH_BYTES : 0,
+                 "qmv_ws_static");
 }
 
 int qmv_id(int qtype, const void* Wv, size_t expert_stride_bytes, size_t ldw_bytes, int n_experts, const float* X,

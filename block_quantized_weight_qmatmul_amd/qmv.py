@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
         L.qmv_batch.argtypes = [I, ctypes.POINTER(Problem), I, P]
         L.qmv_ws.restype = I
         L.qmv_ws.argtypes = [I, P, S, P, S, P, S, I, I, I, P, S, P]
+        L.qmv_ws_static.restype = I
+        L.qmv_ws_static.argtypes = [I, P, S, P, S, P, S, I, I, I, P]
         L.qmv_ws_bytes.restype = S
         L.qmv_ws_bytes.argtypes = [I, I, I, I]
         L.qmv_last_error.restype = ctypes.c_char_p
@@ -113,6 +115,11 @@ def raw_qmv(qtype: int, W: int, ldw: int, X: int, ldx: int, Y: int, ldy: int, M:
 def raw_qmv_ws(qtype: int, W: int, ldw: int, X: int, ldx: int, Y: int, ldy: int, M: int, N: int, K: int,
                ws: int, ws_bytes: int, stream: int = 0) -> int:
     return lib().qmv_ws(qtype, W, ldw, X, ldx, Y, ldy, M, N, K, ws, ws_bytes, stream)
+
+
+def raw_qmv_ws_static(qtype: int, W: int, ldw: int, X: int, ldx: int, Y: int, ldy: int, M: int, N: int, K: int,
+                      stream: int = 0) -> int:
+    return lib().qmv_ws_static(qtype, W, ldw, X, ldx, Y, ldy, M, N, K, stream)
 
 
 def ws_bytes(qtype, M: int, N: int, K: int) -> int:

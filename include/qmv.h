@@ -140,6 +140,27 @@ int qmv_ws(int qtype, const void* W, size_t ldw_bytes, const float* X, size_t ld
 size_t qmv_ws_bytes(int qtype, int M, int N, int K);
 
 /*
+ * qmv_ws_static — qmv_ws for callers that cannot allocate memory (code under
+ * HIP graph capture that must not call hipMalloc, tight serving loops,
+ * harnesses that forbid allocation): the K-segment partial sums go to a
+ * scratch array in the library's own device memory, QMV_STATIC_SCRATCH_BYTES
+ * per GPU, held until the process ends; the call itself allocates nothing.
+ *
+ *  Arguments as qmv_ws without the workspace. A call whose
+ *  qmv_ws_bytes(qtype, M, N, K) exceeds QMV_STATIC_SCRATCH_BYTES is rejected
+ *  (QMV_EINVAL) before anything is launched. The device is the current one
+ *  (the array's address is looked up on the first call on each device; that
+ *  lookup failing gives QMV_EHIP).
+ *  Every call on one GPU shares that GPU's array: calls that may overlap in
+ *  time on one GPU (different streams, or graphs replayed concurrently) race
+ *  and give wrong results; order them. Nothing in the array needs to start
+ *  at zero (each call writes the partial sums it reads).
+ */
+#define QMV_STATIC_SCRATCH_BYTES (4 << 20)
+int qmv_ws_static(int qtype, const void* W, size_t ldw_bytes, const float* X, size_t ldx, float* Y, size_t ldy,
+                  int M, int N, int K, void* stream);
+
+/*
  * qmv_q6_k — as qmv_q4_0 with Q6_K super-blocks: 256 weights in 210 bytes.
  *
  * The pages load the lm_head natively in this format (`lm_head_q6k` of
