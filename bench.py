@@ -39,7 +39,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 WARMUP_S = 0.3  # minimum untimed warm-up per measurement, seconds
 METRIC = "effective weight GB/s and % of HBM peak, Q4_0 qmatmul at M=1 and M=16"
-KERNEL_SRC = os.path.join(ROOT, "block_quantized_weight_qmatmul_amd", "csrc", "qmv.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "block_quantized_weight_qmatmul_amd", "csrc", f)
+               for f in ("qmv.hip", "qmv_mq.hip", "qmv_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qmv_decode_layer_h4096.json")
 
 
@@ -48,8 +49,10 @@ def kernel_hash() -> str:
     out, so that the committed counter figures stay attached to the code they
     were taken on and a comment edit does not orphan them."""
     import re
-    with open(KERNEL_SRC, encoding="utf-8") as f:
-        src = f.read()
+    src = ""
+    for path in KERNEL_SRCS:
+        with open(path, encoding="utf-8") as f:
+            src += f.read()
     src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
     src = re.sub(r"//[^\n]*", " ", src)
     src = " ".join(src.split())
@@ -597,9 +600,263 @@ def summarize_trace(trace_csv, out_name, title, kernels, cmd_note):
     print(text)
 
 
+# ---------------------------------------------------------------------------
+# Per-kernel evidence: one representative call set per kernel, run eagerly a
+# few times between separator kernels, for rocprofv3 kernel traces and
+# counter passes; and the summarizer that writes profiles/counters_<kernel>.txt
+# ---------------------------------------------------------------------------
+def kernel_workloads(dev, reps=3):
+    """Returns [(name, {kernel-name substring: algorithmic bytes per dispatch},
+    call)] for the kernels of the library."""
+    import numpy as np
+    import torch
+
+    from block_quantized_weight_qmatmul_amd import qmv, synth
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    out = []
+    probs = {p.name: p for p in synth.CONFIGS[1]["problems"]}
+
+    def w(qtype, N, K, part=0, cfg=9):
+        return T(synth.make_weights(qtype, N, K, cfg=cfg, part=part))
+
+    def x(M, K, part=0, cfg=9):
+        return T(synth.make_x(M, K, cfg=cfg, part=part))
+    # decode layer set (config 1): grouped Q/K/V and gate/up (k_m1c), single O and down (k_m1)
+    qkv = [(w("q4_0", probs[n].N, 4096, i), probs[n].N) for i, n in enumerate(("q", "k", "v"))]
+    xq = x(1, 4096)[0]
+    ys = [torch.empty(n, device=dev) for _, n in qkv]
+    out.append(("layer_qkv_q4_0_4096", {"k_m1c": sum(probs[n].weight_bytes for n in ("q", "k", "v"))},
+                lambda: qmv.qmv_batch("q4_0", [(W_, xq, y_) for (W_, _), y_ in zip(qkv, ys)])))
+    Wo, xo, yo = w("q4_0", 4096, 4096, 3), x(1, 4096, 3), torch.empty((1, 4096), device=dev)
+    out.append(("layer_o_q4_0_4096x4096", {"k_m1": probs["o"].weight_bytes}, lambda: qmv.qmv_q4_0(Wo, xo, yo)))
+    gu = [w("q4_0", 14336, 4096, 4 + i) for i in range(2)]
+    xg = x(1, 4096, 4)[0]
+    yg = [torch.empty(14336, device=dev) for _ in range(2)]
+    out.append(("layer_gate_up_q4_0_4096x14336x2", {"k_m1c": 2 * probs["gate"].weight_bytes},
+                lambda: qmv.qmv_batch("q4_0", [(gu[i], xg, yg[i]) for i in range(2)])))
+    Wd, xd, yd = w("q4_0", 4096, 14336, 6), x(1, 14336, 6), torch.empty((1, 4096), device=dev)
+    out.append(("layer_down_q4_0_14336x4096", {"k_m1": probs["down"].weight_bytes}, lambda: qmv.qmv_q4_0(Wd, xd, yd)))
+    # config 2, Q8_0
+    W8a, x8a, y8a = w("q8_0", 14336, 4096, 7), x(1, 4096, 7), torch.empty((1, 14336), device=dev)
+    W8b, x8b, y8b = w("q8_0", 4096, 14336, 8), x(1, 14336, 8), torch.empty((1, 4096), device=dev)
+    out.append(("q8_0_m1_4096x14336", {"k_m1": 14336 * 128 * 34}, lambda: qmv.qmv_q8_0(W8a, x8a, y8a)))
+    out.append(("q8_0_m1_14336x4096", {"k_m1": 4096 * 448 * 34}, lambda: qmv.qmv_q8_0(W8b, x8b, y8b)))
+    # config 3 (M = 16, K = 5120): the matrix cores, without and with a workspace
+    for N in (27648, 5120, 1024):
+        Wm, Xm, Ym = w("q4_0", N, 5120, N), x(16, 5120, N), torch.empty((16, N), device=dev)
+        wsb = qmv.ws_bytes("q4_0", 16, N, 5120)
+        ws = torch.empty(max(256, wsb), dtype=torch.uint8, device=dev)
+        kb = {"k_mq<": N * 160 * 18}
+        if wsb:
+            kb["k_mqred"] = wsb + 16 * N * 4
+            out.append((f"m16_q4_0_5120x{N}_ws", kb, lambda Wm=Wm, Xm=Xm, Ym=Ym, ws=ws: qmv.qmv_ws("q4_0", Wm, Xm, Ym, ws)))
+        else:
+            out.append((f"m16_q4_0_5120x{N}", kb, lambda Wm=Wm, Xm=Xm, Ym=Ym: qmv.qmv_q4_0(Wm, Xm, Ym)))
+    Wq8, Xq8, Yq8 = w("q8_0", 27648, 5120, 9), x(16, 5120, 9), torch.empty((16, 27648), device=dev)
+    out.append(("m16_q8_0_5120x27648", {"k_mq<": 27648 * 160 * 34}, lambda: qmv.qmv_q8_0(Wq8, Xq8, Yq8)))
+    # config 4 MoE (T = 1 and 32) and the FFN epilogue
+    for Tn in (1, 32):
+        d = synth.moe_inputs(Tn)
+        dd = {k: T(v) for k, v in d.items()}
+        dd["ids"] = dd["ids"].to(torch.int32).contiguous()
+        g, dn = synth.moe_calls(Tn)
+        ne = synth.distinct(d["ids"])
+        Ygu = torch.empty(Tn * g.top_k, g.N, device=dev)
+        Ydn = torch.empty(Tn * g.top_k, dn.N, device=dev)
+        o = torch.empty(Tn, dn.N, device=dev)
+        kid = "k_idv" if Tn == 1 else "k_id<"
+        out.append((f"moe_t{Tn}_gate_up_id", {kid: ne * g.N * (g.K // 32) * 18},
+                    lambda dd=dd, g=g, Ygu=Ygu: qmv.qmv_id("q4_0", dd["W_gate_up"], dd["X_gate_up"], dd["ids"], Ygu,
+                                                            g.N, g.K, expert_scale=dd["expert_scale"])))
+        out.append((f"moe_t{Tn}_down_id", {"k_id": ne * dn.N * (dn.K // 32) * 18},
+                    lambda dd=dd, dn=dn, Ydn=Ydn: qmv.qmv_id("q4_0", dd["W_down"], dd["X_down"], dd["ids"].view(-1, 1),
+                                                              Ydn, dn.N, dn.K, expert_scale=dd["expert_scale"])))
+        if Tn == 1:
+            out.append(("moe_t1_down_fused", {"k_moe_down": ne * dn.N * (dn.K // 32) * 18},
+                        lambda dd=dd, dn=dn, o=o: qmv.qmv_moe_down("q4_0", dd["W_down"], dd["G_down"], dd["ids"],
+                                                                   dd["weights"], o, dn.N, dn.K,
+                                                                   expert_scale=dd["expert_scale"])))
+            out.append(("moe_t1_wsum", {"k_wsum": 8 * dn.N * 4 + dn.N * 4},
+                        lambda dd=dd, Ydn=Ydn, o=o: qmv.qmv_moe_wsum(Ydn, dd["weights"], o, 8)))
+    # super-block formats
+    N6, K6 = 262144, 2816
+    W6, x6, y6 = w("q6_k", N6, K6, 10), x(1, K6, 10)[0], torch.empty(N6, device=dev)
+    out.append(("q6_k_lm_head_2816x262144", {"k_q6k": N6 * synth.row_bytes("q6_k", K6)}, lambda: qmv.qmv_q6_k(W6, x6, y6)))
+    W5 = [w("q5_k", n, 2816, 11 + i) for i, n in enumerate((5760, 5760, 128))]
+    x5 = x(1, 2816, 11)[0]
+    y5 = [torch.empty(n, device=dev) for n in (5760, 5760, 128)]
+    out.append(("q5_k_b9_2816x5760x2_128", {"k_q6k": (5760 * 2 + 128) * synth.row_bytes("q5_k", 2816)},
+                lambda: [qmv.qmv_q5_k(W_, x5, y_) for W_, y_ in zip(W5, y5)]))
+    E6 = torch.from_numpy(synth.make_weights("q6_k", 128 * 1408, 2816, cfg=9, part=12).reshape(128, 1408, -1)).to(dev)
+    x6e = x(1, 2816, 12)
+    ids6 = T(synth.router_topk(1, 128, 8, cfg=9, part=12).astype(np.int32))
+    y6e = torch.empty(8, 1408, device=dev)
+    out.append(("q6_k_moe_gate_up_t1", {"k_id_q6": 8 * 1408 * synth.row_bytes("q6_k", 2816)},
+                lambda: qmv.qmv_id("q6_k", E6, x6e, ids6, y6e, 1408, 2816)))
+    # the generic kernel (K % 64 != 0) and a prefill block set
+    Wg, Xg, Yg = w("q4_0", 4096, 4064, 13), x(1, 4064, 13), torch.empty((1, 4096), device=dev)
+    out.append(("generic_q4_0_4064x4096", {"k_generic": 4096 * 127 * 18}, lambda: qmv.qmv_q4_0(Wg, Xg, Yg, K=4064)))
+    Wp, Xp, Yp = w("q4_0", 14336, 4096, 14), x(512, 4096, 14), torch.empty((512, 14336), device=dev)
+    # prefill: weights once + X + Y (its 32 row blocks re-read the weights, partly from L2)
+    out.append(("prefill_q4_0_m512_4096x14336", {"k_mq<": 14336 * 128 * 18 + 512 * 4096 * 4 + 512 * 14336 * 4},
+                lambda: qmv.qmv_gemm("q4_0", Wp, Xp, Yp)))
+    return out
+
+
+def run_kernel_workloads(dev, reps, manifest_path):
+    """Calibration copies, then each workload `reps` times after a separator
+    kernel (a 1-element fill), synchronized; writes the manifest."""
+    import torch
+    wl = kernel_workloads(dev)
+    sep = torch.empty(1, device=dev)
+    src = torch.empty(256 * 2**20 // 4, dtype=torch.float32, device=dev).uniform_()
+    dst = torch.empty_like(src)
+    for fn in [c for _, _, c in wl]:  # one untimed pass: library set-up stays out
+        fn()
+    torch.cuda.synchronize()
+    for _ in range(5):
+        torch.mul(src, 1.0, out=dst)  # calibration: reads and writes 256 MiB
+    torch.cuda.synchronize()
+    del src, dst
+    for i, (_, _, fn) in enumerate(wl):
+        sep.fill_(float(i))
+        torch.cuda.synchronize()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+    man = {"reps": reps, "workloads": [{"name": n, "kernels": kb} for n, kb, _ in wl]}
+    with open(manifest_path, "w") as f:
+        json.dump(man, f, indent=1)
+    print(f"kernel workloads done: {len(wl)} x {reps}", flush=True)
+
+
+def summarize_kernels(trace_dir, pmc_dirs, manifest_path, cmd_note):
+    """rocprofv3 CSV output of run_kernel_workloads (a kernel trace and
+    counter passes) -> profiles/counters_<kernel>.txt, one per library
+    kernel: duration, HBM traffic against algorithmic bytes (scaled by a
+    256 MiB copy), L2 hit rate, VALU busy and instructions, occupancy."""
+    import csv
+    import glob
+    import statistics
+    man = json.load(open(manifest_path))
+    wls = man["workloads"]
+
+    def rows(d, pat):
+        return [r for f in glob.glob(os.path.join(d, "**", pat), recursive=True) for r in csv.DictReader(open(f))]
+
+    def segment(disp):
+        """dispatches (dict id -> name) in id order split at the fill separators"""
+        seg, cur, calib = {}, None, []
+        for i in sorted(disp):
+            n = disp[i]
+            if "FillFunctor" in n or "fill" in n.lower():
+                cur = 0 if cur is None else cur + 1
+                continue
+            if cur is None:
+                if "MulFunctor" in n:
+                    calib.append(i)
+                continue
+            seg[i] = cur
+        return seg, calib
+    tr = rows(trace_dir, "*kernel_trace.csv")
+    tdisp = {int(r["Dispatch_Id"]): r["Kernel_Name"] for r in tr}
+    tdur = {int(r["Dispatch_Id"]): (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in tr}
+    tseg, _ = segment(tdisp)
+    # counters: value per (dispatch, counter), summed over instances
+    # the CSV holds each counter summed over its instances; GRBM_GUI_ACTIVE
+    # (elapsed GPU cycles) is counted once per XCD, so it is divided by
+    # their number (the vendor's derived metrics take its maximum)
+    agents = [a for a in rows(pmc_dirs[0], "*agent_info.csv") if a.get("Name", "").startswith("gfx")]
+    xcc = int(agents[0].get("Num_Xcc", 1)) if agents else 1
+    ncu = int(agents[0].get("Cu_Count", 256)) if agents else 256
+    cnt, cdisp = {}, {}
+    for d in pmc_dirs:
+        for r in rows(d, "*counter_collection.csv"):
+            key = (d, int(r["Dispatch_Id"]))
+            cdisp[key] = r["Kernel_Name"]
+            c, v = r["Counter_Name"], float(r["Counter_Value"])
+            if c == "GRBM_GUI_ACTIVE":
+                v /= xcc
+            cnt.setdefault(key, {})[c] = cnt.setdefault(key, {}).get(c, 0.0) + v
+    per = {}  # (workload index, kernel key) -> counter name -> [values]
+    calib = {}
+    for d in pmc_dirs:
+        disp = {i: n for (dd, i), n in cdisp.items() if dd == d}
+        seg, cal = segment(disp)
+        for i in cal:
+            for c, v in cnt[(d, i)].items():
+                calib.setdefault(c, []).append(v)
+        for i, wi in seg.items():
+            name = disp[i]
+            for kk in wls[wi]["kernels"]:
+                if kk in name:
+                    for c, v in cnt[(d, i)].items():
+                        per.setdefault((wi, kk), {}).setdefault(c, []).append(v)
+    reps = man["reps"]
+    copy = 256 * 2**20
+    f_scale = copy / (1024 * statistics.median(calib["FETCH_SIZE"])) if calib.get("FETCH_SIZE") else None
+    w_scale = copy / (1024 * statistics.median(calib["WRITE_SIZE"])) if calib.get("WRITE_SIZE") else None
+    by_kernel = {}
+    for wi, wl in enumerate(wls):
+        for kk, alg in wl["kernels"].items():
+            # per call of the workload (a call may launch the kernel several
+            # times, e.g. the three projections of a group): sums over its
+            # dispatches / calls; rates are cycle-weighted over them
+            durs = [tdur[i] for i, s in tseg.items() if s == wi and kk in tdisp[i]]
+            pv = per.get((wi, kk), {})
+            c = {k: sum(v) / reps for k, v in pv.items()}
+            line = {"workload": wl["name"], "dispatches_per_call": round(len(durs) / reps, 2),
+                    "us_per_call": round(sum(durs) / reps, 2) if durs else None, "alg_bytes": alg}
+            if durs:
+                line["alg_GBps"] = round(alg / (sum(durs) / reps) / 1e3, 1)
+            if "FETCH_SIZE" in c and f_scale:
+                line["fetch_bytes"] = round(c["FETCH_SIZE"] * 1024 * f_scale)
+                line["fetch_over_alg"] = round(line["fetch_bytes"] / alg, 3)
+            if "WRITE_SIZE" in c and w_scale:
+                line["write_bytes"] = round(c["WRITE_SIZE"] * 1024 * w_scale)
+            if "TCC_HIT" in c and "TCC_MISS" in c and c["TCC_HIT"] + c["TCC_MISS"] > 0:
+                line["l2_hit_pct"] = round(100 * c["TCC_HIT"] / (c["TCC_HIT"] + c["TCC_MISS"]), 1)
+            g = c.get("GRBM_GUI_ACTIVE")
+            if g and "SQ_ACTIVE_INST_VALU" in c:
+                line["valu_busy_pct"] = round(100 * c["SQ_ACTIVE_INST_VALU"] / ncu / g, 1)
+            if g and "SQ_WAVE_CYCLES" in c:
+                line["occupancy_pct"] = round(400 * c["SQ_WAVE_CYCLES"] / g / ncu / 32, 1)
+            if "SQ_INSTS_VALU" in c and "SQ_WAVES" in c:
+                line["valu_insts_per_wave"] = round(c["SQ_INSTS_VALU"] / max(1, c["SQ_WAVES"]))
+                wts = alg / (0.5625 if "q4_0" in wl["name"] else 34 / 32 if "q8_0" in wl["name"] else 1)
+                line["valu_lane_insts_per_weight"] = round(c["SQ_INSTS_VALU"] * 64 / wts, 2)
+            if g and "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+                line["mfma_util_pct"] = round(100 * c["SQ_VALU_MFMA_BUSY_CYCLES"] / (g * ncu * 4), 1)
+            if g and "TCP_TCP_TA_DATA_STALL_CYCLES" in c:
+                line["ta_data_stall_pct"] = round(100 * c["TCP_TCP_TA_DATA_STALL_CYCLES"] / g / ncu, 1)
+            if g and "SQ_WAIT_INST_ANY" in c and "SQ_WAVE_CYCLES" in c and c["SQ_WAVE_CYCLES"] > 0:
+                line["wave_wait_inst_pct"] = round(100 * c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"], 1)
+            by_kernel.setdefault(kk.strip("<"), []).append(line)
+    for k, lines in by_kernel.items():
+        text = [f"# {k}: figures per call of each workload (over {reps} calls), kernel sources {kernel_hash()}",
+                f"# command: {cmd_note}",
+                f"# traffic = FETCH_SIZE / WRITE_SIZE x the scale that makes a 256 MiB copy read 256 MiB "
+                f"(fetch scale {f_scale and round(f_scale, 4)}, write scale {w_scale and round(w_scale, 4)}); "
+                "valu_busy = SQ_ACTIVE_INST_VALU / CUs / GRBM_GUI_ACTIVE; occupancy = SQ_WAVE_CYCLES share of "
+                "32 wave slots per CU; VALU lane instructions per weight = SQ_INSTS_VALU x 64 / weights"]
+        text += [json.dumps(ln) for ln in lines]
+        with open(os.path.join(ROOT, "profiles", f"counters_{k}.txt"), "w") as f:
+            f.write("\n".join(text) + "\n")
+        print("\n".join(text))
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize":
         summarize(sys.argv[2], sys.argv[3], sys.argv[4], " ".join(sys.argv[5:]))
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-kernels":
+        summarize_kernels(sys.argv[2], sys.argv[3].split(","), sys.argv[4], " ".join(sys.argv[5:]))
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--kernel-workloads":
+        import torch
+        from block_quantized_weight_qmatmul_amd import qmv
+        qmv.lib()
+        run_kernel_workloads(torch.device("cuda:0"), int(sys.argv[2]), sys.argv[3])
         return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-trace":
         summarize_trace(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], " ".join(sys.argv[6:]))
