@@ -93,24 +93,6 @@ __host__ __device__ constexpr int block_bytes(int qtype) { return qtype == QMV_Q
 // Device helpers
 // ---------------------------------------------------------------------------
 
-// (code - 8) / 16 for the low nibble of byte B of w, where w already holds
-// the code bytes XORed with 0x88 (v_cvt_off_f32_i4 reads bits [3:0] as a
-// signed 4-bit value and divides by 16; code ^ 8 sign-extends to code - 8).
-template <int B>
-__device__ __forceinline__ float nib(uint32_t w) {
-    float r;
-    if constexpr (B == 0) {
-        r = __builtin_amdgcn_cvt_off_f32_i4((int)w);
-    } else if constexpr (B == 1) {
-        asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(r) : "v"(w));
-    } else if constexpr (B == 2) {
-        asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(r) : "v"(w));
-    } else {
-        asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(r) : "v"(w));
-    }
-    return r;
-}
-
 // Signed int8 code in byte B of w, as float.
 template <int B>
 __device__ __forceinline__ float sbyte(uint32_t w) {
@@ -127,7 +109,7 @@ __device__ __forceinline__ void unroll(F&& f) {
 }
 
 // Sum over one Q4_0 block whose 16 code bytes start at byte QB of the
-// register window u[] (u = raw ^ 0x88888888, u4 = u >> 4); xv = the block's
+// register window u[] (u = raw ^ 0x88888888, u4 = hi_nibbles(u)); xv = the block's
 // 32 activations. Returns sum_j (code_j - 8) / 16 * x_j.
 template <int QB>
 __device__ __forceinline__ float q4_block(const uint32_t* u, const uint32_t* u4, const float4* xv) {
@@ -169,7 +151,7 @@ __device__ __forceinline__ float q4_pair(const uint32_t* r, const float4* xv) {
 #pragma unroll
     for (int i = 0; i < 9; ++i) {
         u[i] = r[i] ^ 0x88888888u;
-        u4[i] = u[i] >> 4;
+        u4[i] = hi_nibbles(u[i]);
     }
     const float d0 = half_lo(r[0]);
     const float d1 = half_hi(r[4]);
@@ -325,6 +307,47 @@ __device__ __forceinline__ void stage_swiglu(float* xs, size_t xstride, const fl
     }
 }
 
+// nx activation rows gathered by pair into the padded layout, row i at
+// xs + i * xstride: pair plist[i] uses row plist[i] / top_k of X (with SW the
+// row holds 2K values and its SwiGLU is staged). The loads of all rows go out
+// before any store (CH 16-byte chunks per thread at a time, half that with
+// SW), so staging several rows costs about one memory latency, not one per
+// row.
+template <int NT, bool SW, int CH0 = 8>
+__device__ __forceinline__ void stage_gather(float* xs, size_t xstride, const float* __restrict__ X, size_t ldx,
+                                             const int* plist, int top_k, int nx, int K) {
+    constexpr int CH = SW ? CH0 / 2 : CH0;
+    const int nch = K >> 2;
+    const int total = nx * nch;
+    for (int c0 = threadIdx.x; c0 < total; c0 += CH * NT) {
+        f32x4u_t a[CH], b[CH];
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int c = c0 + i * NT;
+            if (c < total) {
+                const int r = c / nch, cc = c - r * nch;
+                const float* src = X + (size_t)(plist[r] / top_k) * ldx + 4 * cc;
+                a[i] = *reinterpret_cast<const f32x4u_t*>(src);
+                if constexpr (SW) b[i] = *reinterpret_cast<const f32x4u_t*>(src + K);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int c = c0 + i * NT;
+            if (c < total) {
+                const int r = c / nch, cc = c - r * nch;
+                float4 v;
+                if constexpr (SW)
+                    v = make_float4(silu_f(a[i].x) * b[i].x, silu_f(a[i].y) * b[i].y, silu_f(a[i].z) * b[i].z,
+                                    silu_f(a[i].w) * b[i].w);
+                else
+                    v = make_float4(a[i].x, a[i].y, a[i].z, a[i].w);
+                *reinterpret_cast<float4*>(xs + (size_t)r * xstride + (cc >> 4) * XS_PAIR + 4 * (cc & 15)) = v;
+            }
+        }
+    }
+}
+
 // v + (v of another lane chosen by a DPP control); lanes outside row_mask
 // add 0.
 template <int CTRL, int ROW_MASK = 0xF>
@@ -375,9 +398,7 @@ __device__ __forceinline__ void m1_stream(const uint8_t* __restrict__ W, size_t 
     if (tile >= ntiles) return;  // uniform over the workgroup
     int it = 0;
     // Two register buffers take turns: the next step's loads go into one
-    // while the other is decoded, with no copy between them; the last step
-    // is decoded on a path of its own, so that the wait before every other
-    // decode counts exactly the loads issued after it.
+    // while the other is decoded, with no copy between them.
     uint32_t bufA[RPT][DW], bufB[RPT][DW];
     auto issue = [&](long tl, int i, uint32_t (&b)[RPT][DW]) {
         const long row0 = tl * ROWS + lrow;
@@ -401,17 +422,23 @@ __device__ __forceinline__ void m1_stream(const uint8_t* __restrict__ W, size_t 
         stage_x_load<WAVES * 64, XCH>(xv, x, K);
         issue(tile, 0, bufA);
         stage_x_store<WAVES * 64, XCH>(xs, xv, K);
+        wait_vmcnt<RPT * pair_loads<DW>()>();  // x loaded; only the weight loads remain
         lds_barrier();
     }
     float tot[RPT];
 #pragma unroll
     for (int r = 0; r < RPT; ++r) tot[r] = 0.f;
     auto consume = [&](const uint32_t (&cb)[RPT][DW]) {
+        // Lanes past the row end decode the clamped pair they loaded and add
+        // zero: no branch around the decode, whose wait for this buffer's
+        // loads must lie on every path (the next issue overwrites them).
         const int p = j + it * LPR;
-        if (p < P) {
-            const float4* xv = reinterpret_cast<const float4*>(xs + p * XS_PAIR);
+        const bool in = p < P;
+        const float4* xv = reinterpret_cast<const float4*>(xs + (in ? p : P - 1) * XS_PAIR);
 #pragma unroll
-            for (int r = 0; r < RPT; ++r) tot[r] += T::dot(cb[r], xv);
+        for (int r = 0; r < RPT; ++r) {
+            const float d = T::dot(cb[r], xv);
+            tot[r] += in ? d : 0.f;
         }
         if (it == IPT - 1) {
             const long row0 = tile * ROWS + lrow;
@@ -423,25 +450,34 @@ __device__ __forceinline__ void m1_stream(const uint8_t* __restrict__ W, size_t 
             }
         }
     };
-    auto step = [&](uint32_t (&cb)[RPT][DW], uint32_t (&nb)[RPT][DW]) -> bool {
+    // One step: issue the next step into `nb` and decode `cb`. Past the
+    // last tile the loads are issued anyway (rows and pairs are clamped, the
+    // data is never used), so that every step has the same shape and the
+    // wait before each decode counts exactly the loads issued after it.
+    auto step = [&](uint32_t (&cb)[RPT][DW], uint32_t (&nb)[RPT][DW]) {
         int it2 = it + 1;
         long tile2 = tile;
         if (it2 == IPT) {
             it2 = 0;
             tile2 += tile_stride;
         }
-        if (tile2 >= ntiles) {
-            consume(cb);
-            return false;
-        }
         issue(tile2, it2, nb);
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) pin_regs<DW>(cb[r]);
         consume(cb);
         tile = tile2;
         it = it2;
-        return true;
     };
-    while (step(bufA, bufB) && step(bufB, bufA)) {
+    // A counted loop with one exit: with an exit after each of the two
+    // steps, the compiler joins the exits, and the joined path makes it wait
+    // for the other buffer's loads before every issue.
+    const long nsteps = ((ntiles - 1 - first_tile) / tile_stride + 1) * IPT;
+    long s = 0;
+    for (; s + 2 <= nsteps; s += 2) {
+        step(bufA, bufB);
+        step(bufB, bufA);
     }
+    if (s < nsteps) step(bufA, bufB);
 }
 
 // ---------------------------------------------------------------------------
@@ -558,9 +594,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_m1c(const M1Cat<MAXP> C) {
     long st0 = it0;
     int it = 0;
     // Two register buffers take turns: the next step's loads go into one
-    // while the other is decoded, with no copy between them. The last step
-    // is decoded on a path of its own, so that on every other step the wait
-    // before the decode counts exactly the loads issued after it.
+    // while the other is decoded, with no copy between them.
     uint32_t bufA[DW], bufB[DW];
     auto issue = [&](long tl, int i, uint32_t (&b)[DW]) {
         const long row = (tl - it0) * ROWS + lrow;
@@ -575,13 +609,16 @@ __global__ __launch_bounds__(WAVES * 64) void k_m1c(const M1Cat<MAXP> C) {
         stage_x_load<WAVES * 64, XCH>(xv, C.x, K);
         issue(tile, 0, bufA);
         stage_x_store<WAVES * 64, XCH>(xs, xv, K);
+        wait_vmcnt<pair_loads<DW>()>();  // x loaded; only the weight loads remain
         lds_barrier();
     }
     float tot = 0.f;
     // decode the current step from `cb`; write the row at the end of a tile
     auto consume = [&](const uint32_t (&cb)[DW]) {
-        const int p = j + it * LPR;
-        if (p < P) tot += T::dot(cb, reinterpret_cast<const float4*>(xs + p * XS_PAIR));
+        const int p = j + it * LPR;  // past the row end: decode the clamped pair, add zero (see m1_stream)
+        const bool in = p < P;
+        const float d = T::dot(cb, reinterpret_cast<const float4*>(xs + (in ? p : P - 1) * XS_PAIR));
+        tot += in ? d : 0.f;
         if (it == IPT - 1) {
             const long row = (tile - st0) * ROWS + lrow;
             const float sum = lane_group_sum<LPR>(tot);
@@ -589,9 +626,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_m1c(const M1Cat<MAXP> C) {
             tot = 0.f;
         }
     };
-    // One step: issue the next step into `nb` and decode `cb`; false after
-    // the last step.
-    auto step = [&](uint32_t (&cb)[DW], uint32_t (&nb)[DW]) -> bool {
+    // One step: issue the next step into `nb` and decode `cb`.
+    auto step = [&](uint32_t (&cb)[DW], uint32_t (&nb)[DW]) {
         int it2 = it + 1;
         long tile2 = tile;
         if (it2 == IPT) {
@@ -608,11 +644,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_m1c(const M1Cat<MAXP> C) {
                 }
             }
         }
-        if (tile2 >= ntiles) {
-            consume(cb);
-            return false;
-        }
+        // Past the last tile the loads are issued anyway (rows and pairs are
+        // clamped, the data is never used), so that every step has the same
+        // shape and the wait before each decode counts exactly the loads
+        // issued after it.
         issue(tile2, it2, nb);
+        pin_regs<DW>(cb);
         consume(cb);
         if (it2 == 0) {  // the next step starts the tile just issued
             sy = C.y[ip];
@@ -621,10 +658,17 @@ __global__ __launch_bounds__(WAVES * 64) void k_m1c(const M1Cat<MAXP> C) {
         }
         tile = tile2;
         it = it2;
-        return true;
     };
-    while (step(bufA, bufB) && step(bufB, bufA)) {
+    // A counted loop with one exit: with an exit after each of the two
+    // steps, the compiler joins the exits, and the joined path makes it wait
+    // for the other buffer's loads before every issue.
+    const long nsteps = ((ntiles - 1 - blockIdx.x) / stride + 1) * IPT;
+    long s = 0;
+    for (; s + 2 <= nsteps; s += 2) {
+        step(bufA, bufB);
+        step(bufB, bufA);
     }
+    if (s < nsteps) step(bufA, bufB);
 }
 
 // ---------------------------------------------------------------------------
@@ -733,7 +777,7 @@ __device__ __forceinline__ void decode_pair(const uint32_t* r, float* w, float& 
 #pragma unroll
         for (int i = 0; i < 9; ++i) {
             u[i] = r[i] ^ 0x88888888u;
-            u4[i] = u[i] >> 4;
+            u4[i] = hi_nibbles(u[i]);
         }
         unroll<0, 2>([&](auto R) {
             constexpr int QB = R ? 20 : 2;
@@ -755,6 +799,31 @@ __device__ __forceinline__ void decode_pair(const uint32_t* r, float* w, float& 
         });
         d0 = half_lo(r[0]);
         d1 = half_hi(r[8]);
+    }
+}
+
+// Weights 16H .. 16H + 15 ((code - 8) / 16 for Q4_0, code for Q8_0) of
+// block R (0 or 1) of a pair held in registers r, as decode_pair gives them.
+template <int QT, int R, int H>
+__device__ __forceinline__ void decode_half_w(const uint32_t* r, float* w) {
+    if constexpr (QT == QMV_Q4_0) {
+        constexpr int QB = R ? 20 : 2;  // the block's 16 code bytes: low nibbles 0..15, high 16..31
+        uint32_t u[5];
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+            u[i] = r[QB / 4 + i] ^ 0x88888888u;
+            if constexpr (H == 1) u[i] = hi_nibbles(u[i]);
+        }
+        unroll<0, 16>([&](auto I) {
+            constexpr int t = QB % 4 + I;
+            w[I] = nib<t % 4>(u[t / 4]);
+        });
+    } else {
+        constexpr int QB = (R ? 36 : 2) + 16 * H;
+        unroll<0, 16>([&](auto I) {
+            constexpr int t = QB + I;
+            w[I] = sbyte<t % 4>(r[t / 4]);
+        });
     }
 }
 
@@ -959,6 +1028,265 @@ __global__ __launch_bounds__(WAVES * 64) void k_id(const uint8_t* __restrict__ W
 }
 
 // ---------------------------------------------------------------------------
+// Expert-indexed product grouped by expert, for calls with many pairs
+// (batched decode, prefill). Every workgroup first groups the call's pairs by
+// expert in LDS: the distinct experts u = 0 .. U-1 in order of first
+// appearance and, for each, the pairs that select it. The rows of the
+// distinct experts form one virtual matrix (virtual row v = u * N + n); each
+// persistent workgroup takes an equal contiguous range of it, cut where the
+// expert changes into segments. For a segment the workgroup stages the
+// activation rows of its expert's pairs (mxcap at a time) and streams the
+// segment's weight rows once, decoding each pair of blocks once and
+// multiplying it into every staged row. So every selected expert is read once
+// per call (once per mxcap of its pairs when more select it), with no
+// workspace. A pair whose id is outside [0, n_experts) gets a NaN row and sets
+// *err_flag. Per-pair results do not depend on how pairs are grouped, so the
+// order of the atomics that fill the pair lists does not change any output.
+// ---------------------------------------------------------------------------
+constexpr int IDP_MAX_EXPERTS = 1024;  // experts the LDS tables index
+constexpr int IDP_MAX_PAIRS = 1024;    // pairs one launch groups
+constexpr int IDP_MX = 8;              // activation rows streamed together
+// Rows per lane group. Two (the staged rows read once for both) measured
+// slower on the MoE gate_up / down calls at 32 tokens (203 vs 163 us per
+// pair of calls): fewer staged rows per pass and larger tiles.
+constexpr int IDP_RPT = 1;
+
+template <int QT, int LPR, int RPT, int WAVES, bool SW>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_idp(
+    const uint8_t* __restrict__ W, size_t estride, size_t ldw, int n_experts, const float* __restrict__ X,
+    size_t ldx, const uint32_t* __restrict__ ids, int n_pairs, int top_k, float* __restrict__ Y, size_t ldy, int N,
+    int K, const float* __restrict__ escale, int* __restrict__ err_flag, int mxcap) {
+    using T = PairTraits<QT>;
+    constexpr int DW = T::DW, PB = DW * 4;
+    constexpr int NT = WAVES * 64;
+    constexpr int QPT = IDP_MAX_PAIRS / NT;  // ids per thread
+    constexpr int GROUPS = 64 / LPR;
+    constexpr int ROWS = GROUPS * RPT * WAVES;
+    constexpr int MXR = IDP_MX / RPT;  // staged rows per pass (registers)
+    __shared__ int s_map[IDP_MAX_EXPERTS];  // first pair of expert e, later its u
+    __shared__ int s_uexp[IDP_MAX_PAIRS];   // expert of u
+    __shared__ int s_ustart[IDP_MAX_PAIRS + 1];
+    __shared__ int s_cnt[IDP_MAX_PAIRS];    // pairs of u, later the fill cursor
+    __shared__ int s_plist[IDP_MAX_PAIRS];  // pairs grouped by u
+    __shared__ int s_U;
+    extern __shared__ __align__(16) float xs[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    // ---- group the pairs by expert ----
+    uint32_t myid[QPT];
+#pragma unroll
+    for (int k = 0; k < QPT; ++k) {
+        const int q = tid + k * NT;
+        myid[k] = q < n_pairs ? ids[q] : 0xFFFFFFFFu;
+    }
+    for (int e = tid; e < n_experts; e += NT) s_map[e] = 0x7FFFFFFF;
+    for (int u = tid; u < IDP_MAX_PAIRS; u += NT) s_cnt[u] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < QPT; ++k)
+        if (myid[k] < (uint32_t)n_experts) atomicMin(&s_map[myid[k]], tid + k * NT);
+    __syncthreads();
+    if (wave == 0) {  // distinct experts in order of first appearance
+        int base = 0;
+        for (int q0 = 0; q0 < n_pairs; q0 += 64) {
+            const int q = q0 + lane;
+            const uint32_t e = q < n_pairs ? ids[q] : 0xFFFFFFFFu;
+            const bool first = e < (uint32_t)n_experts && s_map[e] == q;
+            const uint64_t m = __ballot(first);
+            if (first) s_uexp[base + __popcll(m & ((1ull << lane) - 1ull))] = (int)e;
+            base += __popcll(m);
+        }
+        if (lane == 0) s_U = base;
+    }
+    __syncthreads();
+    const int U = s_U;
+    for (int u = tid; u < U; u += NT) s_map[s_uexp[u]] = u;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < QPT; ++k)
+        if (myid[k] < (uint32_t)n_experts) atomicAdd(&s_cnt[s_map[myid[k]]], 1);
+    __syncthreads();
+    if (wave == 0) {  // exclusive scan of the counts; the counts become cursors
+        int base = 0;
+        for (int u0 = 0; u0 < U; u0 += 64) {
+            const int u = u0 + lane;
+            const int c = u < U ? s_cnt[u] : 0;
+            int incl = c;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int t = __shfl_up(incl, o, 64);
+                if (lane >= o) incl += t;
+            }
+            if (u < U) {
+                s_ustart[u] = base + incl - c;
+                s_cnt[u] = base + incl - c;
+            }
+            base += __shfl(incl, 63, 64);
+        }
+        if (lane == 0) s_ustart[U] = base;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < QPT; ++k)
+        if (myid[k] < (uint32_t)n_experts) s_plist[atomicAdd(&s_cnt[s_map[myid[k]]], 1)] = tid + k * NT;
+    // pairs with an id out of range: NaN rows, spread over the workgroups
+    for (int q = blockIdx.x; q < n_pairs; q += gridDim.x) {
+        if (ids[q] >= (uint32_t)n_experts) {
+            for (int n = tid; n < N; n += NT) Y[(size_t)q * ldy + n] = __builtin_nanf("");
+            if (tid == 0 && err_flag) *err_flag = 1;
+        }
+    }
+    __syncthreads();
+
+    // ---- stream this workgroup's share of the virtual matrix ----
+    const int g = lane / LPR, j = lane % LPR;
+    const int P = K >> 6;
+    const int IPT = (P + LPR - 1) / LPR;
+    const size_t xstride = (size_t)P * XS_PAIR;
+    // Work is split by cost, not rows: a row of expert u costs its pairs
+    // plus 2 (the weight load and decode), so experts that many pairs select
+    // spread over more workgroups. Row n of u sits at cost B(u) + n * c(u);
+    // this workgroup takes the rows whose cost position is in [lo, hi).
+    auto B = [&](int u) { return (long)N * (s_ustart[u] + 2L * u); };
+    const long C = B(U);
+    const long lo = C * blockIdx.x / gridDim.x, hi = C * (blockIdx.x + 1) / gridDim.x;
+    int u = 0;
+    for (int span = 1 << 10; span > 0; span >>= 1)  // last u < U with B(u) <= lo
+        if (u + span < U && B(u + span) <= lo) u += span;
+    uint32_t bufA[RPT][DW], bufB[RPT][DW];
+    bool staged = false;  // xs holds rows another segment may still be reading
+    for (; u < U && B(u) < hi; ++u) {
+        const long cu = s_ustart[u + 1] - s_ustart[u] + 2;
+        const long a = lo - B(u), b = hi - B(u);
+        const int n0 = a <= 0 ? 0 : (int)((a + cu - 1) / cu);
+        const int n1 = (int)((b + cu - 1) / cu < N ? (b + cu - 1) / cu : N);
+        if (n0 >= n1) continue;
+        const uint32_t e = (uint32_t)s_uexp[u];
+        const uint8_t* We = W + (size_t)e * estride;
+        const float sc = (escale ? escale[e] : 1.f) * T::OUT_SCALE;
+        const int pbeg = s_ustart[u], pend = s_ustart[u + 1];
+        const int ntl = (n1 - n0 + ROWS - 1) / ROWS;
+        const int lrow = (wave * GROUPS + g) * RPT;  // this lane group's first row in a tile
+        for (int c0 = pbeg; c0 < pend; c0 += mxcap) {
+            const int nx = pend - c0 < mxcap ? pend - c0 : mxcap;
+            int tile = 0, it = 0;
+            auto issue = [&](int tl, int i, uint32_t (&b)[RPT][DW]) {
+                int pp = j + i * LPR;
+                pp = pp < P ? pp : P - 1;
+#pragma unroll
+                for (int r = 0; r < RPT; ++r) {
+                    int row = n0 + tl * ROWS + lrow + r;
+                    row = row < n1 ? row : n1 - 1;
+                    load_pair<DW>(We + (size_t)row * ldw + (size_t)pp * PB, b[r]);
+                }
+            };
+            issue(0, 0, bufA);
+            if (staged) lds_barrier();  // the previous rows' LDS reads are done
+            // (fewer chunks in flight with two rows' weight loads pending)
+            stage_gather<NT, SW, RPT == 1 ? 8 : 4>(xs, xstride, X, ldx, s_plist + c0, top_k, nx, K);
+            wait_vmcnt<RPT * pair_loads<DW>()>();  // x loaded; only the weight loads remain
+            lds_barrier();
+            staged = true;
+            float tot[RPT][MXR];
+#pragma unroll
+            for (int r = 0; r < RPT; ++r)
+#pragma unroll
+                for (int i = 0; i < MXR; ++i) tot[r][i] = 0.f;
+            // decode each half block (16 weights) of the RPT pairs once and
+            // multiply it into every staged row (x read once for the RPT
+            // rows; 16 weights per row live at a time); the sums run over a
+            // block's weights in order, as in the other kernels. Lanes past
+            // the row end decode the clamped pair and add zero.
+            auto consume = [&](const uint32_t (&cb)[RPT][DW]) {
+                const int pp = j + it * LPR;
+                const bool in = pp < P;
+                const int pc = in ? pp : P - 1;
+                float sb[2][RPT][MXR];  // per block
+                unroll<0, 4>([&](auto RH) {
+                    constexpr int R = RH / 2, H = RH % 2;
+                    float w[RPT][16];
+#pragma unroll
+                    for (int r = 0; r < RPT; ++r) decode_half_w<QT, R, H>(cb[r], w[r]);
+#pragma unroll
+                    for (int i = 0; i < MXR; ++i) {
+                        if constexpr (H == 0) {
+#pragma unroll
+                            for (int r = 0; r < RPT; ++r) sb[R][r][i] = 0.f;
+                        }
+                        if (i < nx) {
+                            const float4* xv =
+                                reinterpret_cast<const float4*>(xs + i * xstride + pc * XS_PAIR) + 8 * R + 4 * H;
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                const float4 x4 = xv[q];
+#pragma unroll
+                                for (int r = 0; r < RPT; ++r) {
+                                    sb[R][r][i] = fmaf(w[r][4 * q], x4.x, sb[R][r][i]);
+                                    sb[R][r][i] = fmaf(w[r][4 * q + 1], x4.y, sb[R][r][i]);
+                                    sb[R][r][i] = fmaf(w[r][4 * q + 2], x4.z, sb[R][r][i]);
+                                    sb[R][r][i] = fmaf(w[r][4 * q + 3], x4.w, sb[R][r][i]);
+                                }
+                            }
+                        }
+                    }
+                    // one half block at a time: hoisting the next decode
+                    // above these products only holds more registers
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+#pragma unroll
+                for (int r = 0; r < RPT; ++r) {
+                    const float d0 = half_lo(cb[r][0]), d1 = QT == QMV_Q4_0 ? half_hi(cb[r][4]) : half_hi(cb[r][8]);
+#pragma unroll
+                    for (int i = 0; i < MXR; ++i) {
+                        if (i < nx) {
+                            const float d = fmaf(d1, sb[1][r][i], d0 * sb[0][r][i]);
+                            tot[r][i] += in ? d : 0.f;
+                        }
+                    }
+                }
+                if (it == IPT - 1) {
+                    const int row0 = n0 + tile * ROWS + lrow;
+#pragma unroll
+                    for (int i = 0; i < MXR; ++i) {
+                        if (i < nx) {
+                            float* yr = Y + (size_t)s_plist[c0 + i] * ldy;
+#pragma unroll
+                            for (int r = 0; r < RPT; ++r) {
+                                const float sum = lane_group_sum<LPR>(tot[r][i]);
+                                if (j == LPR - 1 && row0 + r < n1) yr[row0 + r] = sum * sc;
+                            }
+                        }
+#pragma unroll
+                        for (int r = 0; r < RPT; ++r) tot[r][i] = 0.f;
+                    }
+                }
+            };
+            // one step, the same shape every time (see m1_stream)
+            auto step = [&](uint32_t (&cb)[RPT][DW], uint32_t (&nb)[RPT][DW]) {
+                int it2 = it + 1, tile2 = tile;
+                if (it2 == IPT) {
+                    it2 = 0;
+                    ++tile2;
+                }
+                issue(tile2, it2, nb);
+#pragma unroll
+                for (int r = 0; r < RPT; ++r) pin_regs<DW>(cb[r]);
+                consume(cb);
+                tile = tile2;
+                it = it2;
+            };
+            const int nsteps = ntl * IPT;
+            int st = 0;
+            for (; st + 2 <= nsteps; st += 2) {
+                step(bufA, bufB);
+                step(bufB, bufA);
+            }
+            if (st < nsteps) step(bufA, bufB);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Expert-indexed product for decode-sized calls (few pairs). The n_pairs x N
 // output rows form one virtual matrix, virtual row v = p * N + n (row n of
 // expert ids[p], output row p, activation row p / top_k), streamed by
@@ -1037,6 +1365,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_idv(const uint8_t* __restrict__ 
         issue(wrow(n, e), 0, bufA);
         stage_swiglu<NT>(xs, xstride, X, ldx, n_xrows, K);
     }
+    wait_vmcnt<pair_loads<DW>()>();  // x loaded; only the weight loads remain
     // each pair's scale, needed first at the end of the first tile
     const float scq = lane < n_pairs && escale && idq < (uint32_t)n_experts ? escale[idq] : 1.f;
     lds_barrier();
@@ -1044,11 +1373,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_idv(const uint8_t* __restrict__ 
     int it = 0;
     float tot = 0.f;
     auto consume = [&](const uint32_t (&cb)[DW]) {
-        const int pp = j + it * LPR;
-        if (pp < P) {
-            const float* xr = xs + (size_t)(p / top_k) * xstride + pp * XS_PAIR;
-            tot += T::dot(cb, reinterpret_cast<const float4*>(xr));
-        }
+        const int pp = j + it * LPR;  // past the row end: decode the clamped pair, add zero (see m1_stream)
+        const bool in = pp < P;
+        const float* xr = xs + (size_t)(p / top_k) * xstride + (in ? pp : P - 1) * XS_PAIR;
+        const float d = T::dot(cb, reinterpret_cast<const float4*>(xr));
+        tot += in ? d : 0.f;
         if (it == IPT - 1) {
             const float sc = __shfl(scq, p, 64) * T::OUT_SCALE;
             const float sum = lane_group_sum<LPR>(tot) * sc;
@@ -1061,7 +1390,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_idv(const uint8_t* __restrict__ 
             tot = 0.f;
         }
     };
-    auto step = [&](uint32_t (&cb)[DW], uint32_t (&nb)[DW]) -> bool {
+    // one step, the same shape every time (see m1_stream; rowinfo clamps
+    // rows past the last tile)
+    auto step = [&](uint32_t (&cb)[DW], uint32_t (&nb)[DW]) {
         int it2 = it + 1, tile2 = tile;
         int p2 = p, n2 = n;
         uint32_t e2 = e;
@@ -1069,22 +1400,23 @@ __global__ __launch_bounds__(WAVES * 64) void k_idv(const uint8_t* __restrict__ 
             it2 = 0;
             tile2 += gridDim.x;
         }
-        if (tile2 >= ntiles) {  // the last step, on a path of its own
-            consume(cb);
-            return false;
-        }
         if (tile2 != tile) rowinfo(tile2, p2, n2, e2);
         issue(wrow(n2, e2), it2, nb);
+        pin_regs<DW>(cb);
         consume(cb);
         tile = tile2;
         it = it2;
         p = p2;
         n = n2;
         e = e2;
-        return true;
     };
-    while (step(bufA, bufB) && step(bufB, bufA)) {
+    const int nsteps = ((ntiles - 1 - (int)blockIdx.x) / (int)gridDim.x + 1) * IPT;
+    int s = 0;
+    for (; s + 2 <= nsteps; s += 2) {
+        step(bufA, bufB);
+        step(bufB, bufA);
     }
+    if (s < nsteps) step(bufA, bufB);
 }
 
 // The few-pairs kernel for rows of at most idv_deep(QT) steps per lane: all
@@ -1267,8 +1599,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_moe_down(const uint8_t* __restri
             if (s2 < top_k) bn = base(s2);
         }
         if (s2 < top_k) issue(bn, it2);
-        const int p = j + it * LPR;
-        if (p < P) tot += T::dot(cur, reinterpret_cast<const float4*>(xs + (size_t)s * xstride + p * XS_PAIR));
+        pin_regs<DW>(cur);
+        const int p = j + it * LPR;  // past the row end: decode the clamped pair, add zero (see m1_stream)
+        const bool in = p < P;
+        const float d = T::dot(cur, reinterpret_cast<const float4*>(xs + (size_t)s * xstride + (in ? p : P - 1) * XS_PAIR));
+        tot += in ? d : 0.f;
         if (it == IPT - 1) {
             const uint32_t e = tids[s];
             const bool ok = e < (uint32_t)n_experts;
@@ -1336,7 +1671,11 @@ __device__ __forceinline__ void load_q6_unit(const uint8_t* sb, int h, uint32_t*
     const u32x2a2 sc = *reinterpret_cast<const u32x2a2*>(sb + 192 + 8 * h);
     r[24] = sc.x;
     r[25] = sc.y;
-    r[26] = *reinterpret_cast<const uint16_t*>(sb + 208);
+    // d is the high half of the dword ending the block (scales 14, 15 and
+    // d): a 16-bit load would be zero-extended where the compiler chooses,
+    // and that use makes it wait for all of a step's loads
+    typedef uint32_t u32a2 __attribute__((aligned(2)));
+    r[26] = *reinterpret_cast<const u32a2*>(sb + 206);
 }
 
 // Stage nx rows of x (row i at X + xoff[i]) for the Q6_K kernel: row i's
@@ -1394,7 +1733,7 @@ struct Q6Stage {
 template <int MX>
 __device__ __forceinline__ void q6_unit_dot(const uint32_t* r, const float* xs, size_t xstride, const float* gs,
                                             size_t gstride, int nx, float* tot) {
-    const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)(r[26] & 0xFFFFu));
+    const float d = half_hi(r[26]);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
 #pragma unroll
@@ -1660,7 +1999,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_q6k(const uint8_t* __restrict__ 
     long tile = blockIdx.x;
     if (tile >= ntiles) return;  // uniform over the workgroup
     int it = 0;
-    // two register buffers in turn (see k_m1c)
+    // two register buffers in turn (see m1_stream)
     uint32_t bufA[F::DW], bufB[F::DW];
     auto issue = [&](long tl, int i, uint32_t (&b)[F::DW]) {
         long row = tl * ROWS + lrow;
@@ -1690,8 +2029,16 @@ __global__ __launch_bounds__(WAVES * 64) void k_q6k(const uint8_t* __restrict__ 
 #pragma unroll
     for (int i = 0; i < MX; ++i) tot[i] = 0.f;
     auto consume = [&](const uint32_t (&cb)[F::DW]) {
-        const int u = j + it * LPR;
-        if (u < U) F::template dot<MX>(cb, u, K, xs + (size_t)u * XS_Q6, xstride, gs + 8 * u, gstride, nx, tot);
+        // past the row end: decode the clamped unit, add zero (see m1_stream)
+        const int u0 = j + it * LPR;
+        const bool in = u0 < U;
+        const int u = in ? u0 : U - 1;
+        float part[MX];
+#pragma unroll
+        for (int i = 0; i < MX; ++i) part[i] = 0.f;
+        F::template dot<MX>(cb, u, K, xs + (size_t)u * XS_Q6, xstride, gs + 8 * u, gstride, nx, part);
+#pragma unroll
+        for (int i = 0; i < MX; ++i) tot[i] += in ? part[i] : 0.f;
         if (it == IPT - 1) {
             const long row = tile * ROWS + lrow;
 #pragma unroll
@@ -1704,25 +2051,27 @@ __global__ __launch_bounds__(WAVES * 64) void k_q6k(const uint8_t* __restrict__ 
             }
         }
     };
-    auto step = [&](uint32_t (&cb)[F::DW], uint32_t (&nb)[F::DW]) -> bool {
+    // one step, the same shape every time (see m1_stream)
+    auto step = [&](uint32_t (&cb)[F::DW], uint32_t (&nb)[F::DW]) {
         int it2 = it + 1;
         long tile2 = tile;
         if (it2 == IPT) {
             it2 = 0;
             tile2 += gridDim.x;
         }
-        if (tile2 >= ntiles) {  // the last step, on a path of its own
-            consume(cb);
-            return false;
-        }
         issue(tile2, it2, nb);
+        pin_regs<F::DW>(cb);
         consume(cb);
         tile = tile2;
         it = it2;
-        return true;
     };
-    while (step(bufA, bufB) && step(bufB, bufA)) {
+    const long nsteps = ((ntiles - 1 - (long)blockIdx.x) / gridDim.x + 1) * IPT;
+    long s = 0;
+    for (; s + 2 <= nsteps; s += 2) {
+        step(bufA, bufB);
+        step(bufB, bufA);
     }
+    if (s < nsteps) step(bufA, bufB);
 }
 
 // Expert-indexed super-block (Q6_K, Q5_K) product: one workgroup per (tile of ROWS rows, pair
@@ -1800,18 +2149,24 @@ constexpr size_t LDS_PER_CU = 160 * 1024;  // gfx950
 // Lanes per row: the largest power of two (<= 64) whose lane utilisation
 // P / (LPR * ceil(P / LPR)) is within 5% of the best one, so long rows keep
 // a full wave on one row and short rows still use every lane.
-int pick_lpr(int P) {
+int pick_lpr(int P, int widest = 64) {
     const int cands[] = {64, 32, 16, 8, 4};
     double eff[5], best = 0;
     for (int i = 0; i < 5; ++i) {
         const int l = cands[i];
-        eff[i] = (double)P / ((double)l * ((P + l - 1) / l));
+        eff[i] = l > widest ? 0. : (double)P / ((double)l * ((P + l - 1) / l));
         if (eff[i] > best) best = eff[i];
     }
     for (int i = 0; i < 5; ++i)
         if (eff[i] >= best * 0.95) return cands[i];
     return 4;
 }
+
+// Lanes per row of the dense M = 1 kernels: as pick_lpr, at most 32, so
+// that rows of 64 pairs (K = 4096) take two steps per lane, which halves the
+// per-row reductions and overlaps the decode of one step with the loads of
+// the next (Q4_0 28672 x 4096: 14.0 vs 14.9 us; 4096 x 4096: 4.21 vs 4.38 us).
+int pick_lpr_m1(int P) { return pick_lpr(P, 32); }
 
 // Lanes per row for the Q6_K kernel (U units of 128 weights per row): the
 // widest group whose lane utilisation U / (LPR * ceil(U / LPR)) is at least
@@ -1846,14 +2201,13 @@ int launch_m1_t(const uint8_t* W, size_t ldw, const float* X, float* Y, int N, i
 // block is read before anything else starts.)
 template <int QT>
 int launch_m1(const uint8_t* W, size_t ldw, const float* X, float* Y, int N, int K, hipStream_t st) {
-    int lpr = pick_lpr(K / 64);
+    int lpr = pick_lpr_m1(K / 64);
     // Large matrices (at least two 32-row tiles per workgroup) with 1024 <=
     // K <= 8192: 16 lanes per row, so that a row's reduction and store come
     // once per several steps (Q4_0 65536 x 4096: 28.8 vs 31.1 us; 262144 x
     // 2816: 79.6 vs 83.2 us; Q8_0 262144 x 2816: 133.4 vs 137.0 us).
     if (N >= 32768 && K >= 1024 && K <= 8192) lpr = 16;
     switch (lpr) {
-        case 64: return launch_m1_t<QT, 64, 1, 8>(W, ldw, X, Y, N, K, 2, st);
         case 32: return launch_m1_t<QT, 32, 1, 8>(W, ldw, X, Y, N, K, 2, st);
         case 16: return launch_m1_t<QT, 16, 1, 8>(W, ldw, X, Y, N, K, 2, st);
         case 8: return launch_m1_t<QT, 8, 1, 8>(W, ldw, X, Y, N, K, 2, st);
@@ -1888,7 +2242,7 @@ int launch_m1c_n(const M1Prob* probs, int n, int wgs_per_cu, hipStream_t st) {
     C.x = probs[0].x;
     C.K = probs[0].K;
     C.n = n;
-    const int lpr = pick_lpr(C.K / 64);
+    const int lpr = pick_lpr_m1(C.K / 64);
     const long rows = (long)(64 / lpr) * 8;
     C.t0[0] = 0;
     for (int i = 0; i < n; ++i) {
@@ -1901,7 +2255,6 @@ int launch_m1c_n(const M1Prob* probs, int n, int wgs_per_cu, hipStream_t st) {
     const long tiles = C.t0[n];
     if (tiles > 0x7FFFFFFF) return fail(QMV_EINVAL, "N too large");
     switch (lpr) {
-        case 64: return launch_m1c_t<QT, 64, MAXP>(C, tiles, wgs_per_cu, st);
         case 32: return launch_m1c_t<QT, 32, MAXP>(C, tiles, wgs_per_cu, st);
         case 16: return launch_m1c_t<QT, 16, MAXP>(C, tiles, wgs_per_cu, st);
         case 8: return launch_m1c_t<QT, 8, MAXP>(C, tiles, wgs_per_cu, st);
@@ -2039,6 +2392,48 @@ int launch_id_t(const uint8_t* W, size_t es, size_t ldw, int E, const float* X, 
     hipLaunchKernelGGL((k_id<QT, LPR, RPT, WAVES, SW>), dim3((unsigned)tiles, (unsigned)n_pairs), dim3(WAVES * 64), lds,
                        st, W, es, ldw, E, X, ldx, ids, n_pairs, top_k, Y, ldy, N, K, sc, err, fast, mxcap);
     return check_launch("qmv_id kernel");
+}
+
+// The grouped kernel k_idp: 8 waves, two workgroups per CU when two staged
+// rows fit in the LDS that leaves (else one), as many staged rows per pass
+// as fit, at most IDP_MX.
+template <int QT, int LPR, int RPT, bool SW>
+int launch_idp_t(const uint8_t* W, size_t es, size_t ldw, int E, const float* X, size_t ldx, const uint32_t* ids,
+                 int n_pairs, int top_k, float* Y, size_t ldy, int N, int K, const float* sc, int* err,
+                 hipStream_t st) {
+    constexpr int WAVES = 8;
+    constexpr size_t STATIC_LDS = (size_t)(IDP_MAX_EXPERTS + 4 * IDP_MAX_PAIRS + 2) * sizeof(int);
+    const size_t one = xs_bytes(K);
+    int per_cu = 2;
+    long mx = (long)((LDS_PER_CU / 2 - STATIC_LDS) / one);
+    if (mx < 2) {
+        per_cu = 1;
+        mx = (long)((LDS_PER_CU - STATIC_LDS) / one);
+    }
+    mx = mx > IDP_MX / RPT ? IDP_MX / RPT : mx;
+    if (mx < 1) return fail(QMV_EINVAL, "internal: K=%d too large for the grouped id kernel", K);
+    // at most min(n_pairs, E) distinct experts of N rows each
+    const long umax = n_pairs < E ? n_pairs : E;
+    const long rows = (64 / LPR) * RPT * WAVES;
+    const long tiles = (umax * N + rows - 1) / rows;
+    long grid = (long)num_cus() * per_cu;
+    grid = grid < tiles ? grid : tiles;
+    grid = grid < 1 ? 1 : grid;
+    hipLaunchKernelGGL((k_idp<QT, LPR, RPT, WAVES, SW>), dim3((unsigned)grid), dim3(WAVES * 64), (size_t)mx * one, st, W,
+                       es, ldw, E, X, ldx, ids, n_pairs, top_k, Y, ldy, N, K, sc, err, (int)mx);
+    return check_launch("qmv_id grouped kernel");
+}
+
+template <int QT, bool SW>
+int launch_idp(const uint8_t* W, size_t es, size_t ldw, int E, const float* X, size_t ldx, const uint32_t* ids,
+               int n_pairs, int top_k, float* Y, size_t ldy, int N, int K, const float* sc, int* err,
+               hipStream_t st) {
+    const int lpr = pick_lpr(K / 64);
+#define QMV_IDP_CASE(L) \
+    if (lpr == L) return launch_idp_t<QT, L, IDP_RPT, SW>(W, es, ldw, E, X, ldx, ids, n_pairs, top_k, Y, ldy, N, K, sc, err, st);
+    QMV_IDP_CASE(64) QMV_IDP_CASE(32) QMV_IDP_CASE(16) QMV_IDP_CASE(8) QMV_IDP_CASE(4)
+#undef QMV_IDP_CASE
+    return fail(QMV_EINVAL, "internal: no grouped id kernel for lpr=%d", lpr);
 }
 
 template <int QT, int LPR, bool SW>
@@ -2206,8 +2601,10 @@ int id_common(const char* fn, int qtype, const void* Wv, size_t expert_stride_by
                                               top_k, n_tokens, Y, ldy, N, K, expert_scale, err_flag, pl.lpr, 0,
                                               pl.deep, st);
     }
-    // A leader gathers at most ID_MAX_LIST pairs, so a call is split into
-    // launches over whole tokens holding at most that many pairs each.
+    // A launch groups at most ID_MAX_LIST pairs (the grouped kernel's lists,
+    // the generic kernel's leader), so a call is split into launches over
+    // whole tokens holding at most that many pairs each.
+    static_assert(IDP_MAX_PAIRS == ID_MAX_LIST, "one pair limit per launch");
     const int tok_per_launch = ID_MAX_LIST / top_k;
     for (int t0 = 0; t0 < n_tokens; t0 += tok_per_launch) {
         const int nt = n_tokens - t0 < tok_per_launch ? n_tokens - t0 : tok_per_launch;
@@ -2215,11 +2612,20 @@ int id_common(const char* fn, int qtype, const void* Wv, size_t expert_stride_by
         const float* Xs = X + (size_t)t0 * ldx;
         const uint32_t* is = ids + p0;
         float* Ys = Y + p0 * ldy;
-        const int rc = qtype == QMV_Q4_0
-                           ? launch_id<QMV_Q4_0, SW>(W, expert_stride_bytes, ldw_bytes, n_experts, Xs, ldx, is, nt * top_k,
-                                                 top_k, Ys, ldy, N, K, expert_scale, err_flag, fast, st)
-                           : launch_id<QMV_Q8_0, SW>(W, expert_stride_bytes, ldw_bytes, n_experts, Xs, ldx, is, nt * top_k,
-                                                 top_k, Ys, ldy, N, K, expert_scale, err_flag, fast, st);
+        const bool grouped = fast && n_experts <= IDP_MAX_EXPERTS;
+        int rc;
+        if (grouped)
+            rc = qtype == QMV_Q4_0
+                     ? launch_idp<QMV_Q4_0, SW>(W, expert_stride_bytes, ldw_bytes, n_experts, Xs, ldx, is, nt * top_k,
+                                                top_k, Ys, ldy, N, K, expert_scale, err_flag, st)
+                     : launch_idp<QMV_Q8_0, SW>(W, expert_stride_bytes, ldw_bytes, n_experts, Xs, ldx, is, nt * top_k,
+                                                top_k, Ys, ldy, N, K, expert_scale, err_flag, st);
+        else
+            rc = qtype == QMV_Q4_0
+                     ? launch_id<QMV_Q4_0, SW>(W, expert_stride_bytes, ldw_bytes, n_experts, Xs, ldx, is, nt * top_k,
+                                               top_k, Ys, ldy, N, K, expert_scale, err_flag, fast, st)
+                     : launch_id<QMV_Q8_0, SW>(W, expert_stride_bytes, ldw_bytes, n_experts, Xs, ldx, is, nt * top_k,
+                                               top_k, Ys, ldy, N, K, expert_scale, err_flag, fast, st);
         if (rc) return rc;
     }
     return QMV_OK;

@@ -51,6 +51,24 @@ __device__ __forceinline__ float half_hi(uint32_t w) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
 }
 
+// (code - 8) / 16 for the low nibble of byte B of w, where w holds code
+// bytes XORed with 0x88 (v_cvt_off_f32_i4 reads bits [3:0] as a signed 4-bit
+// value and divides by 16; code ^ 8 read that way is code - 8). The byte is
+// selected with a shift and mask that the compiler folds into the
+// instruction's SDWA operand select, so no separate shift is issued.
+template <int B>
+__device__ __forceinline__ float nib(uint32_t w) {
+    if constexpr (B == 0) return __builtin_amdgcn_cvt_off_f32_i4((int)w);
+    else if constexpr (B == 3) return __builtin_amdgcn_cvt_off_f32_i4((int)(w >> 24));
+    else return __builtin_amdgcn_cvt_off_f32_i4((int)((w >> (8 * B)) & 0xFFu));
+}
+
+// w with each byte's high nibble moved into its low nibble, for nib<B>. A
+// rotation rather than a shift, so that the compiler cannot prove the other
+// bits of each byte zero and narrow nib's byte mask, which would stop it from
+// folding the byte select into the convert.
+__device__ __forceinline__ uint32_t hi_nibbles(uint32_t w) { return (w >> 4) | (w << 28); }
+
 // DW dwords from a 4-byte aligned address, with 16-byte vector loads.
 template <int DW>
 __device__ __forceinline__ void load_pair(const uint8_t* p, uint32_t* r) {
@@ -67,6 +85,32 @@ __device__ __forceinline__ void load_pair(const uint8_t* p, uint32_t* r) {
 #pragma unroll
         for (int i = DW & ~3; i < DW; ++i) r[i] = reinterpret_cast<const uint32_t*>(p)[i];
     }
+}
+
+// An empty volatile asm that reads and rewrites the N registers of b and
+// clobbers memory. Placed after the next step's loads are issued, it keeps
+// the decode of b below them: otherwise the compiler may hoist part of the
+// decode above the issue, and its wait for b's loads then holds back the
+// next loads, leaving one step in flight instead of two.
+template <int N>
+__device__ __forceinline__ void pin_regs(uint32_t* b) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(b[i])::"memory");
+}
+
+// Load instructions load_pair<DW> issues.
+template <int DW>
+constexpr int pair_loads() { return DW / 4 + DW % 4; }
+
+// s_waitcnt vmcnt(N): wait until at most N vector memory operations of this
+// wave are outstanding. Also tells the compiler's wait bookkeeping that the
+// older ones are done, which it cannot infer after loads and LDS stores made
+// conditional per lane (it would otherwise wait for them again later, at the
+// first reuse of their registers, behind loads issued since).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
 // 4 x 4 transpose across the four 16-lane rows of a wave: on entry lane row

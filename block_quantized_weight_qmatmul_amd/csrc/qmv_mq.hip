@@ -73,28 +73,10 @@ __device__ __forceinline__ uint32_t pack_bf16_exact(float a, float b) {
     return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, a), 0x07060302u);
 }
 
-// (code - 8) / 16 for the low nibble of byte B of w, where w holds code
-// bytes XORed with 0x88 (v_cvt_off_f32_i4 reads bits [3:0] as a signed
-// 4-bit value and divides by 16).
-template <int B>
-__device__ __forceinline__ float nib(uint32_t w) {
-    float r;
-    if constexpr (B == 0) {
-        r = __builtin_amdgcn_cvt_off_f32_i4((int)w);
-    } else if constexpr (B == 1) {
-        asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(r) : "v"(w));
-    } else if constexpr (B == 2) {
-        asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(r) : "v"(w));
-    } else {
-        asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(r) : "v"(w));
-    }
-    return r;
-}
-
 // Q4_0 slice: one qs dword -> 8 bf16 (code - 8) / 16, elements
 // 4G, 4G+1, 4G+2, 4G+3, 16+4G, 16+4G+1, 16+4G+2, 16+4G+3.
 __device__ __forceinline__ bf16x8_t dec_q4(uint32_t q) {
-    const uint32_t u = q ^ 0x88888888u, u4 = u >> 4;
+    const uint32_t u = q ^ 0x88888888u, u4 = hi_nibbles(u);
     const uint32_t p0 = pack_bf16_exact(nib<0>(u), nib<1>(u));
     const uint32_t p1 = pack_bf16_exact(nib<2>(u), nib<3>(u));
     const uint32_t p2 = pack_bf16_exact(nib<0>(u4), nib<1>(u4));

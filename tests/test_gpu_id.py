@@ -145,6 +145,44 @@ def test_out_of_range_id_gives_nan_row_and_sets_flag():
     assert flag == 0
 
 
+def test_out_of_range_ids_among_many_pairs():
+    """More pairs than the few-pairs kernel takes: the grouped kernel writes
+    NaN rows for ids out of range and serves the rest."""
+    E, N, K = 12, 72, 192
+    W = synth.make_weights("q4_0", E * N, K, cfg=83).reshape(E, N, -1)
+    T, k = 40, 2  # 80 pairs
+    X = synth.make_x(T, K, cfg=83)
+    ids = np.random.default_rng(83).integers(0, E, size=(T, k)).astype(np.uint32)
+    bad = [(3, 1), (17, 0), (39, 1)]
+    for t, s in bad:
+        ids[t, s] = E + 7 * t
+    y, flag, _ = run_id("q4_0", W, X, ids, N, K, err=True)
+    assert flag == 1
+    badrows = [t * k + s for t, s in bad]
+    assert np.all(np.isnan(y[badrows]))
+    keep = np.ones(T * k, bool)
+    keep[badrows] = False
+    ids_ok = ids.copy()
+    for t, s in bad:
+        ids_ok[t, s] = 0
+    yo, a = oracle.qmv_id("q4_0", W, X, ids_ok, N, K)
+    assert_within_tol(y[keep], yo[keep], a[keep], "valid rows")
+
+
+def test_more_experts_than_the_grouping_tables():
+    """1100 experts (beyond what the grouped kernel's LDS tables index): the
+    per-expert leader kernel serves the call."""
+    E, N, K = 1100, 24, 128
+    W = synth.make_weights("q8_0", E * N, K, cfg=84).reshape(E, N, -1)
+    T, k = 40, 3
+    X = synth.make_x(T, K, cfg=84)
+    ids = np.random.default_rng(84).integers(0, E, size=(T, k)).astype(np.uint32)
+    ids[5, 0] = ids[9, 2] = 1099
+    y, _, _ = run_id("q8_0", W, X, ids, N, K)
+    yo, a = oracle.qmv_id("q8_0", W, X, ids, N, K)
+    assert_within_tol(y, yo, a, "1100 experts")
+
+
 def test_many_pairs_split_across_launches_and_padded_ldy():
     E, N, K = 32, 48, 128
     W = synth.make_weights("q4_0", E * N, K, cfg=82).reshape(E, N, -1)
