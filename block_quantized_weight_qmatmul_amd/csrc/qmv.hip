@@ -400,18 +400,27 @@ __device__ __forceinline__ void m1_stream(const uint8_t* __restrict__ W, size_t 
     // Two register buffers take turns: the next step's loads go into one
     // while the other is decoded, with no copy between them.
     uint32_t bufA[RPT][DW], bufB[RPT][DW];
-    auto issue = [&](long tl, int i, uint32_t (&b)[RPT][DW]) {
+    // This lane's rows of the tile being loaded: recomputed when a step
+    // starts a tile (ldw < 2^32, so one 32 x 32 -> 64-bit multiply per row),
+    // not every step.
+    const uint8_t* irow[RPT];
+    auto set_row = [&](long tl) {
         const long row0 = tl * ROWS + lrow;
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            const uint32_t rr = (uint32_t)(row0 + r < N ? row0 + r : N - 1);
+            irow[r] = W + (uint64_t)rr * (uint32_t)ldw;
+        }
+    };
+    auto issue = [&](int i, uint32_t (&b)[RPT][DW]) {
         int p = j + i * LPR;
         p = p < P ? p : P - 1;
 #pragma unroll
-        for (int r = 0; r < RPT; ++r) {
-            const long rr = row0 + r < N ? row0 + r : N - 1;
-            load_pair<DW>(W + rr * ldw + (size_t)p * PB, b[r]);
-        }
+        for (int r = 0; r < RPT; ++r) load_pair<DW>(irow[r] + (uint32_t)(p * PB), b[r]);
     };
+    set_row(tile);
     if constexpr (SW) {
-        issue(tile, 0, bufA);
+        issue(0, bufA);
         stage_swiglu<WAVES * 64>(xs, 0, x, 0, 1, K);
         __syncthreads();
     } else {
@@ -420,7 +429,7 @@ __device__ __forceinline__ void m1_stream(const uint8_t* __restrict__ W, size_t 
         constexpr int XCH = (KMAX_STAGE / 4 + WAVES * 64 - 1) / (WAVES * 64);
         f32x4u_t xv[XCH];
         stage_x_load<WAVES * 64, XCH>(xv, x, K);
-        issue(tile, 0, bufA);
+        issue(0, bufA);
         stage_x_store<WAVES * 64, XCH>(xs, xv, K);
         wait_vmcnt<RPT * pair_loads<DW>()>();  // x loaded; only the weight loads remain
         lds_barrier();
@@ -460,8 +469,9 @@ __device__ __forceinline__ void m1_stream(const uint8_t* __restrict__ W, size_t 
         if (it2 == IPT) {
             it2 = 0;
             tile2 += tile_stride;
+            set_row(tile2);
         }
-        issue(tile2, it2, nb);
+        issue(it2, nb);
 #pragma unroll
         for (int r = 0; r < RPT; ++r) pin_regs<DW>(cb[r]);
         consume(cb);
@@ -596,18 +606,25 @@ __global__ __launch_bounds__(WAVES * 64) void k_m1c(const M1Cat<MAXP> C) {
     // Two register buffers take turns: the next step's loads go into one
     // while the other is decoded, with no copy between them.
     uint32_t bufA[DW], bufB[DW];
-    auto issue = [&](long tl, int i, uint32_t (&b)[DW]) {
+    // This lane's row of the tile being loaded: recomputed when a step starts
+    // a tile (ldw < 2^32, so one 32 x 32 -> 64-bit multiply), not every step.
+    const uint8_t* irow = nullptr;
+    auto set_row = [&](long tl) {
         const long row = (tl - it0) * ROWS + lrow;
-        const long rr = row < iN ? row : iN - 1;
+        const uint32_t rr = (uint32_t)(row < iN ? row : iN - 1);
+        irow = iW + (uint64_t)rr * (uint32_t)ildw;
+    };
+    auto issue = [&](int i, uint32_t (&b)[DW]) {
         int p = j + i * LPR;
         p = p < P ? p : P - 1;
-        load_pair<DW>(iW + rr * ildw + (size_t)p * PB, b);
+        load_pair<DW>(irow + (uint32_t)(p * PB), b);
     };
     {
         constexpr int XCH = (KMAX_STAGE / 4 + WAVES * 64 - 1) / (WAVES * 64);
         f32x4u_t xv[XCH];
         stage_x_load<WAVES * 64, XCH>(xv, C.x, K);
-        issue(tile, 0, bufA);
+        set_row(tile);
+        issue(0, bufA);
         stage_x_store<WAVES * 64, XCH>(xs, xv, K);
         wait_vmcnt<pair_loads<DW>()>();  // x loaded; only the weight loads remain
         lds_barrier();
@@ -648,7 +665,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_m1c(const M1Cat<MAXP> C) {
         // clamped, the data is never used), so that every step has the same
         // shape and the wait before each decode counts exactly the loads
         // issued after it.
-        issue(tile2, it2, nb);
+        if (it2 == 0) set_row(tile2);
+        issue(it2, nb);
         pin_regs<DW>(cb);
         consume(cb);
         if (it2 == 0) {  // the next step starts the tile just issued
@@ -2218,7 +2236,7 @@ int launch_m1(const uint8_t* W, size_t ldw, const float* X, float* Y, int N, int
 // Plan for the x-stationary kernel: lanes per row and K segments.
 bool m1b_eligible(const uint8_t* W, size_t ldw, const float* x, int K) {
     return K > 0 && K % 64 == 0 && K <= KMAX_FAST && ((uintptr_t)W & 3) == 0 && (ldw & 3) == 0 &&
-           ((uintptr_t)x & 3) == 0;
+           ldw <= 0xFFFFFFFFu && ((uintptr_t)x & 3) == 0;
 }
 
 // Launch the batched M = 1 kernel over n problems (n <= MAXB), all eligible.
@@ -2363,7 +2381,7 @@ int dense(int qtype, const void* Wv, size_t ldw, const float* X, size_t ldx, flo
     hipStream_t st = (hipStream_t)stream;
     const uint8_t* W = (const uint8_t*)Wv;
     const bool fast_ok = M == 1 && K > 0 && K % 64 == 0 && K <= KMAX_FAST && ((uintptr_t)W & 3) == 0 &&
-                         (ldw & 3) == 0 && ((uintptr_t)X & 3) == 0;
+                         (ldw & 3) == 0 && ldw <= 0xFFFFFFFFu && ((uintptr_t)X & 3) == 0;
     if (fast_ok) {
         return qtype == QMV_Q4_0 ? launch_m1<QMV_Q4_0>(W, ldw, X, Y, N, K, st)
                                  : launch_m1<QMV_Q8_0>(W, ldw, X, Y, N, K, st);
@@ -2584,6 +2602,7 @@ int id_common(const char* fn, int qtype, const void* Wv, size_t expert_stride_by
                             ldy, N, K, expert_scale, err_flag, qtype, st);
     // (K = 0 of any type: the generic kernel reads no weights and writes zeros)
     const int fast = K > 0 && K % 64 == 0 && K <= KMAX_FAST_ID && ((uintptr_t)W & 3) == 0 && (ldw_bytes & 3) == 0 &&
+                     ldw_bytes <= 0xFFFFFFFFu &&
                      (expert_stride_bytes & 3) == 0;
     // Up to 64 pairs (decode and short batches): stream all pairs' rows as
     // one matrix. Measured against the grouped kernel on the MoE calls
