@@ -91,6 +91,12 @@ def step_bytes():
     return sum(p.weight_bytes for p in synth.CONFIGS[1]["problems"])
 
 
+def group_bytes(g):
+    """Weight bytes of one launch group of the layer set."""
+    from block_quantized_weight_qmatmul_amd import synth
+    return sum(p.weight_bytes for p in synth.CONFIGS[1]["problems"] if p.name in g)
+
+
 def fused_layer_set_throughput(sets, args):
     """The layer-set step with Q/K/V stored as one [6144, 4096] matrix and
     gate/up as one [28672, 4096] matrix (a loader may concatenate weights that
@@ -176,6 +182,78 @@ def time_steps(fn, sets, steps, warmup):
     torch.cuda.synchronize()
     del full, part
     return e0.elapsed_time(e1) / 1e3
+
+
+def stream_read_reference(dev, steps=200):
+    """The streaming-read reference (qmv_stream_read: every byte once with
+    16-byte non-temporal loads) at the sizes of the layer set's four launches
+    and at 1 GiB, graph-timed over windows of a 1.25 GiB buffer (several
+    sweeps beyond the Infinity Cache). The sum of the four launches' times is
+    the floor of a step made of four dependent streaming launches."""
+    import torch
+
+    from block_quantized_weight_qmatmul_amd import qmv
+    total = 5 * 2**28
+    buf = torch.empty(total, dtype=torch.uint8, device=dev)
+    buf.fill_(0x5A)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    sizes = {}
+    for g in GROUPS:
+        sizes["+".join(g)] = group_bytes(g)
+    sizes["1GiB"] = 2**30
+    out = {"kernel": "k_stream_read (qmv_stream_read)", "buffer_bytes": total}
+    floor_t = 0.0
+    for name, nb in sizes.items():
+        n = max(1, min(64, total // nb))
+        wins = [buf[i * nb:(i + 1) * nb] for i in range(n)]
+        st = steps if nb < 2**29 else 20
+        t = time_steps(lambda w: qmv.stream_read(w, sink), wins, st, max(n, 8)) / st
+        out[name] = {"bytes": nb, "windows": n, "us_per_call": round(t * 1e6, 2), "GBps": round(nb / t / 1e9, 1),
+                     "pct_hbm_peak": round(100 * nb / t / 1e9 / HBM_PEAK_GBS, 2)}
+        if name != "1GiB":
+            floor_t += t
+    nbytes = step_bytes()
+    out["layer_set_floor"] = {"us_per_step": round(floor_t * 1e6, 2), "GBps": round(nbytes / floor_t / 1e9, 1),
+                              "pct_hbm_peak": round(100 * nbytes / floor_t / 1e9 / HBM_PEAK_GBS, 2)}
+    del buf
+    torch.cuda.empty_cache()
+    return out
+
+
+def cold_single(dev, sets, reps=5):
+    """Cold-single timing: before each launch a 1 GiB streaming read evicts
+    the caches, then one launch of each of the layer set's four groups is
+    timed alone between HIP events (launch overhead included; median of
+    reps). Reported for transparency next to the steady-state sweep."""
+    import statistics
+
+    import torch
+
+    from block_quantized_weight_qmatmul_amd import qmv
+    flush = torch.empty(2**30, dtype=torch.uint8, device=dev)
+    flush.fill_(0)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    s0 = sets[0]
+    out = {"flush_bytes": 2**30, "reps": reps, "stat": "median"}
+    tot = 0.0
+    for g in GROUPS:
+        nb = group_bytes(g)
+        ts = []
+        for _ in range(reps):
+            qmv.stream_read(flush, sink)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            qmv.qmv_batch("q4_0", [s0[n] for n in g])
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / 1e3)
+        t = statistics.median(ts)
+        tot += t
+        out["+".join(g)] = {"bytes": nb, "us": round(t * 1e6, 2), "GBps": round(nb / t / 1e9, 1)}
+    out["layer_set"] = {"us": round(tot * 1e6, 2), "GBps": round(step_bytes() / tot / 1e9, 1)}
+    del flush
+    torch.cuda.empty_cache()
+    return out
 
 
 def m16_throughput(dev, qtype="q4_0", steps=40, workspace=True):
@@ -467,37 +545,65 @@ def moe_affine4_throughput(dev, steps=48):
             "pct_hbm_peak": round(100 * nbytes / t / 1e9 / HBM_PEAK_GBS, 2)}
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (as lscpu prints it, read from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(target_s: float):
     """The CPU oracle (fp64, OpenMP over rows) timed on a bounded sample of
-    the layer set: the first rows of every projection, sized to take about
-    target_s seconds. Returns (GB/s of weight bytes, threads, description)."""
-    import numpy as np
+    the layer set: the first rows of every projection, one thread and all
+    the threads this process may use, each the median of 5 passes, the
+    sample sized so that all passes together take about target_s seconds.
+    Returns the JSON object of the cpu_baseline field."""
+    import statistics
 
     import oracle
     from block_quantized_weight_qmatmul_amd import synth
     probs = synth.CONFIGS[1]["problems"]
     full = {}
     for part, p in enumerate(probs):
-        rows = max(16, p.N // 16)
-        W = synth.make_weights("q4_0", rows, p.K, cfg=1, part=part)
+        W = synth.make_weights("q4_0", p.N, p.K, cfg=1, part=part)
         X = synth.make_x(1, p.K, cfg=1, part=part)
         full[p.name] = (W, X)
+    # all cores of the affinity mask, within the thread budget the
+    # environment sets for OpenMP (the host's share when it is shared)
+    ncpu = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    cores = min(ncpu, int(env)) if env.isdigit() and int(env) > 0 else ncpu
 
-    def run(frac):
+    def run(frac, threads):
         nbytes, t0 = 0, time.perf_counter()
         for p in probs:
             W, X = full[p.name]
             rows = max(1, int(W.shape[0] * frac))
-            oracle.qmv("q4_0", W[:rows], X)
+            oracle.qmv("q4_0", W[:rows], X, nthreads=threads)
             nbytes += rows * W.shape[1]
         return nbytes, time.perf_counter() - t0
-    nb, t = run(1 / 16)  # calibration
-    frac = min(1.0, (1 / 16) * target_s / max(t, 1e-3))
-    nb, t = run(frac)
-    rows_frac = frac / 16
-    desc = (f"first {rows_frac * 100:.2f}% of the rows of each of the 7 projections of the layer set "
-            f"({nb / 1e6:.1f} MB of Q4_0 weights), one pass")
-    return nb / t / 1e9, oracle.max_threads(), desc
+
+    def leg(threads, budget):
+        nb, t = run(1 / 64, threads)  # calibration
+        frac = min(1.0, (1 / 64) * budget / 5 / max(t, 1e-4))
+        res = [run(frac, threads) for _ in range(5)]
+        gbs = statistics.median(b / t / 1e9 for b, t in res)
+        return gbs, frac, res[0][0]
+
+    one, f1, b1 = leg(1, target_s * 0.5)
+    allc, fa, ba = leg(cores, target_s * 0.5)
+
+    def desc(frac, nb):
+        return (f"first {frac * 100:.2f}% of the rows of each of the 7 projections of the layer set "
+                f"({nb / 1e6:.1f} MB of Q4_0 weights), median of 5 passes")
+    return {"value": round(allc, 4), "unit": "GB/s", "cores": cores, "kind": "oracle", "sample": desc(fa, ba),
+            "one_thread": {"value": round(one, 4), "unit": "GB/s", "sample": desc(f1, b1)},
+            "cpu_model": cpu_model(), "affinity_cpus": ncpu}
 
 
 def read_traffic(launch_bytes):
@@ -919,6 +1025,14 @@ def main():
         del src, dst
 
     extra = {}
+    # the streaming-read reference and the cold-single timing (a few seconds)
+    ref = stream_read_reference(dev)
+    extra["stream_read"] = ref
+    floor = ref["layer_set_floor"]
+    roofline["reference"] = {"stream_read_1GiB_GBps": ref["1GiB"]["GBps"],
+                             "layer_set_floor_GBps": floor["GBps"],
+                             "frac_of_floor": round(value / floor["GBps"], 4)}
+    extra["cold_single"] = cold_single(dev, sets)
     if not args.no_extra:
         names = ("q", "k", "v", "o", "gate", "up", "down")
         t1 = time_steps(lambda s: qmv.qmv_batch("q4_0", [s[n] for n in names]), sets, args.steps, args.warmup)
@@ -949,8 +1063,7 @@ def main():
 
     cpu = None
     if args.cpu_seconds > 0:
-        gbs, cores, desc = cpu_baseline(args.cpu_seconds)
-        cpu = {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle", "sample": desc}
+        cpu = cpu_baseline(args.cpu_seconds)
 
     out = {
         "metric": METRIC,

@@ -2818,6 +2818,34 @@ int kq_dense(const char* name, const void* Wv, size_t ldw, const float* X, size_
     return launch_q6k<F>((const uint8_t*)Wv, ldw, X, ldx, Y, ldy, M, N, K, 0, 0, st);
 }
 
+// ---------------------------------------------------------------------------
+// Streaming-read reference for measurements: every 16-byte chunk of a buffer
+// read once with non-temporal loads (the pattern closest to HBM peak here),
+// eight per thread in flight, XOR-folded. A word is written to sink only if
+// a workgroup's fold equals a constant that the data never produces in
+// practice, so that the loads cannot be dropped; the write does not matter.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_stream_read(const u32x4* __restrict__ src, size_t n16, uint32_t* sink) {
+    constexpr int U = 8;
+    const size_t chunk = (size_t)256 * U;
+    const size_t nch = n16 / chunk;
+    uint32_t acc = 0;
+    for (size_t c = blockIdx.x; c < nch; c += gridDim.x) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(src + c * chunk + u * 256 + threadIdx.x);
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    // the tail (fewer than 256 * U chunks of 16 bytes) by workgroup 0
+    if (blockIdx.x == 0)
+        for (size_t i = nch * chunk + threadIdx.x; i < n16; i += 256) {
+            const u32x4 t = src[i];
+            acc ^= t.x ^ t.y ^ t.z ^ t.w;
+        }
+    if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -3187,6 +3215,19 @@ int qmv_batch(int qtype, const qmv_problem* problems, int n_problems, void* stre
 }
 
 const char* qmv_last_error(void) { return g_err; }
+
+int qmv_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+    if (bytes == 0) return QMV_OK;
+    if (!src || !sink) return fail(QMV_EINVAL, "qmv_stream_read: NULL src or sink");
+    if (((uintptr_t)src & 15) || (bytes & 15) || ((uintptr_t)sink & 3))
+        return fail(QMV_EALIGN, "qmv_stream_read: src and bytes must be 16-byte aligned, sink 4-byte aligned");
+    const size_t n16 = bytes / 16, chunks = n16 / 2048;
+    size_t grid = (size_t)num_cus() * 8;
+    grid = grid < chunks ? grid : (chunks ? chunks : 1);
+    hipLaunchKernelGGL(k_stream_read, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, (const u32x4*)src, n16,
+                       sink);
+    return check_launch("qmv_stream_read");
+}
 
 
 

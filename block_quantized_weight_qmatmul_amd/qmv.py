@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
         L.qmv_ws_bytes.argtypes = [I, I, I, I]
         L.qmv_last_error.restype = ctypes.c_char_p
         L.qmv_last_error.argtypes = []
+        L.qmv_stream_read.restype = I
+        L.qmv_stream_read.argtypes = [P, S, P, P]
         _lib = L
     return _lib
 
@@ -120,6 +122,16 @@ def raw_qmv_ws(qtype: int, W: int, ldw: int, X: int, ldx: int, Y: int, ldy: int,
 def raw_qmv_ws_static(qtype: int, W: int, ldw: int, X: int, ldx: int, Y: int, ldy: int, M: int, N: int, K: int,
                       stream: int = 0) -> int:
     return lib().qmv_ws_static(qtype, W, ldw, X, ldx, Y, ldy, M, N, K, stream)
+
+
+def raw_stream_read(src: int, nbytes: int, sink: int, stream: int = 0) -> int:
+    return lib().qmv_stream_read(src, nbytes, sink, stream)
+
+
+def stream_read(buf, sink, stream=None) -> None:
+    """Read every byte of the device tensor buf once (the streaming-read
+    reference of measurements); sink: a device int32 tensor of one element."""
+    _check(raw_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)))
 
 
 def ws_bytes(qtype, M: int, N: int, K: int) -> int:

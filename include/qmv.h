@@ -417,6 +417,20 @@ int qmv_batch(int qtype, const qmv_problem* problems, int n_problems, void* stre
 /* Message for the last non-zero status returned on the calling thread. */
 const char* qmv_last_error(void);
 
+/*
+ * qmv_stream_read — the memory-roofline reference for measurements, not part
+ * of the product: reads every byte of [src, src + bytes) once from device
+ * memory with 16-byte non-temporal loads and discards the data. A
+ * benchmark times it next to the qmv calls so that their bandwidth can be
+ * read against what a plain streaming read reaches on the same GPU.
+ *
+ *  src     device, 16-byte aligned; bytes a multiple of 16 (0: no-op).
+ *  sink    device, one uint32 the kernel may overwrite (4-byte aligned).
+ *  stream  hipStream_t, asynchronous. Errors as for the other calls
+ *          (QMV_EINVAL for NULL pointers, QMV_EALIGN for alignment).
+ */
+int qmv_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

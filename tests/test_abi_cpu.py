@@ -27,7 +27,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     names = declared_functions()
     assert {"qmv_q4_0", "qmv_q8_0", "qmv_q5_k", "qmv_q6_k", "qmv_gemm", "qmv_affine4", "qmv_affine4_id", "qmv_id", "qmv_id_swiglu", "qmv_moe_wsum", "qmv_moe_down",
-            "qmv_batch", "qmv_ws", "qmv_ws_bytes", "qmv_last_error"} <= set(names)
+            "qmv_batch", "qmv_ws", "qmv_ws_bytes", "qmv_last_error", "qmv_stream_read"} <= set(names)
     L = ctypes.CDLL(qmv.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -315,3 +315,19 @@ def _a4(**kw):
 def test_affine4_argument_checks(kw, status, msg):
     assert _a4(**kw) == status
     assert msg in qmv.last_error()
+
+
+@pytest.mark.parametrize("args,status,msg", [
+    ((0, 4096, 64), qmv.QMV_EINVAL, "NULL src"),
+    ((64, 4096, 0), qmv.QMV_EINVAL, "NULL src or sink"),
+    ((72, 4096, 64), qmv.QMV_EALIGN, "16-byte aligned"),
+    ((64, 4100, 64), qmv.QMV_EALIGN, "16-byte aligned"),
+    ((64, 4096, 66), qmv.QMV_EALIGN, "sink 4-byte aligned"),
+])
+def test_stream_read_argument_checks(args, status, msg):
+    assert qmv.raw_stream_read(*args) == status
+    assert msg in qmv.last_error()
+
+
+def test_stream_read_empty_is_a_no_op():
+    assert qmv.raw_stream_read(0, 0, 0) == qmv.QMV_OK
