@@ -37,6 +37,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+CLOCK_HZ = 2.4e9       # MI355X peak engine clock (counter rates are taken against it)
+# rocprofv3's derived metrics collected by the per-kernel profile, passed through
+DERIVED = ("VALUBusy", "VALUUtilization", "VmemLatency", "LdsLatency", "LDSBankConflict", "LdsUtil",
+           "MemUnitStalled", "OccupancyPercent", "MfmaUtil")
 WARMUP_S = 0.3  # minimum untimed warm-up per measurement, seconds
 METRIC = "effective weight GB/s and % of HBM peak, Q4_0 qmatmul at M=1 and M=16"
 KERNEL_SRCS = [os.path.join(ROOT, "block_quantized_weight_qmatmul_amd", "csrc", f)
@@ -770,11 +774,11 @@ def kernel_workloads(dev, reps=3):
         Ygu = torch.empty(Tn * g.top_k, g.N, device=dev)
         Ydn = torch.empty(Tn * g.top_k, dn.N, device=dev)
         o = torch.empty(Tn, dn.N, device=dev)
-        kid = "k_idv" if Tn == 1 else "k_id<"
+        kid = "k_idv" if Tn == 1 else "k_idp"  # few pairs: all rows as one matrix; many: grouped by expert
         out.append((f"moe_t{Tn}_gate_up_id", {kid: ne * g.N * (g.K // 32) * 18},
                     lambda dd=dd, g=g, Ygu=Ygu: qmv.qmv_id("q4_0", dd["W_gate_up"], dd["X_gate_up"], dd["ids"], Ygu,
                                                             g.N, g.K, expert_scale=dd["expert_scale"])))
-        out.append((f"moe_t{Tn}_down_id", {"k_id": ne * dn.N * (dn.K // 32) * 18},
+        out.append((f"moe_t{Tn}_down_id", {kid: ne * dn.N * (dn.K // 32) * 18},
                     lambda dd=dd, dn=dn, Ydn=Ydn: qmv.qmv_id("q4_0", dd["W_down"], dd["X_down"], dd["ids"].view(-1, 1),
                                                               Ydn, dn.N, dn.K, expert_scale=dd["expert_scale"])))
         if Tn == 1:
@@ -799,6 +803,12 @@ def kernel_workloads(dev, reps=3):
     y6e = torch.empty(8, 1408, device=dev)
     out.append(("q6_k_moe_gate_up_t1", {"k_id_q6": 8 * 1408 * synth.row_bytes("q6_k", 2816)},
                 lambda: qmv.qmv_id("q6_k", E6, x6e, ids6, y6e, 1408, 2816)))
+    # the streaming-read reference on 66 MB (the gate+up launch's bytes)
+    # (no fill: a fill kernel would read as a workload separator; the data
+    # does not matter to the read)
+    sbuf = torch.empty(66060288, dtype=torch.uint8, device=dev)
+    ssink = torch.empty(1, dtype=torch.int32, device=dev)
+    out.append(("stream_read_66MB", {"k_stream_read": 66060288}, lambda: qmv.stream_read(sbuf, ssink)))
     # the generic kernel (K % 64 != 0) and a prefill block set
     Wg, Xg, Yg = w("q4_0", 4096, 4064, 13), x(1, 4064, 13), torch.empty((1, 4096), device=dev)
     out.append(("generic_q4_0_4064x4096", {"k_generic": 4096 * 127 * 18}, lambda: qmv.qmv_q4_0(Wg, Xg, Yg, K=4064)))
@@ -876,11 +886,13 @@ def summarize_kernels(trace_dir, pmc_dirs, manifest_path, cmd_note):
     xcc = int(agents[0].get("Num_Xcc", 1)) if agents else 1
     ncu = int(agents[0].get("Cu_Count", 256)) if agents else 256
     cnt, cdisp = {}, {}
-    for d in pmc_dirs:
+    for pi, d in enumerate(pmc_dirs):
         for r in rows(d, "*counter_collection.csv"):
             key = (d, int(r["Dispatch_Id"]))
             cdisp[key] = r["Kernel_Name"]
             c, v = r["Counter_Name"], float(r["Counter_Value"])
+            if pi > 0 and c in ("GRBM_GUI_ACTIVE", "SQ_WAVE_CYCLES", "SQ_INSTS_VMEM_RD"):
+                c = f"{c}@{pi}"  # counters taken in several passes: each pass's own
             if c == "GRBM_GUI_ACTIVE":
                 v /= xcc
             cnt.setdefault(key, {})[c] = cnt.setdefault(key, {}).get(c, 0.0) + v
@@ -911,6 +923,11 @@ def summarize_kernels(trace_dir, pmc_dirs, manifest_path, cmd_note):
             durs = [tdur[i] for i, s in tseg.items() if s == wi and kk in tdisp[i]]
             pv = per.get((wi, kk), {})
             c = {k: sum(v) / reps for k, v in pv.items()}
+            # the vendor's derived metrics (rocprofv3 computes them per
+            # dispatch): averaged over the workload's dispatches
+            for k in DERIVED:
+                if k in pv:
+                    c[k] = sum(pv[k]) / len(pv[k])
             line = {"workload": wl["name"], "dispatches_per_call": round(len(durs) / reps, 2),
                     "us_per_call": round(sum(durs) / reps, 2) if durs else None, "alg_bytes": alg}
             if durs:
@@ -923,18 +940,37 @@ def summarize_kernels(trace_dir, pmc_dirs, manifest_path, cmd_note):
             if "TCC_HIT" in c and "TCC_MISS" in c and c["TCC_HIT"] + c["TCC_MISS"] > 0:
                 line["l2_hit_pct"] = round(100 * c["TCC_HIT"] / (c["TCC_HIT"] + c["TCC_MISS"]), 1)
             g = c.get("GRBM_GUI_ACTIVE")
-            if g and "SQ_ACTIVE_INST_VALU" in c:
-                line["valu_busy_pct"] = round(100 * c["SQ_ACTIVE_INST_VALU"] / ncu / g, 1)
+            # cycles of the kernel's time at the nominal 2.4 GHz clock, on
+            # every SIMD (4 per CU) or CU of the chip
+            cyc = sum(durs) / reps * 1e-6 * CLOCK_HZ if durs else None
+            if cyc and "SQ_INSTS_VALU" in c:
+                # a wave64 VALU instruction occupies a 16-lane SIMD for 4 cycles
+                line["valu_busy_pct"] = round(100 * 4 * c["SQ_INSTS_VALU"] / (4 * ncu * cyc), 1)
             if g and "SQ_WAVE_CYCLES" in c:
                 line["occupancy_pct"] = round(400 * c["SQ_WAVE_CYCLES"] / g / ncu / 32, 1)
+            if "SQ_INST_LEVEL_VMEM" in c and c.get("SQ_INSTS_VMEM_RD@2"):
+                # Little's law: vector memory instructions in flight summed per
+                # cycle over completed ones = mean latency in cycles
+                line["vmem_latency_cycles"] = round(c["SQ_INST_LEVEL_VMEM"] / c["SQ_INSTS_VMEM_RD@2"])
+            if "SQ_LDS_BANK_CONFLICT" in c and c.get("SQ_ACTIVE_INST_LDS"):
+                line["lds_bank_conflict_pct"] = round(100 * c["SQ_LDS_BANK_CONFLICT"] / c["SQ_ACTIVE_INST_LDS"], 1)
+            if cyc and "SQ_ACTIVE_INST_LDS" in c:
+                line["lds_active_pct"] = round(100 * c["SQ_ACTIVE_INST_LDS"] / (ncu * cyc), 1)
+            if "SQ_WAIT_INST_LDS" in c and c.get("SQ_WAVE_CYCLES@2"):
+                line["wave_wait_lds_pct"] = round(100 * c["SQ_WAIT_INST_LDS"] / c["SQ_WAVE_CYCLES@2"], 1)
+            if cyc and "TA_BUSY" in c:
+                line["ta_busy_pct"] = round(100 * c["TA_BUSY"] / (ncu * cyc), 1)
+            for k in DERIVED:
+                if k in c:
+                    line[k] = round(c[k], 2)
             if "SQ_INSTS_VALU" in c and "SQ_WAVES" in c:
                 line["valu_insts_per_wave"] = round(c["SQ_INSTS_VALU"] / max(1, c["SQ_WAVES"]))
                 wts = alg / (0.5625 if "q4_0" in wl["name"] else 34 / 32 if "q8_0" in wl["name"] else 1)
                 line["valu_lane_insts_per_weight"] = round(c["SQ_INSTS_VALU"] * 64 / wts, 2)
-            if g and "SQ_VALU_MFMA_BUSY_CYCLES" in c:
-                line["mfma_util_pct"] = round(100 * c["SQ_VALU_MFMA_BUSY_CYCLES"] / (g * ncu * 4), 1)
-            if g and "TCP_TCP_TA_DATA_STALL_CYCLES" in c:
-                line["ta_data_stall_pct"] = round(100 * c["TCP_TCP_TA_DATA_STALL_CYCLES"] / g / ncu, 1)
+            if cyc and "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+                line["mfma_util_pct"] = round(100 * c["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * ncu * 4), 1)
+            if cyc and "TCP_TCP_TA_DATA_STALL_CYCLES" in c:
+                line["ta_data_stall_pct"] = round(100 * c["TCP_TCP_TA_DATA_STALL_CYCLES"] / cyc / ncu, 1)
             if g and "SQ_WAIT_INST_ANY" in c and "SQ_WAVE_CYCLES" in c and c["SQ_WAVE_CYCLES"] > 0:
                 line["wave_wait_inst_pct"] = round(100 * c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"], 1)
             by_kernel.setdefault(kk.strip("<"), []).append(line)
@@ -943,8 +979,13 @@ def summarize_kernels(trace_dir, pmc_dirs, manifest_path, cmd_note):
                 f"# command: {cmd_note}",
                 f"# traffic = FETCH_SIZE / WRITE_SIZE x the scale that makes a 256 MiB copy read 256 MiB "
                 f"(fetch scale {f_scale and round(f_scale, 4)}, write scale {w_scale and round(w_scale, 4)}); "
-                "valu_busy = SQ_ACTIVE_INST_VALU / CUs / GRBM_GUI_ACTIVE; occupancy = SQ_WAVE_CYCLES share of "
-                "32 wave slots per CU; VALU lane instructions per weight = SQ_INSTS_VALU x 64 / weights"]
+                "valu_busy = 4 cycles x SQ_INSTS_VALU / (SIMDs x kernel cycles at 2.4 GHz); occupancy = "
+                "SQ_WAVE_CYCLES share of 32 wave slots per CU; VALU lane instructions per weight = SQ_INSTS_VALU "
+                "x 64 / weights; vmem_latency = SQ_INST_LEVEL_VMEM / SQ_INSTS_VMEM_RD (cycles); lds_active = "
+                "SQ_ACTIVE_INST_LDS / (CUs x kernel cycles); lds_bank_conflict = SQ_LDS_BANK_CONFLICT / "
+                "SQ_ACTIVE_INST_LDS; wave_wait_lds = SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES; ta_busy = TA_BUSY / (CUs x "
+                "kernel cycles); mfma_util = SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x kernel cycles); wave_wait_inst = "
+                "SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (two passes)"]
         text += [json.dumps(ln) for ln in lines]
         with open(os.path.join(ROOT, "profiles", f"counters_{k}.txt"), "w") as f:
             f.write("\n".join(text) + "\n")
