@@ -2957,6 +2957,10 @@ int qmv_q6_k(const void* Wv, size_t ldw, const float* X, size_t ldx, float* Y, s
     return kq_dense<FmtQ6K>("qmv_q6_k", Wv, ldw, X, ldx, Y, ldy, M, N, K, stream);
 }
 
+// Activation rows from which qmv_gemm takes the tiled kernel (its tiles are
+// 128 rows; below this the 16-row blocks of k_mq waste less).
+constexpr int GEMM_MIN_M = 64;
+
 int qmv_gemm(int qtype, const void* Wv, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N,
              int K, void* stream) {
     const char* name = "qmv_gemm";
@@ -2985,10 +2989,15 @@ int qmv_gemm(int qtype, const void* Wv, size_t ldw, const float* X, size_t ldx, 
     const size_t ybytes = ((size_t)(M - 1) * ldy + N) * 4;
     if (overlaps(Y, ybytes, Wv, wbytes) || overlaps(Y, ybytes, X, xbytes))
         return fail(QMV_EINVAL, "%s: Y overlaps W or X", name);
-    // Q4_0 and Q8_0: every block of 16 rows in one matrix-core launch (blocks
-    // that read the same weights run side by side and share them through L2).
-    if ((qtype == QMV_Q4_0 || qtype == QMV_Q8_0) && M > QMV_MAX_M && K > 0 && K % 64 == 0 &&
-        ((uintptr_t)Wv & 3) == 0 && (ldw & 3) == 0)
+    // Q4_0 and Q8_0 with at least GEMM_MIN_M rows and 16-byte aligned rows of
+    // X: tiles of 128 x 128 outputs, each weight decoded once per 128 rows.
+    // Otherwise every block of 16 rows in one matrix-core launch (blocks that
+    // read the same weights run side by side and share them through L2).
+    const bool q = (qtype == QMV_Q4_0 || qtype == QMV_Q8_0) && K > 0 && K % 64 == 0 && ((uintptr_t)Wv & 3) == 0 &&
+                   (ldw & 3) == 0;
+    if (q && M >= GEMM_MIN_M && ldw <= 0xFFFFFFFFu && ((uintptr_t)X & 15) == 0 && (ldx & 3) == 0)
+        return launch_gemm(qtype, (const uint8_t*)Wv, ldw, X, ldx, Y, ldy, M, N, K, (hipStream_t)stream);
+    if (q && M > QMV_MAX_M)
         return launch_mq(qtype, (const uint8_t*)Wv, ldw, X, ldx, Y, ldy, M, N, K, nullptr, 0, 0, 0, 0,
                          (hipStream_t)stream);
     // Blocks of up to 16 activation rows, each through the dense call of its

@@ -36,6 +36,12 @@ QMV_HIDDEN int launch_mq(int qtype, const uint8_t* W, size_t ldw, const float* X
 // Workspace bytes launch_mq would use for M, N, K given unlimited room (0 if
 // it would not split K).
 QMV_HIDDEN size_t mq_ws_bytes(int M, int N, int K);
+// Tiled matrix-core product for many activation rows (qmv_mq.hip): tiles of
+// 128 x 128 outputs, each weight decoded once per tile. Requirements, checked
+// by the caller: qtype Q4_0 or Q8_0, K > 0 and K % 64 == 0, W and ldw 4-byte
+// aligned, ldw < 2^32, X 16-byte aligned, ldx % 4 == 0, Y 4-byte aligned.
+QMV_HIDDEN int launch_gemm(int qtype, const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy,
+                           int M, int N, int K, hipStream_t st);
 
 // ---------------------------------------------------------------------------
 // Device helpers

@@ -145,6 +145,27 @@ __device__ __forceinline__ void split_bf16(const float (&v)[8], uint32_t (&hw)[4
     }
 }
 
+// Eight activations -> A operand record with hi = x truncated to bf16 (never
+// rounds up, so every finite x has a finite hi) and lo = bf16(x - hi) of the
+// exact difference. Infinities and NaNs, the only inputs whose difference is
+// a NaN, take split_bf16's per-element rules instead; that test is one wave
+// ballot per pair, combined in scalar registers.
+__device__ __forceinline__ void split_bf16_trunc(const float (&v)[8], uint32_t (&hw)[4], uint32_t (&lw)[4]) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    uint64_t bad = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t a = __builtin_bit_cast(uint32_t, v[2 * k]), b = __builtin_bit_cast(uint32_t, v[2 * k + 1]);
+        const float r0 = v[2 * k] - __builtin_bit_cast(float, a & 0xFFFF0000u);
+        const float r1 = v[2 * k + 1] - __builtin_bit_cast(float, b & 0xFFFF0000u);
+        bad |= __builtin_amdgcn_ballot_w64(__builtin_isunordered(r0, r1));
+        hw[k] = __builtin_amdgcn_perm(b, a, 0x07060302u);
+        const bf16x2 l = {(__bf16)r0, (__bf16)r1};
+        lw[k] = __builtin_bit_cast(uint32_t, l);
+    }
+    if (__builtin_expect(bad != 0, 0)) split_bf16(v, hw, lw);
+}
+
 // ---------------------------------------------------------------------------
 // The kernel. grid.x = (tile groups) * mblocks, the 16-row block of X / Y
 // fastest, so the workgroups that read one weight tile run side by side.
@@ -456,9 +477,284 @@ int launch_mq_q(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float*
     return fail(QMV_EINVAL, "internal: no matrix-core kernel for waves=%d ks=%d", p.waves, p.ks);
 }
 
+// ---------------------------------------------------------------------------
+// Prefill: many activation rows. A workgroup of four waves owns a tile of 64
+// activation rows x 256 weight rows and walks K in rounds of one block pair
+// (64 columns). Wave w multiplies all four 16-row activation blocks of the
+// tile by its own four 16-row weight blocks (rows 64w .. 64w+63 of the tile):
+// 4 x 4 MFMA tiles, the block scale applied per block in fp32 as in k_mq.
+//   Weights go from global memory to registers and never through LDS: lane
+// (G, j) of wave w loads the round's pair of tile row 64w + 16G + j, which
+// holds all four k slices of that row; a 4 x 4 transpose across the wave's
+// lane rows (xpose4) turns that into slice G of rows 16c + j, c = 0..3, the B
+// operands of the wave's four weight blocks, decoded in registers. Each weight
+// is decoded once per 64 activation rows.
+//   Activations are shared by the four waves through LDS: each round the
+// workgroup converts the 64 x 64 activations of the round after next into
+// bf16 hi/lo A operands (two records per thread) in one of four LDS buffers,
+// with one barrier per two rounds. Loads run two rounds ahead (weights) and
+// four rounds ahead (activations) of their use, in two register sets each,
+// past the end clamped to the last round (not used).
+//   Tiles are numbered with the activation block fastest and each XCD
+// (workgroups b with the same b % 8) takes a contiguous share of them: the
+// workgroups of one XCD run one range of weight rows against all activation
+// blocks side by side, so each weight tile comes into that XCD's L2 once and
+// the activations (a few MB) are re-read from L2, not from memory.
+//   The products take about 350 vector instructions per wave and round
+// against 64 MFMAs, and the two share the SIMD's issue port (an MFMA issues in
+// 4 cycles, then runs 16 in the matrix pipe); the scaling FMAs are
+// interleaved with the MFMAs, and the block scales are converted to fp32 once
+// per round (FMAs that read them as halves issue at a lower rate).
+// Requirements (checked by the caller): K % 64 == 0, K > 0, W and ldw 4-byte
+// aligned, ldw < 2^32, X 16-byte aligned and ldx % 4 == 0.
+// ---------------------------------------------------------------------------
+constexpr int GM_MBK = 4;                                  // 16-row activation blocks per tile
+constexpr int GM_BM = 16 * GM_MBK, GM_BN = 256, GM_NT = 256;
+constexpr int GM_REC = GM_MBK * 2 * 64 / GM_NT;            // A records per thread per round
+constexpr int GM_BUF = GM_MBK * 2 * 2 * 1024;              // one round: [m block][block][hi, lo][lane] x 16 B
+constexpr int GM_LDS = 4 * GM_BUF;
+
+// WPE: waves per SIMD the register budget is cut for.
+template <int QT, int WPE>
+__global__ __launch_bounds__(GM_NT) __attribute__((amdgpu_waves_per_eu(WPE))) void k_gemm(
+    const uint8_t* __restrict__ W, size_t ldw, const float* __restrict__ X, size_t ldx, float* __restrict__ Y,
+    size_t ldy, int M, int N, int K, int tiles_n, int tiles, int per_xcd) {
+    using F = MqFmt<QT>;
+    constexpr int DW = F::DW, PB = 4 * DW;
+    extern __shared__ __align__(16) uint8_t smem[];
+
+    const int t = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+    if (t >= tiles) return;  // uniform over the workgroup
+    const int tiles_m = tiles / tiles_n;
+    const int m0 = (t % tiles_m) * GM_BM, n0 = (t / tiles_m) * GM_BN;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int G = lane >> 4, j = lane & 15;
+    const int R = K >> 6;  // rounds (block pairs)
+
+    // ---- weights: this lane's row of the tile (past N: the last row, not stored)
+    const int wn = n0 + tid < N ? n0 + tid : N - 1;
+    const uint8_t* __restrict__ wrow = W + (uint64_t)(uint32_t)wn * (uint32_t)ldw;
+    auto fetch_w = [&](int r, uint32_t (&b)[DW]) __attribute__((always_inline)) {
+        load_pair<DW>(wrow + (size_t)(r < R ? r : R - 1) * PB, b);
+    };
+    // ---- activations: record q = tid + 256 i is lane (G, j) = q % 64, block
+    // (q / 64) % 2 and activation block q / 128 of the round. Rows past M are
+    // read from row M - 1: a product row depends on its own activation row
+    // only, and those rows are not stored.
+    const float* xrec[GM_REC];
+#pragma unroll
+    for (int i = 0; i < GM_REC; ++i) {
+        const int q = tid + GM_NT * i;
+        const int rl = q & 63, rb = (q >> 6) & 1, mbk = q >> 7;
+        const int m = m0 + mbk * 16 + (rl & 15);
+        xrec[i] = X + (size_t)(m < M ? m : M - 1) * ldx + 32 * rb + F::xoff(rl >> 4, 0);
+    }
+    constexpr int XD = F::xoff(0, 1) - F::xoff(0, 0);  // second 4-float run of a record
+    auto fetch_x = [&](int r, f32x4_t (&xr)[GM_REC][2]) __attribute__((always_inline)) {
+        const int rr = r < R ? r : R - 1;
+#pragma unroll
+        for (int i = 0; i < GM_REC; ++i) {
+            const float* p = xrec[i] + 64 * rr;
+            xr[i][0] = *reinterpret_cast<const f32x4_t*>(p);
+            xr[i][1] = *reinterpret_cast<const f32x4_t*>(p + XD);
+        }
+    };
+    auto put_x = [&](int buf, const f32x4_t (&xr)[GM_REC][2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < GM_REC; ++i) {
+            const int q = tid + GM_NT * i;
+            const float v[8] = {xr[i][0][0], xr[i][0][1], xr[i][0][2], xr[i][0][3],
+                                xr[i][1][0], xr[i][1][1], xr[i][1][2], xr[i][1][3]};
+            uint32_t hw[4], lw[4];
+            split_bf16_trunc(v, hw, lw);
+            const u32x4 hi = (u32x4){hw[0], hw[1], hw[2], hw[3]};
+            const u32x4 lo = (u32x4){lw[0], lw[1], lw[2], lw[3]};
+            uint8_t* rec = smem + buf * GM_BUF + (((q >> 6) * 2) * 64 + (q & 63)) * 16;
+            *reinterpret_cast<u32x4*>(rec) = hi;
+            *reinterpret_cast<u32x4*>(rec + 1024) = lo;
+        }
+    };
+
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[a][c] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    // ---- one round: the pair in b (this lane's row) times the A operands in LDS buffer buf
+    auto compute = [&](int buf, const uint32_t (&b)[DW]) __attribute__((always_inline)) {
+        // both block scales of a row in one dword; dd[c] = those of row 16c + j
+        uint32_t dd[4];
+        const uint32_t dpk = (b[0] & 0xFFFFu) | (b[QT == QMV_Q4_0 ? 4 : 8] & 0xFFFF0000u);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dd[c] = dpk;
+        xpose4(dd);
+        // v0[c] / v1[c]: code dword(s) of slice G of block 0 / 1 of row 16c + j
+        uint32_t v0[4], v1[4], w0[4], w1[4];
+        if constexpr (QT == QMV_Q4_0) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                v0[u] = __builtin_amdgcn_alignbyte(b[u + 1], b[u], 2);
+                v1[u] = b[5 + u];
+            }
+            xpose4(v0);
+            xpose4(v1);
+        } else {
+            // block 0 codes at bytes 2..33 (dwords 0..8, shifted by 2), block 1 at 36..67 (dwords 9..16)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                v0[u] = __builtin_amdgcn_alignbyte(b[2 * u + 1], b[2 * u], 2);
+                w0[u] = __builtin_amdgcn_alignbyte(b[2 * u + 2], b[2 * u + 1], 2);
+                v1[u] = b[9 + 2 * u];
+                w1[u] = b[10 + 2 * u];
+            }
+            xpose4(v0);
+            xpose4(w0);
+            xpose4(v1);
+            xpose4(w1);
+        }
+        const uint8_t* xa = smem + buf * GM_BUF + lane * 16;
+        // eight steps s = (block, activation block) = (s / 4, s % 4): step s
+        // reads the A operands of step s + 1, issues its eight MFMAs (four
+        // independent hi-then-lo chains) and scales the products of step s - 1
+        // into the accumulators; scheduling barriers keep the steps in this
+        // order, so that at most two steps' products are live
+        bf16x8_t bq[4], ah[2], al[2];
+        f32x4_t cc[2][4];
+        auto read_a = [&](int s) __attribute__((always_inline)) {
+            const uint8_t* ra = xa + (((s & 3) * 2 + (s >> 2)) * 2) * 1024;
+            ah[s & 1] = *reinterpret_cast<const bf16x8_t*>(ra);
+            al[s & 1] = *reinterpret_cast<const bf16x8_t*>(ra + 1024);
+        };
+        auto decode = [&](int blk) __attribute__((always_inline)) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                if constexpr (QT == QMV_Q4_0)
+                    bq[c] = dec_q4(blk ? v1[c] : v0[c]);
+                else
+                    bq[c] = blk ? dec_q8(v1[c], w1[c]) : dec_q8(v0[c], w0[c]);
+            }
+        };
+        // the block scales as fp32 once per round (the mixed-precision FMA
+        // that would read them as halves issues at a lower rate)
+        float scf[2][4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            scf[0][c] = half_lo(dd[c]);
+            scf[1][c] = half_hi(dd[c]);
+            asm volatile("" : "+v"(scf[0][c]), "+v"(scf[1][c]));
+        }
+        auto scale = [&](int s) __attribute__((always_inline)) {
+            const int a = s & 3, blk = s >> 2;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const float sc = scf[blk][c];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[a][c][i] = fmaf(sc, cc[s & 1][c][i], acc[a][c][i]);
+            }
+        };
+        decode(0);
+        read_a(0);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            if (s == 4) {
+                // the second block's codes are decoded here, not hoisted above
+                pin_regs<4>(v1);
+                if constexpr (QT == QMV_Q8_0) pin_regs<4>(w1);
+                decode(1);
+            }
+            if (s + 1 < 8) read_a(s + 1);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                cc[s & 1][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[s & 1], bq[c], (f32x4_t){0.f, 0.f, 0.f, 0.f},
+                                                                        0, 0, 0);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                cc[s & 1][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[s & 1], bq[c], cc[s & 1][c], 0, 0, 0);
+            if (s > 0) {
+                scale(s - 1);
+                // the scaling happens here, not sunk below later steps
+#pragma unroll
+                for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(acc[(s - 1) & 3][c])::"memory");
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        scale(7);
+    };
+
+    // ---- pipeline over four LDS buffers: round r's A operands are put into
+    // buffer r % 4 two rounds before its products, from activations loaded
+    // two rounds before that (register set r % 2); round r's weights are
+    // loaded two rounds ahead (set r % 2). A barrier after every second round
+    // orders each buffer's writes before its reads and its reads before it is
+    // written again. In each round the activation loads go out before the
+    // weight loads, so that waiting for the oldest activations never waits
+    // for weights issued with them.
+    uint32_t wA[DW], wB[DW];
+    f32x4_t xA[GM_REC][2], xB[GM_REC][2];
+    // (the loads outstanding when the loop is entered are those of two
+    // earlier rounds in the loop's own order, so the compiler's wait counts
+    // at the top of the loop hold for its first iteration too)
+    fetch_x(0, xA);
+    fetch_x(1, xB);
+    put_x(0, xA);
+    put_x(1, xB);
+    fetch_x(2, xA);
+    fetch_w(0, wA);
+    fetch_x(3, xB);
+    fetch_w(1, wB);
+    lds_barrier();
+    auto body = [&](int r, uint32_t (&w)[DW], f32x4_t (&xs)[GM_REC][2], bool sync) __attribute__((always_inline)) {
+        compute(r & 3, w);
+        put_x((r + 2) & 3, xs);
+        fetch_x(r + 4, xs);
+        fetch_w(r + 2, w);
+        if (sync) lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    int r = 0;
+    for (; r + 2 <= R; r += 2) {
+        body(r, wA, xA, false);
+        body(r + 1, wB, xB, true);
+    }
+    if (r < R) body(r, wA, xA, false);
+
+    // ---- write the 16 x 16 tiles: lane (G, j) holds rows 4G .. 4G+3 of column j
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int n = n0 + 64 * wave + 16 * c + j;
+        if (n >= N) continue;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = m0 + a * 16 + 4 * G + i;
+                if (m < M) Y[(size_t)m * ldy + n] = acc[a][c][i] * F::OUT_SCALE;
+            }
+        }
+    }
+}
+
+template <int QT, int WPE = 2>
+int launch_gemm_q(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N,
+                  int K, hipStream_t st) {
+    const long tiles_m = ((long)M + GM_BM - 1) / GM_BM, tiles_n = ((long)N + GM_BN - 1) / GM_BN;
+    const long tiles = tiles_m * tiles_n;
+    if (tiles > 0x3FFFFFFF) return fail(QMV_EINVAL, "qmv_gemm: M x N too large");
+    const long per_xcd = (tiles + 7) / 8;
+    hipLaunchKernelGGL((k_gemm<QT, WPE>), dim3((unsigned)(8 * per_xcd)), dim3(GM_NT), GM_LDS, st, W, ldw, X, ldx, Y,
+                       ldy, M, N, K, (int)tiles_n, (int)tiles, (int)per_xcd);
+    return check_launch("qmv_gemm tiled kernel");
+}
+
 }  // namespace
 
 size_t mq_ws_bytes(int M, int N, int K) { return M >= 2 && N > 0 && K > 0 ? plan_mq(M, N, K, SIZE_MAX).ws_bytes : 0; }
+
+int launch_gemm(int qtype, const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M,
+                int N, int K, hipStream_t st) {
+    return qtype == QMV_Q4_0 ? launch_gemm_q<QMV_Q4_0>(W, ldw, X, ldx, Y, ldy, M, N, K, st)
+                             : launch_gemm_q<QMV_Q8_0>(W, ldw, X, ldx, Y, ldy, M, N, K, st);
+}
 
 int launch_mq(int qtype, const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N,
               int K, void* ws, size_t ws_bytes, int waves, int ks, int S, hipStream_t st) {

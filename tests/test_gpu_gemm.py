@@ -26,7 +26,7 @@ def run(qtype, W, X, N, ldy=None):
 
 
 @pytest.mark.parametrize("qtype,M,N,K", [("q4_0", 17, 300, 1088), ("q4_0", 33, 129, 4096), ("q4_0", 100, 64, 512),
-                                         ("q4_0", 131, 1000, 2112),
+                                         ("q4_0", 131, 1000, 2112), ("q4_0", 64, 128, 64), ("q8_0", 150, 260, 1088),
                                          ("q8_0", 40, 200, 1024), ("q6_k", 20, 150, 2816), ("q5_k", 21, 150, 2816),
                                          ("q4_0", 5, 77, 96)])
 def test_gemm_against_oracle(qtype, M, N, K):
@@ -63,3 +63,24 @@ def test_gemm_row_blocks_agree_with_the_16_row_call_and_repeat_bitwise():
     yo, a = oracle.qmv("q4_0", W, X[16:32])
     assert_within_tol(y[16:32], yo, a, "rows 16..31 of the 40-row call")
     assert_within_tol(Y16.cpu().numpy(), yo, a, "16-row call")
+
+
+@pytest.mark.parametrize("qtype", ["q4_0", "q8_0"])
+def test_tiled_gemm_repeat_bitwise_and_unaligned_rows_fall_back(qtype):
+    """The tiled kernel (>= 64 rows, 16-byte aligned X rows) repeats bitwise;
+    the same product with X rows 4-byte aligned only (ldx = K + 1) goes
+    through the 16-row blocks and also meets the oracle."""
+    M, N, K = 200, 300, 1536
+    W = synth.make_weights(qtype, N, K, cfg=93)
+    X = synth.make_x(M, K, cfg=93)
+    y1, _ = run(qtype, W, X, N)
+    y2, _ = run(qtype, W, X, N)
+    assert np.array_equal(y1, y2)
+    yo, a = oracle.qmv(qtype, W, X)
+    assert_within_tol(y1, yo, a, "tiled")
+    Xp = torch.zeros((M, K + 1), dtype=torch.float32, device=DEV)
+    Xp[:, :K] = torch.from_numpy(X).to(DEV)
+    Y = torch.full((M, N), np.nan, dtype=torch.float32, device=DEV)
+    qmv.qmv_gemm(qtype, torch.from_numpy(W).to(DEV), Xp[:, :K], Y)
+    torch.cuda.synchronize()
+    assert_within_tol(Y.cpu().numpy(), yo, a, "unaligned rows")
