@@ -813,8 +813,8 @@ def kernel_workloads(dev, reps=3):
     Wg, Xg, Yg = w("q4_0", 4096, 4064, 13), x(1, 4064, 13), torch.empty((1, 4096), device=dev)
     out.append(("generic_q4_0_4064x4096", {"k_generic": 4096 * 127 * 18}, lambda: qmv.qmv_q4_0(Wg, Xg, Yg, K=4064)))
     Wp, Xp, Yp = w("q4_0", 14336, 4096, 14), x(512, 4096, 14), torch.empty((512, 14336), device=dev)
-    # prefill: weights once + X + Y (its 32 row blocks re-read the weights, partly from L2)
-    out.append(("prefill_q4_0_m512_4096x14336", {"k_mq<": 14336 * 128 * 18 + 512 * 4096 * 4 + 512 * 14336 * 4},
+    # prefill (the tiled kernel): weights once + X + Y
+    out.append(("prefill_q4_0_m512_4096x14336", {"k_gemm": 14336 * 128 * 18 + 512 * 4096 * 4 + 512 * 14336 * 4},
                 lambda: qmv.qmv_gemm("q4_0", Wp, Xp, Yp)))
     return out
 

@@ -2990,7 +2990,7 @@ int qmv_gemm(int qtype, const void* Wv, size_t ldw, const float* X, size_t ldx, 
     if (overlaps(Y, ybytes, Wv, wbytes) || overlaps(Y, ybytes, X, xbytes))
         return fail(QMV_EINVAL, "%s: Y overlaps W or X", name);
     // Q4_0 and Q8_0 with at least GEMM_MIN_M rows and 16-byte aligned rows of
-    // X: tiles of 128 x 128 outputs, each weight decoded once per 128 rows.
+    // X: tiles of 64 x 256 outputs, each weight decoded once per 64 rows.
     // Otherwise every block of 16 rows in one matrix-core launch (blocks that
     // read the same weights run side by side and share them through L2).
     const bool q = (qtype == QMV_Q4_0 || qtype == QMV_Q8_0) && K > 0 && K % 64 == 0 && ((uintptr_t)Wv & 3) == 0 &&

@@ -218,15 +218,19 @@ int qmv_q5_k(const void* W, size_t ldw_bytes, const float* X, size_t ldx, float*
  * quantized weight pre-dequantized to F16 after load, so that
  * `dispatch_qmatmul` takes an F16-input matmul for m > 8; about 1 GB extra,
  * +16% prefill at 2K tokens). Here the weights
- * stay block-quantized: the rows of X go in blocks of 16 through the
- * product of the type (matrix cores for Q4_0 and Q8_0), each block reading
- * the weights, so the weight traffic is up to ceil(M/16) times that of one
- * call (blocks that read a weight tile run side by side and share it in L2).
+ * stay block-quantized and no shadow is kept. Q4_0 and Q8_0 with M >= 64,
+ * K a multiple of 64, X 16-byte aligned with ldx % 4 == 0 and W, ldw_bytes
+ * 4-byte aligned (ldw_bytes < 2^32) go through one tiled matrix-core launch:
+ * tiles of 64 activation rows x 256 weight rows, each weight decoded once
+ * per 64 activation rows and each activation converted once per 256 weight
+ * rows. Other Q4_0 / Q8_0 calls take the rows of X in blocks of 16 through
+ * the matrix-core product (one launch, blocks that read a weight tile side
+ * by side), and Q5_K / Q6_K through their own product, up to 16 rows a
+ * launch.
  *
  *  qtype   QMV_Q4_0, QMV_Q8_0, QMV_Q5_K or QMV_Q6_K.
  *  M       >= 0 (0: nothing to do); other arguments and rules as qmv_q4_0
- *          (qmv_q6_k / qmv_q5_k for the super-block types). Q4_0 and Q8_0
- *          take all blocks of 16 rows in one matrix-core launch.
+ *          (qmv_q6_k / qmv_q5_k for the super-block types).
  */
 int qmv_gemm(int qtype, const void* W, size_t ldw_bytes, const float* X, size_t ldx, float* Y, size_t ldy,
              int M, int N, int K, void* stream);
