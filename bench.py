@@ -764,8 +764,8 @@ def kernel_workloads(dev, reps=3):
             out.append((f"m16_q4_0_5120x{N}", kb, lambda Wm=Wm, Xm=Xm, Ym=Ym: qmv.qmv_q4_0(Wm, Xm, Ym)))
     Wq8, Xq8, Yq8 = w("q8_0", 27648, 5120, 9), x(16, 5120, 9), torch.empty((16, 27648), device=dev)
     out.append(("m16_q8_0_5120x27648", {"k_mq<": 27648 * 160 * 34}, lambda: qmv.qmv_q8_0(Wq8, Xq8, Yq8)))
-    # config 4 MoE (T = 1 and 32) and the FFN epilogue
-    for Tn in (1, 32):
+    # config 4 MoE (T = 1 and 32; and 128 tokens) and the FFN epilogue
+    for Tn in (1, 32, 128):
         d = synth.moe_inputs(Tn)
         dd = {k: T(v) for k, v in d.items()}
         dd["ids"] = dd["ids"].to(torch.int32).contiguous()
@@ -774,7 +774,9 @@ def kernel_workloads(dev, reps=3):
         Ygu = torch.empty(Tn * g.top_k, g.N, device=dev)
         Ydn = torch.empty(Tn * g.top_k, dn.N, device=dev)
         o = torch.empty(Tn, dn.N, device=dev)
-        kid = "k_idv" if Tn == 1 else "k_idp"  # few pairs: all rows as one matrix; many: grouped by expert
+        # few pairs: all rows as one matrix; many: grouped by expert, on the
+        # matrix cores when experts serve several pairs each
+        kid = {1: "k_idv", 32: "k_idp", 128: "k_idq"}[Tn]
         out.append((f"moe_t{Tn}_gate_up_id", {kid: ne * g.N * (g.K // 32) * 18},
                     lambda dd=dd, g=g, Ygu=Ygu: qmv.qmv_id("q4_0", dd["W_gate_up"], dd["X_gate_up"], dd["ids"], Ygu,
                                                             g.N, g.K, expert_scale=dd["expert_scale"])))
@@ -1089,6 +1091,8 @@ def main():
         extra["m16_q8_0"] = m16_throughput(dev, "q8_0")
         extra["moe_t1"] = moe_throughput(dev, 1)
         extra["moe_t32"] = moe_throughput(dev, 32)
+        # 1024 pairs, about 8 per expert: the matrix-core grouped kernel
+        extra["moe_t128"] = moe_throughput(dev, 128)
         extra["moe_ffn_t1_fused"] = moe_throughput(dev, 1, mode="ffn_fused")
         extra["moe_ffn_t1_two_call"] = moe_throughput(dev, 1, mode="ffn_two_call")
         extra["moe_ffn_t32_two_call"] = moe_throughput(dev, 32, mode="ffn_two_call")

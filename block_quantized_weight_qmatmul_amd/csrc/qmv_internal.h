@@ -37,11 +37,18 @@ QMV_HIDDEN int launch_mq(int qtype, const uint8_t* W, size_t ldw, const float* X
 // it would not split K).
 QMV_HIDDEN size_t mq_ws_bytes(int M, int N, int K);
 // Tiled matrix-core product for many activation rows (qmv_mq.hip): tiles of
-// 128 x 128 outputs, each weight decoded once per tile. Requirements, checked
+// 64 x 256 outputs, each weight decoded once per tile. Requirements, checked
 // by the caller: qtype Q4_0 or Q8_0, K > 0 and K % 64 == 0, W and ldw 4-byte
 // aligned, ldw < 2^32, X 16-byte aligned, ldx % 4 == 0, Y 4-byte aligned.
 QMV_HIDDEN int launch_gemm(int qtype, const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy,
                            int M, int N, int K, hipStream_t st);
+// Expert-indexed product on the matrix cores (qmv_mq.hip), Q4_0 or Q8_0.
+// Requirements, checked by the caller: K > 0 and K % 64 == 0, at most 1024
+// pairs and 1024 experts, W, ldw and es 4-byte aligned, ldw < 2^32, X
+// 16-byte aligned, ldx % 4 == 0.
+QMV_HIDDEN int launch_idq(int qtype, const uint8_t* W, size_t es, size_t ldw, int E, const float* X, size_t ldx,
+                          const uint32_t* ids, int n_pairs, int top_k, float* Y, size_t ldy, int N, int K,
+                          const float* sc, int* err, hipStream_t st);
 
 // ---------------------------------------------------------------------------
 // Device helpers
@@ -136,6 +143,93 @@ __device__ __forceinline__ void xpose4(uint32_t* v) {
 // not for its outstanding global loads (__syncthreads waits for those too,
 // which would drain the weight loads already in flight).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+
+// Expert grouping shared by the expert-indexed kernels that serve many pairs.
+constexpr int IDP_MAX_EXPERTS = 1024;  // experts the LDS tables index
+constexpr int IDP_MAX_PAIRS = 1024;    // pairs one launch groups
+
+// Groups the launch's pairs by expert in LDS (all NT threads of the
+// workgroup take part): the distinct experts u = 0 .. U-1 in order of first
+// appearance (s_uexp[u]), the pairs of u at s_plist[s_ustart[u] ..
+// s_ustart[u + 1]) (in no fixed order: they are filled with atomics, and no
+// result depends on it), s_map[e] = u. A pair whose id is outside
+// [0, n_experts) gets a NaN output row and sets *err_flag (those rows spread
+// over the workgroups). Returns U.
+template <int NT>
+__device__ __forceinline__ int group_by_expert(const uint32_t* __restrict__ ids, int n_pairs, int n_experts,
+                                               int* s_map, int* s_uexp, int* s_ustart, int* s_cnt, int* s_plist,
+                                               int* s_U, float* __restrict__ Y, size_t ldy, int N,
+                                               int* __restrict__ err_flag) {
+    constexpr int QPT = IDP_MAX_PAIRS / NT;  // ids per thread
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t myid[QPT];
+#pragma unroll
+    for (int k = 0; k < QPT; ++k) {
+        const int q = tid + k * NT;
+        myid[k] = q < n_pairs ? ids[q] : 0xFFFFFFFFu;
+    }
+    for (int e = tid; e < n_experts; e += NT) s_map[e] = 0x7FFFFFFF;
+    for (int u = tid; u < IDP_MAX_PAIRS; u += NT) s_cnt[u] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < QPT; ++k)
+        if (myid[k] < (uint32_t)n_experts) atomicMin(&s_map[myid[k]], tid + k * NT);
+    __syncthreads();
+    if (wave == 0) {  // distinct experts in order of first appearance
+        int base = 0;
+        for (int q0 = 0; q0 < n_pairs; q0 += 64) {
+            const int q = q0 + lane;
+            const uint32_t e = q < n_pairs ? ids[q] : 0xFFFFFFFFu;
+            const bool first = e < (uint32_t)n_experts && s_map[e] == q;
+            const uint64_t m = __ballot(first);
+            if (first) s_uexp[base + __popcll(m & ((1ull << lane) - 1ull))] = (int)e;
+            base += __popcll(m);
+        }
+        if (lane == 0) *s_U = base;
+    }
+    __syncthreads();
+    const int U = *s_U;
+    for (int u = tid; u < U; u += NT) s_map[s_uexp[u]] = u;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < QPT; ++k)
+        if (myid[k] < (uint32_t)n_experts) atomicAdd(&s_cnt[s_map[myid[k]]], 1);
+    __syncthreads();
+    if (wave == 0) {  // exclusive scan of the counts; the counts become cursors
+        int base = 0;
+        for (int u0 = 0; u0 < U; u0 += 64) {
+            const int u = u0 + lane;
+            const int c = u < U ? s_cnt[u] : 0;
+            int incl = c;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int t = __shfl_up(incl, o, 64);
+                if (lane >= o) incl += t;
+            }
+            if (u < U) {
+                s_ustart[u] = base + incl - c;
+                s_cnt[u] = base + incl - c;
+            }
+            base += __shfl(incl, 63, 64);
+        }
+        if (lane == 0) s_ustart[U] = base;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < QPT; ++k)
+        if (myid[k] < (uint32_t)n_experts) s_plist[atomicAdd(&s_cnt[s_map[myid[k]]], 1)] = tid + k * NT;
+    // pairs with an id out of range: NaN rows, spread over the workgroups
+    for (int q = blockIdx.x; q < n_pairs; q += gridDim.x) {
+        if (ids[q] >= (uint32_t)n_experts) {
+            for (int n = tid; n < N; n += NT) Y[(size_t)q * ldy + n] = __builtin_nanf("");
+            if (tid == 0 && err_flag) *err_flag = 1;
+        }
+    }
+    __syncthreads();
+
+    return U;
+}
 
 }  // namespace qmvi
 

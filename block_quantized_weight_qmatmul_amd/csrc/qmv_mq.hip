@@ -746,6 +746,305 @@ int launch_gemm_q(const uint8_t* W, size_t ldw, const float* X, size_t ldx, floa
     return check_launch("qmv_gemm tiled kernel");
 }
 
+// ---------------------------------------------------------------------------
+// Expert-indexed product on the matrix cores, for calls with many pairs
+// (batched decode, prefill through the experts). Every workgroup groups the
+// launch's pairs by expert in LDS (group_by_expert). Work items are (distinct
+// expert u, block of up to 16 of its pairs, tile of 64 weight rows), numbered
+// expert by expert; persistent workgroups take them in turn. A wave owns the
+// tile's 64 rows: lane (G, j) loads the round's pair of row 16G + j (a
+// transpose across lane rows gives the B operands of the four 16-row
+// blocks, as in k_gemm) and the activation slice G of pair j's row, which is
+// already the A operand lane (G, j) of the MFMA needs: the activations go
+// from global memory to registers, are split into bf16 hi/lo there and never
+// pass through LDS. KS waves share an item by splitting K into KS parts,
+// their partial sums added in part order through LDS at the item's end; with
+// KS = 1 each wave runs items on its own. So each selected expert is read
+// once per 16 of its pairs, decoded once, and multiplied on the matrix
+// cores; per weight the vector work is the decode, a share of the split and
+// one FMA of the block scale per 16 x 16 products.
+// Requirements (checked by the caller): K % 64 == 0, K / 64 a multiple of
+// KS and at least 4 KS, W, ldw and estride 4-byte aligned, ldw < 2^32, X
+// 16-byte aligned and ldx % 4 == 0, n_pairs <= IDP_MAX_PAIRS, n_experts <=
+// IDP_MAX_EXPERTS.
+// ---------------------------------------------------------------------------
+constexpr int IQ_NT = 256;
+
+template <int QT, int KS>
+__global__ __launch_bounds__(IQ_NT) __attribute__((amdgpu_waves_per_eu(2))) void k_idq(
+    const uint8_t* __restrict__ W, size_t estride, size_t ldw, int n_experts, const float* __restrict__ X,
+    size_t ldx, const uint32_t* __restrict__ ids, int n_pairs, int top_k, float* __restrict__ Y, size_t ldy, int N,
+    int K, const float* __restrict__ escale, int* __restrict__ err_flag) {
+    using F = MqFmt<QT>;
+    constexpr int DW = F::DW, PB = 4 * DW;
+    constexpr int SLOTS = 4 / KS;  // items a workgroup runs side by side
+    __shared__ int s_map[IDP_MAX_EXPERTS];
+    __shared__ int s_uexp[IDP_MAX_PAIRS];
+    __shared__ int s_ustart[IDP_MAX_PAIRS + 1];
+    __shared__ int s_cnt[IDP_MAX_PAIRS];
+    __shared__ int s_plist[IDP_MAX_PAIRS];
+    __shared__ int s_istart[IDP_MAX_PAIRS + 1];  // first item of u
+    __shared__ int s_U;
+    __shared__ __align__(16) float s_part[KS > 1 ? 4 * 1024 : 4];  // a wave's 16 sums per lane
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int G = lane >> 4, j = lane & 15;
+    const int U = group_by_expert<IQ_NT>(ids, n_pairs, n_experts, s_map, s_uexp, s_ustart, s_cnt, s_plist, &s_U, Y,
+                                         ldy, N, err_flag);
+    // The workgroups split an expert's pairs into blocks of 16, so every
+    // workgroup must list them in the same order: each expert's pairs sorted
+    // by index (the atomics filled them in any order) into s_cnt, free now.
+    for (int p = tid; p < s_ustart[U]; p += IQ_NT) {
+        const int v = s_plist[p];
+        const int u = s_map[ids[v]];
+        int rank = 0;
+        for (int q = s_ustart[u]; q < s_ustart[u + 1]; ++q) rank += s_plist[q] < v;
+        s_cnt[s_ustart[u] + rank] = v;
+    }
+    __syncthreads();
+    const int* __restrict__ plist = s_cnt;
+    const int tiles = (N + 63) >> 6;
+    if (wave == 0) {  // items of u: blocks of 16 pairs x tiles; exclusive scan
+        int base = 0;
+        for (int u0 = 0; u0 < U; u0 += 64) {
+            const int u = u0 + lane;
+            const int c = u < U ? ((s_ustart[u + 1] - s_ustart[u] + 15) >> 4) * tiles : 0;
+            int incl = c;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int t = __shfl_up(incl, o, 64);
+                if (lane >= o) incl += t;
+            }
+            if (u < U) s_istart[u] = base + incl - c;
+            base += __shfl(incl, 63, 64);
+        }
+        if (lane == 0) s_istart[U] = base;
+    }
+    __syncthreads();
+    const int I = s_istart[U];
+    const int P = K >> 6;
+    const int kq = wave % KS;  // this wave's part of K: pairs [pb, pb + R)
+    const int R = P / KS, pb = kq * R;
+    constexpr int XD = F::xoff(0, 1) - F::xoff(0, 0);  // second 4-float run of a record
+
+    // This wave's items: it0, it0 + stride, ... below I. Every wave of a
+    // workgroup runs the same items when KS > 1 (one slot), so the barriers
+    // of the part sums match.
+    const int it0 = blockIdx.x * SLOTS + wave / KS, stride = gridDim.x * SLOTS;
+    const int nit = it0 < I ? (I - it0 + stride - 1) / stride : 0;
+    if (nit == 0) return;  // uniform over the workgroup when KS > 1 (one slot); no barrier follows
+    // an item's addresses and pairs
+    struct Item {
+        const uint8_t* wrow;  // this lane's weight row (pair 0)
+        const float* xrow;    // this lane's activation slice G of pair j's row
+        int e, pbeg, cnt, n0;
+    };
+    auto decode_item = [&](int it) __attribute__((always_inline)) {
+        int u = 0;  // last u with s_istart[u] <= it
+        for (int span = IDP_MAX_PAIRS / 2; span > 0; span >>= 1)
+            if (u + span < U && s_istart[u + span] <= it) u += span;
+        const int rem = it - s_istart[u];
+        Item t;
+        t.n0 = (rem % tiles) * 64;
+        t.pbeg = s_ustart[u] + 16 * (rem / tiles);
+        t.cnt = s_ustart[u + 1] - t.pbeg < 16 ? s_ustart[u + 1] - t.pbeg : 16;
+        t.e = s_uexp[u];
+        const int wn = t.n0 + 16 * G + j < N ? t.n0 + 16 * G + j : N - 1;  // past N: the last row, not stored
+        t.wrow = W + (size_t)t.e * estride + (uint64_t)(uint32_t)wn * (uint32_t)ldw + (size_t)pb * PB;
+        // pairs past cnt read pair cnt - 1's row: a product row depends on its
+        // own activation row only, and those rows are not stored
+        const int pr = plist[t.pbeg + (j < t.cnt ? j : t.cnt - 1)];
+        t.xrow = X + (size_t)(pr / top_k) * ldx + 64 * pb + F::xoff(G, 0);
+        return t;
+    };
+    // Steps s = k * R + r (item k of this wave, round r) run as one stream:
+    // the weight loads of step s + 4 and the activation loads of step s + 2
+    // are issued after step s (the activations first, so waiting for them
+    // never waits for weights issued later), and they cross item boundaries,
+    // so a new item starts with its loads in flight. R >= 4 (checked by the
+    // caller), so those loads belong to the current or the next item. Steps
+    // past the last item (up to a multiple of 4) load the last item again and
+    // are not stored.
+    Item cur = decode_item(it0);
+    Item nxt = nit > 1 ? decode_item(it0 + stride) : cur;
+    const int S = nit * R;
+    int kcur = 0;  // item of cur
+    auto fetch_w = [&](int s, uint32_t (&wb)[DW]) __attribute__((always_inline)) {
+        const int k = s / R, r = s - k * R;
+        const uint8_t* p = (k == kcur ? cur.wrow : nxt.wrow) + (size_t)r * PB;
+        load_pair<DW>(p, wb);
+    };
+    auto fetch_x = [&](int s, f32x4_t (&xb)[2][2]) __attribute__((always_inline)) {
+        const int k = s / R, r = s - k * R;
+        const float* q = (k == kcur ? cur.xrow : nxt.xrow) + 64 * r;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            xb[h][0] = *reinterpret_cast<const f32x4_t*>(q + 32 * h);
+            xb[h][1] = *reinterpret_cast<const f32x4_t*>(q + 32 * h + XD);
+        }
+    };
+    f32x4_t acc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](const uint32_t (&bl)[DW], const f32x4_t (&xb)[2][2]) __attribute__((always_inline)) {
+        // the loaded registers stay untouched (the transposes below swap
+        // registers in place): working copies, made opaque so that they are
+        // not merged back into the load targets
+        uint32_t b[DW];
+#pragma unroll
+        for (int q = 0; q < DW; ++q) {
+            b[q] = bl[q];
+            asm volatile("" : "+v"(b[q]));
+        }
+        // dd[c]: both block scales of row 16c + j; v0/v1 (w0/w1): slice G of its blocks
+        uint32_t dd[4];
+        const uint32_t dpk = (b[0] & 0xFFFFu) | (b[QT == QMV_Q4_0 ? 4 : 8] & 0xFFFF0000u);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dd[c] = dpk;
+        xpose4(dd);
+        // the block scales as fp32, once (FMAs reading halves issue slower)
+        float scf[2][4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            scf[0][c] = half_lo(dd[c]);
+            scf[1][c] = half_hi(dd[c]);
+            asm volatile("" : "+v"(scf[0][c]), "+v"(scf[1][c]));
+        }
+        uint32_t v0[4], v1[4], w0[4], w1[4];
+        if constexpr (QT == QMV_Q4_0) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                v0[q] = __builtin_amdgcn_alignbyte(b[q + 1], b[q], 2);
+                v1[q] = b[5 + q];
+            }
+            xpose4(v0);
+            xpose4(v1);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                v0[q] = __builtin_amdgcn_alignbyte(b[2 * q + 1], b[2 * q], 2);
+                w0[q] = __builtin_amdgcn_alignbyte(b[2 * q + 2], b[2 * q + 1], 2);
+                v1[q] = b[9 + 2 * q];
+                w1[q] = b[10 + 2 * q];
+            }
+            xpose4(v0);
+            xpose4(w0);
+            xpose4(v1);
+            xpose4(w1);
+        }
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            const float v[8] = {xb[blk][0][0], xb[blk][0][1], xb[blk][0][2], xb[blk][0][3],
+                                xb[blk][1][0], xb[blk][1][1], xb[blk][1][2], xb[blk][1][3]};
+            uint32_t hw[4], lw[4];
+            split_bf16_trunc(v, hw, lw);
+            typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+            const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, (u32x4v){hw[0], hw[1], hw[2], hw[3]});
+            const bf16x8_t al = __builtin_bit_cast(bf16x8_t, (u32x4v){lw[0], lw[1], lw[2], lw[3]});
+            bf16x8_t bq[4];
+            f32x4_t cc[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                if constexpr (QT == QMV_Q4_0)
+                    bq[c] = dec_q4(blk ? v1[c] : v0[c]);
+                else
+                    bq[c] = blk ? dec_q8(v1[c], w1[c]) : dec_q8(v0[c], w0[c]);
+                cc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bq[c], (f32x4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) cc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bq[c], cc[c], 0, 0, 0);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[c][i] = fmaf(scf[blk][c], cc[c][i], acc[c][i]);
+            }
+        }
+    };
+    // the item's outputs: lane (G, j) holds rows 4G .. 4G+3 (pairs) of column j
+    auto finish = [&]() __attribute__((always_inline)) {
+        // (the expert is uniform over the wave: a scalar load, which the
+        // vector-load counter that orders the prefetched loads does not see)
+        const float sc = (escale ? escale[__builtin_amdgcn_readfirstlane(cur.e)] : 1.f) * F::OUT_SCALE;
+        if constexpr (KS > 1) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s_part[wave * 1024 + (c * 4 + i) * 64 + lane] = acc[c][i];
+            lds_barrier();  // (not __syncthreads: that would also wait for the loads in flight)
+            if (kq == 0) {
+#pragma unroll
+                for (int q = 1; q < KS; ++q)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc[c][i] += s_part[(wave + q) * 1024 + (c * 4 + i) * 64 + lane];
+            }
+        }
+        if (kq == 0) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int n = cur.n0 + 16 * c + j;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int m = 4 * G + i;
+                    if (m < cur.cnt && n < N) Y[(size_t)plist[cur.pbeg + m] * ldy + n] = acc[c][i] * sc;
+                }
+            }
+        }
+        if constexpr (KS > 1) lds_barrier();  // the part sums are read before the next item writes them
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        ++kcur;
+        cur = nxt;
+        if (kcur + 1 < nit) nxt = decode_item(it0 + (kcur + 1) * stride);
+    };
+    // register sets: weights of step s in wS[s % 4], activations in xS[s % 2]
+    uint32_t w0s[DW], w1s[DW], w2s[DW], w3s[DW];
+    f32x4_t x0s[2][2], x1s[2][2];
+    // (in the order the loop issues them, so that its wait counts hold from
+    // the first step)
+    fetch_w(0, w0s);
+    fetch_w(1, w1s);
+    fetch_x(0, x0s);
+    fetch_w(2, w2s);
+    fetch_x(1, x1s);
+    fetch_w(3, w3s);
+    // step s needs the activations of step s (issued two steps ago, then
+    // the weights of step s + 2 and all of step s - 1's loads) and the
+    // weights of step s (older): at most 2 * XL + 3 * WL newer loads
+    constexpr int XL = 4, WL = pair_loads<DW>();
+    auto step = [&](int s, uint32_t (&wb)[DW], f32x4_t (&xb)[2][2]) __attribute__((always_inline)) {
+        wait_vmcnt<XL + 2 * WL>();
+        __builtin_amdgcn_sched_barrier(0);  // nothing of the step above the wait
+        compute(wb, xb);
+        fetch_x(s + 2, xb);
+        fetch_w(s + 4, wb);
+        if (s - kcur * R == R - 1 && kcur < nit) finish();
+    };
+    for (int s = 0; s < S; s += 4) {
+        step(s, w0s, x0s);
+        step(s + 1, w1s, x1s);
+        step(s + 2, w2s, x0s);
+        step(s + 3, w3s, x1s);
+    }
+}
+
+template <int QT, int KS>
+int launch_idq_t(const uint8_t* W, size_t es, size_t ldw, int E, const float* X, size_t ldx, const uint32_t* ids,
+                 int n_pairs, int top_k, float* Y, size_t ldy, int N, int K, const float* sc, int* err,
+                 hipStream_t st) {
+    // items: at most (distinct experts + n_pairs / 16) x 64-row tiles
+    const long umax = n_pairs < E ? n_pairs : E;
+    const long items = (umax + n_pairs / 16 + 1) * ((N + 63) / 64);
+    long grid = (long)num_cus() * 2;
+    const long need = (items + 4 / KS - 1) / (4 / KS);
+    grid = grid < need ? grid : need;
+    grid = grid < 1 ? 1 : grid;
+    hipLaunchKernelGGL((k_idq<QT, KS>), dim3((unsigned)grid), dim3(IQ_NT), 0, st, W, es, ldw, E, X, ldx, ids, n_pairs,
+                       top_k, Y, ldy, N, K, sc, err);
+    return check_launch("qmv_id matrix-core kernel");
+}
+
 }  // namespace
 
 size_t mq_ws_bytes(int M, int N, int K) { return M >= 2 && N > 0 && K > 0 ? plan_mq(M, N, K, SIZE_MAX).ws_bytes : 0; }
@@ -754,6 +1053,19 @@ int launch_gemm(int qtype, const uint8_t* W, size_t ldw, const float* X, size_t 
                 int N, int K, hipStream_t st) {
     return qtype == QMV_Q4_0 ? launch_gemm_q<QMV_Q4_0>(W, ldw, X, ldx, Y, ldy, M, N, K, st)
                              : launch_gemm_q<QMV_Q8_0>(W, ldw, X, ldx, Y, ldy, M, N, K, st);
+}
+
+int launch_idq(int qtype, const uint8_t* W, size_t es, size_t ldw, int E, const float* X, size_t ldx,
+               const uint32_t* ids, int n_pairs, int top_k, float* Y, size_t ldy, int N, int K, const float* sc,
+               int* err, hipStream_t st) {
+    const int P = K / 64;
+    if (P < 4) return fail(QMV_EINVAL, "internal: K=%d too small for the matrix-core id kernel", K);
+    const bool ks4 = P >= 16 && P % 4 == 0;
+    if (qtype == QMV_Q4_0)
+        return ks4 ? launch_idq_t<QMV_Q4_0, 4>(W, es, ldw, E, X, ldx, ids, n_pairs, top_k, Y, ldy, N, K, sc, err, st)
+                   : launch_idq_t<QMV_Q4_0, 1>(W, es, ldw, E, X, ldx, ids, n_pairs, top_k, Y, ldy, N, K, sc, err, st);
+    return ks4 ? launch_idq_t<QMV_Q8_0, 4>(W, es, ldw, E, X, ldx, ids, n_pairs, top_k, Y, ldy, N, K, sc, err, st)
+               : launch_idq_t<QMV_Q8_0, 1>(W, es, ldw, E, X, ldx, ids, n_pairs, top_k, Y, ldy, N, K, sc, err, st);
 }
 
 int launch_mq(int qtype, const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N,

@@ -98,6 +98,13 @@ def test_moe_t32_full(call_idx):
     print("ratio", _moe_check(32, call_idx))
 
 
+@pytest.mark.parametrize("call_idx", [0, 1])
+def test_moe_t128_full(call_idx):
+    """128 tokens (1024 pairs, 8 per expert on average): the matrix-core
+    grouped kernel, every output element against the oracle."""
+    print("ratio", _moe_check(128, call_idx))
+
+
 def test_moe_without_expert_scale():
     _moe_check(1, 0, escale=False)
 
@@ -193,6 +200,52 @@ def test_many_pairs_split_across_launches_and_padded_ldy():
     yo, a = oracle.qmv_id("q4_0", W, X, ids, N, K)
     assert_within_tol(y, yo, a, "1200 pairs")
     assert np.all(np.isnan(yfull[:, N:]))
+
+
+@pytest.mark.parametrize("qtype", ["q4_0", "q8_0"])
+@pytest.mark.parametrize("K", [2816, 704, 256])
+def test_grouped_matrix_core_path(qtype, K):
+    """Many pairs per expert take the matrix-core grouped kernel: 8 experts,
+    160 tokens x top-4 = 640 pairs (about 80 per expert: several 16-pair
+    blocks, the last ragged), N = 200 (a ragged 64-row tile), expert scales
+    and padded output rows. K = 2816 splits K over four waves of an item,
+    704 and 256 run one wave per item. A second call is bitwise equal."""
+    E, T, k, N = 8, 160, 4, 200
+    W = synth.make_weights(qtype, E * N, K, cfg=97, part=K).reshape(E, N, -1)
+    X = synth.make_x(T, K, cfg=97, part=K)
+    ids = np.random.default_rng(97 + K).integers(0, E, size=(T, k)).astype(np.uint32)
+    sc = synth.expert_scale(E, cfg=97)
+    y, _, yfull = run_id(qtype, W, X, ids, N, K, escale=sc, ldy=N + 3)
+    yo, a = oracle.qmv_id(qtype, W, X, ids, N, K, sc)
+    assert_within_tol(y, yo, a, f"{qtype} K={K}")
+    assert np.all(np.isnan(yfull[:, N:]))
+    y2, _, _ = run_id(qtype, W, X, ids, N, K, escale=sc, ldy=N + 3)
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+
+
+def test_grouped_matrix_core_bad_ids_and_two_launches():
+    """1200 pairs over 16 experts (two launches of at most 1024 pairs, both
+    on the matrix-core grouped kernel) with ids out of range: NaN rows, the
+    flag set, every other row against the oracle."""
+    E, N, K = 16, 72, 512
+    W = synth.make_weights("q4_0", E * N, K, cfg=98).reshape(E, N, -1)
+    T, k = 300, 4
+    X = synth.make_x(T, K, cfg=98)
+    ids = np.random.default_rng(98).integers(0, E, size=(T, k)).astype(np.uint32)
+    bad = [(0, 3), (255, 0), (256, 1), (299, 3)]  # both launches
+    for t, s_ in bad:
+        ids[t, s_] = E + t
+    y, flag, _ = run_id("q4_0", W, X, ids, N, K, err=True)
+    assert flag == 1
+    badrows = [t * k + s_ for t, s_ in bad]
+    assert np.all(np.isnan(y[badrows]))
+    keep = np.ones(T * k, bool)
+    keep[badrows] = False
+    ids_ok = ids.copy()
+    for t, s_ in bad:
+        ids_ok[t, s_] = 0
+    yo, a = oracle.qmv_id("q4_0", W, X, ids_ok, N, K)
+    assert_within_tol(y[keep], yo[keep], a[keep], "valid rows")
 
 
 def test_zero_tokens_is_a_no_op():
