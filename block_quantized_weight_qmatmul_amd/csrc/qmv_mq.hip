@@ -787,7 +787,10 @@ __global__ __launch_bounds__(IQ_NT) __attribute__((amdgpu_waves_per_eu(2))) void
     __shared__ int s_U;
     __shared__ __align__(16) float s_part[KS > 1 ? 4 * 1024 : 4];  // a wave's 16 sums per lane
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // the wave index in a scalar register: the item loop below is then
+    // uniform per wave (its trip count derives from it), not exec-masked
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int G = lane >> 4, j = lane & 15;
     const int U = group_by_expert<IQ_NT>(ids, n_pairs, n_experts, s_map, s_uexp, s_ustart, s_cnt, s_plist, &s_U, Y,
                                          ldy, N, err_flag);
@@ -886,16 +889,7 @@ __global__ __launch_bounds__(IQ_NT) __attribute__((amdgpu_waves_per_eu(2))) void
     f32x4_t acc[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[c] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-    auto compute = [&](const uint32_t (&bl)[DW], const f32x4_t (&xb)[2][2]) __attribute__((always_inline)) {
-        // the loaded registers stay untouched (the transposes below swap
-        // registers in place): working copies, made opaque so that they are
-        // not merged back into the load targets
-        uint32_t b[DW];
-#pragma unroll
-        for (int q = 0; q < DW; ++q) {
-            b[q] = bl[q];
-            asm volatile("" : "+v"(b[q]));
-        }
+    auto compute = [&](const uint32_t (&b)[DW], const f32x4_t (&xb)[2][2]) __attribute__((always_inline)) {
         // dd[c]: both block scales of row 16c + j; v0/v1 (w0/w1): slice G of its blocks
         uint32_t dd[4];
         const uint32_t dpk = (b[0] & 0xFFFFu) | (b[QT == QMV_Q4_0 ? 4 : 8] & 0xFFFF0000u);
@@ -1036,7 +1030,7 @@ int launch_idq_t(const uint8_t* W, size_t es, size_t ldw, int E, const float* X,
     // items: at most (distinct experts + n_pairs / 16) x 64-row tiles
     const long umax = n_pairs < E ? n_pairs : E;
     const long items = (umax + n_pairs / 16 + 1) * ((N + 63) / 64);
-    long grid = (long)num_cus() * 2;
+    long grid = (long)num_cus() * 2;  // (three per CU measured slower)
     const long need = (items + 4 / KS - 1) / (4 / KS);
     grid = grid < need ? grid : need;
     grid = grid < 1 ? 1 : grid;
