@@ -99,14 +99,6 @@ __device__ __forceinline__ float sbyte(uint32_t w) {
     return (float)(int8_t)(w >> (8 * B));
 }
 
-// Compile-time unrolled loop helper.
-template <int I, int N, typename F>
-__device__ __forceinline__ void unroll(F&& f) {
-    if constexpr (I < N) {
-        f(std::integral_constant<int, I>{});
-        unroll<I + 1, N>(f);
-    }
-}
 
 // Sum over one Q4_0 block whose 16 code bytes start at byte QB of the
 // register window u[] (u = raw ^ 0x88888888, u4 = hi_nibbles(u)); xv = the block's

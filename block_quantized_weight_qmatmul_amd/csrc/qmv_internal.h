@@ -8,6 +8,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "qmv.h"
 
 #define QMV_HIDDEN __attribute__((visibility("hidden")))
@@ -97,6 +99,15 @@ __device__ __forceinline__ void load_pair(const uint8_t* p, uint32_t* r) {
     if constexpr (DW % 4) {
 #pragma unroll
         for (int i = DW & ~3; i < DW; ++i) r[i] = reinterpret_cast<const uint32_t*>(p)[i];
+    }
+}
+
+// Compile-time unrolled loop helper.
+template <int I, int N, typename F>
+__device__ __forceinline__ void unroll(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        unroll<I + 1, N>(f);
     }
 }
 

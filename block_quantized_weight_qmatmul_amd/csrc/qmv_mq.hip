@@ -860,26 +860,29 @@ __global__ __launch_bounds__(IQ_NT) __attribute__((amdgpu_waves_per_eu(2))) void
         t.xrow = X + (size_t)(pr / top_k) * ldx + 64 * pb + F::xoff(G, 0);
         return t;
     };
-    // Steps s = k * R + r (item k of this wave, round r) run as one stream:
-    // the weight loads of step s + 4 and the activation loads of step s + 2
-    // are issued after step s (the activations first, so waiting for them
-    // never waits for weights issued later), and they cross item boundaries,
-    // so a new item starts with its loads in flight. R >= 4 (checked by the
-    // caller), so those loads belong to the current or the next item. Steps
-    // past the last item (up to a multiple of 4) load the last item again and
-    // are not stored.
+    // The rounds of this wave's items run as one stream of slots g = k * R4
+    // + i (item k, slot i < R4 = R rounded up to a multiple of 4; slots i >=
+    // R are skipped). Weights go in super-steps of four rounds: at the first
+    // slot of super-step t, the lane loads the four pairs of super-step t + 1
+    // (its row's pairs in one burst, so each line of the row is requested
+    // while the others are in flight, not again rounds later), into the other
+    // of two register sets. Activations go per round, two rounds ahead, in
+    // two register sets. The loads cross item boundaries, so a new item starts
+    // with its loads in flight; past the last item they repeat the last one's
+    // addresses and are not used.
     Item cur = decode_item(it0);
     Item nxt = nit > 1 ? decode_item(it0 + stride) : cur;
-    const int S = nit * R;
+    const int R4 = (R + 3) & ~3, T4 = R4 >> 2;
     int kcur = 0;  // item of cur
-    auto fetch_w = [&](int s, uint32_t (&wb)[DW]) __attribute__((always_inline)) {
-        const int k = s / R, r = s - k * R;
-        const uint8_t* p = (k == kcur ? cur.wrow : nxt.wrow) + (size_t)r * PB;
-        load_pair<DW>(p, wb);
+    auto fetch_w = [&](int sg, uint32_t (&wb)[4][DW]) __attribute__((always_inline)) {  // super-step sg
+        const int k = sg / T4, t = sg - k * T4;
+        const uint8_t* p = k == kcur ? cur.wrow : nxt.wrow;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) load_pair<DW>(p + (size_t)(4 * t + q < R ? 4 * t + q : R - 1) * PB, wb[q]);
     };
-    auto fetch_x = [&](int s, f32x4_t (&xb)[2][2]) __attribute__((always_inline)) {
-        const int k = s / R, r = s - k * R;
-        const float* q = (k == kcur ? cur.xrow : nxt.xrow) + 64 * r;
+    auto fetch_x = [&](int g, f32x4_t (&xb)[2][2]) __attribute__((always_inline)) {  // slot g
+        const int k = g / R4, r = g - k * R4;
+        const float* q = (k == kcur ? cur.xrow : nxt.xrow) + 64 * (r < R ? r : R - 1);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             xb[h][0] = *reinterpret_cast<const f32x4_t*>(q + 32 * h);
@@ -992,34 +995,36 @@ __global__ __launch_bounds__(IQ_NT) __attribute__((amdgpu_waves_per_eu(2))) void
         cur = nxt;
         if (kcur + 1 < nit) nxt = decode_item(it0 + (kcur + 1) * stride);
     };
-    // register sets: weights of step s in wS[s % 4], activations in xS[s % 2]
-    uint32_t w0s[DW], w1s[DW], w2s[DW], w3s[DW];
+    uint32_t wA[4][DW], wB[4][DW];
     f32x4_t x0s[2][2], x1s[2][2];
-    // (in the order the loop issues them, so that its wait counts hold from
-    // the first step)
-    fetch_w(0, w0s);
-    fetch_w(1, w1s);
+    fetch_w(0, wA);
     fetch_x(0, x0s);
-    fetch_w(2, w2s);
     fetch_x(1, x1s);
-    fetch_w(3, w3s);
-    // step s needs the activations of step s (issued two steps ago, then
-    // the weights of step s + 2 and all of step s - 1's loads) and the
-    // weights of step s (older): at most 2 * XL + 3 * WL newer loads
-    constexpr int XL = 4, WL = pair_loads<DW>();
-    auto step = [&](int s, uint32_t (&wb)[DW], f32x4_t (&xb)[2][2]) __attribute__((always_inline)) {
-        wait_vmcnt<XL + 2 * WL>();
-        __builtin_amdgcn_sched_barrier(0);  // nothing of the step above the wait
-        compute(wb, xb);
-        fetch_x(s + 2, xb);
-        fetch_w(s + 4, wb);
-        if (s - kcur * R == R - 1 && kcur < nit) finish();
+    constexpr int XL = 4, WL = 4 * pair_loads<DW>();
+    // super-step sg: its four slots with weight set w, the next super-step's
+    // weights into set wn; each slot waits for its activations (loads issued
+    // after them: the next slot's activations, and the next weights when
+    // those went out in between)
+    auto superstep = [&](int sg, uint32_t (&w)[4][DW], uint32_t (&wn)[4][DW]) __attribute__((always_inline)) {
+        const int t = sg - kcur * T4;  // super-step within the item (past the last item: t >= T4)
+        unroll<0, 4>([&](auto Q) {
+            constexpr int q = Q;
+            if constexpr (q == 0) fetch_w(sg + 1, wn);
+            if constexpr (q < 2)
+                wait_vmcnt<XL + WL>();
+            else
+                wait_vmcnt<XL>();
+            __builtin_amdgcn_sched_barrier(0);
+            const int g = sg * 4 + q;
+            if (4 * t + q < R && kcur < nit) compute(w[q], (q & 1) ? x1s : x0s);
+            fetch_x(g + 2, (q & 1) ? x1s : x0s);
+        });
+        if (t == T4 - 1 && kcur < nit) finish();
     };
-    for (int s = 0; s < S; s += 4) {
-        step(s, w0s, x0s);
-        step(s + 1, w1s, x1s);
-        step(s + 2, w2s, x0s);
-        step(s + 3, w3s, x1s);
+    const int NS = nit * T4;
+    for (int sg = 0; sg < NS; sg += 2) {
+        superstep(sg, wA, wB);
+        superstep(sg + 1, wB, wA);
     }
 }
 
