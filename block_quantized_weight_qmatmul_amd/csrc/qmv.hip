@@ -2565,7 +2565,8 @@ int id_common(const char* fn, int qtype, const void* Wv, size_t expert_stride_by
         // MoE calls (128 experts, top-8): 1.6x faster than the vector kernel
         // at 128 and 256 tokens, slower at 32 (2 pairs per expert).
         const bool mfma = grouped && !SW && K >= 256 && (long)nt * top_k >= 4L * n_experts &&
-                          ((uintptr_t)Xs & 15) == 0 && (ldx & 3) == 0;
+                          ((uintptr_t)Xs & 15) == 0 && (ldx & 3) == 0 &&
+                          ((size_t)(nt - 1) * ldx + (size_t)K) * 4 < 0x80000000u;  // X by 32-bit offsets
         int rc;
         if (mfma)
             rc = launch_idq(qtype, W, expert_stride_bytes, ldw_bytes, n_experts, Xs, ldx, is, nt * top_k, top_k, Ys, ldy,

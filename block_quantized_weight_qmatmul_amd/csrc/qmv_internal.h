@@ -45,9 +45,9 @@ QMV_HIDDEN size_t mq_ws_bytes(int M, int N, int K);
 QMV_HIDDEN int launch_gemm(int qtype, const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy,
                            int M, int N, int K, hipStream_t st);
 // Expert-indexed product on the matrix cores (qmv_mq.hip), Q4_0 or Q8_0.
-// Requirements, checked by the caller: K > 0 and K % 64 == 0, at most 1024
+// Requirements, checked by the caller: K >= 256 and K % 64 == 0, at most 1024
 // pairs and 1024 experts, W, ldw and es 4-byte aligned, ldw < 2^32, X
-// 16-byte aligned, ldx % 4 == 0.
+// 16-byte aligned, ldx % 4 == 0, the launch's X rows below 2 GiB.
 QMV_HIDDEN int launch_idq(int qtype, const uint8_t* W, size_t es, size_t ldw, int E, const float* X, size_t ldx,
                           const uint32_t* ids, int n_pairs, int top_k, float* Y, size_t ldy, int N, int K,
                           const float* sc, int* err, hipStream_t st);

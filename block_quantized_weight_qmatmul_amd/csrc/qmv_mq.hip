@@ -769,12 +769,16 @@ int launch_gemm_q(const uint8_t* W, size_t ldw, const float* X, size_t ldx, floa
 // IDP_MAX_EXPERTS.
 // ---------------------------------------------------------------------------
 constexpr int IQ_NT = 256;
+// Buffer resource word 3 for raw 32-bit loads on gfx9 parts, and an offset
+// past every buffer the kernel is given (X is below 2 GiB there).
+constexpr int IQ_RSRC_WORD3 = 0x00020000;
+constexpr uint32_t IQ_X_OFF = 0x80000000u;
 
 template <int QT, int KS>
 __global__ __launch_bounds__(IQ_NT) __attribute__((amdgpu_waves_per_eu(2))) void k_idq(
     const uint8_t* __restrict__ W, size_t estride, size_t ldw, int n_experts, const float* __restrict__ X,
     size_t ldx, const uint32_t* __restrict__ ids, int n_pairs, int top_k, float* __restrict__ Y, size_t ldy, int N,
-    int K, const float* __restrict__ escale, int* __restrict__ err_flag) {
+    int K, const float* __restrict__ escale, int* __restrict__ err_flag, int x_bytes) {
     using F = MqFmt<QT>;
     constexpr int DW = F::DW, PB = 4 * DW;
     constexpr int SLOTS = 4 / KS;  // items a workgroup runs side by side
@@ -829,6 +833,8 @@ __global__ __launch_bounds__(IQ_NT) __attribute__((amdgpu_waves_per_eu(2))) void
     const int kq = wave % KS;  // this wave's part of K: pairs [pb, pb + R)
     const int R = P / KS, pb = kq * R;
     constexpr int XD = F::xoff(0, 1) - F::xoff(0, 0);  // second 4-float run of a record
+    // activations through a buffer resource over the launch's x_bytes of X
+    const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(X), 0, x_bytes, IQ_RSRC_WORD3);
 
     // This wave's items: it0, it0 + stride, ... below I. Every wave of a
     // workgroup runs the same items when KS > 1 (one slot), so the barriers
@@ -839,7 +845,7 @@ __global__ __launch_bounds__(IQ_NT) __attribute__((amdgpu_waves_per_eu(2))) void
     // an item's addresses and pairs
     struct Item {
         const uint8_t* wrow;  // this lane's weight row (pair 0)
-        const float* xrow;    // this lane's activation slice G of pair j's row
+        uint32_t xoff;        // byte offset in X of this lane's activation slice G of pair j's row
         int e, pbeg, cnt, n0;
     };
     auto decode_item = [&](int it) __attribute__((always_inline)) {
@@ -854,10 +860,11 @@ __global__ __launch_bounds__(IQ_NT) __attribute__((amdgpu_waves_per_eu(2))) void
         t.e = s_uexp[u];
         const int wn = t.n0 + 16 * G + j < N ? t.n0 + 16 * G + j : N - 1;  // past N: the last row, not stored
         t.wrow = W + (size_t)t.e * estride + (uint64_t)(uint32_t)wn * (uint32_t)ldw + (size_t)pb * PB;
-        // pairs past cnt read pair cnt - 1's row: a product row depends on its
-        // own activation row only, and those rows are not stored
+        // lanes past cnt get an offset beyond the buffer: their loads return
+        // zeros without touching memory (a product row depends on its own
+        // activation row only, and those rows are not stored)
         const int pr = plist[t.pbeg + (j < t.cnt ? j : t.cnt - 1)];
-        t.xrow = X + (size_t)(pr / top_k) * ldx + 64 * pb + F::xoff(G, 0);
+        t.xoff = j < t.cnt ? (uint32_t)(((size_t)(pr / top_k) * ldx + 64 * pb + F::xoff(G, 0)) * 4) : IQ_X_OFF;
         return t;
     };
     // The rounds of this wave's items run as one stream of slots g = k * R4
@@ -882,11 +889,12 @@ __global__ __launch_bounds__(IQ_NT) __attribute__((amdgpu_waves_per_eu(2))) void
     };
     auto fetch_x = [&](int g, f32x4_t (&xb)[2][2]) __attribute__((always_inline)) {  // slot g
         const int k = g / R4, r = g - k * R4;
-        const float* q = (k == kcur ? cur.xrow : nxt.xrow) + 64 * (r < R ? r : R - 1);
+        const uint32_t o = (k == kcur ? cur.xoff : nxt.xoff) + 256u * (uint32_t)(r < R ? r : R - 1);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            xb[h][0] = *reinterpret_cast<const f32x4_t*>(q + 32 * h);
-            xb[h][1] = *reinterpret_cast<const f32x4_t*>(q + 32 * h + XD);
+            xb[h][0] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, (int)(o + 128 * h), 0, 0));
+            xb[h][1] = __builtin_bit_cast(f32x4_t,
+                                          __builtin_amdgcn_raw_buffer_load_b128(xrsrc, (int)(o + 128 * h + 4 * XD), 0, 0));
         }
     };
     f32x4_t acc[4];
@@ -1039,8 +1047,10 @@ int launch_idq_t(const uint8_t* W, size_t es, size_t ldw, int E, const float* X,
     const long need = (items + 4 / KS - 1) / (4 / KS);
     grid = grid < need ? grid : need;
     grid = grid < 1 ? 1 : grid;
+    // the launch's activation rows, in bytes (below 2 GiB: checked by the caller)
+    const long x_bytes = (long)(((size_t)(n_pairs / top_k - 1) * ldx + (size_t)K) * 4);
     hipLaunchKernelGGL((k_idq<QT, KS>), dim3((unsigned)grid), dim3(IQ_NT), 0, st, W, es, ldw, E, X, ldx, ids, n_pairs,
-                       top_k, Y, ldy, N, K, sc, err);
+                       top_k, Y, ldy, N, K, sc, err, (int)x_bytes);
     return check_launch("qmv_id matrix-core kernel");
 }
 
