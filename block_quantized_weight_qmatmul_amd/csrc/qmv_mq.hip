@@ -537,17 +537,20 @@ __global__ __launch_bounds__(GM_NT) __attribute__((amdgpu_waves_per_eu(WPE))) vo
     auto fetch_w = [&](int r, uint32_t (&b)[DW]) __attribute__((always_inline)) {
         load_pair<DW>(wrow + (size_t)(r < R ? r : R - 1) * PB, b);
     };
-    // ---- activations: record q = tid + 256 i is lane (G, j) = q % 64, block
-    // (q / 64) % 2 and activation block q / 128 of the round. Rows past M are
-    // read from row M - 1: a product row depends on its own activation row
-    // only, and those rows are not stored.
+    // ---- activations: record q = tid + 256 i is slice G = q % 4 of row
+    // j = (q % 64) / 4 (operand lane (G, j)), block (q / 64) % 2 and
+    // activation block q / 128 of the round. Rows past M are read from row
+    // M - 1: a product row depends on its own activation row only, and those
+    // rows are not stored.
     const float* xrec[GM_REC];
 #pragma unroll
     for (int i = 0; i < GM_REC; ++i) {
         const int q = tid + GM_NT * i;
+        // lanes 4r .. 4r+3 of a load take slices 0..3 of one activation row,
+        // 64 contiguous bytes (one cache line a lane quad)
         const int rl = q & 63, rb = (q >> 6) & 1, mbk = q >> 7;
-        const int m = m0 + mbk * 16 + (rl & 15);
-        xrec[i] = X + (size_t)(m < M ? m : M - 1) * ldx + 32 * rb + F::xoff(rl >> 4, 0);
+        const int m = m0 + mbk * 16 + (rl >> 2);
+        xrec[i] = X + (size_t)(m < M ? m : M - 1) * ldx + 32 * rb + F::xoff(rl & 3, 0);
     }
     constexpr int XD = F::xoff(0, 1) - F::xoff(0, 0);  // second 4-float run of a record
     auto fetch_x = [&](int r, f32x4_t (&xr)[GM_REC][2]) __attribute__((always_inline)) {
@@ -569,7 +572,8 @@ __global__ __launch_bounds__(GM_NT) __attribute__((amdgpu_waves_per_eu(WPE))) vo
             split_bf16_trunc(v, hw, lw);
             const u32x4 hi = (u32x4){hw[0], hw[1], hw[2], hw[3]};
             const u32x4 lo = (u32x4){lw[0], lw[1], lw[2], lw[3]};
-            uint8_t* rec = smem + buf * GM_BUF + (((q >> 6) * 2) * 64 + (q & 63)) * 16;
+            // its operand slot: lane (G, j) = (slice, row) of the MFMA
+            uint8_t* rec = smem + buf * GM_BUF + (((q >> 6) * 2) * 64 + 16 * (q & 3) + ((q & 63) >> 2)) * 16;
             *reinterpret_cast<u32x4*>(rec) = hi;
             *reinterpret_cast<u32x4*>(rec + 1024) = lo;
         }
