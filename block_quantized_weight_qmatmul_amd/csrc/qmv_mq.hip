@@ -215,13 +215,16 @@ __global__ __launch_bounds__(WAVES * 64) void k_mq(const uint8_t* __restrict__ W
     };
     // ---- activations. Record rho of a round = (step in round, block, slice
     // G, row m) with rho = tid + i * NT: every record of a thread has the
-    // thread's own (G, m) = (lane / 16, lane % 16) and block (wave + i * WAVES)
+    // thread's own (G, m) = (lane % 4, lane / 4) and block (wave + i * WAVES)
     // of the round. Every lane loads from a valid address (rows past M and
     // blocks past K clamped), so the loads carry no branch and the wait before
     // their use counts exactly the loads issued after them; such records are
     // stored as zeros.
-    const bool mok = j < Mb;
-    const float* __restrict__ xb = X + (size_t)(mok ? j : Mb - 1) * ldx + F::xoff(G, 0);
+    // (the thread loads slice xg of row xj: the four lanes of a quad read one
+    // row's 64 contiguous bytes; the record goes to operand slot (xg, xj))
+    const int xj = lane >> 2, xg = lane & 3;
+    const bool mok = xj < Mb;
+    const float* __restrict__ xb = X + (size_t)(mok ? xj : Mb - 1) * ldx + F::xoff(xg, 0);
     constexpr int XD = F::xoff(0, 1) - F::xoff(0, 0);  // second 4-float run of a record
     auto fetch_x = [&](int r, f32x4a_t (&xr)[RPT][2]) __attribute__((always_inline)) {
 #pragma unroll
@@ -234,7 +237,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_mq(const uint8_t* __restrict__ W
         }
     };
     auto put_x = [&](int r, int buf, const f32x4a_t (&xr)[RPT][2]) __attribute__((always_inline)) {
-        uint8_t* base = smem + buf * ROUND_BYTES + wave * 2048 + lane * 16;
+        uint8_t* base = smem + buf * ROUND_BYTES + wave * 2048 + (16 * xg + xj) * 16;
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
             if ((8 * KS) % WAVES != 0 && wave + i * WAVES >= 8 * KS) continue;  // past the round's blocks
