@@ -18,13 +18,13 @@
 //    their weight row; two 4 x 4 transposes across the wave's 16-lane rows
 //    hand every lane its MFMA slice of each of the step's 8 blocks.
 //  * A: each fp32 activation x split into two bf16, x = hi + lo + r with
-//    hi = bf16(x), lo = bf16(x - hi) (round to nearest even, |r| <= 2^-16 |x|
-//    for every finite x within the bf16 range: bf16 keeps the fp32 exponent,
-//    so no activation row needs scaling and no value can fall out of range).
-//    A finite x beyond the largest bf16 takes hi = x rounded toward zero
-//    (|r| <= 2^-15 |x|); an infinity or NaN keeps its value in hi, lo = 0. Each workgroup converts the
-//    activation columns of the step it is about to use into LDS, one step
-//    ahead, from registers loaded one step before that.
+//    hi = x truncated to bf16 (never rounded up, so finite for every finite
+//    x) and lo = bf16(x - hi) of the exact difference: |x - hi| < 2^-7 |x|,
+//    so |r| < 2^-16 |x|. bf16 keeps the fp32 exponent, so no activation row
+//    needs scaling and no value can fall out of range. An infinity or NaN
+//    keeps its value in hi, lo = 0. Each workgroup converts the activation
+//    columns of the step it is about to use into LDS, one step ahead, from
+//    registers loaded one step before that.
 //
 // Work split: a tile is 16 weight rows. A workgroup owns WAVES / KS tiles;
 // the KS waves of a tile take its steps (8 blocks = 256 columns) in turn,
@@ -247,7 +247,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_mq(const uint8_t* __restrict__ W
                 const float v[8] = {xr[i][0].x, xr[i][0].y, xr[i][0].z, xr[i][0].w,
                                     xr[i][1].x, xr[i][1].y, xr[i][1].z, xr[i][1].w};
                 uint32_t hw[4], lw[4];
-                split_bf16(v, hw, lw);
+                split_bf16_trunc(v, hw, lw);
                 hi = (u32x4){hw[0], hw[1], hw[2], hw[3]};
                 lo = (u32x4){lw[0], lw[1], lw[2], lw[3]};
             }
@@ -408,20 +408,30 @@ __global__ __launch_bounds__(256) void k_mqred(const float* __restrict__ part, i
     Y[(size_t)(i / N) * ldy + (size_t)(i % N)] = t;
 }
 
-// Launch plan: workgroup shape and K segments (S = 1: no segments, no workspace).
 struct MqPlan {
     int waves, ks, S, seg_rounds;
     size_t ws_bytes;
 };
 
 // ws_cap: the most workspace bytes the call may use (0: none, scratch-free).
-MqPlan plan_mq(int M, int N, int K, size_t ws_cap) {
+MqPlan plan_mq(int qtype, int M, int N, int K, size_t ws_cap) {
     const long tiles = ((long)N + 15) / 16;
     const long ncu = num_cus();
     const long mblocks = ((long)M + 15) / 16;
     const int steps = ((K >> 6) + 3) >> 2;
     MqPlan p{8, 1, 1, steps, 0};
-    if (tiles * mblocks >= 4 * ncu) return p;  // one wave per tile fills the chip
+    if (tiles * mblocks >= 4 * ncu) {
+        // one wave per tile fills the chip; Q4_0 with at most 8 tiles per
+        // compute unit takes the fewest waves per workgroup that still need
+        // only one workgroup per unit, so that every unit gets one (N = 27648:
+        // 7 waves, 33.9 -> 32.9 us; Q8_0 was slower that way, 46 -> 66 us)
+        for (int w = qtype == QMV_Q4_0 ? 6 : 8; w <= 8; ++w)
+            if ((tiles * mblocks + w - 1) / w <= ncu) {
+                p.waves = w;
+                break;
+            }
+        return p;
+    }
     // Few tiles. Without a workspace: two tiles per workgroup, each split over
     // two waves, every workgroup reading and converting all of X. With one:
     // four tiles per workgroup and K cut into segments of whole steps over
@@ -475,6 +485,8 @@ int launch_mq_q(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float*
                 const MqPlan& p, float* part, hipStream_t st) {
     const int S = p.S, sr = p.seg_rounds;
     if (p.waves == 8 && p.ks == 1) return launch_mq_t<QT, 8, 1>(W, ldw, X, ldx, Y, ldy, M, N, K, S, sr, part, st);
+    if (p.waves == 7 && p.ks == 1) return launch_mq_t<QT, 7, 1>(W, ldw, X, ldx, Y, ldy, M, N, K, S, sr, part, st);
+    if (p.waves == 6 && p.ks == 1) return launch_mq_t<QT, 6, 1>(W, ldw, X, ldx, Y, ldy, M, N, K, S, sr, part, st);
     if (p.waves == 4 && p.ks == 1) return launch_mq_t<QT, 4, 1>(W, ldw, X, ldx, Y, ldy, M, N, K, S, sr, part, st);
     if (p.waves == 4 && p.ks == 2) return launch_mq_t<QT, 4, 2>(W, ldw, X, ldx, Y, ldy, M, N, K, S, sr, part, st);
     return fail(QMV_EINVAL, "internal: no matrix-core kernel for waves=%d ks=%d", p.waves, p.ks);
@@ -1063,7 +1075,10 @@ int launch_idq_t(const uint8_t* W, size_t es, size_t ldw, int E, const float* X,
 
 }  // namespace
 
-size_t mq_ws_bytes(int M, int N, int K) { return M >= 2 && N > 0 && K > 0 ? plan_mq(M, N, K, SIZE_MAX).ws_bytes : 0; }
+// (the workspace size does not depend on the format)
+size_t mq_ws_bytes(int M, int N, int K) {
+    return M >= 2 && N > 0 && K > 0 ? plan_mq(QMV_Q4_0, M, N, K, SIZE_MAX).ws_bytes : 0;
+}
 
 int launch_gemm(int qtype, const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M,
                 int N, int K, hipStream_t st) {
@@ -1086,7 +1101,7 @@ int launch_idq(int qtype, const uint8_t* W, size_t es, size_t ldw, int E, const 
 
 int launch_mq(int qtype, const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N,
               int K, void* ws, size_t ws_bytes, int waves, int ks, int S, hipStream_t st) {
-    MqPlan p = plan_mq(M, N, K, ws ? ws_bytes : 0);
+    MqPlan p = plan_mq(qtype, M, N, K, ws ? ws_bytes : 0);
     if (waves) {  // a forced shape (tuning): S segments of K when given workspace allows
         const int steps = ((K >> 6) + 3) >> 2;
         const int rounds = (steps + ks - 1) / ks;
