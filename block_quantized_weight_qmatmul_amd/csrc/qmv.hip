@@ -2314,7 +2314,7 @@ int dense(int qtype, const void* Wv, size_t ldw, const float* X, size_t ldx, flo
                                  : launch_m1<QMV_Q8_0>(W, ldw, X, Y, N, K, st);
     }
     const bool mq_ok = M >= 2 && K > 0 && K % 64 == 0 && ((uintptr_t)W & 3) == 0 && (ldw & 3) == 0;
-    if (mq_ok) return launch_mq(qtype, W, ldw, X, ldx, Y, ldy, M, N, K, ws, ws ? ws_bytes : 0, 0, 0, 0, st);
+    if (mq_ok) return launch_mq(qtype, W, ldw, X, ldx, Y, ldy, M, N, K, ws, ws ? ws_bytes : 0, st);
     return qtype == QMV_Q4_0 ? launch_generic<QMV_Q4_0>(W, ldw, X, ldx, Y, ldy, M, N, K, st)
                              : launch_generic<QMV_Q8_0>(W, ldw, X, ldx, Y, ldy, M, N, K, st);
 }
@@ -2936,8 +2936,7 @@ int qmv_gemm(int qtype, const void* Wv, size_t ldw, const float* X, size_t ldx, 
     if (q && M >= GEMM_MIN_M && ldw <= 0xFFFFFFFFu && ((uintptr_t)X & 15) == 0 && (ldx & 3) == 0)
         return launch_gemm(qtype, (const uint8_t*)Wv, ldw, X, ldx, Y, ldy, M, N, K, (hipStream_t)stream);
     if (q && M > QMV_MAX_M)
-        return launch_mq(qtype, (const uint8_t*)Wv, ldw, X, ldx, Y, ldy, M, N, K, nullptr, 0, 0, 0, 0,
-                         (hipStream_t)stream);
+        return launch_mq(qtype, (const uint8_t*)Wv, ldw, X, ldx, Y, ldy, M, N, K, nullptr, 0, (hipStream_t)stream);
     // Blocks of up to 16 activation rows, each through the dense call of its
     // type (matrix cores for Q4_0); every block reads the weights once.
     for (int m0 = 0; m0 < M; m0 += QMV_MAX_M) {

@@ -31,10 +31,10 @@ QMV_HIDDEN int num_cus();
 // K % 64 == 0, W and ldw 4-byte aligned, X and Y 4-byte aligned, M >= 1.
 // ws / ws_bytes: a caller workspace the call may use for K-segment partial
 // sums (NULL / 0: none; the call then needs no memory beyond X, W and Y).
-// waves = 0 picks the launch shape; otherwise waves, ks and S force it
-// (tuning).
+// The launch shape follows from M, N, K and the workspace given (ws_bytes of
+// it at ws; none: ws = nullptr).
 QMV_HIDDEN int launch_mq(int qtype, const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy,
-                         int M, int N, int K, void* ws, size_t ws_bytes, int waves, int ks, int S, hipStream_t st);
+                         int M, int N, int K, void* ws, size_t ws_bytes, hipStream_t st);
 // Workspace bytes launch_mq would use for M, N, K given unlimited room (0 if
 // it would not split K).
 QMV_HIDDEN size_t mq_ws_bytes(int M, int N, int K);

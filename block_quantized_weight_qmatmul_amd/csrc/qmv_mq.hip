@@ -170,7 +170,7 @@ __device__ __forceinline__ void split_bf16_trunc(const float (&v)[8], uint32_t (
 // The kernel. grid.x = (tile groups) * mblocks, the 16-row block of X / Y
 // fastest, so the workgroups that read one weight tile run side by side.
 // ---------------------------------------------------------------------------
-template <int QT, int WAVES, int KS>
+template <int QT, int WAVES, int KS, int WD = 4>
 __global__ __launch_bounds__(WAVES * 64) void k_mq(const uint8_t* __restrict__ W, size_t ldw,
                                                    const float* __restrict__ X, size_t ldx, float* __restrict__ Y,
                                                    size_t ldy, int M, int N, int K, int mblocks, int seg_rounds,
@@ -182,7 +182,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_mq(const uint8_t* __restrict__ W
     constexpr int REC = 512 * KS;              // A records (16 B hi + 16 B lo) per round
     constexpr int RPT = (REC + NT - 1) / NT;   // records per thread
     // activation register sets in flight (fewer with the 68-byte Q8_0 pairs)
-    constexpr int XS = ((QT == QMV_Q8_0 || WAVES % 4 != 0) && RPT <= 2) ? 2 : RPT <= 4 ? 4 : 2;
+    constexpr int XS = WD == 1 ? 1 : WD == 2 ? 2 : ((QT == QMV_Q8_0 || WAVES % 4 != 0) && RPT <= 2) ? 2 : RPT <= 4 ? 4 : 2;
+    static_assert(WD % XS == 0, "activation sets must divide the weight depth");
     constexpr int ROUND_BYTES = KS * MQ_STEP_BYTES;
     extern __shared__ __align__(16) uint8_t smem[];  // A operands of two rounds
 
@@ -317,29 +318,26 @@ __global__ __launch_bounds__(WAVES * 64) void k_mq(const uint8_t* __restrict__ W
         }
     };
 
-    // ---- pipeline: weights four rounds ahead; activations converted one
-    // round ahead, from
-    // registers loaded XS rounds before that (XS register sets, X(k) in set
-    // k % XS). Loads past the last round read valid addresses and are not
-    // used, so that no load is conditional (a conditional load makes the
-    // compiler wait for all loads).
+    // ---- pipeline: weights WD rounds ahead; activations converted one
+    // round ahead, from registers loaded XS rounds before that (XS register
+    // sets, X(k) in set k % XS). Loads past the last round read valid
+    // addresses and are not used, so that no load is conditional (a
+    // conditional load makes the compiler wait for all loads).
     f32x4a_t xr[XS][RPT][2];
-    uint32_t b0[DW], b1[DW], b2[DW], b3[DW];
+    uint32_t bw[WD][DW];
     fetch_x(0, xr[0]);  // before the weight loads: waiting for it leaves them in flight
-    issue(0, b0);
-    issue(1, b1);
-    issue(2, b2);
-    issue(3, b3);
+#pragma unroll
+    for (int k = 0; k < WD; ++k) issue(k, bw[k]);
     put_x(0, 0, xr[0]);
 #pragma unroll
     for (int k = 1; k <= XS; ++k) fetch_x(k, xr[k % XS]);
     lds_barrier();
-    // round r: its step, the weights of round r + 4, the activations of
+    // round r: its step, the weights of round r + WD, the activations of
     // round r + 1 into LDS and those of round r + 1 + XS into the freed set
     auto body = [&](int r, uint32_t (&bb)[DW], auto SET) __attribute__((always_inline)) {
         constexpr int xs = decltype(SET)::value;
         compute(r, bb);
-        issue(r + 4, bb);
+        issue(r + WD, bb);
         put_x(r + 1, (r + 1) & 1, xr[xs]);
         fetch_x(r + 1 + XS, xr[xs]);
         lds_barrier();
@@ -347,22 +345,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_mq(const uint8_t* __restrict__ W
         // barrier (it would only hold registers)
         __builtin_amdgcn_sched_barrier(0);
     };
-    using S1 = std::integral_constant<int, 1 % XS>;
-    using S2 = std::integral_constant<int, 2 % XS>;
-    using S3 = std::integral_constant<int, 3 % XS>;
-    using S0 = std::integral_constant<int, 0>;
-    // Whole groups of four rounds in the loop, the rest after it: every path
+    // Whole groups of WD rounds in the loop, the rest after it: every path
     // into the loop's first round then has the same loads in flight.
     int r = 0;
-    for (; r + 4 <= nr; r += 4) {
-        body(r, b0, S1{});
-        body(r + 1, b1, S2{});
-        body(r + 2, b2, S3{});
-        body(r + 3, b3, S0{});
-    }
-    if (r < nr) body(r, b0, S1{});
-    if (r + 1 < nr) body(r + 1, b1, S2{});
-    if (r + 2 < nr) body(r + 2, b2, S3{});
+    for (; r + WD <= nr; r += WD)
+        unroll<0, WD>([&](auto k) { body(r + k, bw[k], std::integral_constant<int, (k + 1) % XS>{}); });
+    unroll<0, WD - 1>([&](auto k) {
+        if (r + k < nr) body(r + k, bw[k], std::integral_constant<int, (k + 1) % XS>{});
+    });
 
     // ---- the KS partial sums of a tile, added in order sp = 0, 1, ...
     // lane (G, j) holds activation rows 4G..4G+3 of weight row j
@@ -391,23 +381,28 @@ __global__ __launch_bounds__(WAVES * 64) void k_mq(const uint8_t* __restrict__ W
     }
 }
 
-// Y[m, n] = the S partial sums part[s][m][n] added in segment order.
+// Y[m, n] = the S partial sums part[s][m][n] added in segment order. Up to
+// 16 partial sums are loaded at once (the addresses of those past S clamped
+// to the last one, not added), so S <= 16 costs one memory latency.
 __global__ __launch_bounds__(256) void k_mqred(const float* __restrict__ part, int S, int M, int N,
                                                float* __restrict__ Y, size_t ldy) {
     const long i = (long)blockIdx.x * 256 + threadIdx.x;
     if (i >= (long)M * N) return;
     const size_t mn = (size_t)M * N;
     const float* p = part + i;
-    float t = p[0];
-    int s = 1;
-    for (; s + 4 <= S; s += 4) {  // four loads in flight, added in order
-        const float a = p[s * mn], b = p[(s + 1) * mn], c = p[(s + 2) * mn], d = p[(s + 3) * mn];
-        t = (((t + a) + b) + c) + d;
+    float t = 0.f;
+    for (int s0 = 0; s0 < S; s0 += 16) {
+        float v[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) v[k] = p[(size_t)(s0 + k < S ? s0 + k : S - 1) * mn];
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            if (s0 + k < S) t = s0 + k == 0 ? v[k] : t + v[k];
     }
-    for (; s < S; ++s) t += p[s * mn];
     Y[(size_t)(i / N) * ldy + (size_t)(i % N)] = t;
 }
 
+// Launch plan: workgroup shape and K segments (S = 1: no segments, no workspace).
 struct MqPlan {
     int waves, ks, S, seg_rounds;
     size_t ws_bytes;
@@ -421,24 +416,24 @@ MqPlan plan_mq(int qtype, int M, int N, int K, size_t ws_cap) {
     const int steps = ((K >> 6) + 3) >> 2;
     MqPlan p{8, 1, 1, steps, 0};
     if (tiles * mblocks >= 4 * ncu) {
-        // one wave per tile fills the chip; Q4_0 with at most 8 tiles per
-        // compute unit takes the fewest waves per workgroup that still need
-        // only one workgroup per unit, so that every unit gets one (N = 27648:
-        // 7 waves, 33.9 -> 32.9 us; Q8_0 was slower that way, 46 -> 66 us)
-        for (int w = qtype == QMV_Q4_0 ? 6 : 8; w <= 8; ++w)
-            if ((tiles * mblocks + w - 1) / w <= ncu) {
-                p.waves = w;
-                break;
-            }
+        // One wave per tile fills the chip. Seven tiles per workgroup,
+        // each split over two waves that take alternate steps, with the
+        // weights one round ahead (96 registers, so 14 waves fit a compute
+        // unit; a streaming read with 7-8 waves per unit runs 10-15% slower
+        // than with 16). N = 27648: 30.0 us, against 32.9 with one wave per
+        // tile and weights four rounds ahead (Q4_0); Q8_0 44.0 against 45.8.
+        p.waves = 14;
+        p.ks = 2;
         return p;
     }
     // Few tiles. Without a workspace: two tiles per workgroup, each split over
     // two waves, every workgroup reading and converting all of X. With one:
-    // four tiles per workgroup and K cut into segments of whole steps over
-    // grid.y, so that about one workgroup per compute unit each reads and
-    // converts only its segment of X; the partial sums go to the workspace
-    // and a second launch adds them in segment order (M = 16, K = 5120,
-    // graph-timed: N = 5120 17 us with 3 segments, N = 1024 11 us with 10).
+    // four tiles per workgroup (each split over two waves) and K cut into
+    // segments of whole rounds over grid.y, so that about one workgroup per
+    // compute unit each reads and converts only its segment of X; the partial
+    // sums go to the workspace and a second launch adds them in segment order
+    // (M = 16, K = 5120, graph-timed: N = 5120 13.8 us with 3 segments,
+    // N = 1024 8.6 us with 10).
     const long groups = ((tiles + 3) / 4) * mblocks;
     long S = (ncu + groups / 2) / groups;  // about one workgroup per compute unit
     S = S < steps ? S : steps;
@@ -450,16 +445,20 @@ MqPlan plan_mq(int qtype, int M, int N, int K, size_t ws_cap) {
         p.seg_rounds = (steps + 1) / 2;
         return p;
     }
-    const int seg = (int)((steps + S - 1) / S);
-    p.waves = 4;
-    p.ks = 1;
+    // each tile split over two waves (weights one round ahead): 8 waves a
+    // workgroup instead of 4 (M = 16, K = 5120: N = 5120 15.6 -> 13.8 us,
+    // N = 1024 9.1 -> 8.6 us)
+    const int rds = (steps + 1) / 2;
+    const int seg = (int)((rds + S - 1) / S);
+    p.waves = 8;
+    p.ks = 2;
     p.seg_rounds = seg;
-    p.S = (steps + seg - 1) / seg;
+    p.S = (rds + seg - 1) / seg;
     p.ws_bytes = (size_t)p.S * per_seg;
     return p;
 }
 
-template <int QT, int WAVES, int KS>
+template <int QT, int WAVES, int KS, int WD = 4>
 int launch_mq_t(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N, int K,
                 int S, int seg_rounds, float* part, hipStream_t st) {
     constexpr int TWG = WAVES / KS;
@@ -468,7 +467,7 @@ int launch_mq_t(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float*
     const long mblocks = ((long)M + 15) / 16;
     if (groups * mblocks > 0x7FFFFFFF || S > 65535) return fail(QMV_EINVAL, "N too large");
     const size_t lds = (size_t)2 * KS * MQ_STEP_BYTES;
-    hipLaunchKernelGGL((k_mq<QT, WAVES, KS>), dim3((unsigned)(groups * mblocks), (unsigned)S), dim3(WAVES * 64), lds,
+    hipLaunchKernelGGL((k_mq<QT, WAVES, KS, WD>), dim3((unsigned)(groups * mblocks), (unsigned)S), dim3(WAVES * 64), lds,
                        st, W, ldw, X, ldx, Y, ldy, M, N, K, (int)mblocks, seg_rounds, S > 1 ? part : nullptr);
     int rc = check_launch("qmv matrix-core kernel");
     if (rc == QMV_OK && S > 1) {
@@ -484,10 +483,8 @@ template <int QT>
 int launch_mq_q(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N, int K,
                 const MqPlan& p, float* part, hipStream_t st) {
     const int S = p.S, sr = p.seg_rounds;
-    if (p.waves == 8 && p.ks == 1) return launch_mq_t<QT, 8, 1>(W, ldw, X, ldx, Y, ldy, M, N, K, S, sr, part, st);
-    if (p.waves == 7 && p.ks == 1) return launch_mq_t<QT, 7, 1>(W, ldw, X, ldx, Y, ldy, M, N, K, S, sr, part, st);
-    if (p.waves == 6 && p.ks == 1) return launch_mq_t<QT, 6, 1>(W, ldw, X, ldx, Y, ldy, M, N, K, S, sr, part, st);
-    if (p.waves == 4 && p.ks == 1) return launch_mq_t<QT, 4, 1>(W, ldw, X, ldx, Y, ldy, M, N, K, S, sr, part, st);
+    if (p.waves == 14 && p.ks == 2) return launch_mq_t<QT, 14, 2, 1>(W, ldw, X, ldx, Y, ldy, M, N, K, S, sr, part, st);
+    if (p.waves == 8 && p.ks == 2) return launch_mq_t<QT, 8, 2, 1>(W, ldw, X, ldx, Y, ldy, M, N, K, S, sr, part, st);
     if (p.waves == 4 && p.ks == 2) return launch_mq_t<QT, 4, 2>(W, ldw, X, ldx, Y, ldy, M, N, K, S, sr, part, st);
     return fail(QMV_EINVAL, "internal: no matrix-core kernel for waves=%d ks=%d", p.waves, p.ks);
 }
@@ -1100,19 +1097,8 @@ int launch_idq(int qtype, const uint8_t* W, size_t es, size_t ldw, int E, const 
 }
 
 int launch_mq(int qtype, const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N,
-              int K, void* ws, size_t ws_bytes, int waves, int ks, int S, hipStream_t st) {
-    MqPlan p = plan_mq(qtype, M, N, K, ws ? ws_bytes : 0);
-    if (waves) {  // a forced shape (tuning): S segments of K when given workspace allows
-        const int steps = ((K >> 6) + 3) >> 2;
-        const int rounds = (steps + ks - 1) / ks;
-        p.waves = waves;
-        p.ks = ks;
-        S = S < 1 ? 1 : (S > rounds ? rounds : S);
-        p.seg_rounds = (rounds + S - 1) / S;
-        p.S = (rounds + p.seg_rounds - 1) / p.seg_rounds;
-        p.ws_bytes = p.S > 1 ? (size_t)p.S * M * N * sizeof(float) : 0;
-        if (p.ws_bytes > (ws ? ws_bytes : 0)) return fail(QMV_EINVAL, "internal: workspace too small for S=%d", S);
-    }
+              int K, void* ws, size_t ws_bytes, hipStream_t st) {
+    const MqPlan p = plan_mq(qtype, M, N, K, ws ? ws_bytes : 0);
     return qtype == QMV_Q4_0 ? launch_mq_q<QMV_Q4_0>(W, ldw, X, ldx, Y, ldy, M, N, K, p, (float*)ws, st)
                              : launch_mq_q<QMV_Q8_0>(W, ldw, X, ldx, Y, ldy, M, N, K, p, (float*)ws, st);
 }
