@@ -2019,6 +2019,124 @@ __global__ __launch_bounds__(WAVES * 64) void k_q6k(const uint8_t* __restrict__ 
     if (s < nsteps) step(bufA, bufB);
 }
 
+// Several M = 1 super-block products that share x and K in one launch
+// (qmv_batch): the problems' rows are streamed as one virtual matrix of
+// tiles, problem p owning tiles t0[p] .. t0[p + 1] - 1 (a tile never spans
+// two problems), in k_q6k's loop. The loading tile's problem and the summing
+// tile's output live in registers and change only at tile boundaries.
+template <int MAXP>
+struct Q6Cat {
+    const uint8_t* W[MAXP];
+    size_t ldw[MAXP];
+    float* y[MAXP];
+    int N[MAXP];
+    long t0[MAXP + 1];
+    const float* x;
+    int K, n;
+};
+
+template <class F, int LPR, int WAVES, int MAXP>
+__global__ __launch_bounds__(WAVES * 64) void k_q6kc(const Q6Cat<MAXP> C) {
+    constexpr int GROUPS = 64 / LPR;
+    constexpr int ROWS = GROUPS * WAVES;
+    constexpr int NT = WAVES * 64;
+    constexpr int GCH = (KMAX_Q6 / 16 + NT - 1) / NT;
+    extern __shared__ __align__(16) float xs[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane / LPR, j = lane % LPR;
+    const int K = C.K;
+    const int U = F::units(K);
+    const int IPT = (U + LPR - 1) / LPR;
+    const long ntiles = C.t0[C.n];
+    const long lrow = (long)(wave * GROUPS + g);
+    float* gs = xs + (size_t)U * XS_Q6;
+
+    long tile = blockIdx.x;
+    if (tile >= ntiles) return;  // uniform over the workgroup
+    // the problem of a tile (uniform: a few scalar compares)
+    auto prob = [&](long tl) {
+        int ip = 0;
+#pragma unroll
+        for (int q = 1; q < MAXP; ++q) ip += (q < C.n && tl >= C.t0[q]) ? 1 : 0;
+        return ip;
+    };
+    int ip = prob(tile);
+    const uint8_t* iW = C.W[ip];
+    size_t ildw = C.ldw[ip];
+    int iN = C.N[ip];
+    long it0 = C.t0[ip];
+    float* sy = C.y[ip];
+    int sN = iN;
+    long st0 = it0;
+    int it = 0;
+    uint32_t bufA[F::DW], bufB[F::DW];
+    auto issue = [&](long tl, int i, uint32_t (&b)[F::DW]) {
+        long row = (tl - it0) * ROWS + lrow;
+        row = row < iN ? row : iN - 1;
+        int u = j + i * LPR;
+        u = u < U ? u : U - 1;
+        F::load(iW + (size_t)row * ildw, nullptr, nullptr, u, K, b);
+    };
+    {
+        // x loads first, then the first weight loads (see m1_stream)
+        const size_t xo = 0;
+        Q6Stage<NT, GCH, 1> stg;
+        stg.load(C.x, &xo, 1, K);
+        issue(tile, 0, bufA);
+        stg.store(xs, 0, gs, 0, 1, K);
+    }
+    lds_barrier();
+    float tot = 0.f;
+    auto consume = [&](const uint32_t (&cb)[F::DW]) {
+        // past the row end: decode the clamped unit, add zero (see m1_stream)
+        const int u0 = j + it * LPR;
+        const bool in = u0 < U;
+        const int u = in ? u0 : U - 1;
+        float part[1] = {0.f};
+        F::template dot<1>(cb, u, K, xs + (size_t)u * XS_Q6, 0, gs + 8 * u, 0, 1, part);
+        tot += in ? part[0] : 0.f;
+        if (it == IPT - 1) {
+            const long row = (tile - st0) * ROWS + lrow;
+            const float sum = lane_group_sum<LPR>(tot);
+            if (j == LPR - 1 && row < sN) sy[row] = sum;
+            tot = 0.f;
+        }
+    };
+    // one step, the same shape every time (see m1_stream)
+    auto step = [&](uint32_t (&cb)[F::DW], uint32_t (&nb)[F::DW]) {
+        int it2 = it + 1;
+        long tile2 = tile;
+        if (it2 == IPT) {
+            it2 = 0;
+            tile2 += gridDim.x;
+            if (tile2 < ntiles) {
+                ip = prob(tile2);
+                iW = C.W[ip];
+                ildw = C.ldw[ip];
+                iN = C.N[ip];
+                it0 = C.t0[ip];
+            }
+        }
+        issue(tile2, it2, nb);
+        pin_regs<F::DW>(cb);
+        consume(cb);
+        if (it2 == 0) {  // the next step starts the tile just issued
+            sy = C.y[ip];
+            sN = iN;
+            st0 = it0;
+        }
+        tile = tile2;
+        it = it2;
+    };
+    const long nsteps = ((ntiles - 1 - (long)blockIdx.x) / gridDim.x + 1) * IPT;
+    long s = 0;
+    for (; s + 2 <= nsteps; s += 2) {
+        step(bufA, bufB);
+        step(bufB, bufA);
+    }
+    if (s < nsteps) step(bufA, bufB);
+}
+
 // Expert-indexed super-block (Q6_K, Q5_K) product: one workgroup per (tile of ROWS rows, pair
 // p); expert ids[p]'s rows against activation row p / top_k. Pairs are not
 // grouped by expert (each reads its expert's rows): the form for decode,
@@ -2700,6 +2818,52 @@ int launch_id_q6(const uint8_t* W, size_t es, size_t ldw, int E, const float* X,
                              : launch_id_kq<FmtQ6K>(W, es, ldw, E, X, ldx, ids, n_pairs, top_k, Y, ldy, N, K, sc, err, st);
 }
 
+// Batched M = 1 super-block products sharing x and K (k_q6kc): lane groups
+// widened, as for one call of all the rows, until every compute unit has a
+// tile.
+template <class F, int LPR, int MAXP>
+int launch_q6kc_t(const M1Prob* probs, int n, hipStream_t st) {
+    constexpr int WAVES = 8, ROWS = (64 / LPR) * WAVES;
+    Q6Cat<MAXP> C{};
+    long t = 0;
+    for (int i = 0; i < n; ++i) {
+        C.W[i] = probs[i].W;
+        C.ldw[i] = probs[i].ldw;
+        C.y[i] = probs[i].y;
+        C.N[i] = probs[i].N;
+        C.t0[i] = t;
+        t += ((long)probs[i].N + ROWS - 1) / ROWS;
+    }
+    C.t0[n] = t;
+    C.x = probs[0].x;
+    C.K = probs[0].K;
+    C.n = n;
+    long nwg = (long)num_cus() * 2;
+    nwg = nwg < t ? nwg : t;
+    hipLaunchKernelGGL((k_q6kc<F, LPR, WAVES, MAXP>), dim3((unsigned)nwg), dim3(WAVES * 64), q6_xs_bytes(C.K), st, C);
+    return check_launch("batched super-block kernel");
+}
+
+template <class F, int MAXP>
+int launch_q6kc_n(const M1Prob* probs, int n, hipStream_t st) {
+    long rows = 0;
+    for (int i = 0; i < n; ++i) rows += probs[i].N;
+    int lpr = pick_lpr_q6(F::units(probs[0].K));
+    while (lpr < 64 && (rows + (64 / lpr) * 8 - 1) / ((64 / lpr) * 8) < num_cus()) lpr *= 2;
+    switch (lpr) {
+        case 64: return launch_q6kc_t<F, 64, MAXP>(probs, n, st);
+        case 32: return launch_q6kc_t<F, 32, MAXP>(probs, n, st);
+        case 16: return launch_q6kc_t<F, 16, MAXP>(probs, n, st);
+        case 8: return launch_q6kc_t<F, 8, MAXP>(probs, n, st);
+        default: return launch_q6kc_t<F, 4, MAXP>(probs, n, st);
+    }
+}
+
+template <class F>
+int launch_q6kc(const M1Prob* probs, int n, hipStream_t st) {
+    return n <= 4 ? launch_q6kc_n<F, 4>(probs, n, st) : launch_q6kc_n<F, QMV_MAX_BATCH>(probs, n, st);
+}
+
 // Rows of X in launches of up to 4 (one launch when M = 1).
 template <class F>
 int launch_q6k(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float* Y, size_t ldy, int M, int N, int K,
@@ -3107,21 +3271,26 @@ int qmv_moe_down(int qtype, const void* Wv, size_t expert_stride_bytes, size_t l
 }
 
 int qmv_batch(int qtype, const qmv_problem* problems, int n_problems, void* stream) {
-    if (qtype != QMV_Q4_0 && qtype != QMV_Q8_0) return fail(QMV_EUNSUPPORTED, "qmv_batch: qtype %d not supported", qtype);
+    const bool kq = qtype == QMV_Q5_K || qtype == QMV_Q6_K;
+    if (qtype != QMV_Q4_0 && qtype != QMV_Q8_0 && !kq)
+        return fail(QMV_EUNSUPPORTED, "qmv_batch: qtype %d not supported", qtype);
     if (n_problems < 0 || n_problems > QMV_MAX_BATCH)
         return fail(QMV_EINVAL, "qmv_batch: n_problems=%d outside 0..%d", n_problems, QMV_MAX_BATCH);
     if (n_problems == 0) return QMV_OK;
     if (!problems) return fail(QMV_EINVAL, "qmv_batch: problems is NULL");
-    const int bb = block_bytes(qtype);
+    // bytes per block of qk weights
+    const int qk = kq ? 256 : QK;
+    const int bb = qtype == QMV_Q5_K ? Q5_SB_BYTES : qtype == QMV_Q6_K ? Q6_SB_BYTES : block_bytes(qtype);
     size_t wb[QMV_MAX_BATCH], xb[QMV_MAX_BATCH], yb[QMV_MAX_BATCH];
     for (int i = 0; i < n_problems; ++i) {
         const qmv_problem& p = problems[i];
         if (p.N < 0) return fail(QMV_EINVAL, "qmv_batch: problem %d: N=%d < 0", i, p.N);
-        if (p.K < 0 || p.K % QK) return fail(QMV_EINVAL, "qmv_batch: problem %d: K=%d is not a non-negative multiple of 32", i, p.K);
-        const size_t row = (size_t)(p.K / QK) * bb;
+        if (p.K < 0 || p.K % qk) return fail(QMV_EINVAL, "qmv_batch: problem %d: K=%d is not a non-negative multiple of %d", i, p.K, qk);
+        if (kq && p.K > KMAX_Q6) return fail(QMV_EUNSUPPORTED, "qmv_batch: problem %d: K=%d exceeds %d", i, p.K, KMAX_Q6);
+        const size_t row = (size_t)(p.K / qk) * bb;
         if (p.N > 0 && !p.y) return fail(QMV_EINVAL, "qmv_batch: problem %d: y is NULL", i);
         if (p.N > 0 && p.K > 0 && (!p.W || !p.x)) return fail(QMV_EINVAL, "qmv_batch: problem %d: W or x is NULL", i);
-        if (p.ldw_bytes < row) return fail(QMV_EINVAL, "qmv_batch: problem %d: ldw_bytes=%zu < K/32*%d=%zu", i, p.ldw_bytes, bb, row);
+        if (p.ldw_bytes < row) return fail(QMV_EINVAL, "qmv_batch: problem %d: ldw_bytes=%zu < K/%d*%d=%zu", i, p.ldw_bytes, qk, bb, row);
         if (((uintptr_t)p.W & 1) || (p.ldw_bytes & 1)) return fail(QMV_EALIGN, "qmv_batch: problem %d: W and ldw_bytes must be 2-byte aligned", i);
         if (((uintptr_t)p.x & 3) || ((uintptr_t)p.y & 3)) return fail(QMV_EALIGN, "qmv_batch: problem %d: x and y must be 4-byte aligned", i);
         if (p.N > 0 && (size_t)p.N > (SIZE_MAX - row) / (p.ldw_bytes ? p.ldw_bytes : 1)) return fail(QMV_EINVAL, "qmv_batch: problem %d: N*ldw overflows", i);
@@ -3136,6 +3305,44 @@ int qmv_batch(int qtype, const qmv_problem* problems, int n_problems, void* stre
                 return fail(QMV_EINVAL, "qmv_batch: output of problem %d overlaps an input or another output (problem %d)", i, k);
         }
     hipStream_t st = (hipStream_t)stream;
+    if (kq) {
+        // Super-block types: problems that share x and K (K > 0) in one
+        // launch of k_q6kc; any others, and K = 0, one call each.
+        M1Prob sh[QMV_MAX_BATCH];
+        int ns = 0;
+        const float* x0 = nullptr;
+        int K0 = -1;
+        for (int i = 0; i < n_problems; ++i)
+            if (problems[i].N > 0 && problems[i].K > 0) {
+                x0 = problems[i].x;
+                K0 = problems[i].K;
+                break;
+            }
+        for (int i = 0; i < n_problems; ++i) {
+            const qmv_problem& p = problems[i];
+            if (p.N == 0) continue;
+            const uint8_t* W = (const uint8_t*)p.W;
+            if (p.K > 0 && p.x == x0 && p.K == K0) {
+                M1Prob& q = sh[ns++];
+                q.W = W;
+                q.x = p.x;
+                q.y = p.y;
+                q.ldw = p.ldw_bytes;
+                q.N = p.N;
+                q.K = p.K;
+                continue;
+            }
+            int rc;
+            if (p.K == 0)
+                rc = launch_generic<QMV_Q4_0>(W, p.ldw_bytes, p.x, 0, p.y, p.N, 1, p.N, 0, st);
+            else
+                rc = qtype == QMV_Q5_K ? launch_q6k<FmtQ5K>(W, p.ldw_bytes, p.x, p.K, p.y, p.N, 1, p.N, p.K, 0, 0, st)
+                                       : launch_q6k<FmtQ6K>(W, p.ldw_bytes, p.x, p.K, p.y, p.N, 1, p.N, p.K, 0, 0, st);
+            if (rc) return rc;
+        }
+        if (ns == 0) return QMV_OK;
+        return qtype == QMV_Q5_K ? launch_q6kc<FmtQ5K>(sh, ns, st) : launch_q6kc<FmtQ6K>(sh, ns, st);
+    }
     M1Prob fast[QMV_MAX_BATCH];
     int nf = 0;
     for (int i = 0; i < n_problems; ++i) {

@@ -395,14 +395,21 @@ int qmv_moe_down(int qtype, const void* W, size_t expert_stride_bytes, size_t ld
  * groups before the first and the ninth block of dispatches). Problems may
  * share x; their outputs must not overlap each other or any W or x. When
  * every problem reads the same x pointer with the same K, their rows are
- * streamed as one matrix (the results equal the single calls' bit for bit).
+ * streamed as one matrix (Q4_0 and Q8_0: the results equal the single calls'
+ * bit for bit; Q5_K and Q6_K: the launch picks its lane-group width for all
+ * the rows together, so a result may differ from the single call's in the
+ * order of its fp32 sums, both within the tolerance). For the super-block
+ * types the problems on the first problem's x and K go out as one launch,
+ * any others one call each.
  *
- *  qtype        QMV_Q4_0 or QMV_Q8_0 (all problems of a batch have one type).
+ *  qtype        QMV_Q4_0, QMV_Q8_0, QMV_Q5_K or QMV_Q6_K (all problems of a
+ *               batch have one type).
  *  problems     HOST array of n_problems descriptors, read during the call.
  *  n_problems   0..QMV_MAX_BATCH (0: nothing to do).
- * Each descriptor follows qmv_q4_0's rules for M = 1 (W 2-byte aligned,
- * ldw_bytes even and >= K/32 * block bytes, x and y 4-byte aligned, K a
- * non-negative multiple of 32). Every problem is validated before anything
+ * Each descriptor follows the single call's rules for M = 1 (W 2-byte
+ * aligned, ldw_bytes even and >= the row's blocks in bytes, x and y 4-byte
+ * aligned; K a non-negative multiple of 32, and for Q5_K / Q6_K of 256 and
+ * at most 16384: QMV_EUNSUPPORTED above). Every problem is validated before anything
  * is launched; one bad descriptor rejects the whole call.
  */
 #define QMV_MAX_BATCH 16

@@ -161,6 +161,18 @@ def test_batch_argument_checks(probs, status, msg):
     assert msg in qmv.last_error()
 
 
+@pytest.mark.parametrize("probs,status,msg", [
+    ([_bp(K=128, ldw=176)], qmv.QMV_EINVAL, "multiple of 256"),
+    ([_bp(K=16640, ldw=176 * 65)], qmv.QMV_EUNSUPPORTED, "exceeds"),
+    ([_bp(K=512, ldw=176 * 2 - 2)], qmv.QMV_EINVAL, "ldw_bytes"),
+    ([_bp(K=512, ldw=176 * 2 + 1)], qmv.QMV_EALIGN, "2-byte"),
+])
+def test_batch_super_block_argument_checks(probs, status, msg):
+    """Q5_K batches: K a multiple of 256 up to 16384, rows of K/256 super-blocks."""
+    assert qmv.raw_qmv_batch(qmv.QMV_Q5_K, probs) == status
+    assert msg in qmv.last_error()
+
+
 def test_batch_bad_qtype_and_empty():
     assert qmv.raw_qmv_batch(5, [_bp()]) == qmv.QMV_EUNSUPPORTED
     assert qmv.raw_qmv_batch(Q4, []) == qmv.QMV_OK
