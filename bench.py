@@ -800,8 +800,8 @@ def kernel_workloads(dev, reps=3):
     W5 = [w("q5_k", n, 2816, 11 + i) for i, n in enumerate((5760, 5760, 128))]
     x5 = x(1, 2816, 11)[0]
     y5 = [torch.empty(n, device=dev) for n in (5760, 5760, 128)]
-    out.append(("q5_k_b9_2816x5760x2_128", {"k_q6k": (5760 * 2 + 128) * synth.row_bytes("q5_k", 2816)},
-                lambda: [qmv.qmv_q5_k(W_, x5, y_) for W_, y_ in zip(W5, y5)]))
+    out.append(("q5_k_b9_2816x5760x2_128", {"k_q6kc": (5760 * 2 + 128) * synth.row_bytes("q5_k", 2816)},
+                lambda: qmv.qmv_batch("q5_k", [(W_, x5, y_) for W_, y_ in zip(W5, y5)])))
     E6 = torch.from_numpy(synth.make_weights("q6_k", 128 * 1408, 2816, cfg=9, part=12).reshape(128, 1408, -1)).to(dev)
     x6e = x(1, 2816, 12)
     ids6 = T(synth.router_topk(1, 128, 8, cfg=9, part=12).astype(np.int32))
