@@ -427,7 +427,7 @@ MqPlan plan_mq(int qtype, int M, int N, int K, size_t ws_cap) {
         return p;
     }
     // Few tiles. Without a workspace: two tiles per workgroup, each split over
-    // two waves, every workgroup reading and converting all of X. With one:
+    // four waves, every workgroup reading and converting all of X. With one:
     // four tiles per workgroup (each split over two waves) and K cut into
     // segments of whole rounds over grid.y, so that about one workgroup per
     // compute unit each reads and converts only its segment of X; the partial
@@ -440,9 +440,12 @@ MqPlan plan_mq(int qtype, int M, int N, int K, size_t ws_cap) {
     const size_t per_seg = (size_t)M * N * sizeof(float);
     if (ws_cap / per_seg < (size_t)S) S = (long)(ws_cap / per_seg);
     if (S < 2) {
-        p.waves = 4;
-        p.ks = 2;
-        p.seg_rounds = (steps + 1) / 2;
+        // two tiles per workgroup, each split over four waves (M = 16,
+        // K = 5120: N = 5120 19.8 -> 14.7 us, N = 1024 19.4 -> 14.4 us
+        // against two waves per tile)
+        p.waves = 8;
+        p.ks = 4;
+        p.seg_rounds = (steps + 3) / 4;
         return p;
     }
     // each tile split over two waves (weights one round ahead): 8 waves a
@@ -485,7 +488,7 @@ int launch_mq_q(const uint8_t* W, size_t ldw, const float* X, size_t ldx, float*
     const int S = p.S, sr = p.seg_rounds;
     if (p.waves == 14 && p.ks == 2) return launch_mq_t<QT, 14, 2, 1>(W, ldw, X, ldx, Y, ldy, M, N, K, S, sr, part, st);
     if (p.waves == 8 && p.ks == 2) return launch_mq_t<QT, 8, 2, 1>(W, ldw, X, ldx, Y, ldy, M, N, K, S, sr, part, st);
-    if (p.waves == 4 && p.ks == 2) return launch_mq_t<QT, 4, 2>(W, ldw, X, ldx, Y, ldy, M, N, K, S, sr, part, st);
+    if (p.waves == 8 && p.ks == 4) return launch_mq_t<QT, 8, 4, 1>(W, ldw, X, ldx, Y, ldy, M, N, K, S, sr, part, st);
     return fail(QMV_EINVAL, "internal: no matrix-core kernel for waves=%d ks=%d", p.waves, p.ks);
 }
 
