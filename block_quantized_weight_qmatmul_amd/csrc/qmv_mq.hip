@@ -31,7 +31,9 @@
 // so all waves of the workgroup work on the same KS consecutive steps
 // (one "round") at a time, and their partial sums are added in a fixed order
 // through LDS at the end (no atomics: bitwise reproducible). Each wave keeps
-// the weight loads of its next four rounds in flight.
+// the weight loads of its next round in flight (the launch shapes split every
+// tile over two or four waves, so that the kernel fits in 96-116 registers and
+// a compute unit runs 8-14 waves).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
