@@ -240,7 +240,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_mq(const uint8_t* __restrict__ W
         }
     };
     auto put_x = [&](int r, int buf, const f32x4a_t (&xr)[RPT][2]) __attribute__((always_inline)) {
-        uint8_t* base = smem + buf * ROUND_BYTES + wave * 2048 + (16 * xg + xj) * 16;
+        // operand slot (G, m) of a block sits at G * 256 + ((m + 4G) % 16) * 16:
+        // the 16 lanes of a quarter wave (four rows, four slices each) then
+        // store to 16 different bank groups, and a lane row G of the reads
+        // still covers one contiguous 256-byte row
+        uint8_t* base = smem + buf * ROUND_BYTES + wave * 2048 + xg * 256 + ((xj + 4 * xg) & 15) * 16;
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
             if ((8 * KS) % WAVES != 0 && wave + i * WAVES >= 8 * KS) continue;  // past the round's blocks
@@ -264,7 +268,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_mq(const uint8_t* __restrict__ W
     auto compute = [&](int r, const uint32_t (&b)[DW]) __attribute__((always_inline)) {
         const int t = (r0 + r) * KS + sp;
         const bool valid = t * 4 + G < P;
-        const uint8_t* xa = smem + (r & 1) * ROUND_BYTES + sp * MQ_STEP_BYTES + G * 256 + j * 16;
+        const uint8_t* xa = smem + (r & 1) * ROUND_BYTES + sp * MQ_STEP_BYTES + G * 256 + ((j + 4 * G) & 15) * 16;
         // both block scales of this lane's pair in one dword; zero past K
         uint32_t dd[4];
         const uint32_t dpk = valid ? ((b[0] & 0xFFFFu) | (QT == QMV_Q4_0 ? (b[4] & 0xFFFF0000u) : (b[8] & 0xFFFF0000u))) : 0u;
@@ -589,8 +593,11 @@ __global__ __launch_bounds__(GM_NT) __attribute__((amdgpu_waves_per_eu(WPE))) vo
             split_bf16_trunc(v, hw, lw);
             const u32x4 hi = (u32x4){hw[0], hw[1], hw[2], hw[3]};
             const u32x4 lo = (u32x4){lw[0], lw[1], lw[2], lw[3]};
-            // its operand slot: lane (G, j) = (slice, row) of the MFMA
-            uint8_t* rec = smem + buf * GM_BUF + (((q >> 6) * 2) * 64 + 16 * (q & 3) + ((q & 63) >> 2)) * 16;
+            // its operand slot (G, j) = (slice, row) of the MFMA, at
+            // G * 256 + ((j + 4G) % 16) * 16 in its 1 KB: a quarter wave's 16
+            // stores then go to 16 different bank groups
+            const int sg = q & 3, sj = (q & 63) >> 2;
+            uint8_t* rec = smem + buf * GM_BUF + (q >> 6) * 2048 + sg * 256 + ((sj + 4 * sg) & 15) * 16;
             *reinterpret_cast<u32x4*>(rec) = hi;
             *reinterpret_cast<u32x4*>(rec + 1024) = lo;
         }
@@ -633,7 +640,7 @@ __global__ __launch_bounds__(GM_NT) __attribute__((amdgpu_waves_per_eu(WPE))) vo
             xpose4(v1);
             xpose4(w1);
         }
-        const uint8_t* xa = smem + buf * GM_BUF + lane * 16;
+        const uint8_t* xa = smem + buf * GM_BUF + G * 256 + ((j + 4 * G) & 15) * 16;
         // eight steps s = (block, activation block) = (s / 4, s % 4): step s
         // reads the A operands of step s + 1, issues its eight MFMAs (four
         // independent hi-then-lo chains) and scales the products of step s - 1
