@@ -240,10 +240,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_mq(const uint8_t* __restrict__ W
         }
     };
     auto put_x = [&](int r, int buf, const f32x4a_t (&xr)[RPT][2]) __attribute__((always_inline)) {
-        // operand slot (G, m) of a block sits at G * 256 + ((m + 4G) % 16) * 16:
-        // the 16 lanes of a quarter wave (four rows, four slices each) then
-        // store to 16 different bank groups, and a lane row G of the reads
-        // still covers one contiguous 256-byte row
+        // operand slot (G, m) of a block sits at G * 256 + ((m + 4G) % 16) * 16,
+        // which spreads the stores of a quarter wave (four rows, four slices
+        // each) over the row while a lane row G of the reads still covers one
+        // contiguous 256-byte row (measured about 1% faster than slot 16G + m)
         uint8_t* base = smem + buf * ROUND_BYTES + wave * 2048 + xg * 256 + ((xj + 4 * xg) & 15) * 16;
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
@@ -594,8 +594,7 @@ __global__ __launch_bounds__(GM_NT) __attribute__((amdgpu_waves_per_eu(WPE))) vo
             const u32x4 hi = (u32x4){hw[0], hw[1], hw[2], hw[3]};
             const u32x4 lo = (u32x4){lw[0], lw[1], lw[2], lw[3]};
             // its operand slot (G, j) = (slice, row) of the MFMA, at
-            // G * 256 + ((j + 4G) % 16) * 16 in its 1 KB: a quarter wave's 16
-            // stores then go to 16 different bank groups
+            // G * 256 + ((j + 4G) % 16) * 16 in its 1 KB (the layout of k_mq)
             const int sg = q & 3, sj = (q & 63) >> 2;
             uint8_t* rec = smem + buf * GM_BUF + (q >> 6) * 2048 + sg * 256 + ((sj + 4 * sg) & 15) * 16;
             *reinterpret_cast<u32x4*>(rec) = hi;
