@@ -469,9 +469,9 @@ def q5k_b9_throughput(dev, steps=48):
 
 def prefill_throughput(dev, M=512, steps=10):
     """Prefill-sized product (qmv_gemm): M = 512 activation rows through the
-    Q4_0 FFN gate matrix 4096 -> 14336 (33 MB), eager raw calls (the M >= 2
-    path takes stream-ordered scratch). Beside it, the pages' F16-shadow route
-    timed on the same shape: an fp16 GEMM of dequantized weights through
+    Q4_0 FFN gate matrix 4096 -> 14336 (33 MB), eager raw calls (a call runs
+    ~150 us, so the host's launch cost does not show). Beside it, the pages'
+    F16-shadow route timed on the same shape: an fp16 GEMM of dequantized weights through
     torch.matmul (hipBLASLt) -- timing only, its fp16 activations do not meet
     the parity tolerance."""
     import torch
