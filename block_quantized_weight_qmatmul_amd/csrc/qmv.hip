@@ -1080,8 +1080,13 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4)))
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
     // ---- group the pairs by expert ----
-    const int U = group_by_expert<NT>(ids, n_pairs, n_experts, s_map, s_uexp, s_ustart, s_cnt, s_plist, &s_U, Y, ldy,
-                                      N, err_flag);
+    // The tables are read by every lane at one address; readfirstlane tells
+    // the compiler so, which keeps the values below in scalar registers and
+    // the per-row tests `i < nx` scalar branches (as lane masks they cost a
+    // few VALU instructions per staged row and half block).
+    const int U = __builtin_amdgcn_readfirstlane(group_by_expert<NT>(
+        ids, n_pairs, n_experts, s_map, s_uexp, s_ustart, s_cnt, s_plist, &s_U, Y, ldy, N, err_flag));
+    auto ust = [&](int u) { return __builtin_amdgcn_readfirstlane(s_ustart[u]); };
 
     // ---- stream this workgroup's share of the virtual matrix ----
     const int g = lane / LPR, j = lane % LPR;
@@ -1092,7 +1097,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4)))
     // plus 2 (the weight load and decode), so experts that many pairs select
     // spread over more workgroups. Row n of u sits at cost B(u) + n * c(u);
     // this workgroup takes the rows whose cost position is in [lo, hi).
-    auto B = [&](int u) { return (long)N * (s_ustart[u] + 2L * u); };
+    auto B = [&](int u) { return (long)N * (ust(u) + 2L * u); };
     const long C = B(U);
     const long lo = C * blockIdx.x / gridDim.x, hi = C * (blockIdx.x + 1) / gridDim.x;
     int u = 0;
@@ -1101,15 +1106,15 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4)))
     uint32_t bufA[RPT][DW], bufB[RPT][DW];
     bool staged = false;  // xs holds rows another segment may still be reading
     for (; u < U && B(u) < hi; ++u) {
-        const long cu = s_ustart[u + 1] - s_ustart[u] + 2;
+        const int pbeg = ust(u), pend = ust(u + 1);
+        const long cu = pend - pbeg + 2;
         const long a = lo - B(u), b = hi - B(u);
         const int n0 = a <= 0 ? 0 : (int)((a + cu - 1) / cu);
         const int n1 = (int)((b + cu - 1) / cu < N ? (b + cu - 1) / cu : N);
         if (n0 >= n1) continue;
-        const uint32_t e = (uint32_t)s_uexp[u];
+        const uint32_t e = (uint32_t)__builtin_amdgcn_readfirstlane(s_uexp[u]);
         const uint8_t* We = W + (size_t)e * estride;
         const float sc = (escale ? escale[e] : 1.f) * T::OUT_SCALE;
-        const int pbeg = s_ustart[u], pend = s_ustart[u + 1];
         const int ntl = (n1 - n0 + ROWS - 1) / ROWS;
         const int lrow = (wave * GROUPS + g) * RPT;  // this lane group's first row in a tile
         for (int c0 = pbeg; c0 < pend; c0 += mxcap) {
@@ -1152,13 +1157,18 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4)))
                     float w[RPT][16];
 #pragma unroll
                     for (int r = 0; r < RPT; ++r) decode_half_w<QT, R, H>(cb[r], w[r]);
+                    // a fresh scalar copy of nx per half block: the row tests
+                    // stay scalar compares and branches, not lane masks
+                    // hoisted out of the loop and rebuilt at every use
+                    int nxh = nx;
+                    asm volatile("" : "+s"(nxh));
 #pragma unroll
                     for (int i = 0; i < MXR; ++i) {
                         if constexpr (H == 0) {
 #pragma unroll
                             for (int r = 0; r < RPT; ++r) sb[R][r][i] = 0.f;
                         }
-                        if (i < nx) {
+                        if (i < nxh) {
                             const float4* xv =
                                 reinterpret_cast<const float4*>(xs + i * xstride + pc * XS_PAIR) + 8 * R + 4 * H;
 #pragma unroll
@@ -1178,12 +1188,14 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4)))
                     // above these products only holds more registers
                     __builtin_amdgcn_sched_barrier(0);
                 });
+                int nxt = nx;
+                asm volatile("" : "+s"(nxt));
 #pragma unroll
                 for (int r = 0; r < RPT; ++r) {
                     const float d0 = half_lo(cb[r][0]), d1 = QT == QMV_Q4_0 ? half_hi(cb[r][4]) : half_hi(cb[r][8]);
 #pragma unroll
                     for (int i = 0; i < MXR; ++i) {
-                        if (i < nx) {
+                        if (i < nxt) {
                             const float d = fmaf(d1, sb[1][r][i], d0 * sb[0][r][i]);
                             tot[r][i] += in ? d : 0.f;
                         }
@@ -1194,7 +1206,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4)))
 #pragma unroll
                     for (int i = 0; i < MXR; ++i) {
                         if (i < nx) {
-                            float* yr = Y + (size_t)s_plist[c0 + i] * ldy;
+                            float* yr = Y + (size_t)__builtin_amdgcn_readfirstlane(s_plist[c0 + i]) * ldy;
 #pragma unroll
                             for (int r = 0; r < RPT; ++r) {
                                 const float sum = lane_group_sum<LPR>(tot[r][i]);
@@ -2053,12 +2065,16 @@ __global__ __launch_bounds__(WAVES * 64) void k_q6kc(const Q6Cat<MAXP> C) {
 
     long tile = blockIdx.x;
     if (tile >= ntiles) return;  // uniform over the workgroup
-    // the problem of a tile (uniform: a few scalar compares)
+    // The problem of a tile. Tile indices fit in 32 bits (the launch checks
+    // it), and 32-bit compares stay scalar; as 64-bit compares they run on
+    // the VALU, and the problem index, held in a vector register, then
+    // makes every table read below a vector memory load on the step's path.
     auto prob = [&](long tl) {
+        const int t = (int)tl;
         int ip = 0;
 #pragma unroll
-        for (int q = 1; q < MAXP; ++q) ip += (q < C.n && tl >= C.t0[q]) ? 1 : 0;
-        return ip;
+        for (int q = 1; q < MAXP; ++q) ip += (q < C.n && t >= (int)C.t0[q]) ? 1 : 0;
+        return __builtin_amdgcn_readfirstlane(ip);
     };
     int ip = prob(tile);
     const uint8_t* iW = C.W[ip];
@@ -2839,6 +2855,7 @@ int launch_q6kc_t(const M1Prob* probs, int n, hipStream_t st) {
     C.x = probs[0].x;
     C.K = probs[0].K;
     C.n = n;
+    if (t > 0x7FFFFFFF) return fail(QMV_EINVAL, "qmv_batch: N too large");  // tile indices are 32-bit
     long nwg = (long)num_cus() * 2;
     nwg = nwg < t ? nwg : t;
     hipLaunchKernelGGL((k_q6kc<F, LPR, WAVES, MAXP>), dim3((unsigned)nwg), dim3(WAVES * 64), q6_xs_bytes(C.K), st, C);
